@@ -1,0 +1,110 @@
+"""Slot mapping, block-table gather and decode attention in fp64
+(test infrastructure only; see package docstring).
+
+Definitions followed:
+
+* Attention output is softmax(q K^T / sqrt(d)) V (bjdmk.com.cn article,
+  §2.1 从注意力公式推导KV Cache为什么必须存在).  In decode the query is the
+  single newest token and it attends over every cached position, its own
+  included ("KV Cache 原理与 PagedAttention", §一: generating token t needs
+  K_1..K_t and V_1..V_t).  So ``context_len`` counts the token being decoded;
+  no mask other than the context length applies.
+* The cache is split into fixed-size blocks; a sequence's table maps logical
+  block i to a physical block, and attention gathers the scattered physical
+  blocks through that table ("KV Cache 原理与 PagedAttention", §三 工作方式
+  steps 1, 2 and 4).  Logical position t lives in logical block t // B at
+  offset t % B, i.e. in slot table[t // B] * B + t % B.
+* Grouped-query attention: with Hq query heads sharing Hkv < Hq KV heads
+  (same page, §一 GQA / MQA 为什么省 KV Cache), query head h reads KV head
+  h // G, G = Hq / Hkv (contiguous groups; the pages only count heads, the
+  grouping order is this library's reading).
+
+The oracle resolves the table into contiguous fp64 K/V and applies the
+textbook formula with an explicit max subtraction.  It never splits contexts
+and never uses a streaming softmax.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import codecs
+from .layout import (KV_BF16, KV_FP8_E5M2, KV_INT8, PoolImage, k_offset,
+                     scale_offset, v_offset)
+
+
+def slot_of(block_table_row: np.ndarray, pos, block_size: int):
+    """Physical slot of logical position(s) ``pos`` of one sequence."""
+    pos = np.asarray(pos, dtype=np.int64)
+    row = np.asarray(block_table_row, dtype=np.int64)
+    return row[pos // block_size] * block_size + pos % block_size
+
+
+def gather_kv(img: PoolImage, layer: int, block_table_row: np.ndarray,
+              ctx: int, k_scale: float = 1.0, v_scale: float = 1.0):
+    """Contiguous dequantised K and V, each [ctx, Hkv, D] float64."""
+    p = img.shape
+    if ctx == 0:
+        z = np.zeros((0, p.num_kv_heads, p.head_dim))
+        return z, z.copy()
+    pos = np.arange(ctx, dtype=np.int64)
+    slots = slot_of(block_table_row, pos, p.block_size)
+    blk = (slots // p.block_size)[:, None, None]
+    t = (slots % p.block_size)[:, None, None]
+    h = np.arange(p.num_kv_heads)[None, :, None]
+    d = np.arange(p.head_dim)[None, None, :]
+    kraw = img.k[k_offset(p, layer, blk, h, t, d)]
+    vraw = img.v[v_offset(p, layer, blk, h, t, d)]
+    if p.kv_dtype == KV_BF16:
+        return codecs.bf16_bits_to_f64(kraw), codecs.bf16_bits_to_f64(vraw)
+    if p.kv_dtype == KV_FP8_E5M2:
+        ks = np.float64(np.float32(k_scale))
+        vs = np.float64(np.float32(v_scale))
+        return codecs.e5m2_decode(kraw) * ks, codecs.e5m2_decode(vraw) * vs
+    if p.kv_dtype == KV_INT8:
+        so = scale_offset(p, layer, blk[:, :, 0], h[:, :, 0], t[:, :, 0])
+        return (codecs.int8_dequant(kraw, img.k_scale[so]),
+                codecs.int8_dequant(vraw, img.v_scale[so]))
+    raise ValueError(p.kv_dtype)
+
+
+def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """Decode attention of one sequence on contiguous fp64 K/V.
+
+    q: [Hq, D] float64; K, V: [ctx, Hkv, D] float64; scale: the fp32 softmax
+    scale (used as its exact float64 value).  Returns [Hq, D] float64.
+    """
+    hq, dim = q.shape
+    ctx, hkv, _ = K.shape
+    out = np.zeros((hq, dim), dtype=np.float64)
+    if ctx == 0:
+        return out
+    group = hq // hkv
+    sc = np.float64(np.float32(scale))
+    for h in range(hq):
+        g = h // group
+        z = sc * (K[:, g, :] @ q[h])                     # [ctx]
+        w = np.exp(z - np.max(z))
+        p = w / np.sum(w)
+        out[h] = p @ V[:, g, :]
+    return out
+
+
+def paged_decode(q_bits: np.ndarray, img: PoolImage, layer: int,
+                 block_tables: np.ndarray, context_lens: np.ndarray,
+                 scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+                 seqs=None) -> np.ndarray:
+    """Paged decode for every sequence (or the listed ``seqs``).
+
+    q_bits: [S, Hq, D] bf16 bit patterns.  Returns [S, Hq, D] float64 (rows
+    of sequences not in ``seqs`` are left zero).
+    """
+    q_bits = np.asarray(q_bits, dtype=np.uint16)
+    S, hq, dim = q_bits.shape
+    out = np.zeros((S, hq, dim), dtype=np.float64)
+    idx = range(S) if seqs is None else seqs
+    for s in idx:
+        ctx = int(context_lens[s])
+        K, V = gather_kv(img, layer, block_tables[s], ctx, k_scale, v_scale)
+        out[s] = attend(codecs.bf16_bits_to_f64(q_bits[s]), K, V, scale)
+    return out

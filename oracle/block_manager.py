@@ -1,0 +1,139 @@
+"""Python model of the host block manager (test infrastructure only).
+
+What it models:
+
+* A pool of ``num_blocks`` preallocated physical blocks of ``block_size``
+  token slots, handed to sequences on demand and returned when a sequence
+  ends ("KV Cache 原理与 PagedAttention", §三 工作方式 steps 1-3; aiworkagent.org
+  Q17, PagedAttention 的关键数据结构: KV Memory Pool).
+* A per-sequence block table: entry i is the physical block of logical block i
+  (same sources).  A sequence of n tokens holds exactly ceil(n / B) blocks, so
+  at most one block, its last, is partly empty (§三 收益 table).
+* Sharing: a forked sequence points at its parent's physical blocks; before a
+  sequence writes into a block that someone else also references, the block is
+  copied, the writer's table is repointed at the copy, then the write happens
+  (bjdmk.com.cn article, §3.1 and §3.2 Copy-on-Write).
+
+Rules that the pages leave open, fixed here (and in the C++ manager) so that
+tables, slots and copy pairs are unique and comparable bit for bit:
+
+* Free blocks form a FIFO queue.  Its initial order is supplied by the caller
+  (an explicit permutation of all block ids); allocation pops the front, a
+  block whose reference count drops to zero is pushed to the back.
+* Appending to a sequence of current length n writes position n.  If n % B == 0
+  a fresh block is appended to the table.  Otherwise, if the last block's
+  reference count exceeds one, a fresh block ``dst`` is taken, the pair
+  (src=last, dst) is reported for copying, the count of ``src`` drops by one,
+  ``dst`` starts at one and replaces ``src`` in the writer's table; the last
+  remaining holder writes in place.  The slot is table[n // B] * B + n % B.
+* A batch append processes sequences in the order given and is all or
+  nothing: if the pool cannot serve every block the batch needs, it fails,
+  the failed-allocation counter rises by one and nothing else changes.
+* Freeing a sequence releases its blocks in table order.
+* Table rows are padded with 0 past the sequence's blocks.
+"""
+
+from __future__ import annotations
+
+from collections import deque
+
+OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_OUT_OF_BLOCKS = 0, -1, -2, -3
+
+
+class BlockManagerModel:
+    def __init__(self, num_blocks: int, block_size: int, initial_order=None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise ValueError("bad sizes")
+        order = list(range(num_blocks)) if initial_order is None else [int(b) for b in initial_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise ValueError("initial order must be a permutation of all block ids")
+        self.num_blocks = num_blocks
+        self.B = block_size
+        self.free = deque(order)
+        self.ref = [0] * num_blocks
+        self.tables: dict[int, list[int]] = {}
+        self.ctx: dict[int, int] = {}
+        self.failed_allocs = 0
+
+    # ------------------------------------------------------------ helpers
+    def _take(self) -> int:
+        b = self.free.popleft()
+        self.ref[b] = 1
+        return b
+
+    # ------------------------------------------------------------ API
+    def add_seq(self, seq: int, ctx_len: int) -> int:
+        if seq in self.tables or ctx_len < 0:
+            return ERR_INVALID
+        need = -(-ctx_len // self.B)
+        if need > len(self.free):
+            self.failed_allocs += 1
+            return ERR_OUT_OF_BLOCKS
+        self.tables[seq] = [self._take() for _ in range(need)]
+        self.ctx[seq] = ctx_len
+        return OK
+
+    def fork(self, parent: int, child: int) -> int:
+        if parent not in self.tables or child in self.tables:
+            return ERR_INVALID
+        self.tables[child] = list(self.tables[parent])
+        self.ctx[child] = self.ctx[parent]
+        for b in self.tables[child]:
+            self.ref[b] += 1
+        return OK
+
+    def append_batch(self, seqs):
+        """Returns (status, slots list, cow pairs list)."""
+        seqs = [int(s) for s in seqs]
+        if len(set(seqs)) != len(seqs) or any(s not in self.tables for s in seqs):
+            return ERR_INVALID, [], []
+        # dry run: count the fresh blocks the batch needs
+        need = 0
+        ref_delta: dict[int, int] = {}
+        for s in seqs:
+            pos = self.ctx[s]
+            if pos % self.B == 0:
+                need += 1
+            else:
+                last = self.tables[s][pos // self.B]
+                if self.ref[last] + ref_delta.get(last, 0) > 1:
+                    need += 1
+                    ref_delta[last] = ref_delta.get(last, 0) - 1
+        if need > len(self.free):
+            self.failed_allocs += 1
+            return ERR_OUT_OF_BLOCKS, [], []
+        slots, pairs = [], []
+        for s in seqs:
+            pos = self.ctx[s]
+            tab = self.tables[s]
+            if pos % self.B == 0:
+                tab.append(self._take())
+            else:
+                last = tab[pos // self.B]
+                if self.ref[last] > 1:
+                    dst = self._take()
+                    self.ref[last] -= 1
+                    tab[pos // self.B] = dst
+                    pairs.append((last, dst))
+            slots.append(tab[pos // self.B] * self.B + pos % self.B)
+            self.ctx[s] = pos + 1
+        return OK, slots, pairs
+
+    def free_seq(self, seq: int) -> int:
+        if seq not in self.tables:
+            return ERR_INVALID
+        for b in self.tables.pop(seq):
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.append(b)
+        del self.ctx[seq]
+        return OK
+
+    def block_table(self, seq: int, width: int):
+        tab = self.tables[seq]
+        if len(tab) > width:
+            raise ValueError("table wider than width")
+        return tab + [0] * (width - len(tab))
+
+    def stats(self):
+        return self.num_blocks - len(self.free), self.num_blocks, self.failed_allocs

@@ -1,0 +1,93 @@
+"""Expected pool contents after the two write operations (test infrastructure only).
+
+* ``reshape_and_cache``: when token t is generated its K_t and V_t are computed
+  once and appended to the end of the sequence's cache
+  ("KV Cache 原理与 PagedAttention", §一, the decode-step box); in a paged cache
+  "the end" is the slot that the block table gives for position t (§三 工作方式
+  steps 2-3).  Each new token's K/V for every KV head lands in its slot,
+  quantised on the way in for 8-bit storage; every other byte of the pool is
+  left unchanged.  A negative slot means "no token" and writes nothing.
+
+* ``copy_blocks``: copy-on-write splitting of a shared block copies the whole
+  physical block before the writer's table is repointed (bjdmk.com.cn article,
+  §3.2 Copy-on-Write).  Every layer's K tile, V tile and (INT8) scale rows of
+  ``src`` are copied to ``dst``; all copies read the state before the call.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import codecs
+from .layout import (KV_BF16, KV_FP8_E5M2, KV_INT8, PoolImage, k_offset,
+                     scale_offset, tile_base, v_offset)
+
+
+def reshape_and_cache(img: PoolImage, layer: int, key_bits: np.ndarray,
+                      value_bits: np.ndarray, slots: np.ndarray,
+                      k_scale: float = 1.0, v_scale: float = 1.0) -> PoolImage:
+    """Return a new pool image with tokens ``key_bits/value_bits`` [N, Hkv, D]
+    (bf16 bit patterns) written at ``slots`` [N] of ``layer``."""
+    p = img.shape
+    out = img.copy()
+    key_bits = np.asarray(key_bits, dtype=np.uint16)
+    value_bits = np.asarray(value_bits, dtype=np.uint16)
+    slots = np.asarray(slots, dtype=np.int64)
+    n_tok, hkv, d = key_bits.shape
+    assert hkv == p.num_kv_heads and d == p.head_dim
+
+    keep = np.nonzero(slots >= 0)[0]
+    if keep.size == 0:
+        return out
+    blk = slots[keep] // p.block_size
+    t = slots[keep] % p.block_size
+    # broadcast to [n, Hkv, D]
+    blk3 = blk[:, None, None]
+    t3 = t[:, None, None]
+    h3 = np.arange(hkv)[None, :, None]
+    d3 = np.arange(d)[None, None, :]
+    ko = k_offset(p, layer, blk3, h3, t3, d3)
+    vo = v_offset(p, layer, blk3, h3, t3, d3)
+    kx = key_bits[keep]
+    vx = value_bits[keep]
+
+    if p.kv_dtype == KV_BF16:
+        out.k[ko] = kx
+        out.v[vo] = vx
+    elif p.kv_dtype == KV_FP8_E5M2:
+        out.k[ko] = codecs.e5m2_encode(codecs.bf16_bits_to_f32(kx), k_scale)
+        out.v[vo] = codecs.e5m2_encode(codecs.bf16_bits_to_f32(vx), v_scale)
+    elif p.kv_dtype == KV_INT8:
+        kc, ks = codecs.int8_quantize(codecs.bf16_bits_to_f32(kx))
+        vc, vs = codecs.int8_quantize(codecs.bf16_bits_to_f32(vx))
+        out.k[ko] = kc
+        out.v[vo] = vc
+        so = scale_offset(p, layer, blk[:, None], np.arange(hkv)[None, :], t[:, None])
+        out.k_scale[so] = ks
+        out.v_scale[so] = vs
+    else:
+        raise ValueError(p.kv_dtype)
+    return out
+
+
+def copy_blocks(img: PoolImage, pairs: np.ndarray) -> PoolImage:
+    """Return a new image where, in every layer, block dst holds a byte copy of
+    block src for each (src, dst) row of ``pairs``."""
+    p = img.shape
+    src_img = img
+    out = img.copy()
+    pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    te = p.tile_elems
+    for layer in range(p.num_layers):
+        for src, dst in pairs:
+            for h in range(p.num_kv_heads):
+                s0 = int(tile_base(p, layer, src, h))
+                d0 = int(tile_base(p, layer, dst, h))
+                out.k[d0:d0 + te] = src_img.k[s0:s0 + te]
+                out.v[d0:d0 + te] = src_img.v[s0:s0 + te]
+                if p.has_scales:
+                    ss = int(scale_offset(p, layer, src, h, 0))
+                    ds = int(scale_offset(p, layer, dst, h, 0))
+                    out.k_scale[ds:ds + p.block_size] = src_img.k_scale[ss:ss + p.block_size]
+                    out.v_scale[ds:ds + p.block_size] = src_img.v_scale[ss:ss + p.block_size]
+    return out

@@ -1,0 +1,171 @@
+"""Pool layout as a plain index function (test infrastructure only).
+
+The pages fix only the logical structure: a pool of preallocated, fixed-size
+physical blocks, each holding the K/V of ``block_size`` consecutive tokens, and
+a per-sequence table mapping logical block i to a physical block
+("KV Cache 原理与 PagedAttention", §三 工作方式 steps 1-2; aiworkagent.org Q17,
+PagedAttention 的关键数据结构).  The byte layout inside the pool is this
+library's own choice, documented in ``include/pkv.h``; this module restates that
+documentation as arithmetic so that the oracle can read and write pools
+produced by the device code.
+
+Element offsets below are in *elements* of the storage type (bf16: 2 bytes,
+fp8/int8: 1 byte) from the start of the K (or V) region:
+
+    K:  ((((layer * NB + block) * Hkv + head) * B * D)
+          + ((d // X) * B + t) * X + (d % X))          X = 16 // elem_bytes
+    V:  ((((layer * NB + block) * Hkv + head) * B * D)
+          + ((t // 4) * D + d) * 4 + (t % 4))
+    K/V scales (INT8 only, fp32 elements):
+          ((layer * NB + block) * Hkv + head) * B + t
+
+Regions are laid out K, V, K-scales, V-scales, each starting at a multiple of
+256 bytes from the pool base.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+KV_BF16, KV_FP8_E5M2, KV_INT8 = 0, 1, 2
+ELEM_BYTES = {KV_BF16: 2, KV_FP8_E5M2: 1, KV_INT8: 1}
+REGION_ALIGN = 256
+
+
+@dataclass(frozen=True)
+class PoolShape:
+    num_layers: int
+    num_blocks: int
+    block_size: int
+    num_kv_heads: int
+    head_dim: int
+    kv_dtype: int = KV_BF16
+
+    @property
+    def elem_bytes(self) -> int:
+        return ELEM_BYTES[self.kv_dtype]
+
+    @property
+    def x(self) -> int:
+        return 16 // self.elem_bytes
+
+    @property
+    def tile_elems(self) -> int:
+        return self.block_size * self.head_dim
+
+    @property
+    def region_elems(self) -> int:
+        return self.num_layers * self.num_blocks * self.num_kv_heads * self.tile_elems
+
+    @property
+    def has_scales(self) -> bool:
+        return self.kv_dtype == KV_INT8
+
+
+def _align(n: int) -> int:
+    return (n + REGION_ALIGN - 1) // REGION_ALIGN * REGION_ALIGN
+
+
+def region_offsets(p: PoolShape):
+    """Byte offsets (k, v, k_scale, v_scale, total).  Scale offsets are None
+    when the storage type carries no per-token-head scales."""
+    kv_bytes = p.region_elems * p.elem_bytes
+    k_off = 0
+    v_off = _align(k_off + kv_bytes)
+    end = _align(v_off + kv_bytes)
+    if p.has_scales:
+        s_bytes = p.num_layers * p.num_blocks * p.num_kv_heads * p.block_size * 4
+        ks_off = end
+        vs_off = _align(ks_off + s_bytes)
+        end = _align(vs_off + s_bytes)
+        return k_off, v_off, ks_off, vs_off, end
+    return k_off, v_off, None, None, end
+
+
+def tile_base(p: PoolShape, layer, block, head):
+    return (((np.asarray(layer, dtype=np.int64) * p.num_blocks + block)
+             * p.num_kv_heads + head) * p.tile_elems)
+
+
+def k_offset(p: PoolShape, layer, block, head, t, d):
+    t = np.asarray(t, dtype=np.int64)
+    d = np.asarray(d, dtype=np.int64)
+    return tile_base(p, layer, block, head) + ((d // p.x) * p.block_size + t) * p.x + (d % p.x)
+
+
+def v_offset(p: PoolShape, layer, block, head, t, d):
+    t = np.asarray(t, dtype=np.int64)
+    d = np.asarray(d, dtype=np.int64)
+    return tile_base(p, layer, block, head) + ((t // 4) * p.head_dim + d) * 4 + (t % 4)
+
+
+def scale_offset(p: PoolShape, layer, block, head, t):
+    return ((np.asarray(layer, dtype=np.int64) * p.num_blocks + block)
+            * p.num_kv_heads + head) * p.block_size + np.asarray(t, dtype=np.int64)
+
+
+# ------------------------------------------------------------ host pool image
+@dataclass
+class PoolImage:
+    """Host copy of a whole pool, split into typed flat regions."""
+    shape: PoolShape
+    k: np.ndarray                 # uint16 (bf16 bits) or uint8 / int8 codes
+    v: np.ndarray
+    k_scale: np.ndarray | None    # float32
+    v_scale: np.ndarray | None
+
+    def copy(self) -> "PoolImage":
+        return PoolImage(self.shape, self.k.copy(), self.v.copy(),
+                         None if self.k_scale is None else self.k_scale.copy(),
+                         None if self.v_scale is None else self.v_scale.copy())
+
+
+def _storage_dtype(p: PoolShape):
+    return {KV_BF16: np.uint16, KV_FP8_E5M2: np.uint8, KV_INT8: np.int8}[p.kv_dtype]
+
+
+def empty_image(p: PoolShape, fill: int = 0) -> PoolImage:
+    dt = _storage_dtype(p)
+    k = np.full(p.region_elems, fill, dtype=dt)
+    v = np.full(p.region_elems, fill, dtype=dt)
+    ks = vs = None
+    if p.has_scales:
+        n = p.num_layers * p.num_blocks * p.num_kv_heads * p.block_size
+        ks = np.zeros(n, dtype=np.float32)
+        vs = np.zeros(n, dtype=np.float32)
+    return PoolImage(p, k, v, ks, vs)
+
+
+def image_from_bytes(p: PoolShape, raw: np.ndarray) -> PoolImage:
+    """Split the raw bytes of a whole pool (uint8) into its typed regions."""
+    raw = np.asarray(raw, dtype=np.uint8)
+    k_off, v_off, ks_off, vs_off, total = region_offsets(p)
+    assert raw.size >= total, (raw.size, total)
+    nb = p.region_elems * p.elem_bytes
+    dt = _storage_dtype(p)
+    k = raw[k_off:k_off + nb].view(dt).copy()
+    v = raw[v_off:v_off + nb].view(dt).copy()
+    ks = vs = None
+    if p.has_scales:
+        sb = p.num_layers * p.num_blocks * p.num_kv_heads * p.block_size * 4
+        ks = raw[ks_off:ks_off + sb].view(np.float32).copy()
+        vs = raw[vs_off:vs_off + sb].view(np.float32).copy()
+    return PoolImage(p, k, v, ks, vs)
+
+
+def image_to_bytes(img: PoolImage) -> np.ndarray:
+    p = img.shape
+    k_off, v_off, ks_off, vs_off, total = region_offsets(p)
+    raw = np.zeros(total, dtype=np.uint8)
+    kb = img.k.view(np.uint8)
+    raw[k_off:k_off + kb.size] = kb
+    vb = img.v.view(np.uint8)
+    raw[v_off:v_off + vb.size] = vb
+    if p.has_scales:
+        ksb = img.k_scale.view(np.uint8)
+        raw[ks_off:ks_off + ksb.size] = ksb
+        vsb = img.v_scale.view(np.uint8)
+        raw[vs_off:vs_off + vsb.size] = vsb
+    return raw

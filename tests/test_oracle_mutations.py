@@ -1,0 +1,55 @@
+"""Planted mistakes in the oracle (on the CPU) must be caught by its pins.
+
+Each case monkeypatches one plausible slip into the oracle and re-runs a pin
+that should then fail: a transposed grouping, a slot off by one, a dropped
+softmax scale, a wrong e5m2 exponent bias.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.attention as att
+import oracle.codecs as codecs
+from tests import test_oracle_attention as ta
+from tests import test_oracle_codecs as tc
+
+
+def _fails(fn):
+    try:
+        fn()
+    except AssertionError:
+        return True
+    return False
+
+
+def test_wrong_group_mapping_is_caught(monkeypatch):
+    orig = att.attend
+
+    def attend_bad(q, K, V, scale):
+        hq = q.shape[0]
+        hkv = K.shape[1]
+        perm = np.arange(hq).reshape(hkv, hq // hkv).T.ravel()   # h % Hkv grouping
+        return orig(q[perm], K, V, scale)[np.argsort(perm)]
+    monkeypatch.setattr(att, "attend", attend_bad)
+    assert _fails(ta.test_tiny_config_matches_sdpa)
+
+
+def test_slot_off_by_one_is_caught(monkeypatch):
+    def slot_bad(row, pos, B):
+        pos = np.asarray(pos, dtype=np.int64)
+        row = np.asarray(row, dtype=np.int64)
+        return row[pos // B] * B + (pos + 1) % B
+    monkeypatch.setattr(att, "slot_of", slot_bad)
+    assert _fails(ta.test_tiny_config_matches_sdpa)
+
+
+def test_dropped_scale_is_caught(monkeypatch):
+    orig = att.attend
+    monkeypatch.setattr(att, "attend", lambda q, K, V, s: orig(q, K, V, 1.0))
+    assert _fails(lambda: ta.test_random_small_cases_match_sdpa(3))
+
+
+def test_wrong_e5m2_bias_is_caught(monkeypatch):
+    orig = codecs.e5m2_decode
+    monkeypatch.setattr(codecs, "e5m2_decode", lambda c: orig(c) * 2.0)
+    assert _fails(tc.test_e5m2_decode_matches_binary16_high_byte)
