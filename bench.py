@@ -1,0 +1,251 @@
+"""Benchmark: one paged decode step of a 70B-shaped model on one MI355X.
+
+A step is the whole hot path over one batch: the host block manager appends
+one token to each of the 100 sequences (slots, any copy-on-write pairs,
+tables), the tables / lengths / slots are uploaded, then for each of the 80
+layers the new token's K/V is written into its slot and paged decode
+attention runs over every sequence's ~4K-token history (partition size 512).
+
+Workload (synthetic, seeded): 80 layers, 64 query / 8 KV heads, head_dim 128,
+bf16, 16-token blocks, 100 sequences with contexts ~N(4096, 256) clipped to
+[3072, 5120], blocks placed by a seeded permutation of a pool 1.02x the
+blocks needed (+ room for the appended tokens).  Cached K/V are N(0, 1)
+draws made on the device.
+
+Prints one JSON line: KV-read GB/s (whole step), seq-steps/s, % of the MI355X
+HBM peak, a roofline entry for the decode kernels (HIP events around every
+decode call of the timed steps), and the fp64 CPU oracle timed on a bounded
+sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--partition 512]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0    # MI355X HBM3E, AMD's published peak
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--partition", type=int, default=512)
+    ap.add_argument("--layers", type=int, default=80,
+                    help="layers per step (the workload has 80; fewer only for quick experiments)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import paged_kv_cache_436_amd as pkv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    steps_total = args.warmup + args.steps + 1
+    w = workloads.llama70b(num_layers=80, extra_steps=steps_total)
+    L = args.layers
+    S, Hq, Hkv, D, B, W = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.table_width
+    P = args.partition
+
+    # ---------------------------------------------------------------- state
+    bm = pkv.BlockManager(w.num_blocks, B, w.block_order)
+    for s in range(S):
+        bm.add_seq(s, int(w.context_lens[s]) - 1)      # history; each step appends one token
+    cfg = pkv.make_config(w.num_layers, w.num_blocks, B, Hkv, D, pkv.PKV_KV_BF16)
+    log(f"pool: {pkv.kv_pool_bytes(cfg) / 1e9:.1f} GB, {w.num_blocks} blocks/layer x {w.num_layers} layers")
+    pool = pkv.Pool(cfg, device=dev)
+    k_off, v_off, _, _ = pool.region_offsets()
+    lb = pool.desc.layer_bytes
+    t0 = time.time()
+    for layer in range(w.num_layers):
+        g = torch.Generator(device=dev)
+        g.manual_seed(436003 * 1000 + layer)
+        for off in (k_off, v_off):
+            pool.memory[off + layer * lb: off + (layer + 1) * lb].view(torch.bfloat16).normal_(generator=g)
+    torch.cuda.synchronize()
+    log(f"pool filled in {time.time() - t0:.1f} s")
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(436003)
+    q = torch.randn((L, S, Hq, D), generator=g, device=dev).to(torch.bfloat16)
+    newk = torch.randn((L, S, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+    newv = torch.randn((L, S, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, pkv.paged_attn_workspace_bytes(S, Hq, D, W, B, P)), dtype=torch.uint8, device=dev)
+    scale = w.scale
+
+    # double-buffered pinned host staging for tables / lengths / slots
+    seqs = np.arange(S, dtype=np.int32)
+    h_tab = [torch.empty((S, W), dtype=torch.int32).pin_memory() for _ in range(2)]
+    h_ctx = [torch.empty(S, dtype=torch.int32).pin_memory() for _ in range(2)]
+    h_slot = [torch.empty(S, dtype=torch.int64).pin_memory() for _ in range(2)]
+    h_done = [torch.cuda.Event() for _ in range(2)]
+    d_tab = torch.empty((S, W), dtype=torch.int32, device=dev)
+    d_ctx = torch.empty(S, dtype=torch.int32, device=dev)
+    d_slot = torch.empty(S, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+    kv_bytes = []
+    dec_events = []
+
+    def step(i, timed):
+        b = i % 2
+        h_done[b].synchronize()                       # staging buffer b is free again
+        slots, pairs = bm.append(seqs)
+        assert pairs.shape[0] == 0                    # no sharing in this workload
+        bm.block_tables(seqs, W, out=h_tab[b].numpy(), ctx_out=h_ctx[b].numpy())
+        h_slot[b].numpy()[:] = slots
+        d_tab.copy_(h_tab[b], non_blocking=True)
+        d_ctx.copy_(h_ctx[b], non_blocking=True)
+        d_slot.copy_(h_slot[b], non_blocking=True)
+        h_done[b].record(stream)
+        kv_bytes.append(int(h_ctx[b].numpy().astype(np.int64).sum()) * Hkv * 2 * D * 2 * L)
+        for layer in range(L):
+            pkv.reshape_and_cache(pool, layer, newk[layer], newv[layer], d_slot, stream=stream)
+            if timed:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            pkv.paged_attn_decode(out, q[layer], pool, layer, d_tab, d_ctx, scale, partition_size=P,
+                                  workspace=ws, stream=stream)
+            if timed:
+                e1.record(stream)
+                dec_events.append((e0, e1, int(h_ctx[b].numpy().astype(np.int64).sum())))
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    log("warmup done")
+    kv_bytes.clear()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    kv_per_step = sum(kv_bytes) / args.steps
+    gbs = sum(kv_bytes) / elapsed / 1e9
+    dec_ms = [e0.elapsed_time(e1) for e0, e1, _ in dec_events]
+    dec_bytes = [n * Hkv * 2 * D * 2 for _, _, n in dec_events]
+    avg_dec_ms = float(np.mean(dec_ms))
+    avg_dec_bytes = float(np.mean(dec_bytes))
+    achieved = avg_dec_bytes / (avg_dec_ms * 1e-3) / 1e9
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {gbs:.1f} GB/s; "
+        f"decode call avg {avg_dec_ms * 1e3:.1f} us = {achieved:.1f} GB/s")
+
+    # ---------------------------------------------------------------- sampled parity + CPU baseline
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        cpu, parity = cpu_baseline(args, pkv, w, pool, bm, q, out, ws, d_tab, d_ctx, scale, P, stream)
+
+    res = {
+        "metric": "paged decode KV-read GB/s (% of MI355X HBM peak) + decode seq-steps/s",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "70B-shaped paged decode step: 80 layers x 100 seqs x ~4K ctx, "
+                               "64q/8kv heads, head_dim 128, bf16 KV, block 16",
+                   "layers": L, "seqs": S, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+                   "block_size": B, "partition_size": P, "kv_bytes_per_step": int(kv_per_step)},
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "seq_steps_per_s": round(S / (elapsed / args.steps), 1),
+        "seq_tokens_per_s": round(kv_per_step / (Hkv * 2 * D * 2 * L) / (elapsed / args.steps), 1),
+        "roofline": {"bound": "hbm", "kernel": "paged_attn_decode call (partition kernel + merge kernel)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_call_us": round(avg_dec_ms * 1e3, 2), "bytes_per_call": int(avg_dec_bytes)},
+        "cpu_baseline": cpu,
+        "parity_sample": parity,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(args, pkv, w, pool, bm, q, out, ws, d_tab, d_ctx, scale, P, stream):
+    """Time the fp64 oracle on a bounded sample (layer 0, as many sequences as
+    fit the time budget) and check the GPU's layer-0 output on that sample."""
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention, layout
+
+    S, Hq, Hkv, D, B, W = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.table_width
+    layer = 0
+    pkv.paged_attn_decode(out, q[layer], pool, layer, d_tab, d_ctx, scale, partition_size=P, workspace=ws,
+                          stream=stream)
+    torch.cuda.synchronize()
+    gpu_out = out.cpu().numpy()
+    tabs = d_tab.cpu().numpy()
+    ctxs = d_ctx.cpu().numpy()
+    qbits = q[layer].view(torch.int16).cpu().numpy().view(np.uint16)
+    k_off, v_off, _, _ = pool.region_offsets()
+    tile = pool.desc.tile_bytes
+    rng = np.random.default_rng(436)
+    order = rng.permutation(S)
+    spent, done, worst = 0.0, [], 0.0
+    for s in order:
+        n = int(ctxs[s])
+        nblk = math.ceil(n / B)
+        blocks = tabs[s, :nblk]
+        # copy this sequence's tiles of layer 0 to the host as a small pool
+        sub = layout.PoolShape(1, nblk, B, Hkv, D)
+        img = layout.empty_image(sub)
+        idx = torch.from_numpy(blocks.astype(np.int64)).to(pool.memory.device)
+        for region, dst in ((k_off, img.k), (v_off, img.v)):
+            lay = pool.memory[region: region + pool.desc.layer_bytes].view(w.num_blocks, Hkv * tile)
+            dst[:] = lay.index_select(0, idx).cpu().numpy().view(np.uint16).reshape(-1)
+        local = np.arange(nblk, dtype=np.int32)
+        t0 = time.perf_counter()
+        ref = attention.paged_decode(qbits[s:s + 1], img, 0, local[None, :], np.array([n]), scale)
+        spent += time.perf_counter() - t0
+        done.append(n)
+        worst = max(worst, float(np.max(np.abs(gpu_out[s] - ref[0]))))
+        if spent >= args.cpu_seconds:
+            break
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    bytes_done = sum(done) * Hkv * 2 * D * 2
+    cpu = {"value": round(bytes_done / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+           "kind": "oracle",
+           "sample": f"layer 0 of the same step, {len(done)} of {S} sequences ({sum(done)} tokens), "
+                     f"{spent:.1f} s of fp64 numpy decode (gather + softmax attention)",
+           "host_cpus": len(os.sched_getaffinity(0))}
+    parity = {"seqs_checked": len(done), "max_abs_err": worst, "bar": 1e-2}
+    log(f"cpu oracle: {cpu['value']} GB/s on {threads} threads; parity max abs err {worst:.2e}")
+    return cpu, parity
+
+
+if __name__ == "__main__":
+    main()

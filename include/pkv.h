@@ -1,0 +1,252 @@
+/*
+ * pkv.h - paged KV cache and paged decode attention for AMD MI355X (gfx950).
+ *
+ * A C ABI over plain pointers and sizes.  Device pointers are HIP device
+ * memory owned by the caller; the library never allocates or frees device
+ * memory and never synchronises a stream.  Every GPU call is asynchronous on
+ * the stream it is given (NULL = the default stream).  Host-side argument
+ * checks return PKV_ERR_INVALID / PKV_ERR_UNSUPPORTED and set a thread-local
+ * message readable with pkv_last_error(); nothing is launched then.
+ * Values that live in device memory (table entries, context lengths, slots,
+ * copy pairs) are not inspected on the host by the GPU calls; the kernels
+ * clamp table entries and skip out-of-range slots and pairs so that a bad
+ * value never reads or writes outside the pool, but the numbers they produce
+ * for such input are unspecified.  pkv_check_* validate host copies.
+ *
+ * What the library computes comes from three web pages on the KV cache:
+ *   [KVP]  "KV Cache 原理与 PagedAttention" (notebook.any.me.uk)
+ *   [BJD]  the bjdmk.com.cn article on KV-cache management (news/6246348)
+ *   [AWA]  aiworkagent.org, Transformer architecture, question 17
+ * Each declaration names the section it follows.
+ *
+ * ---------------------------------------------------------------------------
+ * Pool layout (this library's choice; the pages fix only the logical
+ * structure: fixed-size physical blocks in a preallocated pool, reached
+ * through per-sequence block tables - [KVP] §三 工作方式, [AWA]
+ * PagedAttention 的关键数据结构).
+ *
+ *   L = num_layers, NB = num_blocks, B = block_size, H = num_kv_heads,
+ *   D = head_dim, e = element bytes (2 for bf16, 1 for fp8-e5m2 and int8),
+ *   X = 16 / e (elements per 16-byte piece).
+ *
+ *   The pool is one caller-owned device buffer split into regions, each
+ *   starting at a multiple of 256 bytes from the base, in this order:
+ *     K        [L][NB][H][tile]      tile = B*D elements
+ *     V        [L][NB][H][tile]
+ *     K scales [L][NB][H][B] float   (int8 storage only)
+ *     V scales [L][NB][H][B] float   (int8 storage only)
+ *   Inside a K tile, element (token t, dim d) is at
+ *       ((d / X) * B + t) * X + d % X
+ *   i.e. the tile is D/X runs of B 16-byte pieces: the 16 bytes of dims
+ *   [X*c, X*c+X) of consecutive tokens are adjacent, so a wavefront reads a
+ *   whole 16-token block in fully contiguous 1 KB loads.
+ *   Inside a V tile, element (t, d) is at
+ *       ((t / 4) * D + d) * 4 + t % 4
+ *   i.e. groups of 4 consecutive tokens are stored dim by dim, so the
+ *   4 tokens x 1 dim operand of the P.V matrix-core step is one 4e-byte
+ *   word and 16 consecutive dims are one contiguous run.
+ *   A slot is block * B + t.  Requirements: D in {64, 128}; B in {16, 32}.
+ *
+ * Query, output: q is bf16 [S][Hq][D], out is fp32 [S][Hq][D], both dense.
+ * Block tables: int32 [S][W], row-major; entry i of row s is the physical
+ * block of logical block i of sequence s.  Only entries i < ceil(ctx_s / B)
+ * are read.  Context lengths: int32 [S], counting the token being decoded.
+ * GQA: query head h reads KV head h / (Hq / H) ([KVP] §一 GQA / MQA).
+ * ------------------------------------------------------------------------- */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = -1,        /* bad argument (message in pkv_last_error) */
+  PKV_ERR_UNSUPPORTED = -2,    /* valid but not built (e.g. head_dim 96)   */
+  PKV_ERR_OUT_OF_BLOCKS = -3,  /* block manager: pool exhausted, no change */
+  PKV_ERR_HIP = -4             /* a HIP runtime call failed                */
+} pkv_status;
+
+typedef enum {
+  PKV_KV_BF16 = 0,       /* K/V stored as bf16                               */
+  PKV_KV_FP8_E5M2 = 1,   /* OCP e5m2, one fp32 scale per tensor ([KVP] §四)  */
+  PKV_KV_INT8 = 2        /* symmetric int8, one fp32 scale per (token, head)
+                            for K and for V ([BJD] §5.2 量化粒度)             */
+} pkv_kv_dtype;
+
+typedef struct {
+  int32_t num_layers;
+  int32_t num_blocks;     /* physical blocks per layer                      */
+  int32_t block_size;     /* tokens per block, B                            */
+  int32_t num_kv_heads;   /* H                                              */
+  int32_t head_dim;       /* D                                              */
+  int32_t kv_dtype;       /* pkv_kv_dtype                                   */
+} pkv_pool_config;
+
+/* Filled by kv_pool_create; plain data, may be copied freely.  Pointers are
+ * device addresses inside the caller's buffer (scales NULL unless int8). */
+typedef struct {
+  pkv_pool_config cfg;
+  void* base;
+  uint64_t bytes;
+  void* k;
+  void* v;
+  float* k_scale;
+  float* v_scale;
+  uint64_t tile_bytes;    /* B * D * e                                       */
+  uint64_t layer_bytes;   /* NB * H * tile_bytes: one layer of K (or of V)   */
+} pkv_pool;
+
+/* fp8 per-tensor scales: stored = value / scale, value = stored * scale.
+ * Ignored for bf16 and int8 storage.  NULL means 1.0 and 1.0. */
+typedef struct {
+  float k_scale;
+  float v_scale;
+} pkv_kv_scales;
+
+/* Thread-local message for the last failed call on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* ------------------------------------------------------------- pool sizing */
+
+/* Bytes of device memory a pool with this configuration needs (regions and
+ * their 256-byte alignment included); 0 if the configuration is invalid.
+ * The K/V payload is 2 * L * NB * B * H * D * e bytes: the KV-size formula of
+ * [KVP] §一 显存占用公式 applied to NB*B token slots per layer. */
+uint64_t kv_pool_bytes(const pkv_pool_config* cfg);
+
+/* Largest num_blocks whose pool fits in budget_bytes (cfg->num_blocks is
+ * ignored); -1 if the rest of the configuration is invalid.  Sizing the pool
+ * from a memory budget follows [BJD] §7.2 显存容量估算 and the
+ * gpu-memory-utilization setting of [KVP] §四. */
+int64_t kv_pool_num_blocks_for_budget(const pkv_pool_config* cfg, uint64_t budget_bytes);
+
+/* Describe a pool living in dev_mem (device, >= kv_pool_bytes(cfg) bytes,
+ * 256-byte aligned).  Host only: records pointers, touches no memory. */
+pkv_status kv_pool_create(const pkv_pool_config* cfg, void* dev_mem, uint64_t bytes,
+                          pkv_pool* out);
+
+/* ------------------------------------------------------------- cache write */
+
+/* Write the K and V of num_tokens new tokens into their slots of one layer
+ * ([KVP] §一: each step computes only the newest token's K and V and appends
+ * them to the cache; §三 工作方式: the append goes to the slot the block table
+ * names).
+ *   key, value    device, bf16 [num_tokens][H][D]
+ *   slot_mapping  device, int64 [num_tokens]; slot = block * B + t; a
+ *                 negative slot (padding) or one >= NB*B writes nothing
+ *   scales        host; fp8: stored = e5m2_rne_sat(fp32(x / scale)); NULL=1
+ * int8 storage computes per (token, head): scale = fp32(absmax) / 127,
+ * code = clamp(rint_even(fp32(x / scale)), -127, 127) (0 if absmax is 0) and
+ * writes the scale beside the codes.  Two tokens with the same slot in one
+ * call race (pkv_check_slots rejects that). */
+pkv_status reshape_and_cache(const pkv_pool* pool, int32_t layer, const void* key,
+                             const void* value, const int64_t* slot_mapping,
+                             int32_t num_tokens, const pkv_kv_scales* scales,
+                             hipStream_t stream);
+
+/* Copy-on-write split: for each row (src, dst) of pairs (device, int64
+ * [num_pairs][2]) copy physical block src to dst in every layer - K tile, V
+ * tile and int8 scale rows - byte for byte ([BJD] §3.2 Copy-on-Write: the
+ * shared block is copied before the writer's table is repointed).  A pair
+ * with an index outside [0, NB) is skipped.  A dst that is also some pair's
+ * src, or repeated, races (pkv_check_pairs rejects that). */
+pkv_status copy_blocks(const pkv_pool* pool, const int64_t* pairs, int32_t num_pairs,
+                       hipStream_t stream);
+
+/* ------------------------------------------------------------- decode */
+
+/* Workspace bytes paged_attn_decode needs for these sizes (0 when
+ * partition_size is 0: the single-pass form needs none). */
+uint64_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                    int32_t table_width, int32_t block_size,
+                                    int32_t partition_size);
+
+/* Decode attention for one layer: for every sequence s and query head h,
+ *   out[s][h] = softmax(scale * q[s][h] . K_s^T) V_s
+ * over the ctx_s cached tokens of KV head h / G, gathered through the block
+ * table ([BJD] §2.1 for the formula; [KVP] §三 工作方式 step 4 for the gather;
+ * [KVP] §一 for the GQA grouping).  8-bit K/V are widened exactly to bf16 and
+ * their scales applied in fp32 before they meet q or p ([KVP] §四: dequantise
+ * before compute).  ctx_s == 0 gives a zero row.  Arithmetic: bf16 inputs,
+ * fp32 accumulation and softmax.  A stored inf or NaN in V gives a
+ * non-finite output element (inf may surface as NaN).
+ *   out           device fp32 [S][Hq][D]
+ *   q             device bf16 [S][Hq][D]
+ *   block_tables  device int32 [S][table_width]
+ *   context_lens  device int32 [S], each <= table_width * B
+ *   kv_dtype      must equal pool->cfg.kv_dtype
+ *   kv_scales     host; fp8 per-tensor scales (NULL = 1.0)
+ *   partition_size 0: one pass per (sequence, KV head).  Otherwise a
+ *                 multiple of 32: each partition of that many tokens is
+ *                 reduced separately and a second kernel merges them
+ *                 (needs workspace of paged_attn_workspace_bytes bytes,
+ *                 device, 256-byte aligned; its contents are scratch).
+ * Hq must be a multiple of H. */
+pkv_status paged_attn_decode(float* out, const void* q, const pkv_pool* pool, int32_t layer,
+                             const int32_t* block_tables, int32_t table_width,
+                             const int32_t* context_lens, int32_t num_seqs,
+                             int32_t num_q_heads, float scale, int32_t kv_dtype,
+                             const pkv_kv_scales* kv_scales, int32_t partition_size,
+                             void* workspace, uint64_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------- host checks
+ * Validators over HOST copies of device inputs, for callers that want to
+ * rule out racing or out-of-range values before a launch.  Return PKV_OK or
+ * PKV_ERR_INVALID with a message naming the first bad entry. */
+pkv_status pkv_check_slots(const int64_t* slots, int32_t n, int64_t num_slots);
+pkv_status pkv_check_pairs(const int64_t* pairs, int32_t n, int32_t num_blocks);
+pkv_status pkv_check_tables(const int32_t* tables, const int32_t* context_lens, int32_t num_seqs,
+                            int32_t table_width, int32_t block_size, int32_t num_blocks);
+
+/* ------------------------------------------------------------- block manager
+ * Host-only bookkeeping of the pool ([KVP] §三 工作方式 steps 1-3: blocks
+ * handed out on demand and reused; [AWA] KV Memory Pool; [BJD] §3.1-3.2
+ * sharing and copy-on-write).  Rules fixed by this library:
+ *  - free blocks form a FIFO; the caller gives the initial order (a
+ *    permutation of 0..NB-1, or NULL for 0..NB-1); allocation pops the front,
+ *    blocks whose count drops to 0 are pushed to the back in table order;
+ *  - a sequence of n tokens holds ceil(n / B) blocks;
+ *  - appending to a sequence of length n writes position n: if n % B == 0 a
+ *    new block is appended; else if the last block is shared (count > 1) a
+ *    new block dst is taken, (src, dst) is reported for copy_blocks, src's
+ *    count drops by one and dst replaces it in this table; the slot is
+ *    table[n / B] * B + n % B;
+ *  - a batch append handles sequences in the order given and is all or
+ *    nothing: if the pool cannot supply every block it needs, it returns
+ *    PKV_ERR_OUT_OF_BLOCKS, counts one failed allocation, changes nothing.
+ * Not thread-safe: one manager per thread, or external locking. */
+typedef struct pkv_bm pkv_bm;
+
+pkv_status kv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_order,
+                        pkv_bm** out);
+void kv_bm_destroy(pkv_bm* bm);
+/* New sequence holding ctx_len tokens (ceil(ctx_len / B) fresh blocks). */
+pkv_status kv_bm_add_seq(pkv_bm* bm, int32_t seq, int32_t ctx_len);
+/* child shares all of parent's blocks (counts + 1) and its length. */
+pkv_status kv_bm_fork(pkv_bm* bm, int32_t parent, int32_t child);
+/* Append one token to each of seqs[0..n) (host arrays).  slots: int64 [n]
+ * out; cow_pairs: int64 [n][2] out; *num_pairs: pairs written. */
+pkv_status kv_bm_append(pkv_bm* bm, const int32_t* seqs, int32_t n, int64_t* slots,
+                        int64_t* cow_pairs, int32_t* num_pairs);
+pkv_status kv_bm_free_seq(pkv_bm* bm, int32_t seq);
+/* Rows of tables (host int32 [n][width]) for seqs[0..n), padded with 0, and
+ * their lengths (context_lens may be NULL). */
+pkv_status kv_bm_block_tables(const pkv_bm* bm, const int32_t* seqs, int32_t n, int32_t* tables,
+                              int32_t width, int32_t* context_lens);
+/* used = blocks referenced by some table; total = NB ([KVP] §六 cache usage);
+ * failed_allocs = calls refused for lack of blocks ([KVP] §六 preemptions). */
+pkv_status kv_bm_stats(const pkv_bm* bm, int32_t* used, int32_t* total, int64_t* failed_allocs);
+/* Reference count of one block (for tests and leak checks). */
+int32_t kv_bm_ref_count(const pkv_bm* bm, int32_t block);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,241 @@
+// Host block manager: the bookkeeping side of paging.
+//
+// Physical blocks of a preallocated pool are handed to sequences on demand and
+// reused when sequences end ("KV Cache 原理与 PagedAttention", §三 工作方式
+// steps 1-3; aiworkagent.org Q17, KV Memory Pool).  Each sequence has a block
+// table mapping logical block i to a physical block.  Forked sequences share
+// their parent's blocks; the first write into a shared block copies it and
+// repoints the writer's table (bjdmk.com.cn article, §3.1 and §3.2
+// Copy-on-Write).  The tie-break rules that make tables, slots and copy pairs
+// unique are stated with the declarations in pkv.h.
+#include <deque>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "pkv_internal.h"
+
+struct pkv_bm {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::deque<int32_t> free_list;            // FIFO: pop front, push back
+  std::vector<int32_t> ref;                 // per physical block
+  struct Seq {
+    std::vector<int32_t> table;
+    int32_t len = 0;
+  };
+  std::unordered_map<int32_t, Seq> seqs;
+  int64_t failed_allocs = 0;
+
+  int32_t take() {
+    const int32_t b = free_list.front();
+    free_list.pop_front();
+    ref[(size_t)b] = 1;
+    return b;
+  }
+};
+
+using namespace pkv;
+
+extern "C" {
+
+pkv_status kv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_order,
+                        pkv_bm** out) {
+  if (!out) return fail(PKV_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  if (num_blocks <= 0 || block_size <= 0) return fail(PKV_ERR_INVALID, "num_blocks and block_size must be positive");
+  pkv_bm* bm = new (std::nothrow) pkv_bm;
+  if (!bm) return fail(PKV_ERR_INVALID, "out of host memory");
+  bm->num_blocks = num_blocks;
+  bm->block_size = block_size;
+  bm->ref.assign((size_t)num_blocks, 0);
+  if (initial_order) {
+    std::vector<uint8_t> seen((size_t)num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      const int32_t b = initial_order[i];
+      if (b < 0 || b >= num_blocks || seen[(size_t)b]) {
+        delete bm;
+        set_error("initial_order is not a permutation of 0..%d (entry %d = %d)", num_blocks - 1, i, b);
+        return PKV_ERR_INVALID;
+      }
+      seen[(size_t)b] = 1;
+      bm->free_list.push_back(b);
+    }
+  } else {
+    for (int32_t b = 0; b < num_blocks; ++b) bm->free_list.push_back(b);
+  }
+  *out = bm;
+  clear_error();
+  return PKV_OK;
+}
+
+void kv_bm_destroy(pkv_bm* bm) { delete bm; }
+
+pkv_status kv_bm_add_seq(pkv_bm* bm, int32_t seq, int32_t ctx_len) {
+  if (!bm) return fail(PKV_ERR_INVALID, "bm is NULL");
+  if (ctx_len < 0) return fail(PKV_ERR_INVALID, "ctx_len is negative");
+  if (bm->seqs.count(seq)) {
+    set_error("sequence %d already exists", seq);
+    return PKV_ERR_INVALID;
+  }
+  const int64_t need = ((int64_t)ctx_len + bm->block_size - 1) / bm->block_size;
+  if (need > (int64_t)bm->free_list.size()) {
+    bm->failed_allocs++;
+    set_error("sequence %d needs %lld blocks, %zu free", seq, (long long)need, bm->free_list.size());
+    return PKV_ERR_OUT_OF_BLOCKS;
+  }
+  pkv_bm::Seq s;
+  s.table.reserve((size_t)need);
+  for (int64_t i = 0; i < need; ++i) s.table.push_back(bm->take());
+  s.len = ctx_len;
+  bm->seqs.emplace(seq, std::move(s));
+  clear_error();
+  return PKV_OK;
+}
+
+pkv_status kv_bm_fork(pkv_bm* bm, int32_t parent, int32_t child) {
+  if (!bm) return fail(PKV_ERR_INVALID, "bm is NULL");
+  auto it = bm->seqs.find(parent);
+  if (it == bm->seqs.end()) {
+    set_error("parent %d does not exist", parent);
+    return PKV_ERR_INVALID;
+  }
+  if (bm->seqs.count(child)) {
+    set_error("child %d already exists", child);
+    return PKV_ERR_INVALID;
+  }
+  pkv_bm::Seq c = it->second;
+  for (int32_t b : c.table) bm->ref[(size_t)b]++;
+  bm->seqs.emplace(child, std::move(c));
+  clear_error();
+  return PKV_OK;
+}
+
+pkv_status kv_bm_append(pkv_bm* bm, const int32_t* seqs, int32_t n, int64_t* slots, int64_t* cow_pairs,
+                        int32_t* num_pairs) {
+  if (!bm) return fail(PKV_ERR_INVALID, "bm is NULL");
+  if (n < 0 || (n > 0 && (!seqs || !slots || !cow_pairs)) || !num_pairs)
+    return fail(PKV_ERR_INVALID, "bad append arguments");
+  *num_pairs = 0;
+  const int32_t B = bm->block_size;
+  std::vector<pkv_bm::Seq*> ptr((size_t)n);
+  {
+    std::unordered_map<int32_t, int32_t> dup;
+    for (int32_t i = 0; i < n; ++i) {
+      auto it = bm->seqs.find(seqs[i]);
+      if (it == bm->seqs.end()) {
+        set_error("sequence %d does not exist", seqs[i]);
+        return PKV_ERR_INVALID;
+      }
+      if (dup.count(seqs[i])) {
+        set_error("sequence %d appears twice in one append", seqs[i]);
+        return PKV_ERR_INVALID;
+      }
+      dup[seqs[i]] = i;
+      ptr[(size_t)i] = &it->second;
+    }
+  }
+  // dry run: fresh blocks the whole batch needs
+  int64_t need = 0;
+  std::unordered_map<int32_t, int32_t> ref_delta;
+  for (int32_t i = 0; i < n; ++i) {
+    const pkv_bm::Seq& s = *ptr[(size_t)i];
+    if (s.len % B == 0) {
+      ++need;
+    } else {
+      const int32_t last = s.table[(size_t)(s.len / B)];
+      auto d = ref_delta.find(last);
+      const int32_t delta = d == ref_delta.end() ? 0 : d->second;
+      if (bm->ref[(size_t)last] + delta > 1) {
+        ++need;
+        ref_delta[last] = delta - 1;
+      }
+    }
+  }
+  if (need > (int64_t)bm->free_list.size()) {
+    bm->failed_allocs++;
+    set_error("append needs %lld blocks, %zu free", (long long)need, bm->free_list.size());
+    return PKV_ERR_OUT_OF_BLOCKS;
+  }
+  int32_t np = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    pkv_bm::Seq& s = *ptr[(size_t)i];
+    const int32_t pos = s.len;
+    const size_t lb = (size_t)(pos / B);
+    if (pos % B == 0) {
+      s.table.push_back(bm->take());
+    } else {
+      const int32_t last = s.table[lb];
+      if (bm->ref[(size_t)last] > 1) {
+        const int32_t dst = bm->take();
+        bm->ref[(size_t)last]--;
+        s.table[lb] = dst;
+        cow_pairs[2 * np] = last;
+        cow_pairs[2 * np + 1] = dst;
+        ++np;
+      }
+    }
+    slots[i] = (int64_t)s.table[lb] * B + pos % B;
+    s.len = pos + 1;
+  }
+  *num_pairs = np;
+  clear_error();
+  return PKV_OK;
+}
+
+pkv_status kv_bm_free_seq(pkv_bm* bm, int32_t seq) {
+  if (!bm) return fail(PKV_ERR_INVALID, "bm is NULL");
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) {
+    set_error("sequence %d does not exist", seq);
+    return PKV_ERR_INVALID;
+  }
+  for (int32_t b : it->second.table) {
+    if (--bm->ref[(size_t)b] == 0) bm->free_list.push_back(b);
+  }
+  bm->seqs.erase(it);
+  clear_error();
+  return PKV_OK;
+}
+
+pkv_status kv_bm_block_tables(const pkv_bm* bm, const int32_t* seqs, int32_t n, int32_t* tables,
+                              int32_t width, int32_t* context_lens) {
+  if (!bm) return fail(PKV_ERR_INVALID, "bm is NULL");
+  if (n < 0 || width <= 0 || (n > 0 && (!seqs || !tables))) return fail(PKV_ERR_INVALID, "bad table arguments");
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end()) {
+      set_error("sequence %d does not exist", seqs[i]);
+      return PKV_ERR_INVALID;
+    }
+    if ((int64_t)it->second.table.size() > width) {
+      set_error("sequence %d holds %zu blocks, wider than %d", seqs[i], it->second.table.size(), width);
+      return PKV_ERR_INVALID;
+    }
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const pkv_bm::Seq& s = bm->seqs.find(seqs[i])->second;
+    int32_t* row = tables + (int64_t)i * width;
+    size_t j = 0;
+    for (; j < s.table.size(); ++j) row[j] = s.table[j];
+    for (; j < (size_t)width; ++j) row[j] = 0;
+    if (context_lens) context_lens[i] = s.len;
+  }
+  clear_error();
+  return PKV_OK;
+}
+
+pkv_status kv_bm_stats(const pkv_bm* bm, int32_t* used, int32_t* total, int64_t* failed_allocs) {
+  if (!bm) return fail(PKV_ERR_INVALID, "bm is NULL");
+  if (used) *used = bm->num_blocks - (int32_t)bm->free_list.size();
+  if (total) *total = bm->num_blocks;
+  if (failed_allocs) *failed_allocs = bm->failed_allocs;
+  return PKV_OK;
+}
+
+int32_t kv_bm_ref_count(const pkv_bm* bm, int32_t block) {
+  if (!bm || block < 0 || block >= bm->num_blocks) return -1;
+  return bm->ref[(size_t)block];
+}
+
+}  // extern "C"

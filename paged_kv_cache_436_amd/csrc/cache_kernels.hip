@@ -1,0 +1,225 @@
+// Cache write (reshape_and_cache) and copy-on-write block copy (copy_blocks)
+// for gfx950.
+//
+// reshape_and_cache puts the newest token's K and V into the slot its block
+// table names ("KV Cache 原理与 PagedAttention", §一 decode step: only K_t and
+// V_t are computed and appended; §三 工作方式 steps 2-3), quantising on the way
+// in for 8-bit storage (same page, §四; bjdmk.com.cn article, §5.2 per-token-
+// head scales).  copy_blocks copies a shared block before its writer is
+// repointed (bjdmk.com.cn article, §3.2 Copy-on-Write).
+#include <hip/hip_runtime.h>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ codecs
+// fp32 -> OCP e5m2, round to nearest even, finite overflow saturates to
+// +-57344, +-inf stays inf, NaN becomes 0x7F with the input's sign.
+__device__ __forceinline__ uint32_t encode_e5m2(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu | sign;
+  if (a == 0x7f800000u) return 0x7cu | sign;
+  if (a >= 0x38800000u) {  // |y| >= 2^-14: e5m2 normal range before rounding
+    // keep 2 of the 23 mantissa bits, ties to even; a carry bumps the exponent
+    const uint32_t r = (a + 0x000fffffu + ((a >> 21) & 1u)) >> 21;
+    uint32_t code = r - (112u << 2);  // rebias the exponent from 127 to 15
+    if (code > 0x7bu) code = 0x7bu;   // saturate
+    return code | sign;
+  }
+  // subnormal range: a multiple of 2^-16; 4 * 2^-16 is the smallest normal
+  const float n = __builtin_rintf(__uint_as_float(a) * 65536.0f);
+  return (uint32_t)n | sign;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// ------------------------------------------------------------------ kernels
+// One wavefront per (token, kv head).  Lane i handles dims i, i+64, ...
+// Tile offsets follow the documented layout: K (t, d) at
+// ((d / X) * B + t) * X + d % X, V (t, d) at ((t / 4) * D + d) * 4 + t % 4.
+template <int KVT>
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
+    const int64_t* __restrict__ slots, int32_t num_tokens, int32_t H, int32_t D, int32_t B,
+    int64_t num_slots, void* __restrict__ kdst, void* __restrict__ vdst,
+    float* __restrict__ kscale, float* __restrict__ vscale, float k_scale, float v_scale) {
+  const int wave = (int)(blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  if (wave >= num_tokens * H) return;
+  const int n = wave / H;
+  const int h = wave % H;
+  const int64_t slot = slots[n];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / B;
+  const int t = (int)(slot % B);
+  const int64_t tile = (blk * H + h) * (int64_t)B * D;  // in elements
+  const uint16_t* kx = key + ((int64_t)n * H + h) * D;
+  const uint16_t* vx = value + ((int64_t)n * H + h) * D;
+
+  if constexpr (KVT == PKV_KV_BF16) {
+    uint16_t* kd = static_cast<uint16_t*>(kdst) + tile;
+    uint16_t* vd = static_cast<uint16_t*>(vdst) + tile;
+    for (int d = lane; d < D; d += kWave) {
+      kd[((d >> 3) * B + t) * 8 + (d & 7)] = kx[d];
+      vd[((t >> 2) * D + d) * 4 + (t & 3)] = vx[d];
+    }
+  } else if constexpr (KVT == PKV_KV_FP8_E5M2) {
+    uint8_t* kd = static_cast<uint8_t*>(kdst) + tile;
+    uint8_t* vd = static_cast<uint8_t*>(vdst) + tile;
+    for (int d = lane; d < D; d += kWave) {
+      const float yk = __fdiv_rn(bf16_bits_to_float(kx[d]), k_scale);
+      const float yv = __fdiv_rn(bf16_bits_to_float(vx[d]), v_scale);
+      kd[((d >> 4) * B + t) * 16 + (d & 15)] = (uint8_t)encode_e5m2(yk);
+      vd[((t >> 2) * D + d) * 4 + (t & 3)] = (uint8_t)encode_e5m2(yv);
+    }
+  } else {  // INT8, symmetric per (token, head)
+    int8_t* kd = static_cast<int8_t*>(kdst) + tile;
+    int8_t* vd = static_cast<int8_t*>(vdst) + tile;
+    float kmax = 0.f, vmax = 0.f;
+    for (int d = lane; d < D; d += kWave) {
+      kmax = fmaxf(kmax, fabsf(bf16_bits_to_float(kx[d])));
+      vmax = fmaxf(vmax, fabsf(bf16_bits_to_float(vx[d])));
+    }
+    kmax = wave_max(kmax);
+    vmax = wave_max(vmax);
+    const float ks = __fdiv_rn(kmax, 127.0f);
+    const float vs = __fdiv_rn(vmax, 127.0f);
+    for (int d = lane; d < D; d += kWave) {
+      float ck = 0.f, cv = 0.f;
+      if (ks > 0.f) ck = fminf(fmaxf(__builtin_rintf(__fdiv_rn(bf16_bits_to_float(kx[d]), ks)), -127.f), 127.f);
+      if (vs > 0.f) cv = fminf(fmaxf(__builtin_rintf(__fdiv_rn(bf16_bits_to_float(vx[d]), vs)), -127.f), 127.f);
+      kd[((d >> 4) * B + t) * 16 + (d & 15)] = (int8_t)(int)ck;
+      vd[((t >> 2) * D + d) * 4 + (t & 3)] = (int8_t)(int)cv;
+    }
+    if (lane == 0) {
+      const int64_t so = (blk * H + h) * (int64_t)B + t;
+      kscale[so] = ks;
+      vscale[so] = vs;
+    }
+  }
+}
+
+// One workgroup per (pair, layer, region).  A block of one layer is a single
+// contiguous run of H tiles in the K and in the V region (H * B floats in each
+// scale region), so the copy is a straight 16-byte-vector memcpy.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(
+    const int64_t* __restrict__ pairs, int32_t num_pairs, int32_t num_layers, int32_t num_blocks,
+    char* __restrict__ k, char* __restrict__ v, char* __restrict__ ks, char* __restrict__ vs,
+    uint64_t block_bytes, uint64_t scale_block_bytes) {
+  const int pi = blockIdx.x / num_layers;
+  const int layer = blockIdx.x % num_layers;
+  const int region = blockIdx.y;  // 0 K, 1 V, 2 K scales, 3 V scales
+  if (pi >= num_pairs) return;
+  const int64_t src = pairs[2 * pi], dst = pairs[2 * pi + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  char* base = region == 0 ? k : region == 1 ? v : region == 2 ? ks : vs;
+  const uint64_t bytes = region < 2 ? block_bytes : scale_block_bytes;
+  const uint64_t layer_off = (uint64_t)layer * num_blocks * bytes;
+  const uint4* s = reinterpret_cast<const uint4*>(base + layer_off + (uint64_t)src * bytes);
+  uint4* d = reinterpret_cast<uint4*>(base + layer_off + (uint64_t)dst * bytes);
+  const uint64_t n16 = bytes / 16;
+  for (uint64_t i = threadIdx.x; i < n16; i += blockDim.x) d[i] = s[i];
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" pkv_status reshape_and_cache(const pkv_pool* pool, int32_t layer, const void* key,
+                                        const void* value, const int64_t* slot_mapping,
+                                        int32_t num_tokens, const pkv_kv_scales* scales,
+                                        hipStream_t stream) {
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  const pkv_pool_config& c = pool->cfg;
+  if (layer < 0 || layer >= c.num_layers) {
+    set_error("layer %d outside [0, %d)", layer, c.num_layers);
+    return PKV_ERR_INVALID;
+  }
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID, "num_tokens is negative");
+  if (num_tokens == 0) { clear_error(); return PKV_OK; }
+  if (!key || !value || !slot_mapping) return fail(PKV_ERR_INVALID, "key, value and slot_mapping must be non-NULL");
+  float ksc = 1.f, vsc = 1.f;
+  if (scales && c.kv_dtype == PKV_KV_FP8_E5M2) {
+    ksc = scales->k_scale;
+    vsc = scales->v_scale;
+    if (!(ksc > 0.f) || !(vsc > 0.f)) return fail(PKV_ERR_INVALID, "fp8 scales must be positive");
+  }
+  const int64_t waves = (int64_t)num_tokens * c.num_kv_heads;
+  const int64_t grid = (waves + 3) / 4;
+  if (grid > INT32_MAX) return fail(PKV_ERR_INVALID, "too many tokens in one call");
+  char* kl = static_cast<char*>(pool->k) + (uint64_t)layer * pool->layer_bytes;
+  char* vl = static_cast<char*>(pool->v) + (uint64_t)layer * pool->layer_bytes;
+  const uint64_t scale_layer = (uint64_t)c.num_blocks * c.num_kv_heads * c.block_size;
+  float* ksl = pool->k_scale ? pool->k_scale + layer * scale_layer : nullptr;
+  float* vsl = pool->v_scale ? pool->v_scale + layer * scale_layer : nullptr;
+  const int64_t num_slots = (int64_t)c.num_blocks * c.block_size;
+  const auto* kx = static_cast<const uint16_t*>(key);
+  const auto* vx = static_cast<const uint16_t*>(value);
+  switch (c.kv_dtype) {
+    case PKV_KV_BF16:
+      hipLaunchKernelGGL(reshape_and_cache_kernel<PKV_KV_BF16>, dim3((uint32_t)grid), dim3(256), 0, stream,
+                         kx, vx, slot_mapping, num_tokens, c.num_kv_heads, c.head_dim, c.block_size,
+                         num_slots, kl, vl, ksl, vsl, ksc, vsc);
+      break;
+    case PKV_KV_FP8_E5M2:
+      hipLaunchKernelGGL(reshape_and_cache_kernel<PKV_KV_FP8_E5M2>, dim3((uint32_t)grid), dim3(256), 0,
+                         stream, kx, vx, slot_mapping, num_tokens, c.num_kv_heads, c.head_dim,
+                         c.block_size, num_slots, kl, vl, ksl, vsl, ksc, vsc);
+      break;
+    default:
+      hipLaunchKernelGGL(reshape_and_cache_kernel<PKV_KV_INT8>, dim3((uint32_t)grid), dim3(256), 0, stream,
+                         kx, vx, slot_mapping, num_tokens, c.num_kv_heads, c.head_dim, c.block_size,
+                         num_slots, kl, vl, ksl, vsl, ksc, vsc);
+      break;
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("reshape_and_cache launch failed: %s", hipGetErrorString(e));
+    return PKV_ERR_HIP;
+  }
+  clear_error();
+  return PKV_OK;
+}
+
+extern "C" pkv_status copy_blocks(const pkv_pool* pool, const int64_t* pairs, int32_t num_pairs,
+                                  hipStream_t stream) {
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  if (num_pairs < 0) return fail(PKV_ERR_INVALID, "num_pairs is negative");
+  if (num_pairs == 0) { clear_error(); return PKV_OK; }
+  if (!pairs) return fail(PKV_ERR_INVALID, "pairs is NULL");
+  const pkv_pool_config& c = pool->cfg;
+  const uint64_t block_bytes = (uint64_t)c.num_kv_heads * pool->tile_bytes;
+  const uint64_t scale_block_bytes = (uint64_t)c.num_kv_heads * c.block_size * sizeof(float);
+  if (block_bytes % 16 || scale_block_bytes % 16) return fail(PKV_ERR_UNSUPPORTED, "block bytes not a multiple of 16");
+  const int64_t gx = (int64_t)num_pairs * c.num_layers;
+  if (gx > INT32_MAX) return fail(PKV_ERR_INVALID, "too many pairs in one call");
+  const int regions = c.kv_dtype == PKV_KV_INT8 ? 4 : 2;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((uint32_t)gx, regions), dim3(256), 0, stream, pairs,
+                     num_pairs, c.num_layers, c.num_blocks, static_cast<char*>(pool->k),
+                     static_cast<char*>(pool->v), reinterpret_cast<char*>(pool->k_scale),
+                     reinterpret_cast<char*>(pool->v_scale), block_bytes, scale_block_bytes);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("copy_blocks launch failed: %s", hipGetErrorString(e));
+    return PKV_ERR_HIP;
+  }
+  clear_error();
+  return PKV_OK;
+}

@@ -1,0 +1,42 @@
+// Internal helpers shared by the library's translation units (not installed).
+#pragma once
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "pkv.h"
+
+namespace pkv {
+
+void set_error(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+void clear_error();
+
+inline pkv_status fail(pkv_status st, const char* msg) {
+  set_error("%s", msg);
+  return st;
+}
+
+inline int elem_bytes(int32_t kv_dtype) {
+  switch (kv_dtype) {
+    case PKV_KV_BF16: return 2;
+    case PKV_KV_FP8_E5M2: return 1;
+    case PKV_KV_INT8: return 1;
+    default: return 0;
+  }
+}
+
+constexpr uint64_t kRegionAlign = 256;
+inline uint64_t align_up(uint64_t n) { return (n + kRegionAlign - 1) / kRegionAlign * kRegionAlign; }
+
+// Region byte offsets of a pool; false if the configuration is invalid
+// (message set).
+struct Regions {
+  uint64_t k, v, ks, vs, total, kv_bytes, scale_bytes;
+};
+bool pool_regions(const pkv_pool_config* cfg, Regions* r);
+
+pkv_status check_pool(const pkv_pool* pool);
+
+}  // namespace pkv
