@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_436_amd.build` "
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python paged_kv_cache_436_amd/build.py` "
                       "(or __graft_entry__.build())")
 # torch ships its own HIP runtime.  Load it first so that libpkv's dependency
 # on libamdhip64.so.7 resolves to that same, already loaded runtime: two HIP

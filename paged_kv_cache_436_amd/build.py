@@ -1,6 +1,6 @@
 """Build libpkv.so in-tree for gfx950.
 
-    python -m paged_kv_cache_436_amd.build          # build (always recompiles)
+    python paged_kv_cache_436_amd/build.py          # build (always recompiles)
 
 HIP sources are compiled by hipcc for --offload-arch=gfx950 with packed-fp32
 instruction selection disabled; host-only C++ (pool description, block
