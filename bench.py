@@ -4,7 +4,7 @@ A step is the whole hot path over one batch: the host block manager appends
 one token to each of the 100 sequences (slots, any copy-on-write pairs,
 tables), the tables / lengths / slots are uploaded, then for each of the 80
 layers the new token's K/V is written into its slot and paged decode
-attention runs over every sequence's ~4K-token history (partition size 512).
+attention runs over every sequence's ~4K-token history (split-context form).
 
 Workload (synthetic, seeded): 80 layers, 64 query / 8 KV heads, head_dim 128,
 bf16, 16-token blocks, 100 sequences with contexts ~N(4096, 256) clipped to
@@ -17,7 +17,7 @@ HBM peak, a roofline entry for the decode kernels (HIP events around every
 decode call of the timed steps), and the fp64 CPU oracle timed on a bounded
 sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--partition 512]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--partition P]
 """
 
 from __future__ import annotations
@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--partition", type=int, default=512)
+    ap.add_argument("--partition", type=int, default=-1,
+                    help="split-context partition size in tokens (-1: the whole table span, one partition)")
     ap.add_argument("--layers", type=int, default=80,
                     help="layers per step (the workload has 80; fewer only for quick experiments)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
@@ -71,7 +72,7 @@ def main():
     w = workloads.llama70b(num_layers=80, extra_steps=steps_total)
     L = args.layers
     S, Hq, Hkv, D, B, W = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.table_width
-    P = args.partition
+    P = args.partition if args.partition > 0 else (W * B + 31) // 32 * 32
 
     # ---------------------------------------------------------------- state
     bm = pkv.BlockManager(w.num_blocks, B, w.block_order)
@@ -184,7 +185,7 @@ def main():
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(S / (elapsed / args.steps), 1),
         "seq_tokens_per_s": round(kv_per_step / (Hkv * 2 * D * 2 * L) / (elapsed / args.steps), 1),
-        "roofline": {"bound": "hbm", "kernel": "paged_attn_decode call (partition kernel + merge kernel)",
+        "roofline": {"bound": "hbm", "kernel": "pa_split_kernel (the one launch of a split-context paged_attn_decode call)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "avg_call_us": round(avg_dec_ms * 1e3, 2), "bytes_per_call": int(avg_dec_bytes)},

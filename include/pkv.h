@@ -161,8 +161,10 @@ pkv_status copy_blocks(const pkv_pool* pool, const int64_t* pairs, int32_t num_p
 
 /* ------------------------------------------------------------- decode */
 
-/* Workspace bytes paged_attn_decode needs for these sizes (0 when
- * partition_size is 0: the single-pass form needs none). */
+/* Workspace bytes paged_attn_decode needs for these sizes on the current
+ * device (0 when partition_size is 0: the single-pass form needs none).  The
+ * split form's grid is sized to the device's compute units, so a workspace
+ * sized on one device model may not fit another. */
 uint64_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                     int32_t table_width, int32_t block_size,
                                     int32_t partition_size);
@@ -182,11 +184,18 @@ uint64_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
  *   context_lens  device int32 [S], each <= table_width * B
  *   kv_dtype      must equal pool->cfg.kv_dtype
  *   kv_scales     host; fp8 per-tensor scales (NULL = 1.0)
- *   partition_size 0: one pass per (sequence, KV head).  Otherwise a
- *                 multiple of 32: each partition of that many tokens is
- *                 reduced separately and a second kernel merges them
- *                 (needs workspace of paged_attn_workspace_bytes bytes,
- *                 device, 256-byte aligned; its contents are scratch).
+ *   partition_size 0: single pass, one workgroup per (sequence, KV head), no
+ *                 workspace.  Otherwise the split-context form, a positive
+ *                 multiple of 32: the work of all sequences and heads is cut
+ *                 into equal ranges, one per wavefront of a grid sized to the
+ *                 GPU; each range yields one partial result per piece of
+ *                 context it covers, pieces never crossing a multiple of
+ *                 partition_size tokens, and the wavefront that completes a
+ *                 sequence's KV head merges its partials.  Needs a device
+ *                 workspace of paged_attn_workspace_bytes bytes, 256-byte
+ *                 aligned; its contents are scratch (no initialisation
+ *                 needed).  Calls sharing a workspace must not overlap in
+ *                 time (same stream, or ordered by events).
  * Hq must be a multiple of H. */
 pkv_status paged_attn_decode(float* out, const void* q, const pkv_pool* pool, int32_t layer,
                              const int32_t* block_tables, int32_t table_width,

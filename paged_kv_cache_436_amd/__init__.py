@@ -194,7 +194,8 @@ def paged_attn_decode(out, q, pool: Pool, layer: int, block_tables, context_lens
                       kv_dtype: int | None = None, k_scale: float = 1.0, v_scale: float = 1.0,
                       partition_size: int = 0, workspace=None, stream=None):
     """out: fp32 [S, Hq, D]; q: bf16 [S, Hq, D]; block_tables: int32 [S, W];
-    context_lens: int32 [S]; workspace: uint8 device tensor (split form)."""
+    context_lens: int32 [S]; workspace: uint8 device tensor for the split form
+    (partition_size > 0); its contents are scratch."""
     S, hq, _ = q.shape
     W = block_tables.shape[1]
     kvd = pool.cfg.kv_dtype if kv_dtype is None else kv_dtype

@@ -1,33 +1,43 @@
 // Paged decode attention for gfx950 (CDNA4).
 //
-// For each sequence s and query head h the kernel computes
+// For each sequence s and query head h the kernels compute
 //     out[s][h] = softmax(scale * q[s][h] . K^T) V
 // over the ctx_s cached tokens of KV head h / G (bjdmk.com.cn article, §2.1),
 // fetching each token's K/V through the sequence's block table ("KV Cache
 // 原理与 PagedAttention", §三 工作方式 step 4).  Query heads sharing a KV head
-// (same page, §一 GQA / MQA) are served by one workgroup so their K/V is read
-// from HBM once.  8-bit K/V is widened exactly to bf16 and its scale applied in
+// (same page, §一 GQA / MQA) are served together so their K/V is read from
+// HBM once.  8-bit K/V is widened exactly to bf16 and its scale applied in
 // fp32 before it meets q or p (same page, §四: dequantise before compute).
 //
-// Work decomposition
-//   workgroup  = (sequence, KV head, tile of <= 16 query heads, partition)
-//   wavefront  = every NW-th "step" of 32 consecutive tokens of the partition
-//   step       = two 16-token chunks; each chunk is one 16x16 matrix-core tile
-// Per step a wavefront
-//   1. loads the chunks' K tiles (1 KB contiguous per load instruction) and V
-//      tiles straight into matrix-core operand registers, one step ahead;
-//   2. computes logits[16 tokens][16 heads] per chunk with
-//      v_mfma_f32_16x16x32_bf16 (A = K rows, B = the query group);
-//   3. updates a running max / sum per head (online softmax, exp2 domain);
-//   4. accumulates acc^T[d][head] += V^T[d][32 tokens] . P[32 tokens][head]
-//      with 16x16x32 MFMAs per 16 dims (P split into bf16 hi and lo parts):
-//      the logits' register layout is exactly the B-operand layout of this
-//      product, so P needs no shuffle.
-// Waves then merge their (max, sum, acc) through LDS.  With one partition the
-// workgroup writes the normalised output; otherwise it writes the partition's
-// (max, sum, acc) and pa_reduce_kernel merges the partitions:
-//     out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
+// Matrix-core formulation, per 16-token chunk of one KV head:
+//   logits^T[16 tokens][16 heads] = K[16 tokens][D] . Q^T[D][16 heads]
+//       v_mfma_f32_16x16x32_bf16, A = K rows, B = the query group;
+//   acc^T[D][16 heads] += V^T[D][16 tokens] . P[16 tokens][16 heads]
+//       v_mfma_f32_16x16x16_bf16 (one chunk) or 16x16x32 (two chunks), with P
+//       split into bf16 hi and lo parts so the product carries ~16 bits of p.
+// The logits' accumulator layout is exactly the B-operand layout of the P.V
+// product, so P never moves between lanes.  The softmax is the streaming form
+// (running max and sum per head, exp2 domain).
+//
+// Two launch forms:
+//   partition_size == 0  pa_decode_kernel: one workgroup per (sequence, KV
+//       head, tile of <= 16 query heads); its four waves split the context and
+//       merge through LDS; it writes the output directly.
+//   partition_size  > 0  split-context: pa_split_kernel is a persistent grid
+//       sized to the GPU.  The work of all (sequence, KV head, head tile)
+//       rows is laid end to end as a list of fixed-size token steps and every
+//       wavefront takes one equal contiguous range of it, so all waves finish
+//       together whatever the context lengths.  A wave keeps NBUF-1 steps of
+//       K/V loads in flight, across row boundaries too.  It emits one partial
+//       (running max m, sum l, unnormalised acc) per segment: the part of its
+//       range inside one row and one partition of partition_size tokens.  The
+//       wave that completes a row combines the row's partials:
+//           out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k,  M = max m_k.
 #include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <chrono>
+#include <mutex>
 
 #include "pkv_internal.h"
 
@@ -36,30 +46,16 @@ namespace {
 
 constexpr int kWave = 64;
 constexpr int kNW = 4;            // wavefronts per workgroup
-constexpr int kStep = 32;         // tokens per step
+constexpr int kStep = 32;         // tokens per step of the single-pass kernel
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-struct DecodeParams {
-  const uint16_t* q;          // [S][Hq][D] bf16
-  float* out;                 // [S][Hq][D]          (single pass)
-  float* part_acc;            // [S][Hq][NP][D]      (split)
-  float* part_ml;             // [S][Hq][NP][2]      (split: max, sum)
-  const char* k;              // this layer's K region
-  const char* v;              // this layer's V region
-  const float* ks;            // this layer's K scales (int8) or null
-  const float* vs;            // this layer's V scales (int8) or null
-  const int32_t* bt;          // [S][W]
-  const int32_t* ctx;         // [S]
-  int32_t W, S, Hq, Hkv, G, QT, NP, P, num_blocks;
-  int32_t num_items;          // S * Hkv * QT * NP
-  float qk_scale;             // softmax scale * log2(e) (* fp8 k scale)
-  float out_scale;            // fp8 v scale, else 1
-};
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ u32x4 ld16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
 
@@ -82,7 +78,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Four bytes of w (byte i = token i) -> 4 bf16 in 2 dwords.
+// Four bytes of w (byte i = token or dim i) -> 4 bf16 in 2 dwords.
 template <int KVT>
 __device__ __forceinline__ void widen4(uint32_t w, uint32_t& lo, uint32_t& hi) {
   if constexpr (KVT == PKV_KV_FP8_E5M2) {
@@ -107,6 +103,71 @@ __device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
   return __builtin_bit_cast(bf16x8, u32x4{a, b, c, d});
 }
 
+// Wave-uniform read of memory that no kernel of this launch writes (block
+// tables, context lengths): through the constant address space it becomes a
+// scalar load, which does not occupy the vector-memory counter that the K/V
+// prefetch pipeline waits on.
+__device__ __forceinline__ int32_t uniform_load(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
+// Combine each lane's value with that of lane ^ 16 / lane ^ 32 (the other
+// token groups of the same head in the MFMA accumulator layout).  gfx950's
+// row / half swaps do this in the VALU, without an LDS round trip.
+__device__ __forceinline__ float max_x16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_x16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maximum).
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ int clamp_ctx(int c, int max_ctx) { return c < 0 ? 0 : (c > max_ctx ? max_ctx : c); }
+
+// Query dims held by lane slot j of q.K MFMA kk (the same dims the K operand
+// of that slot holds).
+template <int E>
+__device__ __forceinline__ int q_dim0(int kk, int j) {
+  return (E == 2) ? (32 * kk + 8 * j) : (64 * (kk >> 1) + 16 * j + 8 * (kk & 1));
+}
+
+// Output dim of accumulator element i of tile c in lane slot j:
+//   bf16: 32u + 8j + 2i + e  (c = 2u + e)   8-bit: 64u + 16j + 4i + e (c = 4u + e)
+template <int E>
+__device__ __forceinline__ int acc_dim(int c, int j, int i) {
+  return (E == 2) ? (32 * (c >> 1) + 8 * j + 2 * i + (c & 1)) : (64 * (c >> 2) + 16 * j + 4 * i + (c & 3));
+}
+
+// =====================================================================
+// Single-pass kernel (partition_size == 0)
+// =====================================================================
+struct DecodeParams {
+  const uint16_t* q;          // [S][Hq][D] bf16
+  float* out;                 // [S][Hq][D]
+  const char* k;              // this layer's K region
+  const char* v;              // this layer's V region
+  const float* ks;            // this layer's K scales (int8) or null
+  const float* vs;            // this layer's V scales (int8) or null
+  const int32_t* bt;          // [S][W]
+  const int32_t* ctx;         // [S]
+  int32_t W, S, Hq, Hkv, G, QT, num_blocks;
+  int32_t num_items;          // S * Hkv * QT
+  float qk_scale;             // softmax scale * log2(e) (* fp8 k scale)
+  float out_scale;            // fp8 v scale, else 1
+};
+
 template <int D, int KVT>
 struct Tile {
   static constexpr int E = KVT == PKV_KV_BF16 ? 2 : 1;        // bytes per element
@@ -127,7 +188,7 @@ struct StepRegs {
 
 template <int D, int KVT, int B>
 __device__ __forceinline__ void issue_step(StepRegs<D, KVT>& r, const DecodeParams& p, const int32_t* bt_row,
-                                           int g, int tok0, int ctx_lim, int lane) {
+                                           int g, int tok0, int lane) {
   using T = Tile<D, KVT>;
   constexpr int E = T::E;
   const int row = lane & 15;
@@ -159,7 +220,6 @@ __device__ __forceinline__ void issue_step(StepRegs<D, KVT>& r, const DecodePara
       r.vsc[h] = *reinterpret_cast<const f32x4*>(p.vs + so);
     }
   }
-  (void)ctx_lim;
 }
 
 template <int D, int KVT, int B>
@@ -169,17 +229,15 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
   __shared__ float sm_ml[kNW][2][16];
   __shared__ float sm_acc[kNW][16][D + 4];
 
-  // ---- which item: XCD-aware order so that consecutive items (partitions of
-  // one sequence and KV head) run on the same XCD
+  // XCD-aware order: consecutive items run on the same XCD
   const int nwg = (int)gridDim.x;
   const int xcd = (int)blockIdx.x % 8;
   const int per_xcd = (nwg + 7) / 8;
   const int item = xcd * per_xcd + (int)blockIdx.x / 8;
   if (item >= p.num_items) return;
-  const int part = item % p.NP;
-  const int qt = (item / p.NP) % p.QT;
-  const int g = (item / (p.NP * p.QT)) % p.Hkv;
-  const int s = item / (p.NP * p.QT * p.Hkv);
+  const int qt = item % p.QT;
+  const int g = (item / p.QT) % p.Hkv;
+  const int s = item / (p.QT * p.Hkv);
 
   const int lane = threadIdx.x % kWave;
   const int w = threadIdx.x / kWave;
@@ -188,30 +246,23 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
   const int gt = min(16, p.G - qt * 16);           // query heads in this tile
   const int h0 = g * p.G + qt * 16;                // first query head of the tile
 
-  int ctx = p.ctx[s];
-  ctx = ctx < 0 ? 0 : (ctx > p.W * B ? p.W * B : ctx);
-  const int t_begin = p.P > 0 ? part * p.P : 0;
-  const int t_end = p.P > 0 ? min(t_begin + p.P, ctx) : ctx;
-  if (t_begin >= t_end) {
-    if (p.P == 0) {  // empty context: zero output rows
-      for (int i = threadIdx.x; i < gt * D; i += blockDim.x)
-        p.out[((int64_t)s * p.Hq + h0 + i / D) * D + i % D] = 0.f;
-    }
-    return;  // split: the reduce kernel ignores partitions past ctx
+  const int t_end = clamp_ctx(p.ctx[s], p.W * B);
+  if (t_end == 0) {  // empty context: zero output rows
+    for (int i = threadIdx.x; i < gt * D; i += blockDim.x)
+      p.out[((int64_t)s * p.Hq + h0 + i / D) * D + i % D] = 0.f;
+    return;
   }
-  const int nsteps = (t_end - t_begin + kStep - 1) / kStep;
+  const int nsteps = (t_end + kStep - 1) / kStep;
   const int32_t* bt_row = p.bt + (int64_t)s * p.W;
 
-  // ---- query tile as the B operand of q.K: lane (j, row) holds head row,
-  // dims d0(kk, j) .. +7 (the same dims the K operand of that lane slot holds)
+  // query tile as the B operand of q.K: lane (j, row) holds head row
   bf16x8 qop[T::KK];
   {
     const bool valid = row < gt;
     const uint16_t* qh = p.q + ((int64_t)s * p.Hq + h0 + (valid ? row : 0)) * D;
 #pragma unroll
     for (int kk = 0; kk < T::KK; ++kk) {
-      const int d0 = (E == 2) ? (32 * kk + 8 * j) : (64 * (kk >> 1) + 16 * j + 8 * (kk & 1));
-      u32x4 raw = *reinterpret_cast<const u32x4*>(qh + d0);
+      u32x4 raw = *reinterpret_cast<const u32x4*>(qh + q_dim0<E>(kk, j));
       if (!valid) raw = u32x4{0, 0, 0, 0};
       qop[kk] = __builtin_bit_cast(bf16x8, raw);
     }
@@ -242,7 +293,6 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
       }
       z[h] = c;
     }
-    // scale, mask, max
     float mloc = -INFINITY;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -262,8 +312,6 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
     float psum = 0.f;
-    // p enters the P.V product as bf16 hi + lo parts (two MFMAs), so the
-    // product carries ~16 significant bits of p instead of 8
     uint32_t ph[2][2], pl[2][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -288,7 +336,6 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
     // zero V of masked tokens so that garbage (NaN/inf bit patterns in unwritten
     // slots) cannot reach the accumulator through 0 * NaN
     const bool tail = tok0 + kStep > t_end;
-    // P.V: A = V^T[d][tokens], slots 0..3 = chunk 0 tokens 4j..4j+3, 4..7 = chunk 1
 #pragma unroll
     for (int c = 0; c < T::NC; ++c) {
       uint32_t a0, a1, a2, a3;
@@ -317,40 +364,33 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
     }
   };
 
-  // ---- main loop: wave w takes steps w, w+NW, ...; loads run one step ahead
+  // wave w takes steps w, w+NW, ...; loads run one step ahead
   StepRegs<D, KVT> r0, r1;
   int i = w;
-  if (i < nsteps) issue_step<D, KVT, B>(r0, p, bt_row, g, t_begin + i * kStep, t_end, lane);
+  if (i < nsteps) issue_step<D, KVT, B>(r0, p, bt_row, g, i * kStep, lane);
   while (i < nsteps) {
     int nx = i + kNW;
-    if (nx < nsteps) issue_step<D, KVT, B>(r1, p, bt_row, g, t_begin + nx * kStep, t_end, lane);
-    compute(r0, t_begin + i * kStep);
+    if (nx < nsteps) issue_step<D, KVT, B>(r1, p, bt_row, g, nx * kStep, lane);
+    compute(r0, i * kStep);
     i = nx;
     if (i >= nsteps) break;
     nx = i + kNW;
-    if (nx < nsteps) issue_step<D, KVT, B>(r0, p, bt_row, g, t_begin + nx * kStep, t_end, lane);
-    compute(r1, t_begin + i * kStep);
+    if (nx < nsteps) issue_step<D, KVT, B>(r0, p, bt_row, g, nx * kStep, lane);
+    compute(r1, i * kStep);
     i = nx;
   }
 
-  // ---- merge the waves: per head max, sum and accumulator through LDS
+  // merge the waves: per head max, sum and accumulator through LDS
   l_run += __shfl_xor(l_run, 16, kWave);
   l_run += __shfl_xor(l_run, 32, kWave);
   if (j == 0) {
     sm_ml[w][0][row] = m_run;
     sm_ml[w][1][row] = l_run;
   }
-  // acc^T rows: lane (j, row) holds head `row`, dims
-  //   bf16: 32u + 8j + 2i + e  (c = 2u + e)    8-bit: 64u + 16j + 4i + e (c = 4u + e)
 #pragma unroll
   for (int c = 0; c < T::NC; ++c) {
 #pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) {
-      int d;
-      if constexpr (E == 2) d = 32 * (c >> 1) + 8 * j + 2 * i2 + (c & 1);
-      else d = 64 * (c >> 2) + 16 * j + 4 * i2 + (c & 3);
-      sm_acc[w][row][d] = acc[c][i2];
-    }
+    for (int i2 = 0; i2 < 4; ++i2) sm_acc[w][row][acc_dim<E>(c, j, i2)] = acc[c][i2];
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < gt * D; idx += blockDim.x) {
@@ -367,70 +407,762 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
       L += f * sm_ml[ww][1][hh];
       A += f * sm_acc[ww][hh][d];
     }
-    const int64_t sh = (int64_t)s * p.Hq + h0 + hh;
-    if (p.P == 0) {
-      p.out[sh * D + d] = A / L * p.out_scale;
-    } else {
-      p.part_acc[(sh * p.NP + part) * D + d] = A;
-      if (d == 0) {
-        p.part_ml[(sh * p.NP + part) * 2 + 0] = M;
-        p.part_ml[(sh * p.NP + part) * 2 + 1] = L;
-      }
+    p.out[((int64_t)s * p.Hq + h0 + hh) * D + d] = A / L * p.out_scale;
+  }
+}
+
+// =====================================================================
+// Split-context persistent kernel (partition_size > 0)
+// =====================================================================
+// A "row" x = (sequence s, KV head g, head tile qt), numbered
+// x = s * HQ + xi with xi = g * QT + qt and HQ = Hkv * QT.  Row x has
+// n_s = ceil(ctx_s / TS) steps of TS tokens.  The flat step list is
+// row 0's steps, then row 1's, ...; row x starts at cum_s * HQ + xi * n_s where
+// cum_s = sum over s' < s of n_s'.  Wave w of NWV takes flat steps
+// [w * per, min((w + 1) * per, N)), per = ceil(N / NWV).
+// Partition p of row x covers its tokens [p * P, (p + 1) * P); unit
+// u = x * NP + p.  The segment of unit u computed by wave w is stored in
+// partial slot u + w: walking the (unit, wave) pairs in order raises u or w
+// (or both) at every step, so the sum is unique.
+// When a wave has computed its whole range it makes its partials visible
+// (device-scope release) and adds, for every row it touched, the number of
+// that row's steps it computed to the row's counter.  The wave whose addition
+// completes the row (the sum reaches n_s) merges all of the row's partials
+// into the output.  A counter is 64 bits: the call's epoch (a number the host
+// draws anew for every call) above the step count, updated by compare-and-
+// swap; a counter carrying any other epoch counts as zero, so the workspace
+// needs no clearing between calls, whatever sizes earlier calls had.
+struct SplitParams {
+  const uint16_t* q;          // [S][Hq][D] bf16
+  float* out;                 // [S][Hq][D]
+  const char* k;
+  const char* v;
+  const float* ks;
+  const float* vs;
+  const int32_t* bt;
+  const int32_t* ctx;
+  uint64_t* row_done;         // workspace: [rows] (epoch << 32) | steps reported
+  float* part_ml;             // workspace: [slots][16][2]  (m, l)
+  float* part_acc;            // workspace: [slots][NC][64 lanes][4]
+  int32_t W, S, Hq, Hkv, G, QT, HQ, num_blocks;
+  int32_t P;                  // partition size (tokens, multiple of 32)
+  int32_t NP;                 // partitions per row: ceil(W * B / P)
+  int32_t NWV;                // waves in the grid
+  uint32_t epoch;             // this call's tag for row_done
+  float qk_scale;
+  float out_scale;
+};
+
+template <int D, int KVT>
+struct SplitGeo {
+  static constexpr int E = KVT == PKV_KV_BF16 ? 2 : 1;
+  static constexpr int CH = E == 2 ? 1 : 2;       // 16-token chunks per step
+  static constexpr int TS = 16 * CH;              // tokens per step
+  static constexpr int LPC = D * E / 64;          // 16-byte loads per chunk per lane, for K and for V
+  static constexpr int KK = D / 32;               // q.K MFMAs per chunk
+  static constexpr int NC = D / 16;               // accumulator tiles of 16 dims
+};
+
+template <int D, int KVT>
+struct SplitBuf {
+  using G_ = SplitGeo<D, KVT>;
+  u32x4 k[G_::CH][G_::LPC];
+  u32x4 v[G_::CH][G_::LPC];
+  f32x4 ksc[G_::CH];
+  f32x4 vsc[G_::CH];
+};
+
+// Wave-uniform description of one issued step.
+struct StepMeta {
+  int t0;       // first token of the step within its row
+  int t_end;    // row's context length
+  int slot;     // partial slot of the step's segment
+  int flags;    // kNewRow | kQReady | kFlush
+  int qs, qh0;  // sequence and first head of the row (for a direct q load)
+};
+constexpr int kNewRow = 1;   // first step of a row in this wave: load the row's q
+constexpr int kQReady = 2;   // ... and that q was prefetched into qnext
+constexpr int kFlush = 4;    // last step of a segment: write the partial
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// The query group of one row as the B operand of q.K: lane (j, row) holds
+// head row of the tile.
+template <int KK>
+struct QRegs {
+  bf16x8 q[KK];
+};
+
+template <int D, int KVT>
+__device__ __forceinline__ QRegs<SplitGeo<D, KVT>::KK> load_q(const SplitParams& p, int s, int h0, int gt,
+                                                               int lane) {
+  using GE = SplitGeo<D, KVT>;
+  const int row = lane & 15;
+  const int j = lane >> 4;
+  // rows past the tile's heads read a valid head; their columns are never stored
+  const uint16_t* qh = p.q + ((int64_t)s * p.Hq + h0 + (row < gt ? row : 0)) * D;
+  QRegs<GE::KK> r;
+#pragma unroll
+  for (int kk = 0; kk < GE::KK; ++kk)
+    r.q[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + q_dim0<GE::E>(kk, j)));
+  return r;
+}
+
+// Load the K/V (and int8 scales) of one step.  A chunk at or past t_end -
+// the tail of a row, or any chunk of a step past the wave's range - reads the
+// tile of block 0, head 0 instead: it is masked or never consumed, and the
+// load keeps the number of loads per step fixed, which the compiler's
+// wait-count tracking needs to let later steps' loads stay in flight.
+template <int D, int KVT, int B>
+__device__ __forceinline__ void issue_chunks(SplitBuf<D, KVT>& r, const SplitParams& p, const int (&phys)[2],
+                                             int g, int t0, int t_end, int lane) {
+  using GE = SplitGeo<D, KVT>;
+  constexpr int E = GE::E;
+  const int row = lane & 15;
+  const int j = lane >> 4;
+#pragma unroll
+  for (int h = 0; h < GE::CH; ++h) {
+    const int t = t0 + 16 * h;
+    const bool live = t < t_end;                   // wave-uniform
+    const int toff = live ? t % B : 0;
+    const int64_t tile = live ? ((int64_t)phys[h] * p.Hkv + g) : 0;
+    const char* kt = p.k + tile * (int64_t)(B * D * E);
+    const char* vt = p.v + tile * (int64_t)(B * D * E);
+#pragma unroll
+    for (int u = 0; u < GE::LPC; ++u) r.k[h][u] = ld16(kt + ((4 * u + j) * B + toff + row) * 16);
+    const int grp = (toff >> 2) + j;
+#pragma unroll
+    for (int u = 0; u < GE::LPC; ++u) {
+      const int d = (E == 2) ? (32 * u + 2 * row) : (64 * u + 4 * row);
+      r.v[h][u] = ld16(vt + (grp * D + d) * 4 * E);
+    }
+    if constexpr (KVT == PKV_KV_INT8) {
+      const int64_t so = tile * B + toff + 4 * j;
+      r.ksc[h] = *reinterpret_cast<const f32x4*>(p.ks + so);
+      r.vsc[h] = *reinterpret_cast<const f32x4*>(p.vs + so);
     }
   }
 }
 
-// One workgroup of D threads per (sequence, query head): merge the partitions.
-template <int D>
-__global__ __launch_bounds__(D) void pa_reduce_kernel(float* __restrict__ out, const float* __restrict__ part_acc,
-                                                      const float* __restrict__ part_ml,
-                                                      const int32_t* __restrict__ ctx_lens, int32_t Hq,
-                                                      int32_t NP, int32_t P, int32_t max_ctx, float out_scale) {
-  const int sh = blockIdx.x;
-  const int s = sh / Hq;
-  const int d = threadIdx.x;
-  int ctx = ctx_lens[s];
-  ctx = ctx < 0 ? 0 : (ctx > max_ctx ? max_ctx : ctx);
-  const int np = (ctx + P - 1) / P;
-  if (np == 0) {
-    out[(int64_t)sh * D + d] = 0.f;
-    return;
-  }
-  const float* ml = part_ml + (int64_t)sh * NP * 2;
-  float M = -INFINITY;
-  for (int k = 0; k < np; ++k) M = fmaxf(M, ml[2 * k]);
-  float L = 0.f, A = 0.f;
-  const float* pa = part_acc + (int64_t)sh * NP * D + d;
-  for (int k = 0; k < np; ++k) {
-    const float f = __builtin_amdgcn_exp2f(ml[2 * k] - M);
-    L += f * ml[2 * k + 1];
-    A += f * pa[(int64_t)k * D];
-  }
-  out[(int64_t)sh * D + d] = A / L * out_scale;
+// Rescale threshold of the streaming softmax, in log2 units: the reference
+// max m_run is only raised when a logit exceeds it by more than this, so p
+// stays below 2^8 and the accumulator is rescaled a handful of times per
+// segment instead of every step.  Any reference gives the same softmax.
+constexpr float kRescaleSlack = 8.0f;
+
+// Byte / half-word masks keeping the tokens of lane slot j that lie below
+// t_end: token t0 + 4j + i owns byte i (8-bit) or half-word i (bf16 pairs).
+__device__ __forceinline__ uint32_t tok_mask8(int tb, int t_end) {
+  return (tb + 0 < t_end ? 0x000000ffu : 0u) | (tb + 1 < t_end ? 0x0000ff00u : 0u) |
+         (tb + 2 < t_end ? 0x00ff0000u : 0u) | (tb + 3 < t_end ? 0xff000000u : 0u);
+}
+__device__ __forceinline__ uint32_t tok_mask16(int tb, int t_end) {
+  return (tb < t_end ? 0x0000ffffu : 0u) | (tb + 1 < t_end ? 0xffff0000u : 0u);
 }
 
+// Online-softmax update of (m_run, l_run, acc) with one step.
+template <int D, int KVT>
+__device__ __forceinline__ void compute_step(const SplitBuf<D, KVT>& r, const QRegs<SplitGeo<D, KVT>::KK>& qop,
+                                             const SplitParams& p, int t0, int t_end, int lane, float& m_run,
+                                             float& l_run, f32x4* acc) {
+  using GE = SplitGeo<D, KVT>;
+  constexpr int E = GE::E;
+  constexpr int CH = GE::CH;
+  const int j = lane >> 4;
+  f32x4 z[CH];
+#pragma unroll
+  for (int h = 0; h < CH; ++h) {
+    f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < GE::KK; ++kk) {
+      bf16x8 a;
+      if constexpr (E == 2) {
+        a = __builtin_bit_cast(bf16x8, r.k[h][kk]);
+      } else {
+        const u32x4 wv = r.k[h][kk >> 1];
+        a = (kk & 1) ? widen8<KVT>(wv[2], wv[3]) : widen8<KVT>(wv[0], wv[1]);
+      }
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop.q[kk], c, 0, 0, 0);
+    }
+    z[h] = c;
+  }
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int h = 0; h < CH; ++h) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 16 * h + 4 * j + i;
+      float zz = z[h][i] * p.qk_scale;
+      if constexpr (KVT == PKV_KV_INT8) zz *= r.ksc[h][i];
+      zz = t < t_end ? zz : -INFINITY;
+      z[h][i] = zz;
+      mloc = fmaxf(mloc, zz);
+    }
+  }
+  mloc = max_x32(max_x16(mloc));              // finite: token t0 < t_end is in every step
+  const bool bump = mloc > m_run + kRescaleSlack;   // always true on a segment's first step
+  const float m_ref = bump ? mloc : m_run;
+  const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - m_ref) : 1.0f;
+  // the accumulator is zero until the first step has run, so only a raise of a
+  // finite reference needs the rescale (wave-uniform branch)
+  if (__builtin_amdgcn_ballot_w64(bump && m_run > -INFINITY)) {
+#pragma unroll
+    for (int c = 0; c < GE::NC; ++c) acc[c] = acc[c] * alpha;
+  }
+  m_run = m_ref;
+  float psum = 0.f;
+  uint32_t ph[CH][2], pl[CH][2];
+#pragma unroll
+  for (int h = 0; h < CH; ++h) {
+    float pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = __builtin_amdgcn_exp2f(z[h][i] - m_ref);
+      psum += pv[i];
+      if constexpr (KVT == PKV_KV_INT8) {
+        const int t = t0 + 16 * h + 4 * j + i;
+        pv[i] = t < t_end ? pv[i] * r.vsc[h][i] : 0.f;   // fold the V scale into p
+      }
+    }
+    ph[h][0] = pack_bf16x2(pv[0], pv[1]);
+    ph[h][1] = pack_bf16x2(pv[2], pv[3]);
+    pl[h][0] = pack_bf16x2(pv[0] - bf16_lo(ph[h][0]), pv[1] - bf16_hi(ph[h][0]));
+    pl[h][1] = pack_bf16x2(pv[2] - bf16_lo(ph[h][1]), pv[3] - bf16_hi(ph[h][1]));
+  }
+  l_run = l_run * alpha + psum;
+  // V of tokens at or past t_end is zeroed so that unwritten slots (any bit
+  // pattern) cannot reach the accumulator through 0 * NaN (wave-uniform branch)
+  u32x4 v[CH][GE::LPC];
+#pragma unroll
+  for (int h = 0; h < CH; ++h)
+#pragma unroll
+    for (int u = 0; u < GE::LPC; ++u) v[h][u] = r.v[h][u];
+  if (t0 + GE::TS > t_end) {
+#pragma unroll
+    for (int h = 0; h < CH; ++h) {
+      const int tb = t0 + 16 * h + 4 * j;
+      if constexpr (E == 2) {
+        const u32x4 m = u32x4{tok_mask16(tb, t_end), tok_mask16(tb + 2, t_end), tok_mask16(tb, t_end),
+                              tok_mask16(tb + 2, t_end)};
+#pragma unroll
+        for (int u = 0; u < GE::LPC; ++u) v[h][u] &= m;
+      } else {
+        const uint32_t m = tok_mask8(tb, t_end);
+#pragma unroll
+        for (int u = 0; u < GE::LPC; ++u) v[h][u] &= u32x4{m, m, m, m};
+      }
+    }
+  }
+  if constexpr (CH == 1) {
+    const s16x4 pop = __builtin_bit_cast(s16x4, u32x2{ph[0][0], ph[0][1]});
+    const s16x4 pop_lo = __builtin_bit_cast(s16x4, u32x2{pl[0][0], pl[0][1]});
+#pragma unroll
+    for (int c = 0; c < GE::NC; ++c) {
+      const int u = c >> 1, e = c & 1;      // load u holds dims (32u + 2row, +1) x 4 tokens
+      const s16x4 aop = __builtin_bit_cast(s16x4, u32x2{v[0][u][2 * e], v[0][u][2 * e + 1]});
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, pop, acc[c], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, pop_lo, acc[c], 0, 0, 0);
+    }
+  } else {
+    const bf16x8 pop = __builtin_bit_cast(bf16x8, u32x4{ph[0][0], ph[0][1], ph[1][0], ph[1][1]});
+    const bf16x8 pop_lo = __builtin_bit_cast(bf16x8, u32x4{pl[0][0], pl[0][1], pl[1][0], pl[1][1]});
+#pragma unroll
+    for (int c = 0; c < GE::NC; ++c) {
+      uint32_t a0, a1, a2, a3;
+      const int u = c >> 2, e = c & 3;      // load u holds dims (64u + 4row .. +3) x 4 tokens
+      widen4<KVT>(v[0][u][e], a0, a1);
+      widen4<KVT>(v[1][u][e], a2, a3);
+      const bf16x8 aop = __builtin_bit_cast(bf16x8, u32x4{a0, a1, a2, a3});
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, pop, acc[c], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, pop_lo, acc[c], 0, 0, 0);
+    }
+  }
+}
+
+// Where the issue side of a wave stands in the flat step list.
+struct Cursor {
+  int s, xi, j;     // sequence, row within the sequence, step within the row
+  int n;            // steps of sequence s's rows
+  int ctx;          // context length of sequence s
+  int phys[2];      // table entries of the step at the cursor (prefetched)
+};
+
+template <int B, int TS>
+__device__ __forceinline__ void cursor_tables(Cursor& c, const SplitParams& p) {
+  const int32_t* row = p.bt + (int64_t)c.s * p.W;
+#pragma unroll
+  for (int h = 0; h < TS / 16; ++h) {
+    int lb = (c.j * TS + 16 * h) / B;
+    lb = lb < p.W ? lb : p.W - 1;                  // never index past the table row
+    int phys = uniform_load(row + lb);
+    c.phys[h] = phys < 0 ? 0 : (phys >= p.num_blocks ? p.num_blocks - 1 : phys);  // stay inside the pool
+  }
+}
+
+// Partials cross from the waves that write them to the wave that merges them,
+// which may sit on another XCD, whose L2 is not coherent with the writer's.
+// They are therefore stored and loaded as agent-scope relaxed atomics, which
+// go to the coherent level instead of a per-XCD L2; this avoids device-scope
+// fences, which write back or invalidate a whole L2 each time.
+__device__ __forceinline__ void st_agent(float* p, float a, float b) {
+  const unsigned long long v = (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x2 ld_agent(const float* p) {
+  const unsigned long long v =
+      __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return f32x2{__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32))};
+}
+
+// Add `mine` steps to an epoch-tagged row counter; returns the row's total
+// for this epoch after the addition.  A counter of another epoch (an earlier
+// call, or whatever the scratch memory held) restarts from zero.
+__device__ __forceinline__ int add_steps(uint64_t* ctr, uint32_t epoch, int mine) {
+  unsigned long long* c = reinterpret_cast<unsigned long long*>(ctr);
+  unsigned long long expect = 0;
+  while (true) {
+    const uint32_t base = (uint32_t)(expect >> 32) == epoch ? (uint32_t)expect : 0u;
+    const unsigned long long want = ((unsigned long long)epoch << 32) | (base + (uint32_t)mine);
+    unsigned long long prev = expect;
+    if (__hip_atomic_compare_exchange_strong(c, &prev, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return (int)(base + (uint32_t)mine);
+    expect = prev;
+  }
+}
+
+// Merge the partials of row x into the output rows of its query heads.
+// Wave-cooperative, in the accumulator lane layout; loads go out four slots
+// at a time so that their latencies overlap.
+template <int D, int E>
+__device__ __forceinline__ void merge_row(const SplitParams& p, int x, int s, int xi, int ns, int sx, int per,
+                                          int TS, int lane) {
+  constexpr int NC = D / 16;
+  const int g = xi / p.QT;
+  const int qt = xi - g * p.QT;
+  const int row = lane & 15;
+  const int j = lane >> 4;
+  const int gt = min(16, p.G - qt * 16);
+  const int h0 = g * p.G + qt * 16;
+  const int PS = p.P / TS;                        // steps per partition
+  const int np = (ns + PS - 1) / PS;
+  float M = -INFINITY, L = 0.f;
+  f32x4 A[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) A[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // slots in order: partitions pp, and for each the waves wv covering it
+  int pp = 0;
+  int wv = sx / per;
+  while (pp < np) {
+    int slot[4];
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (pp < np) {
+        slot[k] = x * p.NP + pp + wv;
+        ++cnt;
+        const int e = sx + min((pp + 1) * PS, ns);     // end of partition pp (flat steps)
+        if (++wv > (e - 1) / per) {
+          ++pp;
+          wv = (sx + pp * PS) / per;
+        }
+      } else {
+        slot[k] = slot[0];
+      }
+    }
+    f32x2 ml[4];
+    f32x4 a[4][NC];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      ml[k] = ld_agent(p.part_ml + ((int64_t)slot[k] * 16 + row) * 2);
+      const float* pa = p.part_acc + (int64_t)slot[k] * (NC * 256) + lane * 4;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const f32x2 lo = ld_agent(pa + c * 256);
+        const f32x2 hi = ld_agent(pa + c * 256 + 2);
+        a[k][c] = f32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (k < cnt) {
+        const float Mn = fmaxf(M, ml[k][0]);
+        const float fa = __builtin_amdgcn_exp2f(M - Mn);
+        const float fk = __builtin_amdgcn_exp2f(ml[k][0] - Mn);
+        L = L * fa + ml[k][1] * fk;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) A[c] = A[c] * fa + a[k][c] * fk;
+        M = Mn;
+      }
+    }
+  }
+  if (row < gt) {
+    float* orow = p.out + ((int64_t)s * p.Hq + h0 + row) * D;
+    const float inv = p.out_scale / L;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) orow[acc_dim<E>(c, j, i)] = A[c][i] * inv;
+  }
+}
+
+template <int D, int KVT, int B, int NBUF>
+__global__ __launch_bounds__(kWave * kNW) void pa_split_kernel(const SplitParams p) {
+  using GE = SplitGeo<D, KVT>;
+  constexpr int TS = GE::TS;
+  const int lane = threadIdx.x % kWave;
+  const int row = lane & 15;
+  const int j = lane >> 4;
+  // XCD-aware numbering: workgroup b runs on XCD b % 8; each XCD gets a
+  // contiguous run of wave ranges
+  const int nwg = (int)gridDim.x;                  // a multiple of 8
+  const int b = (int)blockIdx.x;
+  const int wg = (b % 8) * (nwg / 8) + b / 8;
+  // wave-uniform, and said so: everything derived from it stays in SGPRs
+  const int w = __builtin_amdgcn_readfirstlane(wg * kNW + (int)threadIdx.x / kWave);
+  const int max_ctx = p.W * B;
+
+  // ---- total steps N; wave 0 also zeroes the output of empty sequences
+  int total = 0;
+  for (int base = 0; base < p.S; base += kWave) {
+    const int s = base + lane;
+    const int n = s < p.S ? (clamp_ctx(p.ctx[s], max_ctx) + TS - 1) / TS : 0;
+    total += wave_sum(n);
+    if (w == 0) {
+      uint64_t empty = __ballot(s < p.S && n == 0);
+      while (empty) {
+        const int se = base + __builtin_ctzll(empty);
+        empty &= empty - 1;
+        float* o = p.out + (int64_t)se * p.Hq * D;
+        for (int i = lane * 4; i < p.Hq * D; i += kWave * 4)
+          *reinterpret_cast<f32x4*>(o + i) = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  }
+  const int N = __builtin_amdgcn_readfirstlane(total) * p.HQ;
+  if (N == 0) return;
+  const int per = (N + p.NWV - 1) / p.NWV;
+  const int start = w * per;
+  if (start >= N) return;
+  const int nsteps = min(per, N - start);
+
+  // ---- locate the first step: sequence s with cum_s * HQ <= start < cum_{s+1} * HQ
+  Cursor cur{};
+  int cum0 = 0;
+  {
+    int acc0 = 0;
+    for (int base = 0; base < p.S; base += kWave) {
+      const int s = base + lane;
+      const int c = s < p.S ? clamp_ctx(p.ctx[s], max_ctx) : 0;
+      const int n = (c + TS - 1) / TS;
+      const int incl = wave_incl_scan(n, lane);
+      const bool hit = (acc0 + incl - n) * p.HQ <= start && start < (acc0 + incl) * p.HQ;
+      const uint64_t m = __ballot(hit);
+      if (m) {
+        const int l = __builtin_ctzll(m);
+        cur.s = base + l;
+        cur.n = __shfl(n, l, kWave);
+        cur.ctx = __shfl(c, l, kWave);
+        cum0 = acc0 + __shfl(incl - n, l, kWave);
+        const int off = start - cum0 * p.HQ;
+        cur.xi = off / cur.n;
+        cur.j = off % cur.n;
+        break;
+      }
+      acc0 += __shfl(incl, kWave - 1, kWave);
+    }
+  }
+  cur.s = __builtin_amdgcn_readfirstlane(cur.s);
+  cur.n = __builtin_amdgcn_readfirstlane(cur.n);
+  cur.ctx = __builtin_amdgcn_readfirstlane(cur.ctx);
+  cur.xi = __builtin_amdgcn_readfirstlane(cur.xi);
+  cur.j = __builtin_amdgcn_readfirstlane(cur.j);
+  cum0 = __builtin_amdgcn_readfirstlane(cum0);
+  const Cursor first = cur;
+  cursor_tables<B, TS>(cur, p);
+
+  SplitBuf<D, KVT> buf[NBUF];
+  StepMeta meta[NBUF];
+  QRegs<GE::KK> qnext;
+  QRegs<GE::KK> qop;
+  int qowner = -1;          // index of the step whose q sits in qnext
+  int issued = 0;
+
+  // Issue the step at the cursor into buffer r, then advance the cursor.
+  // `done` = index of the oldest step not yet computed.  Past the end of the
+  // range the loads still happen (see issue_chunks) but nothing is consumed.
+  auto issue = [&](SplitBuf<D, KVT>& r, StepMeta& m, int done) {
+    const bool live = issued < nsteps;
+    const int g = cur.xi / p.QT;
+    const int qt = cur.xi - g * p.QT;
+    const int h0 = g * p.G + qt * 16;
+    const int gt = min(16, p.G - qt * 16);
+    const bool last = issued + 1 == nsteps;
+    const bool row_end = cur.j + 1 == cur.n;
+    const bool part_end = ((cur.j + 1) * TS) % p.P == 0;
+    m.t0 = cur.j * TS;
+    m.t_end = live ? cur.ctx : 0;
+    m.slot = (cur.s * p.HQ + cur.xi) * p.NP + (cur.j * TS) / p.P + w;
+    m.qs = cur.s;
+    m.qh0 = h0;
+    int f = (last || row_end || part_end) ? kFlush : 0;
+    if (live && (cur.j == 0 || issued == 0)) {
+      f |= kNewRow;
+      if (qowner < done) {       // qnext is free: prefetch this row's q
+        qnext = load_q<D, KVT>(p, cur.s, h0, gt, lane);
+        qowner = issued;
+        f |= kQReady;
+      }
+    }
+    m.flags = f;
+    issue_chunks<D, KVT, B>(r, p, cur.phys, g, m.t0, m.t_end, lane);
+    ++issued;
+    if (issued < nsteps) {     // advance to the next step and fetch its table entries
+      if (++cur.j == cur.n) {
+        cur.j = 0;
+        if (++cur.xi == p.HQ) {
+          cur.xi = 0;
+          do {
+            ++cur.s;
+            cur.ctx = clamp_ctx(uniform_load(p.ctx + cur.s), max_ctx);
+            cur.n = (cur.ctx + TS - 1) / TS;
+          } while (cur.n == 0);
+        }
+      }
+      cursor_tables<B, TS>(cur, p);
+    }
+  };
+
+  f32x4 acc[GE::NC];
+#pragma unroll
+  for (int c = 0; c < GE::NC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  auto consume = [&](const SplitBuf<D, KVT>& r, const StepMeta& m) {
+    if (m.flags & kNewRow) {
+      if (m.flags & kQReady) {
+        qop = qnext;
+      } else {
+        // two rows began within the prefetch window: load this one now, and
+        // wait here, so the compiler does not carry a pending load of unknown
+        // distance into the compute (which would make it drain every step)
+        const int gt = min(16, p.G - (m.qh0 % p.G));
+        qop = load_q<D, KVT>(p, m.qs, m.qh0, gt, lane);
+        wait_vm_all();
+      }
+    }
+    compute_step<D, KVT>(r, qop, p, m.t0, m.t_end, lane, m_run, l_run, acc);
+    if (m.flags & kFlush) {
+      const float l = sum_x32(sum_x16(l_run));
+      const int gt = min(16, p.G - (m.qh0 % p.G));
+      if (row < gt) {
+        float* pa = p.part_acc + (int64_t)m.slot * (GE::NC * 256) + lane * 4;
+#pragma unroll
+        for (int c = 0; c < GE::NC; ++c) {
+          st_agent(pa + c * 256, acc[c][0], acc[c][1]);
+          st_agent(pa + c * 256 + 2, acc[c][2], acc[c][3]);
+        }
+        if (j == 0) st_agent(p.part_ml + ((int64_t)m.slot * 16 + row) * 2, m_run, l);
+      }
+#pragma unroll
+      for (int c = 0; c < GE::NC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_run = -INFINITY;
+      l_run = 0.f;
+    }
+  };
+
+  // ---- pipeline: NBUF - 1 steps of loads in flight ahead of the one computed.
+  // Every step issues the same loads (live or not) so the wait before each
+  // compute only covers that step's loads.
+#pragma unroll
+  for (int bb = 0; bb < NBUF - 1; ++bb) issue(buf[bb], meta[bb], 0);
+  for (int base = 0; base < nsteps; base += NBUF) {
+#pragma unroll
+    for (int bb = 0; bb < NBUF; ++bb) {
+      const int idx = base + bb;
+      issue(buf[(bb + NBUF - 1) % NBUF], meta[(bb + NBUF - 1) % NBUF], idx);
+      if (idx < nsteps) consume(buf[bb], meta[bb]);
+    }
+  }
+
+  // ---- report the rows this range touched; the wave completing a row merges it
+  // this wave's partial stores have completed (and, being agent-scope, are
+  // visible to every XCD) before any counter below is raised
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  wait_vm_all();
+  int rs = first.s, rxi = first.xi, rn = first.n, rj = first.j, rcum = cum0;
+  int left = nsteps;
+  while (left > 0) {
+    const int mine = min(left, rn - rj);
+    const int x = rs * p.HQ + rxi;
+    int done_now = 0;
+    if (lane == 0) done_now = add_steps(p.row_done + x, p.epoch, mine);
+    done_now = __builtin_amdgcn_readfirstlane(done_now);
+    if (done_now == rn) {   // every partial of the row is in place
+      merge_row<D, GE::E>(p, x, rs, rxi, rn, rcum * p.HQ + rxi * rn, per, TS, lane);
+    }
+    left -= mine;
+    rj = 0;
+    if (left > 0 && ++rxi == p.HQ) {
+      rxi = 0;
+      rcum += rn;
+      do {
+        ++rs;
+        rn = (clamp_ctx(uniform_load(p.ctx + rs), max_ctx) + TS - 1) / TS;
+      } while (rn == 0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launches
 template <int D, int KVT, int B>
-hipError_t launch(const DecodeParams& p, int grid, hipStream_t stream) {
+hipError_t launch_single(const DecodeParams& p, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((pa_decode_kernel<D, KVT, B>), dim3(grid), dim3(kWave * kNW), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int KVT>
-hipError_t launch_b(const DecodeParams& p, int B, int grid, hipStream_t stream) {
-  return B == 16 ? launch<D, KVT, 16>(p, grid, stream) : launch<D, KVT, 32>(p, grid, stream);
-}
-
 template <int D>
-hipError_t launch_kv(const DecodeParams& p, int kvt, int B, int grid, hipStream_t stream) {
+hipError_t launch_single_kv(const DecodeParams& p, int kvt, int B, int grid, hipStream_t stream) {
   switch (kvt) {
-    case PKV_KV_BF16: return launch_b<D, PKV_KV_BF16>(p, B, grid, stream);
-    case PKV_KV_FP8_E5M2: return launch_b<D, PKV_KV_FP8_E5M2>(p, B, grid, stream);
-    default: return launch_b<D, PKV_KV_INT8>(p, B, grid, stream);
+    case PKV_KV_BF16:
+      return B == 16 ? launch_single<D, PKV_KV_BF16, 16>(p, grid, stream) : launch_single<D, PKV_KV_BF16, 32>(p, grid, stream);
+    case PKV_KV_FP8_E5M2:
+      return B == 16 ? launch_single<D, PKV_KV_FP8_E5M2, 16>(p, grid, stream)
+                     : launch_single<D, PKV_KV_FP8_E5M2, 32>(p, grid, stream);
+    default:
+      return B == 16 ? launch_single<D, PKV_KV_INT8, 16>(p, grid, stream) : launch_single<D, PKV_KV_INT8, 32>(p, grid, stream);
   }
 }
 
-uint64_t part_acc_bytes(int32_t S, int32_t Hq, int32_t D, int32_t NP) {
-  return align_up((uint64_t)S * Hq * NP * D * sizeof(float));
+constexpr int kNBuf = 4;                 // steps per wave: 1 computed + 3 in flight
+constexpr int kMaxBlocksPerCU = 2;       // persistent grid: at most this many workgroups per CU
+
+template <int D, int KVT, int B>
+const void* split_fn() {
+  return reinterpret_cast<const void*>(&pa_split_kernel<D, KVT, B, kNBuf>);
+}
+
+const void* split_kernel_fn(int D, int kvt, int B) {
+  if (D == 64) {
+    if (kvt == PKV_KV_BF16) return B == 16 ? split_fn<64, PKV_KV_BF16, 16>() : split_fn<64, PKV_KV_BF16, 32>();
+    if (kvt == PKV_KV_FP8_E5M2) return B == 16 ? split_fn<64, PKV_KV_FP8_E5M2, 16>() : split_fn<64, PKV_KV_FP8_E5M2, 32>();
+    return B == 16 ? split_fn<64, PKV_KV_INT8, 16>() : split_fn<64, PKV_KV_INT8, 32>();
+  }
+  if (kvt == PKV_KV_BF16) return B == 16 ? split_fn<128, PKV_KV_BF16, 16>() : split_fn<128, PKV_KV_BF16, 32>();
+  if (kvt == PKV_KV_FP8_E5M2) return B == 16 ? split_fn<128, PKV_KV_FP8_E5M2, 16>() : split_fn<128, PKV_KV_FP8_E5M2, 32>();
+  return B == 16 ? split_fn<128, PKV_KV_INT8, 16>() : split_fn<128, PKV_KV_INT8, 32>();
+}
+
+// Compute units of the current device (cached per device).
+int device_cus(int* cus) {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  std::lock_guard<std::mutex> lk(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
+    cache[dev] = n;
+  }
+  *cus = cache[dev];
+  return 0;
+}
+
+// Resident workgroups per CU of one split-kernel variant (cached).
+int split_blocks_per_cu(int D, int kvt, int B) {
+  static std::mutex mu;
+  static int cache[64][2][3][2] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  const int di = D == 64 ? 0 : 1, bi = B == 16 ? 0 : 1;
+  std::lock_guard<std::mutex> lk(mu);
+  int& c = cache[dev][di][kvt][bi];
+  if (c == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, split_kernel_fn(D, kvt, B), kWave * kNW, 0) != hipSuccess)
+      n = 1;
+    c = n < 1 ? 1 : (n > kMaxBlocksPerCU ? kMaxBlocksPerCU : n);
+  }
+  return c;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// A fresh tag per split-context call.  The sequence starts at a value drawn
+// from the clock and the address space, so stale counters left in reused
+// memory by another process are not mistaken for this call's.
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> counter{(uint32_t)(std::chrono::steady_clock::now().time_since_epoch().count() ^
+                                                  (uintptr_t)&counter ^ 0x9e3779b9u)};
+  return counter.fetch_add(1, std::memory_order_relaxed);
+}
+
+// Workgroups of the split kernel: one resident wave per SIMD slot the
+// variant can use, but never more waves than there are steps.
+int64_t split_grid(int64_t steps_ub, int cus, int blocks_per_cu) {
+  int64_t nwg = (int64_t)cus * blocks_per_cu;
+  nwg = std::min<int64_t>(nwg, ceil_div(steps_ub, kNW));
+  return std::max<int64_t>(8, ceil_div(nwg, 8) * 8);
+}
+
+struct SplitSizes {
+  int64_t rows, np, slots_cap, cnt_bytes, ml_bytes, acc_bytes;
+};
+
+// Workspace regions for the largest grid any variant may launch.
+bool split_sizes(int32_t S, int32_t Hq, int32_t Hkv_or_0, int32_t D, int32_t W, int32_t B, int32_t P,
+                 SplitSizes* z) {
+  int cus = 0;
+  if (device_cus(&cus) != 0) return false;
+  (void)Hkv_or_0;
+  // rows: at most S * Hq (one head per row when G == 1)
+  z->rows = (int64_t)S * Hq;
+  z->np = ceil_div((int64_t)W * B, P);
+  const int64_t steps_ub = z->rows * ceil_div((int64_t)W * B, 16);
+  const int64_t waves_cap = split_grid(steps_ub, cus, kMaxBlocksPerCU) * kNW;
+  z->slots_cap = z->rows * z->np + waves_cap;
+  z->cnt_bytes = align_up((uint64_t)z->rows * sizeof(uint64_t));
+  z->ml_bytes = align_up((uint64_t)z->slots_cap * 16 * 2 * sizeof(float));
+  z->acc_bytes = align_up((uint64_t)z->slots_cap * (D / 16) * 256 * sizeof(float));
+  return true;
+}
+
+template <int D, int KVT, int B>
+void launch_split_t(const SplitParams& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((pa_split_kernel<D, KVT, B, kNBuf>), dim3(grid), dim3(kWave * kNW), 0, stream, p);
+}
+
+template <int D>
+void launch_split_kv(const SplitParams& p, int kvt, int B, int grid, hipStream_t stream) {
+  switch (kvt) {
+    case PKV_KV_BF16:
+      if (B == 16) launch_split_t<D, PKV_KV_BF16, 16>(p, grid, stream);
+      else launch_split_t<D, PKV_KV_BF16, 32>(p, grid, stream);
+      break;
+    case PKV_KV_FP8_E5M2:
+      if (B == 16) launch_split_t<D, PKV_KV_FP8_E5M2, 16>(p, grid, stream);
+      else launch_split_t<D, PKV_KV_FP8_E5M2, 32>(p, grid, stream);
+      break;
+    default:
+      if (B == 16) launch_split_t<D, PKV_KV_INT8, 16>(p, grid, stream);
+      else launch_split_t<D, PKV_KV_INT8, 32>(p, grid, stream);
+      break;
+  }
 }
 
 }  // namespace
@@ -444,9 +1176,9 @@ extern "C" uint64_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_h
   if (partition_size <= 0 || num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || table_width <= 0 ||
       block_size <= 0)
     return 0;
-  const int64_t np = ((int64_t)table_width * block_size + partition_size - 1) / partition_size;
-  return part_acc_bytes(num_seqs, num_q_heads, head_dim, (int32_t)np) +
-         align_up((uint64_t)num_seqs * num_q_heads * np * 2 * sizeof(float));
+  SplitSizes z;
+  if (!split_sizes(num_seqs, num_q_heads, 0, head_dim, table_width, block_size, partition_size, &z)) return 0;
+  return (uint64_t)(z.cnt_bytes + z.ml_bytes + z.acc_bytes);
 }
 
 extern "C" pkv_status paged_attn_decode(float* out, const void* q, const pkv_pool* pool, int32_t layer,
@@ -484,7 +1216,6 @@ extern "C" pkv_status paged_attn_decode(float* out, const void* q, const pkv_poo
     set_error("block_size %d not built (16, 32)", c.block_size);
     return PKV_ERR_UNSUPPORTED;
   }
-  if (pool->layer_bytes > (uint64_t)INT64_MAX) return fail(PKV_ERR_INVALID, "pool too large");
   if (((uintptr_t)q) % 16 || ((uintptr_t)out) % 16) return fail(PKV_ERR_INVALID, "q and out must be 16-byte aligned");
   float ksc = 1.f, vsc = 1.f;
   if (kv_scales && c.kv_dtype == PKV_KV_FP8_E5M2) {
@@ -495,65 +1226,92 @@ extern "C" pkv_status paged_attn_decode(float* out, const void* q, const pkv_poo
   }
   const int32_t G = num_q_heads / c.num_kv_heads;
   const int32_t QT = (G + 15) / 16;
-  int32_t NP = 1;
-  if (partition_size != 0) {
-    if (partition_size < 0 || partition_size % kStep != 0) {
-      set_error("partition_size %d must be 0 or a positive multiple of %d", partition_size, kStep);
+  const int64_t rows = (int64_t)num_seqs * c.num_kv_heads * QT;
+  const uint64_t scale_layer = (uint64_t)c.num_blocks * c.num_kv_heads * c.block_size;
+  const char* kl = static_cast<const char*>(pool->k) + (uint64_t)layer * pool->layer_bytes;
+  const char* vl = static_cast<const char*>(pool->v) + (uint64_t)layer * pool->layer_bytes;
+  const float* ksl = pool->k_scale ? pool->k_scale + layer * scale_layer : nullptr;
+  const float* vsl = pool->v_scale ? pool->v_scale + layer * scale_layer : nullptr;
+
+  hipError_t e = hipSuccess;
+  if (partition_size == 0) {
+    const int64_t grid = (rows + 7) / 8 * 8;
+    if (grid > INT32_MAX) return fail(PKV_ERR_INVALID, "too many work items");
+    DecodeParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.out = out;
+    p.k = kl;
+    p.v = vl;
+    p.ks = ksl;
+    p.vs = vsl;
+    p.bt = block_tables;
+    p.ctx = context_lens;
+    p.W = table_width;
+    p.S = num_seqs;
+    p.Hq = num_q_heads;
+    p.Hkv = c.num_kv_heads;
+    p.G = G;
+    p.QT = QT;
+    p.num_blocks = c.num_blocks;
+    p.num_items = (int32_t)rows;
+    p.qk_scale = scale * kLog2e * ksc;
+    p.out_scale = vsc;
+    e = c.head_dim == 64 ? launch_single_kv<64>(p, c.kv_dtype, c.block_size, (int)grid, stream)
+                         : launch_single_kv<128>(p, c.kv_dtype, c.block_size, (int)grid, stream);
+  } else {
+    if (partition_size < 0 || partition_size % 32 != 0) {
+      set_error("partition_size %d must be 0 or a positive multiple of 32", partition_size);
       return PKV_ERR_INVALID;
     }
-    NP = (int32_t)(((int64_t)table_width * c.block_size + partition_size - 1) / partition_size);
-    const uint64_t need = paged_attn_workspace_bytes(num_seqs, num_q_heads, c.head_dim, table_width, c.block_size,
-                                                     partition_size);
+    const int TS = c.kv_dtype == PKV_KV_BF16 ? 16 : 32;
+    const int64_t steps_ub = rows * ceil_div((int64_t)table_width * c.block_size, TS);
+    const int64_t np = ceil_div((int64_t)table_width * c.block_size, partition_size);
+    if (steps_ub > INT32_MAX / 2 || rows * np > INT32_MAX / 4) return fail(PKV_ERR_INVALID, "problem too large for one call");
+    SplitSizes z;
+    if (!split_sizes(num_seqs, num_q_heads, c.num_kv_heads, c.head_dim, table_width, c.block_size, partition_size,
+                     &z))
+      return fail(PKV_ERR_HIP, "could not query the current device");
+    const uint64_t need = (uint64_t)(z.cnt_bytes + z.ml_bytes + z.acc_bytes);
     if (!workspace || workspace_bytes < need) {
       set_error("workspace of %llu bytes needed, got %llu", (unsigned long long)need,
                 (unsigned long long)workspace_bytes);
       return PKV_ERR_INVALID;
     }
     if (((uintptr_t)workspace) % 256) return fail(PKV_ERR_INVALID, "workspace must be 256-byte aligned");
-  }
-  const int64_t items = (int64_t)num_seqs * c.num_kv_heads * QT * NP;
-  const int64_t grid = (items + 7) / 8 * 8;
-  if (grid > INT32_MAX) return fail(PKV_ERR_INVALID, "too many work items");
-
-  DecodeParams p{};
-  p.q = static_cast<const uint16_t*>(q);
-  p.out = out;
-  if (partition_size != 0) {
-    p.part_acc = static_cast<float*>(workspace);
-    p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                         part_acc_bytes(num_seqs, num_q_heads, c.head_dim, NP));
-  }
-  p.k = static_cast<const char*>(pool->k) + (uint64_t)layer * pool->layer_bytes;
-  p.v = static_cast<const char*>(pool->v) + (uint64_t)layer * pool->layer_bytes;
-  const uint64_t scale_layer = (uint64_t)c.num_blocks * c.num_kv_heads * c.block_size;
-  p.ks = pool->k_scale ? pool->k_scale + layer * scale_layer : nullptr;
-  p.vs = pool->v_scale ? pool->v_scale + layer * scale_layer : nullptr;
-  p.bt = block_tables;
-  p.ctx = context_lens;
-  p.W = table_width;
-  p.S = num_seqs;
-  p.Hq = num_q_heads;
-  p.Hkv = c.num_kv_heads;
-  p.G = G;
-  p.QT = QT;
-  p.NP = NP;
-  p.P = partition_size;
-  p.num_blocks = c.num_blocks;
-  p.num_items = (int32_t)items;
-  p.qk_scale = scale * kLog2e * ksc;
-  p.out_scale = vsc;
-
-  hipError_t e = c.head_dim == 64 ? launch_kv<64>(p, c.kv_dtype, c.block_size, (int)grid, stream)
-                                  : launch_kv<128>(p, c.kv_dtype, c.block_size, (int)grid, stream);
-  if (e == hipSuccess && partition_size != 0) {
-    const int64_t rg = (int64_t)num_seqs * num_q_heads;
-    const int32_t max_ctx = table_width * c.block_size;
-    if (c.head_dim == 64)
-      hipLaunchKernelGGL(pa_reduce_kernel<64>, dim3((uint32_t)rg), dim3(64), 0, stream, out, p.part_acc, p.part_ml,
-                         context_lens, num_q_heads, NP, partition_size, max_ctx, vsc);
-    else
-      hipLaunchKernelGGL(pa_reduce_kernel<128>, dim3((uint32_t)rg), dim3(128), 0, stream, out, p.part_acc,
-                         p.part_ml, context_lens, num_q_heads, NP, partition_size, max_ctx, vsc);
+    int cus = 0;
+    device_cus(&cus);
+    const int bpc = split_blocks_per_cu(c.head_dim, c.kv_dtype, c.block_size);
+    const int64_t grid = split_grid(steps_ub, cus, bpc);
+    if (grid * kNW + rows * np > z.slots_cap) return fail(PKV_ERR_INVALID, "internal: workspace sizing");
+    SplitParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.out = out;
+    p.k = kl;
+    p.v = vl;
+    p.ks = ksl;
+    p.vs = vsl;
+    p.bt = block_tables;
+    p.ctx = context_lens;
+    char* ws = static_cast<char*>(workspace);
+    p.row_done = reinterpret_cast<uint64_t*>(ws);
+    p.part_ml = reinterpret_cast<float*>(ws + z.cnt_bytes);
+    p.part_acc = reinterpret_cast<float*>(ws + z.cnt_bytes + z.ml_bytes);
+    p.W = table_width;
+    p.S = num_seqs;
+    p.Hq = num_q_heads;
+    p.Hkv = c.num_kv_heads;
+    p.G = G;
+    p.QT = QT;
+    p.HQ = c.num_kv_heads * QT;
+    p.num_blocks = c.num_blocks;
+    p.P = partition_size;
+    p.NP = (int32_t)np;
+    p.NWV = (int32_t)(grid * kNW);
+    p.epoch = next_epoch();
+    p.qk_scale = scale * kLog2e * ksc;
+    p.out_scale = vsc;
+    if (c.head_dim == 64) launch_split_kv<64>(p, c.kv_dtype, c.block_size, (int)grid, stream);
+    else launch_split_kv<128>(p, c.kv_dtype, c.block_size, (int)grid, stream);
     e = hipGetLastError();
   }
   if (e != hipSuccess) {

@@ -243,6 +243,61 @@ def test_aliased_tables_from_block_table_notes():
     assert mx <= 1e-2 and rel <= 1e-3
 
 
+# ----------------------------------------------------------------------- split-context form
+def _run_with_ws(c, P, ws):
+    import torch
+    D = c.cfg.head_dim
+    S = len(c.ctx)
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
+    out = torch.full((S, c.hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    pkv.paged_attn_decode(out, c.d_q, c.pool, 0, c.d_tables, c.d_ctx, scale, c.cfg.kv_dtype, c.kscale,
+                          c.vscale, P, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), scale
+
+
+def test_split_workspace_reuse_across_sizes():
+    # one workspace serves calls of different sizes back to back, starting
+    # from garbage: the row counters of one call never confuse the next
+    import torch
+    say("split workspace reuse")
+    rng = np.random.default_rng(6100)
+    big = build_case(rng, 40, 2, 4, 128, 16, pkv.PKV_KV_BF16, rng.integers(0, 600, size=40))
+    small = build_case(rng, 5, 2, 4, 128, 16, pkv.PKV_KV_BF16, [1, 17, 300, 0, 64])
+    nbytes = max(pkv.paged_attn_workspace_bytes(40, big.hq, 128, big.width, 16, 64),
+                 pkv.paged_attn_workspace_bytes(5, small.hq, 128, small.width, 16, 64))
+    ws = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda")
+    for c, P in ((big, 64), (small, 64), (big, 512), (big, 64), (small, 32)):
+        got, scale = _run_with_ws(c, P, ws)
+        mx, rel = errors(got, oracle_out(c, scale))
+        say(f"reuse S={len(c.ctx)} P={P}: max_abs={mx:.3e} rel={rel:.3e}")
+        assert mx <= 1e-2 and rel <= 1e-3
+
+
+def test_split_many_short_rows_and_empty_sequences():
+    # hundreds of 0..40-token sequences: waves cover many rows, rows start
+    # inside the prefetch window of the previous one, empty rows are zeroed
+    say("split short rows")
+    rng = np.random.default_rng(6200)
+    ctx = rng.integers(0, 41, size=300)
+    ctx[::7] = 0
+    c = build_case(rng, 300, 2, 3, 64, 16, pkv.PKV_KV_BF16, ctx)
+    for P in (32, 64):
+        got, _ = check(c, P, f"short rows P={P}")
+        assert not got[ctx == 0].any()
+
+
+@pytest.mark.parametrize("dt", [pkv.PKV_KV_BF16, pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8])
+def test_split_long_rows_spread_over_many_waves(dt):
+    # two long sequences on one KV head: each row is cut over hundreds of
+    # wavefronts, so the merge combines hundreds of partials
+    say(f"split long rows dt={dt}")
+    rng = np.random.default_rng(6300 + dt)
+    c = build_case(rng, 2, 1, 8, 128, 32, dt, [20000, 12345], needles=True)
+    for P in (512, 20480):
+        check(c, P, f"long rows dt={dt} P={P}")
+
+
 # ----------------------------------------------------------------------- exhaustive codes
 def test_every_fp8_code_decodes_exactly():
     # context 1 returns the token's dequantised V exactly: V holds all 256 codes
