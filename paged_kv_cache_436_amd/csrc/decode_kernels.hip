@@ -420,6 +420,13 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
 // row 0's steps, then row 1's, ...; row x starts at cum_s * HQ + xi * n_s where
 // cum_s = sum over s' < s of n_s'.  Wave w of NWV takes flat steps
 // [w * per, min((w + 1) * per, N)), per = ceil(N / NWV).
+// The grid is one workgroup of four waves per CU.  Workgroups are dispatched
+// to the eight XCDs in turn (workgroup b runs on XCD b % 8), and waves are
+// numbered so that XCD x holds waves [x * WX, (x + 1) * WX), WX = NWV / 8.
+// Measured on MI355X, waves on odd-numbered XCDs stream about 10% slower than
+// those on even ones, so XCD x takes a share of the flat list proportional to
+// kXcdWeight[x], split equally among its waves; all waves then finish
+// together.  The split depends only on N and the grid, never on timing.
 // Partition p of row x covers its tokens [p * P, (p + 1) * P); unit
 // u = x * NP + p.  The segment of unit u computed by wave w is stored in
 // partial slot u + w: walking the (unit, wave) pairs in order raises u or w
@@ -744,11 +751,43 @@ __device__ __forceinline__ int add_steps(uint64_t* ctr, uint32_t epoch, int mine
   }
 }
 
+constexpr int kXcdWeight[8] = {256, 231, 256, 231, 256, 231, 256, 231};
+
+// First flat step of XCD x's share of N steps.
+__device__ __forceinline__ int xcd_begin(int N, int x) {
+  int64_t acc = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    acc += i < x ? kXcdWeight[i] : 0;
+    tot += kXcdWeight[i];
+  }
+  return (int)((int64_t)N * acc / tot);
+}
+
+// Flat steps [a, e) of wave w; WX waves per XCD.
+__device__ __forceinline__ void wave_range(int N, int w, int WX, int& a, int& e) {
+  const int x = w / WX, li = w - x * WX;
+  const int b0 = xcd_begin(N, x), b1 = xcd_begin(N, x + 1);
+  const int per = (b1 - b0 + WX - 1) / WX;
+  a = min(b0 + li * per, b1);
+  e = min(a + per, b1);
+}
+
+// The wave whose range holds flat step t < N.
+__device__ __forceinline__ int wave_of(int t, int N, int WX) {
+  int x = 0;
+#pragma unroll
+  for (int i = 1; i < 8; ++i) x += t >= xcd_begin(N, i) ? 1 : 0;
+  const int b0 = xcd_begin(N, x), b1 = xcd_begin(N, x + 1);
+  const int per = (b1 - b0 + WX - 1) / WX;
+  return x * WX + (t - b0) / per;
+}
+
 // Merge the partials of row x into the output rows of its query heads.
 // Wave-cooperative, in the accumulator lane layout; loads go out four slots
 // at a time so that their latencies overlap.
 template <int D, int E>
-__device__ __forceinline__ void merge_row(const SplitParams& p, int x, int s, int xi, int ns, int sx, int per,
+__device__ __forceinline__ void merge_row(const SplitParams& p, int x, int s, int xi, int ns, int sx, int N,
                                           int TS, int lane) {
   constexpr int NC = D / 16;
   const int g = xi / p.QT;
@@ -764,21 +803,25 @@ __device__ __forceinline__ void merge_row(const SplitParams& p, int x, int s, in
 #pragma unroll
   for (int c = 0; c < NC; ++c) A[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   // slots in order: partitions pp, and for each the waves wv covering it
+  const int WX = p.NWV / 8;
+  // walk the row by position: the wave holding step t, then the first step
+  // past that wave's range (waves with empty ranges are never visited)
   int pp = 0;
-  int wv = sx / per;
+  int t = sx;
   while (pp < np) {
     int slot[4];
     int cnt = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       if (pp < np) {
+        const int wv = wave_of(t, N, WX);
         slot[k] = x * p.NP + pp + wv;
         ++cnt;
         const int e = sx + min((pp + 1) * PS, ns);     // end of partition pp (flat steps)
-        if (++wv > (e - 1) / per) {
-          ++pp;
-          wv = (sx + pp * PS) / per;
-        }
+        int ra, re;
+        wave_range(N, wv, WX, ra, re);
+        t = min(re, e);
+        if (t >= e) ++pp;
       } else {
         slot[k] = slot[0];
       }
@@ -854,10 +897,10 @@ __global__ __launch_bounds__(kWave * kNW) void pa_split_kernel(const SplitParams
   }
   const int N = __builtin_amdgcn_readfirstlane(total) * p.HQ;
   if (N == 0) return;
-  const int per = (N + p.NWV - 1) / p.NWV;
-  const int start = w * per;
-  if (start >= N) return;
-  const int nsteps = min(per, N - start);
+  int start, stop;
+  wave_range(N, w, p.NWV / 8, start, stop);
+  if (start >= stop) return;
+  const int nsteps = stop - start;
 
   // ---- locate the first step: sequence s with cum_s * HQ <= start < cum_{s+1} * HQ
   Cursor cur{};
@@ -1013,7 +1056,7 @@ __global__ __launch_bounds__(kWave * kNW) void pa_split_kernel(const SplitParams
     if (lane == 0) done_now = add_steps(p.row_done + x, p.epoch, mine);
     done_now = __builtin_amdgcn_readfirstlane(done_now);
     if (done_now == rn) {   // every partial of the row is in place
-      merge_row<D, GE::E>(p, x, rs, rxi, rn, rcum * p.HQ + rxi * rn, per, TS, lane);
+      merge_row<D, GE::E>(p, x, rs, rxi, rn, rcum * p.HQ + rxi * rn, N, TS, lane);
     }
     left -= mine;
     rj = 0;
@@ -1048,12 +1091,15 @@ hipError_t launch_single_kv(const DecodeParams& p, int kvt, int B, int grid, hip
   }
 }
 
-constexpr int kNBuf = 4;                 // steps per wave: 1 computed + 3 in flight
-constexpr int kMaxBlocksPerCU = 2;       // persistent grid: at most this many workgroups per CU
+// Steps of K/V registers per wave: one computed, the rest in flight (about
+// 40 KB per wave, 160 KB per CU with one wave per SIMD).
+template <int D>
+constexpr int split_nbuf() { return D == 128 ? 6 : 8; }
+constexpr int kMaxBlocksPerCU = 1;       // persistent grid: one workgroup (a wave per SIMD) per CU
 
 template <int D, int KVT, int B>
 const void* split_fn() {
-  return reinterpret_cast<const void*>(&pa_split_kernel<D, KVT, B, kNBuf>);
+  return reinterpret_cast<const void*>(&pa_split_kernel<D, KVT, B, split_nbuf<D>()>);
 }
 
 const void* split_kernel_fn(int D, int kvt, int B) {
@@ -1144,7 +1190,7 @@ bool split_sizes(int32_t S, int32_t Hq, int32_t Hkv_or_0, int32_t D, int32_t W, 
 
 template <int D, int KVT, int B>
 void launch_split_t(const SplitParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((pa_split_kernel<D, KVT, B, kNBuf>), dim3(grid), dim3(kWave * kNW), 0, stream, p);
+  hipLaunchKernelGGL((pa_split_kernel<D, KVT, B, split_nbuf<D>()>), dim3(grid), dim3(kWave * kNW), 0, stream, p);
 }
 
 template <int D>
