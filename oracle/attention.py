@@ -31,6 +31,9 @@ import numpy as np
 from . import codecs
 from .layout import (KV_BF16, KV_FP8_E5M2, KV_INT8, PoolImage, k_offset,
                      scale_offset, v_offset)
+from .layout import k_tiles_as_tokens as layout_k_tokens
+from .layout import scales_as_tokens as layout_scale_tokens
+from .layout import v_tiles_as_tokens as layout_v_tokens
 
 
 def slot_of(block_table_row: np.ndarray, pos, block_size: int):
@@ -42,7 +45,37 @@ def slot_of(block_table_row: np.ndarray, pos, block_size: int):
 
 def gather_kv(img: PoolImage, layer: int, block_table_row: np.ndarray,
               ctx: int, k_scale: float = 1.0, v_scale: float = 1.0):
-    """Contiguous dequantised K and V, each [ctx, Hkv, D] float64."""
+    """Contiguous dequantised K and V, each [ctx, Hkv, D] float64.
+
+    Reads whole tiles of the blocks the table names (layout.*_as_tokens);
+    ``gather_kv_by_slot`` reads the same values one element at a time through
+    the slot mapping and the layout's index functions, and the two agree
+    exactly (tests/test_oracle_paging.py)."""
+    p = img.shape
+    if ctx == 0:
+        z = np.zeros((0, p.num_kv_heads, p.head_dim))
+        return z, z.copy()
+    nblk = -(-ctx // p.block_size)
+    blocks = np.asarray(block_table_row, dtype=np.int64)[:nblk]
+    kraw = layout_k_tokens(p, img.k, layer, blocks)[:ctx]
+    vraw = layout_v_tokens(p, img.v, layer, blocks)[:ctx]
+    if p.kv_dtype == KV_BF16:
+        return codecs.bf16_bits_to_f64(kraw), codecs.bf16_bits_to_f64(vraw)
+    if p.kv_dtype == KV_FP8_E5M2:
+        ks = np.float64(np.float32(k_scale))
+        vs = np.float64(np.float32(v_scale))
+        return codecs.e5m2_decode(kraw) * ks, codecs.e5m2_decode(vraw) * vs
+    if p.kv_dtype == KV_INT8:
+        ksc = layout_scale_tokens(p, img.k_scale, layer, blocks)[:ctx]
+        vsc = layout_scale_tokens(p, img.v_scale, layer, blocks)[:ctx]
+        return codecs.int8_dequant(kraw, ksc), codecs.int8_dequant(vraw, vsc)
+    raise ValueError(p.kv_dtype)
+
+
+def gather_kv_by_slot(img: PoolImage, layer: int, block_table_row: np.ndarray,
+                      ctx: int, k_scale: float = 1.0, v_scale: float = 1.0):
+    """``gather_kv`` element by element: token t of the sequence is read at
+    slot table[t // B] * B + t % B through the layout's index functions."""
     p = img.shape
     if ctx == 0:
         z = np.zeros((0, p.num_kv_heads, p.head_dim))

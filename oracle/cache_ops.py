@@ -25,11 +25,13 @@ from .layout import (KV_BF16, KV_FP8_E5M2, KV_INT8, PoolImage, k_offset,
 
 def reshape_and_cache(img: PoolImage, layer: int, key_bits: np.ndarray,
                       value_bits: np.ndarray, slots: np.ndarray,
-                      k_scale: float = 1.0, v_scale: float = 1.0) -> PoolImage:
-    """Return a new pool image with tokens ``key_bits/value_bits`` [N, Hkv, D]
-    (bf16 bit patterns) written at ``slots`` [N] of ``layer``."""
+                      k_scale: float = 1.0, v_scale: float = 1.0,
+                      inplace: bool = False) -> PoolImage:
+    """Return a pool image with tokens ``key_bits/value_bits`` [N, Hkv, D]
+    (bf16 bit patterns) written at ``slots`` [N] of ``layer``: a new image,
+    or ``img`` itself updated when ``inplace`` (for multi-GB images)."""
     p = img.shape
-    out = img.copy()
+    out = img if inplace else img.copy()
     key_bits = np.asarray(key_bits, dtype=np.uint16)
     value_bits = np.asarray(value_bits, dtype=np.uint16)
     slots = np.asarray(slots, dtype=np.int64)
@@ -70,12 +72,17 @@ def reshape_and_cache(img: PoolImage, layer: int, key_bits: np.ndarray,
     return out
 
 
-def copy_blocks(img: PoolImage, pairs: np.ndarray) -> PoolImage:
-    """Return a new image where, in every layer, block dst holds a byte copy of
-    block src for each (src, dst) row of ``pairs``."""
+def copy_blocks(img: PoolImage, pairs: np.ndarray, inplace: bool = False) -> PoolImage:
+    """Return an image where, in every layer, block dst holds a byte copy of
+    block src for each (src, dst) row of ``pairs``.  All copies read the state
+    before the call: with ``inplace`` the sources are snapshotted first, so a
+    block that is both a source and a destination still reads its old bytes."""
     p = img.shape
     src_img = img
-    out = img.copy()
+    if inplace:
+        pairs_ = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+        src_img = _snapshot_blocks(img, np.unique(pairs_[:, 0]))
+    out = img if inplace else img.copy()
     pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
     te = p.tile_elems
     for layer in range(p.num_layers):
@@ -91,3 +98,24 @@ def copy_blocks(img: PoolImage, pairs: np.ndarray) -> PoolImage:
                     out.k_scale[ds:ds + p.block_size] = src_img.k_scale[ss:ss + p.block_size]
                     out.v_scale[ds:ds + p.block_size] = src_img.v_scale[ss:ss + p.block_size]
     return out
+
+
+def _snapshot_blocks(img: PoolImage, blocks: np.ndarray) -> PoolImage:
+    """An image holding copies of the listed blocks' tiles and scale rows (in
+    every layer) at their own positions; other positions are never read."""
+    p = img.shape
+    snap = PoolImage(p, np.empty_like(img.k), np.empty_like(img.v),
+                     None if img.k_scale is None else np.empty_like(img.k_scale),
+                     None if img.v_scale is None else np.empty_like(img.v_scale))
+    te = p.tile_elems
+    for layer in range(p.num_layers):
+        for b in blocks:
+            for h in range(p.num_kv_heads):
+                o = int(tile_base(p, layer, int(b), h))
+                snap.k[o:o + te] = img.k[o:o + te]
+                snap.v[o:o + te] = img.v[o:o + te]
+                if p.has_scales:
+                    so = int(scale_offset(p, layer, int(b), h, 0))
+                    snap.k_scale[so:so + p.block_size] = img.k_scale[so:so + p.block_size]
+                    snap.v_scale[so:so + p.block_size] = img.v_scale[so:so + p.block_size]
+    return snap

@@ -106,6 +106,38 @@ def scale_offset(p: PoolShape, layer, block, head, t):
             * p.num_kv_heads + head) * p.block_size + np.asarray(t, dtype=np.int64)
 
 
+def k_tiles_as_tokens(p: PoolShape, region: np.ndarray, layer: int, blocks) -> np.ndarray:
+    """K of the listed blocks of one layer as [len(blocks) * B, Hkv, D],
+    token-major, in storage elements.  Each (block, head) tile is contiguous
+    and, by the K formula above, is the array [D / X][B][X] (piece, token,
+    lane); putting the token axis first and merging piece and lane gives
+    [B][D]."""
+    blocks = np.asarray(blocks, dtype=np.int64)
+    t = region.reshape(p.num_layers, p.num_blocks, p.num_kv_heads,
+                       p.head_dim // p.x, p.block_size, p.x)[layer][blocks]
+    # [nb, H, D/X, B, X] -> [nb, B, H, D/X, X]
+    t = t.transpose(0, 3, 1, 2, 4)
+    return t.reshape(blocks.size * p.block_size, p.num_kv_heads, p.head_dim)
+
+
+def v_tiles_as_tokens(p: PoolShape, region: np.ndarray, layer: int, blocks) -> np.ndarray:
+    """V of the listed blocks as [len(blocks) * B, Hkv, D]: by the V formula a
+    tile is the array [B / 4][D][4] (token group, dim, token in group)."""
+    blocks = np.asarray(blocks, dtype=np.int64)
+    t = region.reshape(p.num_layers, p.num_blocks, p.num_kv_heads,
+                       p.block_size // 4, p.head_dim, 4)[layer][blocks]
+    # [nb, H, B/4, D, 4] -> [nb, B/4, 4, H, D]
+    t = t.transpose(0, 2, 4, 1, 3)
+    return t.reshape(blocks.size * p.block_size, p.num_kv_heads, p.head_dim)
+
+
+def scales_as_tokens(p: PoolShape, region: np.ndarray, layer: int, blocks) -> np.ndarray:
+    """Per-token-head scales of the listed blocks as [len(blocks) * B, Hkv]."""
+    blocks = np.asarray(blocks, dtype=np.int64)
+    t = region.reshape(p.num_layers, p.num_blocks, p.num_kv_heads, p.block_size)[layer][blocks]
+    return t.transpose(0, 2, 1).reshape(blocks.size * p.block_size, p.num_kv_heads)
+
+
 # ------------------------------------------------------------ host pool image
 @dataclass
 class PoolImage:

@@ -12,6 +12,8 @@ import oracle.attention as att
 import oracle.codecs as codecs
 from tests import test_oracle_attention as ta
 from tests import test_oracle_codecs as tc
+from tests import test_oracle_paging as tp
+from oracle import layout
 
 
 def _fails(fn):
@@ -35,11 +37,19 @@ def test_wrong_group_mapping_is_caught(monkeypatch):
 
 
 def test_slot_off_by_one_is_caught(monkeypatch):
+    # the element-by-element gather follows slot_of; the whole-tile gather must
+    # equal it, so a slot slip shows as a mismatch between the two
     def slot_bad(row, pos, B):
         pos = np.asarray(pos, dtype=np.int64)
         row = np.asarray(row, dtype=np.int64)
         return row[pos // B] * B + (pos + 1) % B
     monkeypatch.setattr(att, "slot_of", slot_bad)
+    assert _fails(lambda: tp.test_tile_gather_equals_slot_gather(layout.KV_BF16, 16, 64))
+
+
+def test_token_shift_in_tile_read_is_caught(monkeypatch):
+    orig = att.layout_k_tokens
+    monkeypatch.setattr(att, "layout_k_tokens", lambda *a: np.roll(orig(*a), 1, axis=0))
     assert _fails(ta.test_tiny_config_matches_sdpa)
 
 

@@ -184,3 +184,63 @@ def test_copy_on_write_keeps_outputs():
     K, _ = attention.gather_kv(img3, 0, tables2[0], 21)
     assert np.array_equal(K[20], codecs.bf16_bits_to_f64(kn[0]))
     assert np.array_equal(after0[1:], before[0][1:])
+
+
+@pytest.mark.parametrize("dt", [layout.KV_BF16, layout.KV_INT8])
+def test_inplace_cache_ops_equal_copying_ones(dt):
+    # the in-place forms (used on multi-GB images) give byte-identical images,
+    # including a copy whose destination is also another pair's source: every
+    # copy reads the state before the call
+    rng = np.random.default_rng(77)
+    p = layout.PoolShape(2, 6, 16, 2, 64, dt)
+    img = layout.empty_image(p)
+    img.k[:] = rng.integers(0, 2**8 if dt else 2**16, size=img.k.size).astype(img.k.dtype)
+    img.v[:] = rng.integers(0, 2**8 if dt else 2**16, size=img.v.size).astype(img.v.dtype)
+    if p.has_scales:
+        img.k_scale[:] = rng.random(img.k_scale.size).astype(np.float32)
+        img.v_scale[:] = rng.random(img.v_scale.size).astype(np.float32)
+    pairs = np.array([[0, 3], [3, 4], [5, 1]], np.int64)
+    want = cache_ops.copy_blocks(img, pairs)
+    got = cache_ops.copy_blocks(img.copy(), pairs, inplace=True)
+    for name in ("k", "v", "k_scale", "v_scale"):
+        a, b = getattr(want, name), getattr(got, name)
+        assert (a is None and b is None) or np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    # block 4 holds block 3's old bytes, not block 0's
+    t3 = int(layout.tile_base(p, 1, 3, 1))
+    t4 = int(layout.tile_base(p, 1, 4, 1))
+    assert np.array_equal(got.k[t4:t4 + p.tile_elems], img.k[t3:t3 + p.tile_elems])
+    kb = workloads.to_bf16_bits(rng.standard_normal((5, 2, 64), dtype=np.float32))
+    slots = np.array([3, 17, -1, 40, 95], np.int64)
+    want = cache_ops.reshape_and_cache(img, 1, kb, kb, slots)
+    got = cache_ops.reshape_and_cache(img.copy(), 1, kb, kb, slots, inplace=True)
+    for name in ("k", "v", "k_scale", "v_scale"):
+        a, b = getattr(want, name), getattr(got, name)
+        assert (a is None and b is None) or np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+@pytest.mark.parametrize("dt", [layout.KV_BF16, layout.KV_FP8_E5M2, layout.KV_INT8])
+@pytest.mark.parametrize("B,D", [(16, 64), (32, 128), (8, 32)])
+def test_tile_gather_equals_slot_gather(dt, B, D):
+    # the whole-tile read used by the oracle's decode equals the definition
+    # (slot mapping + element index functions), bit for bit
+    rng = np.random.default_rng(91 + dt + B + D)
+    p = layout.PoolShape(2, 7, B, 3, D, dt)
+    img = layout.empty_image(p)
+    if dt == layout.KV_BF16:
+        img.k[:] = rng.integers(0, 2**16, size=img.k.size, dtype=np.uint16) & np.uint16(0x3FFF)
+        img.v[:] = rng.integers(0, 2**16, size=img.v.size, dtype=np.uint16) & np.uint16(0x3FFF)
+    else:
+        img.k[:] = rng.integers(0, 256, size=img.k.size).astype(img.k.dtype)
+        img.v[:] = rng.integers(0, 256, size=img.v.size).astype(img.v.dtype)
+        if dt == layout.KV_FP8_E5M2:   # keep the codes finite (exponent < 31)
+            img.k[:] = img.k & np.uint8(0xBB)
+            img.v[:] = img.v & np.uint8(0xBB)
+    if p.has_scales:
+        img.k_scale[:] = rng.random(img.k_scale.size).astype(np.float32)
+        img.v_scale[:] = rng.random(img.v_scale.size).astype(np.float32)
+    row = rng.permutation(7).astype(np.int32)
+    for ctx in (0, 1, B - 1, B, B + 1, 7 * B):
+        for layer in (0, 1):
+            a = attention.gather_kv(img, layer, row, ctx, 0.5, 1.5)
+            b = attention.gather_kv_by_slot(img, layer, row, ctx, 0.5, 1.5)
+            assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
