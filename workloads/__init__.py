@@ -184,6 +184,16 @@ def token_kv(w: Workload, num_tokens: int, stream: int = 3):
     return k, v
 
 
+def sequence_kv(w: Workload, seq: int, num_tokens: int):
+    """bf16 bits K and V, each [num_tokens, Hkv, D], drawn from a stream of
+    their own for sequence ``seq`` (for workloads written one sequence at a
+    time)."""
+    r = np.random.default_rng(np.random.SeedSequence([436000 + w.config_id, 1000 + seq]))
+    k = normal_bf16(r, (num_tokens, w.num_kv_heads, w.head_dim))
+    v = normal_bf16(r, (num_tokens, w.num_kv_heads, w.head_dim))
+    return k, v
+
+
 def plant_needles(w: Workload, q_bits: np.ndarray, k_tok: np.ndarray,
                   token_seq: np.ndarray, token_pos: np.ndarray,
                   per_seq: int = 8, stream: int = 5) -> np.ndarray:
