@@ -58,6 +58,27 @@ def parse():
     return ap.parse_args()
 
 
+PROFILE = os.path.join(ROOT, "profiles", "pa_split_kernel_llama70b_bf16.md")
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_436_amd", "csrc", "decode_kernels.hip")
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary, or None when the kernel source has changed since the counters
+    were taken (the summary records the source's sha256)."""
+    import hashlib
+    import re
+    try:
+        text = open(PROFILE, encoding="utf-8").read()
+        src = open(KERNEL_SRC, "rb").read()
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_launch = (\d+); kernel_source_sha256 = ([0-9a-f]{64})", text)
+    if not m or m.group(2) != hashlib.sha256(src).hexdigest():
+        return None
+    return int(m.group(1))
+
+
 def copy_calibration():
     """A plain device copy of known size, for calibrating HBM byte counters."""
     import torch
@@ -207,7 +228,8 @@ def main():
         "seq_tokens_per_s": round(kv_per_step / (Hkv * 2 * D * 2 * L) / (elapsed / args.steps), 1),
         "roofline": {"bound": "hbm", "kernel": "pa_split_kernel (the one launch of a split-context paged_attn_decode call)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
                      "avg_call_us": round(avg_dec_ms * 1e3, 2), "bytes_per_call": int(avg_dec_bytes)},
         "cpu_baseline": cpu,
         "parity_sample": parity,
