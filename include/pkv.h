@@ -204,6 +204,25 @@ pkv_status paged_attn_decode(float* out, const void* q, const pkv_pool* pool, in
                              const pkv_kv_scales* kv_scales, int32_t partition_size,
                              void* workspace, uint64_t workspace_bytes, hipStream_t stream);
 
+/* One decode step with its cache write in the same launch: for each sequence s
+ * with ctx_s > 0, the new token's K and V (key, value: device bf16
+ * [S][H][D], 16-byte aligned) are stored at position ctx_s - 1 - the slot the
+ * block table names - exactly as reshape_and_cache would store them (same
+ * quantisation), and the decode of paged_attn_decode over ctx_s tokens,
+ * including that one, is computed.  The result and the pool afterwards equal
+ * reshape_and_cache with those slots followed by paged_attn_decode ([KVP] §一:
+ * the step computes only K_t, V_t and appends them; §三 工作方式 steps 3-4).
+ * The token's block must not be shared with another sequence (copy_blocks
+ * first).  Split-context form only: partition_size > 0, else
+ * PKV_ERR_UNSUPPORTED.  Other arguments as for paged_attn_decode; kv_scales
+ * also give the fp8 encoding scales. */
+pkv_status paged_attn_decode_append(float* out, const void* q, const pkv_pool* pool, int32_t layer,
+                                    const void* key, const void* value, const int32_t* block_tables,
+                                    int32_t table_width, const int32_t* context_lens, int32_t num_seqs,
+                                    int32_t num_q_heads, float scale, int32_t kv_dtype,
+                                    const pkv_kv_scales* kv_scales, int32_t partition_size, void* workspace,
+                                    uint64_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------- host checks
  * Validators over HOST copies of device inputs, for callers that want to
  * rule out racing or out-of-range values before a launch.  Return PKV_OK or

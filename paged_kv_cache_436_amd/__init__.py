@@ -80,6 +80,8 @@ SIGNATURES = {
     "paged_attn_workspace_bytes": (_U64, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "paged_attn_decode": (_I32, [_P, _P, ctypes.POINTER(PoolDesc), _I32, _P, _I32, _P, _I32, _I32,
                                  _F, _I32, ctypes.POINTER(KVScales), _I32, _P, _U64, _P]),
+    "paged_attn_decode_append": (_I32, [_P, _P, ctypes.POINTER(PoolDesc), _I32, _P, _P, _P, _I32, _P, _I32,
+                                        _I32, _F, _I32, ctypes.POINTER(KVScales), _I32, _P, _U64, _P]),
     "pkv_check_slots": (_I32, [_I64P, _I32, _I64]),
     "pkv_check_pairs": (_I32, [_I64P, _I32, _I32]),
     "pkv_check_tables": (_I32, [_I32P, _I32P, _I32, _I32, _I32, _I32]),
@@ -204,6 +206,22 @@ def paged_attn_decode(out, q, pool: Pool, layer: int, block_tables, context_lens
     _check(_lib.paged_attn_decode(_ptr(out), _ptr(q), ctypes.byref(pool.desc), layer, _ptr(block_tables), W,
                                   _ptr(context_lens), S, hq, float(scale), kvd, ctypes.byref(sc),
                                   partition_size, _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def paged_attn_decode_append(out, q, pool: Pool, layer: int, key, value, block_tables, context_lens,
+                             scale: float, kv_dtype: int | None = None, k_scale: float = 1.0,
+                             v_scale: float = 1.0, partition_size: int = 0, workspace=None, stream=None):
+    """Decode with the cache write in the same launch: key, value are bf16
+    [S, Hkv, D], stored at position context_lens[s] - 1 of each sequence."""
+    S, hq, _ = q.shape
+    W = block_tables.shape[1]
+    kvd = pool.cfg.kv_dtype if kv_dtype is None else kv_dtype
+    sc = KVScales(k_scale, v_scale)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.paged_attn_decode_append(_ptr(out), _ptr(q), ctypes.byref(pool.desc), layer, _ptr(key),
+                                         _ptr(value), _ptr(block_tables), W, _ptr(context_lens), S, hq,
+                                         float(scale), kvd, ctypes.byref(sc), partition_size, _ptr(workspace),
+                                         ws_bytes, _stream(stream)))
 
 
 # ------------------------------------------------------------------- checks

@@ -9,37 +9,13 @@
 // repointed (bjdmk.com.cn article, §3.2 Copy-on-Write).
 #include <hip/hip_runtime.h>
 
+#include "pkv_codecs.h"
 #include "pkv_internal.h"
 
 namespace pkv {
 namespace {
 
 constexpr int kWave = 64;
-
-// ------------------------------------------------------------------ codecs
-// fp32 -> OCP e5m2, round to nearest even, finite overflow saturates to
-// +-57344, +-inf stays inf, NaN becomes 0x7F with the input's sign.
-__device__ __forceinline__ uint32_t encode_e5m2(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return 0x7fu | sign;
-  if (a == 0x7f800000u) return 0x7cu | sign;
-  if (a >= 0x38800000u) {  // |y| >= 2^-14: e5m2 normal range before rounding
-    // keep 2 of the 23 mantissa bits, ties to even; a carry bumps the exponent
-    const uint32_t r = (a + 0x000fffffu + ((a >> 21) & 1u)) >> 21;
-    uint32_t code = r - (112u << 2);  // rebias the exponent from 127 to 15
-    if (code > 0x7bu) code = 0x7bu;   // saturate
-    return code | sign;
-  }
-  // subnormal range: a multiple of 2^-16; 4 * 2^-16 is the smallest normal
-  const float n = __builtin_rintf(__uint_as_float(a) * 65536.0f);
-  return (uint32_t)n | sign;
-}
-
-__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
-  return __uint_as_float((uint32_t)b << 16);
-}
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -81,10 +57,8 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     uint8_t* kd = static_cast<uint8_t*>(kdst) + tile;
     uint8_t* vd = static_cast<uint8_t*>(vdst) + tile;
     for (int d = lane; d < D; d += kWave) {
-      const float yk = __fdiv_rn(bf16_bits_to_float(kx[d]), k_scale);
-      const float yv = __fdiv_rn(bf16_bits_to_float(vx[d]), v_scale);
-      kd[((d >> 4) * B + t) * 16 + (d & 15)] = (uint8_t)encode_e5m2(yk);
-      vd[((t >> 2) * D + d) * 4 + (t & 3)] = (uint8_t)encode_e5m2(yv);
+      kd[((d >> 4) * B + t) * 16 + (d & 15)] = (uint8_t)fp8_store(kx[d], k_scale);
+      vd[((t >> 2) * D + d) * 4 + (t & 3)] = (uint8_t)fp8_store(vx[d], v_scale);
     }
   } else {  // INT8, symmetric per (token, head)
     int8_t* kd = static_cast<int8_t*>(kdst) + tile;
@@ -96,14 +70,11 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     }
     kmax = wave_max(kmax);
     vmax = wave_max(vmax);
-    const float ks = __fdiv_rn(kmax, 127.0f);
-    const float vs = __fdiv_rn(vmax, 127.0f);
+    const float ks = int8_scale(kmax);
+    const float vs = int8_scale(vmax);
     for (int d = lane; d < D; d += kWave) {
-      float ck = 0.f, cv = 0.f;
-      if (ks > 0.f) ck = fminf(fmaxf(__builtin_rintf(__fdiv_rn(bf16_bits_to_float(kx[d]), ks)), -127.f), 127.f);
-      if (vs > 0.f) cv = fminf(fmaxf(__builtin_rintf(__fdiv_rn(bf16_bits_to_float(vx[d]), vs)), -127.f), 127.f);
-      kd[((d >> 4) * B + t) * 16 + (d & 15)] = (int8_t)(int)ck;
-      vd[((t >> 2) * D + d) * 4 + (t & 3)] = (int8_t)(int)cv;
+      kd[((d >> 4) * B + t) * 16 + (d & 15)] = (int8_t)int8_store(kx[d], ks);
+      vd[((t >> 2) * D + d) * 4 + (t & 3)] = (int8_t)int8_store(vx[d], vs);
     }
     if (lane == 0) {
       const int64_t so = (blk * H + h) * (int64_t)B + t;

@@ -36,9 +36,11 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <utility>
 #include <chrono>
 #include <mutex>
 
+#include "pkv_codecs.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -133,6 +135,16 @@ __device__ __forceinline__ float sum_x32(float x) {
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maximum).
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 __device__ __forceinline__ int clamp_ctx(int c, int max_ctx) { return c < 0 ? 0 : (c > max_ctx ? max_ctx : c); }
 
@@ -442,10 +454,13 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
 struct SplitParams {
   const uint16_t* q;          // [S][Hq][D] bf16
   float* out;                 // [S][Hq][D]
-  const char* k;
-  const char* v;
-  const float* ks;
-  const float* vs;
+  char* k;                    // this layer's K region (written only when appending)
+  char* v;
+  float* ks;
+  float* vs;
+  const uint16_t* new_k;      // appending decode: [S][Hkv][D] bf16 new tokens, else null
+  const uint16_t* new_v;
+  float enc_k, enc_v;         // fp8 per-tensor scales for encoding the new token
   const int32_t* bt;
   const int32_t* ctx;
   uint64_t* row_done;         // workspace: [rows] (epoch << 32) | steps reported
@@ -484,12 +499,17 @@ struct StepMeta {
   int t0;       // first token of the step within its row
   int t_end;    // row's context length
   int slot;     // partial slot of the step's segment
-  int flags;    // kNewRow | kQReady | kFlush
+  int flags;    // kNewRow | kQReady | kFlush | kAppend | kAReady
   int qs, qh0;  // sequence and first head of the row (for a direct q load)
+  int ag;       // KV head of the row
+  int aphys0;   // appending: physical blocks of the step's two 16-token chunks
+  int aphys1;
 };
 constexpr int kNewRow = 1;   // first step of a row in this wave: load the row's q
 constexpr int kQReady = 2;   // ... and that q was prefetched into qnext
 constexpr int kFlush = 4;    // last step of a segment: write the partial
+constexpr int kAppend = 8;   // appending decode, the row's last step: holds the new token
+constexpr int kAReady = 16;  // ... and its K/V input was prefetched into anext
 
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
@@ -562,6 +582,202 @@ __device__ __forceinline__ void issue_chunks(SplitBuf<D, KVT>& r, const SplitPar
       r.vsc[h] = *reinterpret_cast<const f32x4*>(p.vs + so);
     }
   }
+}
+
+// ---- appending decode: the new token of a row enters through registers.
+// The wave that computes a row's last step loads the new token's K and V
+// (bf16 input), stores them into its K/V registers in the tile layout, encoded
+// exactly as the cache write would store them, computes the step, and writes
+// those register pieces back to the pool.  No other wave of the launch reads
+// the bytes it writes: the token's block is not shared (copy-on-write happens
+// before the append) and the rest of its tile belongs to other steps.
+
+// The new token's input values a lane needs, laid out like its registers.
+template <int D, int KVT>
+struct AppendRegs {
+  using GE = SplitGeo<D, KVT>;
+  static constexpr int KIN = GE::E == 2 ? GE::LPC : 2 * GE::LPC;   // 16-byte loads for the K pieces
+  u32x4 k[KIN];
+  u32x2 v[GE::LPC];     // bf16 storage: .x holds dims (d, d+1); 8-bit: 4 dims
+};
+
+template <int D, int KVT>
+__device__ __forceinline__ AppendRegs<D, KVT> load_append(const SplitParams& p, int s, int g, int lane) {
+  using GE = SplitGeo<D, KVT>;
+  const int row = lane & 15;
+  const int j = lane >> 4;
+  const uint16_t* kx = p.new_k + ((int64_t)s * p.Hkv + g) * D;
+  const uint16_t* vx = p.new_v + ((int64_t)s * p.Hkv + g) * D;
+  AppendRegs<D, KVT> a;
+  if constexpr (GE::E == 2) {
+#pragma unroll
+    for (int u = 0; u < GE::LPC; ++u) {
+      a.k[u] = *reinterpret_cast<const u32x4*>(kx + 8 * (4 * u + j));            // dims of piece 4u + j
+      a.v[u] = u32x2{*reinterpret_cast<const uint32_t*>(vx + 32 * u + 2 * row), 0u};  // dims 32u + 2row, +1
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < GE::LPC; ++u) {
+      a.k[2 * u] = *reinterpret_cast<const u32x4*>(kx + 16 * (4 * u + j));       // dims 16(4u+j) .. +7
+      a.k[2 * u + 1] = *reinterpret_cast<const u32x4*>(kx + 16 * (4 * u + j) + 8);  // .. +15
+      a.v[u] = *reinterpret_cast<const u32x2*>(vx + 64 * u + 4 * row);           // dims 64u + 4row .. +3
+    }
+  }
+  return a;
+}
+
+__device__ __forceinline__ uint32_t half_of(uint32_t w, int i) { return i ? (w >> 16) : (w & 0xffffu); }
+__device__ __forceinline__ float abs_bf16(uint32_t b) { return fabsf(bf16_bits_to_float(b & 0xffffu)); }
+
+// Put token tt (0 <= tt < TS) of the step, taken from `a`, into chunk H of r
+// (the chunk is a template argument so every register index stays static).
+template <int H, int D, int KVT>
+__device__ __forceinline__ void patch_chunk(SplitBuf<D, KVT>& r, const AppendRegs<D, KVT>& a, const SplitParams& p,
+                                            int tt, float sk, float sv, int lane) {
+  using GE = SplitGeo<D, KVT>;
+  const int row = lane & 15;
+  const int j = lane >> 4;
+  // position of the token in chunk H: outside [0, 16) when another chunk
+  // holds it, and then no lane matches below
+  const int rt = tt - 16 * H, jj = rt >> 2, ii = rt & 3;
+  if (row == rt) {                                 // K: this lane's pieces are the token's
+#pragma unroll
+    for (int u = 0; u < GE::LPC; ++u) {
+      if constexpr (GE::E == 2) {
+        r.k[H][u] = a.k[u];
+      } else {
+        u32x4 w;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {           // output dword q4 = input dims 4q4 .. 4q4+3
+          const u32x4 src = a.k[2 * u + (q4 >> 1)];
+          const uint32_t x0 = src[(q4 & 1) * 2], x1 = src[(q4 & 1) * 2 + 1];
+          uint32_t b0, b1, b2, b3;
+          if constexpr (KVT == PKV_KV_FP8_E5M2) {
+            b0 = fp8_store(half_of(x0, 0), p.enc_k);
+            b1 = fp8_store(half_of(x0, 1), p.enc_k);
+            b2 = fp8_store(half_of(x1, 0), p.enc_k);
+            b3 = fp8_store(half_of(x1, 1), p.enc_k);
+          } else {
+            b0 = int8_store(half_of(x0, 0), sk);
+            b1 = int8_store(half_of(x0, 1), sk);
+            b2 = int8_store(half_of(x1, 0), sk);
+            b3 = int8_store(half_of(x1, 1), sk);
+          }
+          w[q4] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        }
+        r.k[H][u] = w;
+      }
+    }
+  }
+  if (j == jj) {                                   // V: token ii of this lane's group
+#pragma unroll
+    for (int u = 0; u < GE::LPC; ++u) {
+      if constexpr (GE::E == 2) {
+        const uint32_t nv = a.v[u][0];             // dims d (low half), d + 1 (high half)
+        const int sh = (ii & 1) * 16;
+        const uint32_t keep = ~(0xffffu << sh);
+        // dword ii/2 holds dim d, dword 2 + ii/2 dim d + 1 (two tokens each)
+        const uint32_t lo = (ii >> 1) ? r.v[H][u][1] : r.v[H][u][0];
+        const uint32_t hi = (ii >> 1) ? r.v[H][u][3] : r.v[H][u][2];
+        const uint32_t nlo = (lo & keep) | (half_of(nv, 0) << sh);
+        const uint32_t nhi = (hi & keep) | (half_of(nv, 1) << sh);
+        r.v[H][u][0] = (ii >> 1) ? r.v[H][u][0] : nlo;
+        r.v[H][u][1] = (ii >> 1) ? nlo : r.v[H][u][1];
+        r.v[H][u][2] = (ii >> 1) ? r.v[H][u][2] : nhi;
+        r.v[H][u][3] = (ii >> 1) ? nhi : r.v[H][u][3];
+      } else {
+        const int sh = ii * 8;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {              // dword e = dim 64u + 4row + e
+          const uint32_t x = half_of(a.v[u][e >> 1], e & 1);
+          const uint32_t b = KVT == PKV_KV_FP8_E5M2 ? fp8_store(x, p.enc_v) : int8_store(x, sv);
+          r.v[H][u][e] = (r.v[H][u][e] & ~(0xffu << sh)) | (b << sh);
+        }
+      }
+    }
+    if constexpr (KVT == PKV_KV_INT8) {
+      r.ksc[H][0] = ii == 0 ? sk : r.ksc[H][0];
+      r.ksc[H][1] = ii == 1 ? sk : r.ksc[H][1];
+      r.ksc[H][2] = ii == 2 ? sk : r.ksc[H][2];
+      r.ksc[H][3] = ii == 3 ? sk : r.ksc[H][3];
+      r.vsc[H][0] = ii == 0 ? sv : r.vsc[H][0];
+      r.vsc[H][1] = ii == 1 ? sv : r.vsc[H][1];
+      r.vsc[H][2] = ii == 2 ? sv : r.vsc[H][2];
+      r.vsc[H][3] = ii == 3 ? sv : r.vsc[H][3];
+    }
+  }
+}
+
+// Put token tt (0 <= tt < TS) of the step, taken from `a`, into r.
+template <int D, int KVT>
+__device__ __forceinline__ void patch_append(SplitBuf<D, KVT>& r, const AppendRegs<D, KVT>& a, const SplitParams& p,
+                                             int tt, int lane) {
+  using GE = SplitGeo<D, KVT>;
+  float sk = 0.f, sv = 0.f;   // int8 scales of the token
+  if constexpr (KVT == PKV_KV_INT8) {
+    // every lane with the same j holds the same K dims, every lane with the
+    // same row the same V dims: reduce over j for K and over row for V
+    float mk = 0.f, mv = 0.f;
+#pragma unroll
+    for (int u = 0; u < AppendRegs<D, KVT>::KIN; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mk = fmaxf(mk, fmaxf(abs_bf16(a.k[u][e]), abs_bf16(a.k[u][e] >> 16)));
+#pragma unroll
+    for (int u = 0; u < GE::LPC; ++u)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) mv = fmaxf(mv, fmaxf(abs_bf16(a.v[u][e]), abs_bf16(a.v[u][e] >> 16)));
+    mk = max_x32(max_x16(mk));
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) mv = fmaxf(mv, __shfl_xor(mv, off, kWave));
+    sk = int8_scale(mk);
+    sv = int8_scale(mv);
+  }
+  // both chunks, so that every register index stays static (a runtime choice
+  // of chunk would move the buffers to scratch memory)
+  patch_chunk<0, D, KVT>(r, a, p, tt, sk, sv, lane);
+  if constexpr (GE::CH == 2) patch_chunk<1, D, KVT>(r, a, p, tt, sk, sv, lane);
+}
+
+// Write the register pieces of chunk H that hold token tt back to the pool,
+// at the addresses issue_chunks read them from.
+template <int H, int D, int KVT, int B>
+__device__ __forceinline__ void writeback_chunk(const SplitBuf<D, KVT>& r, const SplitParams& p, int phys, int g,
+                                                int t0, int tt, int lane) {
+  using GE = SplitGeo<D, KVT>;
+  constexpr int E = GE::E;
+  const int row = lane & 15;
+  const int j = lane >> 4;
+  const int rt = tt - 16 * H, jj = rt >> 2;       // no lane matches unless chunk H holds the token
+  const int toff = (t0 + 16 * H) % B;
+  const int64_t tile = (int64_t)phys * p.Hkv + g;
+  char* kt = p.k + tile * (int64_t)(B * D * E);
+  char* vt = p.v + tile * (int64_t)(B * D * E);
+  if (row == rt) {
+#pragma unroll
+    for (int u = 0; u < GE::LPC; ++u) *reinterpret_cast<u32x4*>(kt + ((4 * u + j) * B + toff + row) * 16) = r.k[H][u];
+  }
+  if (j == jj) {
+    const int grp = (toff >> 2) + j;
+#pragma unroll
+    for (int u = 0; u < GE::LPC; ++u) {
+      const int d = (E == 2) ? (32 * u + 2 * row) : (64 * u + 4 * row);
+      *reinterpret_cast<u32x4*>(vt + (grp * D + d) * 4 * E) = r.v[H][u];
+    }
+    if constexpr (KVT == PKV_KV_INT8) {
+      if (row == 0) {
+        const int64_t so = tile * B + toff + 4 * j;
+        *reinterpret_cast<f32x4*>(p.ks + so) = r.ksc[H];
+        *reinterpret_cast<f32x4*>(p.vs + so) = r.vsc[H];
+      }
+    }
+  }
+}
+
+template <int D, int KVT, int B>
+__device__ __forceinline__ void writeback_append(const SplitBuf<D, KVT>& r, const SplitParams& p, int phys0,
+                                                 int phys1, int g, int t0, int tt, int lane) {
+  writeback_chunk<0, D, KVT, B>(r, p, phys0, g, t0, tt, lane);
+  if constexpr (SplitGeo<D, KVT>::CH == 2) writeback_chunk<1, D, KVT, B>(r, p, phys1, g, t0, tt, lane);
 }
 
 // Rescale threshold of the streaming softmax, in log2 units: the reference
@@ -862,8 +1078,11 @@ __device__ __forceinline__ void merge_row(const SplitParams& p, int x, int s, in
   }
 }
 
+// Launched with one workgroup (one wave per SIMD) per CU, so the compiler may
+// use the whole register file for a wave's in-flight loads.
 template <int D, int KVT, int B, int NBUF>
-__global__ __launch_bounds__(kWave * kNW) void pa_split_kernel(const SplitParams p) {
+__global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 1))) void pa_split_kernel(
+    const SplitParams p) {
   using GE = SplitGeo<D, KVT>;
   constexpr int TS = GE::TS;
   const int lane = threadIdx.x % kWave;
@@ -942,12 +1161,14 @@ __global__ __launch_bounds__(kWave * kNW) void pa_split_kernel(const SplitParams
   QRegs<GE::KK> qnext;
   QRegs<GE::KK> qop;
   int qowner = -1;          // index of the step whose q sits in qnext
+  AppendRegs<D, KVT> anext;
+  int aowner = -1;          // index of the step whose new token sits in anext
   int issued = 0;
 
   // Issue the step at the cursor into buffer r, then advance the cursor.
   // `done` = index of the oldest step not yet computed.  Past the end of the
   // range the loads still happen (see issue_chunks) but nothing is consumed.
-  auto issue = [&](SplitBuf<D, KVT>& r, StepMeta& m, int done) {
+  auto issue = [&](SplitBuf<D, KVT>& r, StepMeta& m, int done) __attribute__((always_inline)) {
     const bool live = issued < nsteps;
     const int g = cur.xi / p.QT;
     const int qt = cur.xi - g * p.QT;
@@ -961,7 +1182,18 @@ __global__ __launch_bounds__(kWave * kNW) void pa_split_kernel(const SplitParams
     m.slot = (cur.s * p.HQ + cur.xi) * p.NP + (cur.j * TS) / p.P + w;
     m.qs = cur.s;
     m.qh0 = h0;
+    m.ag = g;
+    m.aphys0 = cur.phys[0];
+    m.aphys1 = cur.phys[TS > 16 ? 1 : 0];
     int f = (last || row_end || part_end) ? kFlush : 0;
+    if (live && row_end && p.new_k) {   // the step holding token ctx - 1
+      f |= kAppend;
+      if (aowner < done) {
+        anext = load_append<D, KVT>(p, cur.s, g, lane);
+        aowner = issued;
+        f |= kAReady;
+      }
+    }
     if (live && (cur.j == 0 || issued == 0)) {
       f |= kNewRow;
       if (qowner < done) {       // qnext is free: prefetch this row's q
@@ -995,7 +1227,7 @@ __global__ __launch_bounds__(kWave * kNW) void pa_split_kernel(const SplitParams
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  auto consume = [&](const SplitBuf<D, KVT>& r, const StepMeta& m) {
+  auto consume = [&](SplitBuf<D, KVT>& r, const StepMeta& m) __attribute__((always_inline)) {
     if (m.flags & kNewRow) {
       if (m.flags & kQReady) {
         qop = qnext;
@@ -1008,7 +1240,18 @@ __global__ __launch_bounds__(kWave * kNW) void pa_split_kernel(const SplitParams
         wait_vm_all();
       }
     }
+    const int tt = m.t_end - 1 - m.t0;
+    if (m.flags & kAppend) {
+      if (m.flags & kAReady) {
+        patch_append<D, KVT>(r, anext, p, tt, lane);
+      } else {   // as for q: a direct load, waited for here
+        const AppendRegs<D, KVT> a = load_append<D, KVT>(p, m.qs, m.ag, lane);
+        wait_vm_all();
+        patch_append<D, KVT>(r, a, p, tt, lane);
+      }
+    }
     compute_step<D, KVT>(r, qop, p, m.t0, m.t_end, lane, m_run, l_run, acc);
+    if (m.flags & kAppend) writeback_append<D, KVT, B>(r, p, m.aphys0, m.aphys1, m.ag, m.t0, tt, lane);
     if (m.flags & kFlush) {
       const float l = sum_x32(sum_x16(l_run));
       const int gt = min(16, p.G - (m.qh0 % p.G));
@@ -1031,15 +1274,21 @@ __global__ __launch_bounds__(kWave * kNW) void pa_split_kernel(const SplitParams
   // ---- pipeline: NBUF - 1 steps of loads in flight ahead of the one computed.
   // Every step issues the same loads (live or not) so the wait before each
   // compute only covers that step's loads.
-#pragma unroll
-  for (int bb = 0; bb < NBUF - 1; ++bb) issue(buf[bb], meta[bb], 0);
+  // (the buffer indices must be compile-time constants, or the buffers move
+  // to scratch memory: the steps are expanded from an index sequence rather
+  // than left to loop unrolling)
+  static_for<NBUF - 1>([&](auto bbc) {
+    constexpr int bb = decltype(bbc)::value;
+    issue(buf[bb], meta[bb], 0);
+  });
   for (int base = 0; base < nsteps; base += NBUF) {
-#pragma unroll
-    for (int bb = 0; bb < NBUF; ++bb) {
+    static_for<NBUF>([&](auto bbc) {
+      constexpr int bb = decltype(bbc)::value;
+      constexpr int nb = (bb + NBUF - 1) % NBUF;
       const int idx = base + bb;
-      issue(buf[(bb + NBUF - 1) % NBUF], meta[(bb + NBUF - 1) % NBUF], idx);
+      issue(buf[nb], meta[nb], idx);
       if (idx < nsteps) consume(buf[bb], meta[bb]);
-    }
+    });
   }
 
   // ---- report the rows this range touched; the wave completing a row merges it
@@ -1093,13 +1342,13 @@ hipError_t launch_single_kv(const DecodeParams& p, int kvt, int B, int grid, hip
 
 // Steps of K/V registers per wave: one computed, the rest in flight (about
 // 40 KB per wave, 160 KB per CU with one wave per SIMD).
-template <int D>
-constexpr int split_nbuf() { return D == 128 ? 6 : 8; }
+template <int D, int KVT>
+constexpr int split_nbuf() { return D == 64 ? 8 : (KVT == PKV_KV_INT8 ? 5 : 6); }
 constexpr int kMaxBlocksPerCU = 1;       // persistent grid: one workgroup (a wave per SIMD) per CU
 
 template <int D, int KVT, int B>
 const void* split_fn() {
-  return reinterpret_cast<const void*>(&pa_split_kernel<D, KVT, B, split_nbuf<D>()>);
+  return reinterpret_cast<const void*>(&pa_split_kernel<D, KVT, B, split_nbuf<D, KVT>()>);
 }
 
 const void* split_kernel_fn(int D, int kvt, int B) {
@@ -1190,7 +1439,7 @@ bool split_sizes(int32_t S, int32_t Hq, int32_t Hkv_or_0, int32_t D, int32_t W, 
 
 template <int D, int KVT, int B>
 void launch_split_t(const SplitParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((pa_split_kernel<D, KVT, B, split_nbuf<D>()>), dim3(grid), dim3(kWave * kNW), 0, stream, p);
+  hipLaunchKernelGGL((pa_split_kernel<D, KVT, B, split_nbuf<D, KVT>()>), dim3(grid), dim3(kWave * kNW), 0, stream, p);
 }
 
 template <int D>
@@ -1227,12 +1476,14 @@ extern "C" uint64_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_h
   return (uint64_t)(z.cnt_bytes + z.ml_bytes + z.acc_bytes);
 }
 
-extern "C" pkv_status paged_attn_decode(float* out, const void* q, const pkv_pool* pool, int32_t layer,
-                                        const int32_t* block_tables, int32_t table_width,
-                                        const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                                        float scale, int32_t kv_dtype, const pkv_kv_scales* kv_scales,
-                                        int32_t partition_size, void* workspace, uint64_t workspace_bytes,
-                                        hipStream_t stream) {
+namespace {
+
+pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t layer, const void* key,
+                       const void* value, const int32_t* block_tables, int32_t table_width,
+                       const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                       int32_t kv_dtype, const pkv_kv_scales* kv_scales, int32_t partition_size, void* workspace,
+                       uint64_t workspace_bytes, hipStream_t stream) {
+  const bool append = key != nullptr || value != nullptr;
   pkv_status st = check_pool(pool);
   if (st != PKV_OK) return st;
   const pkv_pool_config& c = pool->cfg;
@@ -1247,6 +1498,11 @@ extern "C" pkv_status paged_attn_decode(float* out, const void* q, const pkv_poo
   if (num_seqs < 0) return fail(PKV_ERR_INVALID, "num_seqs is negative");
   if (num_seqs == 0) { clear_error(); return PKV_OK; }
   if (!out || !q || !block_tables || !context_lens) return fail(PKV_ERR_INVALID, "NULL device pointer");
+  if (append && (!key || !value)) return fail(PKV_ERR_INVALID, "key and value must both be given");
+  if (append && partition_size == 0)
+    return fail(PKV_ERR_UNSUPPORTED, "the appending decode runs in the split-context form (partition_size > 0)");
+  if (append && ((uintptr_t)key % 16 || (uintptr_t)value % 16))
+    return fail(PKV_ERR_INVALID, "key and value must be 16-byte aligned");
   if (num_q_heads <= 0 || num_q_heads % c.num_kv_heads != 0) {
     set_error("num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads, c.num_kv_heads);
     return PKV_ERR_INVALID;
@@ -1274,10 +1530,10 @@ extern "C" pkv_status paged_attn_decode(float* out, const void* q, const pkv_poo
   const int32_t QT = (G + 15) / 16;
   const int64_t rows = (int64_t)num_seqs * c.num_kv_heads * QT;
   const uint64_t scale_layer = (uint64_t)c.num_blocks * c.num_kv_heads * c.block_size;
-  const char* kl = static_cast<const char*>(pool->k) + (uint64_t)layer * pool->layer_bytes;
-  const char* vl = static_cast<const char*>(pool->v) + (uint64_t)layer * pool->layer_bytes;
-  const float* ksl = pool->k_scale ? pool->k_scale + layer * scale_layer : nullptr;
-  const float* vsl = pool->v_scale ? pool->v_scale + layer * scale_layer : nullptr;
+  char* kl = static_cast<char*>(pool->k) + (uint64_t)layer * pool->layer_bytes;
+  char* vl = static_cast<char*>(pool->v) + (uint64_t)layer * pool->layer_bytes;
+  float* ksl = pool->k_scale ? pool->k_scale + layer * scale_layer : nullptr;
+  float* vsl = pool->v_scale ? pool->v_scale + layer * scale_layer : nullptr;
 
   hipError_t e = hipSuccess;
   if (partition_size == 0) {
@@ -1338,6 +1594,10 @@ extern "C" pkv_status paged_attn_decode(float* out, const void* q, const pkv_poo
     p.vs = vsl;
     p.bt = block_tables;
     p.ctx = context_lens;
+    p.new_k = static_cast<const uint16_t*>(key);
+    p.new_v = static_cast<const uint16_t*>(value);
+    p.enc_k = ksc;
+    p.enc_v = vsc;
     char* ws = static_cast<char*>(workspace);
     p.row_done = reinterpret_cast<uint64_t*>(ws);
     p.part_ml = reinterpret_cast<float*>(ws + z.cnt_bytes);
@@ -1366,4 +1626,28 @@ extern "C" pkv_status paged_attn_decode(float* out, const void* q, const pkv_poo
   }
   clear_error();
   return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" pkv_status paged_attn_decode(float* out, const void* q, const pkv_pool* pool, int32_t layer,
+                                        const int32_t* block_tables, int32_t table_width,
+                                        const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                        float scale, int32_t kv_dtype, const pkv_kv_scales* kv_scales,
+                                        int32_t partition_size, void* workspace, uint64_t workspace_bytes,
+                                        hipStream_t stream) {
+  return decode_impl(out, q, pool, layer, nullptr, nullptr, block_tables, table_width, context_lens, num_seqs,
+                     num_q_heads, scale, kv_dtype, kv_scales, partition_size, workspace, workspace_bytes, stream);
+}
+
+extern "C" pkv_status paged_attn_decode_append(float* out, const void* q, const pkv_pool* pool, int32_t layer,
+                                               const void* key, const void* value, const int32_t* block_tables,
+                                               int32_t table_width, const int32_t* context_lens,
+                                               int32_t num_seqs, int32_t num_q_heads, float scale,
+                                               int32_t kv_dtype, const pkv_kv_scales* kv_scales,
+                                               int32_t partition_size, void* workspace,
+                                               uint64_t workspace_bytes, hipStream_t stream) {
+  if (!key || !value) return fail(PKV_ERR_INVALID, "key and value must be non-NULL");
+  return decode_impl(out, q, pool, layer, key, value, block_tables, table_width, context_lens, num_seqs,
+                     num_q_heads, scale, kv_dtype, kv_scales, partition_size, workspace, workspace_bytes, stream);
 }

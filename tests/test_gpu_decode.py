@@ -298,6 +298,87 @@ def test_split_long_rows_spread_over_many_waves(dt):
         check(c, P, f"long rows dt={dt} P={P}")
 
 
+# ----------------------------------------------------------------------- appending decode
+def _append_and_compare(rng, ctx, hkv, G, D, B, dt, P, label):
+    # one launch that stores each sequence's new token and decodes over it
+    # must leave the same pool bytes and give the same output bits as
+    # reshape_and_cache followed by paged_attn_decode; both match the oracle
+    import torch
+    say(label)
+    ctx = [int(x) for x in ctx]
+    S = len(ctx)
+    hist = [max(x - 1, 0) for x in ctx]
+    ks, vs = (0.75, 1.25) if dt == pkv.PKV_KV_FP8_E5M2 else (1.0, 1.0)
+    c = build_case(rng, S, hkv, G, D, B, dt, hist, ks, vs, spare=S + 2, poison=True,
+                   width=max(1, math.ceil(max(ctx) / B)))
+    # the new token of each sequence lands at position ctx - 1 of its table;
+    # a block the history does not reach comes from the spare blocks
+    used = set(int(c.tables[s, i]) for s in range(S) for i in range(math.ceil(hist[s] / B)))
+    free = [b for b in range(c.cfg.num_blocks) if b not in used]
+    for s in range(S):
+        for i in range(math.ceil(hist[s] / B), math.ceil(ctx[s] / B)):
+            c.tables[s, i] = free.pop()
+    c.ctx = np.asarray(ctx, np.int32)
+    c.d_ctx = dev(c.ctx)
+    c.d_tables = dev(c.tables)
+    kn = workloads.to_bf16_bits(rng.standard_normal((S, hkv, D), dtype=np.float32) * 2)
+    vn = workloads.to_bf16_bits(rng.standard_normal((S, hkv, D), dtype=np.float32))
+    slots = np.array([attention.slot_of(c.tables[s], ctx[s] - 1, B) if ctx[s] else -1 for s in range(S)],
+                     np.int64)
+    before = c.pool.memory.clone()
+    pkv.reshape_and_cache(c.pool, 0, bf16_dev(kn), bf16_dev(vn), dev(slots), k_scale=ks, v_scale=vs)
+    got_a, scale = run_decode(c, P)
+    pool_a = c.pool.memory.clone()
+    c.pool.memory.copy_(before)
+    out = torch.full((S, c.hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.randint(0, 256, (pkv.paged_attn_workspace_bytes(S, c.hq, D, c.width, B, P),),
+                       dtype=torch.uint8, device="cuda")
+    pkv.paged_attn_decode_append(out, c.d_q, c.pool, 0, bf16_dev(kn), bf16_dev(vn), c.d_tables, c.d_ctx, scale,
+                                 dt, ks, vs, P, ws)
+    torch.cuda.synchronize()
+    got_b = out.cpu().numpy()
+    assert torch.equal(pool_a, c.pool.memory), f"{label}: pool bytes differ from the two-call step"
+    assert np.array_equal(got_a.view(np.uint32), got_b.view(np.uint32)), f"{label}: outputs differ"
+    keep = slots >= 0
+    img = cache_ops.reshape_and_cache(c.img, 0, kn[keep], vn[keep], slots[keep], ks, vs)
+    want = attention.paged_decode(c.q, img, 0, c.tables, c.ctx, scale, ks, vs)
+    mx, rel = errors(got_b, want)
+    say(f"{label}: max_abs={mx:.3e} rel={rel:.3e}")
+    assert mx <= BAR[dt][0] and rel <= BAR[dt][1]
+    assert not got_b[c.ctx == 0].any()
+
+
+@pytest.mark.parametrize("dt", [pkv.PKV_KV_BF16, pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8])
+@pytest.mark.parametrize("D,B,P", [(128, 16, 64), (128, 32, 512), (64, 16, 32), (64, 32, 4096)])
+def test_decode_append_equals_cache_write_then_decode(dt, D, B, P):
+    rng = np.random.default_rng(8100 + 10 * dt + D + B)
+    hkv, G = (2, 4) if D == 128 else (1, 3)
+    _append_and_compare(rng, [1, 2, 15, 16, 17, 31, 32, 33, 100, 257, 0, 600], hkv, G, D, B, dt, P,
+                        f"decode_append dt={dt} D={D} B={B} P={P}")
+
+
+@pytest.mark.parametrize("dt", [pkv.PKV_KV_BF16, pkv.PKV_KV_INT8])
+def test_decode_append_many_short_rows(dt):
+    # the appended token often sits in a row that starts inside the prefetch
+    # window of the previous one
+    rng = np.random.default_rng(8300 + dt)
+    ctx = rng.integers(0, 41, size=300)
+    ctx[::7] = 0
+    for P in (32, 64):
+        _append_and_compare(rng, ctx, 2, 3, 64, 16, dt, P, f"decode_append short rows dt={dt} P={P}")
+
+
+def test_decode_append_needs_split_form():
+    import torch
+    rng = np.random.default_rng(8200)
+    c = build_case(rng, 2, 2, 2, 128, 16, pkv.PKV_KV_BF16, [10, 20])
+    out = torch.empty((2, 4, 128), dtype=torch.float32, device="cuda")
+    kn = bf16_dev(np.zeros((2, 2, 128), np.uint16))
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.paged_attn_decode_append(out, c.d_q, c.pool, 0, kn, kn, c.d_tables, c.d_ctx, 0.1)
+    assert e.value.status == pkv.PKV_ERR_UNSUPPORTED
+
+
 # ----------------------------------------------------------------------- exhaustive codes
 def test_every_fp8_code_decodes_exactly():
     # context 1 returns the token's dequantised V exactly: V holds all 256 codes
