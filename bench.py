@@ -2,9 +2,11 @@
 
 A step is the whole hot path over one batch: the host block manager appends
 one token to each of the 100 sequences (slots, any copy-on-write pairs,
-tables), the tables / lengths / slots are uploaded, then for each of the 80
-layers the new token's K/V is written into its slot and paged decode
-attention runs over every sequence's ~4K-token history (split-context form).
+tables), the tables / lengths are uploaded, then for each of the 80 layers
+one launch writes the new token's K/V into its slot and runs paged decode
+attention over every sequence's ~4K-token history (split-context form,
+paged_attn_decode_append).  --separate-cache-write times the two-call form
+instead (reshape_and_cache, then paged_attn_decode, per layer).
 
 Workload (synthetic, seeded): 80 layers, 64 query / 8 KV heads, head_dim 128,
 bf16, 16-token blocks, 100 sequences with contexts ~N(4096, 256) clipped to
@@ -13,9 +15,9 @@ blocks needed (+ room for the appended tokens).  Cached K/V are N(0, 1)
 draws made on the device.
 
 Prints one JSON line: KV-read GB/s (whole step), seq-steps/s, % of the MI355X
-HBM peak, a roofline entry for the decode kernels (HIP events around every
-decode call of the timed steps), and the fp64 CPU oracle timed on a bounded
-sample of the same workload.
+HBM peak, a roofline entry for the decode kernel (HIP events around each timed
+step's decode launches), and the fp64 CPU oracle timed on a bounded sample of
+the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--partition P]
 """
@@ -52,6 +54,8 @@ def parse():
                     help="layers per step (the workload has 80; fewer only for quick experiments)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-cache-write", action="store_true",
+                    help="per layer, reshape_and_cache then paged_attn_decode (two launches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB three times (torch copy kernel): the reference for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -155,28 +159,51 @@ def main():
     kv_bytes = []
     dec_events = []
 
+    separate = args.separate_cache_write
+
+    def decode(layer):
+        if separate:
+            pkv.paged_attn_decode(out, q[layer], pool, layer, d_tab, d_ctx, scale, partition_size=P,
+                                  workspace=ws, stream=stream)
+        else:
+            pkv.paged_attn_decode_append(out, q[layer], pool, layer, newk[layer], newv[layer], d_tab, d_ctx,
+                                         scale, partition_size=P, workspace=ws, stream=stream)
+
     def step(i, timed):
         b = i % 2
         h_done[b].synchronize()                       # staging buffer b is free again
         slots, pairs = bm.append(seqs)
         assert pairs.shape[0] == 0                    # no sharing in this workload
         bm.block_tables(seqs, W, out=h_tab[b].numpy(), ctx_out=h_ctx[b].numpy())
-        h_slot[b].numpy()[:] = slots
         d_tab.copy_(h_tab[b], non_blocking=True)
         d_ctx.copy_(h_ctx[b], non_blocking=True)
-        d_slot.copy_(h_slot[b], non_blocking=True)
+        if separate:
+            h_slot[b].numpy()[:] = slots
+            d_slot.copy_(h_slot[b], non_blocking=True)
         h_done[b].record(stream)
-        kv_bytes.append(int(h_ctx[b].numpy().astype(np.int64).sum()) * Hkv * 2 * D * 2 * L)
+        ctx_sum = int(h_ctx[b].numpy().astype(np.int64).sum())
+        kv_bytes.append(ctx_sum * Hkv * 2 * D * 2 * L)
+        # HIP events on the launch stream.  A timing event between two launches
+        # costs ~10 us of idle GPU (the next launch no longer follows the
+        # previous one directly), so the appending form, whose 80 decode
+        # launches run back to back with nothing else between them, is
+        # bracketed once per step; the two-call form per decode call.
+        if timed and not separate:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
         for layer in range(L):
-            pkv.reshape_and_cache(pool, layer, newk[layer], newv[layer], d_slot, stream=stream)
-            if timed:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-            pkv.paged_attn_decode(out, q[layer], pool, layer, d_tab, d_ctx, scale, partition_size=P,
-                                  workspace=ws, stream=stream)
-            if timed:
-                e1.record(stream)
-                dec_events.append((e0, e1, int(h_ctx[b].numpy().astype(np.int64).sum())))
+            if separate:
+                pkv.reshape_and_cache(pool, layer, newk[layer], newv[layer], d_slot, stream=stream)
+                if timed:
+                    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    c0.record(stream)
+            decode(layer)
+            if timed and separate:
+                c1.record(stream)
+                dec_events.append((c0, c1, ctx_sum, 1))
+        if timed and not separate:
+            e1.record(stream)
+            dec_events.append((e0, e1, ctx_sum, L))
 
     for i in range(args.warmup):
         step(i, False)
@@ -192,8 +219,10 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     kv_per_step = sum(kv_bytes) / args.steps
     gbs = sum(kv_bytes) / elapsed / 1e9
-    dec_ms = [e0.elapsed_time(e1) for e0, e1, _ in dec_events]
-    dec_bytes = [n * Hkv * 2 * D * 2 for _, _, n in dec_events]
+    dec_ms = [e0.elapsed_time(e1) / n for e0, e1, _, n in dec_events]
+    # per call: every context token's K and V once; the appending form also
+    # writes the new token's K and V
+    dec_bytes = [(c + (0 if separate else S)) * Hkv * 2 * D * 2 for _, _, c, _ in dec_events]
     avg_dec_ms = float(np.mean(dec_ms))
     avg_dec_bytes = float(np.mean(dec_bytes))
     achieved = avg_dec_bytes / (avg_dec_ms * 1e-3) / 1e9
@@ -204,8 +233,9 @@ def main():
     cpu = None
     parity = None
     if not args.no_cpu_baseline:
-        cpu, parity = cpu_baseline(args, pkv, w, pool, bm, q, out, ws, d_tab, d_ctx, scale, P, stream)
+        cpu, parity = cpu_baseline(args, pkv, w, pool, decode, q, out, d_tab, d_ctx, scale)
 
+    call = "paged_attn_decode" if separate else "paged_attn_decode_append"
     res = {
         "metric": "paged decode KV-read GB/s (% of MI355X HBM peak) + decode seq-steps/s",
         "value": round(gbs, 2),
@@ -222,11 +252,13 @@ def main():
         "config": {"workload": "70B-shaped paged decode step: 80 layers x 100 seqs x ~4K ctx, "
                                "64q/8kv heads, head_dim 128, bf16 KV, block 16",
                    "layers": L, "seqs": S, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
-                   "block_size": B, "partition_size": P, "kv_bytes_per_step": int(kv_per_step)},
+                   "block_size": B, "partition_size": P, "kv_bytes_per_step": int(kv_per_step),
+                   "layer_calls": ("reshape_and_cache + paged_attn_decode" if separate
+                                   else "paged_attn_decode_append")},
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(S / (elapsed / args.steps), 1),
         "seq_tokens_per_s": round(kv_per_step / (Hkv * 2 * D * 2 * L) / (elapsed / args.steps), 1),
-        "roofline": {"bound": "hbm", "kernel": "pa_split_kernel (the one launch of a split-context paged_attn_decode call)",
+        "roofline": {"bound": "hbm", "kernel": f"pa_split_kernel (the one launch of a split-context {call} call)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
@@ -237,55 +269,58 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(args, pkv, w, pool, bm, q, out, ws, d_tab, d_ctx, scale, P, stream):
-    """Time the fp64 oracle on a bounded sample (layer 0, as many sequences as
-    fit the time budget) and check the GPU's layer-0 output on that sample."""
+def cpu_baseline(args, pkv, w, pool, decode, q, out, d_tab, d_ctx, scale):
+    """Time the fp64 oracle on a bounded sample (layer after layer, sequence by
+    sequence, until the time budget is spent) and check the GPU's output of
+    each sampled layer on that sample.  The GPU call is the timed step's own
+    (the appending form writes the last step's token again, the same bytes)."""
     import torch
     from threadpoolctl import threadpool_info
 
     from oracle import attention, layout
 
     S, Hq, Hkv, D, B, W = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.table_width
-    layer = 0
-    pkv.paged_attn_decode(out, q[layer], pool, layer, d_tab, d_ctx, scale, partition_size=P, workspace=ws,
-                          stream=stream)
-    torch.cuda.synchronize()
-    gpu_out = out.cpu().numpy()
     tabs = d_tab.cpu().numpy()
     ctxs = d_ctx.cpu().numpy()
-    qbits = q[layer].view(torch.int16).cpu().numpy().view(np.uint16)
     k_off, v_off, _, _ = pool.region_offsets()
     tile = pool.desc.tile_bytes
     rng = np.random.default_rng(436)
-    order = rng.permutation(S)
-    spent, done, worst = 0.0, [], 0.0
-    for s in order:
-        n = int(ctxs[s])
-        nblk = math.ceil(n / B)
-        blocks = tabs[s, :nblk]
-        # copy this sequence's tiles of layer 0 to the host as a small pool
-        sub = layout.PoolShape(1, nblk, B, Hkv, D)
-        img = layout.empty_image(sub)
-        idx = torch.from_numpy(blocks.astype(np.int64)).to(pool.memory.device)
-        for region, dst in ((k_off, img.k), (v_off, img.v)):
-            lay = pool.memory[region: region + pool.desc.layer_bytes].view(w.num_blocks, Hkv * tile)
-            dst[:] = lay.index_select(0, idx).cpu().numpy().view(np.uint16).reshape(-1)
-        local = np.arange(nblk, dtype=np.int32)
-        t0 = time.perf_counter()
-        ref = attention.paged_decode(qbits[s:s + 1], img, 0, local[None, :], np.array([n]), scale)
-        spent += time.perf_counter() - t0
-        done.append(n)
-        worst = max(worst, float(np.max(np.abs(gpu_out[s] - ref[0]))))
+    spent, done, worst, layers = 0.0, [], 0.0, 0
+    for layer in range(args.layers):
+        decode(layer)
+        torch.cuda.synchronize()
+        gpu_out = out.cpu().numpy()
+        qbits = q[layer].view(torch.int16).cpu().numpy().view(np.uint16)
+        layers += 1
+        for s in rng.permutation(S):
+            n = int(ctxs[s])
+            nblk = math.ceil(n / B)
+            # copy this sequence's tiles of the layer to the host as a small pool
+            sub = layout.PoolShape(1, nblk, B, Hkv, D)
+            img = layout.empty_image(sub)
+            idx = torch.from_numpy(tabs[s, :nblk].astype(np.int64)).to(pool.memory.device)
+            for region, dst in ((k_off, img.k), (v_off, img.v)):
+                base = region + layer * pool.desc.layer_bytes
+                lay = pool.memory[base: base + pool.desc.layer_bytes].view(w.num_blocks, Hkv * tile)
+                dst[:] = lay.index_select(0, idx).cpu().numpy().view(np.uint16).reshape(-1)
+            local = np.arange(nblk, dtype=np.int32)
+            t0 = time.perf_counter()
+            ref = attention.paged_decode(qbits[s:s + 1], img, 0, local[None, :], np.array([n]), scale)
+            spent += time.perf_counter() - t0
+            done.append(n)
+            worst = max(worst, float(np.max(np.abs(gpu_out[s] - ref[0]))))
+            if spent >= args.cpu_seconds:
+                break
         if spent >= args.cpu_seconds:
             break
     threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
     bytes_done = sum(done) * Hkv * 2 * D * 2
     cpu = {"value": round(bytes_done / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
            "kind": "oracle",
-           "sample": f"layer 0 of the same step, {len(done)} of {S} sequences ({sum(done)} tokens), "
-                     f"{spent:.1f} s of fp64 numpy decode (gather + softmax attention)",
+           "sample": f"{len(done)} (sequence, layer) decodes of the same step over {layers} layer(s), "
+                     f"{sum(done)} tokens, {spent:.1f} s of fp64 numpy decode (gather + softmax attention)",
            "host_cpus": len(os.sched_getaffinity(0))}
-    parity = {"seqs_checked": len(done), "max_abs_err": worst, "bar": 1e-2}
+    parity = {"decodes_checked": len(done), "max_abs_err": worst, "bar": 1e-2}
     log(f"cpu oracle: {cpu['value']} GB/s on {threads} threads; parity max abs err {worst:.2e}")
     return cpu, parity
 
