@@ -468,6 +468,7 @@ struct SplitParams {
   float* part_acc;            // workspace: [slots][NC][64 lanes][4]
   int32_t W, S, Hq, Hkv, G, QT, HQ, num_blocks;
   int32_t P;                  // partition size (tokens, multiple of 32)
+  int32_t PS;                 // steps per partition: P / tokens per step
   int32_t NP;                 // partitions per row: ceil(W * B / P)
   int32_t NWV;                // waves in the grid
   uint32_t epoch;             // this call's tag for row_done
@@ -497,19 +498,12 @@ struct SplitBuf {
 // Wave-uniform description of one issued step.
 struct StepMeta {
   int t0;       // first token of the step within its row
-  int t_end;    // row's context length
+  int t_end;    // row's context length (0 for a step past the wave's range)
   int slot;     // partial slot of the step's segment
-  int flags;    // kNewRow | kQReady | kFlush | kAppend | kAReady
-  int qs, qh0;  // sequence and first head of the row (for a direct q load)
-  int ag;       // KV head of the row
-  int aphys0;   // appending: physical blocks of the step's two 16-token chunks
-  int aphys1;
+  int flags;    // kNewRow | kFlush, and the row's query heads (<= 16) from bit 8
 };
-constexpr int kNewRow = 1;   // first step of a row in this wave: load the row's q
-constexpr int kQReady = 2;   // ... and that q was prefetched into qnext
-constexpr int kFlush = 4;    // last step of a segment: write the partial
-constexpr int kAppend = 8;   // appending decode, the row's last step: holds the new token
-constexpr int kAReady = 16;  // ... and its K/V input was prefetched into anext
+constexpr int kNewRow = 1;   // first step of a row in this wave: its q was loaded with the step
+constexpr int kFlush = 2;    // last step of a segment: write the partial
 
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
@@ -584,200 +578,96 @@ __device__ __forceinline__ void issue_chunks(SplitBuf<D, KVT>& r, const SplitPar
   }
 }
 
-// ---- appending decode: the new token of a row enters through registers.
-// The wave that computes a row's last step loads the new token's K and V
-// (bf16 input), stores them into its K/V registers in the tile layout, encoded
-// exactly as the cache write would store them, computes the step, and writes
-// those register pieces back to the pool.  No other wave of the launch reads
-// the bytes it writes: the token's block is not shared (copy-on-write happens
-// before the append) and the rest of its tile belongs to other steps.
-
-// The new token's input values a lane needs, laid out like its registers.
-template <int D, int KVT>
-struct AppendRegs {
-  using GE = SplitGeo<D, KVT>;
-  static constexpr int KIN = GE::E == 2 ? GE::LPC : 2 * GE::LPC;   // 16-byte loads for the K pieces
-  u32x4 k[KIN];
-  u32x2 v[GE::LPC];     // bf16 storage: .x holds dims (d, d+1); 8-bit: 4 dims
-};
-
-template <int D, int KVT>
-__device__ __forceinline__ AppendRegs<D, KVT> load_append(const SplitParams& p, int s, int g, int lane) {
-  using GE = SplitGeo<D, KVT>;
-  const int row = lane & 15;
-  const int j = lane >> 4;
-  const uint16_t* kx = p.new_k + ((int64_t)s * p.Hkv + g) * D;
-  const uint16_t* vx = p.new_v + ((int64_t)s * p.Hkv + g) * D;
-  AppendRegs<D, KVT> a;
-  if constexpr (GE::E == 2) {
+// ---- appending decode.  Before streaming its range, a wave stores the new
+// token (position ctx - 1) of every row whose last step lies in that range,
+// encoded exactly as reshape_and_cache stores it.  The wave reads that tile
+// again at the row's last step, and one wave's accesses to an address are
+// performed in order, so the decode sees the token.  No other wave reads
+// those bytes: the token's block is not shared (copy-on-write runs before the
+// append), the rest of its tile belongs to other steps, and when a KV head
+// has several 16-head rows, each of their last-step waves stores the same
+// bytes itself before reading them.  Stores cover the token's bytes only.
+__device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
-    for (int u = 0; u < GE::LPC; ++u) {
-      a.k[u] = *reinterpret_cast<const u32x4*>(kx + 8 * (4 * u + j));            // dims of piece 4u + j
-      a.v[u] = u32x2{*reinterpret_cast<const uint32_t*>(vx + 32 * u + 2 * row), 0u};  // dims 32u + 2row, +1
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < GE::LPC; ++u) {
-      a.k[2 * u] = *reinterpret_cast<const u32x4*>(kx + 16 * (4 * u + j));       // dims 16(4u+j) .. +7
-      a.k[2 * u + 1] = *reinterpret_cast<const u32x4*>(kx + 16 * (4 * u + j) + 8);  // .. +15
-      a.v[u] = *reinterpret_cast<const u32x2*>(vx + 64 * u + 4 * row);           // dims 64u + 4row .. +3
-    }
-  }
-  return a;
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
 }
-
 __device__ __forceinline__ uint32_t half_of(uint32_t w, int i) { return i ? (w >> 16) : (w & 0xffffu); }
 __device__ __forceinline__ float abs_bf16(uint32_t b) { return fabsf(bf16_bits_to_float(b & 0xffffu)); }
 
-// Put token tt (0 <= tt < TS) of the step, taken from `a`, into chunk H of r
-// (the chunk is a template argument so every register index stays static).
-template <int H, int D, int KVT>
-__device__ __forceinline__ void patch_chunk(SplitBuf<D, KVT>& r, const AppendRegs<D, KVT>& a, const SplitParams& p,
-                                            int tt, float sk, float sv, int lane) {
-  using GE = SplitGeo<D, KVT>;
-  const int row = lane & 15;
-  const int j = lane >> 4;
-  // position of the token in chunk H: outside [0, 16) when another chunk
-  // holds it, and then no lane matches below
-  const int rt = tt - 16 * H, jj = rt >> 2, ii = rt & 3;
-  if (row == rt) {                                 // K: this lane's pieces are the token's
-#pragma unroll
-    for (int u = 0; u < GE::LPC; ++u) {
-      if constexpr (GE::E == 2) {
-        r.k[H][u] = a.k[u];
-      } else {
-        u32x4 w;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {           // output dword q4 = input dims 4q4 .. 4q4+3
-          const u32x4 src = a.k[2 * u + (q4 >> 1)];
-          const uint32_t x0 = src[(q4 & 1) * 2], x1 = src[(q4 & 1) * 2 + 1];
-          uint32_t b0, b1, b2, b3;
-          if constexpr (KVT == PKV_KV_FP8_E5M2) {
-            b0 = fp8_store(half_of(x0, 0), p.enc_k);
-            b1 = fp8_store(half_of(x0, 1), p.enc_k);
-            b2 = fp8_store(half_of(x1, 0), p.enc_k);
-            b3 = fp8_store(half_of(x1, 1), p.enc_k);
-          } else {
-            b0 = int8_store(half_of(x0, 0), sk);
-            b1 = int8_store(half_of(x0, 1), sk);
-            b2 = int8_store(half_of(x1, 0), sk);
-            b3 = int8_store(half_of(x1, 1), sk);
-          }
-          w[q4] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-        }
-        r.k[H][u] = w;
-      }
-    }
-  }
-  if (j == jj) {                                   // V: token ii of this lane's group
-#pragma unroll
-    for (int u = 0; u < GE::LPC; ++u) {
-      if constexpr (GE::E == 2) {
-        const uint32_t nv = a.v[u][0];             // dims d (low half), d + 1 (high half)
-        const int sh = (ii & 1) * 16;
-        const uint32_t keep = ~(0xffffu << sh);
-        // dword ii/2 holds dim d, dword 2 + ii/2 dim d + 1 (two tokens each)
-        const uint32_t lo = (ii >> 1) ? r.v[H][u][1] : r.v[H][u][0];
-        const uint32_t hi = (ii >> 1) ? r.v[H][u][3] : r.v[H][u][2];
-        const uint32_t nlo = (lo & keep) | (half_of(nv, 0) << sh);
-        const uint32_t nhi = (hi & keep) | (half_of(nv, 1) << sh);
-        r.v[H][u][0] = (ii >> 1) ? r.v[H][u][0] : nlo;
-        r.v[H][u][1] = (ii >> 1) ? nlo : r.v[H][u][1];
-        r.v[H][u][2] = (ii >> 1) ? r.v[H][u][2] : nhi;
-        r.v[H][u][3] = (ii >> 1) ? nhi : r.v[H][u][3];
-      } else {
-        const int sh = ii * 8;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {              // dword e = dim 64u + 4row + e
-          const uint32_t x = half_of(a.v[u][e >> 1], e & 1);
-          const uint32_t b = KVT == PKV_KV_FP8_E5M2 ? fp8_store(x, p.enc_v) : int8_store(x, sv);
-          r.v[H][u][e] = (r.v[H][u][e] & ~(0xffu << sh)) | (b << sh);
-        }
-      }
-    }
-    if constexpr (KVT == PKV_KV_INT8) {
-      r.ksc[H][0] = ii == 0 ? sk : r.ksc[H][0];
-      r.ksc[H][1] = ii == 1 ? sk : r.ksc[H][1];
-      r.ksc[H][2] = ii == 2 ? sk : r.ksc[H][2];
-      r.ksc[H][3] = ii == 3 ? sk : r.ksc[H][3];
-      r.vsc[H][0] = ii == 0 ? sv : r.vsc[H][0];
-      r.vsc[H][1] = ii == 1 ? sv : r.vsc[H][1];
-      r.vsc[H][2] = ii == 2 ? sv : r.vsc[H][2];
-      r.vsc[H][3] = ii == 3 ? sv : r.vsc[H][3];
-    }
-  }
-}
-
-// Put token tt (0 <= tt < TS) of the step, taken from `a`, into r.
-template <int D, int KVT>
-__device__ __forceinline__ void patch_append(SplitBuf<D, KVT>& r, const AppendRegs<D, KVT>& a, const SplitParams& p,
-                                             int tt, int lane) {
-  using GE = SplitGeo<D, KVT>;
-  float sk = 0.f, sv = 0.f;   // int8 scales of the token
-  if constexpr (KVT == PKV_KV_INT8) {
-    // every lane with the same j holds the same K dims, every lane with the
-    // same row the same V dims: reduce over j for K and over row for V
-    float mk = 0.f, mv = 0.f;
-#pragma unroll
-    for (int u = 0; u < AppendRegs<D, KVT>::KIN; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) mk = fmaxf(mk, fmaxf(abs_bf16(a.k[u][e]), abs_bf16(a.k[u][e] >> 16)));
-#pragma unroll
-    for (int u = 0; u < GE::LPC; ++u)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) mv = fmaxf(mv, fmaxf(abs_bf16(a.v[u][e]), abs_bf16(a.v[u][e] >> 16)));
-    mk = max_x32(max_x16(mk));
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) mv = fmaxf(mv, __shfl_xor(mv, off, kWave));
-    sk = int8_scale(mk);
-    sv = int8_scale(mv);
-  }
-  // both chunks, so that every register index stays static (a runtime choice
-  // of chunk would move the buffers to scratch memory)
-  patch_chunk<0, D, KVT>(r, a, p, tt, sk, sv, lane);
-  if constexpr (GE::CH == 2) patch_chunk<1, D, KVT>(r, a, p, tt, sk, sv, lane);
-}
-
-// Write the register pieces of chunk H that hold token tt back to the pool,
-// at the addresses issue_chunks read them from.
-template <int H, int D, int KVT, int B>
-__device__ __forceinline__ void writeback_chunk(const SplitBuf<D, KVT>& r, const SplitParams& p, int phys, int g,
-                                                int t0, int tt, int lane) {
-  using GE = SplitGeo<D, KVT>;
-  constexpr int E = GE::E;
-  const int row = lane & 15;
-  const int j = lane >> 4;
-  const int rt = tt - 16 * H, jj = rt >> 2;       // no lane matches unless chunk H holds the token
-  const int toff = (t0 + 16 * H) % B;
+template <int D, int KVT, int B>
+__device__ __forceinline__ void append_token(const SplitParams& p, int s, int g, int ctx, int lane) {
+  constexpr int E = KVT == PKV_KV_BF16 ? 2 : 1;
+  constexpr int X = 16 / E;    // dims per 16-byte K piece
+  constexpr int NPC = D / X;   // K pieces per token (<= 16): lane pc < NPC stores piece pc
+  constexpr int VD = D / 64;   // V dims per lane: lane l stores dims VD*l ..
+  const int pos = ctx - 1;     // ctx <= W * B, so the table index is inside the row
+  int phys = uniform_load(p.bt + (int64_t)s * p.W + pos / B);
+  phys = phys < 0 ? 0 : (phys >= p.num_blocks ? p.num_blocks - 1 : phys);  // stay inside the pool
+  const int t = pos % B;
   const int64_t tile = (int64_t)phys * p.Hkv + g;
   char* kt = p.k + tile * (int64_t)(B * D * E);
   char* vt = p.v + tile * (int64_t)(B * D * E);
-  if (row == rt) {
-#pragma unroll
-    for (int u = 0; u < GE::LPC; ++u) *reinterpret_cast<u32x4*>(kt + ((4 * u + j) * B + toff + row) * 16) = r.k[H][u];
+  const uint16_t* kx = p.new_k + ((int64_t)s * p.Hkv + g) * D;
+  const uint16_t* vx = p.new_v + ((int64_t)s * p.Hkv + g) * D;
+  const bool kl = lane < NPC;
+  u32x4 kin[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};   // bf16 values of the lane's K piece
+  if (kl) {
+    kin[0] = *reinterpret_cast<const u32x4*>(kx + X * lane);
+    if constexpr (E == 1) kin[1] = *reinterpret_cast<const u32x4*>(kx + X * lane + 8);
   }
-  if (j == jj) {
-    const int grp = (toff >> 2) + j;
+  uint32_t vin;                                                 // bf16 values of the lane's V dims
+  if constexpr (VD == 2) vin = *reinterpret_cast<const uint32_t*>(vx + 2 * lane);
+  else vin = vx[lane];
+  float sk = 0.f, sv = 0.f;
+  if constexpr (KVT == PKV_KV_INT8) {
+    float mk = 0.f, mv = 0.f;
 #pragma unroll
-    for (int u = 0; u < GE::LPC; ++u) {
-      const int d = (E == 2) ? (32 * u + 2 * row) : (64 * u + 4 * row);
-      *reinterpret_cast<u32x4*>(vt + (grp * D + d) * 4 * E) = r.v[H][u];
-    }
-    if constexpr (KVT == PKV_KV_INT8) {
-      if (row == 0) {
-        const int64_t so = tile * B + toff + 4 * j;
-        *reinterpret_cast<f32x4*>(p.ks + so) = r.ksc[H];
-        *reinterpret_cast<f32x4*>(p.vs + so) = r.vsc[H];
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mk = fmaxf(mk, fmaxf(abs_bf16(kin[h][e]), abs_bf16(kin[h][e] >> 16)));
+#pragma unroll
+    for (int i = 0; i < VD; ++i) mv = fmaxf(mv, abs_bf16(vin >> (16 * i)));
+    sk = int8_scale(wave_max(mk));
+    sv = int8_scale(wave_max(mv));
+  }
+  if (kl) {
+    u32x4 kout;
+    if constexpr (E == 2) {
+      kout = kin[0];
+    } else {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {   // output word q4 = dims 4q4 .. 4q4+3 of the piece
+        const uint32_t x0 = kin[q4 >> 1][(q4 & 1) * 2], x1 = kin[q4 >> 1][(q4 & 1) * 2 + 1];
+        uint32_t b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t x = half_of(i < 2 ? x0 : x1, i & 1);
+          b[i] = KVT == PKV_KV_FP8_E5M2 ? fp8_store(x, p.enc_k) : int8_store(x, sk);
+        }
+        kout[q4] = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
       }
     }
+    *reinterpret_cast<u32x4*>(kt + (lane * B + t) * 16) = kout;
   }
-}
-
-template <int D, int KVT, int B>
-__device__ __forceinline__ void writeback_append(const SplitBuf<D, KVT>& r, const SplitParams& p, int phys0,
-                                                 int phys1, int g, int t0, int tt, int lane) {
-  writeback_chunk<0, D, KVT, B>(r, p, phys0, g, t0, tt, lane);
-  if constexpr (SplitGeo<D, KVT>::CH == 2) writeback_chunk<1, D, KVT, B>(r, p, phys1, g, t0, tt, lane);
+#pragma unroll
+  for (int i = 0; i < VD; ++i) {
+    const int d = VD * lane + i;
+    const uint32_t x = half_of(vin, i);
+    const int64_t el = ((int64_t)(t >> 2) * D + d) * 4 + (t & 3);
+    if constexpr (E == 2) {
+      reinterpret_cast<uint16_t*>(vt)[el] = (uint16_t)x;
+    } else {
+      const uint32_t code = KVT == PKV_KV_FP8_E5M2 ? fp8_store(x, p.enc_v) : int8_store(x, sv);
+      reinterpret_cast<uint8_t*>(vt)[el] = (uint8_t)code;
+    }
+  }
+  if constexpr (KVT == PKV_KV_INT8) {
+    if (lane == 0) {
+      p.ks[tile * B + t] = sk;
+      p.vs[tile * B + t] = sv;
+    }
+  }
 }
 
 // Rescale threshold of the streaming softmax, in log2 units: the reference
@@ -915,13 +805,29 @@ __device__ __forceinline__ void compute_step(const SplitBuf<D, KVT>& r, const QR
   }
 }
 
-// Where the issue side of a wave stands in the flat step list.
+// Where the issue side of a wave stands in the flat step list, with the
+// constants of its row (recomputed only when the row changes).
 struct Cursor {
   int s, xi, j;     // sequence, row within the sequence, step within the row
   int n;            // steps of sequence s's rows
   int ctx;          // context length of sequence s
+  int g;            // KV head of the row
+  int h0, gt;       // first query head of the row's tile, and its number of heads
+  int unit;         // x * NP + partition of step j (x = s * HQ + xi)
+  int pleft;        // steps of that partition left, step j included
   int phys[2];      // table entries of the step at the cursor (prefetched)
 };
+
+// Row constants of the cursor's row, entered at step j.
+__device__ __forceinline__ void cursor_row(Cursor& c, const SplitParams& p) {
+  c.g = p.QT == 1 ? c.xi : c.xi / p.QT;
+  const int qt = c.xi - c.g * p.QT;
+  c.h0 = c.g * p.G + qt * 16;
+  c.gt = min(16, p.G - qt * 16);
+  const int part = c.j == 0 ? 0 : c.j / p.PS;
+  c.unit = (c.s * p.HQ + c.xi) * p.NP + part;
+  c.pleft = p.PS - (c.j - part * p.PS);
+}
 
 template <int B, int TS>
 __device__ __forceinline__ void cursor_tables(Cursor& c, const SplitParams& p) {
@@ -1154,58 +1060,63 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
   cur.j = __builtin_amdgcn_readfirstlane(cur.j);
   cum0 = __builtin_amdgcn_readfirstlane(cum0);
   const Cursor first = cur;
+
+  // ---- appending decode: store the new token of every row that ends in this range
+  if (p.new_k) {
+    int as = cur.s, axi = cur.xi, aj = cur.j, an = cur.n, actx = cur.ctx, left = nsteps;
+    bool any = false;
+    while (left > 0) {
+      const int mine = min(left, an - aj);
+      if (aj + mine == an) {
+        append_token<D, KVT, B>(p, as, p.QT == 1 ? axi : axi / p.QT, actx, lane);
+        any = true;
+      }
+      left -= mine;
+      aj = 0;
+      if (left > 0 && ++axi == p.HQ) {
+        axi = 0;
+        do {
+          ++as;
+          actx = clamp_ctx(uniform_load(p.ctx + as), max_ctx);
+          an = (actx + TS - 1) / TS;
+        } while (an == 0);
+      }
+    }
+    if (any) wait_vm_all();
+  }
+
+  cursor_row(cur, p);
   cursor_tables<B, TS>(cur, p);
 
   SplitBuf<D, KVT> buf[NBUF];
   StepMeta meta[NBUF];
-  QRegs<GE::KK> qnext;
-  QRegs<GE::KK> qop;
-  int qowner = -1;          // index of the step whose q sits in qnext
-  AppendRegs<D, KVT> anext;
-  int aowner = -1;          // index of the step whose new token sits in anext
+  QRegs<GE::KK> qbuf[NBUF];   // q of a row that starts at the step in the same-index buffer
+  QRegs<GE::KK> qop;          // q of the row being computed
   int issued = 0;
 
-  // Issue the step at the cursor into buffer r, then advance the cursor.
-  // `done` = index of the oldest step not yet computed.  Past the end of the
-  // range the loads still happen (see issue_chunks) but nothing is consumed.
-  auto issue = [&](SplitBuf<D, KVT>& r, StepMeta& m, int done) __attribute__((always_inline)) {
+  // Issue the step at the cursor into buffer r (and, when it starts a row in
+  // this wave, the row's q into qr), then advance the cursor.  Past the end of
+  // the range the K/V loads still happen (see issue_chunks) but nothing is
+  // consumed.  A row's q goes with its first step into the register set of
+  // that step's buffer, so every load is consumed a fixed number of issues
+  // after it was made and the compiler's wait before each compute covers
+  // exactly that step's loads.
+  auto issue = [&](SplitBuf<D, KVT>& r, StepMeta& m, QRegs<GE::KK>& qr) __attribute__((always_inline)) {
     const bool live = issued < nsteps;
-    const int g = cur.xi / p.QT;
-    const int qt = cur.xi - g * p.QT;
-    const int h0 = g * p.G + qt * 16;
-    const int gt = min(16, p.G - qt * 16);
-    const bool last = issued + 1 == nsteps;
-    const bool row_end = cur.j + 1 == cur.n;
-    const bool part_end = ((cur.j + 1) * TS) % p.P == 0;
+    const bool new_row = live && (cur.j == 0 || issued == 0);
+    if (new_row) qr = load_q<D, KVT>(p, cur.s, cur.h0, cur.gt, lane);
+    const bool flush = issued + 1 == nsteps || cur.j + 1 == cur.n || cur.pleft == 1;
     m.t0 = cur.j * TS;
     m.t_end = live ? cur.ctx : 0;
-    m.slot = (cur.s * p.HQ + cur.xi) * p.NP + (cur.j * TS) / p.P + w;
-    m.qs = cur.s;
-    m.qh0 = h0;
-    m.ag = g;
-    m.aphys0 = cur.phys[0];
-    m.aphys1 = cur.phys[TS > 16 ? 1 : 0];
-    int f = (last || row_end || part_end) ? kFlush : 0;
-    if (live && row_end && p.new_k) {   // the step holding token ctx - 1
-      f |= kAppend;
-      if (aowner < done) {
-        anext = load_append<D, KVT>(p, cur.s, g, lane);
-        aowner = issued;
-        f |= kAReady;
-      }
-    }
-    if (live && (cur.j == 0 || issued == 0)) {
-      f |= kNewRow;
-      if (qowner < done) {       // qnext is free: prefetch this row's q
-        qnext = load_q<D, KVT>(p, cur.s, h0, gt, lane);
-        qowner = issued;
-        f |= kQReady;
-      }
-    }
-    m.flags = f;
-    issue_chunks<D, KVT, B>(r, p, cur.phys, g, m.t0, m.t_end, lane);
+    m.slot = cur.unit + w;
+    m.flags = (new_row ? kNewRow : 0) | (flush ? kFlush : 0) | (cur.gt << 8);
+    issue_chunks<D, KVT, B>(r, p, cur.phys, cur.g, m.t0, m.t_end, lane);
     ++issued;
     if (issued < nsteps) {     // advance to the next step and fetch its table entries
+      if (--cur.pleft == 0) {
+        cur.pleft = p.PS;
+        ++cur.unit;
+      }
       if (++cur.j == cur.n) {
         cur.j = 0;
         if (++cur.xi == p.HQ) {
@@ -1216,6 +1127,7 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
             cur.n = (cur.ctx + TS - 1) / TS;
           } while (cur.n == 0);
         }
+        cursor_row(cur, p);
       }
       cursor_tables<B, TS>(cur, p);
     }
@@ -1227,34 +1139,13 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  auto consume = [&](SplitBuf<D, KVT>& r, const StepMeta& m) __attribute__((always_inline)) {
-    if (m.flags & kNewRow) {
-      if (m.flags & kQReady) {
-        qop = qnext;
-      } else {
-        // two rows began within the prefetch window: load this one now, and
-        // wait here, so the compiler does not carry a pending load of unknown
-        // distance into the compute (which would make it drain every step)
-        const int gt = min(16, p.G - (m.qh0 % p.G));
-        qop = load_q<D, KVT>(p, m.qs, m.qh0, gt, lane);
-        wait_vm_all();
-      }
-    }
-    const int tt = m.t_end - 1 - m.t0;
-    if (m.flags & kAppend) {
-      if (m.flags & kAReady) {
-        patch_append<D, KVT>(r, anext, p, tt, lane);
-      } else {   // as for q: a direct load, waited for here
-        const AppendRegs<D, KVT> a = load_append<D, KVT>(p, m.qs, m.ag, lane);
-        wait_vm_all();
-        patch_append<D, KVT>(r, a, p, tt, lane);
-      }
-    }
+  auto consume = [&](const SplitBuf<D, KVT>& r, const StepMeta& m, const QRegs<GE::KK>& qr)
+                     __attribute__((always_inline)) {
+    if (m.flags & kNewRow) qop = qr;
     compute_step<D, KVT>(r, qop, p, m.t0, m.t_end, lane, m_run, l_run, acc);
-    if (m.flags & kAppend) writeback_append<D, KVT, B>(r, p, m.aphys0, m.aphys1, m.ag, m.t0, tt, lane);
     if (m.flags & kFlush) {
       const float l = sum_x32(sum_x16(l_run));
-      const int gt = min(16, p.G - (m.qh0 % p.G));
+      const int gt = m.flags >> 8;
       if (row < gt) {
         float* pa = p.part_acc + (int64_t)m.slot * (GE::NC * 256) + lane * 4;
 #pragma unroll
@@ -1272,22 +1163,21 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
   };
 
   // ---- pipeline: NBUF - 1 steps of loads in flight ahead of the one computed.
-  // Every step issues the same loads (live or not) so the wait before each
+  // Every step issues the same K/V loads (live or not) so the wait before each
   // compute only covers that step's loads.
   // (the buffer indices must be compile-time constants, or the buffers move
   // to scratch memory: the steps are expanded from an index sequence rather
   // than left to loop unrolling)
   static_for<NBUF - 1>([&](auto bbc) {
     constexpr int bb = decltype(bbc)::value;
-    issue(buf[bb], meta[bb], 0);
+    issue(buf[bb], meta[bb], qbuf[bb]);
   });
   for (int base = 0; base < nsteps; base += NBUF) {
     static_for<NBUF>([&](auto bbc) {
       constexpr int bb = decltype(bbc)::value;
       constexpr int nb = (bb + NBUF - 1) % NBUF;
-      const int idx = base + bb;
-      issue(buf[nb], meta[nb], idx);
-      if (idx < nsteps) consume(buf[bb], meta[bb]);
+      issue(buf[nb], meta[nb], qbuf[nb]);
+      if (base + bb < nsteps) consume(buf[bb], meta[bb], qbuf[bb]);
     });
   }
 
@@ -1343,7 +1233,7 @@ hipError_t launch_single_kv(const DecodeParams& p, int kvt, int B, int grid, hip
 // Steps of K/V registers per wave: one computed, the rest in flight (about
 // 40 KB per wave, 160 KB per CU with one wave per SIMD).
 template <int D, int KVT>
-constexpr int split_nbuf() { return D == 64 ? 8 : (KVT == PKV_KV_INT8 ? 5 : 6); }
+constexpr int split_nbuf() { return D == 64 ? 8 : 5; }
 constexpr int kMaxBlocksPerCU = 1;       // persistent grid: one workgroup (a wave per SIMD) per CU
 
 template <int D, int KVT, int B>
@@ -1611,6 +1501,7 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     p.HQ = c.num_kv_heads * QT;
     p.num_blocks = c.num_blocks;
     p.P = partition_size;
+    p.PS = partition_size / TS;
     p.NP = (int32_t)np;
     p.NWV = (int32_t)(grid * kNW);
     p.epoch = next_epoch();
