@@ -581,8 +581,10 @@ __device__ __forceinline__ void issue_chunks(SplitBuf<D, KVT>& r, const SplitPar
 // ---- appending decode.  Before streaming its range, a wave stores the new
 // token (position ctx - 1) of every row whose last step lies in that range,
 // encoded exactly as reshape_and_cache stores it.  The wave reads that tile
-// again at the row's last step, and one wave's accesses to an address are
-// performed in order, so the decode sees the token.  No other wave reads
+// again at the row's last step: a wave's vector memory operations complete
+// in the order it issues them, and the lanes of one wave need no
+// synchronisation among themselves, so that later load sees the token
+// without a wait here.  No other wave reads
 // those bytes: the token's block is not shared (copy-on-write runs before the
 // append), the rest of its tile belongs to other steps, and when a KV head
 // has several 16-head rows, each of their last-step waves stores the same
@@ -1003,20 +1005,36 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
   const int w = __builtin_amdgcn_readfirstlane(wg * kNW + (int)threadIdx.x / kWave);
   const int max_ctx = p.W * B;
 
-  // ---- total steps N; wave 0 also zeroes the output of empty sequences
+  // ---- total steps N (wave 0 also zeroes the output of empty sequences),
+  // this wave's range, and the sequence holding its first step.  Context
+  // lengths are read kSeqRegs * 64 at a time with independent loads; up to
+  // that many sequences they are read once and kept in registers.
+  constexpr int kSeqRegs = 4;
+  int cv[kSeqRegs];          // clamped context length of sequence base + 64k + lane
+  auto load_ctx = [&](int base) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < kSeqRegs; ++k) {
+      const int sq = base + k * kWave + lane;
+      cv[k] = sq < p.S ? clamp_ctx(p.ctx[sq], max_ctx) : 0;
+    }
+  };
   int total = 0;
-  for (int base = 0; base < p.S; base += kWave) {
-    const int s = base + lane;
-    const int n = s < p.S ? (clamp_ctx(p.ctx[s], max_ctx) + TS - 1) / TS : 0;
-    total += wave_sum(n);
-    if (w == 0) {
-      uint64_t empty = __ballot(s < p.S && n == 0);
-      while (empty) {
-        const int se = base + __builtin_ctzll(empty);
-        empty &= empty - 1;
-        float* o = p.out + (int64_t)se * p.Hq * D;
-        for (int i = lane * 4; i < p.Hq * D; i += kWave * 4)
-          *reinterpret_cast<f32x4*>(o + i) = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int base = 0; base < p.S; base += kSeqRegs * kWave) {
+    load_ctx(base);
+#pragma unroll
+    for (int k = 0; k < kSeqRegs; ++k) {
+      const int n = (cv[k] + TS - 1) / TS;
+      total += wave_sum(n);
+      if (w == 0) {
+        const int b0 = base + k * kWave;
+        uint64_t empty = __ballot(b0 + lane < p.S && n == 0);
+        while (empty) {
+          const int se = b0 + __builtin_ctzll(empty);
+          empty &= empty - 1;
+          float* o = p.out + (int64_t)se * p.Hq * D;
+          for (int i = lane * 4; i < p.Hq * D; i += kWave * 4)
+            *reinterpret_cast<f32x4*>(o + i) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
       }
     }
   }
@@ -1027,30 +1045,35 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
   if (start >= stop) return;
   const int nsteps = stop - start;
 
-  // ---- locate the first step: sequence s with cum_s * HQ <= start < cum_{s+1} * HQ
+  // locate the first step: sequence s with cum_s * HQ <= start < cum_{s+1} * HQ
   Cursor cur{};
   int cum0 = 0;
   {
     int acc0 = 0;
-    for (int base = 0; base < p.S; base += kWave) {
-      const int s = base + lane;
-      const int c = s < p.S ? clamp_ctx(p.ctx[s], max_ctx) : 0;
-      const int n = (c + TS - 1) / TS;
-      const int incl = wave_incl_scan(n, lane);
-      const bool hit = (acc0 + incl - n) * p.HQ <= start && start < (acc0 + incl) * p.HQ;
-      const uint64_t m = __ballot(hit);
-      if (m) {
-        const int l = __builtin_ctzll(m);
-        cur.s = base + l;
-        cur.n = __shfl(n, l, kWave);
-        cur.ctx = __shfl(c, l, kWave);
-        cum0 = acc0 + __shfl(incl - n, l, kWave);
-        const int off = start - cum0 * p.HQ;
-        cur.xi = off / cur.n;
-        cur.j = off % cur.n;
-        break;
+    bool found = false;
+    for (int base = 0; base < p.S && !found; base += kSeqRegs * kWave) {
+      if (p.S > kSeqRegs * kWave) load_ctx(base);   // else still held from the count
+#pragma unroll
+      for (int k = 0; k < kSeqRegs; ++k) {
+        if (found) break;
+        const int c = cv[k];
+        const int n = (c + TS - 1) / TS;
+        const int incl = wave_incl_scan(n, lane);
+        const bool hit = (acc0 + incl - n) * p.HQ <= start && start < (acc0 + incl) * p.HQ;
+        const uint64_t m = __ballot(hit);
+        if (m) {
+          const int l = __builtin_ctzll(m);
+          cur.s = base + k * kWave + l;
+          cur.n = __shfl(n, l, kWave);
+          cur.ctx = __shfl(c, l, kWave);
+          cum0 = acc0 + __shfl(incl - n, l, kWave);
+          const int off = start - cum0 * p.HQ;
+          cur.xi = off / cur.n;
+          cur.j = off % cur.n;
+          found = true;
+        }
+        acc0 += __shfl(incl, kWave - 1, kWave);
       }
-      acc0 += __shfl(incl, kWave - 1, kWave);
     }
   }
   cur.s = __builtin_amdgcn_readfirstlane(cur.s);
@@ -1064,12 +1087,10 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
   // ---- appending decode: store the new token of every row that ends in this range
   if (p.new_k) {
     int as = cur.s, axi = cur.xi, aj = cur.j, an = cur.n, actx = cur.ctx, left = nsteps;
-    bool any = false;
     while (left > 0) {
       const int mine = min(left, an - aj);
       if (aj + mine == an) {
         append_token<D, KVT, B>(p, as, p.QT == 1 ? axi : axi / p.QT, actx, lane);
-        any = true;
       }
       left -= mine;
       aj = 0;
@@ -1082,7 +1103,6 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
         } while (an == 0);
       }
     }
-    if (any) wait_vm_all();
   }
 
   cursor_row(cur, p);
@@ -1186,26 +1206,42 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
   // visible to every XCD) before any counter below is raised
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   wait_vm_all();
+  // rows go 64 at a time, one per lane: their counters are raised by
+  // concurrent compare-and-swaps, then the rows this wave completed are merged
   int rs = first.s, rxi = first.xi, rn = first.n, rj = first.j, rcum = cum0;
   int left = nsteps;
   while (left > 0) {
-    const int mine = min(left, rn - rj);
-    const int x = rs * p.HQ + rxi;
-    int done_now = 0;
-    if (lane == 0) done_now = add_steps(p.row_done + x, p.epoch, mine);
-    done_now = __builtin_amdgcn_readfirstlane(done_now);
-    if (done_now == rn) {   // every partial of the row is in place
-      merge_row<D, GE::E>(p, x, rs, rxi, rn, rcum * p.HQ + rxi * rn, N, TS, lane);
+    int lx = -1, lmine = 0, ln = 0, ls = 0, lxi = 0, lsx = 0;
+    for (int k = 0; k < kWave && left > 0; ++k) {
+      const int mine = min(left, rn - rj);
+      if (lane == k) {
+        lx = rs * p.HQ + rxi;
+        lmine = mine;
+        ln = rn;
+        ls = rs;
+        lxi = rxi;
+        lsx = rcum * p.HQ + rxi * rn;
+      }
+      left -= mine;
+      rj = 0;
+      if (left > 0 && ++rxi == p.HQ) {
+        rxi = 0;
+        rcum += rn;
+        do {
+          ++rs;
+          rn = (clamp_ctx(uniform_load(p.ctx + rs), max_ctx) + TS - 1) / TS;
+        } while (rn == 0);
+      }
     }
-    left -= mine;
-    rj = 0;
-    if (left > 0 && ++rxi == p.HQ) {
-      rxi = 0;
-      rcum += rn;
-      do {
-        ++rs;
-        rn = (clamp_ctx(uniform_load(p.ctx + rs), max_ctx) + TS - 1) / TS;
-      } while (rn == 0);
+    int done_now = 0;
+    if (lx >= 0) done_now = add_steps(p.row_done + lx, p.epoch, lmine);
+    uint64_t complete = __ballot(lx >= 0 && done_now == ln);   // every partial of the row is in place
+    while (complete) {
+      const int l = __builtin_ctzll(complete);
+      complete &= complete - 1;
+      merge_row<D, GE::E>(p, __builtin_amdgcn_readlane(lx, l), __builtin_amdgcn_readlane(ls, l),
+                          __builtin_amdgcn_readlane(lxi, l), __builtin_amdgcn_readlane(ln, l),
+                          __builtin_amdgcn_readlane(lsx, l), N, TS, lane);
     }
   }
 }
