@@ -430,15 +430,16 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
 // x = s * HQ + xi with xi = g * QT + qt and HQ = Hkv * QT.  Row x has
 // n_s = ceil(ctx_s / TS) steps of TS tokens.  The flat step list is
 // row 0's steps, then row 1's, ...; row x starts at cum_s * HQ + xi * n_s where
-// cum_s = sum over s' < s of n_s'.  Wave w of NWV takes flat steps
-// [w * per, min((w + 1) * per, N)), per = ceil(N / NWV).
+// cum_s = sum over s' < s of n_s'.  Each wave of the NWV takes one
+// contiguous range of the list.
 // The grid is one workgroup of four waves per CU.  Workgroups are dispatched
 // to the eight XCDs in turn (workgroup b runs on XCD b % 8), and waves are
 // numbered so that XCD x holds waves [x * WX, (x + 1) * WX), WX = NWV / 8.
-// Measured on MI355X, waves on odd-numbered XCDs stream about 10% slower than
-// those on even ones, so XCD x takes a share of the flat list proportional to
-// kXcdWeight[x], split equally among its waves; all waves then finish
-// together.  The split depends only on N and the grid, never on timing.
+// Measured on MI355X, waves on odd-numbered XCDs stream 10-16% slower than
+// those on even ones (it varies from board to board), so XCD x takes a share
+// of the flat list proportional to kXcdWeight[x], split equally among its
+// waves, and the waves finish at about the same time.  The split depends
+// only on N and the grid, never on timing.
 // Partition p of row x covers its tokens [p * P, (p + 1) * P); unit
 // u = x * NP + p.  The segment of unit u computed by wave w is stored in
 // partial slot u + w: walking the (unit, wave) pairs in order raises u or w
@@ -875,7 +876,7 @@ __device__ __forceinline__ int add_steps(uint64_t* ctr, uint32_t epoch, int mine
   }
 }
 
-constexpr int kXcdWeight[8] = {256, 231, 256, 231, 256, 231, 256, 231};
+constexpr int kXcdWeight[8] = {256, 224, 256, 224, 256, 224, 256, 224};
 
 // First flat step of XCD x's share of N steps.
 __device__ __forceinline__ int xcd_begin(int N, int x) {
