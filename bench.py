@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate-cache-write", action="store_true",
                     help="per layer, reshape_and_cache then paged_attn_decode (two launches)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window: each layer's call attends to the last N positions only "
+                         "(paged_attn_decode_ex; bytes counted over those positions)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB three times (torch copy kernel): the reference for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -160,9 +163,16 @@ def main():
     dec_events = []
 
     separate = args.separate_cache_write
+    window = args.window
+    if window and separate:
+        sys.exit("--window runs the appending form only")
 
     def decode(layer):
-        if separate:
+        if window:
+            pkv.paged_attn_decode_ex(out, q[layer], pool, layer, d_tab, d_ctx, scale, partition_size=P,
+                                     workspace=ws, key=newk[layer], value=newv[layer], sliding_window=window,
+                                     stream=stream)
+        elif separate:
             pkv.paged_attn_decode(out, q[layer], pool, layer, d_tab, d_ctx, scale, partition_size=P,
                                   workspace=ws, stream=stream)
         else:
@@ -181,7 +191,8 @@ def main():
             h_slot[b].numpy()[:] = slots
             d_slot.copy_(h_slot[b], non_blocking=True)
         h_done[b].record(stream)
-        ctx_sum = int(h_ctx[b].numpy().astype(np.int64).sum())
+        ctxs = h_ctx[b].numpy().astype(np.int64)
+        ctx_sum = int((np.minimum(ctxs, window) if window else ctxs).sum())   # positions attended
         kv_bytes.append(ctx_sum * Hkv * 2 * D * 2 * L)
         # HIP events on the launch stream.  A timing event between two launches
         # costs ~10 us of idle GPU (the next launch no longer follows the
@@ -234,6 +245,10 @@ def main():
     parity = None
     if not args.no_cpu_baseline:
         cpu, parity = cpu_baseline(args, pkv, w, pool, decode, q, out, d_tab, d_ctx, scale)
+    workload = ("70B-shaped paged decode step: 80 layers x 100 seqs x ~4K ctx, "
+                "64q/8kv heads, head_dim 128, bf16 KV, block 16")
+    if window:
+        workload += f", sliding window of the last {window} positions"
 
     call = "paged_attn_decode" if separate else "paged_attn_decode_append"
     res = {
@@ -249,9 +264,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "70B-shaped paged decode step: 80 layers x 100 seqs x ~4K ctx, "
-                               "64q/8kv heads, head_dim 128, bf16 KV, block 16",
-                   "layers": L, "seqs": S, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+        "config": {"workload": workload,
+                   "sliding_window": window, "layers": L, "seqs": S, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
                    "block_size": B, "partition_size": P, "kv_bytes_per_step": int(kv_per_step),
                    "layer_calls": ("reshape_and_cache + paged_attn_decode" if separate
                                    else "paged_attn_decode_append")},
@@ -260,7 +274,8 @@ def main():
         "seq_tokens_per_s": round(kv_per_step / (Hkv * 2 * D * 2 * L) / (elapsed / args.steps), 1),
         "roofline": {"bound": "hbm", "kernel": f"pa_split_kernel (the one launch of a split-context {call} call)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if window else measured_traffic(),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
                      "avg_call_us": round(avg_dec_ms * 1e3, 2), "bytes_per_call": int(avg_dec_bytes)},
         "cpu_baseline": cpu,
@@ -305,9 +320,10 @@ def cpu_baseline(args, pkv, w, pool, decode, q, out, d_tab, d_ctx, scale):
                 dst[:] = lay.index_select(0, idx).cpu().numpy().view(np.uint16).reshape(-1)
             local = np.arange(nblk, dtype=np.int32)
             t0 = time.perf_counter()
-            ref = attention.paged_decode(qbits[s:s + 1], img, 0, local[None, :], np.array([n]), scale)
+            ref = attention.paged_decode(qbits[s:s + 1], img, 0, local[None, :], np.array([n]), scale,
+                                         window=args.window)
             spent += time.perf_counter() - t0
-            done.append(n)
+            done.append(min(n, args.window) if args.window else n)   # positions attended
             worst = max(worst, float(np.max(np.abs(gpu_out[s] - ref[0]))))
             if spent >= args.cpu_seconds:
                 break

@@ -223,6 +223,44 @@ pkv_status paged_attn_decode_append(float* out, const void* q, const pkv_pool* p
                                     const pkv_kv_scales* kv_scales, int32_t partition_size, void* workspace,
                                     uint64_t workspace_bytes, hipStream_t stream);
 
+/* Every argument of a decode call in one block, for the options the two
+ * calls above do not take.  Fields as for paged_attn_decode_append (key and
+ * value NULL for the plain decode), plus:
+ *   sliding_window  0: attend to the whole context.  w > 0: attend only to
+ *                   the last w positions, [max(0, ctx - w), ctx) - the
+ *                   sliding-window KV of "Transformer 架构" (aiworkagent.org)
+ *                   question 17, 进阶 item 3 (keep only the most recent N
+ *                   tokens).  Blocks that lie wholly before that range are
+ *                   never read: their table entries may name any block, e.g.
+ *                   one already given back to the pool.  Works in both forms
+ *                   (partition_size 0 or > 0); the workspace size does not
+ *                   depend on it.  Negative: PKV_ERR_INVALID. */
+typedef struct {
+  float* out;                  /* device, [S][Hq][D] fp32 */
+  const void* q;               /* device, [S][Hq][D] bf16 */
+  const pkv_pool* pool;        /* host */
+  int32_t layer;
+  const void* key;             /* device [S][Hkv][D] bf16 or NULL (appending form when set) */
+  const void* value;           /* device, set exactly when key is */
+  const int32_t* block_tables; /* device, [S][table_width] */
+  int32_t table_width;
+  const int32_t* context_lens; /* device, [S] */
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  float scale;
+  int32_t kv_dtype;
+  const pkv_kv_scales* kv_scales; /* host, or NULL */
+  int32_t partition_size;
+  int32_t sliding_window;
+  void* workspace;             /* device */
+  uint64_t workspace_bytes;
+} pkv_decode_args;
+
+/* Decode with every option: same behaviour, ownership and errors as
+ * paged_attn_decode (key == NULL) or paged_attn_decode_append (key set);
+ * PKV_ERR_INVALID for a NULL args or a key without a value. */
+pkv_status paged_attn_decode_ex(const pkv_decode_args* args, hipStream_t stream);
+
 /* ------------------------------------------------------------- host checks
  * Validators over HOST copies of device inputs, for callers that want to
  * rule out racing or out-of-range values before a launch.  Return PKV_OK or

@@ -14,6 +14,11 @@ Definitions followed:
   blocks through that table ("KV Cache 原理与 PagedAttention", §三 工作方式
   steps 1, 2 and 4).  Logical position t lives in logical block t // B at
   offset t % B, i.e. in slot table[t // B] * B + t % B.
+* Sliding window ("Transformer 架构", aiworkagent.org, question 17, 进阶
+  item 3: keep only the most recent N tokens): with a window of w > 0
+  positions the query attends to positions [max(0, ctx - w), ctx) only - the
+  same softmax over that shorter range.  Blocks wholly before the range are
+  not read at all (their table entries may name anything).
 * Grouped-query attention: with Hq query heads sharing Hkv < Hq KV heads
   (same page, §一 GQA / MQA 为什么省 KV Cache), query head h reads KV head
   h // G, G = Hq / Hkv (contiguous groups; the pages only count heads, the
@@ -44,21 +49,24 @@ def slot_of(block_table_row: np.ndarray, pos, block_size: int):
 
 
 def gather_kv(img: PoolImage, layer: int, block_table_row: np.ndarray,
-              ctx: int, k_scale: float = 1.0, v_scale: float = 1.0):
-    """Contiguous dequantised K and V, each [ctx, Hkv, D] float64.
+              ctx: int, k_scale: float = 1.0, v_scale: float = 1.0, start: int = 0):
+    """Contiguous dequantised K and V of positions [start, ctx), each
+    [ctx - start, Hkv, D] float64.
 
-    Reads whole tiles of the blocks the table names (layout.*_as_tokens);
-    ``gather_kv_by_slot`` reads the same values one element at a time through
-    the slot mapping and the layout's index functions, and the two agree
-    exactly (tests/test_oracle_paging.py)."""
+    Reads whole tiles of the blocks the table names from block start // B on
+    (layout.*_as_tokens); ``gather_kv_by_slot`` reads the same values one
+    element at a time through the slot mapping and the layout's index
+    functions, and the two agree exactly (tests/test_oracle_paging.py)."""
     p = img.shape
-    if ctx == 0:
+    if ctx <= start:
         z = np.zeros((0, p.num_kv_heads, p.head_dim))
         return z, z.copy()
+    b0 = start // p.block_size
     nblk = -(-ctx // p.block_size)
-    blocks = np.asarray(block_table_row, dtype=np.int64)[:nblk]
-    kraw = layout_k_tokens(p, img.k, layer, blocks)[:ctx]
-    vraw = layout_v_tokens(p, img.v, layer, blocks)[:ctx]
+    blocks = np.asarray(block_table_row, dtype=np.int64)[b0:nblk]
+    cut = slice(start - b0 * p.block_size, ctx - b0 * p.block_size)
+    kraw = layout_k_tokens(p, img.k, layer, blocks)[cut]
+    vraw = layout_v_tokens(p, img.v, layer, blocks)[cut]
     if p.kv_dtype == KV_BF16:
         return codecs.bf16_bits_to_f64(kraw), codecs.bf16_bits_to_f64(vraw)
     if p.kv_dtype == KV_FP8_E5M2:
@@ -66,21 +74,22 @@ def gather_kv(img: PoolImage, layer: int, block_table_row: np.ndarray,
         vs = np.float64(np.float32(v_scale))
         return codecs.e5m2_decode(kraw) * ks, codecs.e5m2_decode(vraw) * vs
     if p.kv_dtype == KV_INT8:
-        ksc = layout_scale_tokens(p, img.k_scale, layer, blocks)[:ctx]
-        vsc = layout_scale_tokens(p, img.v_scale, layer, blocks)[:ctx]
+        ksc = layout_scale_tokens(p, img.k_scale, layer, blocks)[cut]
+        vsc = layout_scale_tokens(p, img.v_scale, layer, blocks)[cut]
         return codecs.int8_dequant(kraw, ksc), codecs.int8_dequant(vraw, vsc)
     raise ValueError(p.kv_dtype)
 
 
 def gather_kv_by_slot(img: PoolImage, layer: int, block_table_row: np.ndarray,
-                      ctx: int, k_scale: float = 1.0, v_scale: float = 1.0):
-    """``gather_kv`` element by element: token t of the sequence is read at
-    slot table[t // B] * B + t % B through the layout's index functions."""
+                      ctx: int, k_scale: float = 1.0, v_scale: float = 1.0, start: int = 0):
+    """``gather_kv`` element by element: token t (start <= t < ctx) of the
+    sequence is read at slot table[t // B] * B + t % B through the layout's
+    index functions."""
     p = img.shape
-    if ctx == 0:
+    if ctx <= start:
         z = np.zeros((0, p.num_kv_heads, p.head_dim))
         return z, z.copy()
-    pos = np.arange(ctx, dtype=np.int64)
+    pos = np.arange(start, ctx, dtype=np.int64)
     slots = slot_of(block_table_row, pos, p.block_size)
     blk = (slots // p.block_size)[:, None, None]
     t = (slots % p.block_size)[:, None, None]
@@ -123,11 +132,17 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndar
     return out
 
 
+def window_start(ctx: int, window: int) -> int:
+    """First position a window of ``window`` positions keeps (0 = no window)."""
+    return ctx - window if 0 < window < ctx else 0
+
+
 def paged_decode(q_bits: np.ndarray, img: PoolImage, layer: int,
                  block_tables: np.ndarray, context_lens: np.ndarray,
                  scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
-                 seqs=None) -> np.ndarray:
-    """Paged decode for every sequence (or the listed ``seqs``).
+                 seqs=None, window: int = 0) -> np.ndarray:
+    """Paged decode for every sequence (or the listed ``seqs``), attending to
+    the last ``window`` positions only when ``window`` > 0.
 
     q_bits: [S, Hq, D] bf16 bit patterns.  Returns [S, Hq, D] float64 (rows
     of sequences not in ``seqs`` are left zero).
@@ -138,6 +153,6 @@ def paged_decode(q_bits: np.ndarray, img: PoolImage, layer: int,
     idx = range(S) if seqs is None else seqs
     for s in idx:
         ctx = int(context_lens[s])
-        K, V = gather_kv(img, layer, block_tables[s], ctx, k_scale, v_scale)
+        K, V = gather_kv(img, layer, block_tables[s], ctx, k_scale, v_scale, window_start(ctx, window))
         out[s] = attend(codecs.bf16_bits_to_f64(q_bits[s]), K, V, scale)
     return out

@@ -63,6 +63,17 @@ class KVScales(ctypes.Structure):
     _fields_ = [("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [("out", ctypes.c_void_p), ("q", ctypes.c_void_p), ("pool", ctypes.POINTER(PoolDesc)),
+                ("layer", ctypes.c_int32), ("key", ctypes.c_void_p), ("value", ctypes.c_void_p),
+                ("block_tables", ctypes.c_void_p), ("table_width", ctypes.c_int32),
+                ("context_lens", ctypes.c_void_p), ("num_seqs", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("scale", ctypes.c_float), ("kv_dtype", ctypes.c_int32),
+                ("kv_scales", ctypes.POINTER(KVScales)), ("partition_size", ctypes.c_int32),
+                ("sliding_window", ctypes.c_int32), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_uint64)]
+
+
 _P = ctypes.c_void_p
 _I32, _I64, _U64, _F = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
 _I32P = ctypes.POINTER(ctypes.c_int32)
@@ -82,6 +93,7 @@ SIGNATURES = {
                                  _F, _I32, ctypes.POINTER(KVScales), _I32, _P, _U64, _P]),
     "paged_attn_decode_append": (_I32, [_P, _P, ctypes.POINTER(PoolDesc), _I32, _P, _P, _P, _I32, _P, _I32,
                                         _I32, _F, _I32, ctypes.POINTER(KVScales), _I32, _P, _U64, _P]),
+    "paged_attn_decode_ex": (_I32, [ctypes.POINTER(DecodeArgs), _P]),
     "pkv_check_slots": (_I32, [_I64P, _I32, _I64]),
     "pkv_check_pairs": (_I32, [_I64P, _I32, _I32]),
     "pkv_check_tables": (_I32, [_I32P, _I32P, _I32, _I32, _I32, _I32]),
@@ -222,6 +234,29 @@ def paged_attn_decode_append(out, q, pool: Pool, layer: int, key, value, block_t
                                          _ptr(value), _ptr(block_tables), W, _ptr(context_lens), S, hq,
                                          float(scale), kvd, ctypes.byref(sc), partition_size, _ptr(workspace),
                                          ws_bytes, _stream(stream)))
+
+
+def paged_attn_decode_ex(out, q, pool: Pool, layer: int, block_tables, context_lens, scale: float,
+                        kv_dtype: int | None = None, k_scale: float = 1.0, v_scale: float = 1.0,
+                        partition_size: int = 0, workspace=None, key=None, value=None, sliding_window: int = 0,
+                        stream=None):
+    """Decode with every option (see pkv.h): the appending form when key and
+    value are given, attention restricted to the last ``sliding_window``
+    positions when it is > 0."""
+    S, hq, _ = q.shape
+    sc = KVScales(k_scale, v_scale)
+    a = DecodeArgs()
+    a.out, a.q, a.pool, a.layer = _ptr(out), _ptr(q), ctypes.pointer(pool.desc), layer
+    a.key, a.value = _ptr(key), _ptr(value)
+    a.block_tables, a.table_width = _ptr(block_tables), block_tables.shape[1]
+    a.context_lens, a.num_seqs, a.num_q_heads = _ptr(context_lens), S, hq
+    a.scale = float(scale)
+    a.kv_dtype = pool.cfg.kv_dtype if kv_dtype is None else kv_dtype
+    a.kv_scales = ctypes.pointer(sc)
+    a.partition_size, a.sliding_window = partition_size, sliding_window
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.paged_attn_decode_ex(ctypes.byref(a), _stream(stream)))
 
 
 # ------------------------------------------------------------------- checks

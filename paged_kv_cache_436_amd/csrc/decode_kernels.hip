@@ -148,6 +148,27 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 __device__ __forceinline__ int clamp_ctx(int c, int max_ctx) { return c < 0 ? 0 : (c > max_ctx ? max_ctx : c); }
 
+// Sliding window: a row of context ctx attends to positions [lo, ctx),
+// lo = ctx - win when a window of win > 0 positions is set and shorter than
+// the context, else 0.  The row's steps of TS tokens start at the step that
+// holds lo (token base = floor(lo / TS) * TS); blocks before it are not read.
+__device__ __forceinline__ int window_lo(int ctx, int win) { return (win > 0 && ctx > win) ? ctx - win : 0; }
+template <int TS>
+__device__ __forceinline__ int row_base(int ctx, int win) { return window_lo(ctx, win) / TS * TS; }
+template <int TS>
+__device__ __forceinline__ int row_steps(int ctx, int win) { return (ctx - row_base<TS>(ctx, win) + TS - 1) / TS; }
+
+// Byte / half-word masks keeping the tokens of lane slot j that lie in
+// [t_lo, t_end): token tb + i owns byte i (8-bit) or half-word i (bf16 pairs).
+__device__ __forceinline__ bool tok_in(int t, int t_lo, int t_end) { return t < t_end && t >= t_lo; }
+__device__ __forceinline__ uint32_t tok_mask8(int tb, int t_lo, int t_end) {
+  return (tok_in(tb + 0, t_lo, t_end) ? 0x000000ffu : 0u) | (tok_in(tb + 1, t_lo, t_end) ? 0x0000ff00u : 0u) |
+         (tok_in(tb + 2, t_lo, t_end) ? 0x00ff0000u : 0u) | (tok_in(tb + 3, t_lo, t_end) ? 0xff000000u : 0u);
+}
+__device__ __forceinline__ uint32_t tok_mask16(int tb, int t_lo, int t_end) {
+  return (tok_in(tb, t_lo, t_end) ? 0x0000ffffu : 0u) | (tok_in(tb + 1, t_lo, t_end) ? 0xffff0000u : 0u);
+}
+
 // Query dims held by lane slot j of q.K MFMA kk (the same dims the K operand
 // of that slot holds).
 template <int E>
@@ -176,6 +197,7 @@ struct DecodeParams {
   const int32_t* ctx;         // [S]
   int32_t W, S, Hq, Hkv, G, QT, num_blocks;
   int32_t num_items;          // S * Hkv * QT
+  int32_t win;                // sliding window (positions), 0 = whole context
   float qk_scale;             // softmax scale * log2(e) (* fp8 k scale)
   float out_scale;            // fp8 v scale, else 1
 };
@@ -200,7 +222,7 @@ struct StepRegs {
 
 template <int D, int KVT, int B>
 __device__ __forceinline__ void issue_step(StepRegs<D, KVT>& r, const DecodeParams& p, const int32_t* bt_row,
-                                           int g, int tok0, int lane) {
+                                           int g, int tok0, int t_lo, int lane) {
   using T = Tile<D, KVT>;
   constexpr int E = T::E;
   const int row = lane & 15;
@@ -210,7 +232,9 @@ __device__ __forceinline__ void issue_step(StepRegs<D, KVT>& r, const DecodePara
     const int t = tok0 + 16 * h;                   // first token of the chunk (multiple of 16)
     int lb = t / B;
     lb = lb < p.W ? lb : p.W - 1;                  // never index past the table row
-    int phys = bt_row[lb];
+    // a chunk wholly before the window does not use its table entry (block 0
+    // instead; its tokens are masked)
+    int phys = t + 16 > t_lo ? bt_row[lb] : 0;
     phys = phys < 0 ? 0 : (phys >= p.num_blocks ? p.num_blocks - 1 : phys);  // stay inside the pool
     const int toff = t % B;                        // chunk offset inside the block (0 or 16)
     const int64_t tile = ((int64_t)phys * p.Hkv + g) * (int64_t)(B * D * E);
@@ -265,6 +289,7 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
     return;
   }
   const int nsteps = (t_end + kStep - 1) / kStep;
+  const int t_lo = window_lo(t_end, p.win);
   const int32_t* bt_row = p.bt + (int64_t)s * p.W;
 
   // query tile as the B operand of q.K: lane (j, row) holds head row
@@ -313,7 +338,7 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
         const int t = tok0 + 16 * h + 4 * j + i;
         float zz = z[h][i] * p.qk_scale;
         if constexpr (KVT == PKV_KV_INT8) zz *= r.ksc[h][i];
-        zz = t < t_end ? zz : -INFINITY;
+        zz = (t < t_end && t >= t_lo) ? zz : -INFINITY;
         z[h][i] = zz;
         mloc = fmaxf(mloc, zz);
       }
@@ -334,7 +359,7 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
         psum += pv[i];
         if constexpr (KVT == PKV_KV_INT8) {
           const int t = tok0 + 16 * h + 4 * j + i;
-          pv[i] = t < t_end ? pv[i] * r.vsc[h][i] : 0.f;   // fold the V scale into p
+          pv[i] = tok_in(t, t_lo, t_end) ? pv[i] * r.vsc[h][i] : 0.f;   // fold the V scale into p
         }
       }
       ph[h][0] = pack_bf16x2(pv[0], pv[1]);
@@ -346,8 +371,8 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
     const bf16x8 pop = __builtin_bit_cast(bf16x8, u32x4{ph[0][0], ph[0][1], ph[1][0], ph[1][1]});
     const bf16x8 pop_lo = __builtin_bit_cast(bf16x8, u32x4{pl[0][0], pl[0][1], pl[1][0], pl[1][1]});
     // zero V of masked tokens so that garbage (NaN/inf bit patterns in unwritten
-    // slots) cannot reach the accumulator through 0 * NaN
-    const bool tail = tok0 + kStep > t_end;
+    // slots, blocks before a window) cannot reach the accumulator through 0 * NaN
+    const bool edge = tok0 + kStep > t_end || tok0 < t_lo;
 #pragma unroll
     for (int c = 0; c < T::NC; ++c) {
       uint32_t a0, a1, a2, a3;
@@ -362,12 +387,12 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
         widen4<KVT>(r.v[0][u][e], a0, a1);
         widen4<KVT>(r.v[1][u][e], a2, a3);
       }
-      if (tail) {
+      if (edge) {
         const int tb0 = tok0 + 4 * j, tb1 = tok0 + 16 + 4 * j;
-        a0 = tb0 + 0 < t_end ? (tb0 + 1 < t_end ? a0 : (a0 & 0xffffu)) : 0u;
-        a1 = tb0 + 2 < t_end ? (tb0 + 3 < t_end ? a1 : (a1 & 0xffffu)) : 0u;
-        a2 = tb1 + 0 < t_end ? (tb1 + 1 < t_end ? a2 : (a2 & 0xffffu)) : 0u;
-        a3 = tb1 + 2 < t_end ? (tb1 + 3 < t_end ? a3 : (a3 & 0xffffu)) : 0u;
+        a0 &= tok_mask16(tb0, t_lo, t_end);
+        a1 &= tok_mask16(tb0 + 2, t_lo, t_end);
+        a2 &= tok_mask16(tb1, t_lo, t_end);
+        a3 &= tok_mask16(tb1 + 2, t_lo, t_end);
       }
       const bf16x8 aop = __builtin_bit_cast(bf16x8, u32x4{a0, a1, a2, a3});
       acc[c] = acc[c] * alpha;
@@ -376,18 +401,19 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
     }
   };
 
-  // wave w takes steps w, w+NW, ...; loads run one step ahead
+  // wave w takes steps i0 + w, i0 + w + NW, ... (i0: the step holding the
+  // window's first position); loads run one step ahead
   StepRegs<D, KVT> r0, r1;
-  int i = w;
-  if (i < nsteps) issue_step<D, KVT, B>(r0, p, bt_row, g, i * kStep, lane);
+  int i = t_lo / kStep + w;
+  if (i < nsteps) issue_step<D, KVT, B>(r0, p, bt_row, g, i * kStep, t_lo, lane);
   while (i < nsteps) {
     int nx = i + kNW;
-    if (nx < nsteps) issue_step<D, KVT, B>(r1, p, bt_row, g, nx * kStep, lane);
+    if (nx < nsteps) issue_step<D, KVT, B>(r1, p, bt_row, g, nx * kStep, t_lo, lane);
     compute(r0, i * kStep);
     i = nx;
     if (i >= nsteps) break;
     nx = i + kNW;
-    if (nx < nsteps) issue_step<D, KVT, B>(r0, p, bt_row, g, nx * kStep, lane);
+    if (nx < nsteps) issue_step<D, KVT, B>(r0, p, bt_row, g, nx * kStep, t_lo, lane);
     compute(r1, i * kStep);
     i = nx;
   }
@@ -472,6 +498,7 @@ struct SplitParams {
   int32_t PS;                 // steps per partition: P / tokens per step
   int32_t NP;                 // partitions per row: ceil(W * B / P)
   int32_t NWV;                // waves in the grid
+  int32_t win;                // sliding window (positions), 0 = whole context
   uint32_t epoch;             // this call's tag for row_done
   float qk_scale;
   float out_scale;
@@ -544,13 +571,14 @@ __device__ __forceinline__ QRegs<SplitGeo<D, KVT>::KK> load_q(const SplitParams&
 }
 
 // Load the K/V (and int8 scales) of one step.  A chunk at or past t_end -
-// the tail of a row, or any chunk of a step past the wave's range - reads the
-// tile of block 0, head 0 instead: it is masked or never consumed, and the
+// the tail of a row, or any chunk of a step past the wave's range - or wholly
+// before the window's first position reads the tile of block 0, head 0
+// instead: it is masked or never consumed, and the
 // load keeps the number of loads per step fixed, which the compiler's
 // wait-count tracking needs to let later steps' loads stay in flight.
 template <int D, int KVT, int B>
 __device__ __forceinline__ void issue_chunks(SplitBuf<D, KVT>& r, const SplitParams& p, const int (&phys)[2],
-                                             int g, int t0, int t_end, int lane) {
+                                             int g, int t0, int t_lo, int t_end, int lane) {
   using GE = SplitGeo<D, KVT>;
   constexpr int E = GE::E;
   const int row = lane & 15;
@@ -558,7 +586,7 @@ __device__ __forceinline__ void issue_chunks(SplitBuf<D, KVT>& r, const SplitPar
 #pragma unroll
   for (int h = 0; h < GE::CH; ++h) {
     const int t = t0 + 16 * h;
-    const bool live = t < t_end;                   // wave-uniform
+    const bool live = t < t_end && t + 16 > t_lo;  // wave-uniform
     const int toff = live ? t % B : 0;
     const int64_t tile = live ? ((int64_t)phys[h] * p.Hkv + g) : 0;
     const char* kt = p.k + tile * (int64_t)(B * D * E);
@@ -679,20 +707,11 @@ __device__ __forceinline__ void append_token(const SplitParams& p, int s, int g,
 // segment instead of every step.  Any reference gives the same softmax.
 constexpr float kRescaleSlack = 8.0f;
 
-// Byte / half-word masks keeping the tokens of lane slot j that lie below
-// t_end: token t0 + 4j + i owns byte i (8-bit) or half-word i (bf16 pairs).
-__device__ __forceinline__ uint32_t tok_mask8(int tb, int t_end) {
-  return (tb + 0 < t_end ? 0x000000ffu : 0u) | (tb + 1 < t_end ? 0x0000ff00u : 0u) |
-         (tb + 2 < t_end ? 0x00ff0000u : 0u) | (tb + 3 < t_end ? 0xff000000u : 0u);
-}
-__device__ __forceinline__ uint32_t tok_mask16(int tb, int t_end) {
-  return (tb < t_end ? 0x0000ffffu : 0u) | (tb + 1 < t_end ? 0xffff0000u : 0u);
-}
-
 // Online-softmax update of (m_run, l_run, acc) with one step.
 template <int D, int KVT>
 __device__ __forceinline__ void compute_step(const SplitBuf<D, KVT>& r, const QRegs<SplitGeo<D, KVT>::KK>& qop,
-                                             const SplitParams& p, int t0, int t_end, int lane, float& m_run,
+                                             const SplitParams& p, int t0, int t_lo, int t_end, int lane,
+                                             float& m_run,
                                              float& l_run, f32x4* acc) {
   using GE = SplitGeo<D, KVT>;
   constexpr int E = GE::E;
@@ -723,7 +742,7 @@ __device__ __forceinline__ void compute_step(const SplitBuf<D, KVT>& r, const QR
       const int t = t0 + 16 * h + 4 * j + i;
       float zz = z[h][i] * p.qk_scale;
       if constexpr (KVT == PKV_KV_INT8) zz *= r.ksc[h][i];
-      zz = t < t_end ? zz : -INFINITY;
+      zz = (t < t_end && t >= t_lo) ? zz : -INFINITY;
       z[h][i] = zz;
       mloc = fmaxf(mloc, zz);
     }
@@ -750,7 +769,7 @@ __device__ __forceinline__ void compute_step(const SplitBuf<D, KVT>& r, const QR
       psum += pv[i];
       if constexpr (KVT == PKV_KV_INT8) {
         const int t = t0 + 16 * h + 4 * j + i;
-        pv[i] = t < t_end ? pv[i] * r.vsc[h][i] : 0.f;   // fold the V scale into p
+        pv[i] = tok_in(t, t_lo, t_end) ? pv[i] * r.vsc[h][i] : 0.f;   // fold the V scale into p
       }
     }
     ph[h][0] = pack_bf16x2(pv[0], pv[1]);
@@ -759,24 +778,25 @@ __device__ __forceinline__ void compute_step(const SplitBuf<D, KVT>& r, const QR
     pl[h][1] = pack_bf16x2(pv[2] - bf16_lo(ph[h][1]), pv[3] - bf16_hi(ph[h][1]));
   }
   l_run = l_run * alpha + psum;
-  // V of tokens at or past t_end is zeroed so that unwritten slots (any bit
-  // pattern) cannot reach the accumulator through 0 * NaN (wave-uniform branch)
+  // V of tokens outside [t_lo, t_end) is zeroed so that unwritten slots and
+  // blocks before a window (any bit pattern) cannot reach the accumulator
+  // through 0 * NaN (wave-uniform branch)
   u32x4 v[CH][GE::LPC];
 #pragma unroll
   for (int h = 0; h < CH; ++h)
 #pragma unroll
     for (int u = 0; u < GE::LPC; ++u) v[h][u] = r.v[h][u];
-  if (t0 + GE::TS > t_end) {
+  if (t0 + GE::TS > t_end || t0 < t_lo) {
 #pragma unroll
     for (int h = 0; h < CH; ++h) {
       const int tb = t0 + 16 * h + 4 * j;
       if constexpr (E == 2) {
-        const u32x4 m = u32x4{tok_mask16(tb, t_end), tok_mask16(tb + 2, t_end), tok_mask16(tb, t_end),
-                              tok_mask16(tb + 2, t_end)};
+        const u32x4 m = u32x4{tok_mask16(tb, t_lo, t_end), tok_mask16(tb + 2, t_lo, t_end),
+                              tok_mask16(tb, t_lo, t_end), tok_mask16(tb + 2, t_lo, t_end)};
 #pragma unroll
         for (int u = 0; u < GE::LPC; ++u) v[h][u] &= m;
       } else {
-        const uint32_t m = tok_mask8(tb, t_end);
+        const uint32_t m = tok_mask8(tb, t_lo, t_end);
 #pragma unroll
         for (int u = 0; u < GE::LPC; ++u) v[h][u] &= u32x4{m, m, m, m};
       }
@@ -812,8 +832,9 @@ __device__ __forceinline__ void compute_step(const SplitBuf<D, KVT>& r, const QR
 // constants of its row (recomputed only when the row changes).
 struct Cursor {
   int s, xi, j;     // sequence, row within the sequence, step within the row
-  int n;            // steps of sequence s's rows
+  int n;            // steps of sequence s's rows (from the window's first step)
   int ctx;          // context length of sequence s
+  int tb;           // first token of the rows' first step (window start, rounded down)
   int g;            // KV head of the row
   int h0, gt;       // first query head of the row's tile, and its number of heads
   int unit;         // x * NP + partition of step j (x = s * HQ + xi)
@@ -837,7 +858,7 @@ __device__ __forceinline__ void cursor_tables(Cursor& c, const SplitParams& p) {
   const int32_t* row = p.bt + (int64_t)c.s * p.W;
 #pragma unroll
   for (int h = 0; h < TS / 16; ++h) {
-    int lb = (c.j * TS + 16 * h) / B;
+    int lb = (c.tb + c.j * TS + 16 * h) / B;
     lb = lb < p.W ? lb : p.W - 1;                  // never index past the table row
     int phys = uniform_load(row + lb);
     c.phys[h] = phys < 0 ? 0 : (phys >= p.num_blocks ? p.num_blocks - 1 : phys);  // stay inside the pool
@@ -1024,7 +1045,7 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
     load_ctx(base);
 #pragma unroll
     for (int k = 0; k < kSeqRegs; ++k) {
-      const int n = (cv[k] + TS - 1) / TS;
+      const int n = row_steps<TS>(cv[k], p.win);
       total += wave_sum(n);
       if (w == 0) {
         const int b0 = base + k * kWave;
@@ -1058,7 +1079,7 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
       for (int k = 0; k < kSeqRegs; ++k) {
         if (found) break;
         const int c = cv[k];
-        const int n = (c + TS - 1) / TS;
+        const int n = row_steps<TS>(c, p.win);
         const int incl = wave_incl_scan(n, lane);
         const bool hit = (acc0 + incl - n) * p.HQ <= start && start < (acc0 + incl) * p.HQ;
         const uint64_t m = __ballot(hit);
@@ -1080,6 +1101,7 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
   cur.s = __builtin_amdgcn_readfirstlane(cur.s);
   cur.n = __builtin_amdgcn_readfirstlane(cur.n);
   cur.ctx = __builtin_amdgcn_readfirstlane(cur.ctx);
+  cur.tb = row_base<TS>(cur.ctx, p.win);
   cur.xi = __builtin_amdgcn_readfirstlane(cur.xi);
   cur.j = __builtin_amdgcn_readfirstlane(cur.j);
   cum0 = __builtin_amdgcn_readfirstlane(cum0);
@@ -1100,7 +1122,7 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
         do {
           ++as;
           actx = clamp_ctx(uniform_load(p.ctx + as), max_ctx);
-          an = (actx + TS - 1) / TS;
+          an = row_steps<TS>(actx, p.win);
         } while (an == 0);
       }
     }
@@ -1127,11 +1149,11 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
     const bool new_row = live && (cur.j == 0 || issued == 0);
     if (new_row) qr = load_q<D, KVT>(p, cur.s, cur.h0, cur.gt, lane);
     const bool flush = issued + 1 == nsteps || cur.j + 1 == cur.n || cur.pleft == 1;
-    m.t0 = cur.j * TS;
+    m.t0 = cur.tb + cur.j * TS;
     m.t_end = live ? cur.ctx : 0;
     m.slot = cur.unit + w;
     m.flags = (new_row ? kNewRow : 0) | (flush ? kFlush : 0) | (cur.gt << 8);
-    issue_chunks<D, KVT, B>(r, p, cur.phys, cur.g, m.t0, m.t_end, lane);
+    issue_chunks<D, KVT, B>(r, p, cur.phys, cur.g, m.t0, window_lo(m.t_end, p.win), m.t_end, lane);
     ++issued;
     if (issued < nsteps) {     // advance to the next step and fetch its table entries
       if (--cur.pleft == 0) {
@@ -1145,8 +1167,9 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
           do {
             ++cur.s;
             cur.ctx = clamp_ctx(uniform_load(p.ctx + cur.s), max_ctx);
-            cur.n = (cur.ctx + TS - 1) / TS;
+            cur.n = row_steps<TS>(cur.ctx, p.win);
           } while (cur.n == 0);
+          cur.tb = row_base<TS>(cur.ctx, p.win);
         }
         cursor_row(cur, p);
       }
@@ -1163,7 +1186,7 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
   auto consume = [&](const SplitBuf<D, KVT>& r, const StepMeta& m, const QRegs<GE::KK>& qr)
                      __attribute__((always_inline)) {
     if (m.flags & kNewRow) qop = qr;
-    compute_step<D, KVT>(r, qop, p, m.t0, m.t_end, lane, m_run, l_run, acc);
+    compute_step<D, KVT>(r, qop, p, m.t0, window_lo(m.t_end, p.win), m.t_end, lane, m_run, l_run, acc);
     if (m.flags & kFlush) {
       const float l = sum_x32(sum_x16(l_run));
       const int gt = m.flags >> 8;
@@ -1230,7 +1253,7 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
         rcum += rn;
         do {
           ++rs;
-          rn = (clamp_ctx(uniform_load(p.ctx + rs), max_ctx) + TS - 1) / TS;
+          rn = row_steps<TS>(clamp_ctx(uniform_load(p.ctx + rs), max_ctx), p.win);
         } while (rn == 0);
       }
     }
@@ -1408,8 +1431,8 @@ namespace {
 pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t layer, const void* key,
                        const void* value, const int32_t* block_tables, int32_t table_width,
                        const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
-                       int32_t kv_dtype, const pkv_kv_scales* kv_scales, int32_t partition_size, void* workspace,
-                       uint64_t workspace_bytes, hipStream_t stream) {
+                       int32_t kv_dtype, const pkv_kv_scales* kv_scales, int32_t partition_size,
+                       int32_t sliding_window, void* workspace, uint64_t workspace_bytes, hipStream_t stream) {
   const bool append = key != nullptr || value != nullptr;
   pkv_status st = check_pool(pool);
   if (st != PKV_OK) return st;
@@ -1426,6 +1449,7 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
   if (num_seqs == 0) { clear_error(); return PKV_OK; }
   if (!out || !q || !block_tables || !context_lens) return fail(PKV_ERR_INVALID, "NULL device pointer");
   if (append && (!key || !value)) return fail(PKV_ERR_INVALID, "key and value must both be given");
+  if (sliding_window < 0) return fail(PKV_ERR_INVALID, "sliding_window is negative");
   if (append && partition_size == 0)
     return fail(PKV_ERR_UNSUPPORTED, "the appending decode runs in the split-context form (partition_size > 0)");
   if (append && ((uintptr_t)key % 16 || (uintptr_t)value % 16))
@@ -1483,6 +1507,7 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     p.QT = QT;
     p.num_blocks = c.num_blocks;
     p.num_items = (int32_t)rows;
+    p.win = sliding_window;
     p.qk_scale = scale * kLog2e * ksc;
     p.out_scale = vsc;
     e = c.head_dim == 64 ? launch_single_kv<64>(p, c.kv_dtype, c.block_size, (int)grid, stream)
@@ -1541,6 +1566,7 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     p.PS = partition_size / TS;
     p.NP = (int32_t)np;
     p.NWV = (int32_t)(grid * kNW);
+    p.win = sliding_window;
     p.epoch = next_epoch();
     p.qk_scale = scale * kLog2e * ksc;
     p.out_scale = vsc;
@@ -1565,7 +1591,8 @@ extern "C" pkv_status paged_attn_decode(float* out, const void* q, const pkv_poo
                                         int32_t partition_size, void* workspace, uint64_t workspace_bytes,
                                         hipStream_t stream) {
   return decode_impl(out, q, pool, layer, nullptr, nullptr, block_tables, table_width, context_lens, num_seqs,
-                     num_q_heads, scale, kv_dtype, kv_scales, partition_size, workspace, workspace_bytes, stream);
+                     num_q_heads, scale, kv_dtype, kv_scales, partition_size, 0, workspace, workspace_bytes,
+                     stream);
 }
 
 extern "C" pkv_status paged_attn_decode_append(float* out, const void* q, const pkv_pool* pool, int32_t layer,
@@ -1577,5 +1604,14 @@ extern "C" pkv_status paged_attn_decode_append(float* out, const void* q, const 
                                                uint64_t workspace_bytes, hipStream_t stream) {
   if (!key || !value) return fail(PKV_ERR_INVALID, "key and value must be non-NULL");
   return decode_impl(out, q, pool, layer, key, value, block_tables, table_width, context_lens, num_seqs,
-                     num_q_heads, scale, kv_dtype, kv_scales, partition_size, workspace, workspace_bytes, stream);
+                     num_q_heads, scale, kv_dtype, kv_scales, partition_size, 0, workspace, workspace_bytes,
+                     stream);
+}
+
+extern "C" pkv_status paged_attn_decode_ex(const pkv_decode_args* a, hipStream_t stream) {
+  if (!a) return fail(PKV_ERR_INVALID, "NULL argument block");
+  if ((a->key == nullptr) != (a->value == nullptr)) return fail(PKV_ERR_INVALID, "key and value must both be given");
+  return decode_impl(a->out, a->q, a->pool, a->layer, a->key, a->value, a->block_tables, a->table_width,
+                     a->context_lens, a->num_seqs, a->num_q_heads, a->scale, a->kv_dtype, a->kv_scales,
+                     a->partition_size, a->sliding_window, a->workspace, a->workspace_bytes, stream);
 }

@@ -1,0 +1,133 @@
+"""Sliding-window decode on the GPU against the oracle (paged_attn_decode_ex).
+
+Table entries of blocks wholly before each window point at a spare block
+filled with 0xFF bytes (NaN bf16 / NaN e5m2 / NaN int8 scales): any read of
+them would reach the output.  Both forms (single pass, split) and the
+appending form are covered; a window covering the context must give the
+plain decode's bits.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_436_amd as pkv
+import workloads
+from oracle import attention, cache_ops
+from tests.gpu_helpers import bf16_dev, dev, errors, say
+from tests.test_gpu_decode import BAR, build_case, run_decode
+
+pytestmark = pytest.mark.gpu
+
+
+def _spare_block(c, tables):
+    used = set(int(b) for s in range(len(c.ctx)) for b in tables[s, :math.ceil(int(c.ctx[s]) / c.cfg.block_size)])
+    return next(b for b in range(c.cfg.num_blocks) if b not in used)
+
+
+def _poison_leading(c, window, tables):
+    """From the original ``tables``, point every entry wholly before a window
+    at a poisoned block."""
+    B = c.cfg.block_size
+    spare = _spare_block(c, tables)
+    c.tables = tables.copy()
+    for s in range(len(c.ctx)):
+        first = attention.window_start(int(c.ctx[s]), window) // B
+        c.tables[s, :first] = spare
+    c.d_tables = dev(c.tables)
+
+
+def _run_ex(c, P, window, key=None, value=None):
+    import torch
+    D = c.cfg.head_dim
+    S = len(c.ctx)
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
+    out = torch.full((S, c.hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    ws = None
+    if P:
+        ws = torch.randint(0, 256, (pkv.paged_attn_workspace_bytes(S, c.hq, D, c.width, c.cfg.block_size, P),),
+                           dtype=torch.uint8, device="cuda")
+    pkv.paged_attn_decode_ex(out, c.d_q, c.pool, 0, c.d_tables, c.d_ctx, scale, c.cfg.kv_dtype, c.kscale,
+                             c.vscale, P, ws, key=key, value=value, sliding_window=window)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), scale
+
+
+@pytest.mark.parametrize("dt", [pkv.PKV_KV_BF16, pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8])
+@pytest.mark.parametrize("D,B", [(128, 16), (64, 32), (128, 32)])
+@pytest.mark.parametrize("P", [0, 32, 512])
+def test_window_matches_oracle(dt, D, B, P):
+    rng = np.random.default_rng(9100 + 7 * dt + D + B + P)
+    ctx = [1, 15, 16, 17, 33, 100, 257, 600, 0, 1030]
+    hkv, G = (2, 4) if D == 128 else (1, 3)
+    ks, vs = (0.75, 1.25) if dt == pkv.PKV_KV_FP8_E5M2 else (1.0, 1.0)
+    c = build_case(rng, len(ctx), hkv, G, D, B, dt, ctx, ks, vs, poison=True)
+    tables = c.tables.copy()
+    for window in (1, 15, 16, 17, 100, 513):
+        say(f"window dt={dt} D={D} B={B} P={P} w={window}")
+        _poison_leading(c, window, tables)
+        got, scale = _run_ex(c, P, window)
+        want = attention.paged_decode(c.q, c.img, 0, c.tables, c.ctx, scale, ks, vs, window=window)
+        assert np.all(np.isfinite(got)), f"w={window}: non-finite output (a block before the window was read?)"
+        mx, rel = errors(got, want)
+        say(f"  max_abs={mx:.3e} rel={rel:.3e}")
+        assert mx <= BAR[dt][0] and rel <= BAR[dt][1], window
+        assert not got[c.ctx == 0].any()
+
+
+@pytest.mark.parametrize("P", [0, 64])
+def test_window_covering_every_context_gives_the_plain_decode_bits(P):
+    rng = np.random.default_rng(9200 + P)
+    c = build_case(rng, 6, 2, 4, 128, 16, pkv.PKV_KV_BF16, [1, 5, 17, 31, 300, 77])
+    plain, _ = run_decode(c, P)
+    for window in (300, 301, 1 << 20):
+        got, _ = _run_ex(c, P, window)
+        assert np.array_equal(got.view(np.uint32), plain.view(np.uint32)), window
+
+
+@pytest.mark.parametrize("dt", [pkv.PKV_KV_BF16, pkv.PKV_KV_INT8])
+def test_window_with_appending_decode(dt):
+    # the appending form under a window: same pool bytes and output bits as
+    # reshape_and_cache followed by the windowed decode
+    import torch
+    rng = np.random.default_rng(9300 + dt)
+    ctx = [1, 16, 17, 40, 300, 513]
+    hist = [c - 1 for c in ctx]
+    B, D, hkv, G, P, window = 16, 128, 2, 4, 64, 50
+    c = build_case(rng, len(ctx), hkv, G, D, B, dt, hist, spare=len(ctx) + 3, poison=True,
+                   width=math.ceil(max(ctx) / B))
+    used = set(int(b) for s in range(len(ctx)) for b in c.tables[s, :math.ceil(hist[s] / B)])
+    free = [b for b in range(c.cfg.num_blocks) if b not in used]
+    for s in range(len(ctx)):
+        for i in range(math.ceil(hist[s] / B), math.ceil(ctx[s] / B)):
+            c.tables[s, i] = free.pop()
+    c.ctx = np.asarray(ctx, np.int32)
+    c.d_ctx = dev(c.ctx)
+    c.d_tables = dev(c.tables)
+    kn = workloads.to_bf16_bits(rng.standard_normal((len(ctx), hkv, D), dtype=np.float32))
+    vn = workloads.to_bf16_bits(rng.standard_normal((len(ctx), hkv, D), dtype=np.float32))
+    slots = np.array([attention.slot_of(c.tables[s], ctx[s] - 1, B) for s in range(len(ctx))], np.int64)
+    before = c.pool.memory.clone()
+    pkv.reshape_and_cache(c.pool, 0, bf16_dev(kn), bf16_dev(vn), dev(slots))
+    got_a, scale = _run_ex(c, P, window)
+    pool_a = c.pool.memory.clone()
+    c.pool.memory.copy_(before)
+    got_b, _ = _run_ex(c, P, window, key=bf16_dev(kn), value=bf16_dev(vn))
+    assert torch.equal(pool_a, c.pool.memory)
+    assert np.array_equal(got_a.view(np.uint32), got_b.view(np.uint32))
+    img = cache_ops.reshape_and_cache(c.img, 0, kn, vn, slots)
+    want = attention.paged_decode(c.q, img, 0, c.tables, c.ctx, scale, window=window)
+    mx, rel = errors(got_b, want)
+    say(f"window append dt={dt}: max_abs={mx:.3e} rel={rel:.3e}")
+    assert mx <= BAR[dt][0] and rel <= BAR[dt][1]
+
+
+def test_negative_window_is_rejected():
+    import torch
+    rng = np.random.default_rng(9400)
+    c = build_case(rng, 2, 2, 2, 128, 16, pkv.PKV_KV_BF16, [10, 20])
+    out = torch.empty((2, 4, 128), dtype=torch.float32, device="cuda")
+    with pytest.raises(pkv.PkvError) as e:
+        pkv.paged_attn_decode_ex(out, c.d_q, c.pool, 0, c.d_tables, c.d_ctx, 0.1, sliding_window=-1)
+    assert e.value.status == pkv.PKV_ERR_INVALID

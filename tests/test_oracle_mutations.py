@@ -2,7 +2,7 @@
 
 Each case monkeypatches one plausible slip into the oracle and re-runs a pin
 that should then fail: a transposed grouping, a slot off by one, a dropped
-softmax scale, a wrong e5m2 exponent bias.
+softmax scale, a wrong e5m2 exponent bias, a window one position too wide.
 """
 
 import numpy as np
@@ -13,6 +13,7 @@ import oracle.codecs as codecs
 from tests import test_oracle_attention as ta
 from tests import test_oracle_codecs as tc
 from tests import test_oracle_paging as tp
+from tests import test_oracle_window as tw
 from oracle import layout
 
 
@@ -63,3 +64,9 @@ def test_wrong_e5m2_bias_is_caught(monkeypatch):
     orig = codecs.e5m2_decode
     monkeypatch.setattr(codecs, "e5m2_decode", lambda c: orig(c) * 2.0)
     assert _fails(tc.test_e5m2_decode_matches_binary16_high_byte)
+
+
+def test_window_off_by_one_is_caught(monkeypatch):
+    orig = att.window_start
+    monkeypatch.setattr(att, "window_start", lambda ctx, w: max(orig(ctx, w) - 1, 0))
+    assert _fails(lambda: tw.test_window_matches_masked_sdpa(3))
