@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window: each layer's call attends to the last N positions only "
                          "(paged_attn_decode_ex; bytes counted over those positions)")
+    ap.add_argument("--swap", type=int, default=0,
+                    help="instead of the decode step: swap N blocks of the 70B-shaped pool out to pinned host "
+                         "memory and back (swap_blocks), and report GB/s each way")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB three times (torch copy kernel): the reference for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -86,6 +89,57 @@ def measured_traffic():
     return int(m.group(1))
 
 
+HOST_LINK_GBS = 64.0     # PCIe Gen5 x16, one direction
+
+
+def swap_bench(args):
+    """swap_blocks of N blocks (80 layers, K and V: 2.6 MB each in the 70B
+    shape) device -> pinned host -> device, timed with HIP events; the bytes
+    are checked to come back unchanged."""
+    import torch
+
+    import paged_kv_cache_436_amd as pkv
+    import workloads
+
+    w = workloads.llama70b(num_layers=80, extra_steps=1)
+    n = args.swap
+    cfg = pkv.make_config(80, n, w.block_size, w.num_kv_heads, w.head_dim, pkv.PKV_KV_BF16)
+    nbytes = pkv.kv_pool_bytes(cfg)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(436005)
+    dev_mem = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
+    host_mem = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    back_mem = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src, host, back = pkv.Pool(cfg, memory=dev_mem), pkv.Pool(cfg, memory=host_mem), pkv.Pool(cfg, memory=back_mem)
+    rng = np.random.default_rng(436005)
+    out_pairs = torch.from_numpy(np.stack([np.arange(n), rng.permutation(n)], 1).astype(np.int64)).cuda()
+    in_pairs = torch.from_numpy(np.stack([out_pairs[:, 1].cpu().numpy(), np.arange(n)], 1)).cuda()
+    moved = n * 80 * 2 * w.num_kv_heads * w.block_size * w.head_dim * 2
+    st = torch.cuda.current_stream()
+    times = {"out": [], "in": []}
+    for rep in range(args.warmup + args.steps):
+        for name, a, b, pr in (("out", src, host, out_pairs), ("in", host, back, in_pairs)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            pkv.swap_blocks(a, b, pr, stream=st)
+            e1.record(st)
+            torch.cuda.synchronize()
+            if rep >= args.warmup:
+                times[name].append(e0.elapsed_time(e1) * 1e-3)
+    assert torch.equal(back_mem[:nbytes], dev_mem), "swap round trip changed bytes"
+    gbs = {k: moved / float(np.median(v)) / 1e9 for k, v in times.items()}
+    res = {"metric": "swap_blocks GB/s (device -> pinned host, host -> device)",
+           "value": round(min(gbs.values()), 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": True, "dtype": "u8", "data": "synthetic",
+           "config": {"workload": f"swap {n} blocks of the 70B-shaped pool (80 layers, 8 KV heads, head_dim 128, "
+                                  "bf16, block 16) out and back", "bytes_each_way": moved},
+           "swap_out_gbs": round(gbs["out"], 2), "swap_in_gbs": round(gbs["in"], 2),
+           "roofline": {"bound": "host link", "peak": HOST_LINK_GBS, "unit": "GB/s",
+                        "achieved": round(min(gbs.values()), 2),
+                        "frac": round(min(gbs.values()) / HOST_LINK_GBS, 4)}}
+    print(json.dumps(res), flush=True)
+
+
 def copy_calibration():
     """A plain device copy of known size, for calibrating HBM byte counters."""
     import torch
@@ -104,6 +158,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.swap:
+        swap_bench(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",

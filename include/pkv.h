@@ -159,6 +159,23 @@ pkv_status reshape_and_cache(const pkv_pool* pool, int32_t layer, const void* ke
 pkv_status copy_blocks(const pkv_pool* pool, const int64_t* pairs, int32_t num_pairs,
                        hipStream_t stream);
 
+/* Offload and restore: for each row (src, dst) of pairs (device, int64
+ * [num_pairs][2]) copy block src of pool `from` to block dst of pool `to` in
+ * every layer - K tile, V tile and int8 scale rows - byte for byte.  The
+ * bjdmk.com.cn article, §6.1, moves the KV blocks of preempted or idle
+ * requests to CPU memory and brings them back when the request is scheduled
+ * again (aiworkagent.org question 17, 进阶 item 5: offloading cold KV).  The
+ * two pools must have the same configuration apart from num_blocks
+ * (PKV_ERR_INVALID otherwise).  Either may live in device memory or in pinned
+ * host memory (hipHostMalloc, torch pin_memory) described with
+ * kv_pool_create: one kernel reads and writes both directly, host memory
+ * through its device mapping; pageable host memory is refused with
+ * PKV_ERR_INVALID before any launch.  A pair with src outside [0, from NB) or
+ * dst outside [0, to NB) is skipped; a repeated dst races.  Asynchronous on
+ * stream: host memory written by a swap-out is complete once the stream is. */
+pkv_status swap_blocks(const pkv_pool* from, const pkv_pool* to, const int64_t* pairs, int32_t num_pairs,
+                       hipStream_t stream);
+
 /* ------------------------------------------------------------- decode */
 
 /* Workspace bytes paged_attn_decode needs for these sizes on the current

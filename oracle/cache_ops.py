@@ -100,6 +100,35 @@ def copy_blocks(img: PoolImage, pairs: np.ndarray, inplace: bool = False) -> Poo
     return out
 
 
+def swap_blocks(src_img: PoolImage, dst_img: PoolImage, pairs: np.ndarray) -> PoolImage:
+    """Offload / restore (bjdmk.com.cn article, §6.1: blocks move to CPU
+    memory and back).  Return a copy of ``dst_img`` where, in every layer,
+    block dst holds a byte copy of block src of ``src_img`` for each (src,
+    dst) row of ``pairs``; the two images have the same shape apart from
+    num_blocks.  A row with src or dst outside its image's blocks is
+    skipped."""
+    ps, pd = src_img.shape, dst_img.shape
+    assert (ps.num_layers, ps.block_size, ps.num_kv_heads, ps.head_dim, ps.kv_dtype) == \
+        (pd.num_layers, pd.block_size, pd.num_kv_heads, pd.head_dim, pd.kv_dtype)
+    out = dst_img.copy()
+    te = ps.tile_elems
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        if not (0 <= src < ps.num_blocks and 0 <= dst < pd.num_blocks):
+            continue
+        for layer in range(ps.num_layers):
+            for h in range(ps.num_kv_heads):
+                s0 = int(tile_base(ps, layer, src, h))
+                d0 = int(tile_base(pd, layer, dst, h))
+                out.k[d0:d0 + te] = src_img.k[s0:s0 + te]
+                out.v[d0:d0 + te] = src_img.v[s0:s0 + te]
+                if ps.has_scales:
+                    ss = int(scale_offset(ps, layer, src, h, 0))
+                    ds = int(scale_offset(pd, layer, dst, h, 0))
+                    out.k_scale[ds:ds + ps.block_size] = src_img.k_scale[ss:ss + ps.block_size]
+                    out.v_scale[ds:ds + ps.block_size] = src_img.v_scale[ss:ss + ps.block_size]
+    return out
+
+
 def _snapshot_blocks(img: PoolImage, blocks: np.ndarray) -> PoolImage:
     """An image holding copies of the listed blocks' tiles and scale rows (in
     every layer) at their own positions; other positions are never read."""

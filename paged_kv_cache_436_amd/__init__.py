@@ -88,6 +88,7 @@ SIGNATURES = {
     "reshape_and_cache": (_I32, [ctypes.POINTER(PoolDesc), _I32, _P, _P, _P, _I32,
                                  ctypes.POINTER(KVScales), _P]),
     "copy_blocks": (_I32, [ctypes.POINTER(PoolDesc), _P, _I32, _P]),
+    "swap_blocks": (_I32, [ctypes.POINTER(PoolDesc), ctypes.POINTER(PoolDesc), _P, _I32, _P]),
     "paged_attn_workspace_bytes": (_U64, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "paged_attn_decode": (_I32, [_P, _P, ctypes.POINTER(PoolDesc), _I32, _P, _I32, _P, _I32, _I32,
                                  _F, _I32, ctypes.POINTER(KVScales), _I32, _P, _U64, _P]),
@@ -197,6 +198,14 @@ def reshape_and_cache(pool: Pool, layer: int, key, value, slot_mapping, k_scale:
 def copy_blocks(pool: Pool, pairs, stream=None):
     n = int(pairs.numel() // 2)
     _check(_lib.copy_blocks(ctypes.byref(pool.desc), _ptr(pairs), n, _stream(stream)))
+
+
+def swap_blocks(src: Pool, dst: Pool, pairs, stream=None):
+    """Copy block pairs[i][0] of ``src`` to block pairs[i][1] of ``dst`` in
+    every layer (pairs: device int64 [n][2]); either pool may be in pinned
+    host memory."""
+    n = int(pairs.numel() // 2)
+    _check(_lib.swap_blocks(ctypes.byref(src.desc), ctypes.byref(dst.desc), _ptr(pairs), n, _stream(stream)))
 
 
 def paged_attn_workspace_bytes(num_seqs, num_q_heads, head_dim, table_width, block_size, partition_size) -> int:

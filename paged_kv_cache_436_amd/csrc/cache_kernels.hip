@@ -6,7 +6,9 @@
 // V_t are computed and appended; §三 工作方式 steps 2-3), quantising on the way
 // in for 8-bit storage (same page, §四; bjdmk.com.cn article, §5.2 per-token-
 // head scales).  copy_blocks copies a shared block before its writer is
-// repointed (bjdmk.com.cn article, §3.2 Copy-on-Write).
+// repointed (bjdmk.com.cn article, §3.2 Copy-on-Write).  swap_blocks moves
+// blocks between the device pool and a pool in pinned host memory, for
+// requests that are preempted and later resumed (same article, §6.1).
 #include <hip/hip_runtime.h>
 
 #include "pkv_codecs.h"
@@ -106,6 +108,77 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(
   for (uint64_t i = threadIdx.x; i < n16; i += blockDim.x) d[i] = s[i];
 }
 
+// One workgroup per (pair, layer, region), copying between two pools of the
+// same shape; either may be pinned host memory that the device reads and
+// writes directly over the host link.  Four 16-byte loads per thread are in
+// flight before their stores, to cover that link's latency.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(
+    const int64_t* __restrict__ pairs, int32_t num_pairs, int32_t num_layers, int32_t src_blocks,
+    int32_t dst_blocks, const char* __restrict__ sk, const char* __restrict__ sv, const char* __restrict__ sks,
+    const char* __restrict__ svs, char* __restrict__ dk, char* __restrict__ dv, char* __restrict__ dks,
+    char* __restrict__ dvs, uint64_t block_bytes, uint64_t scale_block_bytes) {
+  const int pi = blockIdx.x / num_layers;
+  const int layer = blockIdx.x % num_layers;
+  const int region = blockIdx.y;  // 0 K, 1 V, 2 K scales, 3 V scales
+  if (pi >= num_pairs) return;
+  const int64_t src = pairs[2 * pi], dst = pairs[2 * pi + 1];
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const char* sbase = region == 0 ? sk : region == 1 ? sv : region == 2 ? sks : svs;
+  char* dbase = region == 0 ? dk : region == 1 ? dv : region == 2 ? dks : dvs;
+  const uint64_t bytes = region < 2 ? block_bytes : scale_block_bytes;
+  const uint4* s = reinterpret_cast<const uint4*>(sbase + ((uint64_t)layer * src_blocks + (uint64_t)src) * bytes);
+  uint4* d = reinterpret_cast<uint4*>(dbase + ((uint64_t)layer * dst_blocks + (uint64_t)dst) * bytes);
+  const uint64_t n16 = bytes / 16;
+  constexpr int U = 4;
+  uint64_t i = threadIdx.x;
+  for (; i + (U - 1) * blockDim.x < n16; i += U * blockDim.x) {
+    uint4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = s[i + u * blockDim.x];
+#pragma unroll
+    for (int u = 0; u < U; ++u) d[i + u * blockDim.x] = x[u];
+  }
+  for (; i < n16; i += blockDim.x) d[i] = s[i];
+}
+
+// Device address of memory a pool description points into: device memory as
+// it is, pinned host memory through its device mapping; anything else (for
+// instance pageable host memory) is refused.
+bool device_view(const void* p, const char* what, char** out) {
+  hipPointerAttribute_t a{};
+  const hipError_t e = hipPointerGetAttributes(&a, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();   // do not leave the error for the next launch check
+    set_error("%s: not device or pinned host memory (%s)", what, hipGetErrorString(e));
+    return false;
+  }
+  if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) {
+    *out = static_cast<char*>(const_cast<void*>(p));
+    return true;
+  }
+  if (a.type == hipMemoryTypeHost && a.devicePointer && a.hostPointer) {
+    // pinned host memory: its device mapping must also be known to
+    // hipHostGetDevicePointer, which refuses anything not allocated or
+    // registered as pinned
+    void* d = nullptr;
+    if (hipHostGetDevicePointer(&d, const_cast<void*>(p), 0) != hipSuccess || !d) {
+      (void)hipGetLastError();
+      set_error("%s: host memory is not pinned for the device", what);
+      return false;
+    }
+    const char* host = static_cast<const char*>(a.hostPointer);
+    char* mapped = static_cast<char*>(a.devicePointer) + (static_cast<const char*>(p) - host);
+    if (mapped != static_cast<char*>(d)) {
+      set_error("%s: inconsistent device mapping of pinned host memory", what);
+      return false;
+    }
+    *out = mapped;
+    return true;
+  }
+  set_error("%s: memory is not mapped for the device", what);
+  return false;
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -189,6 +262,47 @@ extern "C" pkv_status copy_blocks(const pkv_pool* pool, const int64_t* pairs, in
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("copy_blocks launch failed: %s", hipGetErrorString(e));
+    return PKV_ERR_HIP;
+  }
+  clear_error();
+  return PKV_OK;
+}
+
+extern "C" pkv_status swap_blocks(const pkv_pool* from, const pkv_pool* to, const int64_t* pairs,
+                                  int32_t num_pairs, hipStream_t stream) {
+  pkv_status st = check_pool(from);
+  if (st != PKV_OK) return st;
+  st = check_pool(to);
+  if (st != PKV_OK) return st;
+  const pkv_pool_config& a = from->cfg;
+  const pkv_pool_config& b = to->cfg;
+  if (a.num_layers != b.num_layers || a.block_size != b.block_size || a.num_kv_heads != b.num_kv_heads ||
+      a.head_dim != b.head_dim || a.kv_dtype != b.kv_dtype)
+    return fail(PKV_ERR_INVALID, "the two pools differ in more than num_blocks");
+  if (num_pairs < 0) return fail(PKV_ERR_INVALID, "num_pairs is negative");
+  if (num_pairs == 0) { clear_error(); return PKV_OK; }
+  if (!pairs) return fail(PKV_ERR_INVALID, "pairs is NULL");
+  char* ptr[8];
+  const void* src[8] = {from->k, from->v, from->k_scale, from->v_scale, to->k, to->v, to->k_scale, to->v_scale};
+  const char* names[8] = {"from K", "from V", "from K scales", "from V scales",
+                          "to K", "to V", "to K scales", "to V scales"};
+  const int regions = a.kv_dtype == PKV_KV_INT8 ? 4 : 2;
+  for (int i = 0; i < 8; ++i) {
+    ptr[i] = nullptr;
+    if (i % 4 >= regions) continue;
+    if (!device_view(src[i], names[i], &ptr[i])) return PKV_ERR_INVALID;
+  }
+  const uint64_t block_bytes = (uint64_t)a.num_kv_heads * from->tile_bytes;
+  const uint64_t scale_block_bytes = (uint64_t)a.num_kv_heads * a.block_size * sizeof(float);
+  if (block_bytes % 16 || scale_block_bytes % 16) return fail(PKV_ERR_UNSUPPORTED, "block bytes not a multiple of 16");
+  const int64_t gx = (int64_t)num_pairs * a.num_layers;
+  if (gx > INT32_MAX) return fail(PKV_ERR_INVALID, "too many pairs in one call");
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3((uint32_t)gx, regions), dim3(256), 0, stream, pairs, num_pairs,
+                     a.num_layers, a.num_blocks, b.num_blocks, ptr[0], ptr[1], ptr[2], ptr[3], ptr[4], ptr[5],
+                     ptr[6], ptr[7], block_bytes, scale_block_bytes);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("swap_blocks launch failed: %s", hipGetErrorString(e));
     return PKV_ERR_HIP;
   }
   clear_error();
