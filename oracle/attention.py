@@ -34,7 +34,8 @@ from __future__ import annotations
 import numpy as np
 
 from . import codecs
-from .layout import (KV_BF16, KV_FP8_E5M2, KV_INT8, PoolImage, k_offset,
+from .layout import (KV_BF16, KV_FP8_E5M2, KV_INT8, KV_INT8_CHANNEL, KV_INT8_TENSOR, PoolImage,
+                     channel_scale_offset, k_offset,
                      scale_offset, v_offset)
 from .layout import k_tiles_as_tokens as layout_k_tokens
 from .layout import scales_as_tokens as layout_scale_tokens
@@ -77,6 +78,21 @@ def gather_kv(img: PoolImage, layer: int, block_table_row: np.ndarray,
         ksc = layout_scale_tokens(p, img.k_scale, layer, blocks)[cut]
         vsc = layout_scale_tokens(p, img.v_scale, layer, blocks)[cut]
         return codecs.int8_dequant(kraw, ksc), codecs.int8_dequant(vraw, vsc)
+    return _dequant_fixed_scales(p, img, layer, kraw, vraw, k_scale, v_scale)
+
+
+def _dequant_fixed_scales(p, img, layer, kraw, vraw, k_scale, v_scale):
+    """INT8 codes [n, Hkv, D] under per-tensor scales (the call's) or per-
+    channel scales (the pool's, for this layer): code * scale in float64."""
+    if p.kv_dtype == KV_INT8_TENSOR:
+        ks = np.float64(np.float32(k_scale))
+        vs = np.float64(np.float32(v_scale))
+        return kraw.astype(np.float64) * ks, vraw.astype(np.float64) * vs
+    if p.kv_dtype == KV_INT8_CHANNEL:
+        co = channel_scale_offset(p, layer, np.arange(p.num_kv_heads)[:, None], np.arange(p.head_dim)[None, :])
+        ks = img.k_scale[co].astype(np.float64)[None]      # [1, Hkv, D]
+        vs = img.v_scale[co].astype(np.float64)[None]
+        return kraw.astype(np.float64) * ks, vraw.astype(np.float64) * vs
     raise ValueError(p.kv_dtype)
 
 
@@ -107,6 +123,13 @@ def gather_kv_by_slot(img: PoolImage, layer: int, block_table_row: np.ndarray,
         so = scale_offset(p, layer, blk[:, :, 0], h[:, :, 0], t[:, :, 0])
         return (codecs.int8_dequant(kraw, img.k_scale[so]),
                 codecs.int8_dequant(vraw, img.v_scale[so]))
+    if p.kv_dtype == KV_INT8_CHANNEL:         # element by element, as for the codes
+        co = channel_scale_offset(p, layer, h + 0 * t, d + 0 * t)
+        return (kraw.astype(np.float64) * img.k_scale[co].astype(np.float64),
+                vraw.astype(np.float64) * img.v_scale[co].astype(np.float64))
+    if p.kv_dtype == KV_INT8_TENSOR:
+        return (kraw.astype(np.float64) * np.float64(np.float32(k_scale)),
+                vraw.astype(np.float64) * np.float64(np.float32(v_scale)))
     raise ValueError(p.kv_dtype)
 
 

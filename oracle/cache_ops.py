@@ -19,7 +19,8 @@ from __future__ import annotations
 import numpy as np
 
 from . import codecs
-from .layout import (KV_BF16, KV_FP8_E5M2, KV_INT8, PoolImage, k_offset,
+from .layout import (KV_BF16, KV_FP8_E5M2, KV_INT8, KV_INT8_CHANNEL, KV_INT8_TENSOR, PoolImage,
+                     channel_scale_offset, k_offset,
                      scale_offset, tile_base, v_offset)
 
 
@@ -67,6 +68,13 @@ def reshape_and_cache(img: PoolImage, layer: int, key_bits: np.ndarray,
         so = scale_offset(p, layer, blk[:, None], np.arange(hkv)[None, :], t[:, None])
         out.k_scale[so] = ks
         out.v_scale[so] = vs
+    elif p.kv_dtype == KV_INT8_TENSOR:
+        out.k[ko] = codecs.int8_encode(codecs.bf16_bits_to_f32(kx), k_scale)
+        out.v[vo] = codecs.int8_encode(codecs.bf16_bits_to_f32(vx), v_scale)
+    elif p.kv_dtype == KV_INT8_CHANNEL:
+        co = channel_scale_offset(p, layer, h3, d3)       # [1, Hkv, D]: the layer's calibrated scales
+        out.k[ko] = codecs.int8_encode(codecs.bf16_bits_to_f32(kx), img.k_scale[co])
+        out.v[vo] = codecs.int8_encode(codecs.bf16_bits_to_f32(vx), img.v_scale[co])
     else:
         raise ValueError(p.kv_dtype)
     return out

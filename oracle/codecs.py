@@ -120,6 +120,20 @@ def int8_quantize(x_f32: np.ndarray):
     return code.astype(np.int8), scale
 
 
+def int8_encode(x_f32: np.ndarray, scale) -> np.ndarray:
+    """INT8 codes under a given (calibrated) scale, elementwise: clamp(
+    rint_even(fp32(x / scale)), -127, 127), and 0 where the scale is 0 - the
+    per-tensor and per-channel granularities of the bjdmk.com.cn article,
+    §5.2 (one scale for the whole cache, or one per channel); ``scale``
+    broadcasts against x."""
+    x = np.asarray(x_f32, dtype=np.float32)
+    s = np.broadcast_to(np.asarray(scale, dtype=np.float32), x.shape)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    q = (x / safe).astype(np.float32)                       # fp32 division
+    code = np.where(s > 0, np.clip(np.rint(q), -127, 127), 0)
+    return code.astype(np.int8)
+
+
 def int8_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """code * scale in float64 (scales broadcast over the last axis)."""
     return (np.asarray(codes, dtype=np.int8).astype(np.float64)

@@ -16,8 +16,11 @@ fp8/int8: 1 byte) from the start of the K (or V) region:
           + ((d // X) * B + t) * X + (d % X))          X = 16 // elem_bytes
     V:  ((((layer * NB + block) * Hkv + head) * B * D)
           + ((t // 4) * D + d) * 4 + (t % 4))
-    K/V scales (INT8 only, fp32 elements):
+    K/V scales (INT8 per token-head, fp32 elements):
           ((layer * NB + block) * Hkv + head) * B + t
+    K/V channel scales (INT8 per channel, fp32 elements, set by the caller):
+          (layer * Hkv + head) * D + d
+    INT8 per tensor and FP8 keep no scales in the pool (the call passes them).
 
 Regions are laid out K, V, K-scales, V-scales, each starting at a multiple of
 256 bytes from the pool base.
@@ -29,8 +32,9 @@ from dataclasses import dataclass
 
 import numpy as np
 
-KV_BF16, KV_FP8_E5M2, KV_INT8 = 0, 1, 2
-ELEM_BYTES = {KV_BF16: 2, KV_FP8_E5M2: 1, KV_INT8: 1}
+KV_BF16, KV_FP8_E5M2, KV_INT8, KV_INT8_TENSOR, KV_INT8_CHANNEL = 0, 1, 2, 3, 4
+ELEM_BYTES = {KV_BF16: 2, KV_FP8_E5M2: 1, KV_INT8: 1, KV_INT8_TENSOR: 1, KV_INT8_CHANNEL: 1}
+INT8_CODES = (KV_INT8, KV_INT8_TENSOR, KV_INT8_CHANNEL)
 REGION_ALIGN = 256
 
 
@@ -61,7 +65,21 @@ class PoolShape:
 
     @property
     def has_scales(self) -> bool:
+        """Per (token, head) scales stored beside each block's codes."""
         return self.kv_dtype == KV_INT8
+
+    @property
+    def has_channel_scales(self) -> bool:
+        """Per (layer, head, dim) scales, one K and one V region per pool."""
+        return self.kv_dtype == KV_INT8_CHANNEL
+
+    @property
+    def scale_elems(self) -> int:
+        if self.has_scales:
+            return self.num_layers * self.num_blocks * self.num_kv_heads * self.block_size
+        if self.has_channel_scales:
+            return self.num_layers * self.num_kv_heads * self.head_dim
+        return 0
 
 
 def _align(n: int) -> int:
@@ -70,13 +88,13 @@ def _align(n: int) -> int:
 
 def region_offsets(p: PoolShape):
     """Byte offsets (k, v, k_scale, v_scale, total).  Scale offsets are None
-    when the storage type carries no per-token-head scales."""
+    when the storage type keeps no scales in the pool."""
     kv_bytes = p.region_elems * p.elem_bytes
     k_off = 0
     v_off = _align(k_off + kv_bytes)
     end = _align(v_off + kv_bytes)
-    if p.has_scales:
-        s_bytes = p.num_layers * p.num_blocks * p.num_kv_heads * p.block_size * 4
+    if p.scale_elems:
+        s_bytes = p.scale_elems * 4
         ks_off = end
         vs_off = _align(ks_off + s_bytes)
         end = _align(vs_off + s_bytes)
@@ -104,6 +122,10 @@ def v_offset(p: PoolShape, layer, block, head, t, d):
 def scale_offset(p: PoolShape, layer, block, head, t):
     return ((np.asarray(layer, dtype=np.int64) * p.num_blocks + block)
             * p.num_kv_heads + head) * p.block_size + np.asarray(t, dtype=np.int64)
+
+
+def channel_scale_offset(p: PoolShape, layer, head, d):
+    return (np.asarray(layer, dtype=np.int64) * p.num_kv_heads + head) * p.head_dim + np.asarray(d, dtype=np.int64)
 
 
 def k_tiles_as_tokens(p: PoolShape, region: np.ndarray, layer: int, blocks) -> np.ndarray:
@@ -155,7 +177,8 @@ class PoolImage:
 
 
 def _storage_dtype(p: PoolShape):
-    return {KV_BF16: np.uint16, KV_FP8_E5M2: np.uint8, KV_INT8: np.int8}[p.kv_dtype]
+    return {KV_BF16: np.uint16, KV_FP8_E5M2: np.uint8, KV_INT8: np.int8, KV_INT8_TENSOR: np.int8,
+            KV_INT8_CHANNEL: np.int8}[p.kv_dtype]
 
 
 def empty_image(p: PoolShape, fill: int = 0) -> PoolImage:
@@ -163,10 +186,9 @@ def empty_image(p: PoolShape, fill: int = 0) -> PoolImage:
     k = np.full(p.region_elems, fill, dtype=dt)
     v = np.full(p.region_elems, fill, dtype=dt)
     ks = vs = None
-    if p.has_scales:
-        n = p.num_layers * p.num_blocks * p.num_kv_heads * p.block_size
-        ks = np.zeros(n, dtype=np.float32)
-        vs = np.zeros(n, dtype=np.float32)
+    if p.scale_elems:
+        ks = np.zeros(p.scale_elems, dtype=np.float32)
+        vs = np.zeros(p.scale_elems, dtype=np.float32)
     return PoolImage(p, k, v, ks, vs)
 
 
@@ -180,8 +202,8 @@ def image_from_bytes(p: PoolShape, raw: np.ndarray) -> PoolImage:
     k = raw[k_off:k_off + nb].view(dt).copy()
     v = raw[v_off:v_off + nb].view(dt).copy()
     ks = vs = None
-    if p.has_scales:
-        sb = p.num_layers * p.num_blocks * p.num_kv_heads * p.block_size * 4
+    if p.scale_elems:
+        sb = p.scale_elems * 4
         ks = raw[ks_off:ks_off + sb].view(np.float32).copy()
         vs = raw[vs_off:vs_off + sb].view(np.float32).copy()
     return PoolImage(p, k, v, ks, vs)
@@ -195,7 +217,7 @@ def image_to_bytes(img: PoolImage) -> np.ndarray:
     raw[k_off:k_off + kb.size] = kb
     vb = img.v.view(np.uint8)
     raw[v_off:v_off + vb.size] = vb
-    if p.has_scales:
+    if p.scale_elems:
         ksb = img.k_scale.view(np.uint8)
         raw[ks_off:ks_off + ksb.size] = ksb
         vsb = img.v_scale.view(np.uint8)

@@ -2,7 +2,8 @@
 
 Each case monkeypatches one plausible slip into the oracle and re-runs a pin
 that should then fail: a transposed grouping, a slot off by one, a dropped
-softmax scale, a wrong e5m2 exponent bias, a window one position too wide.
+softmax scale, a wrong e5m2 exponent bias, a window one position too wide,
+per-channel scales read with the dims reversed.
 """
 
 import numpy as np
@@ -13,6 +14,7 @@ import oracle.codecs as codecs
 from tests import test_oracle_attention as ta
 from tests import test_oracle_codecs as tc
 from tests import test_oracle_paging as tp
+from tests import test_oracle_int8_scales as ti
 from tests import test_oracle_window as tw
 from oracle import layout
 
@@ -70,3 +72,10 @@ def test_window_off_by_one_is_caught(monkeypatch):
     orig = att.window_start
     monkeypatch.setattr(att, "window_start", lambda ctx, w: max(orig(ctx, w) - 1, 0))
     assert _fails(lambda: tw.test_window_matches_masked_sdpa(3))
+
+
+def test_reversed_channel_scales_are_caught(monkeypatch):
+    def bad(p, layer, head, d):
+        return (np.asarray(layer, dtype=np.int64) * p.num_kv_heads + head) * p.head_dim + (p.head_dim - 1 - d)
+    monkeypatch.setattr(att, "channel_scale_offset", bad)
+    assert _fails(lambda: ti.test_cache_write_then_gathers_read_code_times_scale(layout.KV_INT8_CHANNEL))
