@@ -75,8 +75,16 @@ typedef enum {
 typedef enum {
   PKV_KV_BF16 = 0,       /* K/V stored as bf16                               */
   PKV_KV_FP8_E5M2 = 1,   /* OCP e5m2, one fp32 scale per tensor ([KVP] §四)  */
-  PKV_KV_INT8 = 2        /* symmetric int8, one fp32 scale per (token, head)
+  PKV_KV_INT8 = 2,       /* symmetric int8, one fp32 scale per (token, head)
                             for K and for V ([BJD] §5.2 量化粒度)             */
+  PKV_KV_INT8_TENSOR = 3,  /* int8 codes, one calibrated fp32 scale for all
+                              of K and one for V, passed with each call like
+                              the fp8 scales ([KVP] §四 INT8 per-tensor;
+                              [BJD] §5.2 per-tensor)                        */
+  PKV_KV_INT8_CHANNEL = 4  /* int8 codes, one calibrated fp32 scale per
+                              (layer, KV head, dim) for K and for V, kept in
+                              the pool's scale regions, which the caller
+                              fills ([KVP] §四 per-channel; [BJD] §5.2)     */
 } pkv_kv_dtype;
 
 typedef struct {
@@ -89,7 +97,11 @@ typedef struct {
 } pkv_pool_config;
 
 /* Filled by kv_pool_create; plain data, may be copied freely.  Pointers are
- * device addresses inside the caller's buffer (scales NULL unless int8). */
+ * device addresses inside the caller's buffer.  k_scale / v_scale: for
+ * PKV_KV_INT8 the per-(token, head) scales [L][NB][H][B] the cache write
+ * fills; for PKV_KV_INT8_CHANNEL the per-channel scales [L][H][D] the caller
+ * writes before caching or decoding a layer (element (l, h, d) at
+ * (l * H + h) * D + d); NULL otherwise. */
 typedef struct {
   pkv_pool_config cfg;
   void* base;
@@ -143,8 +155,11 @@ pkv_status kv_pool_create(const pkv_pool_config* cfg, void* dev_mem, uint64_t by
  *   scales        host; fp8: stored = e5m2_rne_sat(fp32(x / scale)); NULL=1
  * int8 storage computes per (token, head): scale = fp32(absmax) / 127,
  * code = clamp(rint_even(fp32(x / scale)), -127, 127) (0 if absmax is 0) and
- * writes the scale beside the codes.  Two tokens with the same slot in one
- * call race (pkv_check_slots rejects that). */
+ * writes the scale beside the codes.  INT8_TENSOR uses the same code formula
+ * with scales' k_scale / v_scale (positive, PKV_ERR_INVALID otherwise);
+ * INT8_CHANNEL with the pool's channel scales of this layer (a scale of 0
+ * gives code 0).  Two tokens with the same slot in one call race
+ * (pkv_check_slots rejects that). */
 pkv_status reshape_and_cache(const pkv_pool* pool, int32_t layer, const void* key,
                              const void* value, const int64_t* slot_mapping,
                              int32_t num_tokens, const pkv_kv_scales* scales,

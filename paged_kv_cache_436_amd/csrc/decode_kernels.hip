@@ -199,7 +199,9 @@ struct DecodeParams {
   int32_t num_items;          // S * Hkv * QT
   int32_t win;                // sliding window (positions), 0 = whole context
   float qk_scale;             // softmax scale * log2(e) (* fp8 k scale)
-  float out_scale;            // fp8 v scale, else 1
+  float out_scale;            // fp8 / int8 per-tensor v scale, else 1
+  const float* vs_ch;         // int8 per channel: this layer's V scales [Hkv][D] (output scale per dim), else null
+  int32_t q_stride;           // elements between q rows: D, or 2 D for the folded q of int8 per channel
 };
 
 template <int D, int KVT>
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
   bf16x8 qop[T::KK];
   {
     const bool valid = row < gt;
-    const uint16_t* qh = p.q + ((int64_t)s * p.Hq + h0 + (valid ? row : 0)) * D;
+    const uint16_t* qh = p.q + ((int64_t)s * p.Hq + h0 + (valid ? row : 0)) * p.q_stride;
 #pragma unroll
     for (int kk = 0; kk < T::KK; ++kk) {
       u32x4 raw = *reinterpret_cast<const u32x4*>(qh + q_dim0<E>(kk, j));
@@ -445,7 +447,7 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
       L += f * sm_ml[ww][1][hh];
       A += f * sm_acc[ww][hh][d];
     }
-    p.out[((int64_t)s * p.Hq + h0 + hh) * D + d] = A / L * p.out_scale;
+    p.out[((int64_t)s * p.Hq + h0 + hh) * D + d] = A / L * (p.vs_ch ? p.vs_ch[g * D + d] : p.out_scale);
   }
 }
 
@@ -502,6 +504,9 @@ struct SplitParams {
   uint32_t epoch;             // this call's tag for row_done
   float qk_scale;
   float out_scale;
+  const float* ks_ch;         // int8 per channel: this layer's K / V scales [Hkv][D], else null
+  const float* vs_ch;
+  int32_t q_stride;           // elements between q rows: D, or 2 D for the folded q of int8 per channel
 };
 
 template <int D, int KVT>
@@ -562,7 +567,7 @@ __device__ __forceinline__ QRegs<SplitGeo<D, KVT>::KK> load_q(const SplitParams&
   const int row = lane & 15;
   const int j = lane >> 4;
   // rows past the tile's heads read a valid head; their columns are never stored
-  const uint16_t* qh = p.q + ((int64_t)s * p.Hq + h0 + (row < gt ? row : 0)) * D;
+  const uint16_t* qh = p.q + ((int64_t)s * p.Hq + h0 + (row < gt ? row : 0)) * p.q_stride;
   QRegs<GE::KK> r;
 #pragma unroll
   for (int kk = 0; kk < GE::KK; ++kk)
@@ -674,7 +679,13 @@ __device__ __forceinline__ void append_token(const SplitParams& p, int s, int g,
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t x = half_of(i < 2 ? x0 : x1, i & 1);
-          b[i] = KVT == PKV_KV_FP8_E5M2 ? fp8_store(x, p.enc_k) : int8_store(x, sk);
+          if constexpr (KVT == PKV_KV_FP8_E5M2) {
+            b[i] = fp8_store(x, p.enc_k);
+          } else if constexpr (KVT == PKV_KV_INT8) {
+            b[i] = int8_store(x, sk);
+          } else {   // calibrated: per tensor, or per channel (dim X * lane + 4 * q4 + i)
+            b[i] = int8_store(x, p.ks_ch ? p.ks_ch[g * D + X * lane + 4 * q4 + i] : p.enc_k);
+          }
         }
         kout[q4] = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
       }
@@ -689,7 +700,10 @@ __device__ __forceinline__ void append_token(const SplitParams& p, int s, int g,
     if constexpr (E == 2) {
       reinterpret_cast<uint16_t*>(vt)[el] = (uint16_t)x;
     } else {
-      const uint32_t code = KVT == PKV_KV_FP8_E5M2 ? fp8_store(x, p.enc_v) : int8_store(x, sv);
+      uint32_t code;
+      if constexpr (KVT == PKV_KV_FP8_E5M2) code = fp8_store(x, p.enc_v);
+      else if constexpr (KVT == PKV_KV_INT8) code = int8_store(x, sv);
+      else code = int8_store(x, p.vs_ch ? p.vs_ch[g * D + d] : p.enc_v);
       reinterpret_cast<uint8_t*>(vt)[el] = (uint8_t)code;
     }
   }
@@ -1001,10 +1015,14 @@ __device__ __forceinline__ void merge_row(const SplitParams& p, int x, int s, in
   if (row < gt) {
     float* orow = p.out + ((int64_t)s * p.Hq + h0 + row) * D;
     const float inv = p.out_scale / L;
+    const float* vch = p.vs_ch ? p.vs_ch + g * D : nullptr;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) orow[acc_dim<E>(c, j, i)] = A[c][i] * inv;
+      for (int i = 0; i < 4; ++i) {
+        const int dd = acc_dim<E>(c, j, i);
+        orow[dd] = vch ? A[c][i] / L * vch[dd] : A[c][i] * inv;
+      }
   }
 }
 
@@ -1270,6 +1288,24 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
   }
 }
 
+// INT8 with per-channel scales: the K scale of (KV head, dim) is folded into
+// the query, z = sum_d (q_d * s_d) * code_d, so the decode kernels see plain
+// int8 codes.  q'[s][h][d] = bf16(fp32(q) * s_k[h / G][d]) (rounded to
+// nearest even) is written over the first half of the output row out[s][h],
+// which only that row's final merge writes, after every read of q'; the
+// kernels read it with a row stride of 2 D elements.
+__global__ __launch_bounds__(256) void fold_q_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ qf,
+                                                     const float* __restrict__ ks_ch, int64_t n, int32_t Hq,
+                                                     int32_t G, int32_t D) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int d = (int)(i % D);
+  const int64_t row = i / D;
+  const int h = (int)(row % Hq);
+  const float x = bf16_bits_to_float(q[i]) * ks_ch[(h / G) * D + d];
+  qf[row * 2 * D + d] = (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu);
+}
+
 // ---------------------------------------------------------------- launches
 template <int D, int KVT, int B>
 hipError_t launch_single(const DecodeParams& p, int grid, hipStream_t stream) {
@@ -1285,6 +1321,10 @@ hipError_t launch_single_kv(const DecodeParams& p, int kvt, int B, int grid, hip
     case PKV_KV_FP8_E5M2:
       return B == 16 ? launch_single<D, PKV_KV_FP8_E5M2, 16>(p, grid, stream)
                      : launch_single<D, PKV_KV_FP8_E5M2, 32>(p, grid, stream);
+    case PKV_KV_INT8_TENSOR:
+    case PKV_KV_INT8_CHANNEL:   // folded q, per-dim output scale: the same codes kernel
+      return B == 16 ? launch_single<D, PKV_KV_INT8_TENSOR, 16>(p, grid, stream)
+                     : launch_single<D, PKV_KV_INT8_TENSOR, 32>(p, grid, stream);
     default:
       return B == 16 ? launch_single<D, PKV_KV_INT8, 16>(p, grid, stream) : launch_single<D, PKV_KV_INT8, 32>(p, grid, stream);
   }
@@ -1305,10 +1345,14 @@ const void* split_kernel_fn(int D, int kvt, int B) {
   if (D == 64) {
     if (kvt == PKV_KV_BF16) return B == 16 ? split_fn<64, PKV_KV_BF16, 16>() : split_fn<64, PKV_KV_BF16, 32>();
     if (kvt == PKV_KV_FP8_E5M2) return B == 16 ? split_fn<64, PKV_KV_FP8_E5M2, 16>() : split_fn<64, PKV_KV_FP8_E5M2, 32>();
+    if (kvt == PKV_KV_INT8_TENSOR || kvt == PKV_KV_INT8_CHANNEL)
+      return B == 16 ? split_fn<64, PKV_KV_INT8_TENSOR, 16>() : split_fn<64, PKV_KV_INT8_TENSOR, 32>();
     return B == 16 ? split_fn<64, PKV_KV_INT8, 16>() : split_fn<64, PKV_KV_INT8, 32>();
   }
   if (kvt == PKV_KV_BF16) return B == 16 ? split_fn<128, PKV_KV_BF16, 16>() : split_fn<128, PKV_KV_BF16, 32>();
   if (kvt == PKV_KV_FP8_E5M2) return B == 16 ? split_fn<128, PKV_KV_FP8_E5M2, 16>() : split_fn<128, PKV_KV_FP8_E5M2, 32>();
+  if (kvt == PKV_KV_INT8_TENSOR || kvt == PKV_KV_INT8_CHANNEL)
+    return B == 16 ? split_fn<128, PKV_KV_INT8_TENSOR, 16>() : split_fn<128, PKV_KV_INT8_TENSOR, 32>();
   return B == 16 ? split_fn<128, PKV_KV_INT8, 16>() : split_fn<128, PKV_KV_INT8, 32>();
 }
 
@@ -1331,7 +1375,7 @@ int device_cus(int* cus) {
 // Resident workgroups per CU of one split-kernel variant (cached).
 int split_blocks_per_cu(int D, int kvt, int B) {
   static std::mutex mu;
-  static int cache[64][2][3][2] = {};
+  static int cache[64][2][5][2] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
   const int di = D == 64 ? 0 : 1, bi = B == 16 ? 0 : 1;
@@ -1403,6 +1447,11 @@ void launch_split_kv(const SplitParams& p, int kvt, int B, int grid, hipStream_t
       if (B == 16) launch_split_t<D, PKV_KV_FP8_E5M2, 16>(p, grid, stream);
       else launch_split_t<D, PKV_KV_FP8_E5M2, 32>(p, grid, stream);
       break;
+    case PKV_KV_INT8_TENSOR:
+    case PKV_KV_INT8_CHANNEL:
+      if (B == 16) launch_split_t<D, PKV_KV_INT8_TENSOR, 16>(p, grid, stream);
+      else launch_split_t<D, PKV_KV_INT8_TENSOR, 32>(p, grid, stream);
+      break;
     default:
       if (B == 16) launch_split_t<D, PKV_KV_INT8, 16>(p, grid, stream);
       else launch_split_t<D, PKV_KV_INT8, 32>(p, grid, stream);
@@ -1471,27 +1520,46 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
   }
   if (((uintptr_t)q) % 16 || ((uintptr_t)out) % 16) return fail(PKV_ERR_INVALID, "q and out must be 16-byte aligned");
   float ksc = 1.f, vsc = 1.f;
-  if (kv_scales && c.kv_dtype == PKV_KV_FP8_E5M2) {
+  if (kv_scales && (c.kv_dtype == PKV_KV_FP8_E5M2 || c.kv_dtype == PKV_KV_INT8_TENSOR)) {
     ksc = kv_scales->k_scale;
     vsc = kv_scales->v_scale;
     if (!(ksc > 0.f) || !(vsc > 0.f) || !(ksc < INFINITY) || !(vsc < INFINITY))
-      return fail(PKV_ERR_INVALID, "fp8 scales must be positive and finite");
+      return fail(PKV_ERR_INVALID, "per-tensor scales must be positive and finite");
   }
+  const bool channel = c.kv_dtype == PKV_KV_INT8_CHANNEL;
+  if (channel && (const void*)out == q) return fail(PKV_ERR_INVALID, "out must not alias q for per-channel int8");
   const int32_t G = num_q_heads / c.num_kv_heads;
   const int32_t QT = (G + 15) / 16;
   const int64_t rows = (int64_t)num_seqs * c.num_kv_heads * QT;
-  const uint64_t scale_layer = (uint64_t)c.num_blocks * c.num_kv_heads * c.block_size;
+  const uint64_t scale_layer = channel ? (uint64_t)c.num_kv_heads * c.head_dim
+                                      : (uint64_t)c.num_blocks * c.num_kv_heads * c.block_size;
   char* kl = static_cast<char*>(pool->k) + (uint64_t)layer * pool->layer_bytes;
   char* vl = static_cast<char*>(pool->v) + (uint64_t)layer * pool->layer_bytes;
   float* ksl = pool->k_scale ? pool->k_scale + layer * scale_layer : nullptr;
   float* vsl = pool->v_scale ? pool->v_scale + layer * scale_layer : nullptr;
+  // the query the kernels read: q itself, or (per-channel int8) q with the K
+  // channel scales folded in, written into the output rows first
+  const uint16_t* qk = static_cast<const uint16_t*>(q);
+  int32_t q_stride = c.head_dim;
+  if (channel) {
+    const int64_t n = (int64_t)num_seqs * num_q_heads * c.head_dim;
+    const int64_t blocks = (n + 255) / 256;
+    if (blocks > INT32_MAX) return fail(PKV_ERR_INVALID, "too many queries in one call");
+    hipLaunchKernelGGL(fold_q_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, qk,
+                       reinterpret_cast<uint16_t*>(out), ksl, n, num_q_heads, num_q_heads / c.num_kv_heads,
+                       c.head_dim);
+    qk = reinterpret_cast<const uint16_t*>(out);
+    q_stride = 2 * c.head_dim;
+  }
 
   hipError_t e = hipSuccess;
   if (partition_size == 0) {
     const int64_t grid = (rows + 7) / 8 * 8;
     if (grid > INT32_MAX) return fail(PKV_ERR_INVALID, "too many work items");
     DecodeParams p{};
-    p.q = static_cast<const uint16_t*>(q);
+    p.q = qk;
+    p.q_stride = q_stride;
+    p.vs_ch = channel ? vsl : nullptr;
     p.out = out;
     p.k = kl;
     p.v = vl;
@@ -1538,7 +1606,10 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     const int64_t grid = split_grid(steps_ub, cus, bpc);
     if (grid * kNW + rows * np > z.slots_cap) return fail(PKV_ERR_INVALID, "internal: workspace sizing");
     SplitParams p{};
-    p.q = static_cast<const uint16_t*>(q);
+    p.q = qk;
+    p.q_stride = q_stride;
+    p.ks_ch = channel ? ksl : nullptr;
+    p.vs_ch = channel ? vsl : nullptr;
     p.out = out;
     p.k = kl;
     p.v = vl;

@@ -23,6 +23,8 @@ inline int elem_bytes(int32_t kv_dtype) {
     case PKV_KV_BF16: return 2;
     case PKV_KV_FP8_E5M2: return 1;
     case PKV_KV_INT8: return 1;
+    case PKV_KV_INT8_TENSOR: return 1;
+    case PKV_KV_INT8_CHANNEL: return 1;
     default: return 0;
   }
 }

@@ -48,9 +48,11 @@ bool pool_regions(const pkv_pool_config* cfg, Regions* r) {
   r->total = align_up(r->v + kv);
   r->ks = r->vs = 0;
   r->scale_bytes = 0;
-  if (cfg->kv_dtype == PKV_KV_INT8) {
-    const uint64_t sb = (uint64_t)cfg->num_layers * cfg->num_blocks * cfg->num_kv_heads *
-                        cfg->block_size * sizeof(float);
+  if (cfg->kv_dtype == PKV_KV_INT8 || cfg->kv_dtype == PKV_KV_INT8_CHANNEL) {
+    const uint64_t sb = cfg->kv_dtype == PKV_KV_INT8
+                            ? (uint64_t)cfg->num_layers * cfg->num_blocks * cfg->num_kv_heads * cfg->block_size *
+                                  sizeof(float)
+                            : (uint64_t)cfg->num_layers * cfg->num_kv_heads * cfg->head_dim * sizeof(float);
     r->scale_bytes = sb;
     r->ks = r->total;
     r->vs = align_up(r->ks + sb);
@@ -64,7 +66,8 @@ pkv_status check_pool(const pkv_pool* pool) {
   Regions r;
   if (!pool_regions(&pool->cfg, &r)) return PKV_ERR_INVALID;
   if (!pool->k || !pool->v) return fail(PKV_ERR_INVALID, "pool has no K/V pointers (use kv_pool_create)");
-  if (pool->cfg.kv_dtype == PKV_KV_INT8 && (!pool->k_scale || !pool->v_scale))
+  if ((pool->cfg.kv_dtype == PKV_KV_INT8 || pool->cfg.kv_dtype == PKV_KV_INT8_CHANNEL) &&
+      (!pool->k_scale || !pool->v_scale))
     return fail(PKV_ERR_INVALID, "int8 pool has no scale pointers");
   return PKV_OK;
 }
@@ -94,6 +97,7 @@ int64_t kv_pool_num_blocks_for_budget(const pkv_pool_config* cfg, uint64_t budge
   const int e = elem_bytes(c.kv_dtype);
   uint64_t per_block = 2ull * c.num_layers * c.num_kv_heads * c.block_size * c.head_dim * e;
   if (c.kv_dtype == PKV_KV_INT8) per_block += 2ull * c.num_layers * c.num_kv_heads * c.block_size * 4;
+  // (per-channel scales do not grow with the block count: the exact check below covers them)
   int64_t nb = (int64_t)(budget_bytes / per_block);
   if (nb > INT32_MAX) nb = INT32_MAX;
   while (nb > 0) {
@@ -122,7 +126,7 @@ pkv_status kv_pool_create(const pkv_pool_config* cfg, void* dev_mem, uint64_t by
   char* b = static_cast<char*>(dev_mem);
   out->k = b + r.k;
   out->v = b + r.v;
-  if (cfg->kv_dtype == PKV_KV_INT8) {
+  if (r.scale_bytes) {
     out->k_scale = reinterpret_cast<float*>(b + r.ks);
     out->v_scale = reinterpret_cast<float*>(b + r.vs);
   }
