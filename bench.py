@@ -37,6 +37,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0    # MI355X HBM3E, AMD's published peak
+KV_DTYPES = {"bf16": 0, "fp8": 1, "int8": 2, "int8_tensor": 3, "int8_channel": 4}
+TENSOR_SCALE = 0.035     # per-tensor K and V scale of the 8-bit runs (fp8 and int8_tensor)
 
 
 def log(msg):
@@ -59,6 +61,8 @@ def parse():
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window: each layer's call attends to the last N positions only "
                          "(paged_attn_decode_ex; bytes counted over those positions)")
+    ap.add_argument("--kv-dtype", default="bf16", choices=sorted(KV_DTYPES),
+                    help="KV storage of the pool (8-bit pools hold random codes; the oracle sample runs for bf16 only)")
     ap.add_argument("--swap", type=int, default=0,
                     help="instead of the decode step: swap N blocks of the 70B-shaped pool out to pinned host "
                          "memory and back (swap_blocks), and report GB/s each way")
@@ -183,17 +187,32 @@ def main():
     bm = pkv.BlockManager(w.num_blocks, B, w.block_order)
     for s in range(S):
         bm.add_seq(s, int(w.context_lens[s]) - 1)      # history; each step appends one token
-    cfg = pkv.make_config(w.num_layers, w.num_blocks, B, Hkv, D, pkv.PKV_KV_BF16)
+    kvt = KV_DTYPES[args.kv_dtype]
+    e = 2 if kvt == pkv.PKV_KV_BF16 else 1
+    token_scales = 2 * 4 if kvt == pkv.PKV_KV_INT8 else 0          # int8: fp32 K and V scale per (token, head)
+    tok_bytes = Hkv * (2 * D * e + token_scales)                    # KV bytes per token per layer
+    ks_t = vs_t = TENSOR_SCALE if kvt in (pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8_TENSOR) else 1.0
+    if kvt != pkv.PKV_KV_BF16:
+        args.no_cpu_baseline = True
+    cfg = pkv.make_config(w.num_layers, w.num_blocks, B, Hkv, D, kvt)
     log(f"pool: {pkv.kv_pool_bytes(cfg) / 1e9:.1f} GB, {w.num_blocks} blocks/layer x {w.num_layers} layers")
     pool = pkv.Pool(cfg, device=dev)
-    k_off, v_off, _, _ = pool.region_offsets()
+    k_off, v_off, ks_off, vs_off = pool.region_offsets()
     lb = pool.desc.layer_bytes
     t0 = time.time()
     for layer in range(w.num_layers):
         g = torch.Generator(device=dev)
         g.manual_seed(436003 * 1000 + layer)
         for off in (k_off, v_off):
-            pool.memory[off + layer * lb: off + (layer + 1) * lb].view(torch.bfloat16).normal_(generator=g)
+            region = pool.memory[off + layer * lb: off + (layer + 1) * lb]
+            if e == 2:
+                region.view(torch.bfloat16).normal_(generator=g)
+            else:   # random codes (int8: +-127 range; e5m2: finite patterns below the exponent-31 codes)
+                region.random_(0, 120 if kvt == pkv.PKV_KV_FP8_E5M2 else 256, generator=g)
+    if ks_off is not None:     # int8 scales: per-token ones, or the calibrated per-channel ones
+        n = pool.memory[ks_off:vs_off].numel() // 4
+        for off in (ks_off, vs_off):
+            pool.memory[off: off + 4 * n].view(torch.float32).uniform_(0.02, 0.05)
     torch.cuda.synchronize()
     log(f"pool filled in {time.time() - t0:.1f} s")
 
@@ -226,15 +245,16 @@ def main():
 
     def decode(layer):
         if window:
-            pkv.paged_attn_decode_ex(out, q[layer], pool, layer, d_tab, d_ctx, scale, partition_size=P,
-                                     workspace=ws, key=newk[layer], value=newv[layer], sliding_window=window,
+            pkv.paged_attn_decode_ex(out, q[layer], pool, layer, d_tab, d_ctx, scale, k_scale=ks_t,
+                                     v_scale=vs_t, partition_size=P, workspace=ws, key=newk[layer], value=newv[layer], sliding_window=window,
                                      stream=stream)
         elif separate:
-            pkv.paged_attn_decode(out, q[layer], pool, layer, d_tab, d_ctx, scale, partition_size=P,
+            pkv.paged_attn_decode(out, q[layer], pool, layer, d_tab, d_ctx, scale, k_scale=ks_t, v_scale=vs_t,
+                                  partition_size=P,
                                   workspace=ws, stream=stream)
         else:
             pkv.paged_attn_decode_append(out, q[layer], pool, layer, newk[layer], newv[layer], d_tab, d_ctx,
-                                         scale, partition_size=P, workspace=ws, stream=stream)
+                                         scale, k_scale=ks_t, v_scale=vs_t, partition_size=P, workspace=ws, stream=stream)
 
     def step(i, timed):
         b = i % 2
@@ -250,7 +270,7 @@ def main():
         h_done[b].record(stream)
         ctxs = h_ctx[b].numpy().astype(np.int64)
         ctx_sum = int((np.minimum(ctxs, window) if window else ctxs).sum())   # positions attended
-        kv_bytes.append(ctx_sum * Hkv * 2 * D * 2 * L)
+        kv_bytes.append(ctx_sum * tok_bytes * L)
         # HIP events on the launch stream.  A timing event between two launches
         # costs ~10 us of idle GPU (the next launch no longer follows the
         # previous one directly), so the appending form, whose 80 decode
@@ -261,7 +281,8 @@ def main():
             e0.record(stream)
         for layer in range(L):
             if separate:
-                pkv.reshape_and_cache(pool, layer, newk[layer], newv[layer], d_slot, stream=stream)
+                pkv.reshape_and_cache(pool, layer, newk[layer], newv[layer], d_slot, k_scale=ks_t, v_scale=vs_t,
+                                      stream=stream)
                 if timed:
                     c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     c0.record(stream)
@@ -290,7 +311,7 @@ def main():
     dec_ms = [e0.elapsed_time(e1) / n for e0, e1, _, n in dec_events]
     # per call: every context token's K and V once; the appending form also
     # writes the new token's K and V
-    dec_bytes = [(c + (0 if separate else S)) * Hkv * 2 * D * 2 for _, _, c, _ in dec_events]
+    dec_bytes = [(c + (0 if separate else S)) * tok_bytes for _, _, c, _ in dec_events]
     avg_dec_ms = float(np.mean(dec_ms))
     avg_dec_bytes = float(np.mean(dec_bytes))
     achieved = avg_dec_bytes / (avg_dec_ms * 1e-3) / 1e9
@@ -303,7 +324,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu, parity = cpu_baseline(args, pkv, w, pool, decode, q, out, d_tab, d_ctx, scale)
     workload = ("70B-shaped paged decode step: 80 layers x 100 seqs x ~4K ctx, "
-                "64q/8kv heads, head_dim 128, bf16 KV, block 16")
+                f"64q/8kv heads, head_dim 128, {args.kv_dtype} KV, block 16")
     if window:
         workload += f", sliding window of the last {window} positions"
 
@@ -319,7 +340,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.kv_dtype,
         "data": "synthetic",
         "config": {"workload": workload,
                    "sliding_window": window, "layers": L, "seqs": S, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
@@ -328,11 +349,11 @@ def main():
                                    else "paged_attn_decode_append")},
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "seq_steps_per_s": round(S / (elapsed / args.steps), 1),
-        "seq_tokens_per_s": round(kv_per_step / (Hkv * 2 * D * 2 * L) / (elapsed / args.steps), 1),
+        "seq_tokens_per_s": round(kv_per_step / (tok_bytes * L) / (elapsed / args.steps), 1),
         "roofline": {"bound": "hbm", "kernel": f"pa_split_kernel (the one launch of a split-context {call} call)",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if window else measured_traffic(),
+                     "traffic": None if (window or kvt != pkv.PKV_KV_BF16) else measured_traffic(),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)",
                      "avg_call_us": round(avg_dec_ms * 1e3, 2), "bytes_per_call": int(avg_dec_bytes)},
         "cpu_baseline": cpu,
