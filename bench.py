@@ -63,6 +63,9 @@ def parse():
                          "(paged_attn_decode_ex; bytes counted over those positions)")
     ap.add_argument("--kv-dtype", default="bf16", choices=sorted(KV_DTYPES),
                     help="KV storage of the pool (8-bit pools hold random codes; the oracle sample runs for bf16 only)")
+    ap.add_argument("--prefix-cache", type=int, default=0,
+                    help="host only: N requests sharing a 1500-token system prompt through the block manager's "
+                         "prefix cache; report microseconds per request and the prefill tokens it saves")
     ap.add_argument("--swap", type=int, default=0,
                     help="instead of the decode step: swap N blocks of the 70B-shaped pool out to pinned host "
                          "memory and back (swap_blocks), and report GB/s each way")
@@ -94,6 +97,45 @@ def measured_traffic():
 
 
 HOST_LINK_GBS = 64.0     # PCIe Gen5 x16, one direction
+
+
+def prefix_cache_bench(args):
+    """The shared-system-prompt scenario of the bjdmk.com.cn article (§3.2:
+    a 1500-token system prompt, 200 concurrent requests): every request is
+    that prompt plus 64..512 private tokens; time kv_bm_add_seq_tokens per
+    request (SHA-256 keys over every full block, lookups, allocation)."""
+    import paged_kv_cache_436_amd as pkv
+
+    n = args.prefix_cache
+    B = 16
+    rng = np.random.default_rng(436004)
+    system = rng.integers(0, 32000, size=1500).tolist()
+    prompts = [np.asarray(system + rng.integers(0, 32000, size=int(rng.integers(64, 513))).tolist(), np.int32)
+               for _ in range(n)]
+    nb = sum(-(-len(p) // B) for p in prompts) + 8
+    times, saved = [], 0
+    for rep in range(args.warmup + args.steps):
+        bm = pkv.BlockManager(nb, B)
+        t0 = time.perf_counter()
+        cached = [bm.add_seq_tokens(i, p) for i, p in enumerate(prompts)]
+        t1 = time.perf_counter()
+        if rep >= args.warmup:
+            times.append(t1 - t0)
+            saved = sum(cached)
+        lookups, hits, keys = bm.prefix_stats()
+        used = bm.stats()[0]
+        bm.close()
+    per = float(np.median(times)) / n
+    total_tokens = sum(len(p) for p in prompts)
+    res = {"metric": "prefix-cache admission: microseconds per request (host)", "value": round(per * 1e6, 2),
+           "unit": "us/request", "n_gpus": 0, "steps": args.steps, "warmup": args.warmup,
+           "higher_is_better": False, "dtype": "int32", "data": "synthetic",
+           "config": {"workload": f"{n} requests = one 1500-token system prompt + 64..512 private tokens, "
+                                  "block 16", "prompt_tokens": total_tokens},
+           "prefill_tokens_reused": saved, "prefill_fraction_reused": round(saved / total_tokens, 4),
+           "block_lookups": lookups, "block_hits": hits, "blocks_used": used,
+           "blocks_without_sharing": nb - 8}
+    print(json.dumps(res), flush=True)
 
 
 def swap_bench(args):
@@ -165,6 +207,9 @@ def main():
         return
     if args.swap:
         swap_bench(args)
+        return
+    if args.prefix_cache:
+        prefix_cache_bench(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",

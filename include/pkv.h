@@ -343,6 +343,35 @@ pkv_status kv_bm_stats(const pkv_bm* bm, int32_t* used, int32_t* total, int64_t*
 /* Reference count of one block (for tests and leak checks). */
 int32_t kv_bm_ref_count(const pkv_bm* bm, int32_t block);
 
+/* Prefix caching ([BJD] §4.1: a request whose prompt starts like an earlier
+ * one reuses that prompt's KV blocks and skips their prefill; §4.3: only an
+ * exact, position-aligned prefix qualifies).  Rules fixed by this library:
+ *  - a full block i of a prompt (tokens [iB, (i+1)B)) has the key
+ *    SHA-256(key(i-1) || its B token ids as little-endian int32), key(-1) =
+ *    32 zero bytes, so a key names the whole prefix up to that block;
+ *  - kv_bm_add_seq_tokens reuses, for the longest run of leading full blocks
+ *    whose keys are cached, those blocks (count + 1, also when they were
+ *    free); every other block is fresh, and each fresh full block becomes
+ *    the cached holder of its key (the previous holder, if any, loses it);
+ *    the partial last block and blocks filled later by appends are never
+ *    cached; *cached_tokens = reused blocks * B, the prefix whose KV is
+ *    already in the pool (the caller computes the rest);
+ *  - a cached block whose count drops to 0 keeps its key and content while
+ *    it waits on the free FIFO; it leaves the cache only when allocation
+ *    takes it, so the least recently freed cached block is evicted first;
+ *  - all or nothing, like the other calls: PKV_ERR_OUT_OF_BLOCKS with no
+ *    change when the free blocks cannot cover the fresh ones.
+ * The caller must write the KV of fresh blocks before another request can
+ * reuse them (same stream order as the decode that follows). */
+pkv_status kv_bm_add_seq_tokens(pkv_bm* bm, int32_t seq, const int32_t* tokens, int32_t n,
+                                int32_t* cached_tokens);
+/* Full-block lookups and hits of kv_bm_add_seq_tokens so far ([KVP] §六 hit
+ * rate) and the number of keys currently cached. */
+pkv_status kv_bm_prefix_stats(const pkv_bm* bm, int64_t* lookups, int64_t* hits, int32_t* cached_blocks);
+/* The key of a block: SHA-256 of parent (32 bytes; NULL = zeros) followed by
+ * tokens[0..n) as little-endian int32 (host arrays; out: 32 bytes). */
+pkv_status kv_bm_block_key(const uint8_t* parent, const int32_t* tokens, int32_t n, uint8_t* out);
+
 #ifdef __cplusplus
 }
 #endif

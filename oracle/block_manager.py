@@ -31,11 +31,29 @@ tables, slots and copy pairs are unique and comparable bit for bit:
   the failed-allocation counter rises by one and nothing else changes.
 * Freeing a sequence releases its blocks in table order.
 * Table rows are padded with 0 past the sequence's blocks.
+
+Prefix caching (bjdmk.com.cn article, §4.1: a prompt that starts like an
+earlier one reuses that prompt's KV blocks; §4.3: only an exact prefix at the
+same positions qualifies):
+
+* The key of full prompt block i is SHA-256(key(i-1) + its B token ids as
+  little-endian int32), key(-1) = 32 zero bytes - a chain, so a key names the
+  whole prefix up to the block.
+* A new prompt reuses the longest run of leading full blocks whose keys are
+  cached (their counts rise, also from zero); all other blocks are fresh, and
+  each fresh full block becomes the holder of its key.  The partial last
+  block and blocks filled by later appends are not cached.
+* A cached block freed to count zero keeps its key on the free queue and
+  leaves the cache when the queue hands it out again (least recently freed
+  first).  A reused free block is taken out of the queue.
 """
 
 from __future__ import annotations
 
+import hashlib
 from collections import deque
+
+import numpy as np
 
 OK, ERR_INVALID, ERR_UNSUPPORTED, ERR_OUT_OF_BLOCKS = 0, -1, -2, -3
 
@@ -54,11 +72,17 @@ class BlockManagerModel:
         self.tables: dict[int, list[int]] = {}
         self.ctx: dict[int, int] = {}
         self.failed_allocs = 0
+        self.cache: dict[bytes, int] = {}        # prefix key -> block
+        self.block_key: dict[int, bytes] = {}    # block -> its key
+        self.lookups = 0
+        self.hits = 0
 
     # ------------------------------------------------------------ helpers
     def _take(self) -> int:
         b = self.free.popleft()
         self.ref[b] = 1
+        if b in self.block_key:                  # evicted: its content is about to change
+            del self.cache[self.block_key.pop(b)]
         return b
 
     # ------------------------------------------------------------ API
@@ -72,6 +96,54 @@ class BlockManagerModel:
         self.tables[seq] = [self._take() for _ in range(need)]
         self.ctx[seq] = ctx_len
         return OK
+
+    @staticmethod
+    def key(parent: bytes | None, tokens) -> bytes:
+        data = (parent if parent is not None else bytes(32)) + np.asarray(tokens, dtype="<i4").tobytes()
+        return hashlib.sha256(data).digest()
+
+    def add_seq_tokens(self, seq: int, tokens):
+        """Returns (status, cached tokens)."""
+        tokens = [int(t) for t in tokens]
+        if seq in self.tables:
+            return ERR_INVALID, 0
+        B = self.B
+        n = len(tokens)
+        full, total = n // B, -(-n // B)
+        keys = []
+        for i in range(full):
+            keys.append(self.key(keys[-1] if keys else None, tokens[i * B:(i + 1) * B]))
+        matched = 0
+        while matched < full and keys[matched] in self.cache:
+            matched += 1
+        matched_free = sum(1 for i in range(matched) if self.ref[self.cache[keys[i]]] == 0)
+        if total - matched > len(self.free) - matched_free:
+            self.failed_allocs += 1
+            return ERR_OUT_OF_BLOCKS, 0
+        self.lookups += full
+        self.hits += matched
+        table = []
+        for i in range(matched):
+            b = self.cache[keys[i]]
+            if self.ref[b] == 0:
+                self.free.remove(b)
+            self.ref[b] += 1
+            table.append(b)
+        for i in range(matched, total):
+            b = self._take()
+            table.append(b)
+            if i < full:
+                old = self.cache.get(keys[i])
+                if old is not None:
+                    del self.block_key[old]
+                self.cache[keys[i]] = b
+                self.block_key[b] = keys[i]
+        self.tables[seq] = table
+        self.ctx[seq] = n
+        return OK, matched * B
+
+    def prefix_stats(self):
+        return self.lookups, self.hits, len(self.cache)
 
     def fork(self, parent: int, child: int) -> int:
         if parent not in self.tables or child in self.tables:

@@ -107,6 +107,9 @@ SIGNATURES = {
     "kv_bm_block_tables": (_I32, [_P, _I32P, _I32, _I32P, _I32, _I32P]),
     "kv_bm_stats": (_I32, [_P, _I32P, _I32P, _I64P]),
     "kv_bm_ref_count": (_I32, [_P, _I32]),
+    "kv_bm_add_seq_tokens": (_I32, [_P, _I32, _I32P, _I32, _I32P]),
+    "kv_bm_prefix_stats": (_I32, [_P, _I64P, _I64P, _I32P]),
+    "kv_bm_block_key": (_I32, [_P, _I32P, _I32, _P]),
 }
 for _name, (_res, _args) in SIGNATURES.items():
     _fn = getattr(_lib, _name)
@@ -287,6 +290,15 @@ def check_tables(tables: np.ndarray, context_lens: np.ndarray, block_size: int, 
 
 
 # ------------------------------------------------------------------- block manager
+def block_key(parent: bytes | None, tokens) -> bytes:
+    """The library's prefix-cache key of a block (SHA-256, see pkv.h)."""
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    out = (ctypes.c_uint8 * 32)()
+    par = None if parent is None else (ctypes.c_uint8 * 32).from_buffer_copy(parent)
+    _check(_lib.kv_bm_block_key(par, _np_ptr(t, ctypes.c_int32), t.size, out))
+    return bytes(out)
+
+
 class BlockManager:
     """Host block manager (C++).  See pkv.h for its allocation rules."""
 
@@ -342,6 +354,21 @@ class BlockManager:
         _check(_lib.kv_bm_block_tables(self._h, _np_ptr(s, ctypes.c_int32), s.size,
                                        _np_ptr(tab, ctypes.c_int32), width, _np_ptr(ctx, ctypes.c_int32)))
         return tab, ctx
+
+    def add_seq_tokens(self, seq: int, tokens) -> int:
+        """New sequence holding the prompt ``tokens``, reusing cached prefix
+        blocks; returns the number of leading tokens whose KV is already in
+        the pool."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        cached = ctypes.c_int32(0)
+        _check(_lib.kv_bm_add_seq_tokens(self._h, seq, _np_ptr(t, ctypes.c_int32), t.size, ctypes.byref(cached)))
+        return cached.value
+
+    def prefix_stats(self):
+        """(full-block lookups, hits, cached keys)."""
+        lk, hit, cached = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32()
+        _check(_lib.kv_bm_prefix_stats(self._h, ctypes.byref(lk), ctypes.byref(hit), ctypes.byref(cached)))
+        return lk.value, hit.value, cached.value
 
     def stats(self):
         used, total, failed = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()

@@ -6,19 +6,41 @@
 // table mapping logical block i to a physical block.  Forked sequences share
 // their parent's blocks; the first write into a shared block copies it and
 // repoints the writer's table (bjdmk.com.cn article, §3.1 and §3.2
-// Copy-on-Write).  The tie-break rules that make tables, slots and copy pairs
-// unique are stated with the declarations in pkv.h.
+// Copy-on-Write).  Prompt blocks can be found again by content: a full block's
+// key hashes its tokens and the key of the block before it, and a request
+// whose prompt starts with a cached run of blocks reuses them (same article,
+// §4.1 prefix caching; §4.3: only an exact, position-aligned prefix is
+// reused).  The tie-break rules that make tables, slots and copy pairs unique
+// are stated with the declarations in pkv.h.
 #include <deque>
 #include <new>
 #include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "pkv_internal.h"
+#include "sha256.h"
+
+namespace {
+struct DigestHash {
+  size_t operator()(const pkv::Digest& d) const {
+    size_t h;
+    std::memcpy(&h, d.data(), sizeof h);
+    return h;
+  }
+};
+}  // namespace
 
 struct pkv_bm {
   int32_t num_blocks = 0;
   int32_t block_size = 0;
-  std::deque<int32_t> free_list;            // FIFO: pop front, push back
+  // FIFO of free blocks: pop front, push back.  An entry is live while its
+  // generation is the block's current one and the block is unreferenced; a
+  // cached free block that a prefix hit takes back leaves a dead entry
+  // behind, skipped when it reaches the front.
+  std::deque<std::pair<int32_t, uint32_t>> free_list;
+  std::vector<uint32_t> gen;
+  int64_t num_free = 0;
   std::vector<int32_t> ref;                 // per physical block
   struct Seq {
     std::vector<int32_t> table;
@@ -26,12 +48,37 @@ struct pkv_bm {
   };
   std::unordered_map<int32_t, Seq> seqs;
   int64_t failed_allocs = 0;
+  // prefix cache: key -> block; a block's own key while it holds one
+  std::unordered_map<pkv::Digest, int32_t, DigestHash> cache;
+  std::vector<pkv::Digest> block_key;
+  std::vector<uint8_t> keyed;
+  int64_t lookups = 0, hits = 0;
 
+  void push_free(int32_t b) {
+    free_list.emplace_back(b, ++gen[(size_t)b]);
+    ++num_free;
+  }
+  void release(int32_t b) {
+    if (--ref[(size_t)b] == 0) push_free(b);
+  }
+  void unkey(int32_t b) {
+    if (keyed[(size_t)b]) {
+      cache.erase(block_key[(size_t)b]);
+      keyed[(size_t)b] = 0;
+    }
+  }
+  // The front live free block, now referenced once; it leaves the cache
+  // (its content is about to be overwritten).
   int32_t take() {
-    const int32_t b = free_list.front();
-    free_list.pop_front();
-    ref[(size_t)b] = 1;
-    return b;
+    while (true) {
+      const auto e = free_list.front();
+      free_list.pop_front();
+      if (e.second != gen[(size_t)e.first] || ref[(size_t)e.first] != 0) continue;   // dead entry
+      ref[(size_t)e.first] = 1;
+      --num_free;
+      unkey(e.first);
+      return e.first;
+    }
   }
 };
 
@@ -49,6 +96,9 @@ pkv_status kv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* i
   bm->num_blocks = num_blocks;
   bm->block_size = block_size;
   bm->ref.assign((size_t)num_blocks, 0);
+  bm->gen.assign((size_t)num_blocks, 0);
+  bm->block_key.resize((size_t)num_blocks);
+  bm->keyed.assign((size_t)num_blocks, 0);
   if (initial_order) {
     std::vector<uint8_t> seen((size_t)num_blocks, 0);
     for (int32_t i = 0; i < num_blocks; ++i) {
@@ -59,10 +109,10 @@ pkv_status kv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* i
         return PKV_ERR_INVALID;
       }
       seen[(size_t)b] = 1;
-      bm->free_list.push_back(b);
+      bm->push_free(b);
     }
   } else {
-    for (int32_t b = 0; b < num_blocks; ++b) bm->free_list.push_back(b);
+    for (int32_t b = 0; b < num_blocks; ++b) bm->push_free(b);
   }
   *out = bm;
   clear_error();
@@ -79,9 +129,9 @@ pkv_status kv_bm_add_seq(pkv_bm* bm, int32_t seq, int32_t ctx_len) {
     return PKV_ERR_INVALID;
   }
   const int64_t need = ((int64_t)ctx_len + bm->block_size - 1) / bm->block_size;
-  if (need > (int64_t)bm->free_list.size()) {
+  if (need > bm->num_free) {
     bm->failed_allocs++;
-    set_error("sequence %d needs %lld blocks, %zu free", seq, (long long)need, bm->free_list.size());
+    set_error("sequence %d needs %lld blocks, %lld free", seq, (long long)need, (long long)bm->num_free);
     return PKV_ERR_OUT_OF_BLOCKS;
   }
   pkv_bm::Seq s;
@@ -152,9 +202,9 @@ pkv_status kv_bm_append(pkv_bm* bm, const int32_t* seqs, int32_t n, int64_t* slo
       }
     }
   }
-  if (need > (int64_t)bm->free_list.size()) {
+  if (need > bm->num_free) {
     bm->failed_allocs++;
-    set_error("append needs %lld blocks, %zu free", (long long)need, bm->free_list.size());
+    set_error("append needs %lld blocks, %lld free", (long long)need, (long long)bm->num_free);
     return PKV_ERR_OUT_OF_BLOCKS;
   }
   int32_t np = 0;
@@ -190,9 +240,7 @@ pkv_status kv_bm_free_seq(pkv_bm* bm, int32_t seq) {
     set_error("sequence %d does not exist", seq);
     return PKV_ERR_INVALID;
   }
-  for (int32_t b : it->second.table) {
-    if (--bm->ref[(size_t)b] == 0) bm->free_list.push_back(b);
-  }
+  for (int32_t b : it->second.table) bm->release(b);
   bm->seqs.erase(it);
   clear_error();
   return PKV_OK;
@@ -227,7 +275,7 @@ pkv_status kv_bm_block_tables(const pkv_bm* bm, const int32_t* seqs, int32_t n, 
 
 pkv_status kv_bm_stats(const pkv_bm* bm, int32_t* used, int32_t* total, int64_t* failed_allocs) {
   if (!bm) return fail(PKV_ERR_INVALID, "bm is NULL");
-  if (used) *used = bm->num_blocks - (int32_t)bm->free_list.size();
+  if (used) *used = bm->num_blocks - (int32_t)bm->num_free;
   if (total) *total = bm->num_blocks;
   if (failed_allocs) *failed_allocs = bm->failed_allocs;
   return PKV_OK;
@@ -236,6 +284,91 @@ pkv_status kv_bm_stats(const pkv_bm* bm, int32_t* used, int32_t* total, int64_t*
 int32_t kv_bm_ref_count(const pkv_bm* bm, int32_t block) {
   if (!bm || block < 0 || block >= bm->num_blocks) return -1;
   return bm->ref[(size_t)block];
+}
+
+pkv_status kv_bm_block_key(const uint8_t* parent, const int32_t* tokens, int32_t n, uint8_t* out) {
+  if (!out || n < 0 || (n > 0 && !tokens)) return fail(PKV_ERR_INVALID, "bad key arguments");
+  pkv::Sha256 h;
+  uint8_t zero[32] = {0};
+  h.update(parent ? parent : zero, 32);
+  // token ids as little-endian 32-bit words, in one buffer
+  std::vector<uint8_t> buf((size_t)n * 4);
+  for (int32_t i = 0; i < n; ++i) {
+    const uint32_t t = (uint32_t)tokens[i];
+    buf[(size_t)4 * i] = (uint8_t)t;
+    buf[(size_t)4 * i + 1] = (uint8_t)(t >> 8);
+    buf[(size_t)4 * i + 2] = (uint8_t)(t >> 16);
+    buf[(size_t)4 * i + 3] = (uint8_t)(t >> 24);
+  }
+  h.update(buf.data(), buf.size());
+  const pkv::Digest d = h.finish();
+  std::memcpy(out, d.data(), 32);
+  clear_error();
+  return PKV_OK;
+}
+
+pkv_status kv_bm_add_seq_tokens(pkv_bm* bm, int32_t seq, const int32_t* tokens, int32_t n,
+                                int32_t* cached_tokens) {
+  if (!bm) return fail(PKV_ERR_INVALID, "bm is NULL");
+  if (n < 0 || (n > 0 && !tokens)) return fail(PKV_ERR_INVALID, "bad token arguments");
+  if (bm->seqs.count(seq)) {
+    set_error("sequence %d already exists", seq);
+    return PKV_ERR_INVALID;
+  }
+  const int32_t B = bm->block_size;
+  const int64_t full = n / B;
+  const int64_t total = ((int64_t)n + B - 1) / B;
+  std::vector<pkv::Digest> keys((size_t)full);
+  for (int64_t i = 0; i < full; ++i)
+    kv_bm_block_key(i ? keys[(size_t)(i - 1)].data() : nullptr, tokens + i * B, B, keys[(size_t)i].data());
+  // the longest run of leading blocks already cached
+  int64_t matched = 0, matched_free = 0;
+  while (matched < full) {
+    auto it = bm->cache.find(keys[(size_t)matched]);
+    if (it == bm->cache.end()) break;
+    if (bm->ref[(size_t)it->second] == 0) ++matched_free;
+    ++matched;
+  }
+  if (total - matched > bm->num_free - matched_free) {
+    bm->failed_allocs++;
+    set_error("sequence %d needs %lld fresh blocks, %lld free", seq, (long long)(total - matched),
+              (long long)(bm->num_free - matched_free));
+    return PKV_ERR_OUT_OF_BLOCKS;
+  }
+  bm->lookups += full;
+  bm->hits += matched;
+  pkv_bm::Seq s;
+  s.table.reserve((size_t)total);
+  for (int64_t i = 0; i < matched; ++i) {
+    const int32_t b = bm->cache.find(keys[(size_t)i])->second;
+    if (bm->ref[(size_t)b] == 0) --bm->num_free;   // its free-list entry dies
+    bm->ref[(size_t)b]++;
+    s.table.push_back(b);
+  }
+  for (int64_t i = matched; i < total; ++i) {
+    const int32_t b = bm->take();
+    s.table.push_back(b);
+    if (i < full) {   // a full prompt block: findable by its key from now on
+      auto it = bm->cache.find(keys[(size_t)i]);
+      if (it != bm->cache.end()) bm->keyed[(size_t)it->second] = 0;   // an older holder of the key loses it
+      bm->cache[keys[(size_t)i]] = b;
+      bm->block_key[(size_t)b] = keys[(size_t)i];
+      bm->keyed[(size_t)b] = 1;
+    }
+  }
+  s.len = n;
+  bm->seqs.emplace(seq, std::move(s));
+  if (cached_tokens) *cached_tokens = (int32_t)(matched * B);
+  clear_error();
+  return PKV_OK;
+}
+
+pkv_status kv_bm_prefix_stats(const pkv_bm* bm, int64_t* lookups, int64_t* hits, int32_t* cached_blocks) {
+  if (!bm) return fail(PKV_ERR_INVALID, "bm is NULL");
+  if (lookups) *lookups = bm->lookups;
+  if (hits) *hits = bm->hits;
+  if (cached_blocks) *cached_blocks = (int32_t)bm->cache.size();
+  return PKV_OK;
 }
 
 }  // extern "C"

@@ -1,0 +1,65 @@
+"""Prefix caching end to end on the GPU: a second request whose prompt starts
+with the first one's reuses its cached blocks, writes KV only past the
+reused prefix, and decodes to the oracle's output over the full prompt."""
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_436_amd as pkv
+import workloads
+from oracle import attention, cache_ops, codecs
+from tests.gpu_helpers import bf16_dev, dev, errors, read_pool, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("P", [0, 64])
+def test_reused_prefix_blocks_decode_like_a_full_prefill(P):
+    import torch
+    rng = np.random.default_rng(13500 + P)
+    B, H, G, D, NB = 16, 2, 4, 128, 64
+    cfg = pkv.make_config(1, NB, B, H, D, pkv.PKV_KV_BF16)
+    pool = pkv.Pool(cfg)
+    pool.memory.fill_(255)
+    bm = pkv.BlockManager(NB, B, rng.permutation(NB))
+    prefix = rng.integers(0, 1000, size=256).tolist()
+    prompts = [prefix + rng.integers(0, 1000, size=44).tolist(), prefix + rng.integers(0, 1000, size=7).tolist()]
+    # K/V of a token depend on the whole prefix; here: a fixed function of (position, token) for the
+    # shared part and fresh values per request after it
+    kv = {}
+    img = read_pool(pool)
+    for s, pr in enumerate(prompts):
+        cached = bm.add_seq_tokens(s, pr)
+        say(f"request {s}: {len(pr)} tokens, {cached} reused")
+        assert cached == (256 if s else 0)
+        n = len(pr)
+        k = workloads.to_bf16_bits(rng.standard_normal((n, H, D), dtype=np.float32))
+        v = workloads.to_bf16_bits(rng.standard_normal((n, H, D), dtype=np.float32))
+        if s:
+            k[:256], v[:256] = kv[0][0][:256], kv[0][1][:256]   # the reused prefix is request 0's
+        kv[s] = (k, v)
+        tab, _ = bm.block_tables([s], 32)
+        pos = np.arange(cached, n)
+        slots = (tab[0][pos // B].astype(np.int64) * B + pos % B)
+        pkv.reshape_and_cache(pool, 0, bf16_dev(k[cached:]), bf16_dev(v[cached:]), dev(slots))
+        img = cache_ops.reshape_and_cache(img, 0, k[cached:], v[cached:], slots)
+    tables, ctx = bm.block_tables([0, 1], 32)
+    assert (tables[0][:16] == tables[1][:16]).all()
+    q = workloads.to_bf16_bits(rng.standard_normal((2, H * G, D), dtype=np.float32))
+    out = torch.empty((2, H * G, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, pkv.paged_attn_workspace_bytes(2, H * G, D, 32, B, P)), dtype=torch.uint8,
+                     device="cuda")
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
+    pkv.paged_attn_decode(out, bf16_dev(q), pool, 0, dev(tables), dev(ctx), scale, partition_size=P,
+                          workspace=ws if P else None)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = attention.paged_decode(q, img, 0, tables, ctx, scale)
+    # and the same as contiguous attention over each request's full K/V
+    for s in range(2):
+        K = np.asarray(kv[s][0]).view(np.uint16)
+        ref = attention.attend(codecs.bf16_bits_to_f64(q[s]), codecs.bf16_bits_to_f64(K),
+                               codecs.bf16_bits_to_f64(kv[s][1]), scale)
+        assert np.max(np.abs(ref - want[s])) < 1e-12
+    mx, rel = errors(got, want)
+    assert mx <= 1e-2 and rel <= 1e-3
