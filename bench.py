@@ -63,6 +63,10 @@ def parse():
                          "(paged_attn_decode_ex; bytes counted over those positions)")
     ap.add_argument("--kv-dtype", default="bf16", choices=sorted(KV_DTYPES),
                     help="KV storage of the pool (8-bit pools hold random codes; the oracle sample runs for bf16 only)")
+    ap.add_argument("--config", default="", choices=["", "llama8b", "long32k_fp8", "long32k_int8"],
+                    help="instead of the 70B step: one decode layer of another workload (8B-shaped: 64 seqs, "
+                         "ctx 512..4096; 32K quantised: 8 seqs x 32768, block 32, partition 512), rotating over "
+                         "three pool copies so the 256 MB MALL does not hold the working set")
     ap.add_argument("--prefix-cache", type=int, default=0,
                     help="host only: N requests sharing a 1500-token system prompt through the block manager's "
                          "prefix cache; report microseconds per request and the prefill tokens it saves")
@@ -97,6 +101,88 @@ def measured_traffic():
 
 
 HOST_LINK_GBS = 64.0     # PCIe Gen5 x16, one direction
+
+
+def config_bench(args):
+    """One appending decode call per launch on another workload's layer,
+    rotating over three pool copies; HIP events around K back-to-back calls."""
+    import torch
+
+    import paged_kv_cache_436_amd as pkv
+    import workloads
+
+    if args.config == "llama8b":
+        w = workloads.llama8b()
+    else:
+        w = workloads.long_quant(pkv.PKV_KV_FP8_E5M2 if args.config == "long32k_fp8" else pkv.PKV_KV_INT8)
+    S, Hq, Hkv, D, B, W = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.table_width
+    kvt = w.kv_dtype
+    e = 2 if kvt == pkv.PKV_KV_BF16 else 1
+    P = args.partition if args.partition > 0 else (w.partition_size or (W * B + 31) // 32 * 32)
+    cfg = pkv.make_config(1, w.num_blocks, B, Hkv, D, kvt)
+    dev = torch.device("cuda:0")
+    pools = []
+    for i in range(3):
+        pool = pkv.Pool(cfg, device=dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(436006 + i)
+        k_off, v_off, ks_off, vs_off = pool.region_offsets()
+        lb = pool.desc.layer_bytes
+        for off in (k_off, v_off):
+            region = pool.memory[off: off + lb]
+            if e == 2:
+                region.view(torch.bfloat16).normal_(generator=g)
+            else:
+                region.random_(0, 120 if kvt == pkv.PKV_KV_FP8_E5M2 else 256, generator=g)
+        if ks_off is not None:
+            n = (vs_off - ks_off) // 4
+            for off in (ks_off, vs_off):
+                pool.memory[off: off + 4 * n].view(torch.float32).uniform_(0.02, 0.05)
+        pools.append(pool)
+    tables = torch.from_numpy(workloads.static_tables(w)).to(dev)
+    ctx = torch.from_numpy(np.asarray(w.context_lens, np.int32) ).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(436007)
+    q = torch.randn((S, Hq, D), generator=g, device=dev).to(torch.bfloat16)
+    newk = torch.randn((S, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+    newv = torch.randn((S, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(pkv.paged_attn_workspace_bytes(S, Hq, D, W, B, P), dtype=torch.uint8, device=dev)
+    sc = TENSOR_SCALE if kvt == pkv.PKV_KV_FP8_E5M2 else 1.0
+    st = torch.cuda.current_stream()
+
+    def call(i):
+        pkv.paged_attn_decode_append(out, q, pools[i % 3], 0, newk, newv, tables, ctx, w.scale, k_scale=sc,
+                                     v_scale=sc, partition_size=P, workspace=ws, stream=st)
+
+    for i in range(3 * args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    K = 3 * args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for i in range(K):
+        call(i)
+    e1.record(st)
+    torch.cuda.synchronize()
+    per = e0.elapsed_time(e1) * 1e-3 / K
+    tok = int(np.asarray(w.context_lens, np.int64).sum())
+    nbytes = tok * Hkv * (2 * D * e + (8 if kvt == pkv.PKV_KV_INT8 else 0))
+    gbs = nbytes / per / 1e9
+    name = {"llama8b": "8B-shaped decode layer: 64 seqs x ctx 512..4096, 32q/8kv heads, head_dim 128, bf16 KV, "
+                       "block 16",
+            "long32k_fp8": "32K quantised decode layer: 8 seqs x 32768, 64q/8kv heads, head_dim 128, fp8 e5m2 KV, "
+                           "block 32, partition 512",
+            "long32k_int8": "32K quantised decode layer: 8 seqs x 32768, 64q/8kv heads, head_dim 128, int8 "
+                            "per-token KV, block 32, partition 512"}[args.config]
+    res = {"metric": "paged decode KV-read GB/s (% of MI355X HBM peak) + decode seq-steps/s", "value": round(gbs, 2),
+           "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": 3 * args.warmup, "us_per_call": round(per * 1e6, 2),
+           "higher_is_better": True, "dtype": {1: "fp8", 2: "int8"}.get(kvt, "bf16"), "data": "synthetic",
+           "config": {"workload": name, "partition_size": P, "kv_bytes_per_call": nbytes, "pool_copies": 3},
+           "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    print(json.dumps(res), flush=True)
 
 
 def prefix_cache_bench(args):
@@ -202,6 +288,10 @@ def copy_calibration():
 
 def main():
     args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
         return
@@ -211,10 +301,9 @@ def main():
     if args.prefix_cache:
         prefix_cache_bench(args)
         return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
-              file=sys.stderr)
-        sys.exit(2)
+    if args.config:
+        config_bench(args)
+        return
     import torch
 
     import paged_kv_cache_436_amd as pkv

@@ -220,10 +220,15 @@ uint64_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
  *                 workspace.  Otherwise the split-context form, a positive
  *                 multiple of 32: the work of all sequences and heads is cut
  *                 into equal ranges, one per wavefront of a grid sized to the
- *                 GPU; each range yields one partial result per piece of
- *                 context it covers, pieces never crossing a multiple of
- *                 partition_size tokens, and the wavefront that completes a
- *                 sequence's KV head merges its partials.  Needs a device
+ *                 GPU; each range yields one partial result per
+ *                 (sequence, KV head) it covers, and the wavefront that
+ *                 completes a sequence's KV head merges its partials.  A
+ *                 wavefront carries its running softmax across multiples of
+ *                 partition_size, which is the same as merging fixed-length
+ *                 partitions in order, so the result does not depend on the
+ *                 partition size; the size only selects this form.  Too
+ *                 many (sequence, KV head) rows for one call (a partial
+ *                 buffer over 4 GiB) is PKV_ERR_INVALID.  Needs a device
  *                 workspace of paged_attn_workspace_bytes bytes, 256-byte
  *                 aligned; its contents are scratch (no initialisation
  *                 needed).  Calls sharing a workspace must not overlap in

@@ -30,8 +30,8 @@
 //       together whatever the context lengths.  A wave keeps NBUF-1 steps of
 //       K/V loads in flight, across row boundaries too.  It emits one partial
 //       (running max m, sum l, unnormalised acc) per segment: the part of its
-//       range inside one row and one partition of partition_size tokens.  The
-//       wave that completes a row combines the row's partials:
+//       range inside one row.  The wave that completes a row combines the
+//       row's partials:
 //           out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k,  M = max m_k.
 #include <hip/hip_runtime.h>
 
@@ -468,10 +468,16 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
 // of the flat list proportional to kXcdWeight[x], split equally among its
 // waves, and the waves finish at about the same time.  The split depends
 // only on N and the grid, never on timing.
-// Partition p of row x covers its tokens [p * P, (p + 1) * P); unit
-// u = x * NP + p.  The segment of unit u computed by wave w is stored in
-// partial slot u + w: walking the (unit, wave) pairs in order raises u or w
-// (or both) at every step, so the sum is unique.
+// The partials the merge combines are the segments of a row that the waves
+// cover: the part of row x inside wave w's range is stored in partial slot
+// x + w.  Walking the (row, wave) pairs of the flat list in order raises x or
+// w (or both) at every step, so the sum is unique, and slots number at most
+// rows + NWV - 1.  A wave carries its running (m, l, o) across everything it
+// computes of one row: that running state after any prefix of the row's
+// tokens is the merge of the partials of that prefix, so a fixed partition
+// length (a partial every P tokens, merged afterwards) would give the same
+// result up to rounding while adding partials for the final merge to read.
+// The partition size therefore only selects this form.
 // When a wave has computed its whole range it makes its partials visible
 // (device-scope release) and adds, for every row it touched, the number of
 // that row's steps it computed to the row's counter.  The wave whose addition
@@ -480,6 +486,11 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
 // draws anew for every call) above the step count, updated by compare-and-
 // swap; a counter carrying any other epoch counts as zero, so the workspace
 // needs no clearing between calls, whatever sizes earlier calls had.
+// Row counters sit 128 bytes apart: every wave covering a row updates its
+// counter at about the same time, from all eight XCDs, and counters sharing a
+// cache line would serialise the updates of all their rows.
+constexpr int kCounterStride = 16;   // uint64 words
+
 struct SplitParams {
   const uint16_t* q;          // [S][Hq][D] bf16
   float* out;                 // [S][Hq][D]
@@ -492,13 +503,11 @@ struct SplitParams {
   float enc_k, enc_v;         // fp8 per-tensor scales for encoding the new token
   const int32_t* bt;
   const int32_t* ctx;
-  uint64_t* row_done;         // workspace: [rows] (epoch << 32) | steps reported
+  uint64_t* row_done;         // workspace: [rows][kCounterStride] (epoch << 32) | steps reported, in word 0
   float* part_ml;             // workspace: [slots][16][2]  (m, l)
   float* part_acc;            // workspace: [slots][NC][64 lanes][4]
+  uint32_t acc_bytes;         // size of part_acc in bytes (< 4 GiB)
   int32_t W, S, Hq, Hkv, G, QT, HQ, num_blocks;
-  int32_t P;                  // partition size (tokens, multiple of 32)
-  int32_t PS;                 // steps per partition: P / tokens per step
-  int32_t NP;                 // partitions per row: ceil(W * B / P)
   int32_t NWV;                // waves in the grid
   int32_t win;                // sliding window (positions), 0 = whole context
   uint32_t epoch;             // this call's tag for row_done
@@ -851,8 +860,7 @@ struct Cursor {
   int tb;           // first token of the rows' first step (window start, rounded down)
   int g;            // KV head of the row
   int h0, gt;       // first query head of the row's tile, and its number of heads
-  int unit;         // x * NP + partition of step j (x = s * HQ + xi)
-  int pleft;        // steps of that partition left, step j included
+  int x;            // row number s * HQ + xi
   int phys[2];      // table entries of the step at the cursor (prefetched)
 };
 
@@ -862,9 +870,7 @@ __device__ __forceinline__ void cursor_row(Cursor& c, const SplitParams& p) {
   const int qt = c.xi - c.g * p.QT;
   c.h0 = c.g * p.G + qt * 16;
   c.gt = min(16, p.G - qt * 16);
-  const int part = c.j == 0 ? 0 : c.j / p.PS;
-  c.unit = (c.s * p.HQ + c.xi) * p.NP + part;
-  c.pleft = p.PS - (c.j - part * p.PS);
+  c.x = c.s * p.HQ + c.xi;
 }
 
 template <int B, int TS>
@@ -894,15 +900,44 @@ __device__ __forceinline__ f32x2 ld_agent(const float* p) {
   return f32x2{__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32))};
 }
 
+// The accumulator block of one partial slot (NC * 1 KiB) as a buffer
+// resource, and 16-byte loads / stores of it with the same cache policy
+// (the sc1 scope bit) that an agent-scope atomic access of 8 bytes uses, so
+// they too are coherent across XCDs.  The resource's size bounds every access
+// to the slot.
+constexpr int kCoherentScope = 16;     // raw buffer access aux: sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(float* acc, int slot, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(acc + (int64_t)slot * (bytes / 4), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ f32x4 ld_agent4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherentScope));
+}
+__device__ __forceinline__ void st_agent4(__amdgpu_buffer_rsrc_t r, int off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCoherentScope);
+}
+
 // Add `mine` steps to an epoch-tagged row counter; returns the row's total
-// for this epoch after the addition.  A counter of another epoch (an earlier
-// call, or whatever the scratch memory held) restarts from zero.
+// for this epoch after the addition.  Epochs increase from call to call, so
+// raising the counter to (epoch << 32) first turns a counter of an earlier
+// call into a zero count of this one and leaves a counter of this call alone;
+// the add that follows, issued right behind it, takes effect after it (one
+// wave's atomics on one address keep their order).  That costs a single
+// round trip however many waves report at once.  A counter with a larger tag
+// (memory this library never wrote, or epochs that wrapped around) is
+// instead replaced by compare-and-swap; an add that went to such a value is
+// wiped by that replacement and redone by the wave that made it.
 __device__ __forceinline__ int add_steps(uint64_t* ctr, uint32_t epoch, int mine) {
   unsigned long long* c = reinterpret_cast<unsigned long long*>(ctr);
-  unsigned long long expect = 0;
+  const unsigned long long tag = (unsigned long long)epoch << 32;
+  __hip_atomic_fetch_max(c, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long old =
+      __hip_atomic_fetch_add(c, (unsigned long long)(uint32_t)mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((uint32_t)(old >> 32) == epoch) return (int)((uint32_t)old + (uint32_t)mine);
+  unsigned long long expect = old + (uint32_t)mine;
   while (true) {
     const uint32_t base = (uint32_t)(expect >> 32) == epoch ? (uint32_t)expect : 0u;
-    const unsigned long long want = ((unsigned long long)epoch << 32) | (base + (uint32_t)mine);
+    const unsigned long long want = tag | (base + (uint32_t)mine);
     unsigned long long prev = expect;
     if (__hip_atomic_compare_exchange_strong(c, &prev, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT))
@@ -933,84 +968,125 @@ __device__ __forceinline__ void wave_range(int N, int w, int WX, int& a, int& e)
   e = min(a + per, b1);
 }
 
-// The wave whose range holds flat step t < N.
-__device__ __forceinline__ int wave_of(int t, int N, int WX) {
-  int x = 0;
+// Merge the partials of row x into the output rows of its query heads.
+// Wave-cooperative, in the accumulator lane layout: lane (j, row) holds query
+// head row of the tile.  With gt <= 8 heads, the 16 / gp lane groups of the
+// tile (gp = gt rounded up to a power of two) each take a share of the slots,
+// lane (j, row) merging head row % gp, and the groups combine at the end, so
+// that all lanes load.  The slots are those of the waves covering flat steps
+// [sx, sx + ns), which are consecutive waves minus those with empty ranges:
+// lane i tests wave first + i, a ballot gives the set, and the slot of rank n
+// is the n-th wave of the set.  merge_slots() slots per lane group are loaded
+// at a time so that their latencies overlap.
+template <int D>
+constexpr int merge_slots() { return D == 64 ? 16 : 12; }
+
+// Position of the n-th (from 0) set bit of mask, n < popcount(mask).
+__device__ __forceinline__ int nth_set_bit(uint64_t mask, int n) {
+  if ((mask & (mask + 1)) == 0) return n;      // one run from bit 0: the usual case
+  int pos = 0;
 #pragma unroll
-  for (int i = 1; i < 8; ++i) x += t >= xcd_begin(N, i) ? 1 : 0;
-  const int b0 = xcd_begin(N, x), b1 = xcd_begin(N, x + 1);
-  const int per = (b1 - b0 + WX - 1) / WX;
-  return x * WX + (t - b0) / per;
+  for (int w = 32; w >= 1; w >>= 1) {
+    const int c = __builtin_popcountll((mask >> pos) & ((1ull << w) - 1));
+    if (n >= c) {
+      n -= c;
+      pos += w;
+    }
+  }
+  return pos;
 }
 
-// Merge the partials of row x into the output rows of its query heads.
-// Wave-cooperative, in the accumulator lane layout; loads go out four slots
-// at a time so that their latencies overlap.
+// (M, L, A) <- the merge of (M, L, A) and (m, l, a); an empty side has
+// M = -inf, L = 0, A = 0 and contributes nothing.
+template <int NC>
+__device__ __forceinline__ void merge_into(float& M, float& L, f32x4 (&A)[NC], float m, float l,
+                                           const f32x4 (&a)[NC]) {
+  const float Mn = fmaxf(M, m);
+  const float fa = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+  const float fk = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - Mn);
+  L = L * fa + l * fk;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) A[c] = A[c] * fa + a[c] * fk;
+  M = Mn;
+}
+
 template <int D, int E>
 __device__ __forceinline__ void merge_row(const SplitParams& p, int x, int s, int xi, int ns, int sx, int N,
-                                          int TS, int lane) {
+                                          int xbv, int lane) {
   constexpr int NC = D / 16;
+  constexpr int KS = merge_slots<D>();
   const int g = xi / p.QT;
   const int qt = xi - g * p.QT;
   const int row = lane & 15;
   const int j = lane >> 4;
   const int gt = min(16, p.G - qt * 16);
   const int h0 = g * p.G + qt * 16;
-  const int PS = p.P / TS;                        // steps per partition
-  const int np = (ns + PS - 1) / PS;
+  const int gp = gt > 8 ? 16 : gt > 4 ? 8 : gt > 2 ? 4 : gt > 1 ? 2 : 1;
+  const int hs = 16 / gp;                      // lane groups per head
+  const int hr = row & (gp - 1);               // head merged by this lane
+  const int grp = row / gp;                    // its lane group
+  const int src = (j * 16 + hr) * 16;          // byte offset of that head's values in a slot's tile
+  const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(p.part_acc, (short)0, p.acc_bytes, 0x00020000);
   float M = -INFINITY, L = 0.f;
   f32x4 A[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) A[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // slots in order: partitions pp, and for each the waves wv covering it
   const int WX = p.NWV / 8;
-  // walk the row by position: the wave holding step t, then the first step
-  // past that wave's range (waves with empty ranges are never visited)
-  int pp = 0;
-  int t = sx;
-  while (pp < np) {
-    int slot[4];
-    int cnt = 0;
+  const int end = sx + ns;
+  // the loads below follow the counter update that found the row complete
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  // the wave holding step sx (lane i < 9 of xbv holds the first step of XCD
+  // i's share of the list)
+  const int xc = __builtin_popcountll(__ballot(lane >= 1 && lane <= 7 && sx >= xbv));
+  const int b0 = __builtin_amdgcn_readlane(xbv, xc), b1 = __builtin_amdgcn_readlane(xbv, xc + 1);
+  int first = xc * WX + (sx - b0) / ((b1 - b0 + WX - 1) / WX);
+  while (true) {
+    // lane i: does wave first + i hold a partial of this row?
+    const int wl = first + lane;
+    const int xl = min(wl / WX, 8);
+    const int l0 = __shfl(xbv, xl, kWave), l1 = __shfl(xbv, min(xl + 1, 8), kWave);
+    const int al = min(l0 + (wl - xl * WX) * ((l1 - l0 + WX - 1) / WX), l1);   // its first step
+    const uint64_t set = __ballot(xl < 8 && al < l1 && al < end);
+    const int cnt = __builtin_popcountll(set);
+    for (int nb = 0; nb < cnt; nb += KS * hs) {
+      int slot[KS];
+      bool live[KS];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (pp < np) {
-        const int wv = wave_of(t, N, WX);
-        slot[k] = x * p.NP + pp + wv;
-        ++cnt;
-        const int e = sx + min((pp + 1) * PS, ns);     // end of partition pp (flat steps)
-        int ra, re;
-        wave_range(N, wv, WX, ra, re);
-        t = min(re, e);
-        if (t >= e) ++pp;
-      } else {
-        slot[k] = slot[0];
+      for (int k = 0; k < KS; ++k) {
+        const int n = nb + k * hs + grp;
+        live[k] = n < cnt;
+        slot[k] = x + first + nth_set_bit(set, live[k] ? n : 0);
+      }
+      f32x2 ml[KS];
+      f32x4 av[KS][NC];
+      if (hr < gt) {
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          ml[k] = ld_agent(p.part_ml + ((int64_t)slot[k] * 16 + hr) * 2);
+          const uint32_t base = (uint32_t)slot[k] * (NC * 1024u) + src;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) av[k][c] = ld_agent4(pr, base + c * 1024);
+        }
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+          if (live[k]) merge_into<NC>(M, L, A, ml[k][0], ml[k][1], av[k]);
       }
     }
-    f32x2 ml[4];
-    f32x4 a[4][NC];
+    // the next 64 waves, if the last one tested starts inside the row
+    if (__builtin_amdgcn_readlane(xl < 8 && al < end ? 1 : 0, kWave - 1) == 0) break;
+    first += kWave;
+  }
+  // combine the lane groups of each head (partner lanes stay inside the
+  // 16-lane run of one j)
+  for (int off = gp; off < 16; off <<= 1) {
+    const float m2 = __shfl_xor(M, off, kWave);
+    const float l2 = __shfl_xor(L, off, kWave);
+    f32x4 a2[NC];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      ml[k] = ld_agent(p.part_ml + ((int64_t)slot[k] * 16 + row) * 2);
-      const float* pa = p.part_acc + (int64_t)slot[k] * (NC * 256) + lane * 4;
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const f32x2 lo = ld_agent(pa + c * 256);
-        const f32x2 hi = ld_agent(pa + c * 256 + 2);
-        a[k][c] = f32x4{lo[0], lo[1], hi[0], hi[1]};
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (k < cnt) {
-        const float Mn = fmaxf(M, ml[k][0]);
-        const float fa = __builtin_amdgcn_exp2f(M - Mn);
-        const float fk = __builtin_amdgcn_exp2f(ml[k][0] - Mn);
-        L = L * fa + ml[k][1] * fk;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) A[c] = A[c] * fa + a[k][c] * fk;
-        M = Mn;
-      }
-    }
+      for (int i = 0; i < 4; ++i) a2[c][i] = __shfl_xor(A[c][i], off, kWave);
+    merge_into<NC>(M, L, A, m2, l2, a2);
   }
   if (row < gt) {
     float* orow = p.out + ((int64_t)s * p.Hq + h0 + row) * D;
@@ -1166,18 +1242,14 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
     const bool live = issued < nsteps;
     const bool new_row = live && (cur.j == 0 || issued == 0);
     if (new_row) qr = load_q<D, KVT>(p, cur.s, cur.h0, cur.gt, lane);
-    const bool flush = issued + 1 == nsteps || cur.j + 1 == cur.n || cur.pleft == 1;
+    const bool flush = issued + 1 == nsteps || cur.j + 1 == cur.n;
     m.t0 = cur.tb + cur.j * TS;
     m.t_end = live ? cur.ctx : 0;
-    m.slot = cur.unit + w;
+    m.slot = cur.x + w;
     m.flags = (new_row ? kNewRow : 0) | (flush ? kFlush : 0) | (cur.gt << 8);
     issue_chunks<D, KVT, B>(r, p, cur.phys, cur.g, m.t0, window_lo(m.t_end, p.win), m.t_end, lane);
     ++issued;
     if (issued < nsteps) {     // advance to the next step and fetch its table entries
-      if (--cur.pleft == 0) {
-        cur.pleft = p.PS;
-        ++cur.unit;
-      }
       if (++cur.j == cur.n) {
         cur.j = 0;
         if (++cur.xi == p.HQ) {
@@ -1209,12 +1281,9 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
       const float l = sum_x32(sum_x16(l_run));
       const int gt = m.flags >> 8;
       if (row < gt) {
-        float* pa = p.part_acc + (int64_t)m.slot * (GE::NC * 256) + lane * 4;
+        const __amdgpu_buffer_rsrc_t pr = slot_rsrc(p.part_acc, m.slot, GE::NC * 1024);
 #pragma unroll
-        for (int c = 0; c < GE::NC; ++c) {
-          st_agent(pa + c * 256, acc[c][0], acc[c][1]);
-          st_agent(pa + c * 256 + 2, acc[c][2], acc[c][3]);
-        }
+        for (int c = 0; c < GE::NC; ++c) st_agent4(pr, c * 1024 + lane * 16, acc[c]);
         if (j == 0) st_agent(p.part_ml + ((int64_t)m.slot * 16 + row) * 2, m_run, l);
       }
 #pragma unroll
@@ -1251,6 +1320,7 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
   // rows go 64 at a time, one per lane: their counters are raised by
   // concurrent compare-and-swaps, then the rows this wave completed are merged
   int rs = first.s, rxi = first.xi, rn = first.n, rj = first.j, rcum = cum0;
+  const int xbv = lane <= 8 ? xcd_begin(N, lane) : 0;     // XCD boundaries of the flat list, for merges
   int left = nsteps;
   while (left > 0) {
     int lx = -1, lmine = 0, ln = 0, ls = 0, lxi = 0, lsx = 0;
@@ -1276,14 +1346,14 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
       }
     }
     int done_now = 0;
-    if (lx >= 0) done_now = add_steps(p.row_done + lx, p.epoch, lmine);
+    if (lx >= 0) done_now = add_steps(p.row_done + (int64_t)lx * kCounterStride, p.epoch, lmine);
     uint64_t complete = __ballot(lx >= 0 && done_now == ln);   // every partial of the row is in place
     while (complete) {
       const int l = __builtin_ctzll(complete);
       complete &= complete - 1;
       merge_row<D, GE::E>(p, __builtin_amdgcn_readlane(lx, l), __builtin_amdgcn_readlane(ls, l),
                           __builtin_amdgcn_readlane(lxi, l), __builtin_amdgcn_readlane(ln, l),
-                          __builtin_amdgcn_readlane(lsx, l), N, TS, lane);
+                          __builtin_amdgcn_readlane(lsx, l), N, xbv, lane);
     }
   }
 }
@@ -1410,7 +1480,7 @@ int64_t split_grid(int64_t steps_ub, int cus, int blocks_per_cu) {
 }
 
 struct SplitSizes {
-  int64_t rows, np, slots_cap, cnt_bytes, ml_bytes, acc_bytes;
+  int64_t rows, slots_cap, cnt_bytes, ml_bytes, acc_bytes;
 };
 
 // Workspace regions for the largest grid any variant may launch.
@@ -1421,11 +1491,11 @@ bool split_sizes(int32_t S, int32_t Hq, int32_t Hkv_or_0, int32_t D, int32_t W, 
   (void)Hkv_or_0;
   // rows: at most S * Hq (one head per row when G == 1)
   z->rows = (int64_t)S * Hq;
-  z->np = ceil_div((int64_t)W * B, P);
+  (void)P;                       // partials are per (row, wave) segment, whatever the partition size
   const int64_t steps_ub = z->rows * ceil_div((int64_t)W * B, 16);
   const int64_t waves_cap = split_grid(steps_ub, cus, kMaxBlocksPerCU) * kNW;
-  z->slots_cap = z->rows * z->np + waves_cap;
-  z->cnt_bytes = align_up((uint64_t)z->rows * sizeof(uint64_t));
+  z->slots_cap = z->rows + waves_cap;
+  z->cnt_bytes = align_up((uint64_t)z->rows * kCounterStride * sizeof(uint64_t));
   z->ml_bytes = align_up((uint64_t)z->slots_cap * 16 * 2 * sizeof(float));
   z->acc_bytes = align_up((uint64_t)z->slots_cap * (D / 16) * 256 * sizeof(float));
   return true;
@@ -1587,13 +1657,14 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     }
     const int TS = c.kv_dtype == PKV_KV_BF16 ? 16 : 32;
     const int64_t steps_ub = rows * ceil_div((int64_t)table_width * c.block_size, TS);
-    const int64_t np = ceil_div((int64_t)table_width * c.block_size, partition_size);
-    if (steps_ub > INT32_MAX / 2 || rows * np > INT32_MAX / 4) return fail(PKV_ERR_INVALID, "problem too large for one call");
+    if (steps_ub > INT32_MAX / 2) return fail(PKV_ERR_INVALID, "problem too large for one call");
     SplitSizes z;
     if (!split_sizes(num_seqs, num_q_heads, c.num_kv_heads, c.head_dim, table_width, c.block_size, partition_size,
                      &z))
       return fail(PKV_ERR_HIP, "could not query the current device");
     const uint64_t need = (uint64_t)(z.cnt_bytes + z.ml_bytes + z.acc_bytes);
+    if (z.acc_bytes > (int64_t)UINT32_MAX)
+      return fail(PKV_ERR_INVALID, "too many (sequence, KV head) rows for one split-context call: split the batch");
     if (!workspace || workspace_bytes < need) {
       set_error("workspace of %llu bytes needed, got %llu", (unsigned long long)need,
                 (unsigned long long)workspace_bytes);
@@ -1604,7 +1675,7 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     device_cus(&cus);
     const int bpc = split_blocks_per_cu(c.head_dim, c.kv_dtype, c.block_size);
     const int64_t grid = split_grid(steps_ub, cus, bpc);
-    if (grid * kNW + rows * np > z.slots_cap) return fail(PKV_ERR_INVALID, "internal: workspace sizing");
+    if (grid * kNW + rows > z.slots_cap) return fail(PKV_ERR_INVALID, "internal: workspace sizing");
     SplitParams p{};
     p.q = qk;
     p.q_stride = q_stride;
@@ -1625,6 +1696,7 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     p.row_done = reinterpret_cast<uint64_t*>(ws);
     p.part_ml = reinterpret_cast<float*>(ws + z.cnt_bytes);
     p.part_acc = reinterpret_cast<float*>(ws + z.cnt_bytes + z.ml_bytes);
+    p.acc_bytes = (uint32_t)z.acc_bytes;
     p.W = table_width;
     p.S = num_seqs;
     p.Hq = num_q_heads;
@@ -1633,9 +1705,6 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     p.QT = QT;
     p.HQ = c.num_kv_heads * QT;
     p.num_blocks = c.num_blocks;
-    p.P = partition_size;
-    p.PS = partition_size / TS;
-    p.NP = (int32_t)np;
     p.NWV = (int32_t)(grid * kNW);
     p.win = sliding_window;
     p.epoch = next_epoch();
