@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32],
+                    help="tokens per KV block of the 70B step (default 16)")
     ap.add_argument("--partition", type=int, default=-1,
                     help="split-context partition size in tokens (-1: the whole table span, one partition)")
     ap.add_argument("--layers", type=int, default=80,
@@ -312,7 +314,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     steps_total = args.warmup + args.steps + 1
-    w = workloads.llama70b(num_layers=80, extra_steps=steps_total)
+    w = workloads.llama70b(num_layers=80, extra_steps=steps_total, block_size=args.block_size)
     L = args.layers
     S, Hq, Hkv, D, B, W = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.table_width
     P = args.partition if args.partition > 0 else (W * B + 31) // 32 * 32
@@ -458,7 +460,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu, parity = cpu_baseline(args, pkv, w, pool, decode, q, out, d_tab, d_ctx, scale)
     workload = ("70B-shaped paged decode step: 80 layers x 100 seqs x ~4K ctx, "
-                f"64q/8kv heads, head_dim 128, {args.kv_dtype} KV, block 16")
+                f"64q/8kv heads, head_dim 128, {args.kv_dtype} KV, block {B}")
     if window:
         workload += f", sliding window of the last {window} positions"
 

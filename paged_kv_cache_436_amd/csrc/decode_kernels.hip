@@ -232,28 +232,42 @@ __device__ __forceinline__ void issue_step(StepRegs<D, KVT>& r, const DecodePara
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int t = tok0 + 16 * h;                   // first token of the chunk (multiple of 16)
-    int lb = t / B;
-    lb = lb < p.W ? lb : p.W - 1;                  // never index past the table row
-    // a chunk wholly before the window does not use its table entry (block 0
-    // instead; its tokens are masked)
-    int phys = t + 16 > t_lo ? bt_row[lb] : 0;
-    phys = phys < 0 ? 0 : (phys >= p.num_blocks ? p.num_blocks - 1 : phys);  // stay inside the pool
-    const int toff = t % B;                        // chunk offset inside the block (0 or 16)
-    const int64_t tile = ((int64_t)phys * p.Hkv + g) * (int64_t)(B * D * E);
-    const char* kt = p.k + tile;
-    const char* vt = p.v + tile;
+    // a chunk wholly before the window does not use its table entries (block
+    // 0 instead; its tokens are masked).  With B = 8 the chunk spans two blocks.
+    const bool used = t + 16 > t_lo;
+    int ph[2];
+#pragma unroll
+    for (int b = 0; b < (B < 16 ? 2 : 1); ++b) {
+      int lb = t / B + b;
+      lb = lb < p.W ? lb : p.W - 1;                // never index past the table row
+      const int e = used ? bt_row[lb] : 0;
+      ph[b] = e < 0 ? 0 : (e >= p.num_blocks ? p.num_blocks - 1 : e);  // stay inside the pool
+    }
+    if (B >= 16) ph[1] = ph[0];
+    // K: lane row reads token t + row; V and the int8 scales: lane j reads
+    // tokens t + 4j .. t + 4j + 3
+    const int phk = row < 8 ? ph[0] : ph[1];
+    const int phv = j < 2 ? ph[0] : ph[1];
+    // chunks start at multiples of 16 tokens: with B >= 16 the chunk sits at
+    // offset t % B of one block, with B = 8 it starts both of its blocks
+    constexpr int TM = (B < 16 ? B : 16) - 1;
+    const int toff = B < 16 ? 0 : t % B;
+    const int tk = toff + (row & TM);              // token of lane row inside its block
+    const int tv = toff + ((4 * j) & TM);          // first token of lane j's group inside its block
+    const char* kt = p.k + ((int64_t)phk * p.Hkv + g) * (int64_t)(B * D * E);
+    const char* vt = p.v + ((int64_t)phv * p.Hkv + g) * (int64_t)(B * D * E);
     // K: piece c holds dims [X*c, X*c+X) of all B tokens, 16 bytes per token
 #pragma unroll
-    for (int u = 0; u < T::KLOADS; ++u) r.k[h][u] = ld16(kt + ((int64_t)((4 * u + j) * B + toff + row)) * 16);
-    // V: token group (toff/4 + j), 4 tokens x dims as 4E-byte words
-    const int grp = (toff >> 2) + j;
+    for (int u = 0; u < T::KLOADS; ++u) r.k[h][u] = ld16(kt + ((int64_t)((4 * u + j) * B + tk)) * 16);
+    // V: token group tv / 4, 4 tokens x dims as 4E-byte words
+    const int grp = tv >> 2;
 #pragma unroll
     for (int u = 0; u < T::VLOADS; ++u) {
       const int d = (E == 2) ? (32 * u + 2 * row) : (64 * u + 4 * row);
       r.v[h][u] = ld16(vt + ((int64_t)(grp * D + d)) * 4 * E);
     }
     if constexpr (KVT == PKV_KV_INT8) {
-      const int64_t so = ((int64_t)phys * p.Hkv + g) * B + toff + 4 * j;
+      const int64_t so = ((int64_t)phv * p.Hkv + g) * B + tv;
       r.ksc[h] = *reinterpret_cast<const f32x4*>(p.ks + so);
       r.vsc[h] = *reinterpret_cast<const f32x4*>(p.vs + so);
     }
@@ -591,7 +605,7 @@ __device__ __forceinline__ QRegs<SplitGeo<D, KVT>::KK> load_q(const SplitParams&
 // load keeps the number of loads per step fixed, which the compiler's
 // wait-count tracking needs to let later steps' loads stay in flight.
 template <int D, int KVT, int B>
-__device__ __forceinline__ void issue_chunks(SplitBuf<D, KVT>& r, const SplitParams& p, const int (&phys)[2],
+__device__ __forceinline__ void issue_chunks(SplitBuf<D, KVT>& r, const SplitParams& p, const int (&phys)[4],
                                              int g, int t0, int t_lo, int t_end, int lane) {
   using GE = SplitGeo<D, KVT>;
   constexpr int E = GE::E;
@@ -601,20 +615,32 @@ __device__ __forceinline__ void issue_chunks(SplitBuf<D, KVT>& r, const SplitPar
   for (int h = 0; h < GE::CH; ++h) {
     const int t = t0 + 16 * h;
     const bool live = t < t_end && t + 16 > t_lo;  // wave-uniform
-    const int toff = live ? t % B : 0;
-    const int64_t tile = live ? ((int64_t)phys[h] * p.Hkv + g) : 0;
-    const char* kt = p.k + tile * (int64_t)(B * D * E);
-    const char* vt = p.v + tile * (int64_t)(B * D * E);
+    // with B = 8 the chunk spans two blocks: K lane row reads token t + row,
+    // V (and the int8 scales) lane j tokens t + 4j .. t + 4j + 3
+    const int pa = B < 16 ? phys[2 * h] : phys[h];
+    const int pb = B < 16 ? phys[2 * h + 1] : phys[h];
+    const int pk = row < 8 ? pa : pb;
+    const int pv = j < 2 ? pa : pb;
+    // chunks start at multiples of 16 tokens: with B >= 16 the chunk sits at
+    // offset t % B of one block, with B = 8 it starts both of its blocks
+    constexpr int TM = (B < 16 ? B : 16) - 1;
+    const int toff = (B < 16 || !live) ? 0 : t % B;
+    const int tk = toff + (row & TM);
+    const int tv = toff + ((4 * j) & TM);
+    const int64_t tilek = live ? ((int64_t)pk * p.Hkv + g) : 0;
+    const int64_t tilev = live ? ((int64_t)pv * p.Hkv + g) : 0;
+    const char* kt = p.k + tilek * (int64_t)(B * D * E);
+    const char* vt = p.v + tilev * (int64_t)(B * D * E);
 #pragma unroll
-    for (int u = 0; u < GE::LPC; ++u) r.k[h][u] = ld16(kt + ((4 * u + j) * B + toff + row) * 16);
-    const int grp = (toff >> 2) + j;
+    for (int u = 0; u < GE::LPC; ++u) r.k[h][u] = ld16(kt + ((4 * u + j) * B + tk) * 16);
+    const int grp = tv >> 2;
 #pragma unroll
     for (int u = 0; u < GE::LPC; ++u) {
       const int d = (E == 2) ? (32 * u + 2 * row) : (64 * u + 4 * row);
       r.v[h][u] = ld16(vt + (grp * D + d) * 4 * E);
     }
     if constexpr (KVT == PKV_KV_INT8) {
-      const int64_t so = tile * B + toff + 4 * j;
+      const int64_t so = tilev * B + tv;
       r.ksc[h] = *reinterpret_cast<const f32x4*>(p.ks + so);
       r.vsc[h] = *reinterpret_cast<const f32x4*>(p.vs + so);
     }
@@ -861,7 +887,8 @@ struct Cursor {
   int g;            // KV head of the row
   int h0, gt;       // first query head of the row's tile, and its number of heads
   int x;            // row number s * HQ + xi
-  int phys[2];      // table entries of the step at the cursor (prefetched)
+  int phys[4];      // table entries of the step at the cursor (prefetched): one per
+                    // 16-token chunk, two with 8-token blocks
 };
 
 // Row constants of the cursor's row, entered at step j.
@@ -876,9 +903,10 @@ __device__ __forceinline__ void cursor_row(Cursor& c, const SplitParams& p) {
 template <int B, int TS>
 __device__ __forceinline__ void cursor_tables(Cursor& c, const SplitParams& p) {
   const int32_t* row = p.bt + (int64_t)c.s * p.W;
+  constexpr int TB = B < 16 ? B : 16;            // tokens per table entry read
 #pragma unroll
-  for (int h = 0; h < TS / 16; ++h) {
-    int lb = (c.tb + c.j * TS + 16 * h) / B;
+  for (int h = 0; h < TS / TB; ++h) {
+    int lb = (c.tb + c.j * TS + TB * h) / B;
     lb = lb < p.W ? lb : p.W - 1;                  // never index past the table row
     int phys = uniform_load(row + lb);
     c.phys[h] = phys < 0 ? 0 : (phys >= p.num_blocks ? p.num_blocks - 1 : phys);  // stay inside the pool
@@ -1062,6 +1090,7 @@ __device__ __forceinline__ void merge_row(const SplitParams& p, int x, int s, in
       if (hr < gt) {
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
+          if (nb + k * hs >= cnt) break;         // no lane group has a slot k this round
           ml[k] = ld_agent(p.part_ml + ((int64_t)slot[k] * 16 + hr) * 2);
           const uint32_t base = (uint32_t)slot[k] * (NC * 1024u) + src;
 #pragma unroll
@@ -1069,7 +1098,7 @@ __device__ __forceinline__ void merge_row(const SplitParams& p, int x, int s, in
         }
 #pragma unroll
         for (int k = 0; k < KS; ++k)
-          if (live[k]) merge_into<NC>(M, L, A, ml[k][0], ml[k][1], av[k]);
+          if (nb + k * hs < cnt && live[k]) merge_into<NC>(M, L, A, ml[k][0], ml[k][1], av[k]);
       }
     }
     // the next 64 waves, if the last one tested starts inside the row
@@ -1377,27 +1406,38 @@ __global__ __launch_bounds__(256) void fold_q_kernel(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------- launches
-template <int D, int KVT, int B>
-hipError_t launch_single(const DecodeParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((pa_decode_kernel<D, KVT, B>), dim3(grid), dim3(kWave * kNW), 0, stream, p);
-  return hipGetLastError();
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// f(IC<D>, IC<KVT>, IC<B>) for the kernel variant of head dim D (64, 128),
+// storage kv_dtype and block size B (8, 16, 32).  INT8 with per-tensor or
+// per-channel scales runs the per-tensor codes kernel (the channel scales are
+// folded into q and into the output).
+template <class F>
+auto with_variant(int D, int kvt, int B, F&& f) {
+  auto by_b = [&](auto dc, auto kc) {
+    if (B == 8) return f(dc, kc, IC<8>{});
+    if (B == 16) return f(dc, kc, IC<16>{});
+    return f(dc, kc, IC<32>{});
+  };
+  auto by_kv = [&](auto dc) {
+    switch (kvt) {
+      case PKV_KV_BF16: return by_b(dc, IC<PKV_KV_BF16>{});
+      case PKV_KV_FP8_E5M2: return by_b(dc, IC<PKV_KV_FP8_E5M2>{});
+      case PKV_KV_INT8_TENSOR:
+      case PKV_KV_INT8_CHANNEL: return by_b(dc, IC<PKV_KV_INT8_TENSOR>{});
+      default: return by_b(dc, IC<PKV_KV_INT8>{});
+    }
+  };
+  return D == 64 ? by_kv(IC<64>{}) : by_kv(IC<128>{});
 }
 
-template <int D>
-hipError_t launch_single_kv(const DecodeParams& p, int kvt, int B, int grid, hipStream_t stream) {
-  switch (kvt) {
-    case PKV_KV_BF16:
-      return B == 16 ? launch_single<D, PKV_KV_BF16, 16>(p, grid, stream) : launch_single<D, PKV_KV_BF16, 32>(p, grid, stream);
-    case PKV_KV_FP8_E5M2:
-      return B == 16 ? launch_single<D, PKV_KV_FP8_E5M2, 16>(p, grid, stream)
-                     : launch_single<D, PKV_KV_FP8_E5M2, 32>(p, grid, stream);
-    case PKV_KV_INT8_TENSOR:
-    case PKV_KV_INT8_CHANNEL:   // folded q, per-dim output scale: the same codes kernel
-      return B == 16 ? launch_single<D, PKV_KV_INT8_TENSOR, 16>(p, grid, stream)
-                     : launch_single<D, PKV_KV_INT8_TENSOR, 32>(p, grid, stream);
-    default:
-      return B == 16 ? launch_single<D, PKV_KV_INT8, 16>(p, grid, stream) : launch_single<D, PKV_KV_INT8, 32>(p, grid, stream);
-  }
+hipError_t launch_single(const DecodeParams& p, int D, int kvt, int B, int grid, hipStream_t stream) {
+  return with_variant(D, kvt, B, [&](auto dc, auto kc, auto bc) {
+    hipLaunchKernelGGL((pa_decode_kernel<decltype(dc)::value, decltype(kc)::value, decltype(bc)::value>), dim3(grid),
+                       dim3(kWave * kNW), 0, stream, p);
+    return hipGetLastError();
+  });
 }
 
 // Steps of K/V registers per wave: one computed, the rest in flight (about
@@ -1406,24 +1446,11 @@ template <int D, int KVT>
 constexpr int split_nbuf() { return D == 64 ? 8 : 5; }
 constexpr int kMaxBlocksPerCU = 1;       // persistent grid: one workgroup (a wave per SIMD) per CU
 
-template <int D, int KVT, int B>
-const void* split_fn() {
-  return reinterpret_cast<const void*>(&pa_split_kernel<D, KVT, B, split_nbuf<D, KVT>()>);
-}
-
 const void* split_kernel_fn(int D, int kvt, int B) {
-  if (D == 64) {
-    if (kvt == PKV_KV_BF16) return B == 16 ? split_fn<64, PKV_KV_BF16, 16>() : split_fn<64, PKV_KV_BF16, 32>();
-    if (kvt == PKV_KV_FP8_E5M2) return B == 16 ? split_fn<64, PKV_KV_FP8_E5M2, 16>() : split_fn<64, PKV_KV_FP8_E5M2, 32>();
-    if (kvt == PKV_KV_INT8_TENSOR || kvt == PKV_KV_INT8_CHANNEL)
-      return B == 16 ? split_fn<64, PKV_KV_INT8_TENSOR, 16>() : split_fn<64, PKV_KV_INT8_TENSOR, 32>();
-    return B == 16 ? split_fn<64, PKV_KV_INT8, 16>() : split_fn<64, PKV_KV_INT8, 32>();
-  }
-  if (kvt == PKV_KV_BF16) return B == 16 ? split_fn<128, PKV_KV_BF16, 16>() : split_fn<128, PKV_KV_BF16, 32>();
-  if (kvt == PKV_KV_FP8_E5M2) return B == 16 ? split_fn<128, PKV_KV_FP8_E5M2, 16>() : split_fn<128, PKV_KV_FP8_E5M2, 32>();
-  if (kvt == PKV_KV_INT8_TENSOR || kvt == PKV_KV_INT8_CHANNEL)
-    return B == 16 ? split_fn<128, PKV_KV_INT8_TENSOR, 16>() : split_fn<128, PKV_KV_INT8_TENSOR, 32>();
-  return B == 16 ? split_fn<128, PKV_KV_INT8, 16>() : split_fn<128, PKV_KV_INT8, 32>();
+  return with_variant(D, kvt, B, [](auto dc, auto kc, auto bc) {
+    constexpr int Dv = decltype(dc)::value, Kv = decltype(kc)::value, Bv = decltype(bc)::value;
+    return reinterpret_cast<const void*>(&pa_split_kernel<Dv, Kv, Bv, split_nbuf<Dv, Kv>()>);
+  });
 }
 
 // Compute units of the current device (cached per device).
@@ -1445,10 +1472,10 @@ int device_cus(int* cus) {
 // Resident workgroups per CU of one split-kernel variant (cached).
 int split_blocks_per_cu(int D, int kvt, int B) {
   static std::mutex mu;
-  static int cache[64][2][5][2] = {};
+  static int cache[64][2][5][3] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
-  const int di = D == 64 ? 0 : 1, bi = B == 16 ? 0 : 1;
+  const int di = D == 64 ? 0 : 1, bi = B == 8 ? 0 : (B == 16 ? 1 : 2);
   std::lock_guard<std::mutex> lk(mu);
   int& c = cache[dev][di][kvt][bi];
   if (c == 0) {
@@ -1501,32 +1528,13 @@ bool split_sizes(int32_t S, int32_t Hq, int32_t Hkv_or_0, int32_t D, int32_t W, 
   return true;
 }
 
-template <int D, int KVT, int B>
-void launch_split_t(const SplitParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((pa_split_kernel<D, KVT, B, split_nbuf<D, KVT>()>), dim3(grid), dim3(kWave * kNW), 0, stream, p);
-}
-
-template <int D>
-void launch_split_kv(const SplitParams& p, int kvt, int B, int grid, hipStream_t stream) {
-  switch (kvt) {
-    case PKV_KV_BF16:
-      if (B == 16) launch_split_t<D, PKV_KV_BF16, 16>(p, grid, stream);
-      else launch_split_t<D, PKV_KV_BF16, 32>(p, grid, stream);
-      break;
-    case PKV_KV_FP8_E5M2:
-      if (B == 16) launch_split_t<D, PKV_KV_FP8_E5M2, 16>(p, grid, stream);
-      else launch_split_t<D, PKV_KV_FP8_E5M2, 32>(p, grid, stream);
-      break;
-    case PKV_KV_INT8_TENSOR:
-    case PKV_KV_INT8_CHANNEL:
-      if (B == 16) launch_split_t<D, PKV_KV_INT8_TENSOR, 16>(p, grid, stream);
-      else launch_split_t<D, PKV_KV_INT8_TENSOR, 32>(p, grid, stream);
-      break;
-    default:
-      if (B == 16) launch_split_t<D, PKV_KV_INT8, 16>(p, grid, stream);
-      else launch_split_t<D, PKV_KV_INT8, 32>(p, grid, stream);
-      break;
-  }
+void launch_split(const SplitParams& p, int D, int kvt, int B, int grid, hipStream_t stream) {
+  with_variant(D, kvt, B, [&](auto dc, auto kc, auto bc) {
+    constexpr int Dv = decltype(dc)::value, Kv = decltype(kc)::value, Bv = decltype(bc)::value;
+    hipLaunchKernelGGL((pa_split_kernel<Dv, Kv, Bv, split_nbuf<Dv, Kv>()>), dim3(grid), dim3(kWave * kNW), 0, stream,
+                       p);
+    return 0;
+  });
 }
 
 }  // namespace
@@ -1584,8 +1592,8 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     set_error("head_dim %d not built (64, 128)", c.head_dim);
     return PKV_ERR_UNSUPPORTED;
   }
-  if (c.block_size != 16 && c.block_size != 32) {
-    set_error("block_size %d not built (16, 32)", c.block_size);
+  if (c.block_size != 8 && c.block_size != 16 && c.block_size != 32) {
+    set_error("block_size %d not built (8, 16, 32)", c.block_size);
     return PKV_ERR_UNSUPPORTED;
   }
   if (((uintptr_t)q) % 16 || ((uintptr_t)out) % 16) return fail(PKV_ERR_INVALID, "q and out must be 16-byte aligned");
@@ -1648,8 +1656,7 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     p.win = sliding_window;
     p.qk_scale = scale * kLog2e * ksc;
     p.out_scale = vsc;
-    e = c.head_dim == 64 ? launch_single_kv<64>(p, c.kv_dtype, c.block_size, (int)grid, stream)
-                         : launch_single_kv<128>(p, c.kv_dtype, c.block_size, (int)grid, stream);
+    e = launch_single(p, c.head_dim, c.kv_dtype, c.block_size, (int)grid, stream);
   } else {
     if (partition_size < 0 || partition_size % 32 != 0) {
       set_error("partition_size %d must be 0 or a positive multiple of 32", partition_size);
@@ -1710,8 +1717,7 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     p.epoch = next_epoch();
     p.qk_scale = scale * kLog2e * ksc;
     p.out_scale = vsc;
-    if (c.head_dim == 64) launch_split_kv<64>(p, c.kv_dtype, c.block_size, (int)grid, stream);
-    else launch_split_kv<128>(p, c.kv_dtype, c.block_size, (int)grid, stream);
+    launch_split(p, c.head_dim, c.kv_dtype, c.block_size, (int)grid, stream);
     e = hipGetLastError();
   }
   if (e != hipSuccess) {

@@ -34,7 +34,7 @@ def _special_values(D):
 
 
 @pytest.mark.parametrize("dt", [pkv.PKV_KV_BF16, pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8])
-@pytest.mark.parametrize("B,D", [(16, 64), (16, 128), (32, 128), (32, 64)])
+@pytest.mark.parametrize("B,D", [(16, 64), (16, 128), (32, 128), (32, 64), (8, 128), (8, 64)])
 @pytest.mark.parametrize("kscale", [1.0, 0.37])
 def test_reshape_and_cache_bit_exact(dt, B, D, kscale):
     if dt != pkv.PKV_KV_FP8_E5M2 and kscale != 1.0:

@@ -165,7 +165,7 @@ CTX_EDGE = [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 255, 256, 257]
 
 
 @pytest.mark.parametrize("dt", [pkv.PKV_KV_BF16, pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8])
-@pytest.mark.parametrize("D,B", [(64, 16), (128, 16), (128, 32), (64, 32)])
+@pytest.mark.parametrize("D,B", [(64, 16), (128, 16), (128, 32), (64, 32), (128, 8), (64, 8)])
 @pytest.mark.parametrize("P", [0, 32, 96, 512])
 def test_random_shapes(dt, D, B, P):
     idx = (dt * 7 + D + B + P) % 6
@@ -189,13 +189,17 @@ def test_group_sizes(G, hkv):
 
 
 @pytest.mark.parametrize("dt", [pkv.PKV_KV_BF16, pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8])
-def test_poisoned_pool_tail_does_not_leak(dt):
+@pytest.mark.parametrize("B", [32, 8])
+def test_poisoned_pool_tail_does_not_leak(dt, B):
     # unwritten slots hold NaN patterns; masked tokens must not reach the output
-    say(f"poisoned pool dt={dt}")
-    rng = np.random.default_rng(4000 + dt)
-    c = build_case(rng, 6, 2, 4, 128, 32, dt, [1, 5, 17, 31, 33, 100], poison=True)
+    # (with 8-token blocks a 16-token chunk can end in a block the table never
+    # allocated)
+    say(f"poisoned pool dt={dt} B={B}")
+    rng = np.random.default_rng(4000 + dt + B)
+    ctx = [1, 5, 17, 31, 33, 100, 8, 9, 24]
+    c = build_case(rng, len(ctx), 2, 4, 128, B, dt, ctx, poison=True)
     for P in (0, 32, 64):
-        check(c, P, f"poisoned dt={dt} P={P}")
+        check(c, P, f"poisoned dt={dt} B={B} P={P}")
 
 
 @pytest.mark.parametrize("dt", [pkv.PKV_KV_BF16, pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8])
@@ -349,7 +353,7 @@ def _append_and_compare(rng, ctx, hkv, G, D, B, dt, P, label):
 
 
 @pytest.mark.parametrize("dt", [pkv.PKV_KV_BF16, pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8])
-@pytest.mark.parametrize("D,B,P", [(128, 16, 64), (128, 32, 512), (64, 16, 32), (64, 32, 4096)])
+@pytest.mark.parametrize("D,B,P", [(128, 16, 64), (128, 32, 512), (64, 16, 32), (64, 32, 4096), (128, 8, 64), (64, 8, 32)])
 def test_decode_append_equals_cache_write_then_decode(dt, D, B, P):
     rng = np.random.default_rng(8100 + 10 * dt + D + B)
     hkv, G = (2, 4) if D == 128 else (1, 3)

@@ -87,7 +87,7 @@ def test_cache_write_is_bit_exact(dt, D, B):
 
 
 @pytest.mark.parametrize("dt", [pkv.PKV_KV_INT8_TENSOR, pkv.PKV_KV_INT8_CHANNEL])
-@pytest.mark.parametrize("D,B", [(128, 16), (64, 32), (128, 32)])
+@pytest.mark.parametrize("D,B", [(128, 16), (64, 32), (128, 32), (128, 8)])
 @pytest.mark.parametrize("P", [0, 32, 512])
 def test_decode_matches_oracle(dt, D, B, P):
     say(f"int8 scales dt={dt} D={D} B={B} P={P}")

@@ -55,7 +55,7 @@ def _run_ex(c, P, window, key=None, value=None):
 
 
 @pytest.mark.parametrize("dt", [pkv.PKV_KV_BF16, pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8])
-@pytest.mark.parametrize("D,B", [(128, 16), (64, 32), (128, 32)])
+@pytest.mark.parametrize("D,B", [(128, 16), (64, 32), (128, 32), (128, 8)])
 @pytest.mark.parametrize("P", [0, 32, 512])
 def test_window_matches_oracle(dt, D, B, P):
     rng = np.random.default_rng(9100 + 7 * dt + D + B + P)

@@ -104,17 +104,20 @@ def llama8b(seed_offset: int = 0) -> Workload:
     return w
 
 
-def llama70b(num_layers: int = 80, extra_steps: int = 64) -> Workload:
-    """extra_steps: tokens each sequence may still append (bench growth)."""
+def llama70b(num_layers: int = 80, extra_steps: int = 64, block_size: int = 16) -> Workload:
+    """extra_steps: tokens each sequence may still append (bench growth).
+    block_size: tokens per block (16 by default; 8 and 32 are the other sizes
+    the pages' engine offers)."""
     ss = np.random.SeedSequence(436000 + 3)
     r0 = np.random.default_rng(ss.spawn(1)[0])
     S = 100
+    B = block_size
     ctx = np.clip(np.rint(r0.normal(4096.0, 256.0, size=S)), 3072, 5120).astype(np.int32)
-    need = int(sum(math.ceil(c / 16) for c in ctx))
-    grow = S * math.ceil(extra_steps / 16 + 1)
+    need = int(sum(math.ceil(c / B) for c in ctx))
+    grow = S * math.ceil(extra_steps / B + 1)
     nb = math.ceil(1.02 * need) + grow
-    W = math.ceil((5120 + extra_steps) / 16)
-    w = Workload("llama70b", 3, S, 64, 8, 128, 16, num_layers, KV_BF16, ctx, nb,
+    W = math.ceil((5120 + extra_steps) / B)
+    w = Workload("llama70b", 3, S, 64, 8, 128, B, num_layers, KV_BF16, ctx, nb,
                  np.zeros(nb, np.int32), W, partition_size=512)
     r = w.streams()
     w.block_order = r[1].permutation(nb).astype(np.int32)
