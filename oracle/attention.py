@@ -34,8 +34,8 @@ from __future__ import annotations
 import numpy as np
 
 from . import codecs
-from .layout import (KV_BF16, KV_FP8_E5M2, KV_INT8, KV_INT8_CHANNEL, KV_INT8_TENSOR, PoolImage,
-                     channel_scale_offset, k_offset,
+from .layout import (KV_BF16, KV_FP8_E5M2, KV_INT4, KV_INT8, KV_INT8_CHANNEL, KV_INT8_TENSOR, PoolImage,
+                     channel_scale_offset, int4_k_nibble, int4_v_nibble, k_offset, read_nibbles,
                      scale_offset, v_offset)
 from .layout import k_tiles_as_tokens as layout_k_tokens
 from .layout import scales_as_tokens as layout_scale_tokens
@@ -88,7 +88,10 @@ def _dequant_fixed_scales(p, img, layer, kraw, vraw, k_scale, v_scale):
         ks = np.float64(np.float32(k_scale))
         vs = np.float64(np.float32(v_scale))
         return kraw.astype(np.float64) * ks, vraw.astype(np.float64) * vs
-    if p.kv_dtype == KV_INT8_CHANNEL:
+    if p.kv_dtype == KV_INT4:                # stored nibble = code + 8
+        kraw = kraw.astype(np.int64) - 8
+        vraw = vraw.astype(np.int64) - 8
+    if p.kv_dtype in (KV_INT8_CHANNEL, KV_INT4):
         co = channel_scale_offset(p, layer, np.arange(p.num_kv_heads)[:, None], np.arange(p.head_dim)[None, :])
         ks = img.k_scale[co].astype(np.float64)[None]      # [1, Hkv, D]
         vs = img.v_scale[co].astype(np.float64)[None]
@@ -111,6 +114,12 @@ def gather_kv_by_slot(img: PoolImage, layer: int, block_table_row: np.ndarray,
     t = (slots % p.block_size)[:, None, None]
     h = np.arange(p.num_kv_heads)[None, :, None]
     d = np.arange(p.head_dim)[None, None, :]
+    if p.kv_dtype == KV_INT4:
+        kc = read_nibbles(img.k, int4_k_nibble(p, layer, blk, h, t, d)) - 8
+        vc = read_nibbles(img.v, int4_v_nibble(p, layer, blk, h, t, d)) - 8
+        co = channel_scale_offset(p, layer, h + 0 * t, d + 0 * t)
+        return (kc.astype(np.float64) * img.k_scale[co].astype(np.float64),
+                vc.astype(np.float64) * img.v_scale[co].astype(np.float64))
     kraw = img.k[k_offset(p, layer, blk, h, t, d)]
     vraw = img.v[v_offset(p, layer, blk, h, t, d)]
     if p.kv_dtype == KV_BF16:

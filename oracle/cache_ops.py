@@ -19,9 +19,9 @@ from __future__ import annotations
 import numpy as np
 
 from . import codecs
-from .layout import (KV_BF16, KV_FP8_E5M2, KV_INT8, KV_INT8_CHANNEL, KV_INT8_TENSOR, PoolImage,
-                     channel_scale_offset, k_offset,
-                     scale_offset, tile_base, v_offset)
+from .layout import (KV_BF16, KV_FP8_E5M2, KV_INT4, KV_INT8, KV_INT8_CHANNEL, KV_INT8_TENSOR, PoolImage,
+                     channel_scale_offset, int4_k_nibble, int4_v_nibble, k_offset,
+                     scale_offset, tile_base, v_offset, write_nibbles)
 
 
 def reshape_and_cache(img: PoolImage, layer: int, key_bits: np.ndarray,
@@ -49,10 +49,18 @@ def reshape_and_cache(img: PoolImage, layer: int, key_bits: np.ndarray,
     t3 = t[:, None, None]
     h3 = np.arange(hkv)[None, :, None]
     d3 = np.arange(d)[None, None, :]
-    ko = k_offset(p, layer, blk3, h3, t3, d3)
-    vo = v_offset(p, layer, blk3, h3, t3, d3)
     kx = key_bits[keep]
     vx = value_bits[keep]
+    if p.kv_dtype == KV_INT4:
+        # the layer's calibrated channel scales, [1, Hkv, D]; stored nibble = code + 8
+        co = channel_scale_offset(p, layer, h3, d3)
+        kc = codecs.int4_encode(codecs.bf16_bits_to_f32(kx), img.k_scale[co]).astype(np.int64) + 8
+        vc = codecs.int4_encode(codecs.bf16_bits_to_f32(vx), img.v_scale[co]).astype(np.int64) + 8
+        write_nibbles(out.k, int4_k_nibble(p, layer, blk3, h3, t3, d3), kc)
+        write_nibbles(out.v, int4_v_nibble(p, layer, blk3, h3, t3, d3), vc)
+        return out
+    ko = k_offset(p, layer, blk3, h3, t3, d3)
+    vo = v_offset(p, layer, blk3, h3, t3, d3)
 
     if p.kv_dtype == KV_BF16:
         out.k[ko] = kx
@@ -92,7 +100,7 @@ def copy_blocks(img: PoolImage, pairs: np.ndarray, inplace: bool = False) -> Poo
         src_img = _snapshot_blocks(img, np.unique(pairs_[:, 0]))
     out = img if inplace else img.copy()
     pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
-    te = p.tile_elems
+    te = p.tile_units
     for layer in range(p.num_layers):
         for src, dst in pairs:
             for h in range(p.num_kv_heads):
@@ -119,7 +127,7 @@ def swap_blocks(src_img: PoolImage, dst_img: PoolImage, pairs: np.ndarray) -> Po
     assert (ps.num_layers, ps.block_size, ps.num_kv_heads, ps.head_dim, ps.kv_dtype) == \
         (pd.num_layers, pd.block_size, pd.num_kv_heads, pd.head_dim, pd.kv_dtype)
     out = dst_img.copy()
-    te = ps.tile_elems
+    te = ps.tile_units
     for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
         if not (0 <= src < ps.num_blocks and 0 <= dst < pd.num_blocks):
             continue
@@ -144,7 +152,7 @@ def _snapshot_blocks(img: PoolImage, blocks: np.ndarray) -> PoolImage:
     snap = PoolImage(p, np.empty_like(img.k), np.empty_like(img.v),
                      None if img.k_scale is None else np.empty_like(img.k_scale),
                      None if img.v_scale is None else np.empty_like(img.v_scale))
-    te = p.tile_elems
+    te = p.tile_units
     for layer in range(p.num_layers):
         for b in blocks:
             for h in range(p.num_kv_heads):

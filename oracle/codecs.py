@@ -134,6 +134,21 @@ def int8_encode(x_f32: np.ndarray, scale) -> np.ndarray:
     return code.astype(np.int8)
 
 
+def int4_encode(x_f32: np.ndarray, scale) -> np.ndarray:
+    """INT4 codes under a given (calibrated) scale: clamp(rint_even(fp32(x /
+    scale)), -7, 7), and 0 where the scale is 0.  The pages list INT4 KV as
+    the more aggressive step after INT8 that needs calibration and stores a
+    quarter of FP16's bytes ("KV Cache 原理与 PagedAttention", §四); this
+    library reads that as the INT8 per-channel scheme with symmetric 4-bit
+    codes (calibrated channel scales keep the size at a quarter)."""
+    x = np.asarray(x_f32, dtype=np.float32)
+    s = np.broadcast_to(np.asarray(scale, dtype=np.float32), x.shape)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    q = (x / safe).astype(np.float32)                       # fp32 division
+    code = np.where(s > 0, np.clip(np.rint(q), -7, 7), 0)
+    return code.astype(np.int8)
+
+
 def int8_dequant(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """code * scale in float64 (scales broadcast over the last axis)."""
     return (np.asarray(codes, dtype=np.int8).astype(np.float64)

@@ -79,3 +79,21 @@ def test_reversed_channel_scales_are_caught(monkeypatch):
         return (np.asarray(layer, dtype=np.int64) * p.num_kv_heads + head) * p.head_dim + (p.head_dim - 1 - d)
     monkeypatch.setattr(att, "channel_scale_offset", bad)
     assert _fails(lambda: ti.test_cache_write_then_gathers_read_code_times_scale(layout.KV_INT8_CHANNEL))
+
+
+def test_swapped_int4_nibble_halves_are_caught(monkeypatch):
+    from tests import test_oracle_int4 as t4
+    real = layout.int4_v_nibble
+
+    def bad(p, layer, block, head, t, d):
+        return real(p, layer, block, head, t, d) ^ 1      # low and high nibble of each byte swapped
+    monkeypatch.setattr(layout, "int4_v_nibble", bad)
+    assert _fails(lambda: t4.test_each_v_byte_holds_one_token_and_each_k_word_one_mfma_slot(16, 128)) or \
+        _fails(lambda: t4.test_tile_unpack_equals_element_reads(16, 128))
+
+
+def test_int4_offset_of_seven_is_caught(monkeypatch):
+    from tests import test_oracle_int4 as t4
+    real = codecs.int4_encode
+    monkeypatch.setattr(codecs, "int4_encode", lambda x, s: np.clip(real(x, s), -7, 6).astype(np.int8))
+    assert _fails(t4.test_bound_saturation_and_zero_scale)
