@@ -37,7 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0    # MI355X HBM3E, AMD's published peak
-KV_DTYPES = {"bf16": 0, "fp8": 1, "int8": 2, "int8_tensor": 3, "int8_channel": 4}
+KV_DTYPES = {"bf16": 0, "fp8": 1, "int8": 2, "int8_tensor": 3, "int8_channel": 4, "int4": 5}
 TENSOR_SCALE = 0.035     # per-tensor K and V scale of the 8-bit runs (fp8 and int8_tensor)
 
 
@@ -324,9 +324,9 @@ def main():
     for s in range(S):
         bm.add_seq(s, int(w.context_lens[s]) - 1)      # history; each step appends one token
     kvt = KV_DTYPES[args.kv_dtype]
-    e = 2 if kvt == pkv.PKV_KV_BF16 else 1
+    e = 2 if kvt == pkv.PKV_KV_BF16 else 1                          # bytes per stored element (INT4: two per byte)
     token_scales = 2 * 4 if kvt == pkv.PKV_KV_INT8 else 0          # int8: fp32 K and V scale per (token, head)
-    tok_bytes = Hkv * (2 * D * e + token_scales)                    # KV bytes per token per layer
+    tok_bytes = Hkv * (2 * D * e // (2 if kvt == pkv.PKV_KV_INT4 else 1) + token_scales)   # KV bytes per token per layer
     ks_t = vs_t = TENSOR_SCALE if kvt in (pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8_TENSOR) else 1.0
     if kvt != pkv.PKV_KV_BF16:
         args.no_cpu_baseline = True

@@ -45,7 +45,20 @@
  *   i.e. groups of 4 consecutive tokens are stored dim by dim, so the
  *   4 tokens x 1 dim operand of the P.V matrix-core step is one 4e-byte
  *   word and 16 consecutive dims are one contiguous run.
- *   A slot is block * B + t.  Requirements: D in {64, 128}; B in {16, 32}.
+ *   INT4 (two codes per byte, stored as code + 8; a tile is B*D/2 bytes)
+ *   has its own placement, in 4-bit nibbles from the tile start, with
+ *   P = D / 8 bytes per piece and nibble n of a 32-bit little-endian word
+ *   at bits 4n .. 4n+3:
+ *     K (t, d):  2 * ((j * B + t) * P + 4 * kk) + n
+ *                kk = d / 32, j = (d % 32) / 8, i = d % 8,
+ *                n = 4 * (i % 2) + i / 2
+ *     V (t, d):  2 * ((g * 16 + m) * P + 4 * (c / 2)) + n
+ *                g = t / 4, r = t % 4, c = d / 16, m = d % 16,
+ *                n = 4 * (r % 2) + 2 * (r / 2) + c % 2
+ *   so that one word widens to the bf16 pairs a matrix-core operand takes
+ *   with a mask and an OR, and every V byte belongs to one token.
+ *   A slot is block * B + t.  Requirements: D in {64, 128}; B in {8, 16,
+ *   32}.
  *
  * Query, output: q is bf16 [S][Hq][D], out is fp32 [S][Hq][D], both dense.
  * Block tables: int32 [S][W], row-major; entry i of row s is the physical
@@ -81,10 +94,15 @@ typedef enum {
                               of K and one for V, passed with each call like
                               the fp8 scales ([KVP] §四 INT8 per-tensor;
                               [BJD] §5.2 per-tensor)                        */
-  PKV_KV_INT8_CHANNEL = 4  /* int8 codes, one calibrated fp32 scale per
+  PKV_KV_INT8_CHANNEL = 4, /* int8 codes, one calibrated fp32 scale per
                               (layer, KV head, dim) for K and for V, kept in
                               the pool's scale regions, which the caller
                               fills ([KVP] §四 per-channel; [BJD] §5.2)     */
+  PKV_KV_INT4 = 5          /* symmetric 4-bit codes clamp(round(x / s), -7,
+                              7) under calibrated per-(layer, KV head, dim)
+                              scales kept as for PKV_KV_INT8_CHANNEL: a
+                              quarter of bf16's bytes ([KVP] §四 INT4 KV,
+                              which needs calibration)                      */
 } pkv_kv_dtype;
 
 typedef struct {
@@ -99,7 +117,8 @@ typedef struct {
 /* Filled by kv_pool_create; plain data, may be copied freely.  Pointers are
  * device addresses inside the caller's buffer.  k_scale / v_scale: for
  * PKV_KV_INT8 the per-(token, head) scales [L][NB][H][B] the cache write
- * fills; for PKV_KV_INT8_CHANNEL the per-channel scales [L][H][D] the caller
+ * fills; for PKV_KV_INT8_CHANNEL and PKV_KV_INT4 the per-channel scales
+ * [L][H][D] the caller
  * writes before caching or decoding a layer (element (l, h, d) at
  * (l * H + h) * D + d); NULL otherwise. */
 typedef struct {
@@ -110,7 +129,7 @@ typedef struct {
   void* v;
   float* k_scale;
   float* v_scale;
-  uint64_t tile_bytes;    /* B * D * e                                       */
+  uint64_t tile_bytes;    /* B * D * e (B * D / 2 for INT4)                  */
   uint64_t layer_bytes;   /* NB * H * tile_bytes: one layer of K (or of V)   */
 } pkv_pool;
 

@@ -73,6 +73,28 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
       kd[((d >> 4) * B + t) * 16 + (d & 15)] = (int8_t)int8_store(kx[d], ks);
       vd[((t >> 2) * D + d) * 4 + (t & 3)] = (int8_t)int8_store(vx[d], vs);
     }
+  } else if constexpr (KVT == PKV_KV_INT4) {
+    // two codes per byte, each byte belonging to one token; lane b < D / 2
+    // writes K byte b and V byte b of the token (nibble placement as the
+    // pool layout documents)
+    uint8_t* kd = static_cast<uint8_t*>(kdst) + tile / 2;
+    uint8_t* vd = static_cast<uint8_t*>(vdst) + tile / 2;
+    const int P = D / 8;                            // bytes per piece
+    const float* ksc = kscale + h * D;
+    const float* vsc = vscale + h * D;
+    if (lane < D / 2) {
+      // K: piece (j, t), byte o = 4 kk + bw; the byte's low / high nibbles are
+      // elements i and i + 2 of dims 32 kk + 8 j + i
+      const int j = lane / P, o = lane % P, kk = o >> 2, bw = o & 3;
+      const int d0 = 32 * kk + 8 * j + int4_k_lo_elem(bw);
+      kd[(j * B + t) * P + o] = (uint8_t)(int4_store(kx[d0], ksc[d0]) | (int4_store(kx[d0 + 2], ksc[d0 + 2]) << 4));
+      // V: piece (t / 4, m), word w, byte 2 (r % 2) + r / 2 (r = t % 4) holds
+      // dims 16 (2w) + m (low) and 16 (2w + 1) + m (high)
+      const int m = lane % 16, w = lane / 16, r = t & 3;
+      const int e0 = 32 * w + m, e1 = e0 + 16;
+      vd[((t >> 2) * 16 + m) * P + 4 * w + 2 * (r & 1) + (r >> 1)] =
+          (uint8_t)(int4_store(vx[e0], vsc[e0]) | (int4_store(vx[e1], vsc[e1]) << 4));
+    }
   } else {  // INT8, symmetric per (token, head)
     int8_t* kd = static_cast<int8_t*>(kdst) + tile;
     int8_t* vd = static_cast<int8_t*>(vdst) + tile;
@@ -220,7 +242,7 @@ extern "C" pkv_status reshape_and_cache(const pkv_pool* pool, int32_t layer, con
   if (grid > INT32_MAX) return fail(PKV_ERR_INVALID, "too many tokens in one call");
   char* kl = static_cast<char*>(pool->k) + (uint64_t)layer * pool->layer_bytes;
   char* vl = static_cast<char*>(pool->v) + (uint64_t)layer * pool->layer_bytes;
-  const uint64_t scale_layer = c.kv_dtype == PKV_KV_INT8_CHANNEL
+  const uint64_t scale_layer = has_channel_scales(c.kv_dtype)
                                   ? (uint64_t)c.num_kv_heads * c.head_dim
                                   : (uint64_t)c.num_blocks * c.num_kv_heads * c.block_size;
   float* ksl = pool->k_scale ? pool->k_scale + layer * scale_layer : nullptr;
@@ -247,6 +269,11 @@ extern "C" pkv_status reshape_and_cache(const pkv_pool* pool, int32_t layer, con
     case PKV_KV_INT8_CHANNEL:
       hipLaunchKernelGGL(reshape_and_cache_kernel<PKV_KV_INT8_CHANNEL>, dim3((uint32_t)grid), dim3(256), 0,
                          stream, kx, vx, slot_mapping, num_tokens, c.num_kv_heads, c.head_dim, c.block_size,
+                         num_slots, kl, vl, ksl, vsl, ksc, vsc);
+      break;
+    case PKV_KV_INT4:
+      hipLaunchKernelGGL(reshape_and_cache_kernel<PKV_KV_INT4>, dim3((uint32_t)grid), dim3(256), 0, stream,
+                         kx, vx, slot_mapping, num_tokens, c.num_kv_heads, c.head_dim, c.block_size,
                          num_slots, kl, vl, ksl, vsl, ksc, vsc);
       break;
     default:

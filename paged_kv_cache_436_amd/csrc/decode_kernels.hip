@@ -176,11 +176,25 @@ __device__ __forceinline__ int q_dim0(int kk, int j) {
   return (E == 2) ? (32 * kk + 8 * j) : (64 * (kk >> 1) + 16 * j + 8 * (kk & 1));
 }
 
-// Output dim of accumulator element i of tile c in lane slot j:
+// Output dim of accumulator element i of tile c in lane slot j, by the
+// accumulator layout AL of the storage type (its bytes per element, 0 for INT4):
 //   bf16: 32u + 8j + 2i + e  (c = 2u + e)   8-bit: 64u + 16j + 4i + e (c = 4u + e)
-template <int E>
+//   INT4: 16c + 4j + i
+template <int AL>
 __device__ __forceinline__ int acc_dim(int c, int j, int i) {
-  return (E == 2) ? (32 * (c >> 1) + 8 * j + 2 * i + (c & 1)) : (64 * (c >> 2) + 16 * j + 4 * i + (c & 3));
+  if constexpr (AL == 0) return 16 * c + 4 * j + i;
+  return (AL == 2) ? (32 * (c >> 1) + 8 * j + 2 * i + (c & 1)) : (64 * (c >> 2) + 16 * j + 4 * i + (c & 3));
+}
+
+// ---- INT4: a stored nibble u = code + 8 becomes the bf16 of 128 + u =
+// 136 + code (exact: bf16 has 8 significant bits) by OR-ing it into the
+// mantissa of 128.0 (0x4300).  Word nibbles are placed so that pair k of a
+// word - bits 4k .. 4k+3 and 16 + 4k .. 16 + 4k + 3 - is one bf16x2.  The
+// kernels subtract the constant 136 after the products: 136 * sum(q) from
+// each logit, 136 * sum(p) from each accumulator.
+constexpr float kInt4Bias = 136.0f;
+__device__ __forceinline__ uint32_t int4_pair(uint32_t w, int k) {
+  return 0x43004300u | ((w >> (4 * k)) & 0x000F000Fu);
 }
 
 // =====================================================================
@@ -534,12 +548,16 @@ struct SplitParams {
 
 template <int D, int KVT>
 struct SplitGeo {
+  static constexpr bool I4 = KVT == PKV_KV_INT4;
   static constexpr int E = KVT == PKV_KV_BF16 ? 2 : 1;
   static constexpr int CH = E == 2 ? 1 : 2;       // 16-token chunks per step
   static constexpr int TS = 16 * CH;              // tokens per step
-  static constexpr int LPC = D * E / 64;          // 16-byte loads per chunk per lane, for K and for V
+  static constexpr int LPC = I4 ? 1 : D * E / 64; // 16-byte loads per chunk per lane, for K and for V
+                                                  // (INT4: one load of D / 8 bytes)
   static constexpr int KK = D / 32;               // q.K MFMAs per chunk
   static constexpr int NC = D / 16;               // accumulator tiles of 16 dims
+  static constexpr int QL = I4 ? 2 : E;           // query dim layout (q_dim0)
+  static constexpr int AL = I4 ? 0 : E;           // accumulator dim layout (acc_dim)
 };
 
 template <int D, int KVT>
@@ -581,6 +599,7 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 template <int KK>
 struct QRegs {
   bf16x8 q[KK];
+  float qs;       // INT4: the row's head's sum of q over all dims (for the 136 offset)
 };
 
 template <int D, int KVT>
@@ -594,7 +613,16 @@ __device__ __forceinline__ QRegs<SplitGeo<D, KVT>::KK> load_q(const SplitParams&
   QRegs<GE::KK> r;
 #pragma unroll
   for (int kk = 0; kk < GE::KK; ++kk)
-    r.q[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + q_dim0<GE::E>(kk, j)));
+    r.q[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + q_dim0<GE::QL>(kk, j)));
+  r.qs = 0.f;
+  if constexpr (GE::I4) {
+    float a = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < GE::KK; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a += (float)r.q[kk][e];
+    r.qs = sum_x32(sum_x16(a));      // lanes of one head row hold its 4 dim slots
+  }
   return r;
 }
 
@@ -629,6 +657,24 @@ __device__ __forceinline__ void issue_chunks(SplitBuf<D, KVT>& r, const SplitPar
     const int tv = toff + ((4 * j) & TM);
     const int64_t tilek = live ? ((int64_t)pk * p.Hkv + g) : 0;
     const int64_t tilev = live ? ((int64_t)pv * p.Hkv + g) : 0;
+    if constexpr (GE::I4) {
+      // K piece (j, token), V piece (token group, dim row): D / 8 bytes each
+      constexpr int P = D / 8;
+      const char* kt = p.k + tilek * (int64_t)(B * D / 2);
+      const char* vt = p.v + tilev * (int64_t)(B * D / 2);
+      const char* ka = kt + (j * B + tk) * P;
+      const char* va = vt + ((tv >> 2) * 16 + row) * P;
+      if constexpr (P == 16) {
+        r.k[h][0] = ld16(ka);
+        r.v[h][0] = ld16(va);
+      } else {
+        const u32x2 k2 = *reinterpret_cast<const u32x2*>(ka);
+        const u32x2 v2 = *reinterpret_cast<const u32x2*>(va);
+        r.k[h][0] = u32x4{k2[0], k2[1], 0u, 0u};
+        r.v[h][0] = u32x4{v2[0], v2[1], 0u, 0u};
+      }
+      continue;
+    }
     const char* kt = p.k + tilek * (int64_t)(B * D * E);
     const char* vt = p.v + tilev * (int64_t)(B * D * E);
 #pragma unroll
@@ -667,7 +713,7 @@ __device__ __forceinline__ uint32_t half_of(uint32_t w, int i) { return i ? (w >
 __device__ __forceinline__ float abs_bf16(uint32_t b) { return fabsf(bf16_bits_to_float(b & 0xffffu)); }
 
 template <int D, int KVT, int B>
-__device__ __forceinline__ void append_token(const SplitParams& p, int s, int g, int ctx, int lane) {
+__device__ __forceinline__ void append_token_bytes(const SplitParams& p, int s, int g, int ctx, int lane) {
   constexpr int E = KVT == PKV_KV_BF16 ? 2 : 1;
   constexpr int X = 16 / E;    // dims per 16-byte K piece
   constexpr int NPC = D / X;   // K pieces per token (<= 16): lane pc < NPC stores piece pc
@@ -750,6 +796,38 @@ __device__ __forceinline__ void append_token(const SplitParams& p, int s, int g,
   }
 }
 
+template <int D, int KVT, int B>
+__device__ __forceinline__ void append_token(const SplitParams& p, int s, int g, int ctx, int lane) {
+  if constexpr (KVT == PKV_KV_INT4) {
+    // as the INT4 cache write: lane b < D / 2 stores K byte b and V byte b of
+    // the token, each byte holding two of its codes (+ 8)
+    const int pos = ctx - 1;
+    int phys = uniform_load(p.bt + (int64_t)s * p.W + pos / B);
+    phys = phys < 0 ? 0 : (phys >= p.num_blocks ? p.num_blocks - 1 : phys);
+    const int t = pos % B;
+    const int64_t tile = (int64_t)phys * p.Hkv + g;
+    uint8_t* kt = reinterpret_cast<uint8_t*>(p.k) + tile * (int64_t)(B * D / 2);
+    uint8_t* vt = reinterpret_cast<uint8_t*>(p.v) + tile * (int64_t)(B * D / 2);
+    const uint16_t* kx = p.new_k + ((int64_t)s * p.Hkv + g) * D;
+    const uint16_t* vx = p.new_v + ((int64_t)s * p.Hkv + g) * D;
+    const float* ksc = p.ks_ch + g * D;
+    const float* vsc = p.vs_ch + g * D;
+    constexpr int P = D / 8;
+    if (lane < D / 2) {
+      const int j = lane / P, o = lane % P, kk = o >> 2, bw = o & 3;
+      const int d0 = 32 * kk + 8 * j + int4_k_lo_elem(bw);
+      kt[(j * B + t) * P + o] = (uint8_t)(int4_store(kx[d0], ksc[d0]) | (int4_store(kx[d0 + 2], ksc[d0 + 2]) << 4));
+      const int m = lane % 16, w = lane / 16, r = t & 3;
+      const int e0 = 32 * w + m, e1 = e0 + 16;
+      vt[((t >> 2) * 16 + m) * P + 4 * w + 2 * (r & 1) + (r >> 1)] =
+          (uint8_t)(int4_store(vx[e0], vsc[e0]) | (int4_store(vx[e1], vsc[e1]) << 4));
+    }
+    return;
+  } else {
+    append_token_bytes<D, KVT, B>(p, s, g, ctx, lane);
+  }
+}
+
 // Rescale threshold of the streaming softmax, in log2 units: the reference
 // max m_run is only raised when a logit exceeds it by more than this, so p
 // stays below 2^8 and the accumulator is rescaled a handful of times per
@@ -773,7 +851,10 @@ __device__ __forceinline__ void compute_step(const SplitBuf<D, KVT>& r, const QR
 #pragma unroll
     for (int kk = 0; kk < GE::KK; ++kk) {
       bf16x8 a;
-      if constexpr (E == 2) {
+      if constexpr (GE::I4) {
+        const uint32_t wk = r.k[h][0][kk];          // word kk: dims 32 kk + 8 j .. + 7
+        a = __builtin_bit_cast(bf16x8, u32x4{int4_pair(wk, 0), int4_pair(wk, 1), int4_pair(wk, 2), int4_pair(wk, 3)});
+      } else if constexpr (E == 2) {
         a = __builtin_bit_cast(bf16x8, r.k[h][kk]);
       } else {
         const u32x4 wv = r.k[h][kk >> 1];
@@ -781,6 +862,7 @@ __device__ __forceinline__ void compute_step(const SplitBuf<D, KVT>& r, const QR
       }
       c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop.q[kk], c, 0, 0, 0);
     }
+    if constexpr (GE::I4) c -= kInt4Bias * qop.qs;  // the K operand held 136 + code
     z[h] = c;
   }
   float mloc = -INFINITY;
@@ -826,10 +908,36 @@ __device__ __forceinline__ void compute_step(const SplitBuf<D, KVT>& r, const QR
     pl[h][0] = pack_bf16x2(pv[0] - bf16_lo(ph[h][0]), pv[1] - bf16_hi(ph[h][0]));
     pl[h][1] = pack_bf16x2(pv[2] - bf16_lo(ph[h][1]), pv[3] - bf16_hi(ph[h][1]));
   }
+  if constexpr (GE::I4) {
+    // the sum the 136 offset of V is taken back with: that of the p the
+    // products use (hi + lo parts), which is also the softmax denominator
+    psum = 0.f;
+#pragma unroll
+    for (int h = 0; h < CH; ++h)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        psum += (bf16_lo(ph[h][e]) + bf16_lo(pl[h][e])) + (bf16_hi(ph[h][e]) + bf16_hi(pl[h][e]));
+  }
   l_run = l_run * alpha + psum;
   // V of tokens outside [t_lo, t_end) is zeroed so that unwritten slots and
   // blocks before a window (any bit pattern) cannot reach the accumulator
   // through 0 * NaN (wave-uniform branch)
+  if constexpr (GE::I4) {
+    // codes are always finite, and tokens outside [t_lo, t_end) have p = 0
+    const bf16x8 pop = __builtin_bit_cast(bf16x8, u32x4{ph[0][0], ph[0][1], ph[1][0], ph[1][1]});
+    const bf16x8 pop_lo = __builtin_bit_cast(bf16x8, u32x4{pl[0][0], pl[0][1], pl[1][0], pl[1][1]});
+#pragma unroll
+    for (int c = 0; c < GE::NC; ++c) {
+      // word c / 2 of the V piece: pairs (c % 2) and 2 + (c % 2) are tokens
+      // 0, 1 and 2, 3 of the group, dim 16 c + row
+      const uint32_t w0 = r.v[0][0][c >> 1], w1 = r.v[1][0][c >> 1];
+      const bf16x8 aop = __builtin_bit_cast(
+          bf16x8, u32x4{int4_pair(w0, c & 1), int4_pair(w0, 2 + (c & 1)), int4_pair(w1, c & 1), int4_pair(w1, 2 + (c & 1))});
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, pop, acc[c], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, pop_lo, acc[c], 0, 0, 0);
+    }
+    return;
+  }
   u32x4 v[CH][GE::LPC];
 #pragma unroll
   for (int h = 0; h < CH; ++h)
@@ -1038,7 +1146,7 @@ __device__ __forceinline__ void merge_into(float& M, float& L, f32x4 (&A)[NC], f
   M = Mn;
 }
 
-template <int D, int E>
+template <int D, int AL>
 __device__ __forceinline__ void merge_row(const SplitParams& p, int x, int s, int xi, int ns, int sx, int N,
                                           int xbv, int lane) {
   constexpr int NC = D / 16;
@@ -1125,7 +1233,7 @@ __device__ __forceinline__ void merge_row(const SplitParams& p, int x, int s, in
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int dd = acc_dim<E>(c, j, i);
+        const int dd = acc_dim<AL>(c, j, i);
         orow[dd] = vch ? A[c][i] / L * vch[dd] : A[c][i] * inv;
       }
   }
@@ -1308,6 +1416,10 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
     compute_step<D, KVT>(r, qop, p, m.t0, window_lo(m.t_end, p.win), m.t_end, lane, m_run, l_run, acc);
     if (m.flags & kFlush) {
       const float l = sum_x32(sum_x16(l_run));
+      if constexpr (GE::I4) {
+#pragma unroll
+        for (int c = 0; c < GE::NC; ++c) acc[c] -= kInt4Bias * l;   // the V operand held 136 + code
+      }
       const int gt = m.flags >> 8;
       if (row < gt) {
         const __amdgpu_buffer_rsrc_t pr = slot_rsrc(p.part_acc, m.slot, GE::NC * 1024);
@@ -1380,7 +1492,7 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
     while (complete) {
       const int l = __builtin_ctzll(complete);
       complete &= complete - 1;
-      merge_row<D, GE::E>(p, __builtin_amdgcn_readlane(lx, l), __builtin_amdgcn_readlane(ls, l),
+      merge_row<D, GE::AL>(p, __builtin_amdgcn_readlane(lx, l), __builtin_amdgcn_readlane(ls, l),
                           __builtin_amdgcn_readlane(lxi, l), __builtin_amdgcn_readlane(ln, l),
                           __builtin_amdgcn_readlane(lsx, l), N, xbv, lane);
     }
@@ -1413,7 +1525,7 @@ using IC = std::integral_constant<int, V>;
 // storage kv_dtype and block size B (8, 16, 32).  INT8 with per-tensor or
 // per-channel scales runs the per-tensor codes kernel (the channel scales are
 // folded into q and into the output).
-template <class F>
+template <bool kInt4, class F>
 auto with_variant(int D, int kvt, int B, F&& f) {
   auto by_b = [&](auto dc, auto kc) {
     if (B == 8) return f(dc, kc, IC<8>{});
@@ -1426,6 +1538,9 @@ auto with_variant(int D, int kvt, int B, F&& f) {
       case PKV_KV_FP8_E5M2: return by_b(dc, IC<PKV_KV_FP8_E5M2>{});
       case PKV_KV_INT8_TENSOR:
       case PKV_KV_INT8_CHANNEL: return by_b(dc, IC<PKV_KV_INT8_TENSOR>{});
+      case PKV_KV_INT4:
+        if constexpr (kInt4) return by_b(dc, IC<PKV_KV_INT4>{});
+        [[fallthrough]];
       default: return by_b(dc, IC<PKV_KV_INT8>{});
     }
   };
@@ -1433,7 +1548,7 @@ auto with_variant(int D, int kvt, int B, F&& f) {
 }
 
 hipError_t launch_single(const DecodeParams& p, int D, int kvt, int B, int grid, hipStream_t stream) {
-  return with_variant(D, kvt, B, [&](auto dc, auto kc, auto bc) {
+  return with_variant<false>(D, kvt, B, [&](auto dc, auto kc, auto bc) {
     hipLaunchKernelGGL((pa_decode_kernel<decltype(dc)::value, decltype(kc)::value, decltype(bc)::value>), dim3(grid),
                        dim3(kWave * kNW), 0, stream, p);
     return hipGetLastError();
@@ -1443,11 +1558,11 @@ hipError_t launch_single(const DecodeParams& p, int D, int kvt, int B, int grid,
 // Steps of K/V registers per wave: one computed, the rest in flight (about
 // 40 KB per wave, 160 KB per CU with one wave per SIMD).
 template <int D, int KVT>
-constexpr int split_nbuf() { return D == 64 ? 8 : 5; }
+constexpr int split_nbuf() { return KVT == PKV_KV_INT4 ? 8 : (D == 64 ? 8 : 5); }
 constexpr int kMaxBlocksPerCU = 1;       // persistent grid: one workgroup (a wave per SIMD) per CU
 
 const void* split_kernel_fn(int D, int kvt, int B) {
-  return with_variant(D, kvt, B, [](auto dc, auto kc, auto bc) {
+  return with_variant<true>(D, kvt, B, [](auto dc, auto kc, auto bc) {
     constexpr int Dv = decltype(dc)::value, Kv = decltype(kc)::value, Bv = decltype(bc)::value;
     return reinterpret_cast<const void*>(&pa_split_kernel<Dv, Kv, Bv, split_nbuf<Dv, Kv>()>);
   });
@@ -1472,7 +1587,7 @@ int device_cus(int* cus) {
 // Resident workgroups per CU of one split-kernel variant (cached).
 int split_blocks_per_cu(int D, int kvt, int B) {
   static std::mutex mu;
-  static int cache[64][2][5][3] = {};
+  static int cache[64][2][6][3] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
   const int di = D == 64 ? 0 : 1, bi = B == 8 ? 0 : (B == 16 ? 1 : 2);
@@ -1529,7 +1644,7 @@ bool split_sizes(int32_t S, int32_t Hq, int32_t Hkv_or_0, int32_t D, int32_t W, 
 }
 
 void launch_split(const SplitParams& p, int D, int kvt, int B, int grid, hipStream_t stream) {
-  with_variant(D, kvt, B, [&](auto dc, auto kc, auto bc) {
+  with_variant<true>(D, kvt, B, [&](auto dc, auto kc, auto bc) {
     constexpr int Dv = decltype(dc)::value, Kv = decltype(kc)::value, Bv = decltype(bc)::value;
     hipLaunchKernelGGL((pa_split_kernel<Dv, Kv, Bv, split_nbuf<Dv, Kv>()>), dim3(grid), dim3(kWave * kNW), 0, stream,
                        p);
@@ -1604,8 +1719,11 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     if (!(ksc > 0.f) || !(vsc > 0.f) || !(ksc < INFINITY) || !(vsc < INFINITY))
       return fail(PKV_ERR_INVALID, "per-tensor scales must be positive and finite");
   }
-  const bool channel = c.kv_dtype == PKV_KV_INT8_CHANNEL;
-  if (channel && (const void*)out == q) return fail(PKV_ERR_INVALID, "out must not alias q for per-channel int8");
+  if (c.kv_dtype == PKV_KV_INT4 && partition_size == 0)
+    return fail(PKV_ERR_UNSUPPORTED, "INT4 storage decodes in the split-context form (partition_size > 0)");
+  const bool channel = has_channel_scales(c.kv_dtype);
+  if (channel && (const void*)out == q)
+    return fail(PKV_ERR_INVALID, "out must not alias q for storage with per-channel scales");
   const int32_t G = num_q_heads / c.num_kv_heads;
   const int32_t QT = (G + 15) / 16;
   const int64_t rows = (int64_t)num_seqs * c.num_kv_heads * QT;

@@ -52,4 +52,17 @@ __device__ __forceinline__ uint32_t int8_store(uint32_t bf16_bits, float scale) 
   return (uint32_t)(int32_t)c & 0xffu;
 }
 
+// INT4 nibble (code + 8) of a bf16 value under its calibrated channel scale:
+// code = clamp(rint(x / scale), -7, 7), 0 when the scale is not positive.
+__device__ __forceinline__ uint32_t int4_store(uint32_t bf16_bits, float scale) {
+  if (!(scale > 0.f)) return 8u;
+  const float c = fminf(fmaxf(__builtin_rintf(__fdiv_rn(bf16_bits_to_float(bf16_bits), scale)), -7.f), 7.f);
+  return (uint32_t)((int32_t)c + 8);
+}
+
+// Element i (0..7) of the 8 dims one INT4 K word holds sits in nibble
+// 4 (i % 2) + i / 2, so byte b of the word holds elements
+// int4_k_lo_elem(b) (low nibble) and int4_k_lo_elem(b) + 2 (high nibble).
+__device__ __forceinline__ int int4_k_lo_elem(int b) { return (b & 1) * 4 + (b >> 1); }
+
 }  // namespace pkv

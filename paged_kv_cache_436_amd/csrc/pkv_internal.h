@@ -18,15 +18,27 @@ inline pkv_status fail(pkv_status st, const char* msg) {
   return st;
 }
 
-inline int elem_bytes(int32_t kv_dtype) {
+// Bits per stored K/V element; 0 for an unknown dtype.
+inline int elem_bits(int32_t kv_dtype) {
   switch (kv_dtype) {
-    case PKV_KV_BF16: return 2;
-    case PKV_KV_FP8_E5M2: return 1;
-    case PKV_KV_INT8: return 1;
-    case PKV_KV_INT8_TENSOR: return 1;
-    case PKV_KV_INT8_CHANNEL: return 1;
+    case PKV_KV_BF16: return 16;
+    case PKV_KV_FP8_E5M2: return 8;
+    case PKV_KV_INT8: return 8;
+    case PKV_KV_INT8_TENSOR: return 8;
+    case PKV_KV_INT8_CHANNEL: return 8;
+    case PKV_KV_INT4: return 4;
     default: return 0;
   }
+}
+
+// Bytes of one (block, head) tile of K (or V).
+inline uint64_t tile_bytes_of(const pkv_pool_config& c) {
+  return (uint64_t)c.block_size * c.head_dim * elem_bits(c.kv_dtype) / 8;
+}
+
+// Calibrated per-(layer, head, dim) scales kept in the pool.
+inline bool has_channel_scales(int32_t kv_dtype) {
+  return kv_dtype == PKV_KV_INT8_CHANNEL || kv_dtype == PKV_KV_INT4;
 }
 
 constexpr uint64_t kRegionAlign = 256;

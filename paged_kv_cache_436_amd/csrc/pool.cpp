@@ -27,8 +27,8 @@ void clear_error() { g_error.clear(); }
 
 bool pool_regions(const pkv_pool_config* cfg, Regions* r) {
   if (!cfg) { set_error("pool config is NULL"); return false; }
-  const int e = elem_bytes(cfg->kv_dtype);
-  if (e == 0) { set_error("kv_dtype %d is not a pkv_kv_dtype", cfg->kv_dtype); return false; }
+  const int bits = elem_bits(cfg->kv_dtype);
+  if (bits == 0) { set_error("kv_dtype %d is not a pkv_kv_dtype", cfg->kv_dtype); return false; }
   if (cfg->num_layers <= 0 || cfg->num_blocks <= 0 || cfg->block_size <= 0 ||
       cfg->num_kv_heads <= 0 || cfg->head_dim <= 0) {
     set_error("pool dimensions must be positive (layers %d blocks %d block_size %d heads %d dim %d)",
@@ -36,11 +36,12 @@ bool pool_regions(const pkv_pool_config* cfg, Regions* r) {
     return false;
   }
   if (cfg->block_size % 4 != 0) { set_error("block_size %d is not a multiple of 4", cfg->block_size); return false; }
-  if (cfg->head_dim % (16 / e) != 0) {
-    set_error("head_dim %d is not a multiple of %d", cfg->head_dim, 16 / e);
+  const int dmul = bits == 4 ? 32 : 128 / bits;     // dims per 16-byte piece (INT4: per 32-bit word group)
+  if (cfg->head_dim % dmul != 0) {
+    set_error("head_dim %d is not a multiple of %d", cfg->head_dim, dmul);
     return false;
   }
-  const uint64_t tile = (uint64_t)cfg->block_size * cfg->head_dim * e;
+  const uint64_t tile = tile_bytes_of(*cfg);
   const uint64_t kv = (uint64_t)cfg->num_layers * cfg->num_blocks * cfg->num_kv_heads * tile;
   r->kv_bytes = kv;
   r->k = 0;
@@ -48,7 +49,7 @@ bool pool_regions(const pkv_pool_config* cfg, Regions* r) {
   r->total = align_up(r->v + kv);
   r->ks = r->vs = 0;
   r->scale_bytes = 0;
-  if (cfg->kv_dtype == PKV_KV_INT8 || cfg->kv_dtype == PKV_KV_INT8_CHANNEL) {
+  if (cfg->kv_dtype == PKV_KV_INT8 || has_channel_scales(cfg->kv_dtype)) {
     const uint64_t sb = cfg->kv_dtype == PKV_KV_INT8
                             ? (uint64_t)cfg->num_layers * cfg->num_blocks * cfg->num_kv_heads * cfg->block_size *
                                   sizeof(float)
@@ -66,9 +67,9 @@ pkv_status check_pool(const pkv_pool* pool) {
   Regions r;
   if (!pool_regions(&pool->cfg, &r)) return PKV_ERR_INVALID;
   if (!pool->k || !pool->v) return fail(PKV_ERR_INVALID, "pool has no K/V pointers (use kv_pool_create)");
-  if ((pool->cfg.kv_dtype == PKV_KV_INT8 || pool->cfg.kv_dtype == PKV_KV_INT8_CHANNEL) &&
+  if ((pool->cfg.kv_dtype == PKV_KV_INT8 || has_channel_scales(pool->cfg.kv_dtype)) &&
       (!pool->k_scale || !pool->v_scale))
-    return fail(PKV_ERR_INVALID, "int8 pool has no scale pointers");
+    return fail(PKV_ERR_INVALID, "pool has no scale pointers");
   return PKV_OK;
 }
 
@@ -94,8 +95,7 @@ int64_t kv_pool_num_blocks_for_budget(const pkv_pool_config* cfg, uint64_t budge
   if (!pool_regions(&c, &r)) return -1;
   // bytes grow linearly in num_blocks apart from alignment padding: start
   // from the payload estimate and step down until the padded size fits
-  const int e = elem_bytes(c.kv_dtype);
-  uint64_t per_block = 2ull * c.num_layers * c.num_kv_heads * c.block_size * c.head_dim * e;
+  uint64_t per_block = 2ull * c.num_layers * c.num_kv_heads * tile_bytes_of(c);
   if (c.kv_dtype == PKV_KV_INT8) per_block += 2ull * c.num_layers * c.num_kv_heads * c.block_size * 4;
   // (per-channel scales do not grow with the block count: the exact check below covers them)
   int64_t nb = (int64_t)(budget_bytes / per_block);
@@ -130,7 +130,7 @@ pkv_status kv_pool_create(const pkv_pool_config* cfg, void* dev_mem, uint64_t by
     out->k_scale = reinterpret_cast<float*>(b + r.ks);
     out->v_scale = reinterpret_cast<float*>(b + r.vs);
   }
-  out->tile_bytes = (uint64_t)cfg->block_size * cfg->head_dim * elem_bytes(cfg->kv_dtype);
+  out->tile_bytes = tile_bytes_of(*cfg);
   out->layer_bytes = (uint64_t)cfg->num_blocks * cfg->num_kv_heads * out->tile_bytes;
   clear_error();
   return PKV_OK;
