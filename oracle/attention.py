@@ -188,3 +188,40 @@ def paged_decode(q_bits: np.ndarray, img: PoolImage, layer: int,
         K, V = gather_kv(img, layer, block_tables[s], ctx, k_scale, v_scale, window_start(ctx, window))
         out[s] = attend(codecs.bf16_bits_to_f64(q_bits[s]), K, V, scale)
     return out
+
+
+def paged_prefill(q_bits: np.ndarray, img: PoolImage, layer: int, block_tables: np.ndarray,
+                  context_lens: np.ndarray, query_start: np.ndarray, scale: float,
+                  k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+    """Paged prefill of a chunk of new tokens per sequence, causal.
+
+    Prefix caching keeps the KV of a cached prompt prefix and computes only
+    the rest of the prompt (bjdmk.com.cn article, §4.1: the prefill of the
+    prefix is skipped; "KV Cache 原理与 PagedAttention", §五).  Reading of that
+    step: sequence s brings n_s = query_start[s+1] - query_start[s] new
+    tokens, the last n_s of its context_lens[s] positions, whose K/V are
+    already in the cache; new token k sits at position ctx_s - n_s + k and
+    attends to positions 0 .. ctx_s - n_s + k (itself included, nothing
+    after), the decode formula of ``attend`` over that shorter context.
+
+    q_bits: [T, Hq, D] bf16 bits, sequence s's queries in rows
+    query_start[s] .. query_start[s+1] - 1.  Returns [T, Hq, D] float64; a
+    query whose position would be negative (n_s > ctx_s) gets a zero row.
+    """
+    q_bits = np.asarray(q_bits, dtype=np.uint16)
+    T, hq, dim = q_bits.shape
+    qs = np.asarray(query_start, dtype=np.int64)
+    out = np.zeros((T, hq, dim), dtype=np.float64)
+    for s in range(len(context_lens)):
+        ctx = int(context_lens[s])
+        n = int(qs[s + 1] - qs[s])
+        if n == 0:
+            continue
+        K, V = gather_kv(img, layer, block_tables[s], ctx, k_scale, v_scale)
+        q = codecs.bf16_bits_to_f64(q_bits[qs[s]:qs[s + 1]])
+        for k in range(n):
+            pos = ctx - n + k
+            if pos < 0:
+                continue
+            out[qs[s] + k] = attend(q[k], K[:pos + 1], V[:pos + 1], scale)
+    return out

@@ -97,3 +97,26 @@ def test_int4_offset_of_seven_is_caught(monkeypatch):
     real = codecs.int4_encode
     monkeypatch.setattr(codecs, "int4_encode", lambda x, s: np.clip(real(x, s), -7, 6).astype(np.int8))
     assert _fails(t4.test_bound_saturation_and_zero_scale)
+
+
+def test_causal_limit_off_by_one_is_caught(monkeypatch):
+    # each query also attends to the key right after its own position
+    from tests import test_oracle_prefill as tpf
+    real = att.attend
+
+    def attend_one_more(q, K, V, scale):
+        return real(q, K, V, scale)
+
+    def bad(q_bits, img, layer, bt, ctx, qs, scale, ks=1.0, vs=1.0):
+        q_bits = np.asarray(q_bits, dtype=np.uint16)
+        out = np.zeros(q_bits.shape, dtype=np.float64)
+        for s in range(len(ctx)):
+            c, n = int(ctx[s]), int(qs[s + 1] - qs[s])
+            K, V = att.gather_kv(img, layer, bt[s], c, ks, vs)
+            q = codecs.bf16_bits_to_f64(q_bits[qs[s]:qs[s + 1]])
+            for k in range(n):
+                pos = c - n + k
+                out[qs[s] + k] = attend_one_more(q[k], K[:pos + 2], V[:pos + 2], scale)
+        return out
+    monkeypatch.setattr(att, "paged_prefill", bad)
+    assert _fails(lambda: tpf.test_whole_prompt_equals_matrix_causal_attention(1))

@@ -1,0 +1,90 @@
+"""Pins of the oracle's paged prefill (a chunk of new tokens per sequence,
+causal over the cache): the whole-prompt case against a matrix-form causal
+softmax attention written independently here, the chunk's last token against
+the decode oracle, chunking invariance (one chunk or two give the same rows),
+and zero rows for queries with no position.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import attention, cache_ops, codecs, layout
+from tests.helpers import expanded_slots, random_tables
+
+
+def _pool(rng, ctx, B=8, H=2, D=32, dt=layout.KV_BF16):
+    nb = sum(math.ceil(int(c) / B) for c in ctx) + 2
+    p = layout.PoolShape(1, nb, B, H, D, dt)
+    img = layout.empty_image(p)
+    bt = random_tables(rng, nb, np.asarray(ctx), B)
+    k = workloads.to_bf16_bits(rng.standard_normal((int(sum(ctx)), H, D), dtype=np.float32))
+    v = workloads.to_bf16_bits(rng.standard_normal((int(sum(ctx)), H, D), dtype=np.float32))
+    slots = np.concatenate([expanded_slots(bt[s], int(ctx[s]), B) for s in range(len(ctx))])
+    img = cache_ops.reshape_and_cache(img, 0, k, v, slots)
+    return img, bt, k, v
+
+
+def _causal_sdpa(q, k, v, scale, G):
+    """q [n, Hq, D], k/v [n, Hkv, D] (float64): softmax(q k^T * scale + causal
+    mask) v, as matrices."""
+    n, hq, _ = q.shape
+    out = np.zeros_like(q)
+    mask = np.triu(np.ones((n, n), bool), 1)            # key j > query i is hidden
+    for h in range(hq):
+        s = (q[:, h, :] @ k[:, h // G, :].T) * scale
+        s[mask] = -np.inf
+        w = np.exp(s - s.max(axis=1, keepdims=True))
+        out[:, h, :] = (w / w.sum(axis=1, keepdims=True)) @ v[:, h // G, :]
+    return out
+
+
+@pytest.mark.parametrize("G", [1, 3])
+def test_whole_prompt_equals_matrix_causal_attention(G):
+    rng = np.random.default_rng(14000 + G)
+    ctx = [1, 9, 23]
+    H, D = 2, 32
+    img, bt, k, v = _pool(rng, ctx, H=H, D=D)
+    qs = np.concatenate([[0], np.cumsum(ctx)])
+    q = workloads.to_bf16_bits(rng.standard_normal((int(qs[-1]), H * G, D), dtype=np.float32))
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
+    got = attention.paged_prefill(q, img, 0, bt, np.asarray(ctx), qs, scale)
+    for s in range(len(ctx)):
+        a, b = int(qs[s]), int(qs[s + 1])
+        want = _causal_sdpa(codecs.bf16_bits_to_f64(q[a:b]), codecs.bf16_bits_to_f64(k[a:b]),
+                            codecs.bf16_bits_to_f64(v[a:b]), np.float64(np.float32(scale)), G)
+        assert np.allclose(got[a:b], want, atol=1e-12, rtol=1e-12)
+
+
+def test_last_token_of_a_chunk_is_the_decode():
+    rng = np.random.default_rng(14100)
+    ctx = np.array([5, 17, 40, 33])
+    n = np.array([5, 3, 1, 16])                      # whole prompt, chunks, a single token
+    img, bt, _, _ = _pool(rng, ctx)
+    qs = np.concatenate([[0], np.cumsum(n)])
+    q = workloads.to_bf16_bits(rng.standard_normal((int(qs[-1]), 4, 32), dtype=np.float32))
+    got = attention.paged_prefill(q, img, 0, bt, ctx, qs, 0.17)
+    last = q[qs[1:] - 1]
+    want = attention.paged_decode(last, img, 0, bt, ctx, 0.17)
+    assert np.array_equal(got[qs[1:] - 1], want)
+
+
+def test_two_chunks_give_the_rows_of_one():
+    # prefilling positions [0, 12) then [12, 30) equals prefilling [0, 30)
+    rng = np.random.default_rng(14200)
+    img, bt, _, _ = _pool(rng, [30])
+    q = workloads.to_bf16_bits(rng.standard_normal((30, 2, 32), dtype=np.float32))
+    whole = attention.paged_prefill(q, img, 0, bt, np.array([30]), np.array([0, 30]), 0.2)
+    first = attention.paged_prefill(q[:12], img, 0, bt, np.array([12]), np.array([0, 12]), 0.2)
+    second = attention.paged_prefill(q[12:], img, 0, bt, np.array([30]), np.array([0, 18]), 0.2)
+    assert np.array_equal(np.concatenate([first, second]), whole)
+
+
+def test_queries_without_a_position_are_zero():
+    rng = np.random.default_rng(14300)
+    img, bt, _, _ = _pool(rng, [4])
+    q = workloads.to_bf16_bits(rng.standard_normal((6, 2, 32), dtype=np.float32))
+    got = attention.paged_prefill(q, img, 0, bt, np.array([4]), np.array([0, 6]), 0.2)
+    assert not got[:2].any() and np.all(np.abs(got[2:]).sum(axis=(1, 2)) > 0)
