@@ -260,6 +260,32 @@ pkv_status paged_attn_decode(float* out, const void* q, const pkv_pool* pool, in
                              const pkv_kv_scales* kv_scales, int32_t partition_size,
                              void* workspace, uint64_t workspace_bytes, hipStream_t stream);
 
+/* Paged prefill: causal attention of a chunk of new tokens per sequence over
+ * its cached context.  Sequence s brings n_s = query_start[s+1] -
+ * query_start[s] new tokens, the last n_s of its context_lens[s] positions,
+ * whose K/V are already in the pool (reshape_and_cache); new token k sits at
+ * position ctx_s - n_s + k and attends to positions 0 .. ctx_s - n_s + k,
+ * itself included.  This is the prefill that prefix caching leaves to do: the
+ * cached prompt prefix is reused and only the rest is computed ([BJD] §4.1;
+ * [KVP] §五); a whole prompt is the case n_s = ctx_s, a decode step the case
+ * n_s = 1.  Same arithmetic and storage types as paged_attn_decode's
+ * single-pass form (not INT4: PKV_ERR_UNSUPPORTED).
+ *   out           device fp32 [T][Hq][D], T = num_queries = query_start[S]
+ *   q             device bf16 [T][Hq][D]
+ *   query_start   device int32 [S + 1], non-decreasing, query_start[0] = 0
+ *   max_query_len host; >= every n_s (it sizes the grid: tiles of 16
+ *                 (token, head) pairs per KV head; a chunk longer than it is
+ *                 cut, its later tokens left unwritten)
+ *   block_tables, context_lens, kv_scales as for paged_attn_decode.
+ * A query whose position would be negative (n_s > ctx_s) gets a zero row.
+ * For per-channel scales, out must not alias q (the folded query is staged
+ * in out's rows first). */
+pkv_status paged_attn_prefill(float* out, const void* q, const pkv_pool* pool, int32_t layer,
+                              const int32_t* block_tables, int32_t table_width, const int32_t* context_lens,
+                              const int32_t* query_start, int32_t num_seqs, int32_t num_queries,
+                              int32_t max_query_len, int32_t num_q_heads, float scale, int32_t kv_dtype,
+                              const pkv_kv_scales* kv_scales, hipStream_t stream);
+
 /* One decode step with its cache write in the same launch: for each sequence s
  * with ctx_s > 0, the new token's K and V (key, value: device bf16
  * [S][H][D], 16-byte aligned) are stored at position ctx_s - 1 - the slot the

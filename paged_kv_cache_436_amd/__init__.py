@@ -95,6 +95,8 @@ SIGNATURES = {
     "paged_attn_decode_append": (_I32, [_P, _P, ctypes.POINTER(PoolDesc), _I32, _P, _P, _P, _I32, _P, _I32,
                                         _I32, _F, _I32, ctypes.POINTER(KVScales), _I32, _P, _U64, _P]),
     "paged_attn_decode_ex": (_I32, [ctypes.POINTER(DecodeArgs), _P]),
+    "paged_attn_prefill": (_I32, [_P, _P, ctypes.POINTER(PoolDesc), _I32, _P, _I32, _P, _P, _I32, _I32, _I32,
+                                  _I32, _F, _I32, ctypes.POINTER(KVScales), _P]),
     "pkv_check_slots": (_I32, [_I64P, _I32, _I64]),
     "pkv_check_pairs": (_I32, [_I64P, _I32, _I32]),
     "pkv_check_tables": (_I32, [_I32P, _I32P, _I32, _I32, _I32, _I32]),
@@ -269,6 +271,21 @@ def paged_attn_decode_ex(out, q, pool: Pool, layer: int, block_tables, context_l
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.paged_attn_decode_ex(ctypes.byref(a), _stream(stream)))
+
+
+def paged_attn_prefill(out, q, pool: Pool, layer: int, block_tables, context_lens, query_start, scale: float,
+                       max_query_len: int, kv_dtype: int | None = None, k_scale: float = 1.0,
+                       v_scale: float = 1.0, stream=None):
+    """Causal attention of a chunk of new tokens per sequence over its cached
+    context (see pkv.h): q, out are [T][Hq][D] (bf16, fp32); query_start is
+    int32 [S + 1] on the device; max_query_len bounds every chunk."""
+    T, hq, _ = q.shape
+    S = context_lens.shape[0]
+    sc = KVScales(k_scale, v_scale)
+    kvd = pool.cfg.kv_dtype if kv_dtype is None else kv_dtype
+    _check(_lib.paged_attn_prefill(_ptr(out), _ptr(q), ctypes.byref(pool.desc), layer, _ptr(block_tables),
+                                   block_tables.shape[1], _ptr(context_lens), _ptr(query_start), S, T,
+                                   int(max_query_len), hq, float(scale), kvd, ctypes.byref(sc), _stream(stream)))
 
 
 # ------------------------------------------------------------------- checks

@@ -480,6 +480,216 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
 }
 
 // =====================================================================
+// Paged prefill (a chunk of new tokens per sequence, causal)
+// =====================================================================
+// The decode matrix-core step with its 16 columns taken by (query token,
+// query head) pairs of one KV head instead of by query heads: column c of a
+// tile is token c / G of the sequence's chunk and head g G + c % G.  Token k
+// of a chunk of n sits at position ctx - n + k and sees positions 0 .. ctx -
+// n + k, so each column masks the keys at or past its own limit; the tile
+// streams K/V up to its last column's limit once for all 16 columns.  Four
+// waves share the steps and merge through LDS, as the single-pass decode.
+struct PrefillParams {
+  DecodeParams d;             // q [T][Hq][D] (or the folded q), out [T][Hq][D], pool layer, tables, lengths
+  const int32_t* qstart;      // [S + 1]: sequence s's queries are rows qstart[s] .. qstart[s+1] - 1
+  int32_t tiles;              // column tiles per (sequence, KV head): ceil(max_query_len * G / 16)
+  int32_t T;                  // rows of q and out
+};
+
+template <int D, int KVT, int B>
+__global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillParams pp) {
+  const DecodeParams& p = pp.d;
+  using T = Tile<D, KVT>;
+  constexpr int E = T::E;
+  __shared__ float sm_ml[kNW][2][16];
+  __shared__ float sm_acc[kNW][16][D + 4];
+
+  const int nwg = (int)gridDim.x;
+  const int xcd = (int)blockIdx.x % 8;
+  const int per_xcd = (nwg + 7) / 8;
+  const int item = xcd * per_xcd + (int)blockIdx.x / 8;
+  if (item >= p.num_items) return;
+  const int ct = item % pp.tiles;
+  const int g = (item / pp.tiles) % p.Hkv;
+  const int s = item / (pp.tiles * p.Hkv);
+  // query rows, kept inside [0, T) whatever query_start holds
+  const int q0 = min(max(pp.qstart[s], 0), pp.T);
+  const int n = min(max(pp.qstart[s + 1], q0), pp.T) - q0;
+  const int ncol = n * p.G;
+  const int c0 = ct * 16;
+  if (c0 >= ncol) return;
+  const int cols = min(16, ncol - c0);
+
+  const int lane = threadIdx.x % kWave;
+  const int w = threadIdx.x / kWave;
+  const int row = lane & 15;
+  const int j = lane >> 4;
+  const int ctx = clamp_ctx(p.ctx[s], p.W * B);
+  // this lane's column (columns past the tile's last read column 0's query)
+  const int c = c0 + (row < cols ? row : 0);
+  const int kq = c / p.G;
+  const int hq = g * p.G + c % p.G;
+  const int lim = row < cols ? max(0, ctx - n + kq + 1) : 0;     // keys [0, lim)
+  const int t_end = max(0, ctx - n + (c0 + cols - 1) / p.G + 1);  // the tile's largest limit
+  const int nsteps = (t_end + kStep - 1) / kStep;
+  const int32_t* bt_row = p.bt + (int64_t)s * p.W;
+
+  bf16x8 qop[T::KK];
+  {
+    const uint16_t* qh = p.q + ((int64_t)(q0 + kq) * p.Hq + hq) * p.q_stride;
+#pragma unroll
+    for (int kk = 0; kk < T::KK; ++kk)
+      qop[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + q_dim0<E>(kk, j)));
+  }
+
+  f32x4 acc[T::NC];
+#pragma unroll
+  for (int cc = 0; cc < T::NC; ++cc) acc[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;   // running max of scaled logits (log2 domain), column `row`
+  float l_run = 0.f;
+
+  auto compute = [&](const StepRegs<D, KVT>& r, int tok0) {
+    f32x4 z[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f32x4 acc_z = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < T::KK; ++kk) {
+        bf16x8 a;
+        if constexpr (E == 2) {
+          a = __builtin_bit_cast(bf16x8, r.k[h][kk]);
+        } else {
+          const u32x4 wv = r.k[h][kk >> 1];
+          a = (kk & 1) ? widen8<KVT>(wv[2], wv[3]) : widen8<KVT>(wv[0], wv[1]);
+        }
+        acc_z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[kk], acc_z, 0, 0, 0);
+      }
+      z[h] = acc_z;
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = tok0 + 16 * h + 4 * j + i;
+        float zz = z[h][i] * p.qk_scale;
+        if constexpr (KVT == PKV_KV_INT8) zz *= r.ksc[h][i];
+        zz = t < lim ? zz : -INFINITY;          // causal: this column's keys only
+        z[h][i] = zz;
+        mloc = fmaxf(mloc, zz);
+      }
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+    const float m_new = fmaxf(m_run, mloc);
+    // a column with no key yet keeps max -inf; exponents then use 0 so that
+    // its p and rescale factor are 0, not NaN
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    float psum = 0.f;
+    uint32_t ph[2][2], pl[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float pv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(z[h][i] - m_use);
+        psum += pv[i];
+        if constexpr (KVT == PKV_KV_INT8) {
+          const int t = tok0 + 16 * h + 4 * j + i;
+          pv[i] = t < lim ? pv[i] * r.vsc[h][i] : 0.f;   // fold the V scale into p
+        }
+      }
+      ph[h][0] = pack_bf16x2(pv[0], pv[1]);
+      ph[h][1] = pack_bf16x2(pv[2], pv[3]);
+      pl[h][0] = pack_bf16x2(pv[0] - bf16_lo(ph[h][0]), pv[1] - bf16_hi(ph[h][0]));
+      pl[h][1] = pack_bf16x2(pv[2] - bf16_lo(ph[h][1]), pv[3] - bf16_hi(ph[h][1]));
+    }
+    l_run = l_run * alpha + psum;
+    const bf16x8 pop = __builtin_bit_cast(bf16x8, u32x4{ph[0][0], ph[0][1], ph[1][0], ph[1][1]});
+    const bf16x8 pop_lo = __builtin_bit_cast(bf16x8, u32x4{pl[0][0], pl[0][1], pl[1][0], pl[1][1]});
+    // keys past the tile's largest limit may be unwritten slots (any bits):
+    // their V is zeroed; keys below it are written data, masked by p = 0
+    const bool edge = tok0 + kStep > t_end;
+#pragma unroll
+    for (int cc = 0; cc < T::NC; ++cc) {
+      uint32_t a0, a1, a2, a3;
+      if constexpr (E == 2) {
+        const int u = cc >> 1, e = cc & 1;
+        a0 = r.v[0][u][2 * e];
+        a1 = r.v[0][u][2 * e + 1];
+        a2 = r.v[1][u][2 * e];
+        a3 = r.v[1][u][2 * e + 1];
+      } else {
+        const int u = cc >> 2, e = cc & 3;
+        widen4<KVT>(r.v[0][u][e], a0, a1);
+        widen4<KVT>(r.v[1][u][e], a2, a3);
+      }
+      if (edge) {
+        const int tb0 = tok0 + 4 * j, tb1 = tok0 + 16 + 4 * j;
+        a0 &= tok_mask16(tb0, 0, t_end);
+        a1 &= tok_mask16(tb0 + 2, 0, t_end);
+        a2 &= tok_mask16(tb1, 0, t_end);
+        a3 &= tok_mask16(tb1 + 2, 0, t_end);
+      }
+      const bf16x8 aop = __builtin_bit_cast(bf16x8, u32x4{a0, a1, a2, a3});
+      acc[cc] = acc[cc] * alpha;
+      acc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, pop, acc[cc], 0, 0, 0);
+      acc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, pop_lo, acc[cc], 0, 0, 0);
+    }
+  };
+
+  // wave w takes steps w, w + NW, ...; loads run one step ahead
+  StepRegs<D, KVT> r0, r1;
+  int i = w;
+  if (i < nsteps) issue_step<D, KVT, B>(r0, p, bt_row, g, i * kStep, 0, lane);
+  while (i < nsteps) {
+    int nx = i + kNW;
+    if (nx < nsteps) issue_step<D, KVT, B>(r1, p, bt_row, g, nx * kStep, 0, lane);
+    compute(r0, i * kStep);
+    i = nx;
+    if (i >= nsteps) break;
+    nx = i + kNW;
+    if (nx < nsteps) issue_step<D, KVT, B>(r0, p, bt_row, g, nx * kStep, 0, lane);
+    compute(r1, i * kStep);
+    i = nx;
+  }
+
+  // merge the waves per column through LDS
+  l_run += __shfl_xor(l_run, 16, kWave);
+  l_run += __shfl_xor(l_run, 32, kWave);
+  if (j == 0) {
+    sm_ml[w][0][row] = m_run;
+    sm_ml[w][1][row] = l_run;
+  }
+#pragma unroll
+  for (int cc = 0; cc < T::NC; ++cc) {
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) sm_acc[w][row][acc_dim<E>(cc, j, i2)] = acc[cc][i2];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < cols * D; idx += blockDim.x) {
+    const int col = idx / D;
+    const int d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kNW; ++ww) M = fmaxf(M, sm_ml[ww][0][col]);
+    float L = 0.f, A = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kNW; ++ww) {
+      const float mw = sm_ml[ww][0][col];
+      const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      L += f * sm_ml[ww][1][col];
+      A += f * sm_acc[ww][col][d];
+    }
+    const int cq = c0 + col;
+    const int64_t orow = (int64_t)(q0 + cq / p.G) * p.Hq + g * p.G + cq % p.G;
+    p.out[orow * D + d] = L > 0.f ? A / L * (p.vs_ch ? p.vs_ch[g * D + d] : p.out_scale) : 0.f;
+  }
+}
+
+// =====================================================================
 // Split-context persistent kernel (partition_size > 0)
 // =====================================================================
 // A "row" x = (sequence s, KV head g, head tile qt), numbered
@@ -1555,6 +1765,14 @@ hipError_t launch_single(const DecodeParams& p, int D, int kvt, int B, int grid,
   });
 }
 
+hipError_t launch_prefill(const PrefillParams& p, int D, int kvt, int B, int grid, hipStream_t stream) {
+  return with_variant<false>(D, kvt, B, [&](auto dc, auto kc, auto bc) {
+    hipLaunchKernelGGL((pa_prefill_kernel<decltype(dc)::value, decltype(kc)::value, decltype(bc)::value>),
+                       dim3(grid), dim3(kWave * kNW), 0, stream, p);
+    return hipGetLastError();
+  });
+}
+
 // Steps of K/V registers per wave: one computed, the rest in flight (about
 // 40 KB per wave, 160 KB per CU with one wave per SIMD).
 template <int D, int KVT>
@@ -1870,6 +2088,108 @@ extern "C" pkv_status paged_attn_decode_append(float* out, const void* q, const 
   return decode_impl(out, q, pool, layer, key, value, block_tables, table_width, context_lens, num_seqs,
                      num_q_heads, scale, kv_dtype, kv_scales, partition_size, 0, workspace, workspace_bytes,
                      stream);
+}
+
+extern "C" pkv_status paged_attn_prefill(float* out, const void* q, const pkv_pool* pool, int32_t layer,
+                                         const int32_t* block_tables, int32_t table_width,
+                                         const int32_t* context_lens, const int32_t* query_start,
+                                         int32_t num_seqs, int32_t num_queries, int32_t max_query_len,
+                                         int32_t num_q_heads, float scale, int32_t kv_dtype,
+                                         const pkv_kv_scales* kv_scales, hipStream_t stream) {
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  const pkv_pool_config& c = pool->cfg;
+  if (kv_dtype != c.kv_dtype) {
+    set_error("kv_dtype %d does not match the pool's %d", kv_dtype, c.kv_dtype);
+    return PKV_ERR_INVALID;
+  }
+  if (c.kv_dtype == PKV_KV_INT4) return fail(PKV_ERR_UNSUPPORTED, "paged prefill is not built for INT4 storage");
+  if (layer < 0 || layer >= c.num_layers) {
+    set_error("layer %d outside [0, %d)", layer, c.num_layers);
+    return PKV_ERR_INVALID;
+  }
+  if (num_seqs < 0 || num_queries < 0 || max_query_len < 0)
+    return fail(PKV_ERR_INVALID, "num_seqs, num_queries and max_query_len must not be negative");
+  if (num_seqs == 0 || num_queries == 0 || max_query_len == 0) { clear_error(); return PKV_OK; }
+  if (!out || !q || !block_tables || !context_lens || !query_start) return fail(PKV_ERR_INVALID, "NULL device pointer");
+  if (num_q_heads <= 0 || num_q_heads % c.num_kv_heads != 0) {
+    set_error("num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads, c.num_kv_heads);
+    return PKV_ERR_INVALID;
+  }
+  if (table_width <= 0) return fail(PKV_ERR_INVALID, "table_width must be positive");
+  if ((int64_t)table_width * c.block_size > INT32_MAX / 2) return fail(PKV_ERR_INVALID, "table_width too large");
+  if (!(scale > 0.f) || !(scale < INFINITY)) return fail(PKV_ERR_INVALID, "scale must be positive and finite");
+  if (c.head_dim != 64 && c.head_dim != 128) {
+    set_error("head_dim %d not built (64, 128)", c.head_dim);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (c.block_size != 8 && c.block_size != 16 && c.block_size != 32) {
+    set_error("block_size %d not built (8, 16, 32)", c.block_size);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (((uintptr_t)q) % 16 || ((uintptr_t)out) % 16) return fail(PKV_ERR_INVALID, "q and out must be 16-byte aligned");
+  float ksc = 1.f, vsc = 1.f;
+  if (kv_scales && (c.kv_dtype == PKV_KV_FP8_E5M2 || c.kv_dtype == PKV_KV_INT8_TENSOR)) {
+    ksc = kv_scales->k_scale;
+    vsc = kv_scales->v_scale;
+    if (!(ksc > 0.f) || !(vsc > 0.f) || !(ksc < INFINITY) || !(vsc < INFINITY))
+      return fail(PKV_ERR_INVALID, "per-tensor scales must be positive and finite");
+  }
+  const bool channel = has_channel_scales(c.kv_dtype);
+  if (channel && (const void*)out == q)
+    return fail(PKV_ERR_INVALID, "out must not alias q for storage with per-channel scales");
+  const int32_t G = num_q_heads / c.num_kv_heads;
+  const int64_t tiles = ((int64_t)max_query_len * G + 15) / 16;
+  const int64_t items = (int64_t)num_seqs * c.num_kv_heads * tiles;
+  if (items > INT32_MAX / 2) return fail(PKV_ERR_INVALID, "too many query tiles in one call");
+  const uint64_t scale_layer = channel ? (uint64_t)c.num_kv_heads * c.head_dim
+                                      : (uint64_t)c.num_blocks * c.num_kv_heads * c.block_size;
+  float* ksl = pool->k_scale ? pool->k_scale + layer * scale_layer : nullptr;
+  float* vsl = pool->v_scale ? pool->v_scale + layer * scale_layer : nullptr;
+  const uint16_t* qk = static_cast<const uint16_t*>(q);
+  int32_t q_stride = c.head_dim;
+  if (channel) {   // the K channel scales folded into the query, written into the output rows first
+    const int64_t n = (int64_t)num_queries * num_q_heads * c.head_dim;
+    const int64_t blocks = (n + 255) / 256;
+    if (blocks > INT32_MAX) return fail(PKV_ERR_INVALID, "too many queries in one call");
+    hipLaunchKernelGGL(fold_q_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, qk,
+                       reinterpret_cast<uint16_t*>(out), ksl, n, num_q_heads, G, c.head_dim);
+    qk = reinterpret_cast<const uint16_t*>(out);
+    q_stride = 2 * c.head_dim;
+  }
+  PrefillParams pp{};
+  DecodeParams& p = pp.d;
+  p.q = qk;
+  p.q_stride = q_stride;
+  p.vs_ch = channel ? vsl : nullptr;
+  p.out = out;
+  p.k = static_cast<char*>(pool->k) + (uint64_t)layer * pool->layer_bytes;
+  p.v = static_cast<char*>(pool->v) + (uint64_t)layer * pool->layer_bytes;
+  p.ks = ksl;
+  p.vs = vsl;
+  p.bt = block_tables;
+  p.ctx = context_lens;
+  p.W = table_width;
+  p.S = num_seqs;
+  p.Hq = num_q_heads;
+  p.Hkv = c.num_kv_heads;
+  p.G = G;
+  p.QT = 1;
+  p.num_blocks = c.num_blocks;
+  p.num_items = (int32_t)items;
+  p.win = 0;
+  p.qk_scale = scale * kLog2e * ksc;
+  p.out_scale = vsc;
+  pp.qstart = query_start;
+  pp.tiles = (int32_t)tiles;
+  pp.T = num_queries;
+  const hipError_t e = launch_prefill(pp, c.head_dim, c.kv_dtype, c.block_size, (int)((items + 7) / 8 * 8), stream);
+  if (e != hipSuccess) {
+    set_error("paged_attn_prefill launch failed: %s", hipGetErrorString(e));
+    return PKV_ERR_HIP;
+  }
+  clear_error();
+  return PKV_OK;
 }
 
 extern "C" pkv_status paged_attn_decode_ex(const pkv_decode_args* a, hipStream_t stream) {

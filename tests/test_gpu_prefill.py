@@ -1,0 +1,123 @@
+"""Paged prefill on the GPU against the oracle: chunks of new tokens (whole
+prompts, partial chunks after a cached prefix, single tokens, empty chunks,
+chunks longer than the context) over pools written by the GPU cache write,
+for every storage type the single-pass form serves, both head dims, block
+sizes 8 / 16 / 32 and several group sizes.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_436_amd as pkv
+import workloads
+from oracle import attention, cache_ops
+from tests.gpu_helpers import bf16_dev, dev, errors, first_diff, images_equal, read_pool, say
+from tests.helpers import expanded_slots
+
+pytestmark = pytest.mark.gpu
+
+BAR = {pkv.PKV_KV_BF16: (1e-2, 1e-3)}
+BAR8 = (2e-2, 5e-3)
+SCALES = {pkv.PKV_KV_FP8_E5M2: (0.5, 1.5), pkv.PKV_KV_INT8_TENSOR: (0.035, 0.03)}
+
+
+def _run(rng, dt, ctx, chunk, hkv=2, G=4, D=128, B=16, poison=True):
+    import torch
+    ctx = np.asarray(ctx, np.int32)
+    S = len(ctx)
+    need = [math.ceil(int(x) / B) for x in ctx]
+    nb = sum(need) + 3
+    W = max(1, max(need))
+    perm = rng.permutation(nb)
+    tables = np.zeros((S, W), np.int32)
+    pos = 0
+    for s, n in enumerate(need):
+        tables[s, :n] = perm[pos:pos + n]
+        tables[s, n:] = rng.integers(0, 2**31 - 1, size=W - n)      # garbage past the end
+        pos += n
+    cfg = pkv.make_config(1, nb, B, hkv, D, dt)
+    pool = pkv.Pool(cfg)
+    if poison:
+        pool.memory.fill_(255)
+    else:
+        pool.memory.zero_()
+    _, _, ks_off, vs_off = pool.region_offsets()
+    if dt == pkv.PKV_KV_INT8_CHANNEL:
+        n = hkv * D
+        pool.memory[ks_off:ks_off + 4 * n].view(torch.float32).copy_(
+            torch.from_numpy(rng.uniform(0.02, 0.05, n).astype(np.float32)))
+        pool.memory[vs_off:vs_off + 4 * n].view(torch.float32).copy_(
+            torch.from_numpy(rng.uniform(0.02, 0.05, n).astype(np.float32)))
+    ks, vs = SCALES.get(dt, (1.0, 1.0))
+    total = int(ctx.sum())
+    k = workloads.to_bf16_bits(rng.standard_normal((max(total, 1), hkv, D), dtype=np.float32))
+    v = workloads.to_bf16_bits(rng.standard_normal((max(total, 1), hkv, D), dtype=np.float32))
+    img = read_pool(pool)
+    if total:
+        slots = np.concatenate([expanded_slots(tables[s], int(ctx[s]), B) for s in range(S)])
+        pkv.reshape_and_cache(pool, 0, bf16_dev(k[:total]), bf16_dev(v[:total]), dev(slots.astype(np.int64)),
+                              k_scale=ks, v_scale=vs)
+        img = cache_ops.reshape_and_cache(img, 0, k[:total], v[:total], slots, ks, vs)
+        assert images_equal(read_pool(pool), img), first_diff(read_pool(pool), img)
+    chunk = np.asarray(chunk, np.int32)
+    qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    T = int(qs[-1])
+    hq = hkv * G
+    q = workloads.to_bf16_bits(rng.standard_normal((max(T, 1), hq, D), dtype=np.float32))[:T]
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
+    out = torch.full((max(T, 1), hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    pkv.paged_attn_prefill(out, bf16_dev(q) if T else torch.empty((0, hq, D), dtype=torch.bfloat16, device="cuda"),
+                           pool, 0, dev(tables), dev(ctx), dev(qs), scale, int(chunk.max()) if S else 0,
+                           k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()[:T]
+    want = attention.paged_prefill(q, img, 0, tables, ctx, qs, scale, ks, vs)
+    return got, want
+
+
+@pytest.mark.parametrize("dt", [pkv.PKV_KV_BF16, pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8, pkv.PKV_KV_INT8_TENSOR,
+                                pkv.PKV_KV_INT8_CHANNEL])
+@pytest.mark.parametrize("D,B", [(128, 16), (64, 32), (128, 8), (64, 16)])
+def test_prefill_matches_oracle(dt, D, B):
+    say(f"prefill dt={dt} D={D} B={B}")
+    rng = np.random.default_rng(15000 + 10 * dt + D + B)
+    hkv, G = (2, 4) if D == 128 else (1, 3)
+    ctx = [1, 40, 100, 257, 33, 64, 17]
+    chunk = [1, 40, 37, 30, 1, 0, 20]            # whole prompts, chunks after a prefix, single tokens, empty;
+    got, want = _run(rng, dt, ctx, chunk, hkv=hkv, G=G, D=D, B=B)   # the last chunk is longer than its context
+    assert np.all(np.isfinite(got))
+    mx, rel = errors(got, want)
+    say(f"  max_abs={mx:.3e} rel={rel:.3e}")
+    bar = BAR.get(dt, BAR8)
+    assert mx <= bar[0] and rel <= bar[1]
+    assert not got[-20:-17].any()                 # the last chunk's positions -3 .. -1: zero rows
+
+
+@pytest.mark.parametrize("G,hkv", [(1, 3), (5, 2), (8, 1), (16, 1), (24, 1)])
+def test_prefill_group_sizes(G, hkv):
+    say(f"prefill G={G} hkv={hkv}")
+    rng = np.random.default_rng(15100 + G)
+    got, want = _run(rng, pkv.PKV_KV_BF16, [50, 130], [50, 31], hkv=hkv, G=G)
+    mx, rel = errors(got, want)
+    assert mx <= BAR[pkv.PKV_KV_BF16][0] and rel <= BAR[pkv.PKV_KV_BF16][1]
+
+
+def test_prefill_long_prompt_many_tiles():
+    say("prefill long prompt")
+    rng = np.random.default_rng(15200)
+    got, want = _run(rng, pkv.PKV_KV_BF16, [1100, 700], [600, 700], hkv=1, G=8, poison=False)
+    mx, rel = errors(got, want)
+    assert mx <= BAR[pkv.PKV_KV_BF16][0] and rel <= BAR[pkv.PKV_KV_BF16][1]
+
+
+def test_prefill_refuses_int4():
+    import torch
+    cfg = pkv.make_config(1, 4, 16, 1, 128, pkv.PKV_KV_INT4)
+    pool = pkv.Pool(cfg)
+    out = torch.zeros((2, 2, 128), dtype=torch.float32, device="cuda")
+    q = torch.zeros((2, 2, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(pkv.PkvError, match="INT4"):
+        pkv.paged_attn_prefill(out, q, pool, 0, dev(np.zeros((1, 1), np.int32)), dev(np.array([2], np.int32)),
+                               dev(np.array([0, 2], np.int32)), 0.1, 2)
