@@ -75,6 +75,10 @@ def parse():
     ap.add_argument("--swap", type=int, default=0,
                     help="instead of the decode step: swap N blocks of the 70B-shaped pool out to pinned host "
                          "memory and back (swap_blocks), and report GB/s each way")
+    ap.add_argument("--prefill", action="store_true",
+                    help="instead of the decode step: paged prefill after a prefix-cache hit (200 prompts = a "
+                         "1500-token system prompt, cached and shared, + 64..512 own tokens; 70B-shaped heads), "
+                         "one layer per call; TFLOP/s against the bf16 matrix-core peak")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB three times (torch copy kernel): the reference for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -274,6 +278,111 @@ def swap_bench(args):
     print(json.dumps(res), flush=True)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+
+
+def prefill_bench(args):
+    """paged_attn_prefill over the prefix-cache workload: each of the 200
+    prompts attends causally to the shared cached system prompt and to its own
+    tokens.  HIP events around K back-to-back calls; algorithmic flops =
+    sum over new tokens of (positions attended) * Hq * 4 * D.  A few
+    sequences are checked against the oracle, which is timed on them."""
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import paged_kv_cache_436_amd as pkv
+    import workloads
+
+    w = workloads.prefix_prefill()
+    S, Hq, Hkv, D, B, W = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.table_width
+    ctx_np = np.asarray(w.context_lens, np.int64)
+    chunk = np.asarray(w.extra["chunk"], np.int64)
+    qs_np = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    T = int(qs_np[-1])
+    dev = torch.device("cuda:0")
+    cfg = pkv.make_config(1, w.num_blocks, B, Hkv, D, pkv.PKV_KV_BF16)
+    pool = pkv.Pool(cfg, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(436008)
+    k_off, v_off, _, _ = pool.region_offsets()
+    lb = pool.desc.layer_bytes
+    for off in (k_off, v_off):
+        pool.memory[off: off + lb].view(torch.bfloat16).normal_(generator=g)
+    tables = torch.from_numpy(w.extra["tables"]).to(dev)
+    ctx = torch.from_numpy(ctx_np.astype(np.int32)).to(dev)
+    qs = torch.from_numpy(qs_np).to(dev)
+    q = torch.randn((T, Hq, D), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
+    st = torch.cuda.current_stream()
+    maxq = int(chunk.max())
+
+    def call():
+        pkv.paged_attn_prefill(out, q, pool, 0, tables, ctx, qs, w.scale, maxq, stream=st)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(K):
+        call()
+    e1.record(st)
+    torch.cuda.synchronize()
+    per = e0.elapsed_time(e1) * 1e-3 / K
+    # keys attended: token k of a chunk of n over a prompt of c sees c - n + k + 1 positions
+    keys = int(sum(n * (c - n) + n * (n + 1) // 2 for c, n in zip(ctx_np, chunk)))
+    flops = keys * Hq * 4 * D
+    tfs = flops / per / 1e12
+    log(f"prefill: {T} new tokens, {keys} (token, position) pairs per head; {per * 1e3:.3f} ms per call, "
+        f"{tfs:.1f} TFLOP/s")
+
+    # oracle on a bounded sample of sequences (gather + causal attention, fp64)
+    from oracle import attention, layout
+    tile = pool.desc.tile_bytes
+    gpu_out = out.cpu().numpy()
+    qbits = q.view(torch.int16).cpu().numpy().view(np.uint16)
+    tabs = w.extra["tables"]
+    rng = np.random.default_rng(437)
+    spent, keys_done, worst, seqs = 0.0, 0, 0.0, 0
+    for s in rng.permutation(S):
+        c, n = int(ctx_np[s]), int(chunk[s])
+        nblk = math.ceil(c / B)
+        sub = layout.PoolShape(1, nblk, B, Hkv, D)
+        img = layout.empty_image(sub)
+        idx = torch.from_numpy(tabs[s, :nblk].astype(np.int64)).to(dev)
+        for region, dst in ((k_off, img.k), (v_off, img.v)):
+            lay = pool.memory[region: region + lb].view(w.num_blocks, Hkv * tile)
+            dst[:] = lay.index_select(0, idx).cpu().numpy().view(np.uint16).reshape(-1)
+        t0 = time.perf_counter()
+        ref = attention.paged_prefill(qbits[qs_np[s]:qs_np[s + 1]], img, 0, np.arange(nblk, dtype=np.int32)[None, :],
+                                      np.array([c]), np.array([0, n]), w.scale)
+        spent += time.perf_counter() - t0
+        worst = max(worst, float(np.max(np.abs(gpu_out[qs_np[s]:qs_np[s + 1]] - ref))))
+        keys_done += n * (c - n) + n * (n + 1) // 2
+        seqs += 1
+        if spent >= args.cpu_seconds:
+            break
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    cpu_tfs = keys_done * Hq * 4 * D / spent / 1e12
+    log(f"cpu oracle: {cpu_tfs:.6f} TFLOP/s over {seqs} sequences; parity max abs err {worst:.2e}")
+    res = {"metric": "paged prefill TFLOP/s (algorithmic, % of MI355X bf16 matrix-core peak)",
+           "value": round(tfs, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+           "ms_per_call": round(per * 1e3, 4), "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "paged prefill after a prefix-cache hit: 200 prompts = 1500-token shared system "
+                                  "prompt (93 cached blocks) + 64..512 own tokens, 64q/8kv heads, head_dim 128, "
+                                  "bf16 KV, block 16, one layer",
+                      "new_tokens": T, "max_query_len": maxq, "flops_per_call": flops},
+           "roofline": {"bound": "mfma", "kernel": "pa_prefill_kernel", "achieved": round(tfs, 2),
+                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+           "cpu_baseline": {"value": round(cpu_tfs, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+                            "sample": f"{seqs} sequences' prefill ({keys_done} (token, position) pairs per head), "
+                                      f"{spent:.1f} s of fp64 numpy causal attention"},
+           "parity_sample": {"sequences_checked": seqs, "max_abs_err": worst, "bar": 1e-2}}
+    print(json.dumps(res), flush=True)
+
+
 def copy_calibration():
     """A plain device copy of known size, for calibrating HBM byte counters."""
     import torch
@@ -299,6 +408,9 @@ def main():
         return
     if args.swap:
         swap_bench(args)
+        return
+    if args.prefill:
+        prefill_bench(args)
         return
     if args.prefix_cache:
         prefix_cache_bench(args)

@@ -484,25 +484,38 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
 // =====================================================================
 // The decode matrix-core step with its 16 columns taken by (query token,
 // query head) pairs of one KV head instead of by query heads: column c of a
-// tile is token c / G of the sequence's chunk and head g G + c % G.  Token k
+// sequence's chunk is token c / G of the chunk and head g G + c % G.  Token k
 // of a chunk of n sits at position ctx - n + k and sees positions 0 .. ctx -
-// n + k, so each column masks the keys at or past its own limit; the tile
-// streams K/V up to its last column's limit once for all 16 columns.  Four
-// waves share the steps and merge through LDS, as the single-pass decode.
+// n + k, so each column masks the keys at or past its own limit.
+// Every wave owns kPrefillNT tiles of 16 columns and streams all of their
+// keys itself: each K/V step it loads is widened once and feeds the products
+// of all its tiles, and the wave writes its columns' outputs from registers
+// (no cross-wave merge).  The four waves of a workgroup take consecutive
+// column spans of one (sequence, KV head), so they read the same keys at
+// about the same time and share them through L2.  kPrefillBuf steps of K/V
+// are in registers: one computed, the others in flight.  The streaming
+// softmax keeps a reference max per column that is raised only when a logit
+// exceeds it by kPrefillSlack (log2 units), so the accumulators are rescaled
+// a few times per column instead of at every step.
+constexpr int kPrefillNT = 2;          // 16-column tiles per wave
+constexpr int kPrefillBuf = 3;         // K/V steps held per wave
+constexpr float kPrefillSlack = 8.0f;  // p < 2^8 between rescales
+
 struct PrefillParams {
   DecodeParams d;             // q [T][Hq][D] (or the folded q), out [T][Hq][D], pool layer, tables, lengths
   const int32_t* qstart;      // [S + 1]: sequence s's queries are rows qstart[s] .. qstart[s+1] - 1
-  int32_t tiles;              // column tiles per (sequence, KV head): ceil(max_query_len * G / 16)
+  int32_t tiles;              // workgroup column spans per (sequence, KV head):
+                              // ceil(max_query_len * G / (16 kPrefillNT kNW))
   int32_t T;                  // rows of q and out
 };
 
 template <int D, int KVT, int B>
 __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillParams pp) {
+  constexpr int NT = kPrefillNT;
+  constexpr int NB = kPrefillBuf;
   const DecodeParams& p = pp.d;
   using T = Tile<D, KVT>;
   constexpr int E = T::E;
-  __shared__ float sm_ml[kNW][2][16];
-  __shared__ float sm_acc[kNW][16][D + 4];
 
   const int nwg = (int)gridDim.x;
   const int xcd = (int)blockIdx.x % 8;
@@ -512,106 +525,152 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
   const int ct = item % pp.tiles;
   const int g = (item / pp.tiles) % p.Hkv;
   const int s = item / (pp.tiles * p.Hkv);
-  // query rows, kept inside [0, T) whatever query_start holds
-  const int q0 = min(max(pp.qstart[s], 0), pp.T);
-  const int n = min(max(pp.qstart[s + 1], q0), pp.T) - q0;
-  const int ncol = n * p.G;
-  const int c0 = ct * 16;
-  if (c0 >= ncol) return;
-  const int cols = min(16, ncol - c0);
-
   const int lane = threadIdx.x % kWave;
   const int w = threadIdx.x / kWave;
   const int row = lane & 15;
   const int j = lane >> 4;
+  // query rows, kept inside [0, T) whatever query_start holds
+  const int q0 = min(max(pp.qstart[s], 0), pp.T);
+  const int n = min(max(pp.qstart[s + 1], q0), pp.T) - q0;
+  const int ncol = n * p.G;
+  const int c0 = (ct * kNW + w) * 16 * NT;       // this wave's first column
+  if (c0 >= ncol) return;                        // no barrier follows: waves are independent
+  const int cols = min(16 * NT, ncol - c0);
+
   const int ctx = clamp_ctx(p.ctx[s], p.W * B);
-  // this lane's column (columns past the tile's last read column 0's query)
-  const int c = c0 + (row < cols ? row : 0);
-  const int kq = c / p.G;
-  const int hq = g * p.G + c % p.G;
-  const int lim = row < cols ? max(0, ctx - n + kq + 1) : 0;     // keys [0, lim)
-  const int t_end = max(0, ctx - n + (c0 + cols - 1) / p.G + 1);  // the tile's largest limit
+  const int first = ctx - n;                     // position of the chunk's token 0
+  const int t_end = max(0, first + (c0 + cols - 1) / p.G + 1);   // the wave's largest limit
   const int nsteps = (t_end + kStep - 1) / kStep;
   const int32_t* bt_row = p.bt + (int64_t)s * p.W;
 
-  bf16x8 qop[T::KK];
-  {
-    const uint16_t* qh = p.q + ((int64_t)(q0 + kq) * p.Hq + hq) * p.q_stride;
+  // per tile: this lane's column limit (keys [0, lim)) and the query as the
+  // B operand (columns past the chunk read column c0's query, limit 0)
+  bf16x8 qop[NT][T::KK];
+  int lim[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int cl = 16 * nt + row;
+    const bool valid = cl < cols;
+    const int c = c0 + (valid ? cl : 0);
+    lim[nt] = valid ? max(0, first + c / p.G + 1) : 0;
+    const uint16_t* qh = p.q + ((int64_t)(q0 + c / p.G) * p.Hq + g * p.G + c % p.G) * p.q_stride;
 #pragma unroll
     for (int kk = 0; kk < T::KK; ++kk)
-      qop[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + q_dim0<E>(kk, j)));
+      qop[nt][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + q_dim0<E>(kk, j)));
   }
 
-  f32x4 acc[T::NC];
+  f32x4 acc[NT][T::NC];
+  float m_run[NT], l_run[NT];   // reference max of scaled logits (log2 domain) and partial sum, column `row`
 #pragma unroll
-  for (int cc = 0; cc < T::NC; ++cc) acc[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;   // running max of scaled logits (log2 domain), column `row`
-  float l_run = 0.f;
+  for (int nt = 0; nt < NT; ++nt) {
+    m_run[nt] = -INFINITY;
+    l_run[nt] = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < T::NC; ++cc) acc[nt][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
-  auto compute = [&](const StepRegs<D, KVT>& r, int tok0) {
-    f32x4 z[2];
+  auto compute = [&](StepRegs<D, KVT>& r, int tok0) __attribute__((always_inline)) {
+    // K operands, widened once for every tile
+    bf16x8 ka[2][T::KK];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      f32x4 acc_z = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < T::KK; ++kk) {
-        bf16x8 a;
         if constexpr (E == 2) {
-          a = __builtin_bit_cast(bf16x8, r.k[h][kk]);
+          ka[h][kk] = __builtin_bit_cast(bf16x8, r.k[h][kk]);
         } else {
           const u32x4 wv = r.k[h][kk >> 1];
-          a = (kk & 1) ? widen8<KVT>(wv[2], wv[3]) : widen8<KVT>(wv[0], wv[1]);
+          ka[h][kk] = (kk & 1) ? widen8<KVT>(wv[2], wv[3]) : widen8<KVT>(wv[0], wv[1]);
         }
-        acc_z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[kk], acc_z, 0, 0, 0);
-      }
-      z[h] = acc_z;
-    }
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = tok0 + 16 * h + 4 * j + i;
-        float zz = z[h][i] * p.qk_scale;
-        if constexpr (KVT == PKV_KV_INT8) zz *= r.ksc[h][i];
-        zz = t < lim ? zz : -INFINITY;          // causal: this column's keys only
-        z[h][i] = zz;
-        mloc = fmaxf(mloc, zz);
       }
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-    const float m_new = fmaxf(m_run, mloc);
-    // a column with no key yet keeps max -inf; exponents then use 0 so that
-    // its p and rescale factor are 0, not NaN
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    float psum = 0.f;
-    uint32_t ph[2][2], pl[2][2];
+    f32x4 z[NT][2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float pv[4];
+    for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pv[i] = __builtin_amdgcn_exp2f(z[h][i] - m_use);
-        psum += pv[i];
-        if constexpr (KVT == PKV_KV_INT8) {
+      for (int h = 0; h < 2; ++h) {
+        f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < T::KK; ++kk) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[h][kk], qop[nt][kk], c, 0, 0, 0);
+        z[nt][h] = c;
+      }
+    }
+    float alpha[NT], m_use[NT];
+    bool any_rescale = false;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
           const int t = tok0 + 16 * h + 4 * j + i;
-          pv[i] = t < lim ? pv[i] * r.vsc[h][i] : 0.f;   // fold the V scale into p
+          float zz = z[nt][h][i] * p.qk_scale;
+          if constexpr (KVT == PKV_KV_INT8) zz *= r.ksc[h][i];
+          zz = t < lim[nt] ? zz : -INFINITY;     // causal: this column's keys only
+          z[nt][h][i] = zz;
+          mloc = fmaxf(mloc, zz);
         }
       }
-      ph[h][0] = pack_bf16x2(pv[0], pv[1]);
-      ph[h][1] = pack_bf16x2(pv[2], pv[3]);
-      pl[h][0] = pack_bf16x2(pv[0] - bf16_lo(ph[h][0]), pv[1] - bf16_hi(ph[h][0]));
-      pl[h][1] = pack_bf16x2(pv[2] - bf16_lo(ph[h][1]), pv[3] - bf16_hi(ph[h][1]));
+      mloc = max_x32(max_x16(mloc));           // the column's max over the step
+      const bool bump = mloc > m_run[nt] + kPrefillSlack;   // false while the column has no key
+      const float m_ref = bump ? mloc : m_run[nt];
+      alpha[nt] = bump ? __builtin_amdgcn_exp2f(m_run[nt] - m_ref) : 1.0f;
+      any_rescale |= bump && m_run[nt] > -INFINITY;   // the accumulator is zero until the first raise
+      m_run[nt] = m_ref;
+      // a column with no key yet keeps reference -inf; its exponents use 0 so
+      // that p is 0, not NaN
+      m_use[nt] = m_ref == -INFINITY ? 0.f : m_ref;
     }
-    l_run = l_run * alpha + psum;
-    const bf16x8 pop = __builtin_bit_cast(bf16x8, u32x4{ph[0][0], ph[0][1], ph[1][0], ph[1][1]});
-    const bf16x8 pop_lo = __builtin_bit_cast(bf16x8, u32x4{pl[0][0], pl[0][1], pl[1][0], pl[1][1]});
-    // keys past the tile's largest limit may be unwritten slots (any bits):
-    // their V is zeroed; keys below it are written data, masked by p = 0
-    const bool edge = tok0 + kStep > t_end;
+    if (__builtin_amdgcn_ballot_w64(any_rescale)) {   // uniform branch, rarely taken
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int cc = 0; cc < T::NC; ++cc) acc[nt][cc] = acc[nt][cc] * alpha[nt];
+    }
+    // keys at or past the wave's largest limit may be unwritten slots (any
+    // bits): their V is zeroed, in the step's own registers (the next load
+    // overwrites them anyway); keys below it are written data, masked by p = 0
+    if (tok0 + kStep > t_end) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int tb = tok0 + 16 * h + 4 * j;      // lane j's 4 tokens of the chunk
+#pragma unroll
+        for (int u = 0; u < T::VLOADS; ++u) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // bf16: word e holds tokens tb + 2 (e % 2) and + 1 of one dim; 8-bit: tokens tb .. tb + 3
+            r.v[h][u][e] &= E == 2 ? tok_mask16(tb + 2 * (e & 1), 0, t_end) : tok_mask8(tb, 0, t_end);
+          }
+        }
+      }
+    }
+    bf16x8 pop[NT], pop_lo[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float psum = 0.f;
+      uint32_t ph[2][2], pl[2][2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[i] = __builtin_amdgcn_exp2f(z[nt][h][i] - m_use[nt]);
+          psum += pv[i];
+          if constexpr (KVT == PKV_KV_INT8) {
+            const int t = tok0 + 16 * h + 4 * j + i;
+            pv[i] = t < lim[nt] ? pv[i] * r.vsc[h][i] : 0.f;   // fold the V scale into p
+          }
+        }
+        ph[h][0] = pack_bf16x2(pv[0], pv[1]);
+        ph[h][1] = pack_bf16x2(pv[2], pv[3]);
+        pl[h][0] = pack_bf16x2(pv[0] - bf16_lo(ph[h][0]), pv[1] - bf16_hi(ph[h][0]));
+        pl[h][1] = pack_bf16x2(pv[2] - bf16_lo(ph[h][1]), pv[3] - bf16_hi(ph[h][1]));
+      }
+      l_run[nt] = l_run[nt] * alpha[nt] + psum;
+      pop[nt] = __builtin_bit_cast(bf16x8, u32x4{ph[0][0], ph[0][1], ph[1][0], ph[1][1]});
+      pop_lo[nt] = __builtin_bit_cast(bf16x8, u32x4{pl[0][0], pl[0][1], pl[1][0], pl[1][1]});
+    }
 #pragma unroll
     for (int cc = 0; cc < T::NC; ++cc) {
       uint32_t a0, a1, a2, a3;
@@ -626,66 +685,67 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
         widen4<KVT>(r.v[0][u][e], a0, a1);
         widen4<KVT>(r.v[1][u][e], a2, a3);
       }
-      if (edge) {
-        const int tb0 = tok0 + 4 * j, tb1 = tok0 + 16 + 4 * j;
-        a0 &= tok_mask16(tb0, 0, t_end);
-        a1 &= tok_mask16(tb0 + 2, 0, t_end);
-        a2 &= tok_mask16(tb1, 0, t_end);
-        a3 &= tok_mask16(tb1 + 2, 0, t_end);
+      const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{a0, a1, a2, a3});
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[nt][cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop[nt], acc[nt][cc], 0, 0, 0);
+        acc[nt][cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_lo[nt], acc[nt][cc], 0, 0, 0);
       }
-      const bf16x8 aop = __builtin_bit_cast(bf16x8, u32x4{a0, a1, a2, a3});
-      acc[cc] = acc[cc] * alpha;
-      acc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, pop, acc[cc], 0, 0, 0);
-      acc[cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, pop_lo, acc[cc], 0, 0, 0);
     }
   };
 
-  // wave w takes steps w, w + NW, ...; loads run one step ahead
-  StepRegs<D, KVT> r0, r1;
-  int i = w;
-  if (i < nsteps) issue_step<D, KVT, B>(r0, p, bt_row, g, i * kStep, 0, lane);
+  // NB - 1 steps in flight ahead of the one computed.  Every iteration issues
+  // the same loads (a step past the end reads a tile the table clamps into
+  // the pool, unused) so that each wait covers exactly one step's loads.
+  StepRegs<D, KVT> r[NB];
+  static_for<NB - 1>([&](auto b) __attribute__((always_inline)) {
+    issue_step<D, KVT, B>(r[b], p, bt_row, g, (int)b * kStep, 0, lane);
+  });
+  int i = 0;
   while (i < nsteps) {
-    int nx = i + kNW;
-    if (nx < nsteps) issue_step<D, KVT, B>(r1, p, bt_row, g, nx * kStep, 0, lane);
-    compute(r0, i * kStep);
-    i = nx;
-    if (i >= nsteps) break;
-    nx = i + kNW;
-    if (nx < nsteps) issue_step<D, KVT, B>(r0, p, bt_row, g, nx * kStep, 0, lane);
-    compute(r1, i * kStep);
-    i = nx;
+    static_for<NB>([&](auto b) __attribute__((always_inline)) {   // buffer indices are constants
+      if (i < nsteps) {
+        issue_step<D, KVT, B>(r[(b + NB - 1) % NB], p, bt_row, g, (i + NB - 1) * kStep, 0, lane);
+        compute(r[b], i * kStep);
+        ++i;
+      }
+    });
   }
 
-  // merge the waves per column through LDS
-  l_run += __shfl_xor(l_run, 16, kWave);
-  l_run += __shfl_xor(l_run, 32, kWave);
-  if (j == 0) {
-    sm_ml[w][0][row] = m_run;
-    sm_ml[w][1][row] = l_run;
-  }
+  // outputs: column `row` of tile nt; this lane holds dims acc_dim(cc, j, .)
 #pragma unroll
-  for (int cc = 0; cc < T::NC; ++cc) {
+  for (int nt = 0; nt < NT; ++nt) {
+    const int cl = 16 * nt + row;
+    const float L = sum_x32(sum_x16(l_run[nt]));
+    if (cl >= cols) continue;
+    const int cq = c0 + cl;
+    float* orow = p.out + ((int64_t)(q0 + cq / p.G) * p.Hq + g * p.G + cq % p.G) * D;
+    const float inv = L > 0.f ? 1.f / L : 0.f;   // no key at all (position < 0): zero row
+    float o[T::NC][4];
 #pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) sm_acc[w][row][acc_dim<E>(cc, j, i2)] = acc[cc][i2];
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < cols * D; idx += blockDim.x) {
-    const int col = idx / D;
-    const int d = idx % D;
-    float M = -INFINITY;
+    for (int cc = 0; cc < T::NC; ++cc)
 #pragma unroll
-    for (int ww = 0; ww < kNW; ++ww) M = fmaxf(M, sm_ml[ww][0][col]);
-    float L = 0.f, A = 0.f;
+      for (int i2 = 0; i2 < 4; ++i2) {
+        const int d = acc_dim<E>(cc, j, i2);
+        o[cc][i2] = acc[nt][cc][i2] * inv * (p.vs_ch ? p.vs_ch[g * D + d] : p.out_scale);
+      }
+    if constexpr (E == 2) {
+      // tiles 2u, 2u + 1 hold dims 32u + 8j + 2 i2 + {0, 1}: 8 consecutive floats
 #pragma unroll
-    for (int ww = 0; ww < kNW; ++ww) {
-      const float mw = sm_ml[ww][0][col];
-      const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      L += f * sm_ml[ww][1][col];
-      A += f * sm_acc[ww][col][d];
+      for (int u = 0; u < T::NC / 2; ++u) {
+        float* dst = orow + 32 * u + 8 * j;
+        *reinterpret_cast<f32x4*>(dst) = f32x4{o[2 * u][0], o[2 * u + 1][0], o[2 * u][1], o[2 * u + 1][1]};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[2 * u][2], o[2 * u + 1][2], o[2 * u][3], o[2 * u + 1][3]};
+      }
+    } else {
+      // tiles 4u .. 4u + 3 hold dims 64u + 16j + 4 i2 + {0 .. 3}
+#pragma unroll
+      for (int u = 0; u < T::NC / 4; ++u)
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2)
+          *reinterpret_cast<f32x4*>(orow + 64 * u + 16 * j + 4 * i2) =
+              f32x4{o[4 * u][i2], o[4 * u + 1][i2], o[4 * u + 2][i2], o[4 * u + 3][i2]};
     }
-    const int cq = c0 + col;
-    const int64_t orow = (int64_t)(q0 + cq / p.G) * p.Hq + g * p.G + cq % p.G;
-    p.out[orow * D + d] = L > 0.f ? A / L * (p.vs_ch ? p.vs_ch[g * D + d] : p.out_scale) : 0.f;
   }
 }
 
@@ -2139,7 +2199,8 @@ extern "C" pkv_status paged_attn_prefill(float* out, const void* q, const pkv_po
   if (channel && (const void*)out == q)
     return fail(PKV_ERR_INVALID, "out must not alias q for storage with per-channel scales");
   const int32_t G = num_q_heads / c.num_kv_heads;
-  const int64_t tiles = ((int64_t)max_query_len * G + 15) / 16;
+  const int64_t span = 16 * kPrefillNT * kNW;   // columns per workgroup
+  const int64_t tiles = ((int64_t)max_query_len * G + span - 1) / span;
   const int64_t items = (int64_t)num_seqs * c.num_kv_heads * tiles;
   if (items > INT32_MAX / 2) return fail(PKV_ERR_INVALID, "too many query tiles in one call");
   const uint64_t scale_layer = channel ? (uint64_t)c.num_kv_heads * c.head_dim

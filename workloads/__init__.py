@@ -20,6 +20,10 @@ Shapes follow the pages' worked examples:
                     §3.2), each generating 64..512 further tokens.
 * ``long_quant``  - 8 sequences of 32768 tokens, 64 query / 8 KV heads,
                     32-token blocks, FP8-e5m2 or INT8 storage.
+* ``prefix_prefill`` - 200 requests = a 1500-token system prompt (bjdmk.com.cn
+                    article §3.2) + 64..512 private tokens, 70B-shaped heads;
+                    the prompt's 93 full blocks come from the prefix cache
+                    and are shared, the rest of every prompt is prefilled.
 
 Values are fp32 N(0, 1) draws rounded to bf16 (round-to-nearest-even via
 torch), carried as uint16 bit patterns.  Seeds: numpy SeedSequence(436000 +
@@ -155,6 +159,39 @@ def long_quant(kv_dtype: int = KV_FP8_E5M2, num_seqs: int = 8,
                  np.zeros(nb, np.int32), math.ceil(ctx_len / B), partition_size=512)
     r = w.streams()
     w.block_order = r[1].permutation(nb).astype(np.int32)
+    return w
+
+
+def prefix_prefill(num_seqs: int = 200, prefix: int = 1500, lo: int = 64, hi: int = 512,
+                   num_q_heads: int = 64, num_kv_heads: int = 8, head_dim: int = 128) -> Workload:
+    """Prefill after a prefix-cache hit: every prompt is the shared system
+    prompt plus its own tokens; the prompt's full blocks are cached and shared
+    (one physical copy, the first ``prefix // 16`` table entries of every
+    sequence), and each sequence's chunk is everything after them.
+    ``context_lens`` = prompt lengths; ``extra['chunk']`` = tokens to prefill;
+    ``extra['tables']`` = int32 [S, W] block tables."""
+    B = 16
+    ss = np.random.SeedSequence(436000 + 6)
+    r0 = np.random.default_rng(ss.spawn(1)[0])
+    own = r0.integers(lo, hi, size=num_seqs, endpoint=True).astype(np.int32)
+    ctx = (prefix + own).astype(np.int32)
+    shared = prefix // B
+    private = [math.ceil(int(c) / B) - shared for c in ctx]
+    nb = shared + int(sum(private))
+    W = math.ceil((prefix + hi) / B)
+    w = Workload("prefix_prefill", 6, num_seqs, num_q_heads, num_kv_heads, head_dim, B, 1, KV_BF16, ctx, nb,
+                 np.zeros(nb, np.int32), W)
+    r = w.streams()
+    w.block_order = r[1].permutation(nb).astype(np.int32)
+    tables = np.zeros((num_seqs, W), dtype=np.int32)
+    tables[:, :shared] = w.block_order[:shared]
+    pos = shared
+    for s, n in enumerate(private):
+        tables[s, shared:shared + n] = w.block_order[pos:pos + n]
+        pos += n
+    w.extra["tables"] = tables
+    w.extra["chunk"] = (ctx - shared * B).astype(np.int32)
+    w.extra["prefix"] = prefix
     return w
 
 
