@@ -497,8 +497,8 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
 // softmax keeps a reference max per column that is raised only when a logit
 // exceeds it by kPrefillSlack (log2 units), so the accumulators are rescaled
 // a few times per column instead of at every step.
-constexpr int kPrefillNT = 2;          // 16-column tiles per wave
-constexpr int kPrefillBuf = 3;         // K/V steps held per wave
+constexpr int kPrefillNT = 1;          // 16-column tiles per wave
+constexpr int kPrefillBuf = 2;         // K/V steps held per wave
 constexpr float kPrefillSlack = 8.0f;  // p < 2^8 between rescales
 
 struct PrefillParams {
