@@ -30,6 +30,10 @@ CXX_SOURCES = ["pool.cpp", "block_manager.cpp"]
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core operands and results in ordinary VGPRs: without it the
+    # register allocator parks accumulators and K/V buffers in AGPRs and
+    # copies them back for every vector instruction that touches them
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function",
 ]
 CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__"]

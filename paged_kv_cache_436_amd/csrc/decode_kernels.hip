@@ -925,13 +925,15 @@ __device__ __forceinline__ void issue_chunks(SplitBuf<D, KVT>& r, const SplitPar
     const int toff = (B < 16 || !live) ? 0 : t % B;
     const int tk = toff + (row & TM);
     const int tv = toff + ((4 * j) & TM);
-    const int64_t tilek = live ? ((int64_t)pk * p.Hkv + g) : 0;
-    const int64_t tilev = live ? ((int64_t)pv * p.Hkv + g) : 0;
+    // tile numbers are below num_blocks * Hkv < 2^31: unsigned 32-bit
+    // products widened once keep the address arithmetic short
+    const uint32_t tilek = live ? (uint32_t)pk * (uint32_t)p.Hkv + (uint32_t)g : 0u;
+    const uint32_t tilev = live ? (uint32_t)pv * (uint32_t)p.Hkv + (uint32_t)g : 0u;
     if constexpr (GE::I4) {
       // K piece (j, token), V piece (token group, dim row): D / 8 bytes each
       constexpr int P = D / 8;
-      const char* kt = p.k + tilek * (int64_t)(B * D / 2);
-      const char* vt = p.v + tilev * (int64_t)(B * D / 2);
+      const char* kt = p.k + (uint64_t)tilek * (uint32_t)(B * D / 2);
+      const char* vt = p.v + (uint64_t)tilev * (uint32_t)(B * D / 2);
       const char* ka = kt + (j * B + tk) * P;
       const char* va = vt + ((tv >> 2) * 16 + row) * P;
       if constexpr (P == 16) {
@@ -945,8 +947,8 @@ __device__ __forceinline__ void issue_chunks(SplitBuf<D, KVT>& r, const SplitPar
       }
       continue;
     }
-    const char* kt = p.k + tilek * (int64_t)(B * D * E);
-    const char* vt = p.v + tilev * (int64_t)(B * D * E);
+    const char* kt = p.k + (uint64_t)tilek * (uint32_t)(B * D * E);
+    const char* vt = p.v + (uint64_t)tilev * (uint32_t)(B * D * E);
 #pragma unroll
     for (int u = 0; u < GE::LPC; ++u) r.k[h][u] = ld16(kt + ((4 * u + j) * B + tk) * 16);
     const int grp = tv >> 2;
@@ -956,7 +958,7 @@ __device__ __forceinline__ void issue_chunks(SplitBuf<D, KVT>& r, const SplitPar
       r.v[h][u] = ld16(vt + (grp * D + d) * 4 * E);
     }
     if constexpr (KVT == PKV_KV_INT8) {
-      const int64_t so = tilev * B + tv;
+      const uint64_t so = (uint64_t)tilev * B + tv;
       r.ksc[h] = *reinterpret_cast<const f32x4*>(p.ks + so);
       r.vsc[h] = *reinterpret_cast<const f32x4*>(p.vs + so);
     }
