@@ -252,7 +252,7 @@ __device__ __forceinline__ void issue_step(StepRegs<D, KVT>& r, const DecodePara
     int ph[2];
 #pragma unroll
     for (int b = 0; b < (B < 16 ? 2 : 1); ++b) {
-      int lb = t / B + b;
+      int lb = (int)((uint32_t)t / B) + b;         // tokens are never negative
       lb = lb < p.W ? lb : p.W - 1;                // never index past the table row
       const int e = used ? bt_row[lb] : 0;
       ph[b] = e < 0 ? 0 : (e >= p.num_blocks ? p.num_blocks - 1 : e);  // stay inside the pool
@@ -265,23 +265,27 @@ __device__ __forceinline__ void issue_step(StepRegs<D, KVT>& r, const DecodePara
     // chunks start at multiples of 16 tokens: with B >= 16 the chunk sits at
     // offset t % B of one block, with B = 8 it starts both of its blocks
     constexpr int TM = (B < 16 ? B : 16) - 1;
-    const int toff = B < 16 ? 0 : t % B;
+    const int toff = B < 16 ? 0 : (int)((uint32_t)t % B);
     const int tk = toff + (row & TM);              // token of lane row inside its block
     const int tv = toff + ((4 * j) & TM);          // first token of lane j's group inside its block
-    const char* kt = p.k + ((int64_t)phk * p.Hkv + g) * (int64_t)(B * D * E);
-    const char* vt = p.v + ((int64_t)phv * p.Hkv + g) * (int64_t)(B * D * E);
+    // tile numbers are below num_blocks * Hkv < 2^31: unsigned 32-bit
+    // products widened once keep the address arithmetic short
+    const uint32_t tilek = (uint32_t)phk * (uint32_t)p.Hkv + (uint32_t)g;
+    const uint32_t tilev = (uint32_t)phv * (uint32_t)p.Hkv + (uint32_t)g;
+    const char* kt = p.k + (uint64_t)tilek * (uint32_t)(B * D * E);
+    const char* vt = p.v + (uint64_t)tilev * (uint32_t)(B * D * E);
     // K: piece c holds dims [X*c, X*c+X) of all B tokens, 16 bytes per token
 #pragma unroll
-    for (int u = 0; u < T::KLOADS; ++u) r.k[h][u] = ld16(kt + ((int64_t)((4 * u + j) * B + tk)) * 16);
+    for (int u = 0; u < T::KLOADS; ++u) r.k[h][u] = ld16(kt + (uint32_t)((4 * u + j) * B + tk) * 16u);
     // V: token group tv / 4, 4 tokens x dims as 4E-byte words
     const int grp = tv >> 2;
 #pragma unroll
     for (int u = 0; u < T::VLOADS; ++u) {
       const int d = (E == 2) ? (32 * u + 2 * row) : (64 * u + 4 * row);
-      r.v[h][u] = ld16(vt + ((int64_t)(grp * D + d)) * 4 * E);
+      r.v[h][u] = ld16(vt + (uint32_t)(grp * D + d) * (uint32_t)(4 * E));
     }
     if constexpr (KVT == PKV_KV_INT8) {
-      const int64_t so = ((int64_t)phv * p.Hkv + g) * B + tv;
+      const uint64_t so = (uint64_t)tilev * B + tv;
       r.ksc[h] = *reinterpret_cast<const f32x4*>(p.ks + so);
       r.vsc[h] = *reinterpret_cast<const f32x4*>(p.vs + so);
     }
@@ -541,6 +545,9 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
   const int first = ctx - n;                     // position of the chunk's token 0
   const int t_end = max(0, first + (c0 + cols - 1) / p.G + 1);   // the wave's largest limit
   const int nsteps = (t_end + kStep - 1) / kStep;
+  // every valid column sees the keys below this one (column c0's limit, the
+  // smallest): steps wholly below it need no causal mask
+  const int lim_lo = max(0, first + c0 / p.G + 1);
   const int32_t* bt_row = p.bt + (int64_t)s * p.W;
 
   // per tile: this lane's column limit (keys [0, lim)) and the query as the
@@ -597,22 +604,44 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
     }
     float alpha[NT], m_use[NT];
     bool any_rescale = false;
+    // raw logits (int8: times the token's K scale); the softmax scale s > 0
+    // is applied to the max and inside the exponent's fma, max(z) s = max(z s)
+    const bool unmasked = tok0 + kStep <= lim_lo;   // uniform
+    float mlocs[NT];
+    if (unmasked) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (KVT == PKV_KV_INT8) z[nt][h][i] *= r.ksc[h][i];
+            mloc = fmaxf(mloc, z[nt][h][i]);
+          }
+        mlocs[nt] = mloc;
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = tok0 + 16 * h + 4 * j + i;
+            float zz = z[nt][h][i];
+            if constexpr (KVT == PKV_KV_INT8) zz *= r.ksc[h][i];
+            zz = t < lim[nt] ? zz : -INFINITY;     // causal: this column's keys only
+            z[nt][h][i] = zz;
+            mloc = fmaxf(mloc, zz);
+          }
+        mlocs[nt] = mloc;
+      }
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = tok0 + 16 * h + 4 * j + i;
-          float zz = z[nt][h][i] * p.qk_scale;
-          if constexpr (KVT == PKV_KV_INT8) zz *= r.ksc[h][i];
-          zz = t < lim[nt] ? zz : -INFINITY;     // causal: this column's keys only
-          z[nt][h][i] = zz;
-          mloc = fmaxf(mloc, zz);
-        }
-      }
-      mloc = max_x32(max_x16(mloc));           // the column's max over the step
+      const float mloc = max_x32(max_x16(mlocs[nt])) * p.qk_scale;   // the column's scaled max over the step
       const bool bump = mloc > m_run[nt] + kPrefillSlack;   // false while the column has no key
       const float m_ref = bump ? mloc : m_run[nt];
       alpha[nt] = bump ? __builtin_amdgcn_exp2f(m_run[nt] - m_ref) : 1.0f;
@@ -655,11 +684,11 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
         float pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pv[i] = __builtin_amdgcn_exp2f(z[nt][h][i] - m_use[nt]);
+          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[nt][h][i], p.qk_scale, -m_use[nt]));
           psum += pv[i];
           if constexpr (KVT == PKV_KV_INT8) {
             const int t = tok0 + 16 * h + 4 * j + i;
-            pv[i] = t < lim[nt] ? pv[i] * r.vsc[h][i] : 0.f;   // fold the V scale into p
+            pv[i] = (unmasked || t < lim[nt]) ? pv[i] * r.vsc[h][i] : 0.f;   // fold the V scale into p
           }
         }
         ph[h][0] = pack_bf16x2(pv[0], pv[1]);
