@@ -86,18 +86,21 @@ def parse():
 
 
 PROFILE = os.path.join(ROOT, "profiles", "pa_split_kernel_llama70b_bf16.md")
-KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_436_amd", "csrc", "decode_kernels.hip")
+# the sources the split decode kernel is compiled from, hashed in this order
+KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_436_amd", "csrc", f)
+               for f in ("decode_kernels.hip", "decode_common.h", "pkv_codecs.h")]
 
 
 def measured_traffic():
     """HBM bytes per decode launch from the committed rocprofv3 counter
-    summary, or None when the kernel source has changed since the counters
-    were taken (the summary records the source's sha256)."""
+    summary, or None when the kernel's sources have changed since the
+    counters were taken (the summary records the sha256 of the sources
+    concatenated)."""
     import hashlib
     import re
     try:
         text = open(PROFILE, encoding="utf-8").read()
-        src = open(KERNEL_SRC, "rb").read()
+        src = b"".join(open(f, "rb").read() for f in KERNEL_SRCS)
     except OSError:
         return None
     m = re.search(r"traffic_bytes_per_launch = (\d+); kernel_source_sha256 = ([0-9a-f]{64})", text)

@@ -268,8 +268,9 @@ pkv_status paged_attn_decode(float* out, const void* q, const pkv_pool* pool, in
  * itself included.  This is the prefill that prefix caching leaves to do: the
  * cached prompt prefix is reused and only the rest is computed ([BJD] §4.1;
  * [KVP] §五); a whole prompt is the case n_s = ctx_s, a decode step the case
- * n_s = 1.  Same arithmetic and storage types as paged_attn_decode's
- * single-pass form (not INT4: PKV_ERR_UNSUPPORTED).
+ * n_s = 1.  Every storage type of the pool, with the arithmetic of
+ * paged_attn_decode (INT4 and per-channel INT8: the K channel scales are
+ * folded into the query first).
  *   out           device fp32 [T][Hq][D], T = num_queries = query_start[S]
  *   q             device bf16 [T][Hq][D]
  *   query_start   device int32 [S + 1], non-decreasing, query_start[0] = 0

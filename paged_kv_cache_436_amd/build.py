@@ -24,7 +24,7 @@ LIB = os.path.join(HERE, "libpkv.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["cache_kernels.hip", "decode_kernels.hip"]
+HIP_SOURCES = ["cache_kernels.hip", "decode_kernels.hip", "prefill_kernels.hip"]
 CXX_SOURCES = ["pool.cpp", "block_manager.cpp"]
 
 HIPCC_FLAGS = [

@@ -33,265 +33,19 @@
 //       range inside one row.  The wave that completes a row combines the
 //       row's partials:
 //           out = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k,  M = max m_k.
-#include <hip/hip_runtime.h>
-
 #include <atomic>
-#include <utility>
 #include <chrono>
 #include <mutex>
 
-#include "pkv_codecs.h"
-#include "pkv_internal.h"
+#include "decode_common.h"
 
 namespace pkv {
 namespace {
 
-constexpr int kWave = 64;
-constexpr int kNW = 4;            // wavefronts per workgroup
-constexpr int kStep = 32;         // tokens per step of the single-pass kernel
-constexpr float kLog2e = 1.4426950408889634f;
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ u32x4 ld16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
-
-// Two e5m2 bytes (16-bit half HI of w) -> two bf16, exact.
-template <bool HI>
-__device__ __forceinline__ uint32_t e5m2x2_to_bf16x2(uint32_t w) {
-  bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI);
-  return __builtin_bit_cast(uint32_t, r);
-}
-
-// Two floats -> packed bf16x2 (round to nearest even; exact for int8 codes).
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  bf16x2 r;
-  r[0] = (__bf16)a;
-  r[1] = (__bf16)b;
-  return __builtin_bit_cast(uint32_t, r);
-}
-
-// The bf16 in the low / high half of a packed pair, as fp32 (exact).
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Four bytes of w (byte i = token or dim i) -> 4 bf16 in 2 dwords.
-template <int KVT>
-__device__ __forceinline__ void widen4(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  if constexpr (KVT == PKV_KV_FP8_E5M2) {
-    lo = e5m2x2_to_bf16x2<false>(w);
-    hi = e5m2x2_to_bf16x2<true>(w);
-  } else {
-    const float c0 = (float)(int8_t)(w & 0xff);
-    const float c1 = (float)(int8_t)((w >> 8) & 0xff);
-    const float c2 = (float)(int8_t)((w >> 16) & 0xff);
-    const float c3 = (float)(int8_t)(w >> 24);
-    lo = pack_bf16x2(c0, c1);
-    hi = pack_bf16x2(c2, c3);
-  }
-}
-
-// 8 bytes (two dwords) -> 8 bf16 operand (dims d..d+7 of one token).
-template <int KVT>
-__device__ __forceinline__ bf16x8 widen8(uint32_t w0, uint32_t w1) {
-  uint32_t a, b, c, d;
-  widen4<KVT>(w0, a, b);
-  widen4<KVT>(w1, c, d);
-  return __builtin_bit_cast(bf16x8, u32x4{a, b, c, d});
-}
-
-// Wave-uniform read of memory that no kernel of this launch writes (block
-// tables, context lengths): through the constant address space it becomes a
-// scalar load, which does not occupy the vector-memory counter that the K/V
-// prefetch pipeline waits on.
-__device__ __forceinline__ int32_t uniform_load(const int32_t* p) {
-  return *(const __attribute__((address_space(4))) int32_t*)p;
-}
-
-// Combine each lane's value with that of lane ^ 16 / lane ^ 32 (the other
-// token groups of the same head in the MFMA accumulator layout).  gfx950's
-// row / half swaps do this in the VALU, without an LDS round trip.
-__device__ __forceinline__ float max_x16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float max_x32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_x16(float x) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float sum_x32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maximum).
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>).
-template <class F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-__device__ __forceinline__ int clamp_ctx(int c, int max_ctx) { return c < 0 ? 0 : (c > max_ctx ? max_ctx : c); }
-
-// Sliding window: a row of context ctx attends to positions [lo, ctx),
-// lo = ctx - win when a window of win > 0 positions is set and shorter than
-// the context, else 0.  The row's steps of TS tokens start at the step that
-// holds lo (token base = floor(lo / TS) * TS); blocks before it are not read.
-__device__ __forceinline__ int window_lo(int ctx, int win) { return (win > 0 && ctx > win) ? ctx - win : 0; }
-template <int TS>
-__device__ __forceinline__ int row_base(int ctx, int win) { return window_lo(ctx, win) / TS * TS; }
-template <int TS>
-__device__ __forceinline__ int row_steps(int ctx, int win) { return (ctx - row_base<TS>(ctx, win) + TS - 1) / TS; }
-
-// Byte / half-word masks keeping the tokens of lane slot j that lie in
-// [t_lo, t_end): token tb + i owns byte i (8-bit) or half-word i (bf16 pairs).
-__device__ __forceinline__ bool tok_in(int t, int t_lo, int t_end) { return t < t_end && t >= t_lo; }
-__device__ __forceinline__ uint32_t tok_mask8(int tb, int t_lo, int t_end) {
-  return (tok_in(tb + 0, t_lo, t_end) ? 0x000000ffu : 0u) | (tok_in(tb + 1, t_lo, t_end) ? 0x0000ff00u : 0u) |
-         (tok_in(tb + 2, t_lo, t_end) ? 0x00ff0000u : 0u) | (tok_in(tb + 3, t_lo, t_end) ? 0xff000000u : 0u);
-}
-__device__ __forceinline__ uint32_t tok_mask16(int tb, int t_lo, int t_end) {
-  return (tok_in(tb, t_lo, t_end) ? 0x0000ffffu : 0u) | (tok_in(tb + 1, t_lo, t_end) ? 0xffff0000u : 0u);
-}
-
-// Query dims held by lane slot j of q.K MFMA kk (the same dims the K operand
-// of that slot holds).
-template <int E>
-__device__ __forceinline__ int q_dim0(int kk, int j) {
-  return (E == 2) ? (32 * kk + 8 * j) : (64 * (kk >> 1) + 16 * j + 8 * (kk & 1));
-}
-
-// Output dim of accumulator element i of tile c in lane slot j, by the
-// accumulator layout AL of the storage type (its bytes per element, 0 for INT4):
-//   bf16: 32u + 8j + 2i + e  (c = 2u + e)   8-bit: 64u + 16j + 4i + e (c = 4u + e)
-//   INT4: 16c + 4j + i
-template <int AL>
-__device__ __forceinline__ int acc_dim(int c, int j, int i) {
-  if constexpr (AL == 0) return 16 * c + 4 * j + i;
-  return (AL == 2) ? (32 * (c >> 1) + 8 * j + 2 * i + (c & 1)) : (64 * (c >> 2) + 16 * j + 4 * i + (c & 3));
-}
-
-// ---- INT4: a stored nibble u = code + 8 becomes the bf16 of 128 + u =
-// 136 + code (exact: bf16 has 8 significant bits) by OR-ing it into the
-// mantissa of 128.0 (0x4300).  Word nibbles are placed so that pair k of a
-// word - bits 4k .. 4k+3 and 16 + 4k .. 16 + 4k + 3 - is one bf16x2.  The
-// kernels subtract the constant 136 after the products: 136 * sum(q) from
-// each logit, 136 * sum(p) from each accumulator.
-constexpr float kInt4Bias = 136.0f;
-__device__ __forceinline__ uint32_t int4_pair(uint32_t w, int k) {
-  return 0x43004300u | ((w >> (4 * k)) & 0x000F000Fu);
-}
-
 // =====================================================================
-// Single-pass kernel (partition_size == 0)
+// Single-pass kernel (partition_size == 0); its parameter block and step
+// loads are in decode_common.h
 // =====================================================================
-struct DecodeParams {
-  const uint16_t* q;          // [S][Hq][D] bf16
-  float* out;                 // [S][Hq][D]
-  const char* k;              // this layer's K region
-  const char* v;              // this layer's V region
-  const float* ks;            // this layer's K scales (int8) or null
-  const float* vs;            // this layer's V scales (int8) or null
-  const int32_t* bt;          // [S][W]
-  const int32_t* ctx;         // [S]
-  int32_t W, S, Hq, Hkv, G, QT, num_blocks;
-  int32_t num_items;          // S * Hkv * QT
-  int32_t win;                // sliding window (positions), 0 = whole context
-  float qk_scale;             // softmax scale * log2(e) (* fp8 k scale)
-  float out_scale;            // fp8 / int8 per-tensor v scale, else 1
-  const float* vs_ch;         // int8 per channel: this layer's V scales [Hkv][D] (output scale per dim), else null
-  int32_t q_stride;           // elements between q rows: D, or 2 D for the folded q of int8 per channel
-};
-
-template <int D, int KVT>
-struct Tile {
-  static constexpr int E = KVT == PKV_KV_BF16 ? 2 : 1;        // bytes per element
-  static constexpr int KLOADS = D * E / 64;                   // 16-B K loads per chunk per lane
-  static constexpr int VLOADS = D * E / 64;                   // 16-B V loads per chunk per lane
-  static constexpr int KK = D / 32;                           // q.K MFMAs per chunk
-  static constexpr int NC = D / 16;                           // P.V MFMAs per step
-};
-
-// Registers of one step (two chunks).
-template <int D, int KVT>
-struct StepRegs {
-  u32x4 k[2][Tile<D, KVT>::KLOADS];
-  u32x4 v[2][Tile<D, KVT>::VLOADS];
-  f32x4 ksc[2];   // int8: K scales of this lane's 4 tokens per chunk
-  f32x4 vsc[2];
-};
-
-template <int D, int KVT, int B>
-__device__ __forceinline__ void issue_step(StepRegs<D, KVT>& r, const DecodeParams& p, const int32_t* bt_row,
-                                           int g, int tok0, int t_lo, int lane) {
-  using T = Tile<D, KVT>;
-  constexpr int E = T::E;
-  const int row = lane & 15;
-  const int j = lane >> 4;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int t = tok0 + 16 * h;                   // first token of the chunk (multiple of 16)
-    // a chunk wholly before the window does not use its table entries (block
-    // 0 instead; its tokens are masked).  With B = 8 the chunk spans two blocks.
-    const bool used = t + 16 > t_lo;
-    int ph[2];
-#pragma unroll
-    for (int b = 0; b < (B < 16 ? 2 : 1); ++b) {
-      int lb = (int)((uint32_t)t / B) + b;         // tokens are never negative
-      lb = lb < p.W ? lb : p.W - 1;                // never index past the table row
-      const int e = used ? bt_row[lb] : 0;
-      ph[b] = e < 0 ? 0 : (e >= p.num_blocks ? p.num_blocks - 1 : e);  // stay inside the pool
-    }
-    if (B >= 16) ph[1] = ph[0];
-    // K: lane row reads token t + row; V and the int8 scales: lane j reads
-    // tokens t + 4j .. t + 4j + 3
-    const int phk = row < 8 ? ph[0] : ph[1];
-    const int phv = j < 2 ? ph[0] : ph[1];
-    // chunks start at multiples of 16 tokens: with B >= 16 the chunk sits at
-    // offset t % B of one block, with B = 8 it starts both of its blocks
-    constexpr int TM = (B < 16 ? B : 16) - 1;
-    const int toff = B < 16 ? 0 : (int)((uint32_t)t % B);
-    const int tk = toff + (row & TM);              // token of lane row inside its block
-    const int tv = toff + ((4 * j) & TM);          // first token of lane j's group inside its block
-    // tile numbers are below num_blocks * Hkv < 2^31: unsigned 32-bit
-    // products widened once keep the address arithmetic short
-    const uint32_t tilek = (uint32_t)phk * (uint32_t)p.Hkv + (uint32_t)g;
-    const uint32_t tilev = (uint32_t)phv * (uint32_t)p.Hkv + (uint32_t)g;
-    const char* kt = p.k + (uint64_t)tilek * (uint32_t)(B * D * E);
-    const char* vt = p.v + (uint64_t)tilev * (uint32_t)(B * D * E);
-    // K: piece c holds dims [X*c, X*c+X) of all B tokens, 16 bytes per token
-#pragma unroll
-    for (int u = 0; u < T::KLOADS; ++u) r.k[h][u] = ld16(kt + (uint32_t)((4 * u + j) * B + tk) * 16u);
-    // V: token group tv / 4, 4 tokens x dims as 4E-byte words
-    const int grp = tv >> 2;
-#pragma unroll
-    for (int u = 0; u < T::VLOADS; ++u) {
-      const int d = (E == 2) ? (32 * u + 2 * row) : (64 * u + 4 * row);
-      r.v[h][u] = ld16(vt + (uint32_t)(grp * D + d) * (uint32_t)(4 * E));
-    }
-    if constexpr (KVT == PKV_KV_INT8) {
-      const uint64_t so = (uint64_t)tilev * B + tv;
-      r.ksc[h] = *reinterpret_cast<const f32x4*>(p.ks + so);
-      r.vsc[h] = *reinterpret_cast<const f32x4*>(p.vs + so);
-    }
-  }
-}
-
 template <int D, int KVT, int B>
 __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodeParams p) {
   using T = Tile<D, KVT>;
@@ -480,301 +234,6 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
       A += f * sm_acc[ww][hh][d];
     }
     p.out[((int64_t)s * p.Hq + h0 + hh) * D + d] = A / L * (p.vs_ch ? p.vs_ch[g * D + d] : p.out_scale);
-  }
-}
-
-// =====================================================================
-// Paged prefill (a chunk of new tokens per sequence, causal)
-// =====================================================================
-// The decode matrix-core step with its 16 columns taken by (query token,
-// query head) pairs of one KV head instead of by query heads: column c of a
-// sequence's chunk is token c / G of the chunk and head g G + c % G.  Token k
-// of a chunk of n sits at position ctx - n + k and sees positions 0 .. ctx -
-// n + k, so each column masks the keys at or past its own limit.
-// Every wave owns kPrefillNT tiles of 16 columns and streams all of their
-// keys itself: each K/V step it loads is widened once and feeds the products
-// of all its tiles, and the wave writes its columns' outputs from registers
-// (no cross-wave merge).  The four waves of a workgroup take consecutive
-// column spans of one (sequence, KV head), so they read the same keys at
-// about the same time and share them through L2.  kPrefillBuf steps of K/V
-// are in registers: one computed, the others in flight.  The streaming
-// softmax keeps a reference max per column that is raised only when a logit
-// exceeds it by kPrefillSlack (log2 units), so the accumulators are rescaled
-// a few times per column instead of at every step.
-constexpr int kPrefillNT = 1;          // 16-column tiles per wave
-constexpr int kPrefillBuf = 2;         // K/V steps held per wave
-constexpr float kPrefillSlack = 8.0f;  // p < 2^8 between rescales
-
-struct PrefillParams {
-  DecodeParams d;             // q [T][Hq][D] (or the folded q), out [T][Hq][D], pool layer, tables, lengths
-  const int32_t* qstart;      // [S + 1]: sequence s's queries are rows qstart[s] .. qstart[s+1] - 1
-  int32_t tiles;              // workgroup column spans per (sequence, KV head):
-                              // ceil(max_query_len * G / (16 kPrefillNT kNW))
-  int32_t T;                  // rows of q and out
-};
-
-template <int D, int KVT, int B>
-__global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillParams pp) {
-  constexpr int NT = kPrefillNT;
-  constexpr int NB = kPrefillBuf;
-  const DecodeParams& p = pp.d;
-  using T = Tile<D, KVT>;
-  constexpr int E = T::E;
-
-  const int nwg = (int)gridDim.x;
-  const int xcd = (int)blockIdx.x % 8;
-  const int per_xcd = (nwg + 7) / 8;
-  const int item = xcd * per_xcd + (int)blockIdx.x / 8;
-  if (item >= p.num_items) return;
-  const int ct = item % pp.tiles;
-  const int g = (item / pp.tiles) % p.Hkv;
-  const int s = item / (pp.tiles * p.Hkv);
-  const int lane = threadIdx.x % kWave;
-  const int w = threadIdx.x / kWave;
-  const int row = lane & 15;
-  const int j = lane >> 4;
-  // query rows, kept inside [0, T) whatever query_start holds
-  const int q0 = min(max(pp.qstart[s], 0), pp.T);
-  const int n = min(max(pp.qstart[s + 1], q0), pp.T) - q0;
-  const int ncol = n * p.G;
-  const int c0 = (ct * kNW + w) * 16 * NT;       // this wave's first column
-  if (c0 >= ncol) return;                        // no barrier follows: waves are independent
-  const int cols = min(16 * NT, ncol - c0);
-
-  const int ctx = clamp_ctx(p.ctx[s], p.W * B);
-  const int first = ctx - n;                     // position of the chunk's token 0
-  const int t_end = max(0, first + (c0 + cols - 1) / p.G + 1);   // the wave's largest limit
-  const int nsteps = (t_end + kStep - 1) / kStep;
-  // every valid column sees the keys below this one (column c0's limit, the
-  // smallest): steps wholly below it need no causal mask
-  const int lim_lo = max(0, first + c0 / p.G + 1);
-  const int32_t* bt_row = p.bt + (int64_t)s * p.W;
-
-  // per tile: this lane's column limit (keys [0, lim)) and the query as the
-  // B operand (columns past the chunk read column c0's query, limit 0)
-  bf16x8 qop[NT][T::KK];
-  int lim[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int cl = 16 * nt + row;
-    const bool valid = cl < cols;
-    const int c = c0 + (valid ? cl : 0);
-    lim[nt] = valid ? max(0, first + c / p.G + 1) : 0;
-    const uint16_t* qh = p.q + ((int64_t)(q0 + c / p.G) * p.Hq + g * p.G + c % p.G) * p.q_stride;
-#pragma unroll
-    for (int kk = 0; kk < T::KK; ++kk)
-      qop[nt][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + q_dim0<E>(kk, j)));
-  }
-
-  f32x4 acc[NT][T::NC];
-  float m_run[NT], l_run[NT];   // reference max of scaled logits (log2 domain) and partial sum, column `row`
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m_run[nt] = -INFINITY;
-    l_run[nt] = 0.f;
-#pragma unroll
-    for (int cc = 0; cc < T::NC; ++cc) acc[nt][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  auto compute = [&](StepRegs<D, KVT>& r, int tok0) __attribute__((always_inline)) {
-    // K operands, widened once for every tile
-    bf16x8 ka[2][T::KK];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int kk = 0; kk < T::KK; ++kk) {
-        if constexpr (E == 2) {
-          ka[h][kk] = __builtin_bit_cast(bf16x8, r.k[h][kk]);
-        } else {
-          const u32x4 wv = r.k[h][kk >> 1];
-          ka[h][kk] = (kk & 1) ? widen8<KVT>(wv[2], wv[3]) : widen8<KVT>(wv[0], wv[1]);
-        }
-      }
-    }
-    f32x4 z[NT][2];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < T::KK; ++kk) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[h][kk], qop[nt][kk], c, 0, 0, 0);
-        z[nt][h] = c;
-      }
-    }
-    float alpha[NT], m_use[NT];
-    bool any_rescale = false;
-    // raw logits (int8: times the token's K scale); the softmax scale s > 0
-    // is applied to the max and inside the exponent's fma, max(z) s = max(z s)
-    const bool unmasked = tok0 + kStep <= lim_lo;   // uniform
-    float mlocs[NT];
-    if (unmasked) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        float mloc = -INFINITY;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if constexpr (KVT == PKV_KV_INT8) z[nt][h][i] *= r.ksc[h][i];
-            mloc = fmaxf(mloc, z[nt][h][i]);
-          }
-        mlocs[nt] = mloc;
-      }
-    } else {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        float mloc = -INFINITY;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = tok0 + 16 * h + 4 * j + i;
-            float zz = z[nt][h][i];
-            if constexpr (KVT == PKV_KV_INT8) zz *= r.ksc[h][i];
-            zz = t < lim[nt] ? zz : -INFINITY;     // causal: this column's keys only
-            z[nt][h][i] = zz;
-            mloc = fmaxf(mloc, zz);
-          }
-        mlocs[nt] = mloc;
-      }
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const float mloc = max_x32(max_x16(mlocs[nt])) * p.qk_scale;   // the column's scaled max over the step
-      const bool bump = mloc > m_run[nt] + kPrefillSlack;   // false while the column has no key
-      const float m_ref = bump ? mloc : m_run[nt];
-      alpha[nt] = bump ? __builtin_amdgcn_exp2f(m_run[nt] - m_ref) : 1.0f;
-      any_rescale |= bump && m_run[nt] > -INFINITY;   // the accumulator is zero until the first raise
-      m_run[nt] = m_ref;
-      // a column with no key yet keeps reference -inf; its exponents use 0 so
-      // that p is 0, not NaN
-      m_use[nt] = m_ref == -INFINITY ? 0.f : m_ref;
-    }
-    if (__builtin_amdgcn_ballot_w64(any_rescale)) {   // uniform branch, rarely taken
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int cc = 0; cc < T::NC; ++cc) acc[nt][cc] = acc[nt][cc] * alpha[nt];
-    }
-    // keys at or past the wave's largest limit may be unwritten slots (any
-    // bits): their V is zeroed, in the step's own registers (the next load
-    // overwrites them anyway); keys below it are written data, masked by p = 0
-    if (tok0 + kStep > t_end) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int tb = tok0 + 16 * h + 4 * j;      // lane j's 4 tokens of the chunk
-#pragma unroll
-        for (int u = 0; u < T::VLOADS; ++u) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            // bf16: word e holds tokens tb + 2 (e % 2) and + 1 of one dim; 8-bit: tokens tb .. tb + 3
-            r.v[h][u][e] &= E == 2 ? tok_mask16(tb + 2 * (e & 1), 0, t_end) : tok_mask8(tb, 0, t_end);
-          }
-        }
-      }
-    }
-    bf16x8 pop[NT], pop_lo[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float psum = 0.f;
-      uint32_t ph[2][2], pl[2][2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float pv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[nt][h][i], p.qk_scale, -m_use[nt]));
-          psum += pv[i];
-          if constexpr (KVT == PKV_KV_INT8) {
-            const int t = tok0 + 16 * h + 4 * j + i;
-            pv[i] = (unmasked || t < lim[nt]) ? pv[i] * r.vsc[h][i] : 0.f;   // fold the V scale into p
-          }
-        }
-        ph[h][0] = pack_bf16x2(pv[0], pv[1]);
-        ph[h][1] = pack_bf16x2(pv[2], pv[3]);
-        pl[h][0] = pack_bf16x2(pv[0] - bf16_lo(ph[h][0]), pv[1] - bf16_hi(ph[h][0]));
-        pl[h][1] = pack_bf16x2(pv[2] - bf16_lo(ph[h][1]), pv[3] - bf16_hi(ph[h][1]));
-      }
-      l_run[nt] = l_run[nt] * alpha[nt] + psum;
-      pop[nt] = __builtin_bit_cast(bf16x8, u32x4{ph[0][0], ph[0][1], ph[1][0], ph[1][1]});
-      pop_lo[nt] = __builtin_bit_cast(bf16x8, u32x4{pl[0][0], pl[0][1], pl[1][0], pl[1][1]});
-    }
-#pragma unroll
-    for (int cc = 0; cc < T::NC; ++cc) {
-      uint32_t a0, a1, a2, a3;
-      if constexpr (E == 2) {
-        const int u = cc >> 1, e = cc & 1;
-        a0 = r.v[0][u][2 * e];
-        a1 = r.v[0][u][2 * e + 1];
-        a2 = r.v[1][u][2 * e];
-        a3 = r.v[1][u][2 * e + 1];
-      } else {
-        const int u = cc >> 2, e = cc & 3;
-        widen4<KVT>(r.v[0][u][e], a0, a1);
-        widen4<KVT>(r.v[1][u][e], a2, a3);
-      }
-      const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{a0, a1, a2, a3});
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        acc[nt][cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop[nt], acc[nt][cc], 0, 0, 0);
-        acc[nt][cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_lo[nt], acc[nt][cc], 0, 0, 0);
-      }
-    }
-  };
-
-  // NB - 1 steps in flight ahead of the one computed.  Every iteration issues
-  // the same loads (a step past the end reads a tile the table clamps into
-  // the pool, unused) so that each wait covers exactly one step's loads.
-  StepRegs<D, KVT> r[NB];
-  static_for<NB - 1>([&](auto b) __attribute__((always_inline)) {
-    issue_step<D, KVT, B>(r[b], p, bt_row, g, (int)b * kStep, 0, lane);
-  });
-  int i = 0;
-  while (i < nsteps) {
-    static_for<NB>([&](auto b) __attribute__((always_inline)) {   // buffer indices are constants
-      if (i < nsteps) {
-        issue_step<D, KVT, B>(r[(b + NB - 1) % NB], p, bt_row, g, (i + NB - 1) * kStep, 0, lane);
-        compute(r[b], i * kStep);
-        ++i;
-      }
-    });
-  }
-
-  // outputs: column `row` of tile nt; this lane holds dims acc_dim(cc, j, .)
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int cl = 16 * nt + row;
-    const float L = sum_x32(sum_x16(l_run[nt]));
-    if (cl >= cols) continue;
-    const int cq = c0 + cl;
-    float* orow = p.out + ((int64_t)(q0 + cq / p.G) * p.Hq + g * p.G + cq % p.G) * D;
-    const float inv = L > 0.f ? 1.f / L : 0.f;   // no key at all (position < 0): zero row
-    float o[T::NC][4];
-#pragma unroll
-    for (int cc = 0; cc < T::NC; ++cc)
-#pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) {
-        const int d = acc_dim<E>(cc, j, i2);
-        o[cc][i2] = acc[nt][cc][i2] * inv * (p.vs_ch ? p.vs_ch[g * D + d] : p.out_scale);
-      }
-    if constexpr (E == 2) {
-      // tiles 2u, 2u + 1 hold dims 32u + 8j + 2 i2 + {0, 1}: 8 consecutive floats
-#pragma unroll
-      for (int u = 0; u < T::NC / 2; ++u) {
-        float* dst = orow + 32 * u + 8 * j;
-        *reinterpret_cast<f32x4*>(dst) = f32x4{o[2 * u][0], o[2 * u + 1][0], o[2 * u][1], o[2 * u + 1][1]};
-        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[2 * u][2], o[2 * u + 1][2], o[2 * u][3], o[2 * u + 1][3]};
-      }
-    } else {
-      // tiles 4u .. 4u + 3 hold dims 64u + 16j + 4 i2 + {0 .. 3}
-#pragma unroll
-      for (int u = 0; u < T::NC / 4; ++u)
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2)
-          *reinterpret_cast<f32x4*>(orow + 64 * u + 16 * j + 4 * i2) =
-              f32x4{o[4 * u][i2], o[4 * u + 1][i2], o[4 * u + 2][i2], o[4 * u + 3][i2]};
-    }
   }
 }
 
@@ -1800,66 +1259,11 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
   }
 }
 
-// INT8 with per-channel scales: the K scale of (KV head, dim) is folded into
-// the query, z = sum_d (q_d * s_d) * code_d, so the decode kernels see plain
-// int8 codes.  q'[s][h][d] = bf16(fp32(q) * s_k[h / G][d]) (rounded to
-// nearest even) is written over the first half of the output row out[s][h],
-// which only that row's final merge writes, after every read of q'; the
-// kernels read it with a row stride of 2 D elements.
-__global__ __launch_bounds__(256) void fold_q_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ qf,
-                                                     const float* __restrict__ ks_ch, int64_t n, int32_t Hq,
-                                                     int32_t G, int32_t D) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const int d = (int)(i % D);
-  const int64_t row = i / D;
-  const int h = (int)(row % Hq);
-  const float x = bf16_bits_to_float(q[i]) * ks_ch[(h / G) * D + d];
-  qf[row * 2 * D + d] = (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu);
-}
-
 // ---------------------------------------------------------------- launches
-template <int V>
-using IC = std::integral_constant<int, V>;
-
-// f(IC<D>, IC<KVT>, IC<B>) for the kernel variant of head dim D (64, 128),
-// storage kv_dtype and block size B (8, 16, 32).  INT8 with per-tensor or
-// per-channel scales runs the per-tensor codes kernel (the channel scales are
-// folded into q and into the output).
-template <bool kInt4, class F>
-auto with_variant(int D, int kvt, int B, F&& f) {
-  auto by_b = [&](auto dc, auto kc) {
-    if (B == 8) return f(dc, kc, IC<8>{});
-    if (B == 16) return f(dc, kc, IC<16>{});
-    return f(dc, kc, IC<32>{});
-  };
-  auto by_kv = [&](auto dc) {
-    switch (kvt) {
-      case PKV_KV_BF16: return by_b(dc, IC<PKV_KV_BF16>{});
-      case PKV_KV_FP8_E5M2: return by_b(dc, IC<PKV_KV_FP8_E5M2>{});
-      case PKV_KV_INT8_TENSOR:
-      case PKV_KV_INT8_CHANNEL: return by_b(dc, IC<PKV_KV_INT8_TENSOR>{});
-      case PKV_KV_INT4:
-        if constexpr (kInt4) return by_b(dc, IC<PKV_KV_INT4>{});
-        [[fallthrough]];
-      default: return by_b(dc, IC<PKV_KV_INT8>{});
-    }
-  };
-  return D == 64 ? by_kv(IC<64>{}) : by_kv(IC<128>{});
-}
-
 hipError_t launch_single(const DecodeParams& p, int D, int kvt, int B, int grid, hipStream_t stream) {
   return with_variant<false>(D, kvt, B, [&](auto dc, auto kc, auto bc) {
     hipLaunchKernelGGL((pa_decode_kernel<decltype(dc)::value, decltype(kc)::value, decltype(bc)::value>), dim3(grid),
                        dim3(kWave * kNW), 0, stream, p);
-    return hipGetLastError();
-  });
-}
-
-hipError_t launch_prefill(const PrefillParams& p, int D, int kvt, int B, int grid, hipStream_t stream) {
-  return with_variant<false>(D, kvt, B, [&](auto dc, auto kc, auto bc) {
-    hipLaunchKernelGGL((pa_prefill_kernel<decltype(dc)::value, decltype(kc)::value, decltype(bc)::value>),
-                       dim3(grid), dim3(kWave * kNW), 0, stream, p);
     return hipGetLastError();
   });
 }
@@ -2179,109 +1583,6 @@ extern "C" pkv_status paged_attn_decode_append(float* out, const void* q, const 
   return decode_impl(out, q, pool, layer, key, value, block_tables, table_width, context_lens, num_seqs,
                      num_q_heads, scale, kv_dtype, kv_scales, partition_size, 0, workspace, workspace_bytes,
                      stream);
-}
-
-extern "C" pkv_status paged_attn_prefill(float* out, const void* q, const pkv_pool* pool, int32_t layer,
-                                         const int32_t* block_tables, int32_t table_width,
-                                         const int32_t* context_lens, const int32_t* query_start,
-                                         int32_t num_seqs, int32_t num_queries, int32_t max_query_len,
-                                         int32_t num_q_heads, float scale, int32_t kv_dtype,
-                                         const pkv_kv_scales* kv_scales, hipStream_t stream) {
-  pkv_status st = check_pool(pool);
-  if (st != PKV_OK) return st;
-  const pkv_pool_config& c = pool->cfg;
-  if (kv_dtype != c.kv_dtype) {
-    set_error("kv_dtype %d does not match the pool's %d", kv_dtype, c.kv_dtype);
-    return PKV_ERR_INVALID;
-  }
-  if (c.kv_dtype == PKV_KV_INT4) return fail(PKV_ERR_UNSUPPORTED, "paged prefill is not built for INT4 storage");
-  if (layer < 0 || layer >= c.num_layers) {
-    set_error("layer %d outside [0, %d)", layer, c.num_layers);
-    return PKV_ERR_INVALID;
-  }
-  if (num_seqs < 0 || num_queries < 0 || max_query_len < 0)
-    return fail(PKV_ERR_INVALID, "num_seqs, num_queries and max_query_len must not be negative");
-  if (num_seqs == 0 || num_queries == 0 || max_query_len == 0) { clear_error(); return PKV_OK; }
-  if (!out || !q || !block_tables || !context_lens || !query_start) return fail(PKV_ERR_INVALID, "NULL device pointer");
-  if (num_q_heads <= 0 || num_q_heads % c.num_kv_heads != 0) {
-    set_error("num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads, c.num_kv_heads);
-    return PKV_ERR_INVALID;
-  }
-  if (table_width <= 0) return fail(PKV_ERR_INVALID, "table_width must be positive");
-  if ((int64_t)table_width * c.block_size > INT32_MAX / 2) return fail(PKV_ERR_INVALID, "table_width too large");
-  if (!(scale > 0.f) || !(scale < INFINITY)) return fail(PKV_ERR_INVALID, "scale must be positive and finite");
-  if (c.head_dim != 64 && c.head_dim != 128) {
-    set_error("head_dim %d not built (64, 128)", c.head_dim);
-    return PKV_ERR_UNSUPPORTED;
-  }
-  if (c.block_size != 8 && c.block_size != 16 && c.block_size != 32) {
-    set_error("block_size %d not built (8, 16, 32)", c.block_size);
-    return PKV_ERR_UNSUPPORTED;
-  }
-  if (((uintptr_t)q) % 16 || ((uintptr_t)out) % 16) return fail(PKV_ERR_INVALID, "q and out must be 16-byte aligned");
-  float ksc = 1.f, vsc = 1.f;
-  if (kv_scales && (c.kv_dtype == PKV_KV_FP8_E5M2 || c.kv_dtype == PKV_KV_INT8_TENSOR)) {
-    ksc = kv_scales->k_scale;
-    vsc = kv_scales->v_scale;
-    if (!(ksc > 0.f) || !(vsc > 0.f) || !(ksc < INFINITY) || !(vsc < INFINITY))
-      return fail(PKV_ERR_INVALID, "per-tensor scales must be positive and finite");
-  }
-  const bool channel = has_channel_scales(c.kv_dtype);
-  if (channel && (const void*)out == q)
-    return fail(PKV_ERR_INVALID, "out must not alias q for storage with per-channel scales");
-  const int32_t G = num_q_heads / c.num_kv_heads;
-  const int64_t span = 16 * kPrefillNT * kNW;   // columns per workgroup
-  const int64_t tiles = ((int64_t)max_query_len * G + span - 1) / span;
-  const int64_t items = (int64_t)num_seqs * c.num_kv_heads * tiles;
-  if (items > INT32_MAX / 2) return fail(PKV_ERR_INVALID, "too many query tiles in one call");
-  const uint64_t scale_layer = channel ? (uint64_t)c.num_kv_heads * c.head_dim
-                                      : (uint64_t)c.num_blocks * c.num_kv_heads * c.block_size;
-  float* ksl = pool->k_scale ? pool->k_scale + layer * scale_layer : nullptr;
-  float* vsl = pool->v_scale ? pool->v_scale + layer * scale_layer : nullptr;
-  const uint16_t* qk = static_cast<const uint16_t*>(q);
-  int32_t q_stride = c.head_dim;
-  if (channel) {   // the K channel scales folded into the query, written into the output rows first
-    const int64_t n = (int64_t)num_queries * num_q_heads * c.head_dim;
-    const int64_t blocks = (n + 255) / 256;
-    if (blocks > INT32_MAX) return fail(PKV_ERR_INVALID, "too many queries in one call");
-    hipLaunchKernelGGL(fold_q_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, qk,
-                       reinterpret_cast<uint16_t*>(out), ksl, n, num_q_heads, G, c.head_dim);
-    qk = reinterpret_cast<const uint16_t*>(out);
-    q_stride = 2 * c.head_dim;
-  }
-  PrefillParams pp{};
-  DecodeParams& p = pp.d;
-  p.q = qk;
-  p.q_stride = q_stride;
-  p.vs_ch = channel ? vsl : nullptr;
-  p.out = out;
-  p.k = static_cast<char*>(pool->k) + (uint64_t)layer * pool->layer_bytes;
-  p.v = static_cast<char*>(pool->v) + (uint64_t)layer * pool->layer_bytes;
-  p.ks = ksl;
-  p.vs = vsl;
-  p.bt = block_tables;
-  p.ctx = context_lens;
-  p.W = table_width;
-  p.S = num_seqs;
-  p.Hq = num_q_heads;
-  p.Hkv = c.num_kv_heads;
-  p.G = G;
-  p.QT = 1;
-  p.num_blocks = c.num_blocks;
-  p.num_items = (int32_t)items;
-  p.win = 0;
-  p.qk_scale = scale * kLog2e * ksc;
-  p.out_scale = vsc;
-  pp.qstart = query_start;
-  pp.tiles = (int32_t)tiles;
-  pp.T = num_queries;
-  const hipError_t e = launch_prefill(pp, c.head_dim, c.kv_dtype, c.block_size, (int)((items + 7) / 8 * 8), stream);
-  if (e != hipSuccess) {
-    set_error("paged_attn_prefill launch failed: %s", hipGetErrorString(e));
-    return PKV_ERR_HIP;
-  }
-  clear_error();
-  return PKV_OK;
 }
 
 extern "C" pkv_status paged_attn_decode_ex(const pkv_decode_args* a, hipStream_t stream) {

@@ -1,0 +1,513 @@
+// Paged prefill attention for gfx950 (CDNA4): causal attention of a chunk
+// of new tokens per sequence over its paged KV cache, the prefill that a
+// prefix-cache hit leaves to do (bjdmk.com.cn article, §4.1: the cached
+// prefix is reused and only the rest is computed; "KV Cache 原理与
+// PagedAttention", §五).  The K/V of every position, the new tokens included,
+// are in the pool before the call (reshape_and_cache).
+#include "decode_common.h"
+
+namespace pkv {
+namespace {
+
+// =====================================================================
+// Paged prefill (a chunk of new tokens per sequence, causal)
+// =====================================================================
+// The decode matrix-core step with its 16 columns taken by (query token,
+// query head) pairs of one KV head instead of by query heads: column c of a
+// sequence's chunk is token c / G of the chunk and head g G + c % G.  Token k
+// of a chunk of n sits at position ctx - n + k and sees positions 0 .. ctx -
+// n + k, so each column masks the keys at or past its own limit.
+// Every wave owns kPrefillNT tiles of 16 columns and streams all of their
+// keys itself: each K/V step it loads is widened once and feeds the products
+// of all its tiles, and the wave writes its columns' outputs from registers
+// (no cross-wave merge).  The four waves of a workgroup take consecutive
+// column spans of one (sequence, KV head), so they read the same keys at
+// about the same time and share them through L2.  kPrefillBuf steps of K/V
+// are in registers: one computed, the others in flight.  The streaming
+// softmax keeps a reference max per column that is raised only when a logit
+// exceeds it by kPrefillSlack (log2 units), so the accumulators are rescaled
+// a few times per column instead of at every step.
+constexpr int kPrefillNT = 1;          // 16-column tiles per wave
+constexpr int kPrefillBuf = 2;         // K/V steps held per wave
+constexpr float kPrefillSlack = 8.0f;  // p < 2^8 between rescales
+
+// INT4 step loads: per 16-token chunk one K piece (lane slot j, token row)
+// and one V piece (token group of lane slot j, dim row) of D / 8 bytes each,
+// in the INT4 tile layout (the split decode kernel reads the same pieces).
+template <int D, int B>
+__device__ __forceinline__ void issue_step_int4(StepRegs<D, PKV_KV_INT4>& r, const DecodeParams& p,
+                                                const int32_t* bt_row, int g, int tok0, int lane) {
+  constexpr int P = D / 8;
+  const int row = lane & 15;
+  const int j = lane >> 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = tok0 + 16 * h;
+    int ph[2];
+#pragma unroll
+    for (int b = 0; b < (B < 16 ? 2 : 1); ++b) {
+      int lb = (int)((uint32_t)t / B) + b;
+      lb = lb < p.W ? lb : p.W - 1;                // never index past the table row
+      const int e = bt_row[lb];
+      ph[b] = e < 0 ? 0 : (e >= p.num_blocks ? p.num_blocks - 1 : e);  // stay inside the pool
+    }
+    if (B >= 16) ph[1] = ph[0];
+    const int phk = row < 8 ? ph[0] : ph[1];
+    const int phv = j < 2 ? ph[0] : ph[1];
+    constexpr int TM = (B < 16 ? B : 16) - 1;
+    const int toff = B < 16 ? 0 : (int)((uint32_t)t % B);
+    const int tk = toff + (row & TM);
+    const int tv = toff + ((4 * j) & TM);
+    const uint32_t tilek = (uint32_t)phk * (uint32_t)p.Hkv + (uint32_t)g;
+    const uint32_t tilev = (uint32_t)phv * (uint32_t)p.Hkv + (uint32_t)g;
+    const char* ka = p.k + (uint64_t)tilek * (uint32_t)(B * D / 2) + (uint32_t)(j * B + tk) * P;
+    const char* va = p.v + (uint64_t)tilev * (uint32_t)(B * D / 2) + (uint32_t)((tv >> 2) * 16 + row) * P;
+    if constexpr (P == 16) {
+      r.k[h][0] = ld16(ka);
+      r.v[h][0] = ld16(va);
+    } else {
+      const u32x2 k2 = *reinterpret_cast<const u32x2*>(ka);
+      const u32x2 v2 = *reinterpret_cast<const u32x2*>(va);
+      r.k[h][0] = u32x4{k2[0], k2[1], 0u, 0u};
+      r.v[h][0] = u32x4{v2[0], v2[1], 0u, 0u};
+    }
+  }
+}
+
+struct PrefillParams {
+  DecodeParams d;             // q [T][Hq][D] (or the folded q), out [T][Hq][D], pool layer, tables, lengths
+  const int32_t* qstart;      // [S + 1]: sequence s's queries are rows qstart[s] .. qstart[s+1] - 1
+  int32_t tiles;              // workgroup column spans per (sequence, KV head):
+                              // ceil(max_query_len * G / (16 kPrefillNT kNW))
+  int32_t T;                  // rows of q and out
+};
+
+template <int D, int KVT, int B>
+__global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillParams pp) {
+  constexpr int NT = kPrefillNT;
+  constexpr int NB = kPrefillBuf;
+  const DecodeParams& p = pp.d;
+  using T = Tile<D, KVT>;
+  constexpr int E = T::E;
+  // INT4: the K and V operands hold 136 + code (bf16, exact), taken back
+  // after the products; the query dims follow the bf16 slot layout and the
+  // accumulator dims that of the INT4 V pieces
+  constexpr bool I4 = KVT == PKV_KV_INT4;
+  constexpr int QL = I4 ? 2 : E;
+  constexpr int AL = I4 ? 0 : E;
+
+  const int nwg = (int)gridDim.x;
+  const int xcd = (int)blockIdx.x % 8;
+  const int per_xcd = (nwg + 7) / 8;
+  const int item = xcd * per_xcd + (int)blockIdx.x / 8;
+  if (item >= p.num_items) return;
+  const int ct = item % pp.tiles;
+  const int g = (item / pp.tiles) % p.Hkv;
+  const int s = item / (pp.tiles * p.Hkv);
+  const int lane = threadIdx.x % kWave;
+  const int w = threadIdx.x / kWave;
+  const int row = lane & 15;
+  const int j = lane >> 4;
+  // query rows, kept inside [0, T) whatever query_start holds
+  const int q0 = min(max(pp.qstart[s], 0), pp.T);
+  const int n = min(max(pp.qstart[s + 1], q0), pp.T) - q0;
+  const int ncol = n * p.G;
+  const int c0 = (ct * kNW + w) * 16 * NT;       // this wave's first column
+  if (c0 >= ncol) return;                        // no barrier follows: waves are independent
+  const int cols = min(16 * NT, ncol - c0);
+
+  const int ctx = clamp_ctx(p.ctx[s], p.W * B);
+  const int first = ctx - n;                     // position of the chunk's token 0
+  const int t_end = max(0, first + (c0 + cols - 1) / p.G + 1);   // the wave's largest limit
+  const int nsteps = (t_end + kStep - 1) / kStep;
+  // every valid column sees the keys below this one (column c0's limit, the
+  // smallest): steps wholly below it need no causal mask
+  const int lim_lo = max(0, first + c0 / p.G + 1);
+  const int32_t* bt_row = p.bt + (int64_t)s * p.W;
+
+  // per tile: this lane's column limit (keys [0, lim)) and the query as the
+  // B operand (columns past the chunk read column c0's query, limit 0)
+  bf16x8 qop[NT][T::KK];
+  float qsum[NT];   // INT4: the column's sum of q over all dims
+  int lim[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int cl = 16 * nt + row;
+    const bool valid = cl < cols;
+    const int c = c0 + (valid ? cl : 0);
+    lim[nt] = valid ? max(0, first + c / p.G + 1) : 0;
+    const uint16_t* qh = p.q + ((int64_t)(q0 + c / p.G) * p.Hq + g * p.G + c % p.G) * p.q_stride;
+#pragma unroll
+    for (int kk = 0; kk < T::KK; ++kk)
+      qop[nt][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + q_dim0<QL>(kk, j)));
+    qsum[nt] = 0.f;
+    if constexpr (I4) {
+      float a = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < T::KK; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a += (float)qop[nt][kk][e];
+      qsum[nt] = sum_x32(sum_x16(a));   // lanes of one column hold its 4 dim slots
+    }
+  }
+
+  f32x4 acc[NT][T::NC];
+  float m_run[NT], l_run[NT];   // reference max of scaled logits (log2 domain) and partial sum, column `row`
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m_run[nt] = -INFINITY;
+    l_run[nt] = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < T::NC; ++cc) acc[nt][cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto compute = [&](StepRegs<D, KVT>& r, int tok0) __attribute__((always_inline)) {
+    // K operands, widened once for every tile
+    bf16x8 ka[2][T::KK];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int kk = 0; kk < T::KK; ++kk) {
+        if constexpr (I4) {
+          const uint32_t wk = r.k[h][0][kk];        // word kk: dims 32 kk + 8 j .. + 7
+          ka[h][kk] = __builtin_bit_cast(
+              bf16x8, u32x4{int4_pair(wk, 0), int4_pair(wk, 1), int4_pair(wk, 2), int4_pair(wk, 3)});
+        } else if constexpr (E == 2) {
+          ka[h][kk] = __builtin_bit_cast(bf16x8, r.k[h][kk]);
+        } else {
+          const u32x4 wv = r.k[h][kk >> 1];
+          ka[h][kk] = (kk & 1) ? widen8<KVT>(wv[2], wv[3]) : widen8<KVT>(wv[0], wv[1]);
+        }
+      }
+    }
+    f32x4 z[NT][2];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < T::KK; ++kk) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[h][kk], qop[nt][kk], c, 0, 0, 0);
+        if constexpr (I4) c -= kInt4Bias * qsum[nt];   // the K operand held 136 + code
+        z[nt][h] = c;
+      }
+    }
+    float alpha[NT], m_use[NT];
+    bool any_rescale = false;
+    // raw logits (int8: times the token's K scale); the softmax scale s > 0
+    // is applied to the max and inside the exponent's fma, max(z) s = max(z s)
+    const bool unmasked = tok0 + kStep <= lim_lo;   // uniform
+    float mlocs[NT];
+    if (unmasked) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (KVT == PKV_KV_INT8) z[nt][h][i] *= r.ksc[h][i];
+            mloc = fmaxf(mloc, z[nt][h][i]);
+          }
+        mlocs[nt] = mloc;
+      }
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = tok0 + 16 * h + 4 * j + i;
+            float zz = z[nt][h][i];
+            if constexpr (KVT == PKV_KV_INT8) zz *= r.ksc[h][i];
+            zz = t < lim[nt] ? zz : -INFINITY;     // causal: this column's keys only
+            z[nt][h][i] = zz;
+            mloc = fmaxf(mloc, zz);
+          }
+        mlocs[nt] = mloc;
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float mloc = max_x32(max_x16(mlocs[nt])) * p.qk_scale;   // the column's scaled max over the step
+      const bool bump = mloc > m_run[nt] + kPrefillSlack;   // false while the column has no key
+      const float m_ref = bump ? mloc : m_run[nt];
+      alpha[nt] = bump ? __builtin_amdgcn_exp2f(m_run[nt] - m_ref) : 1.0f;
+      any_rescale |= bump && m_run[nt] > -INFINITY;   // the accumulator is zero until the first raise
+      m_run[nt] = m_ref;
+      // a column with no key yet keeps reference -inf; its exponents use 0 so
+      // that p is 0, not NaN
+      m_use[nt] = m_ref == -INFINITY ? 0.f : m_ref;
+    }
+    if (__builtin_amdgcn_ballot_w64(any_rescale)) {   // uniform branch, rarely taken
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int cc = 0; cc < T::NC; ++cc) acc[nt][cc] = acc[nt][cc] * alpha[nt];
+    }
+    // keys at or past the wave's largest limit may be unwritten slots (any
+    // bits): their V is zeroed, in the step's own registers (the next load
+    // overwrites them anyway); keys below it are written data, masked by p = 0
+    if (!I4 && tok0 + kStep > t_end) {   // INT4 codes are finite whatever the bytes: p = 0 masks them
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int tb = tok0 + 16 * h + 4 * j;      // lane j's 4 tokens of the chunk
+#pragma unroll
+        for (int u = 0; u < T::VLOADS; ++u) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // bf16: word e holds tokens tb + 2 (e % 2) and + 1 of one dim; 8-bit: tokens tb .. tb + 3
+            r.v[h][u][e] &= E == 2 ? tok_mask16(tb + 2 * (e & 1), 0, t_end) : tok_mask8(tb, 0, t_end);
+          }
+        }
+      }
+    }
+    bf16x8 pop[NT], pop_lo[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float psum = 0.f;
+      uint32_t ph[2][2], pl[2][2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[nt][h][i], p.qk_scale, -m_use[nt]));
+          psum += pv[i];
+          if constexpr (KVT == PKV_KV_INT8) {
+            const int t = tok0 + 16 * h + 4 * j + i;
+            pv[i] = (unmasked || t < lim[nt]) ? pv[i] * r.vsc[h][i] : 0.f;   // fold the V scale into p
+          }
+        }
+        ph[h][0] = pack_bf16x2(pv[0], pv[1]);
+        ph[h][1] = pack_bf16x2(pv[2], pv[3]);
+        pl[h][0] = pack_bf16x2(pv[0] - bf16_lo(ph[h][0]), pv[1] - bf16_hi(ph[h][0]));
+        pl[h][1] = pack_bf16x2(pv[2] - bf16_lo(ph[h][1]), pv[3] - bf16_hi(ph[h][1]));
+      }
+      if constexpr (I4) {
+        // the sum the 136 offset of V is taken back with: that of the p the
+        // products use (hi + lo parts), which is also the softmax denominator
+        psum = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+            psum += (bf16_lo(ph[h][e]) + bf16_lo(pl[h][e])) + (bf16_hi(ph[h][e]) + bf16_hi(pl[h][e]));
+      }
+      l_run[nt] = l_run[nt] * alpha[nt] + psum;
+      pop[nt] = __builtin_bit_cast(bf16x8, u32x4{ph[0][0], ph[0][1], ph[1][0], ph[1][1]});
+      pop_lo[nt] = __builtin_bit_cast(bf16x8, u32x4{pl[0][0], pl[0][1], pl[1][0], pl[1][1]});
+    }
+#pragma unroll
+    for (int cc = 0; cc < T::NC; ++cc) {
+      uint32_t a0, a1, a2, a3;
+      if constexpr (I4) {
+        // word cc / 2 of the V piece: pairs (cc % 2) and 2 + (cc % 2) are
+        // tokens 0, 1 and 2, 3 of the group, dim 16 cc + row
+        const uint32_t w0 = r.v[0][0][cc >> 1], w1 = r.v[1][0][cc >> 1];
+        a0 = int4_pair(w0, cc & 1);
+        a1 = int4_pair(w0, 2 + (cc & 1));
+        a2 = int4_pair(w1, cc & 1);
+        a3 = int4_pair(w1, 2 + (cc & 1));
+      } else if constexpr (E == 2) {
+        const int u = cc >> 1, e = cc & 1;
+        a0 = r.v[0][u][2 * e];
+        a1 = r.v[0][u][2 * e + 1];
+        a2 = r.v[1][u][2 * e];
+        a3 = r.v[1][u][2 * e + 1];
+      } else {
+        const int u = cc >> 2, e = cc & 3;
+        widen4<KVT>(r.v[0][u][e], a0, a1);
+        widen4<KVT>(r.v[1][u][e], a2, a3);
+      }
+      const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{a0, a1, a2, a3});
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[nt][cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop[nt], acc[nt][cc], 0, 0, 0);
+        acc[nt][cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_lo[nt], acc[nt][cc], 0, 0, 0);
+      }
+    }
+  };
+
+  // NB - 1 steps in flight ahead of the one computed.  Every iteration issues
+  // the same loads (a step past the end reads a tile the table clamps into
+  // the pool, unused) so that each wait covers exactly one step's loads.
+  StepRegs<D, KVT> r[NB];
+  auto issue = [&](StepRegs<D, KVT>& rr, int tok0) __attribute__((always_inline)) {
+    if constexpr (I4)
+      issue_step_int4<D, B>(rr, p, bt_row, g, tok0, lane);
+    else
+      issue_step<D, KVT, B>(rr, p, bt_row, g, tok0, 0, lane);
+  };
+  static_for<NB - 1>([&](auto b) __attribute__((always_inline)) { issue(r[b], (int)b * kStep); });
+  int i = 0;
+  while (i < nsteps) {
+    static_for<NB>([&](auto b) __attribute__((always_inline)) {   // buffer indices are constants
+      if (i < nsteps) {
+        issue(r[(b + NB - 1) % NB], (i + NB - 1) * kStep);
+        compute(r[b], i * kStep);
+        ++i;
+      }
+    });
+  }
+
+  // outputs: column `row` of tile nt; this lane holds dims acc_dim(cc, j, .)
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int cl = 16 * nt + row;
+    const float L = sum_x32(sum_x16(l_run[nt]));
+    if (cl >= cols) continue;
+    const int cq = c0 + cl;
+    float* orow = p.out + ((int64_t)(q0 + cq / p.G) * p.Hq + g * p.G + cq % p.G) * D;
+    const float inv = L > 0.f ? 1.f / L : 0.f;   // no key at all (position < 0): zero row
+    float o[T::NC][4];
+#pragma unroll
+    for (int cc = 0; cc < T::NC; ++cc)
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        const int d = acc_dim<AL>(cc, j, i2);
+        // INT4: the V operand held 136 + code
+        const float a = I4 ? acc[nt][cc][i2] - kInt4Bias * L : acc[nt][cc][i2];
+        o[cc][i2] = a * inv * (p.vs_ch ? p.vs_ch[g * D + d] : p.out_scale);
+      }
+    if constexpr (I4) {
+      // tile cc holds dims 16 cc + 4j + {0 .. 3}
+#pragma unroll
+      for (int cc = 0; cc < T::NC; ++cc)
+        *reinterpret_cast<f32x4*>(orow + 16 * cc + 4 * j) = f32x4{o[cc][0], o[cc][1], o[cc][2], o[cc][3]};
+    } else if constexpr (E == 2) {
+      // tiles 2u, 2u + 1 hold dims 32u + 8j + 2 i2 + {0, 1}: 8 consecutive floats
+#pragma unroll
+      for (int u = 0; u < T::NC / 2; ++u) {
+        float* dst = orow + 32 * u + 8 * j;
+        *reinterpret_cast<f32x4*>(dst) = f32x4{o[2 * u][0], o[2 * u + 1][0], o[2 * u][1], o[2 * u + 1][1]};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[2 * u][2], o[2 * u + 1][2], o[2 * u][3], o[2 * u + 1][3]};
+      }
+    } else {
+      // tiles 4u .. 4u + 3 hold dims 64u + 16j + 4 i2 + {0 .. 3}
+#pragma unroll
+      for (int u = 0; u < T::NC / 4; ++u)
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2)
+          *reinterpret_cast<f32x4*>(orow + 64 * u + 16 * j + 4 * i2) =
+              f32x4{o[4 * u][i2], o[4 * u + 1][i2], o[4 * u + 2][i2], o[4 * u + 3][i2]};
+    }
+  }
+}
+
+hipError_t launch_prefill(const PrefillParams& p, int D, int kvt, int B, int grid, hipStream_t stream) {
+  return with_variant<true>(D, kvt, B, [&](auto dc, auto kc, auto bc) {
+    hipLaunchKernelGGL((pa_prefill_kernel<decltype(dc)::value, decltype(kc)::value, decltype(bc)::value>),
+                       dim3(grid), dim3(kWave * kNW), 0, stream, p);
+    return hipGetLastError();
+  });
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" pkv_status paged_attn_prefill(float* out, const void* q, const pkv_pool* pool, int32_t layer,
+                                         const int32_t* block_tables, int32_t table_width,
+                                         const int32_t* context_lens, const int32_t* query_start,
+                                         int32_t num_seqs, int32_t num_queries, int32_t max_query_len,
+                                         int32_t num_q_heads, float scale, int32_t kv_dtype,
+                                         const pkv_kv_scales* kv_scales, hipStream_t stream) {
+  pkv_status st = check_pool(pool);
+  if (st != PKV_OK) return st;
+  const pkv_pool_config& c = pool->cfg;
+  if (kv_dtype != c.kv_dtype) {
+    set_error("kv_dtype %d does not match the pool's %d", kv_dtype, c.kv_dtype);
+    return PKV_ERR_INVALID;
+  }
+  if (layer < 0 || layer >= c.num_layers) {
+    set_error("layer %d outside [0, %d)", layer, c.num_layers);
+    return PKV_ERR_INVALID;
+  }
+  if (num_seqs < 0 || num_queries < 0 || max_query_len < 0)
+    return fail(PKV_ERR_INVALID, "num_seqs, num_queries and max_query_len must not be negative");
+  if (num_seqs == 0 || num_queries == 0 || max_query_len == 0) { clear_error(); return PKV_OK; }
+  if (!out || !q || !block_tables || !context_lens || !query_start) return fail(PKV_ERR_INVALID, "NULL device pointer");
+  if (num_q_heads <= 0 || num_q_heads % c.num_kv_heads != 0) {
+    set_error("num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads, c.num_kv_heads);
+    return PKV_ERR_INVALID;
+  }
+  if (table_width <= 0) return fail(PKV_ERR_INVALID, "table_width must be positive");
+  if ((int64_t)table_width * c.block_size > INT32_MAX / 2) return fail(PKV_ERR_INVALID, "table_width too large");
+  if (!(scale > 0.f) || !(scale < INFINITY)) return fail(PKV_ERR_INVALID, "scale must be positive and finite");
+  if (c.head_dim != 64 && c.head_dim != 128) {
+    set_error("head_dim %d not built (64, 128)", c.head_dim);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (c.block_size != 8 && c.block_size != 16 && c.block_size != 32) {
+    set_error("block_size %d not built (8, 16, 32)", c.block_size);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (((uintptr_t)q) % 16 || ((uintptr_t)out) % 16) return fail(PKV_ERR_INVALID, "q and out must be 16-byte aligned");
+  float ksc = 1.f, vsc = 1.f;
+  if (kv_scales && (c.kv_dtype == PKV_KV_FP8_E5M2 || c.kv_dtype == PKV_KV_INT8_TENSOR)) {
+    ksc = kv_scales->k_scale;
+    vsc = kv_scales->v_scale;
+    if (!(ksc > 0.f) || !(vsc > 0.f) || !(ksc < INFINITY) || !(vsc < INFINITY))
+      return fail(PKV_ERR_INVALID, "per-tensor scales must be positive and finite");
+  }
+  const bool channel = has_channel_scales(c.kv_dtype);
+  if (channel && (const void*)out == q)
+    return fail(PKV_ERR_INVALID, "out must not alias q for storage with per-channel scales");
+  const int32_t G = num_q_heads / c.num_kv_heads;
+  const int64_t span = 16 * kPrefillNT * kNW;   // columns per workgroup
+  const int64_t tiles = ((int64_t)max_query_len * G + span - 1) / span;
+  const int64_t items = (int64_t)num_seqs * c.num_kv_heads * tiles;
+  if (items > INT32_MAX / 2) return fail(PKV_ERR_INVALID, "too many query tiles in one call");
+  const uint64_t scale_layer = channel ? (uint64_t)c.num_kv_heads * c.head_dim
+                                      : (uint64_t)c.num_blocks * c.num_kv_heads * c.block_size;
+  float* ksl = pool->k_scale ? pool->k_scale + layer * scale_layer : nullptr;
+  float* vsl = pool->v_scale ? pool->v_scale + layer * scale_layer : nullptr;
+  const uint16_t* qk = static_cast<const uint16_t*>(q);
+  int32_t q_stride = c.head_dim;
+  if (channel) {   // the K channel scales folded into the query, written into the output rows first
+    const int64_t n = (int64_t)num_queries * num_q_heads * c.head_dim;
+    const int64_t blocks = (n + 255) / 256;
+    if (blocks > INT32_MAX) return fail(PKV_ERR_INVALID, "too many queries in one call");
+    hipLaunchKernelGGL(fold_q_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, qk,
+                       reinterpret_cast<uint16_t*>(out), ksl, n, num_q_heads, G, c.head_dim);
+    qk = reinterpret_cast<const uint16_t*>(out);
+    q_stride = 2 * c.head_dim;
+  }
+  PrefillParams pp{};
+  DecodeParams& p = pp.d;
+  p.q = qk;
+  p.q_stride = q_stride;
+  p.vs_ch = channel ? vsl : nullptr;
+  p.out = out;
+  p.k = static_cast<char*>(pool->k) + (uint64_t)layer * pool->layer_bytes;
+  p.v = static_cast<char*>(pool->v) + (uint64_t)layer * pool->layer_bytes;
+  p.ks = ksl;
+  p.vs = vsl;
+  p.bt = block_tables;
+  p.ctx = context_lens;
+  p.W = table_width;
+  p.S = num_seqs;
+  p.Hq = num_q_heads;
+  p.Hkv = c.num_kv_heads;
+  p.G = G;
+  p.QT = 1;
+  p.num_blocks = c.num_blocks;
+  p.num_items = (int32_t)items;
+  p.win = 0;
+  p.qk_scale = scale * kLog2e * ksc;
+  p.out_scale = vsc;
+  pp.qstart = query_start;
+  pp.tiles = (int32_t)tiles;
+  pp.T = num_queries;
+  const hipError_t e = launch_prefill(pp, c.head_dim, c.kv_dtype, c.block_size, (int)((items + 7) / 8 * 8), stream);
+  if (e != hipSuccess) {
+    set_error("paged_attn_prefill launch failed: %s", hipGetErrorString(e));
+    return PKV_ERR_HIP;
+  }
+  clear_error();
+  return PKV_OK;
+}

@@ -1,8 +1,9 @@
 """Paged prefill on the GPU against the oracle: chunks of new tokens (whole
 prompts, partial chunks after a cached prefix, single tokens, empty chunks,
 chunks longer than the context) over pools written by the GPU cache write,
-for every storage type the single-pass form serves, both head dims, block
-sizes 8 / 16 / 32 and several group sizes.
+for every storage type (bf16, fp8, int8 per token / per tensor / per
+channel, int4), both head dims, block sizes 8 / 16 / 32 and several group
+sizes.
 """
 
 import math
@@ -44,12 +45,14 @@ def _run(rng, dt, ctx, chunk, hkv=2, G=4, D=128, B=16, poison=True):
     else:
         pool.memory.zero_()
     _, _, ks_off, vs_off = pool.region_offsets()
-    if dt == pkv.PKV_KV_INT8_CHANNEL:
+    if dt in (pkv.PKV_KV_INT8_CHANNEL, pkv.PKV_KV_INT4):
+        # calibrated channel scales: ~absmax / 127 (int8) or / 7 (int4) of N(0, 1) data
+        lo, hi = (0.02, 0.05) if dt == pkv.PKV_KV_INT8_CHANNEL else (0.3, 0.6)
         n = hkv * D
         pool.memory[ks_off:ks_off + 4 * n].view(torch.float32).copy_(
-            torch.from_numpy(rng.uniform(0.02, 0.05, n).astype(np.float32)))
+            torch.from_numpy(rng.uniform(lo, hi, n).astype(np.float32)))
         pool.memory[vs_off:vs_off + 4 * n].view(torch.float32).copy_(
-            torch.from_numpy(rng.uniform(0.02, 0.05, n).astype(np.float32)))
+            torch.from_numpy(rng.uniform(lo, hi, n).astype(np.float32)))
     ks, vs = SCALES.get(dt, (1.0, 1.0))
     total = int(ctx.sum())
     k = workloads.to_bf16_bits(rng.standard_normal((max(total, 1), hkv, D), dtype=np.float32))
@@ -78,7 +81,7 @@ def _run(rng, dt, ctx, chunk, hkv=2, G=4, D=128, B=16, poison=True):
 
 
 @pytest.mark.parametrize("dt", [pkv.PKV_KV_BF16, pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8, pkv.PKV_KV_INT8_TENSOR,
-                                pkv.PKV_KV_INT8_CHANNEL])
+                                pkv.PKV_KV_INT8_CHANNEL, pkv.PKV_KV_INT4])
 @pytest.mark.parametrize("D,B", [(128, 16), (64, 32), (128, 8), (64, 16)])
 def test_prefill_matches_oracle(dt, D, B):
     say(f"prefill dt={dt} D={D} B={B}")
@@ -112,12 +115,12 @@ def test_prefill_long_prompt_many_tiles():
     assert mx <= BAR[pkv.PKV_KV_BF16][0] and rel <= BAR[pkv.PKV_KV_BF16][1]
 
 
-def test_prefill_refuses_int4():
-    import torch
-    cfg = pkv.make_config(1, 4, 16, 1, 128, pkv.PKV_KV_INT4)
-    pool = pkv.Pool(cfg)
-    out = torch.zeros((2, 2, 128), dtype=torch.float32, device="cuda")
-    q = torch.zeros((2, 2, 128), dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(pkv.PkvError, match="INT4"):
-        pkv.paged_attn_prefill(out, q, pool, 0, dev(np.zeros((1, 1), np.int32)), dev(np.array([2], np.int32)),
-                               dev(np.array([0, 2], np.int32)), 0.1, 2)
+def test_prefill_int4_group_sizes():
+    """INT4 over several group sizes, with a long chunk spanning many steps."""
+    say("prefill int4 groups")
+    rng = np.random.default_rng(15300)
+    for G, hkv in ((1, 2), (8, 1), (24, 1)):
+        got, want = _run(rng, pkv.PKV_KV_INT4, [300, 45], [300, 20], hkv=hkv, G=G)
+        mx, rel = errors(got, want)
+        say(f"  G={G}: max_abs={mx:.3e} rel={rel:.3e}")
+        assert mx <= BAR8[0] and rel <= BAR8[1]
