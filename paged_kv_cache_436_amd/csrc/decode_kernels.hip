@@ -1432,8 +1432,8 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     if (!(ksc > 0.f) || !(vsc > 0.f) || !(ksc < INFINITY) || !(vsc < INFINITY))
       return fail(PKV_ERR_INVALID, "per-tensor scales must be positive and finite");
   }
-  if (c.kv_dtype == PKV_KV_INT4 && partition_size == 0)
-    return fail(PKV_ERR_UNSUPPORTED, "INT4 storage decodes in the split-context form (partition_size > 0)");
+  if (c.kv_dtype == PKV_KV_INT4 && partition_size == 0 && sliding_window > 0)
+    return fail(PKV_ERR_UNSUPPORTED, "INT4 storage with a sliding window decodes in the split-context form");
   const bool channel = has_channel_scales(c.kv_dtype);
   if (channel && (const void*)out == q)
     return fail(PKV_ERR_INVALID, "out must not alias q for storage with per-channel scales");
@@ -1462,7 +1462,26 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
   }
 
   hipError_t e = hipSuccess;
-  if (partition_size == 0) {
+  if (partition_size == 0 && c.kv_dtype == PKV_KV_INT4) {
+    // one query per sequence through the prefill kernel, which reads INT4
+    PrefillDecodeArgs a{};
+    a.out = out;
+    a.q = qk;
+    a.q_stride = q_stride;
+    a.pool = pool;
+    a.layer = layer;
+    a.block_tables = block_tables;
+    a.table_width = table_width;
+    a.context_lens = context_lens;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.qk_scale = scale * kLog2e * ksc;
+    a.out_scale = vsc;
+    a.ks = ksl;
+    a.vs = vsl;
+    a.vs_ch = vsl;
+    e = launch_prefill_as_decode(a, stream);
+  } else if (partition_size == 0) {
     const int64_t grid = (rows + 7) / 8 * 8;
     if (grid > INT32_MAX) return fail(PKV_ERR_INVALID, "too many work items");
     DecodeParams p{};

@@ -53,4 +53,26 @@ bool pool_regions(const pkv_pool_config* cfg, Regions* r);
 
 pkv_status check_pool(const pkv_pool* pool);
 
+// The single-pass decode of one query per sequence run by the prefill kernel
+// (prefill_kernels.hip), for storage the single-pass decode kernel does not
+// read.  Arguments are checked by the caller; q is the query the kernels read
+// (folded for per-channel scales, q_stride elements between rows).
+struct PrefillDecodeArgs {
+  float* out;
+  const uint16_t* q;
+  int32_t q_stride;
+  const pkv_pool* pool;
+  int32_t layer;
+  const int32_t* block_tables;
+  int32_t table_width;
+  const int32_t* context_lens;
+  int32_t num_seqs, num_q_heads;
+  float qk_scale;           // softmax scale * log2(e) (* fp8 k scale)
+  float out_scale;          // per-tensor v scale, else 1
+  const float* ks;          // this layer's K / V scale regions, or null
+  const float* vs;
+  const float* vs_ch;       // per-channel V scales of the layer, or null
+};
+hipError_t launch_prefill_as_decode(const PrefillDecodeArgs& a, hipStream_t stream);
+
 }  // namespace pkv

@@ -76,7 +76,8 @@ __device__ __forceinline__ void issue_step_int4(StepRegs<D, PKV_KV_INT4>& r, con
 
 struct PrefillParams {
   DecodeParams d;             // q [T][Hq][D] (or the folded q), out [T][Hq][D], pool layer, tables, lengths
-  const int32_t* qstart;      // [S + 1]: sequence s's queries are rows qstart[s] .. qstart[s+1] - 1
+  const int32_t* qstart;      // [S + 1]: sequence s's queries are rows qstart[s] .. qstart[s+1] - 1;
+                              // null: one query per sequence, row s (a decode step)
   int32_t tiles;              // workgroup column spans per (sequence, KV head):
                               // ceil(max_query_len * G / (16 kPrefillNT kNW))
   int32_t T;                  // rows of q and out
@@ -109,8 +110,8 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
   const int row = lane & 15;
   const int j = lane >> 4;
   // query rows, kept inside [0, T) whatever query_start holds
-  const int q0 = min(max(pp.qstart[s], 0), pp.T);
-  const int n = min(max(pp.qstart[s + 1], q0), pp.T) - q0;
+  const int q0 = pp.qstart ? min(max(pp.qstart[s], 0), pp.T) : s;
+  const int n = pp.qstart ? min(max(pp.qstart[s + 1], q0), pp.T) - q0 : 1;
   const int ncol = n * p.G;
   const int c0 = (ct * kNW + w) * 16 * NT;       // this wave's first column
   if (c0 >= ncol) return;                        // no barrier follows: waves are independent
@@ -406,6 +407,45 @@ hipError_t launch_prefill(const PrefillParams& p, int D, int kvt, int B, int gri
 }
 
 }  // namespace
+
+// A decode step as a prefill of one token per sequence: the single-pass
+// decode of storage types the single-pass decode kernel does not read (INT4).
+hipError_t launch_prefill_as_decode(const PrefillDecodeArgs& a, hipStream_t stream) {
+  const pkv_pool_config& c = a.pool->cfg;
+  const int32_t G = a.num_q_heads / c.num_kv_heads;
+  const int64_t span = 16 * kPrefillNT * kNW;
+  const int64_t tiles = (G + span - 1) / span;
+  const int64_t items = (int64_t)a.num_seqs * c.num_kv_heads * tiles;
+  if (items > INT32_MAX / 2) return hipErrorInvalidValue;
+  PrefillParams pp{};
+  DecodeParams& p = pp.d;
+  p.q = a.q;
+  p.q_stride = a.q_stride;
+  p.vs_ch = a.vs_ch;
+  p.out = a.out;
+  p.k = static_cast<char*>(a.pool->k) + (uint64_t)a.layer * a.pool->layer_bytes;
+  p.v = static_cast<char*>(a.pool->v) + (uint64_t)a.layer * a.pool->layer_bytes;
+  p.ks = a.ks;
+  p.vs = a.vs;
+  p.bt = a.block_tables;
+  p.ctx = a.context_lens;
+  p.W = a.table_width;
+  p.S = a.num_seqs;
+  p.Hq = a.num_q_heads;
+  p.Hkv = c.num_kv_heads;
+  p.G = G;
+  p.QT = 1;
+  p.num_blocks = c.num_blocks;
+  p.num_items = (int32_t)items;
+  p.win = 0;
+  p.qk_scale = a.qk_scale;
+  p.out_scale = a.out_scale;
+  pp.qstart = nullptr;
+  pp.tiles = (int32_t)tiles;
+  pp.T = a.num_seqs;
+  return launch_prefill(pp, c.head_dim, c.kv_dtype, c.block_size, (int)((items + 7) / 8 * 8), stream);
+}
+
 }  // namespace pkv
 
 using namespace pkv;

@@ -2,7 +2,7 @@
 two per byte) on the GPU, against the oracle: the cache write bit for bit,
 the split-context decode (with and without a window) within the quantised
 bar, the appending form giving the bits of the two calls, and the
-single-pass form refusing INT4.
+single-pass form (one query per sequence through the prefill kernel).
 """
 
 import math
@@ -119,11 +119,21 @@ def test_group_sizes(G, hkv):
     assert mx <= BAR[0] and rel <= BAR[1]
 
 
-def test_single_pass_form_refuses_int4():
-    rng = np.random.default_rng(13180)
-    c = _case(rng, [5, 20])
-    with pytest.raises(pkv.PkvError, match="split-context"):
-        _decode(c, 0)
+@pytest.mark.parametrize("D,B,G,hkv", [(128, 16, 4, 2), (64, 32, 3, 1), (128, 8, 8, 1), (128, 16, 24, 1)])
+def test_single_pass_form_matches_oracle(D, B, G, hkv):
+    """partition_size 0 (one query per sequence through the prefill kernel)."""
+    say(f"int4 single pass D={D} B={B} G={G}")
+    rng = np.random.default_rng(13180 + D + B + G)
+    c = _case(rng, [1, 15, 16, 17, 100, 0, 333, 700], hkv=hkv, G=G, D=D, B=B)
+    got, scale = _decode(c, 0)
+    want = attention.paged_decode(c.q, c.img, 1, c.tables, c.ctx, scale)
+    assert np.all(np.isfinite(got))
+    mx, rel = errors(got, want)
+    say(f"  max_abs={mx:.3e} rel={rel:.3e}")
+    assert mx <= BAR[0] and rel <= BAR[1]
+    assert not got[c.ctx == 0].any()
+    with pytest.raises(pkv.PkvError, match="split-context"):   # a window needs the split form
+        _decode(c, 0, window=40)
 
 
 def test_appending_decode_equals_two_calls():
