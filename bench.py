@@ -65,10 +65,12 @@ def parse():
                          "(paged_attn_decode_ex; bytes counted over those positions)")
     ap.add_argument("--kv-dtype", default="bf16", choices=sorted(KV_DTYPES),
                     help="KV storage of the pool (8-bit pools hold random codes; the oracle sample runs for bf16 only)")
-    ap.add_argument("--config", default="", choices=["", "llama8b", "long32k_fp8", "long32k_int8"],
+    ap.add_argument("--config", default="", choices=["", "llama8b", "long32k_fp8", "long32k_int8", "cow_prefix"],
                     help="instead of the 70B step: one decode layer of another workload (8B-shaped: 64 seqs, "
                          "ctx 512..4096; 32K quantised: 8 seqs x 32768, block 32, partition 512), rotating over "
-                         "three pool copies so the 256 MB MALL does not hold the working set")
+                         "three pool copies so the 256 MB MALL does not hold the working set; cow_prefix: the "
+                         "shared-prefix copy-on-write run, 200 sequences forked from a 1500-token prefix, each "
+                         "generating 64..512 tokens)")
     ap.add_argument("--prefix-cache", type=int, default=0,
                     help="host only: N requests sharing a 1500-token system prompt through the block manager's "
                          "prefix cache; report microseconds per request and the prefill tokens it saves")
@@ -191,6 +193,108 @@ def config_bench(args):
            "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    print(json.dumps(res), flush=True)
+
+
+def cow_bench(args):
+    """The shared-prefix copy-on-write run: 200 sequences (40 KV heads, MHA,
+    head_dim 128, block 16) forked from one 1500-token prefix whose last block
+    is partly filled, each generating 64..512 tokens.  Every step: host
+    block-manager append (step 0 copies the shared partial block for 199 of
+    the 200 sharers), upload of tables and lengths, copy_blocks when there
+    are pairs, and one appending decode launch for the active sequences.  The
+    whole run is timed between synchronisations, after warm-up decodes of the
+    shared state.  Logical bytes count every sequence's whole context; unique
+    bytes count the shared prefix blocks once."""
+    import torch
+
+    import paged_kv_cache_436_amd as pkv
+    import workloads
+
+    w = workloads.cow_prefix()
+    S, H, D, B, W = w.num_seqs, w.num_kv_heads, w.head_dim, w.block_size, w.table_width
+    gen = np.asarray(w.extra["gen_steps"], np.int64)
+    prefix = int(w.extra["prefix"])
+    dev = torch.device("cuda:0")
+    cfg = pkv.make_config(1, w.num_blocks, B, H, D)
+    pool = pkv.Pool(cfg, device=dev)
+    pool.memory.zero_()
+    bm = pkv.BlockManager(w.num_blocks, B, w.block_order)
+    bm.add_seq(0, prefix)
+    for i in range(1, S):
+        bm.fork(0, i)
+    tab0, _ = bm.block_tables([0], W)
+    g = torch.Generator(device=dev)
+    g.manual_seed(436009)
+    k_pre = torch.randn((prefix, H, D), generator=g, device=dev).to(torch.bfloat16)
+    v_pre = torch.randn((prefix, H, D), generator=g, device=dev).to(torch.bfloat16)
+    pre_slots = np.array([tab0[0][t // B] * B + t % B for t in range(prefix)], np.int64)
+    pkv.reshape_and_cache(pool, 0, k_pre, v_pre, torch.from_numpy(pre_slots).to(dev))
+    steps = int(gen.max())
+    q_all = torch.randn((S, H, D), generator=g, device=dev).to(torch.bfloat16)
+    kn = torch.randn((S, H, D), generator=g, device=dev).to(torch.bfloat16)
+    vn = torch.randn((S, H, D), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty((S, H, D), dtype=torch.float32, device=dev)
+    P = (W * B + 31) // 32 * 32
+    ws = torch.empty(pkv.paged_attn_workspace_bytes(S, H, D, W, B, P), dtype=torch.uint8, device=dev)
+    st = torch.cuda.current_stream()
+    tab_h = torch.empty((S, W), dtype=torch.int32, pin_memory=True)
+    ctx_h = torch.empty(S, dtype=torch.int32, pin_memory=True)
+    tab_d = torch.empty((S, W), dtype=torch.int32, device=dev)
+    ctx_d = torch.empty(S, dtype=torch.int32, device=dev)
+    # warm-up: decodes of the shared state (no append, nothing changes)
+    t0s, c0s = bm.block_tables(np.arange(S, dtype=np.int32), W)
+    td, cd = torch.from_numpy(t0s).to(dev), torch.from_numpy(c0s).to(dev)
+    for _ in range(args.warmup):
+        pkv.paged_attn_decode(out, q_all, pool, 0, td, cd, w.scale, partition_size=P, workspace=ws, stream=st)
+    torch.cuda.synchronize()
+    logical = unique = seq_steps = pairs_total = 0
+    ev = []
+    prefix_blocks = prefix // B                  # full prefix blocks stay shared for the whole run
+    t_start = time.perf_counter()
+    for step in range(steps):
+        active = np.nonzero(gen > step)[0].astype(np.int32)
+        n = active.size
+        slots, pairs = bm.append(active)
+        tab_np, ctx_np = bm.block_tables(active, W, out=tab_h.numpy()[:n], ctx_out=ctx_h.numpy()[:n])
+        tab_d[:n].copy_(tab_h[:n], non_blocking=True)
+        ctx_d[:n].copy_(ctx_h[:n], non_blocking=True)
+        if pairs.shape[0]:
+            pkv.copy_blocks(pool, torch.from_numpy(pairs).to(dev, non_blocking=False), stream=st)
+            pairs_total += pairs.shape[0]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        pkv.paged_attn_decode_append(out[:n], q_all[:n], pool, 0, kn[:n], vn[:n], tab_d[:n], ctx_d[:n], w.scale,
+                                     partition_size=P, workspace=ws, stream=st)
+        e1.record(st)
+        ev.append((e0, e1))
+        ctx64 = ctx_np.astype(np.int64)
+        logical += int(ctx64.sum()) * H * 2 * D * 2
+        unique += (int((ctx64 - prefix_blocks * B).sum()) + prefix_blocks * B) * H * 2 * D * 2
+        seq_steps += n
+        # the host reuses the pinned buffers next step: the copies must be done
+        st.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    gpu = sum(a.elapsed_time(b) for a, b in ev) * 1e-3
+    blk_bytes = H * 2 * D * 2 * B
+    res = {"metric": "paged decode KV-read GB/s (% of MI355X HBM peak) + decode seq-steps/s",
+           "value": round(seq_steps / wall, 1), "unit": "seq-steps/s", "n_gpus": 1, "steps": steps,
+           "warmup": args.warmup, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "shared-prefix copy-on-write run: 200 seqs forked from a 1500-token prefix, "
+                                  "40q/40kv heads, head_dim 128, bf16 KV, block 16, 64..512 generated tokens each, "
+                                  "appending decode per step",
+                      "seq_steps": seq_steps, "cow_pairs": pairs_total},
+           "wall_s": round(wall, 4), "decode_gpu_s": round(gpu, 4),
+           "logical_kv_gbs_decode": round(logical / gpu / 1e9, 1),
+           "unique_kv_gbs_decode": round(unique / gpu / 1e9, 1),
+           "unique_pct_of_hbm_peak": round(100 * unique / gpu / 1e9 / HBM_PEAK_GBS, 2),
+           "bytes_saved_by_sharing_at_end": (S - 1) * prefix_blocks * blk_bytes,
+           "roofline": {"bound": "hbm", "achieved": round(unique / gpu / 1e9, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(unique / gpu / 1e9 / HBM_PEAK_GBS, 4),
+                        "bytes": "unique KV bytes (shared prefix counted once) / summed decode launch time"}}
+    log(f"cow run: {steps} steps, {seq_steps} seq-steps in {wall:.3f} s wall, decode launches {gpu:.3f} s; "
+        f"logical {logical / gpu / 1e9:.0f} GB/s, unique {unique / gpu / 1e9:.0f} GB/s")
     print(json.dumps(res), flush=True)
 
 
@@ -417,6 +521,9 @@ def main():
         return
     if args.prefix_cache:
         prefix_cache_bench(args)
+        return
+    if args.config == "cow_prefix":
+        cow_bench(args)
         return
     if args.config:
         config_bench(args)
