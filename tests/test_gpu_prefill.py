@@ -24,7 +24,7 @@ BAR8 = (2e-2, 5e-3)
 SCALES = {pkv.PKV_KV_FP8_E5M2: (0.5, 1.5), pkv.PKV_KV_INT8_TENSOR: (0.035, 0.03)}
 
 
-def _run(rng, dt, ctx, chunk, hkv=2, G=4, D=128, B=16, poison=True):
+def _run(rng, dt, ctx, chunk, hkv=2, G=4, D=128, B=16, poison=True, needles=0):
     import torch
     ctx = np.asarray(ctx, np.int32)
     S = len(ctx)
@@ -57,6 +57,27 @@ def _run(rng, dt, ctx, chunk, hkv=2, G=4, D=128, B=16, poison=True):
     total = int(ctx.sum())
     k = workloads.to_bf16_bits(rng.standard_normal((max(total, 1), hkv, D), dtype=np.float32))
     v = workloads.to_bf16_bits(rng.standard_normal((max(total, 1), hkv, D), dtype=np.float32))
+    chunk = np.asarray(chunk, np.int32)
+    qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    T = int(qs[-1])
+    hq = hkv * G
+    q_pre = None
+    if needles:
+        # peaked inputs: in each sequence, `needles` positions get K = 4 sqrt(D)
+        # q / |q| of the chunk's last query (first head of each KV head's
+        # group), so a few keys carry most of the softmax mass
+        q_pre = workloads.to_bf16_bits(rng.standard_normal((max(T, 1), hq, D), dtype=np.float32))[:T]
+        qf = q_pre.astype(np.uint32) << 16
+        qf = qf.view(np.float32).astype(np.float64)
+        offs = np.concatenate([[0], np.cumsum(ctx)])
+        for s_ in range(S):
+            if chunk[s_] == 0 or ctx[s_] == 0:
+                continue
+            picks = rng.choice(int(ctx[s_]), size=min(needles, int(ctx[s_])), replace=False)
+            for g in range(hkv):
+                qh = qf[qs[s_ + 1] - 1, g * G]
+                nv = (qh / max(np.linalg.norm(qh), 1e-6) * 4.0 * math.sqrt(D)).astype(np.float32)
+                k[offs[s_] + picks, g, :] = workloads.to_bf16_bits(np.tile(nv, (picks.size, 1)))
     img = read_pool(pool)
     if total:
         slots = np.concatenate([expanded_slots(tables[s], int(ctx[s]), B) for s in range(S)])
@@ -64,11 +85,8 @@ def _run(rng, dt, ctx, chunk, hkv=2, G=4, D=128, B=16, poison=True):
                               k_scale=ks, v_scale=vs)
         img = cache_ops.reshape_and_cache(img, 0, k[:total], v[:total], slots, ks, vs)
         assert images_equal(read_pool(pool), img), first_diff(read_pool(pool), img)
-    chunk = np.asarray(chunk, np.int32)
-    qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
-    T = int(qs[-1])
-    hq = hkv * G
-    q = workloads.to_bf16_bits(rng.standard_normal((max(T, 1), hq, D), dtype=np.float32))[:T]
+    q = q_pre if q_pre is not None else \
+        workloads.to_bf16_bits(rng.standard_normal((max(T, 1), hq, D), dtype=np.float32))[:T]
     scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
     out = torch.full((max(T, 1), hq, D), float("nan"), dtype=torch.float32, device="cuda")
     pkv.paged_attn_prefill(out, bf16_dev(q) if T else torch.empty((0, hq, D), dtype=torch.bfloat16, device="cuda"),
@@ -124,3 +142,17 @@ def test_prefill_int4_group_sizes():
         mx, rel = errors(got, want)
         say(f"  G={G}: max_abs={mx:.3e} rel={rel:.3e}")
         assert mx <= BAR8[0] and rel <= BAR8[1]
+
+
+@pytest.mark.parametrize("dt", [pkv.PKV_KV_BF16, pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8, pkv.PKV_KV_INT4])
+def test_prefill_peaked_needles(dt):
+    """Planted needle keys: reading a wrong block or mis-masking a column
+    moves outputs by O(1); the bars are relative to max |out| ~ 1 here."""
+    say(f"prefill needles dt={dt}")
+    rng = np.random.default_rng(15400 + dt)
+    got, want = _run(rng, dt, [400, 130, 65, 1000], [400, 50, 17, 300], hkv=2, G=4, needles=8)
+    assert np.max(np.abs(want)) > 0.5          # the needles dominate
+    mx, rel = errors(got, want)
+    say(f"  max_abs={mx:.3e} rel={rel:.3e}")
+    bar = BAR.get(dt, BAR8)
+    assert mx <= bar[0] and rel <= bar[1]
