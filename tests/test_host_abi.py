@@ -209,3 +209,48 @@ def test_workload_static_tables_equal_block_manager_allocation():
         assert np.array_equal(ctx, w.context_lens)
         used = sum(math.ceil(int(c) / w.block_size) for c in w.context_lens)
         assert bm.stats()[0] == used
+
+
+def _fake_pool(dt, L=2, NB=8, B=16, H=2, D=128):
+    cfg = pkv.make_config(L, NB, B, H, D, dt)
+    desc = pkv.PoolDesc()
+    assert pkv._lib.kv_pool_create(ctypes.byref(cfg), 1 << 20, pkv.kv_pool_bytes(cfg), ctypes.byref(desc)) == 0
+    return desc
+
+
+def test_attention_entry_points_check_arguments_on_the_host():
+    """Argument errors come back as status codes before any launch: fake
+    device addresses are never dereferenced."""
+    P = 1 << 24                                   # a 16-byte aligned fake device address
+    bf16, int4 = pkv.PKV_KV_BF16, pkv.PKV_KV_INT4
+    sc = pkv.KVScales(1.0, 1.0)
+    desc = _fake_pool(bf16)
+
+    def prefill(layer=0, hq=4, scale=0.1, kvd=bf16, q=P, nseq=2, nq=5, maxq=3, d=desc):
+        return pkv._lib.paged_attn_prefill(P, q, ctypes.byref(d), layer, P, 4, P, P, nseq, nq, maxq, hq,
+                                           scale, kvd, ctypes.byref(sc), None)
+
+    assert prefill(layer=2) == pkv.PKV_ERR_INVALID and "layer" in pkv.last_error()
+    assert prefill(kvd=pkv.PKV_KV_FP8_E5M2) == pkv.PKV_ERR_INVALID and "kv_dtype" in pkv.last_error()
+    assert prefill(hq=3) == pkv.PKV_ERR_INVALID and "multiple" in pkv.last_error()
+    assert prefill(scale=0.0) == pkv.PKV_ERR_INVALID and "scale" in pkv.last_error()
+    assert prefill(q=P + 2) == pkv.PKV_ERR_INVALID and "aligned" in pkv.last_error()
+    assert prefill(nq=-1) == pkv.PKV_ERR_INVALID
+    assert prefill(nseq=0) == pkv.PKV_OK         # nothing to do: no launch
+    assert prefill(d=_fake_pool(bf16, D=96)) == pkv.PKV_ERR_UNSUPPORTED
+
+    def decode(d=desc, kvd=bf16, part=0, hq=4):
+        return pkv._lib.paged_attn_decode(P, P, ctypes.byref(d), 0, P, 4, P, 2, hq, 0.1, kvd, ctypes.byref(sc),
+                                          part, None, 0, None)
+
+    assert decode(part=33) == pkv.PKV_ERR_INVALID and "partition_size" in pkv.last_error()
+    assert decode(hq=0) == pkv.PKV_ERR_INVALID
+
+    # INT4 in the single-pass form has no sliding window (the split form has)
+    d4 = _fake_pool(int4)
+    args = pkv.DecodeArgs(out=P, q=P, pool=ctypes.pointer(d4), layer=0, key=None, value=None, block_tables=P,
+                          table_width=4, context_lens=P, num_seqs=2, num_q_heads=4, scale=0.1, kv_dtype=int4,
+                          kv_scales=ctypes.pointer(sc), partition_size=0, sliding_window=40, workspace=None,
+                          workspace_bytes=0)
+    assert pkv._lib.paged_attn_decode_ex(ctypes.byref(args), None) == pkv.PKV_ERR_UNSUPPORTED
+    assert "window" in pkv.last_error()
