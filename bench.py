@@ -88,21 +88,22 @@ def parse():
 
 
 PROFILE = os.path.join(ROOT, "profiles", "pa_split_kernel_llama70b_bf16.md")
-# the sources the split decode kernel is compiled from, hashed in this order
-KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_436_amd", "csrc", f)
-               for f in ("decode_kernels.hip", "decode_common.h", "pkv_codecs.h")]
+PREFILL_PROFILE = os.path.join(ROOT, "profiles", "pa_prefill_kernel_prefix_prefill.md")
+_CSRC = os.path.join(ROOT, "paged_kv_cache_436_amd", "csrc")
+# the sources each kernel is compiled from, hashed in this order
+KERNEL_SRCS = [os.path.join(_CSRC, f) for f in ("decode_kernels.hip", "decode_common.h", "pkv_codecs.h")]
+PREFILL_SRCS = [os.path.join(_CSRC, f) for f in ("prefill_kernels.hip", "decode_common.h", "pkv_codecs.h")]
 
 
-def measured_traffic():
-    """HBM bytes per decode launch from the committed rocprofv3 counter
-    summary, or None when the kernel's sources have changed since the
-    counters were taken (the summary records the sha256 of the sources
-    concatenated)."""
+def measured_traffic(profile=PROFILE, srcs=KERNEL_SRCS):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or
+    None when the kernel's sources have changed since the counters were
+    taken (the summary records the sha256 of the sources concatenated)."""
     import hashlib
     import re
     try:
-        text = open(PROFILE, encoding="utf-8").read()
-        src = b"".join(open(f, "rb").read() for f in KERNEL_SRCS)
+        text = open(profile, encoding="utf-8").read()
+        src = b"".join(open(f, "rb").read() for f in srcs)
     except OSError:
         return None
     m = re.search(r"traffic_bytes_per_launch = (\d+); kernel_source_sha256 = ([0-9a-f]{64})", text)
@@ -482,7 +483,9 @@ def prefill_bench(args):
                       "new_tokens": T, "max_query_len": maxq, "flops_per_call": flops},
            "roofline": {"bound": "mfma", "kernel": "pa_prefill_kernel", "achieved": round(tfs, 2),
                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+                        "frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "traffic": measured_traffic(PREFILL_PROFILE, PREFILL_SRCS),
+                        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"},
            "cpu_baseline": {"value": round(cpu_tfs, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
                             "sample": f"{seqs} sequences' prefill ({keys_done} (token, position) pairs per head), "
                                       f"{spent:.1f} s of fp64 numpy causal attention"},
