@@ -156,3 +156,50 @@ def test_prefill_peaked_needles(dt):
     say(f"  max_abs={mx:.3e} rel={rel:.3e}")
     bar = BAR.get(dt, BAR8)
     assert mx <= bar[0] and rel <= bar[1]
+
+
+def test_prefill_prefix_cache_workload_full_size_sampled():
+    """The benchmark's prefill workload at full size (200 prompts sharing the
+    93 cached blocks of a 1500-token system prompt, 60,750 new tokens, 64 q /
+    8 kv heads, the benchmark's launch), checked on sampled sequences: the
+    shortest and longest chunks and two random ones."""
+    import torch
+    from oracle import layout
+    say("prefill prefix-cache workload, full size")
+    w = workloads.prefix_prefill()
+    S, Hq, Hkv, D, B = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    ctx = np.asarray(w.context_lens, np.int32)
+    chunk = np.asarray(w.extra["chunk"], np.int32)
+    qs = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    T = int(qs[-1])
+    tabs = w.extra["tables"]
+    cfg = pkv.make_config(1, w.num_blocks, B, Hkv, D, pkv.PKV_KV_BF16)
+    pool = pkv.Pool(cfg)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(436108)
+    k_off, v_off, _, _ = pool.region_offsets()
+    lb = pool.desc.layer_bytes
+    for off in (k_off, v_off):
+        pool.memory[off: off + lb].view(torch.bfloat16).normal_(generator=g)
+    q = torch.randn((T, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.full((T, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    pkv.paged_attn_prefill(out, q, pool, 0, dev(tabs), dev(ctx), dev(qs), w.scale, int(chunk.max()))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(436109)
+    pick = sorted({int(np.argmin(chunk)), int(np.argmax(chunk)), *rng.choice(S, size=2, replace=False).tolist()})
+    qbits = q.view(torch.int16).cpu().numpy().view(np.uint16)
+    tile = pool.desc.tile_bytes
+    for s in pick:
+        nblk = math.ceil(int(ctx[s]) / B)
+        img = layout.empty_image(layout.PoolShape(1, nblk, B, Hkv, D))
+        idx = torch.from_numpy(tabs[s, :nblk].astype(np.int64)).cuda()
+        for region, dst in ((k_off, img.k), (v_off, img.v)):
+            lay = pool.memory[region: region + lb].view(w.num_blocks, Hkv * tile)
+            dst[:] = lay.index_select(0, idx).cpu().numpy().view(np.uint16).reshape(-1)
+        want = attention.paged_prefill(qbits[qs[s]:qs[s + 1]], img, 0, np.arange(nblk, dtype=np.int32)[None, :],
+                                       ctx[s:s + 1], np.array([0, chunk[s]]), w.scale)
+        got = out[qs[s]:qs[s + 1]].cpu().numpy()
+        mx, rel = errors(got, want)
+        say(f"  seq {s}: ctx {ctx[s]} chunk {chunk[s]} max_abs={mx:.3e} rel={rel:.3e}")
+        assert mx <= BAR[pkv.PKV_KV_BF16][0] and rel <= BAR[pkv.PKV_KV_BF16][1]
+    assert torch.isfinite(out).all()
