@@ -237,8 +237,7 @@ uint64_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
  *   kv_scales     host; fp8 per-tensor scales (NULL = 1.0)
  *   partition_size 0: single pass, one workgroup per (sequence, KV head), no
  *                 workspace (INT4: one query per sequence through the
- *                 paged_attn_prefill kernel; no sliding window there,
- *                 PKV_ERR_UNSUPPORTED).  Otherwise the split-context form, a positive
+ *                 paged_attn_prefill kernel).  Otherwise the split-context form, a positive
  *                 multiple of 32: the work of all sequences and heads is cut
  *                 into equal ranges, one per wavefront of a grid sized to the
  *                 GPU; each range yields one partial result per

@@ -1432,8 +1432,6 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     if (!(ksc > 0.f) || !(vsc > 0.f) || !(ksc < INFINITY) || !(vsc < INFINITY))
       return fail(PKV_ERR_INVALID, "per-tensor scales must be positive and finite");
   }
-  if (c.kv_dtype == PKV_KV_INT4 && partition_size == 0 && sliding_window > 0)
-    return fail(PKV_ERR_UNSUPPORTED, "INT4 storage with a sliding window decodes in the split-context form");
   const bool channel = has_channel_scales(c.kv_dtype);
   if (channel && (const void*)out == q)
     return fail(PKV_ERR_INVALID, "out must not alias q for storage with per-channel scales");
@@ -1475,6 +1473,7 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     a.context_lens = context_lens;
     a.num_seqs = num_seqs;
     a.num_q_heads = num_q_heads;
+    a.sliding_window = sliding_window;
     a.qk_scale = scale * kLog2e * ksc;
     a.out_scale = vsc;
     a.ks = ksl;

@@ -67,6 +67,7 @@ struct PrefillDecodeArgs {
   int32_t table_width;
   const int32_t* context_lens;
   int32_t num_seqs, num_q_heads;
+  int32_t sliding_window;   // 0: whole context; w > 0: the last w positions
   float qk_scale;           // softmax scale * log2(e) (* fp8 k scale)
   float out_scale;          // per-tensor v scale, else 1
   const float* ks;          // this layer's K / V scale regions, or null

@@ -124,6 +124,11 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
   // every valid column sees the keys below this one (column c0's limit, the
   // smallest): steps wholly below it need no causal mask
   const int lim_lo = max(0, first + c0 / p.G + 1);
+  // one query per sequence (a decode step) may attend to a sliding window:
+  // positions [t_lo, ctx); the steps start at the one holding t_lo and the
+  // keys before it are masked (their blocks may hold anything)
+  const int t_lo = pp.qstart ? 0 : window_lo(ctx, p.win);
+  const int s0 = t_lo / kStep;
   const int32_t* bt_row = p.bt + (int64_t)s * p.W;
 
   // per tile: this lane's column limit (keys [0, lim)) and the query as the
@@ -197,7 +202,7 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
     bool any_rescale = false;
     // raw logits (int8: times the token's K scale); the softmax scale s > 0
     // is applied to the max and inside the exponent's fma, max(z) s = max(z s)
-    const bool unmasked = tok0 + kStep <= lim_lo;   // uniform
+    const bool unmasked = tok0 + kStep <= lim_lo && tok0 >= t_lo;   // uniform
     float mlocs[NT];
     if (unmasked) {
 #pragma unroll
@@ -223,7 +228,7 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
             const int t = tok0 + 16 * h + 4 * j + i;
             float zz = z[nt][h][i];
             if constexpr (KVT == PKV_KV_INT8) zz *= r.ksc[h][i];
-            zz = t < lim[nt] ? zz : -INFINITY;     // causal: this column's keys only
+            zz = (t < lim[nt] && t >= t_lo) ? zz : -INFINITY;   // causal: this column's keys only
             z[nt][h][i] = zz;
             mloc = fmaxf(mloc, zz);
           }
@@ -251,7 +256,7 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
     // keys at or past the wave's largest limit may be unwritten slots (any
     // bits): their V is zeroed, in the step's own registers (the next load
     // overwrites them anyway); keys below it are written data, masked by p = 0
-    if (!I4 && tok0 + kStep > t_end) {   // INT4 codes are finite whatever the bytes: p = 0 masks them
+    if (!I4 && (tok0 + kStep > t_end || tok0 < t_lo)) {   // INT4 codes are finite whatever the bytes: p = 0 masks them
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int tb = tok0 + 16 * h + 4 * j;      // lane j's 4 tokens of the chunk
@@ -260,7 +265,7 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             // bf16: word e holds tokens tb + 2 (e % 2) and + 1 of one dim; 8-bit: tokens tb .. tb + 3
-            r.v[h][u][e] &= E == 2 ? tok_mask16(tb + 2 * (e & 1), 0, t_end) : tok_mask8(tb, 0, t_end);
+            r.v[h][u][e] &= E == 2 ? tok_mask16(tb + 2 * (e & 1), t_lo, t_end) : tok_mask8(tb, t_lo, t_end);
           }
         }
       }
@@ -279,7 +284,7 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
           psum += pv[i];
           if constexpr (KVT == PKV_KV_INT8) {
             const int t = tok0 + 16 * h + 4 * j + i;
-            pv[i] = (unmasked || t < lim[nt]) ? pv[i] * r.vsc[h][i] : 0.f;   // fold the V scale into p
+            pv[i] = (unmasked || (t < lim[nt] && t >= t_lo)) ? pv[i] * r.vsc[h][i] : 0.f;   // fold the V scale into p
           }
         }
         ph[h][0] = pack_bf16x2(pv[0], pv[1]);
@@ -342,8 +347,8 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
     else
       issue_step<D, KVT, B>(rr, p, bt_row, g, tok0, 0, lane);
   };
-  static_for<NB - 1>([&](auto b) __attribute__((always_inline)) { issue(r[b], (int)b * kStep); });
-  int i = 0;
+  static_for<NB - 1>([&](auto b) __attribute__((always_inline)) { issue(r[b], (s0 + (int)b) * kStep); });
+  int i = s0;
   while (i < nsteps) {
     static_for<NB>([&](auto b) __attribute__((always_inline)) {   // buffer indices are constants
       if (i < nsteps) {
@@ -437,7 +442,7 @@ hipError_t launch_prefill_as_decode(const PrefillDecodeArgs& a, hipStream_t stre
   p.QT = 1;
   p.num_blocks = c.num_blocks;
   p.num_items = (int32_t)items;
-  p.win = 0;
+  p.win = a.sliding_window;
   p.qk_scale = a.qk_scale;
   p.out_scale = a.out_scale;
   pp.qstart = nullptr;

@@ -132,8 +132,12 @@ def test_single_pass_form_matches_oracle(D, B, G, hkv):
     say(f"  max_abs={mx:.3e} rel={rel:.3e}")
     assert mx <= BAR[0] and rel <= BAR[1]
     assert not got[c.ctx == 0].any()
-    with pytest.raises(pkv.PkvError, match="split-context"):   # a window needs the split form
-        _decode(c, 0, window=40)
+    for win in (40, 100):                          # sliding window: the steps start at the window
+        got_w, _ = _decode(c, 0, window=win)
+        want_w = attention.paged_decode(c.q, c.img, 1, c.tables, c.ctx, scale, window=win)
+        mx, rel = errors(got_w, want_w)
+        say(f"  window {win}: max_abs={mx:.3e} rel={rel:.3e}")
+        assert mx <= BAR[0] and rel <= BAR[1]
 
 
 def test_appending_decode_equals_two_calls():

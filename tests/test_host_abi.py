@@ -246,11 +246,14 @@ def test_attention_entry_points_check_arguments_on_the_host():
     assert decode(part=33) == pkv.PKV_ERR_INVALID and "partition_size" in pkv.last_error()
     assert decode(hq=0) == pkv.PKV_ERR_INVALID
 
-    # INT4 in the single-pass form has no sliding window (the split form has)
+    # a negative sliding window, and q aliasing out with per-channel scales (INT4)
     d4 = _fake_pool(int4)
-    args = pkv.DecodeArgs(out=P, q=P, pool=ctypes.pointer(d4), layer=0, key=None, value=None, block_tables=P,
-                          table_width=4, context_lens=P, num_seqs=2, num_q_heads=4, scale=0.1, kv_dtype=int4,
-                          kv_scales=ctypes.pointer(sc), partition_size=0, sliding_window=40, workspace=None,
-                          workspace_bytes=0)
-    assert pkv._lib.paged_attn_decode_ex(ctypes.byref(args), None) == pkv.PKV_ERR_UNSUPPORTED
+    args = pkv.DecodeArgs(out=P, q=P + 4096, pool=ctypes.pointer(d4), layer=0, key=None, value=None,
+                          block_tables=P, table_width=4, context_lens=P, num_seqs=2, num_q_heads=4, scale=0.1,
+                          kv_dtype=int4, kv_scales=ctypes.pointer(sc), partition_size=0, sliding_window=-1,
+                          workspace=None, workspace_bytes=0)
+    assert pkv._lib.paged_attn_decode_ex(ctypes.byref(args), None) == pkv.PKV_ERR_INVALID
     assert "window" in pkv.last_error()
+    args.sliding_window, args.q = 40, P
+    assert pkv._lib.paged_attn_decode_ex(ctypes.byref(args), None) == pkv.PKV_ERR_INVALID
+    assert "alias" in pkv.last_error()
