@@ -95,10 +95,14 @@ KERNEL_SRCS = [os.path.join(_CSRC, f) for f in ("decode_kernels.hip", "decode_co
 PREFILL_SRCS = [os.path.join(_CSRC, f) for f in ("prefill_kernels.hip", "decode_common.h", "pkv_codecs.h")]
 
 
-def measured_traffic(profile=PROFILE, srcs=KERNEL_SRCS):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, or
-    None when the kernel's sources have changed since the counters were
-    taken (the summary records the sha256 of the sources concatenated)."""
+CONFIGS_PROFILE = os.path.join(ROOT, "profiles", "pa_split_kernel_configs.md")
+
+
+def measured_traffic(profile=PROFILE, srcs=KERNEL_SRCS, key=None):
+    """HBM bytes per launch from a committed rocprofv3 counter summary (the
+    line for workload `key` when given), or None when the kernel's sources
+    have changed since the counters were taken (the summary records the
+    sha256 of the sources concatenated)."""
     import hashlib
     import re
     try:
@@ -106,7 +110,8 @@ def measured_traffic(profile=PROFILE, srcs=KERNEL_SRCS):
         src = b"".join(open(f, "rb").read() for f in srcs)
     except OSError:
         return None
-    m = re.search(r"traffic_bytes_per_launch = (\d+); kernel_source_sha256 = ([0-9a-f]{64})", text)
+    tag = re.escape(f"[{key}]") if key else ""
+    m = re.search(r"traffic_bytes_per_launch" + tag + r" = (\d+); kernel_source_sha256 = ([0-9a-f]{64})", text)
     if not m or m.group(2) != hashlib.sha256(src).hexdigest():
         return None
     return int(m.group(1))
@@ -193,7 +198,9 @@ def config_bench(args):
            "config": {"workload": name, "partition_size": P, "kv_bytes_per_call": nbytes, "pool_copies": 3},
            "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+                        "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic(CONFIGS_PROFILE, KERNEL_SRCS, args.config),
+                        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"}}
     print(json.dumps(res), flush=True)
 
 
