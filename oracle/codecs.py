@@ -8,7 +8,7 @@ channel; the vLLM launch example there selects ``fp8_e5m2``).  The bjdmk.com.cn
 article, §5.2 量化粒度, names per-token-head scales (one scale for each token's
 each attention head) as the usual, most accurate INT8 choice.
 
-Readings taken where the pages stop short (each is listed in the design doc):
+Readings taken where the pages stop short:
 
 * bf16 is the storage type of unquantised K/V; widening is exact.
 * FP8 is the OCP e5m2 format: 1 sign, 5 exponent bits (bias 15), 2 mantissa
