@@ -81,6 +81,8 @@ def parse():
                     help="instead of the decode step: paged prefill after a prefix-cache hit (200 prompts = a "
                          "1500-token system prompt, cached and shared, + 64..512 own tokens; 70B-shaped heads), "
                          "one layer per call; TFLOP/s against the bf16 matrix-core peak")
+    ap.add_argument("--prefill-workload", default="prefix_cache", choices=["prefix_cache", "full_prompt"],
+                    help="with --prefill: prefix_cache (above) or full_prompt (16 whole 4096-token prompts)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB three times (torch copy kernel): the reference for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -408,7 +410,7 @@ def prefill_bench(args):
     import paged_kv_cache_436_amd as pkv
     import workloads
 
-    w = workloads.prefix_prefill()
+    w = workloads.prefix_prefill() if args.prefill_workload == "prefix_cache" else workloads.full_prefill()
     S, Hq, Hkv, D, B, W = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size, w.table_width
     ctx_np = np.asarray(w.context_lens, np.int64)
     chunk = np.asarray(w.extra["chunk"], np.int64)
@@ -484,14 +486,17 @@ def prefill_bench(args):
     res = {"metric": "paged prefill TFLOP/s (algorithmic, % of MI355X bf16 matrix-core peak)",
            "value": round(tfs, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
            "ms_per_call": round(per * 1e3, 4), "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": "paged prefill after a prefix-cache hit: 200 prompts = 1500-token shared system "
-                                  "prompt (93 cached blocks) + 64..512 own tokens, 64q/8kv heads, head_dim 128, "
-                                  "bf16 KV, block 16, one layer",
+           "config": {"workload": ("paged prefill after a prefix-cache hit: 200 prompts = 1500-token shared system "
+                                   "prompt (93 cached blocks) + 64..512 own tokens, 64q/8kv heads, head_dim 128, "
+                                   "bf16 KV, block 16, one layer") if args.prefill_workload == "prefix_cache" else
+                                  ("paged prefill of 16 whole 4096-token prompts, 64q/8kv heads, head_dim 128, bf16 "
+                                   "KV, block 16, one layer"),
                       "new_tokens": T, "max_query_len": maxq, "flops_per_call": flops},
            "roofline": {"bound": "mfma", "kernel": "pa_prefill_kernel", "achieved": round(tfs, 2),
                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4),
-                        "traffic": measured_traffic(PREFILL_PROFILE, PREFILL_SRCS),
+                        "traffic": (measured_traffic(PREFILL_PROFILE, PREFILL_SRCS)
+                                    if args.prefill_workload == "prefix_cache" else None),
                         "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"},
            "cpu_baseline": {"value": round(cpu_tfs, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
                             "sample": f"{seqs} sequences' prefill ({keys_done} (token, position) pairs per head), "

@@ -24,6 +24,8 @@ Shapes follow the pages' worked examples:
                     article §3.2) + 64..512 private tokens, 70B-shaped heads;
                     the prompt's 93 full blocks come from the prefix cache
                     and are shared, the rest of every prompt is prefilled.
+* ``full_prefill`` - 16 whole 4096-token prompts (no cache hit), 70B-shaped
+                    heads, blocks placed by a seeded permutation.
 
 Values are fp32 N(0, 1) draws rounded to bf16 (round-to-nearest-even via
 torch), carried as uint16 bit patterns.  Seeds: numpy SeedSequence(436000 +
@@ -192,6 +194,24 @@ def prefix_prefill(num_seqs: int = 200, prefix: int = 1500, lo: int = 64, hi: in
     w.extra["tables"] = tables
     w.extra["chunk"] = (ctx - shared * B).astype(np.int32)
     w.extra["prefix"] = prefix
+    return w
+
+
+def full_prefill(num_seqs: int = 16, prompt: int = 4096, num_q_heads: int = 64, num_kv_heads: int = 8,
+                 head_dim: int = 128) -> Workload:
+    """Whole-prompt prefill: every sequence's chunk is its whole prompt.
+    ``extra['chunk']`` = tokens to prefill; ``extra['tables']`` = int32
+    [S, W] block tables."""
+    B = 16
+    ctx = np.full(num_seqs, prompt, dtype=np.int32)
+    W = math.ceil(prompt / B)
+    nb = num_seqs * W
+    w = Workload("full_prefill", 7, num_seqs, num_q_heads, num_kv_heads, head_dim, B, 1, KV_BF16, ctx, nb,
+                 np.zeros(nb, np.int32), W)
+    r = w.streams()
+    w.block_order = r[1].permutation(nb).astype(np.int32)
+    w.extra["tables"] = static_tables(w)
+    w.extra["chunk"] = ctx.copy()
     return w
 
 
