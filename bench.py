@@ -248,10 +248,13 @@ def cow_bench(args):
     P = (W * B + 31) // 32 * 32
     ws = torch.empty(pkv.paged_attn_workspace_bytes(S, H, D, W, B, P), dtype=torch.uint8, device=dev)
     st = torch.cuda.current_stream()
-    tab_h = torch.empty((S, W), dtype=torch.int32, pin_memory=True)
-    ctx_h = torch.empty(S, dtype=torch.int32, pin_memory=True)
-    tab_d = torch.empty((S, W), dtype=torch.int32, device=dev)
-    ctx_d = torch.empty(S, dtype=torch.int32, device=dev)
+    # two sets of pinned staging and device tables: the host prepares step
+    # i + 1 while the GPU runs step i
+    tab_h = [torch.empty((S, W), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    ctx_h = [torch.empty(S, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    tab_d = [torch.empty((S, W), dtype=torch.int32, device=dev) for _ in range(2)]
+    ctx_d = [torch.empty(S, dtype=torch.int32, device=dev) for _ in range(2)]
+    done = [None, None]
     # warm-up: decodes of the shared state (no append, nothing changes)
     t0s, c0s = bm.block_tables(np.arange(S, dtype=np.int32), W)
     td, cd = torch.from_numpy(t0s).to(dev), torch.from_numpy(c0s).to(dev)
@@ -263,27 +266,29 @@ def cow_bench(args):
     prefix_blocks = prefix // B                  # full prefix blocks stay shared for the whole run
     t_start = time.perf_counter()
     for step in range(steps):
+        k = step & 1
         active = np.nonzero(gen > step)[0].astype(np.int32)
         n = active.size
         slots, pairs = bm.append(active)
-        tab_np, ctx_np = bm.block_tables(active, W, out=tab_h.numpy()[:n], ctx_out=ctx_h.numpy()[:n])
-        tab_d[:n].copy_(tab_h[:n], non_blocking=True)
-        ctx_d[:n].copy_(ctx_h[:n], non_blocking=True)
+        if done[k] is not None:
+            done[k].synchronize()     # the copies out of this staging set (two steps ago) are done
+        tab_np, ctx_np = bm.block_tables(active, W, out=tab_h[k].numpy()[:n], ctx_out=ctx_h[k].numpy()[:n])
+        tab_d[k][:n].copy_(tab_h[k][:n], non_blocking=True)
+        ctx_d[k][:n].copy_(ctx_h[k][:n], non_blocking=True)
         if pairs.shape[0]:
             pkv.copy_blocks(pool, torch.from_numpy(pairs).to(dev, non_blocking=False), stream=st)
             pairs_total += pairs.shape[0]
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(st)
-        pkv.paged_attn_decode_append(out[:n], q_all[:n], pool, 0, kn[:n], vn[:n], tab_d[:n], ctx_d[:n], w.scale,
-                                     partition_size=P, workspace=ws, stream=st)
+        pkv.paged_attn_decode_append(out[:n], q_all[:n], pool, 0, kn[:n], vn[:n], tab_d[k][:n], ctx_d[k][:n],
+                                     w.scale, partition_size=P, workspace=ws, stream=st)
         e1.record(st)
         ev.append((e0, e1))
+        done[k] = e1
         ctx64 = ctx_np.astype(np.int64)
         logical += int(ctx64.sum()) * H * 2 * D * 2
         unique += (int((ctx64 - prefix_blocks * B).sum()) + prefix_blocks * B) * H * 2 * D * 2
         seq_steps += n
-        # the host reuses the pinned buffers next step: the copies must be done
-        st.synchronize()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     gpu = sum(a.elapsed_time(b) for a, b in ev) * 1e-3
