@@ -275,9 +275,11 @@ pkv_status paged_attn_decode(float* out, const void* q, const pkv_pool* pool, in
  *   out           device fp32 [T][Hq][D], T = num_queries = query_start[S]
  *   q             device bf16 [T][Hq][D]
  *   query_start   device int32 [S + 1], non-decreasing, query_start[0] = 0
- *   max_query_len host; >= every n_s (it sizes the grid: tiles of 16
- *                 (token, head) pairs per KV head; a chunk longer than it is
- *                 cut, its later tokens left unwritten)
+ *   max_query_len host; >= every n_s (it sizes the grid: spans of 64
+ *                 (token, head) pairs per KV head).  Of a chunk longer than
+ *                 it, only the first max_query_len tokens are computed (at
+ *                 their positions in the whole chunk); the rows of the later
+ *                 ones are left unwritten.
  *   block_tables, context_lens, kv_scales as for paged_attn_decode.
  * A query whose position would be negative (n_s > ctx_s) gets a zero row.
  * For per-channel scales, out must not alias q (the folded query is staged

@@ -81,6 +81,7 @@ struct PrefillParams {
   int32_t tiles;              // workgroup column spans per (sequence, KV head):
                               // ceil(max_query_len * G / (16 kPrefillNT kNW))
   int32_t T;                  // rows of q and out
+  int32_t maxq;               // queries per sequence served (later ones are left unwritten)
 };
 
 template <int D, int KVT, int B>
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
   // query rows, kept inside [0, T) whatever query_start holds
   const int q0 = pp.qstart ? min(max(pp.qstart[s], 0), pp.T) : s;
   const int n = pp.qstart ? min(max(pp.qstart[s + 1], q0), pp.T) - q0 : 1;
-  const int ncol = n * p.G;
+  const int ncol = min(n, pp.maxq) * p.G;         // positions still follow the whole chunk
   const int c0 = (ct * kNW + w) * 16 * NT;       // this wave's first column
   if (c0 >= ncol) return;                        // no barrier follows: waves are independent
   const int cols = min(16 * NT, ncol - c0);
@@ -448,6 +449,7 @@ hipError_t launch_prefill_as_decode(const PrefillDecodeArgs& a, hipStream_t stre
   pp.qstart = nullptr;
   pp.tiles = (int32_t)tiles;
   pp.T = a.num_seqs;
+  pp.maxq = 1;
   return launch_prefill(pp, c.head_dim, c.kv_dtype, c.block_size, (int)((items + 7) / 8 * 8), stream);
 }
 
@@ -548,6 +550,7 @@ extern "C" pkv_status paged_attn_prefill(float* out, const void* q, const pkv_po
   pp.qstart = query_start;
   pp.tiles = (int32_t)tiles;
   pp.T = num_queries;
+  pp.maxq = max_query_len;
   const hipError_t e = launch_prefill(pp, c.head_dim, c.kv_dtype, c.block_size, (int)((items + 7) / 8 * 8), stream);
   if (e != hipSuccess) {
     set_error("paged_attn_prefill launch failed: %s", hipGetErrorString(e));

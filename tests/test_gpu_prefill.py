@@ -203,3 +203,45 @@ def test_prefill_prefix_cache_workload_full_size_sampled():
         say(f"  seq {s}: ctx {ctx[s]} chunk {chunk[s]} max_abs={mx:.3e} rel={rel:.3e}")
         assert mx <= BAR[pkv.PKV_KV_BF16][0] and rel <= BAR[pkv.PKV_KV_BF16][1]
     assert torch.isfinite(out).all()
+
+
+def test_prefill_max_query_len_cuts_longer_chunks():
+    """max_query_len sizes the grid: the rows of a chunk past it are left
+    as they were (NaN here), the rows before it are the oracle's."""
+    import torch
+    say("prefill max_query_len cut")
+    rng = np.random.default_rng(15500)
+    B, D, hkv, G = 16, 128, 2, 4
+    ctx = np.array([90, 40], np.int32)
+    chunk = np.array([50, 40], np.int32)
+    need = [math.ceil(int(c) / B) for c in ctx]
+    nb = sum(need)
+    W = max(need)
+    perm = rng.permutation(nb)
+    tables = np.zeros((2, W), np.int32)
+    tables[0, :need[0]] = perm[:need[0]]
+    tables[1, :need[1]] = perm[need[0]:]
+    cfg = pkv.make_config(1, nb, B, hkv, D, pkv.PKV_KV_BF16)
+    pool = pkv.Pool(cfg)
+    pool.memory.zero_()
+    total = int(ctx.sum())
+    k = workloads.to_bf16_bits(rng.standard_normal((total, hkv, D), dtype=np.float32))
+    v = workloads.to_bf16_bits(rng.standard_normal((total, hkv, D), dtype=np.float32))
+    slots = np.concatenate([expanded_slots(tables[s], int(ctx[s]), B) for s in range(2)])
+    img = cache_ops.reshape_and_cache(read_pool(pool), 0, k, v, slots)
+    pkv.reshape_and_cache(pool, 0, bf16_dev(k), bf16_dev(v), dev(slots.astype(np.int64)))
+    qs = np.array([0, 50, 90], np.int32)
+    q = workloads.to_bf16_bits(rng.standard_normal((90, hkv * G, D), dtype=np.float32))
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
+    out = torch.full((90, hkv * G, D), float("nan"), dtype=torch.float32, device="cuda")
+    cut = 20      # the grid covers 20 tokens per sequence
+    pkv.paged_attn_prefill(out, bf16_dev(q), pool, 0, dev(tables), dev(ctx), dev(qs), scale, cut)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = attention.paged_prefill(q, img, 0, tables, ctx, qs, scale)
+    for s in range(2):
+        rows = np.arange(qs[s], qs[s + 1])
+        done, left = rows[:cut], rows[cut:]
+        mx, rel = errors(got[done], want[done])
+        assert mx <= BAR[pkv.PKV_KV_BF16][0] and rel <= BAR[pkv.PKV_KV_BF16][1]
+        assert np.isnan(got[left]).all()
