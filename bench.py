@@ -422,14 +422,24 @@ def prefill_bench(args):
     qs_np = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
     T = int(qs_np[-1])
     dev = torch.device("cuda:0")
-    cfg = pkv.make_config(1, w.num_blocks, B, Hkv, D, pkv.PKV_KV_BF16)
+    kvt = KV_DTYPES[args.kv_dtype]
+    cfg = pkv.make_config(1, w.num_blocks, B, Hkv, D, kvt)
     pool = pkv.Pool(cfg, device=dev)
     g = torch.Generator(device=dev)
     g.manual_seed(436008)
-    k_off, v_off, _, _ = pool.region_offsets()
+    k_off, v_off, ks_off, vs_off = pool.region_offsets()
     lb = pool.desc.layer_bytes
     for off in (k_off, v_off):
-        pool.memory[off: off + lb].view(torch.bfloat16).normal_(generator=g)
+        if kvt == pkv.PKV_KV_BF16:
+            pool.memory[off: off + lb].view(torch.bfloat16).normal_(generator=g)
+        else:   # random codes (e5m2: finite patterns below the exponent-31 codes)
+            pool.memory[off: off + lb].random_(0, 120 if kvt == pkv.PKV_KV_FP8_E5M2 else 256, generator=g)
+    if ks_off is not None:     # int8 per-token scales, or the calibrated per-channel ones (int8, int4)
+        n = (vs_off - ks_off) // 4
+        lo, hi = (0.3, 0.6) if kvt == pkv.PKV_KV_INT4 else (0.02, 0.05)
+        for off in (ks_off, vs_off):
+            pool.memory[off: off + 4 * n].view(torch.float32).uniform_(lo, hi, generator=g)
+    sc = TENSOR_SCALE if kvt in (pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8_TENSOR) else 1.0
     tables = torch.from_numpy(w.extra["tables"]).to(dev)
     ctx = torch.from_numpy(ctx_np.astype(np.int32)).to(dev)
     qs = torch.from_numpy(qs_np).to(dev)
@@ -439,7 +449,7 @@ def prefill_bench(args):
     maxq = int(chunk.max())
 
     def call():
-        pkv.paged_attn_prefill(out, q, pool, 0, tables, ctx, qs, w.scale, maxq, stream=st)
+        pkv.paged_attn_prefill(out, q, pool, 0, tables, ctx, qs, w.scale, maxq, k_scale=sc, v_scale=sc, stream=st)
 
     for _ in range(args.warmup):
         call()
@@ -459,39 +469,48 @@ def prefill_bench(args):
     log(f"prefill: {T} new tokens, {keys} (token, position) pairs per head; {per * 1e3:.3f} ms per call, "
         f"{tfs:.1f} TFLOP/s")
 
-    # oracle on a bounded sample of sequences (gather + causal attention, fp64)
-    from oracle import attention, layout
-    tile = pool.desc.tile_bytes
-    gpu_out = out.cpu().numpy()
-    qbits = q.view(torch.int16).cpu().numpy().view(np.uint16)
-    tabs = w.extra["tables"]
-    rng = np.random.default_rng(437)
-    spent, keys_done, worst, seqs = 0.0, 0, 0.0, 0
-    for s in rng.permutation(S):
-        c, n = int(ctx_np[s]), int(chunk[s])
-        nblk = math.ceil(c / B)
-        sub = layout.PoolShape(1, nblk, B, Hkv, D)
-        img = layout.empty_image(sub)
-        idx = torch.from_numpy(tabs[s, :nblk].astype(np.int64)).to(dev)
-        for region, dst in ((k_off, img.k), (v_off, img.v)):
-            lay = pool.memory[region: region + lb].view(w.num_blocks, Hkv * tile)
-            dst[:] = lay.index_select(0, idx).cpu().numpy().view(np.uint16).reshape(-1)
-        t0 = time.perf_counter()
-        ref = attention.paged_prefill(qbits[qs_np[s]:qs_np[s + 1]], img, 0, np.arange(nblk, dtype=np.int32)[None, :],
-                                      np.array([c]), np.array([0, n]), w.scale)
-        spent += time.perf_counter() - t0
-        worst = max(worst, float(np.max(np.abs(gpu_out[qs_np[s]:qs_np[s + 1]] - ref))))
-        keys_done += n * (c - n) + n * (n + 1) // 2
-        seqs += 1
-        if spent >= args.cpu_seconds:
-            break
-    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
-    cpu_tfs = keys_done * Hq * 4 * D / spent / 1e12
-    log(f"cpu oracle: {cpu_tfs:.6f} TFLOP/s over {seqs} sequences; parity max abs err {worst:.2e}")
+    cpu = parity = None
+    if kvt == pkv.PKV_KV_BF16:   # the oracle sample copies the K/V regions only (no scale regions)
+        # oracle on a bounded sample of sequences (gather + causal attention, fp64)
+        from oracle import attention, layout
+        tile = pool.desc.tile_bytes
+        gpu_out = out.cpu().numpy()
+        qbits = q.view(torch.int16).cpu().numpy().view(np.uint16)
+        tabs = w.extra["tables"]
+        rng = np.random.default_rng(437)
+        spent, keys_done, worst, seqs = 0.0, 0, 0.0, 0
+        for s in rng.permutation(S):
+            c, n = int(ctx_np[s]), int(chunk[s])
+            nblk = math.ceil(c / B)
+            sub = layout.PoolShape(1, nblk, B, Hkv, D)
+            img = layout.empty_image(sub)
+            idx = torch.from_numpy(tabs[s, :nblk].astype(np.int64)).to(dev)
+            for region, dst in ((k_off, img.k), (v_off, img.v)):
+                lay = pool.memory[region: region + lb].view(w.num_blocks, Hkv * tile)
+                dst[:] = lay.index_select(0, idx).cpu().numpy().view(np.uint16).reshape(-1)
+            t0 = time.perf_counter()
+            ref = attention.paged_prefill(qbits[qs_np[s]:qs_np[s + 1]], img, 0, np.arange(nblk, dtype=np.int32)[None, :],
+                                          np.array([c]), np.array([0, n]), w.scale)
+            spent += time.perf_counter() - t0
+            worst = max(worst, float(np.max(np.abs(gpu_out[qs_np[s]:qs_np[s + 1]] - ref))))
+            keys_done += n * (c - n) + n * (n + 1) // 2
+            seqs += 1
+            if spent >= args.cpu_seconds:
+                break
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+        cpu_tfs = keys_done * Hq * 4 * D / spent / 1e12
+        log(f"cpu oracle: {cpu_tfs:.6f} TFLOP/s over {seqs} sequences; parity max abs err {worst:.2e}")
+        cpu = {"value": round(cpu_tfs, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+               "sample": f"{seqs} sequences' prefill ({keys_done} (token, position) pairs per head), "
+                         f"{spent:.1f} s of fp64 numpy causal attention"}
+        parity = {"sequences_checked": seqs, "max_abs_err": worst, "bar": 1e-2}
+    kv_name = {v: k for k, v in KV_DTYPES.items()}[kvt]
     res = {"metric": "paged prefill TFLOP/s (algorithmic, % of MI355X bf16 matrix-core peak)",
            "value": round(tfs, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
-           "ms_per_call": round(per * 1e3, 4), "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": ("paged prefill after a prefix-cache hit: 200 prompts = 1500-token shared system "
+           "ms_per_call": round(per * 1e3, 4), "higher_is_better": True,
+           "dtype": {"bf16": "bf16", "fp8": "fp8"}.get(kv_name, "int8" if kv_name.startswith("int8") else "int4"),
+           "data": "synthetic",
+           "config": {"kv_storage": kv_name, "workload": ("paged prefill after a prefix-cache hit: 200 prompts = 1500-token shared system "
                                    "prompt (93 cached blocks) + 64..512 own tokens, 64q/8kv heads, head_dim 128, "
                                    "bf16 KV, block 16, one layer") if args.prefill_workload == "prefix_cache" else
                                   ("paged prefill of 16 whole 4096-token prompts, 64q/8kv heads, head_dim 128, bf16 "
@@ -501,12 +520,10 @@ def prefill_bench(args):
                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4),
                         "traffic": (measured_traffic(PREFILL_PROFILE, PREFILL_SRCS)
-                                    if args.prefill_workload == "prefix_cache" else None),
+                                    if args.prefill_workload == "prefix_cache" and kvt == pkv.PKV_KV_BF16
+                                    else None),
                         "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"},
-           "cpu_baseline": {"value": round(cpu_tfs, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-                            "sample": f"{seqs} sequences' prefill ({keys_done} (token, position) pairs per head), "
-                                      f"{spent:.1f} s of fp64 numpy causal attention"},
-           "parity_sample": {"sequences_checked": seqs, "max_abs_err": worst, "bar": 1e-2}}
+           "cpu_baseline": cpu, "parity_sample": parity}
     print(json.dumps(res), flush=True)
 
 
