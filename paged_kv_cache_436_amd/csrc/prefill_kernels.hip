@@ -74,6 +74,36 @@ __device__ __forceinline__ void issue_step_int4(StepRegs<D, PKV_KV_INT4>& r, con
   }
 }
 
+// ---- INT8 codes as fp16: a signed byte c becomes u = c + 128 by flipping
+// its top bit, and the fp16 with bits 0x64uu is 1024 + u = 1152 + c exactly
+// (fp16 steps by 1 in [1024, 2048)); one byte permute places two bytes and
+// the constant 0x64.  Three instructions widen four codes where the bf16
+// route takes six, which matters in this vector-ALU-bound kernel.  The
+// constant comes back out after the products: 1152 * sum(q) from each
+// logit, 1152 * sum(p) from each accumulator.  The query enters as
+// fp16(q * 2^-8) (exact for |q| in [2^-6, 2^23]), the 2^8 going back into
+// the softmax scale.
+constexpr float kInt8Bias = 1152.0f;
+constexpr float kInt8QShift = 1.0f / 256.0f;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+template <bool HI>
+__device__ __forceinline__ uint32_t int8x2_to_f16x2(uint32_t w) {
+  return __builtin_amdgcn_perm(0x64646464u, w ^ 0x80808080u, HI ? 0x04030402u : 0x05010400u);
+}
+__device__ __forceinline__ bf16x8 int8x8_to_f16x8(uint32_t w0, uint32_t w1) {
+  return __builtin_bit_cast(bf16x8, u32x4{int8x2_to_f16x2<false>(w0), int8x2_to_f16x2<true>(w0),
+                                          int8x2_to_f16x2<false>(w1), int8x2_to_f16x2<true>(w1)});
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  f16x2 r;
+  r[0] = (_Float16)a;
+  r[1] = (_Float16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
 struct PrefillParams {
   DecodeParams d;             // q [T][Hq][D] (or the folded q), out [T][Hq][D], pool layer, tables, lengths
   const int32_t* qstart;      // [S + 1]: sequence s's queries are rows qstart[s] .. qstart[s+1] - 1;
@@ -95,6 +125,12 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
   // after the products; the query dims follow the bf16 slot layout and the
   // accumulator dims that of the INT4 V pieces
   constexpr bool I4 = KVT == PKV_KV_INT4;
+  // INT8 codes through fp16 (1152 + code) in q.K, and in P.V too where the
+  // V scale is per tensor or per channel (p <= 2^8 then; per-token V scales
+  // are folded into p, whose range fp16 could not hold, so that V stays bf16)
+  constexpr bool I8K = KVT == PKV_KV_INT8 || KVT == PKV_KV_INT8_TENSOR;
+  constexpr bool I8V = KVT == PKV_KV_INT8_TENSOR;
+  const float qks = I8K ? p.qk_scale * (1.0f / kInt8QShift) : p.qk_scale;   // the softmax scale of z
   constexpr int QL = I4 ? 2 : E;
   constexpr int AL = I4 ? 0 : E;
 
@@ -155,6 +191,21 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
 #pragma unroll
         for (int e = 0; e < 8; ++e) a += (float)qop[nt][kk][e];
       qsum[nt] = sum_x32(sum_x16(a));   // lanes of one column hold its 4 dim slots
+    } else if constexpr (I8K) {
+      // the fp16 operand, and the sum of exactly the values it holds
+      float a = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < T::KK; ++kk) {
+        const u32x4 wq = __builtin_bit_cast(u32x4, qop[nt][kk]);
+        u32x4 hq;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hq[e] = pack_f16x2(bf16_lo(wq[e]) * kInt8QShift, bf16_hi(wq[e]) * kInt8QShift);
+          a += f16_lo(hq[e]) + f16_hi(hq[e]);
+        }
+        qop[nt][kk] = __builtin_bit_cast(bf16x8, hq);
+      }
+      qsum[nt] = sum_x32(sum_x16(a));
     }
   }
 
@@ -179,6 +230,9 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
           const uint32_t wk = r.k[h][0][kk];        // word kk: dims 32 kk + 8 j .. + 7
           ka[h][kk] = __builtin_bit_cast(
               bf16x8, u32x4{int4_pair(wk, 0), int4_pair(wk, 1), int4_pair(wk, 2), int4_pair(wk, 3)});
+        } else if constexpr (I8K) {
+          const u32x4 wv = r.k[h][kk >> 1];
+          ka[h][kk] = (kk & 1) ? int8x8_to_f16x8(wv[2], wv[3]) : int8x8_to_f16x8(wv[0], wv[1]);
         } else if constexpr (E == 2) {
           ka[h][kk] = __builtin_bit_cast(bf16x8, r.k[h][kk]);
         } else {
@@ -194,8 +248,15 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
       for (int h = 0; h < 2; ++h) {
         f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < T::KK; ++kk) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[h][kk], qop[nt][kk], c, 0, 0, 0);
-        if constexpr (I4) c -= kInt4Bias * qsum[nt];   // the K operand held 136 + code
+        for (int kk = 0; kk < T::KK; ++kk) {
+          if constexpr (I8K)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ka[h][kk]),
+                                                       __builtin_bit_cast(f16x8, qop[nt][kk]), c, 0, 0, 0);
+          else
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[h][kk], qop[nt][kk], c, 0, 0, 0);
+        }
+        if constexpr (I4) c -= kInt4Bias * qsum[nt];    // the K operand held 136 + code
+        if constexpr (I8K) c -= kInt8Bias * qsum[nt];   // the K operand held 1152 + code
         z[nt][h] = c;
       }
     }
@@ -238,7 +299,7 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const float mloc = max_x32(max_x16(mlocs[nt])) * p.qk_scale;   // the column's scaled max over the step
+      const float mloc = max_x32(max_x16(mlocs[nt])) * qks;   // the column's scaled max over the step
       const bool bump = mloc > m_run[nt] + kPrefillSlack;   // false while the column has no key
       const float m_ref = bump ? mloc : m_run[nt];
       alpha[nt] = bump ? __builtin_amdgcn_exp2f(m_run[nt] - m_ref) : 1.0f;
@@ -257,7 +318,8 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
     // keys at or past the wave's largest limit may be unwritten slots (any
     // bits): their V is zeroed, in the step's own registers (the next load
     // overwrites them anyway); keys below it are written data, masked by p = 0
-    if (!I4 && (tok0 + kStep > t_end || tok0 < t_lo)) {   // INT4 codes are finite whatever the bytes: p = 0 masks them
+    // (INT4 codes, and INT8 codes read as fp16, are finite whatever the bytes: p = 0 masks them)
+    if (!I4 && !I8V && (tok0 + kStep > t_end || tok0 < t_lo)) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int tb = tok0 + 16 * h + 4 * j;      // lane j's 4 tokens of the chunk
@@ -281,17 +343,34 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
         float pv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[nt][h][i], p.qk_scale, -m_use[nt]));
+          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[nt][h][i], qks, -m_use[nt]));
           psum += pv[i];
           if constexpr (KVT == PKV_KV_INT8) {
             const int t = tok0 + 16 * h + 4 * j + i;
             pv[i] = (unmasked || (t < lim[nt] && t >= t_lo)) ? pv[i] * r.vsc[h][i] : 0.f;   // fold the V scale into p
           }
         }
-        ph[h][0] = pack_bf16x2(pv[0], pv[1]);
-        ph[h][1] = pack_bf16x2(pv[2], pv[3]);
-        pl[h][0] = pack_bf16x2(pv[0] - bf16_lo(ph[h][0]), pv[1] - bf16_hi(ph[h][0]));
-        pl[h][1] = pack_bf16x2(pv[2] - bf16_lo(ph[h][1]), pv[3] - bf16_hi(ph[h][1]));
+        if constexpr (I8V) {   // fp16 parts for the fp16 V operand
+          ph[h][0] = pack_f16x2(pv[0], pv[1]);
+          ph[h][1] = pack_f16x2(pv[2], pv[3]);
+          pl[h][0] = pack_f16x2(pv[0] - f16_lo(ph[h][0]), pv[1] - f16_hi(ph[h][0]));
+          pl[h][1] = pack_f16x2(pv[2] - f16_lo(ph[h][1]), pv[3] - f16_hi(ph[h][1]));
+        } else {
+          ph[h][0] = pack_bf16x2(pv[0], pv[1]);
+          ph[h][1] = pack_bf16x2(pv[2], pv[3]);
+          pl[h][0] = pack_bf16x2(pv[0] - bf16_lo(ph[h][0]), pv[1] - bf16_hi(ph[h][0]));
+          pl[h][1] = pack_bf16x2(pv[2] - bf16_lo(ph[h][1]), pv[3] - bf16_hi(ph[h][1]));
+        }
+      }
+      if constexpr (I8V) {
+        // the sum the 1152 offset of V is taken back with: that of the p the
+        // products use (hi + lo parts), which is also the softmax denominator
+        psum = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+            psum += (f16_lo(ph[h][e]) + f16_lo(pl[h][e])) + (f16_hi(ph[h][e]) + f16_hi(pl[h][e]));
       }
       if constexpr (I4) {
         // the sum the 136 offset of V is taken back with: that of the p the
@@ -318,6 +397,12 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
         a1 = int4_pair(w0, 2 + (cc & 1));
         a2 = int4_pair(w1, cc & 1);
         a3 = int4_pair(w1, 2 + (cc & 1));
+      } else if constexpr (I8V) {
+        const int u = cc >> 2, e = cc & 3;
+        a0 = int8x2_to_f16x2<false>(r.v[0][u][e]);
+        a1 = int8x2_to_f16x2<true>(r.v[0][u][e]);
+        a2 = int8x2_to_f16x2<false>(r.v[1][u][e]);
+        a3 = int8x2_to_f16x2<true>(r.v[1][u][e]);
       } else if constexpr (E == 2) {
         const int u = cc >> 1, e = cc & 1;
         a0 = r.v[0][u][2 * e];
@@ -332,8 +417,15 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
       const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{a0, a1, a2, a3});
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        acc[nt][cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop[nt], acc[nt][cc], 0, 0, 0);
-        acc[nt][cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_lo[nt], acc[nt][cc], 0, 0, 0);
+        if constexpr (I8V) {
+          acc[nt][cc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, va),
+                                                               __builtin_bit_cast(f16x8, pop[nt]), acc[nt][cc], 0, 0, 0);
+          acc[nt][cc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, va),
+                                                               __builtin_bit_cast(f16x8, pop_lo[nt]), acc[nt][cc], 0, 0, 0);
+        } else {
+          acc[nt][cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop[nt], acc[nt][cc], 0, 0, 0);
+          acc[nt][cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_lo[nt], acc[nt][cc], 0, 0, 0);
+        }
       }
     }
   };
@@ -376,7 +468,8 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
       for (int i2 = 0; i2 < 4; ++i2) {
         const int d = acc_dim<AL>(cc, j, i2);
         // INT4: the V operand held 136 + code
-        const float a = I4 ? acc[nt][cc][i2] - kInt4Bias * L : acc[nt][cc][i2];
+        const float a = I4 ? acc[nt][cc][i2] - kInt4Bias * L
+                           : (I8V ? acc[nt][cc][i2] - kInt8Bias * L : acc[nt][cc][i2]);
         o[cc][i2] = a * inv * (p.vs_ch ? p.vs_ch[g * D + d] : p.out_scale);
       }
     if constexpr (I4) {
