@@ -104,6 +104,55 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
 __device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
+// bf16 step loads: K as in issue_step; V as 8-byte pieces (4 tokens of one
+// dim) placed so that the P.V operand of 16-dim tile cc is one register
+// quad, words {chunk 0: tokens 4j, 4j+1 | 4j+2, 4j+3; chunk 1: the same} of
+// dim 32 (cc / 2) + 2 row + cc % 2, kept at flat index cc of r.v - so the
+// operand needs no assembly from two 16-byte loads.
+template <int D, int B>
+__device__ __forceinline__ void issue_step_bf16(StepRegs<D, PKV_KV_BF16>& r, const DecodeParams& p,
+                                               const int32_t* bt_row, int g, int tok0, int lane) {
+  using T = Tile<D, PKV_KV_BF16>;
+  constexpr int NC = D / 16;
+  constexpr int VL = T::VLOADS;
+  const int row = lane & 15;
+  const int j = lane >> 4;
+  u32x2 vv[2][NC];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = tok0 + 16 * h;
+    int ph[2];
+#pragma unroll
+    for (int b = 0; b < (B < 16 ? 2 : 1); ++b) {
+      int lb = (int)((uint32_t)t / B) + b;
+      lb = lb < p.W ? lb : p.W - 1;                // never index past the table row
+      const int e = bt_row[lb];
+      ph[b] = e < 0 ? 0 : (e >= p.num_blocks ? p.num_blocks - 1 : e);  // stay inside the pool
+    }
+    if (B >= 16) ph[1] = ph[0];
+    const int phk = row < 8 ? ph[0] : ph[1];
+    const int phv = j < 2 ? ph[0] : ph[1];
+    constexpr int TM = (B < 16 ? B : 16) - 1;
+    const int toff = B < 16 ? 0 : (int)((uint32_t)t % B);
+    const int tk = toff + (row & TM);
+    const int tv = toff + ((4 * j) & TM);
+    const uint32_t tilek = (uint32_t)phk * (uint32_t)p.Hkv + (uint32_t)g;
+    const uint32_t tilev = (uint32_t)phv * (uint32_t)p.Hkv + (uint32_t)g;
+    const char* kt = p.k + (uint64_t)tilek * (uint32_t)(B * D * 2);
+    const char* vt = p.v + (uint64_t)tilev * (uint32_t)(B * D * 2);
+#pragma unroll
+    for (int u = 0; u < T::KLOADS; ++u) r.k[h][u] = ld16(kt + (uint32_t)((4 * u + j) * B + tk) * 16u);
+    const int grp = tv >> 2;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      const int d = 32 * (cc >> 1) + 2 * row + (cc & 1);
+      vv[h][cc] = *reinterpret_cast<const u32x2*>(vt + (uint32_t)(grp * D + d) * 8u);
+    }
+  }
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) r.v[cc / VL][cc % VL] = u32x4{vv[0][cc][0], vv[0][cc][1], vv[1][cc][0], vv[1][cc][1]};
+}
+
 struct PrefillParams {
   DecodeParams d;             // q [T][Hq][D] (or the folded q), out [T][Hq][D], pool layer, tables, lengths
   const int32_t* qstart;      // [S + 1]: sequence s's queries are rows qstart[s] .. qstart[s+1] - 1;
@@ -319,17 +368,21 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
     // bits): their V is zeroed, in the step's own registers (the next load
     // overwrites them anyway); keys below it are written data, masked by p = 0
     // (INT4 codes, and INT8 codes read as fp16, are finite whatever the bytes: p = 0 masks them)
-    if (!I4 && !I8V && (tok0 + kStep > t_end || tok0 < t_lo)) {
+    if (E == 2 && !I4 && (tok0 + kStep > t_end || tok0 < t_lo)) {
+      // bf16 operand quads: chunk 0 tokens tb0 .. tb0 + 3, chunk 1 tokens tb1 .. tb1 + 3
+      const int tb0 = tok0 + 4 * j, tb1 = tok0 + 16 + 4 * j;
+      const u32x4 m = u32x4{tok_mask16(tb0, t_lo, t_end), tok_mask16(tb0 + 2, t_lo, t_end),
+                            tok_mask16(tb1, t_lo, t_end), tok_mask16(tb1 + 2, t_lo, t_end)};
+#pragma unroll
+      for (int cc = 0; cc < T::NC; ++cc) r.v[cc / T::VLOADS][cc % T::VLOADS] &= m;
+    } else if (E != 2 && !I4 && !I8V && (tok0 + kStep > t_end || tok0 < t_lo)) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int tb = tok0 + 16 * h + 4 * j;      // lane j's 4 tokens of the chunk
 #pragma unroll
         for (int u = 0; u < T::VLOADS; ++u) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            // bf16: word e holds tokens tb + 2 (e % 2) and + 1 of one dim; 8-bit: tokens tb .. tb + 3
-            r.v[h][u][e] &= E == 2 ? tok_mask16(tb + 2 * (e & 1), t_lo, t_end) : tok_mask8(tb, t_lo, t_end);
-          }
+          for (int e = 0; e < 4; ++e) r.v[h][u][e] &= tok_mask8(tb, t_lo, t_end);   // 8-bit: tokens tb .. tb + 3
         }
       }
     }
@@ -404,11 +457,11 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
         a2 = int8x2_to_f16x2<false>(r.v[1][u][e]);
         a3 = int8x2_to_f16x2<true>(r.v[1][u][e]);
       } else if constexpr (E == 2) {
-        const int u = cc >> 1, e = cc & 1;
-        a0 = r.v[0][u][2 * e];
-        a1 = r.v[0][u][2 * e + 1];
-        a2 = r.v[1][u][2 * e];
-        a3 = r.v[1][u][2 * e + 1];
+        const u32x4 q4 = r.v[cc / T::VLOADS][cc % T::VLOADS];   // the operand quad (issue_step_bf16)
+        a0 = q4[0];
+        a1 = q4[1];
+        a2 = q4[2];
+        a3 = q4[3];
       } else {
         const int u = cc >> 2, e = cc & 3;
         widen4<KVT>(r.v[0][u][e], a0, a1);
@@ -437,6 +490,8 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
   auto issue = [&](StepRegs<D, KVT>& rr, int tok0) __attribute__((always_inline)) {
     if constexpr (I4)
       issue_step_int4<D, B>(rr, p, bt_row, g, tok0, lane);
+    else if constexpr (E == 2)
+      issue_step_bf16<D, B>(rr, p, bt_row, g, tok0, lane);
     else
       issue_step<D, KVT, B>(rr, p, bt_row, g, tok0, 0, lane);
   };
