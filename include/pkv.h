@@ -175,7 +175,8 @@ pkv_status kv_pool_create(const pkv_pool_config* cfg, void* dev_mem, uint64_t by
  * int8 storage computes per (token, head): scale = fp32(absmax) / 127,
  * code = clamp(rint_even(fp32(x / scale)), -127, 127) (0 if absmax is 0) and
  * writes the scale beside the codes.  INT8_TENSOR uses the same code formula
- * with scales' k_scale / v_scale (positive, PKV_ERR_INVALID otherwise);
+ * with scales' k_scale / v_scale (positive and finite for fp8 and INT8_TENSOR,
+ * PKV_ERR_INVALID otherwise, as for the decode calls);
  * INT8_CHANNEL with the pool's channel scales of this layer (a scale of 0
  * gives code 0).  Two tokens with the same slot in one call race
  * (pkv_check_slots rejects that). */
@@ -404,12 +405,15 @@ int32_t kv_bm_ref_count(const pkv_bm* bm, int32_t block);
  *    SHA-256(key(i-1) || its B token ids as little-endian int32), key(-1) =
  *    32 zero bytes, so a key names the whole prefix up to that block;
  *  - kv_bm_add_seq_tokens reuses, for the longest run of leading full blocks
- *    whose keys are cached, those blocks (count + 1, also when they were
- *    free); every other block is fresh, and each fresh full block becomes
- *    the cached holder of its key (the previous holder, if any, loses it);
- *    the partial last block and blocks filled later by appends are never
- *    cached; *cached_tokens = reused blocks * B, the prefix whose KV is
- *    already in the pool (the caller computes the rest);
+ *    whose keys are cached and which lie wholly before the prompt's last
+ *    token (at most (n - 1) / B blocks), those blocks (count + 1, also when
+ *    they were free); every other block is fresh, and each fresh full block
+ *    becomes the cached holder of its key (the previous holder, if any, loses
+ *    it); the partial last block and blocks filled later by appends are never
+ *    cached; *cached_tokens = reused blocks * B < n, the prefix whose KV is
+ *    already in the pool: the caller computes the rest, which always holds
+ *    at least the last prompt token (its forward pass yields the first new
+ *    token, and its K/V never lands in a block another sequence shares);
  *  - a cached block whose count drops to 0 keeps its key and content while
  *    it waits on the free FIFO; it leaves the cache only when allocation
  *    takes it, so the least recently freed cached block is evicted first;
@@ -419,8 +423,9 @@ int32_t kv_bm_ref_count(const pkv_bm* bm, int32_t block);
  * reuse them (same stream order as the decode that follows). */
 pkv_status kv_bm_add_seq_tokens(pkv_bm* bm, int32_t seq, const int32_t* tokens, int32_t n,
                                 int32_t* cached_tokens);
-/* Full-block lookups and hits of kv_bm_add_seq_tokens so far ([KVP] §六 hit
- * rate) and the number of keys currently cached. */
+/* Lookups (blocks eligible for reuse, as above) and hits of
+ * kv_bm_add_seq_tokens so far ([KVP] §六 hit rate) and the number of keys
+ * currently cached. */
 pkv_status kv_bm_prefix_stats(const pkv_bm* bm, int64_t* lookups, int64_t* hits, int32_t* cached_blocks);
 /* The key of a block: SHA-256 of parent (32 bytes; NULL = zeros) followed by
  * tokens[0..n) as little-endian int32 (host arrays; out: 32 bytes). */

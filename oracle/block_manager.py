@@ -110,17 +110,22 @@ class BlockManagerModel:
         B = self.B
         n = len(tokens)
         full, total = n // B, -(-n // B)
+        # only blocks wholly before the last prompt token can be reused: that
+        # token is always computed, since its forward pass gives the first
+        # generated token (bjdmk.com.cn article, section 4.1: reuse the
+        # cached prefix, compute the rest)
+        eligible = (n - 1) // B if n > 0 else 0
         keys = []
         for i in range(full):
             keys.append(self.key(keys[-1] if keys else None, tokens[i * B:(i + 1) * B]))
         matched = 0
-        while matched < full and keys[matched] in self.cache:
+        while matched < eligible and keys[matched] in self.cache:
             matched += 1
         matched_free = sum(1 for i in range(matched) if self.ref[self.cache[keys[i]]] == 0)
         if total - matched > len(self.free) - matched_free:
             self.failed_allocs += 1
             return ERR_OUT_OF_BLOCKS, 0
-        self.lookups += full
+        self.lookups += eligible
         self.hits += matched
         table = []
         for i in range(matched):

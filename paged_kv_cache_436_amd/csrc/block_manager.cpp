@@ -318,12 +318,17 @@ pkv_status kv_bm_add_seq_tokens(pkv_bm* bm, int32_t seq, const int32_t* tokens, 
   const int32_t B = bm->block_size;
   const int64_t full = n / B;
   const int64_t total = ((int64_t)n + B - 1) / B;
+  // blocks that may be reused: those wholly before the prompt's last token,
+  // which is always left to compute (its forward pass yields the first
+  // generated token, and its K/V would otherwise be rewritten into a block
+  // other sequences share)
+  const int64_t eligible = n > 0 ? ((int64_t)n - 1) / B : 0;
   std::vector<pkv::Digest> keys((size_t)full);
   for (int64_t i = 0; i < full; ++i)
     kv_bm_block_key(i ? keys[(size_t)(i - 1)].data() : nullptr, tokens + i * B, B, keys[(size_t)i].data());
-  // the longest run of leading blocks already cached
+  // the longest run of leading eligible blocks already cached
   int64_t matched = 0, matched_free = 0;
-  while (matched < full) {
+  while (matched < eligible) {
     auto it = bm->cache.find(keys[(size_t)matched]);
     if (it == bm->cache.end()) break;
     if (bm->ref[(size_t)it->second] == 0) ++matched_free;
@@ -335,7 +340,7 @@ pkv_status kv_bm_add_seq_tokens(pkv_bm* bm, int32_t seq, const int32_t* tokens, 
               (long long)(bm->num_free - matched_free));
     return PKV_ERR_OUT_OF_BLOCKS;
   }
-  bm->lookups += full;
+  bm->lookups += eligible;
   bm->hits += matched;
   pkv_bm::Seq s;
   s.table.reserve((size_t)total);

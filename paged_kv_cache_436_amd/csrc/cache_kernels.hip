@@ -235,7 +235,8 @@ extern "C" pkv_status reshape_and_cache(const pkv_pool* pool, int32_t layer, con
   if (scales && (c.kv_dtype == PKV_KV_FP8_E5M2 || c.kv_dtype == PKV_KV_INT8_TENSOR)) {
     ksc = scales->k_scale;
     vsc = scales->v_scale;
-    if (!(ksc > 0.f) || !(vsc > 0.f)) return fail(PKV_ERR_INVALID, "per-tensor scales must be positive");
+    if (!(ksc > 0.f) || !(vsc > 0.f) || !(ksc < INFINITY) || !(vsc < INFINITY))
+      return fail(PKV_ERR_INVALID, "per-tensor scales must be positive and finite");
   }
   const int64_t waves = (int64_t)num_tokens * c.num_kv_heads;
   const int64_t grid = (waves + 3) / 4;

@@ -455,15 +455,21 @@ __device__ __forceinline__ void issue_chunks(SplitBuf<D, KVT>& r, const SplitPar
 
 // ---- appending decode.  Before streaming its range, a wave stores the new
 // token (position ctx - 1) of every row whose last step lies in that range,
-// encoded exactly as reshape_and_cache stores it.  The wave reads that tile
-// again at the row's last step: a wave's vector memory operations complete
-// in the order it issues them, and the lanes of one wave need no
-// synchronisation among themselves, so that later load sees the token
-// without a wait here.  No other wave reads
-// those bytes: the token's block is not shared (copy-on-write runs before the
-// append), the rest of its tile belongs to other steps, and when a KV head
-// has several 16-head rows, each of their last-step waves stores the same
-// bytes itself before reading them.  Stores cover the token's bytes only.
+// encoded exactly as reshape_and_cache stores it, and waits until those
+// stores have completed (s_waitcnt vmcnt(0)) before it issues its first K/V
+// load.  The wave reads that tile again at the row's last step.  A completed
+// store has reached the L2 of the wave's XCD and has updated or invalidated
+// the line in its CU's vector L1, which every wave of that CU shares (the
+// vector L1 is write-through; this is why, in the AMDGPU memory model for
+// gfx942 and gfx950 outside threadgroup-split mode, a workgroup-scope
+// release needs only that wait and an acquire no cache invalidation), so the
+// later load returns the token even when the line is shared with other KV
+// heads' tiles or int8 scale rows that other waves read.  No other wave
+// reads the token's own bytes: its block is not shared (copy-on-write runs
+// before the append), the rest of its tile belongs to other steps, and when
+// a KV head has several 16-head rows, each of their last-step waves stores
+// the same bytes itself before reading them.  Stores cover the token's bytes
+// only.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
@@ -1117,6 +1123,8 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
         } while (an == 0);
       }
     }
+    // the token stores have completed before any load of this wave is issued
+    wait_vm_all();
   }
 
   cursor_row(cur, p);
@@ -1338,14 +1346,15 @@ struct SplitSizes {
   int64_t rows, slots_cap, cnt_bytes, ml_bytes, acc_bytes;
 };
 
-// Workspace regions for the largest grid any variant may launch.
-bool split_sizes(int32_t S, int32_t Hq, int32_t Hkv_or_0, int32_t D, int32_t W, int32_t B, int32_t P,
+// Workspace regions for the largest grid any variant may launch.  rows_or_0:
+// the call's (sequence, KV head, head tile) rows when known, else 0 for the
+// bound S * Hq (one head per row when G == 1), which sizes a workspace
+// without the pool's head count.
+bool split_sizes(int32_t S, int32_t Hq, int32_t rows_or_0, int32_t D, int32_t W, int32_t B, int32_t P,
                  SplitSizes* z) {
   int cus = 0;
   if (device_cus(&cus) != 0) return false;
-  (void)Hkv_or_0;
-  // rows: at most S * Hq (one head per row when G == 1)
-  z->rows = (int64_t)S * Hq;
+  z->rows = rows_or_0 > 0 ? (int64_t)rows_or_0 : (int64_t)S * Hq;
   (void)P;                       // partials are per (row, wave) segment, whatever the partition size
   const int64_t steps_ub = z->rows * ceil_div((int64_t)W * B, 16);
   const int64_t waves_cap = split_grid(steps_ub, cus, kMaxBlocksPerCU) * kNW;
@@ -1444,6 +1453,35 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
   char* vl = static_cast<char*>(pool->v) + (uint64_t)layer * pool->layer_bytes;
   float* ksl = pool->k_scale ? pool->k_scale + layer * scale_layer : nullptr;
   float* vsl = pool->v_scale ? pool->v_scale + layer * scale_layer : nullptr;
+  // the split form's sizes and workspace, checked before anything is launched
+  SplitSizes z{};
+  int64_t split_grid_wg = 0;
+  if (partition_size != 0) {
+    if (partition_size < 0 || partition_size % 32 != 0) {
+      set_error("partition_size %d must be 0 or a positive multiple of 32", partition_size);
+      return PKV_ERR_INVALID;
+    }
+    const int TS = c.kv_dtype == PKV_KV_BF16 ? 16 : 32;
+    const int64_t steps_ub = rows * ceil_div((int64_t)table_width * c.block_size, TS);
+    if (steps_ub > INT32_MAX / 2) return fail(PKV_ERR_INVALID, "problem too large for one call");
+    if (!split_sizes(num_seqs, num_q_heads, 0, c.head_dim, table_width,
+                     c.block_size, partition_size, &z))
+      return fail(PKV_ERR_HIP, "could not query the current device");
+    const uint64_t need = (uint64_t)(z.cnt_bytes + z.ml_bytes + z.acc_bytes);
+    if (z.acc_bytes > (int64_t)UINT32_MAX)
+      return fail(PKV_ERR_INVALID, "too many (sequence, KV head) rows for one split-context call: split the batch");
+    if (!workspace || workspace_bytes < need) {
+      set_error("workspace of %llu bytes needed, got %llu", (unsigned long long)need,
+                (unsigned long long)workspace_bytes);
+      return PKV_ERR_INVALID;
+    }
+    if (((uintptr_t)workspace) % 256) return fail(PKV_ERR_INVALID, "workspace must be 256-byte aligned");
+    int cus = 0;
+    device_cus(&cus);
+    const int bpc = split_blocks_per_cu(c.head_dim, c.kv_dtype, c.block_size);
+    split_grid_wg = split_grid(steps_ub, cus, bpc);
+    if (split_grid_wg * kNW + z.rows > z.slots_cap) return fail(PKV_ERR_INVALID, "internal: workspace sizing");
+  }
   // the query the kernels read: q itself, or (per-channel int8) q with the K
   // channel scales folded in, written into the output rows first
   const uint16_t* qk = static_cast<const uint16_t*>(q);
@@ -1507,31 +1545,7 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     p.out_scale = vsc;
     e = launch_single(p, c.head_dim, c.kv_dtype, c.block_size, (int)grid, stream);
   } else {
-    if (partition_size < 0 || partition_size % 32 != 0) {
-      set_error("partition_size %d must be 0 or a positive multiple of 32", partition_size);
-      return PKV_ERR_INVALID;
-    }
-    const int TS = c.kv_dtype == PKV_KV_BF16 ? 16 : 32;
-    const int64_t steps_ub = rows * ceil_div((int64_t)table_width * c.block_size, TS);
-    if (steps_ub > INT32_MAX / 2) return fail(PKV_ERR_INVALID, "problem too large for one call");
-    SplitSizes z;
-    if (!split_sizes(num_seqs, num_q_heads, c.num_kv_heads, c.head_dim, table_width, c.block_size, partition_size,
-                     &z))
-      return fail(PKV_ERR_HIP, "could not query the current device");
-    const uint64_t need = (uint64_t)(z.cnt_bytes + z.ml_bytes + z.acc_bytes);
-    if (z.acc_bytes > (int64_t)UINT32_MAX)
-      return fail(PKV_ERR_INVALID, "too many (sequence, KV head) rows for one split-context call: split the batch");
-    if (!workspace || workspace_bytes < need) {
-      set_error("workspace of %llu bytes needed, got %llu", (unsigned long long)need,
-                (unsigned long long)workspace_bytes);
-      return PKV_ERR_INVALID;
-    }
-    if (((uintptr_t)workspace) % 256) return fail(PKV_ERR_INVALID, "workspace must be 256-byte aligned");
-    int cus = 0;
-    device_cus(&cus);
-    const int bpc = split_blocks_per_cu(c.head_dim, c.kv_dtype, c.block_size);
-    const int64_t grid = split_grid(steps_ub, cus, bpc);
-    if (grid * kNW + rows > z.slots_cap) return fail(PKV_ERR_INVALID, "internal: workspace sizing");
+    const int64_t grid = split_grid_wg;
     SplitParams p{};
     p.q = qk;
     p.q_stride = q_stride;

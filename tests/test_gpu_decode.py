@@ -372,6 +372,18 @@ def test_decode_append_many_short_rows(dt):
         _append_and_compare(rng, ctx, 2, 3, 64, 16, dt, P, f"decode_append short rows dt={dt} P={P}")
 
 
+@pytest.mark.parametrize("B", [8, 16])
+def test_decode_append_int8_scales_share_cache_lines(B):
+    # INT8 per-token scales take 4 B bytes per (block, KV head) tile, so one
+    # 128-byte line holds the scale rows of several KV heads, which other
+    # waves load while the appending wave stores its token's scale; with 8 KV
+    # heads and 120 sequences that happens throughout the launch
+    rng = np.random.default_rng(8400 + B)
+    ctx = rng.integers(1, 300, size=120)
+    _append_and_compare(rng, ctx, 8, 2, 128, B, pkv.PKV_KV_INT8, 64,
+                        f"decode_append int8 scales B={B} hkv=8 S=120")
+
+
 def test_decode_append_needs_split_form():
     import torch
     rng = np.random.default_rng(8200)

@@ -8,7 +8,7 @@ import pytest
 import paged_kv_cache_436_amd as pkv
 import workloads
 from oracle import attention, cache_ops, codecs
-from tests.gpu_helpers import bf16_dev, dev, errors, read_pool, say
+from tests.gpu_helpers import bf16_dev, dev, errors, first_diff, images_equal, read_pool, say
 
 pytestmark = pytest.mark.gpu
 
@@ -62,4 +62,78 @@ def test_reused_prefix_blocks_decode_like_a_full_prefill(P):
                                codecs.bf16_bits_to_f64(kv[s][1]), scale)
         assert np.max(np.abs(ref - want[s])) < 1e-12
     mx, rel = errors(got, want)
+    assert mx <= 1e-2 and rel <= 1e-3
+
+
+def test_whole_prompt_hit_leaves_last_block_to_prefill_then_decodes():
+    """A second request with the very same 64-token prompt (a multiple of the
+    block size) reuses every block before the last prompt token and prefills
+    the last block into a fresh one of its own; the shared blocks are never
+    written.  Prefill and a following appending decode step of both requests
+    match the oracle (bjdmk.com.cn article, §4.1: reuse the cached prefix,
+    compute the rest; "KV Cache 原理与 PagedAttention", §一: a decode step
+    appends K_t, V_t and attends)."""
+    import torch
+    rng = np.random.default_rng(13600)
+    B, H, G, D, NB, W = 16, 2, 4, 128, 32, 8
+    hq = H * G
+    cfg = pkv.make_config(1, NB, B, H, D, pkv.PKV_KV_BF16)
+    pool = pkv.Pool(cfg)
+    pool.memory.fill_(255)
+    bm = pkv.BlockManager(NB, B, rng.permutation(NB))
+    prompt = rng.integers(0, 1000, size=64).tolist()
+    # the same tokens at the same positions have the same K/V
+    k = workloads.to_bf16_bits(rng.standard_normal((64, H, D), dtype=np.float32))
+    v = workloads.to_bf16_bits(rng.standard_normal((64, H, D), dtype=np.float32))
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
+    img = read_pool(pool)
+    for s in range(2):
+        cached = bm.add_seq_tokens(s, prompt)
+        say(f"request {s}: 64 tokens, {cached} reused")
+        assert cached == (48 if s else 0)
+        tab, ctx = bm.block_tables([s], W)
+        pos = np.arange(cached, 64)
+        slots = tab[0][pos // B].astype(np.int64) * B + pos % B
+        before = read_pool(pool)
+        pkv.reshape_and_cache(pool, 0, bf16_dev(k[cached:]), bf16_dev(v[cached:]), dev(slots))
+        img = cache_ops.reshape_and_cache(img, 0, k[cached:], v[cached:], slots)
+        after = read_pool(pool)
+        assert images_equal(after, img), first_diff(after, img)
+        if s:
+            # the blocks request 0 holds are unchanged by request 1's prefill
+            t0, _ = bm.block_tables([0], W)
+            per_block = H * B * D                  # elements of one block's tiles (one layer)
+            for blk in t0[0][:4]:
+                r = slice(int(blk) * per_block, (int(blk) + 1) * per_block)
+                assert np.array_equal(after.k[r], before.k[r]) and np.array_equal(after.v[r], before.v[r])
+        n = 64 - cached
+        q = workloads.to_bf16_bits(rng.standard_normal((n, hq, D), dtype=np.float32))
+        qs = np.array([0, n], np.int32)
+        out = torch.full((n, hq, D), float("nan"), dtype=torch.float32, device="cuda")
+        pkv.paged_attn_prefill(out, bf16_dev(q), pool, 0, dev(tab), dev(ctx), dev(qs), scale, n)
+        torch.cuda.synchronize()
+        want = attention.paged_prefill(q, img, 0, tab, ctx, qs, scale)
+        mx, rel = errors(out.cpu().numpy(), want)
+        say(f"  prefill of {n} tokens: max_abs={mx:.3e} rel={rel:.3e}")
+        assert mx <= 1e-2 and rel <= 1e-3
+    t_both, _ = bm.block_tables([0, 1], W)
+    assert (t_both[0][:3] == t_both[1][:3]).all() and t_both[0][3] != t_both[1][3]
+    # one appending decode step of both requests (position 64 opens block 4)
+    slots, pairs = bm.append([0, 1])
+    assert pairs.shape[0] == 0
+    tables, ctx = bm.block_tables([0, 1], W)
+    nk = workloads.to_bf16_bits(rng.standard_normal((2, H, D), dtype=np.float32))
+    nv = workloads.to_bf16_bits(rng.standard_normal((2, H, D), dtype=np.float32))
+    q = workloads.to_bf16_bits(rng.standard_normal((2, hq, D), dtype=np.float32))
+    out = torch.empty((2, hq, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(pkv.paged_attn_workspace_bytes(2, hq, D, W, B, 64), dtype=torch.uint8, device="cuda")
+    pkv.paged_attn_decode_append(out, bf16_dev(q), pool, 0, bf16_dev(nk), bf16_dev(nv), dev(tables), dev(ctx),
+                                 scale, partition_size=64, workspace=ws)
+    torch.cuda.synchronize()
+    img = cache_ops.reshape_and_cache(img, 0, nk, nv, slots)
+    got_img = read_pool(pool)
+    assert images_equal(got_img, img), first_diff(got_img, img)
+    want = attention.paged_decode(q, img, 0, tables, ctx, scale)
+    mx, rel = errors(out.cpu().numpy(), want)
+    say(f"  decode: max_abs={mx:.3e} rel={rel:.3e}")
     assert mx <= 1e-2 and rel <= 1e-3

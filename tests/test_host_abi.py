@@ -257,3 +257,15 @@ def test_attention_entry_points_check_arguments_on_the_host():
     args.sliding_window, args.q = 40, P
     assert pkv._lib.paged_attn_decode_ex(ctypes.byref(args), None) == pkv.PKV_ERR_INVALID
     assert "alias" in pkv.last_error()
+
+
+def test_cache_write_refuses_non_finite_per_tensor_scales():
+    """fp8 and INT8-per-tensor cache writes take the same scale rule as the
+    reads: positive and finite; anything else is refused before a launch."""
+    P = 1 << 24
+    for dt in (pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8_TENSOR):
+        d = _fake_pool(dt)
+        for ks, vs in ((float("inf"), 1.0), (1.0, float("inf")), (float("nan"), 1.0), (0.0, 1.0), (1.0, -2.0)):
+            sc = pkv.KVScales(ks, vs)
+            st = pkv._lib.reshape_and_cache(ctypes.byref(d), 0, P, P, P, 3, ctypes.byref(sc), None)
+            assert st == pkv.PKV_ERR_INVALID and "finite" in pkv.last_error(), (dt, ks, vs)

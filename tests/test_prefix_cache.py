@@ -6,7 +6,10 @@ Python model bit for bit (tables, lengths, reused token counts, counters) on
 random mixes of prompts with shared prefixes, appends, forks and frees; and
 the model meets the pages' rules: identical prompts share every full block,
 prompts that first differ at token i share floor(i / B) blocks (an exact,
-position-aligned prefix only: bjdmk.com.cn article, §4.3), the same tokens at
+position-aligned prefix only: bjdmk.com.cn article, §4.3), the last prompt
+token is always left to compute (so at most (n - 1) / B blocks are reused:
+§4.1 reuses the cached prefix and computes the rest, and the rest must hold
+the token whose forward pass gives the first output), the same tokens at
 another position do not match, freed cached blocks are reused until
 allocation evicts them, least recently freed first, and a prompt that cannot
 be served changes nothing.
@@ -92,18 +95,41 @@ def test_cpp_prefix_cache_matches_model(seed):
 def test_identical_and_diverging_prompts():
     B = 8
     m = BlockManagerModel(64, B)
-    base = list(range(100, 140))                     # 40 tokens: 5 full blocks
+    base = list(range(100, 141))                     # 41 tokens: 5 full blocks + 1 token
     assert m.add_seq_tokens(0, base) == (OK, 0)
     assert m.add_seq_tokens(1, base) == (OK, 40)     # every full block reused
-    assert m.tables[1] == m.tables[0]
-    for i in (0, 1, 7, 8, 9, 23, 39):                # first difference at token i
+    assert m.tables[1][:5] == m.tables[0][:5]
+    assert m.tables[1][5] != m.tables[0][5]          # the partial tail is private
+    for i in (0, 1, 7, 8, 9, 23, 39, 40):            # first difference at token i
         other = list(base)
         other[i] += 1
         st, cached = m.add_seq_tokens(10 + i, other)
         assert st == OK and cached == (i // B) * B
         assert m.tables[10 + i][:i // B] == m.tables[0][:i // B]
     # a partial tail is never reused; the full part is
-    assert m.add_seq_tokens(2, base + [1, 2, 3]) == (OK, 40)
+    assert m.add_seq_tokens(2, base + [1, 2]) == (OK, 40)
+
+
+def test_last_prompt_token_is_always_computed():
+    B = 8
+    m = BlockManagerModel(64, B)
+    base = list(range(100, 140))                     # 40 tokens: exactly 5 full blocks
+    assert m.add_seq_tokens(0, base) == (OK, 0)
+    lookups0 = m.prefix_stats()[0]
+    # a whole-prompt hit still leaves the last block (which holds the last
+    # token) to compute, in a fresh block of its own
+    assert m.add_seq_tokens(1, base) == (OK, 32)
+    assert m.tables[1][:4] == m.tables[0][:4]
+    assert m.tables[1][4] != m.tables[0][4]
+    assert m.prefix_stats()[:2] == (lookups0 + 4, 4)
+    assert m.ref[m.tables[1][4]] == 1
+    # the fresh block took over the key: a longer prompt now reuses it
+    assert m.add_seq_tokens(2, base + [7]) == (OK, 40)
+    assert m.tables[2][4] == m.tables[1][4]
+    # prompts of one block, or of a single token, reuse nothing
+    assert m.add_seq_tokens(3, base[:8]) == (OK, 0)
+    assert m.add_seq_tokens(4, base[:1]) == (OK, 0)
+    assert m.add_seq_tokens(5, []) == (OK, 0)
 
 
 def test_same_tokens_elsewhere_do_not_match():
@@ -112,23 +138,23 @@ def test_same_tokens_elsewhere_do_not_match():
     blk = [5, 6, 7, 8]
     assert m.add_seq_tokens(0, blk + blk) == (OK, 0)
     # block 1 of seq 0 holds the same tokens as block 0, but its key includes block 0
-    assert m.add_seq_tokens(1, blk)[1] == 4
-    assert m.add_seq_tokens(2, [9, 9, 9, 9] + blk)[1] == 0
+    assert m.add_seq_tokens(1, blk + [1])[1] == 4
+    assert m.add_seq_tokens(2, [9, 9, 9, 9] + blk + [1])[1] == 0
 
 
 def test_freed_blocks_stay_cached_until_evicted_in_free_order():
     B = 4
-    m = BlockManagerModel(6, B)
-    a = [1] * 8                                      # 2 blocks
-    b = [2] * 8
-    assert m.add_seq_tokens(0, a) == (OK, 0)
-    assert m.add_seq_tokens(1, b) == (OK, 0)
+    m = BlockManagerModel(8, B)
+    a = [1] * 8 + [7]                                # 2 full blocks + a partial one
+    b = [2] * 8 + [7]
+    assert m.add_seq_tokens(0, a) == (OK, 0)         # blocks 0, 1, 2
+    assert m.add_seq_tokens(1, b) == (OK, 0)         # blocks 3, 4, 5
     m.free_seq(0)
     m.free_seq(1)                                    # free queue: 2 never used, then a's, then b's
-    assert m.add_seq_tokens(2, a) == (OK, 8)         # a is still cached
+    assert m.add_seq_tokens(2, a) == (OK, 8)         # a is still cached; its tail takes a new block
     m.free_seq(2)                                    # a's blocks go to the back again
-    # 4 fresh blocks: the 2 never-used ones, then b's (freed before a's): b is evicted
-    assert m.add_seq_tokens(3, [3] * 16) == (OK, 0)
+    # 5 fresh blocks: a never-used one, a's old tail, then b's (freed before a's): b is evicted
+    assert m.add_seq_tokens(3, [3] * 16 + [7]) == (OK, 0)
     m.free_seq(3)
     st, cached = m.add_seq_tokens(5, a)
     assert st == OK and cached == 8                  # a survived
