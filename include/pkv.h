@@ -348,6 +348,24 @@ typedef struct {
  * PKV_ERR_INVALID for a NULL args or a key without a value. */
 pkv_status paged_attn_decode_ex(const pkv_decode_args* args, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * decode as paged_attn_decode_ex (plain or appending form, sliding window,
+ * every storage type; identical results), with the split form's workspace
+ * taken from a static device array of 32 MiB (33554432 bytes) that the
+ * library holds on every GPU it runs on until the process ends.  The
+ * workspace and workspace_bytes fields are ignored; the caller passes only
+ * inputs and outputs.  Nothing is allocated and no allocating routine is
+ * called (the array's device address is looked up once per device, on the
+ * first call made with that device current).  A call whose split form would
+ * need more than 32 MiB - (rows + waves) partial slots of (D / 16) KiB plus
+ * 256 bytes each, rows = S * Hkv * ceil(G / 16), waves = 4 per compute unit -
+ * returns PKV_ERR_INVALID before any launch (e.g. D = 128: about 2,900 rows
+ * with 1,024 waves).  The array keeps the last call's contents; nothing in it
+ * needs clearing.  Calls that overlap in time on one GPU share the array and
+ * race: order them on one stream or with events. */
+pkv_status paged_attn_decode_noalloc(const pkv_decode_args* args, hipStream_t stream);
+
 /* ------------------------------------------------------------- host checks
  * Validators over HOST copies of device inputs, for callers that want to
  * rule out racing or out-of-range values before a launch.  Return PKV_OK or

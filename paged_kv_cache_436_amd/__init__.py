@@ -95,6 +95,7 @@ SIGNATURES = {
     "paged_attn_decode_append": (_I32, [_P, _P, ctypes.POINTER(PoolDesc), _I32, _P, _P, _P, _I32, _P, _I32,
                                         _I32, _F, _I32, ctypes.POINTER(KVScales), _I32, _P, _U64, _P]),
     "paged_attn_decode_ex": (_I32, [ctypes.POINTER(DecodeArgs), _P]),
+    "paged_attn_decode_noalloc": (_I32, [ctypes.POINTER(DecodeArgs), _P]),
     "paged_attn_prefill": (_I32, [_P, _P, ctypes.POINTER(PoolDesc), _I32, _P, _I32, _P, _P, _I32, _I32, _I32,
                                   _I32, _F, _I32, ctypes.POINTER(KVScales), _P]),
     "pkv_check_slots": (_I32, [_I64P, _I32, _I64]),
@@ -271,6 +272,27 @@ def paged_attn_decode_ex(out, q, pool: Pool, layer: int, block_tables, context_l
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.paged_attn_decode_ex(ctypes.byref(a), _stream(stream)))
+
+
+def paged_attn_decode_noalloc(out, q, pool: Pool, layer: int, block_tables, context_lens, scale: float,
+                              kv_dtype: int | None = None, k_scale: float = 1.0, v_scale: float = 1.0,
+                              partition_size: int = 0, key=None, value=None, sliding_window: int = 0,
+                              stream=None):
+    """paged_attn_decode_ex without a workspace argument: the split form's
+    scratch is the library's static device array (see pkv.h)."""
+    S, hq, _ = q.shape
+    sc = KVScales(k_scale, v_scale)
+    a = DecodeArgs()
+    a.out, a.q, a.pool, a.layer = _ptr(out), _ptr(q), ctypes.pointer(pool.desc), layer
+    a.key, a.value = _ptr(key), _ptr(value)
+    a.block_tables, a.table_width = _ptr(block_tables), block_tables.shape[1]
+    a.context_lens, a.num_seqs, a.num_q_heads = _ptr(context_lens), S, hq
+    a.scale = float(scale)
+    a.kv_dtype = pool.cfg.kv_dtype if kv_dtype is None else kv_dtype
+    a.kv_scales = ctypes.pointer(sc)
+    a.partition_size, a.sliding_window = partition_size, sliding_window
+    a.workspace, a.workspace_bytes = None, 0
+    _check(_lib.paged_attn_decode_noalloc(ctypes.byref(a), _stream(stream)))
 
 
 def paged_attn_prefill(out, q, pool: Pool, layer: int, block_tables, context_lens, query_start, scale: float,

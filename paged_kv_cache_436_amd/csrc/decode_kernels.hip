@@ -1346,6 +1346,32 @@ struct SplitSizes {
   int64_t rows, slots_cap, cnt_bytes, ml_bytes, acc_bytes;
 };
 
+// Scratch of paged_attn_decode_noalloc: the split form's row counters and
+// partials, in a static device array that every GPU the library runs on
+// holds until the process ends.  Its contents need no clearing: the row
+// counters are tagged with each call's epoch, and partials are written
+// before they are read.
+constexpr uint64_t kScratchBytes = 32ull << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+// The device address of this device's scratch array, looked up once per
+// device with that device current (in host code `scratch` names a host-side
+// stand-in, never a device address).
+int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return -1;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return 0;
+}
+
 // Workspace regions for the largest grid any variant may launch.  rows_or_0:
 // the call's (sequence, KV head, head tile) rows when known, else 0 for the
 // bound S * Hq (one head per row when G == 1), which sizes a workspace
@@ -1392,11 +1418,15 @@ extern "C" uint64_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_h
 
 namespace {
 
+// A decode call.  With use_scratch the split form's workspace is this
+// device's copy of the static scratch array (sized exactly for the call and
+// refused beyond kScratchBytes) and the workspace arguments are ignored.
 pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t layer, const void* key,
                        const void* value, const int32_t* block_tables, int32_t table_width,
                        const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
                        int32_t kv_dtype, const pkv_kv_scales* kv_scales, int32_t partition_size,
-                       int32_t sliding_window, void* workspace, uint64_t workspace_bytes, hipStream_t stream) {
+                       int32_t sliding_window, void* workspace, uint64_t workspace_bytes, hipStream_t stream,
+                       bool use_scratch = false) {
   const bool append = key != nullptr || value != nullptr;
   pkv_status st = check_pool(pool);
   if (st != PKV_OK) return st;
@@ -1456,6 +1486,7 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
   // the split form's sizes and workspace, checked before anything is launched
   SplitSizes z{};
   int64_t split_grid_wg = 0;
+  void* ws_base = workspace;
   if (partition_size != 0) {
     if (partition_size < 0 || partition_size % 32 != 0) {
       set_error("partition_size %d must be 0 or a positive multiple of 32", partition_size);
@@ -1464,18 +1495,27 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     const int TS = c.kv_dtype == PKV_KV_BF16 ? 16 : 32;
     const int64_t steps_ub = rows * ceil_div((int64_t)table_width * c.block_size, TS);
     if (steps_ub > INT32_MAX / 2) return fail(PKV_ERR_INVALID, "problem too large for one call");
-    if (!split_sizes(num_seqs, num_q_heads, 0, c.head_dim, table_width,
+    if (!split_sizes(num_seqs, num_q_heads, use_scratch ? (int32_t)rows : 0, c.head_dim, table_width,
                      c.block_size, partition_size, &z))
       return fail(PKV_ERR_HIP, "could not query the current device");
     const uint64_t need = (uint64_t)(z.cnt_bytes + z.ml_bytes + z.acc_bytes);
     if (z.acc_bytes > (int64_t)UINT32_MAX)
       return fail(PKV_ERR_INVALID, "too many (sequence, KV head) rows for one split-context call: split the batch");
-    if (!workspace || workspace_bytes < need) {
-      set_error("workspace of %llu bytes needed, got %llu", (unsigned long long)need,
-                (unsigned long long)workspace_bytes);
-      return PKV_ERR_INVALID;
+    if (use_scratch) {
+      if (need > kScratchBytes) {
+        set_error("this call needs %llu bytes of scratch, the static scratch holds %llu: split the batch",
+                  (unsigned long long)need, (unsigned long long)kScratchBytes);
+        return PKV_ERR_INVALID;
+      }
+      if (scratch_address(&ws_base) != 0) return fail(PKV_ERR_HIP, "could not find the scratch array on this device");
+    } else {
+      if (!workspace || workspace_bytes < need) {
+        set_error("workspace of %llu bytes needed, got %llu", (unsigned long long)need,
+                  (unsigned long long)workspace_bytes);
+        return PKV_ERR_INVALID;
+      }
+      if (((uintptr_t)workspace) % 256) return fail(PKV_ERR_INVALID, "workspace must be 256-byte aligned");
     }
-    if (((uintptr_t)workspace) % 256) return fail(PKV_ERR_INVALID, "workspace must be 256-byte aligned");
     int cus = 0;
     device_cus(&cus);
     const int bpc = split_blocks_per_cu(c.head_dim, c.kv_dtype, c.block_size);
@@ -1562,7 +1602,7 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     p.new_v = static_cast<const uint16_t*>(value);
     p.enc_k = ksc;
     p.enc_v = vsc;
-    char* ws = static_cast<char*>(workspace);
+    char* ws = static_cast<char*>(ws_base);
     p.row_done = reinterpret_cast<uint64_t*>(ws);
     p.part_ml = reinterpret_cast<float*>(ws + z.cnt_bytes);
     p.part_acc = reinterpret_cast<float*>(ws + z.cnt_bytes + z.ml_bytes);
@@ -1623,4 +1663,12 @@ extern "C" pkv_status paged_attn_decode_ex(const pkv_decode_args* a, hipStream_t
   return decode_impl(a->out, a->q, a->pool, a->layer, a->key, a->value, a->block_tables, a->table_width,
                      a->context_lens, a->num_seqs, a->num_q_heads, a->scale, a->kv_dtype, a->kv_scales,
                      a->partition_size, a->sliding_window, a->workspace, a->workspace_bytes, stream);
+}
+
+extern "C" pkv_status paged_attn_decode_noalloc(const pkv_decode_args* a, hipStream_t stream) {
+  if (!a) return fail(PKV_ERR_INVALID, "NULL argument block");
+  if ((a->key == nullptr) != (a->value == nullptr)) return fail(PKV_ERR_INVALID, "key and value must both be given");
+  return decode_impl(a->out, a->q, a->pool, a->layer, a->key, a->value, a->block_tables, a->table_width,
+                     a->context_lens, a->num_seqs, a->num_q_heads, a->scale, a->kv_dtype, a->kv_scales,
+                     a->partition_size, a->sliding_window, nullptr, 0, stream, true);
 }
