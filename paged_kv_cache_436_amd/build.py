@@ -34,6 +34,11 @@ HIPCC_FLAGS = [
     # register allocator parks accumulators and K/V buffers in AGPRs and
     # copies them back for every vector instruction that touches them
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # no combining of a wave's atomics on one address into one: the counter
+    # updates are made by a single lane, and the combined form waits for the
+    # atomic's result right after issuing it, which would stall the K/V
+    # pipeline the decode kernel keeps in flight
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function",
 ]
 CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__"]

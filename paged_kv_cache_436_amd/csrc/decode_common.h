@@ -106,6 +106,14 @@ __device__ __forceinline__ float sum_x32(float x) {
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maximum).
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N), N <= 63 (vmcnt bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their maximum): wait until at most N vector memory operations of
+// the wave are outstanding.
+template <int N>
+__device__ __forceinline__ void vm_wait_at_most() {
+  static_assert(N >= 0 && N <= 63, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>).
 template <class F, int... I>
@@ -263,12 +271,14 @@ __device__ __forceinline__ void issue_step(StepRegs<D, KVT>& r, const DecodePara
   }
 }
 
-// INT8 with per-channel scales: the K scale of (KV head, dim) is folded into
-// the query, z = sum_d (q_d * s_d) * code_d, so the decode kernels see plain
-// int8 codes.  q'[s][h][d] = bf16(fp32(q) * s_k[h / G][d]) (rounded to
-// nearest even) is written over the first half of the output row out[s][h],
-// which only that row's final merge writes, after every read of q'; the
-// kernels read it with a row stride of 2 D elements.
+// INT8 with per-channel scales (and INT4): the K scale of (KV head, dim) is
+// folded into the query, z = sum_d (q_d * s_d) * code_d, so the kernels see
+// plain codes.  q'[s][h][d] = fp32(q) * s_k[h / G][d] is written as two bf16
+// parts, hi = bf16(q') and lo = bf16(q' - hi) (round to nearest even; hi + lo
+// carries ~16 significant bits of q'), over the output row out[s][h], which
+// only that row's final store writes, after every read of q': hi in the first
+// D bf16 slots of the row, lo in the next D (row stride 2 D bf16 elements).
+// Kernels that take one bf16 query operand read hi only.
 __global__ __launch_bounds__(256) void fold_q_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ qf,
                                                      const float* __restrict__ ks_ch, int64_t n, int32_t Hq,
                                                      int32_t G, int32_t D) {
@@ -278,7 +288,10 @@ __global__ __launch_bounds__(256) void fold_q_kernel(const uint16_t* __restrict_
   const int64_t row = i / D;
   const int h = (int)(row % Hq);
   const float x = bf16_bits_to_float(q[i]) * ks_ch[(h / G) * D + d];
-  qf[row * 2 * D + d] = (uint16_t)(pack_bf16x2(x, 0.f) & 0xffffu);
+  const uint32_t hi = pack_bf16x2(x, 0.f) & 0xffffu;
+  const uint32_t lo = pack_bf16x2(x - bf16_bits_to_float(hi), 0.f) & 0xffffu;
+  qf[row * 2 * D + d] = (uint16_t)hi;
+  qf[row * 2 * D + D + d] = (uint16_t)lo;
 }
 
 // ---------------------------------------------------------------- launches

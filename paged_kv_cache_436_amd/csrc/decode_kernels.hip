@@ -293,6 +293,7 @@ struct SplitParams {
   float* part_ml;             // workspace: [slots][16][2]  (m, l)
   float* part_acc;            // workspace: [slots][NC][64 lanes][4]
   uint32_t acc_bytes;         // size of part_acc in bytes (< 4 GiB)
+  uint32_t ml_bytes;          // size of part_ml in bytes
   int32_t W, S, Hq, Hkv, G, QT, HQ, num_blocks;
   int32_t NWV;                // waves in the grid
   int32_t win;                // sliding window (positions), 0 = whole context
@@ -307,35 +308,39 @@ struct SplitParams {
 template <int D, int KVT>
 struct SplitGeo {
   static constexpr bool I4 = KVT == PKV_KV_INT4;
-  static constexpr int E = KVT == PKV_KV_BF16 ? 2 : 1;
-  static constexpr int CH = E == 2 ? 1 : 2;       // 16-token chunks per step
+  static constexpr bool BF = KVT == PKV_KV_BF16;
+  static constexpr bool FP8 = KVT == PKV_KV_FP8_E5M2;
+  static constexpr bool TOK = KVT == PKV_KV_INT8;                  // per-(token, head) scales
+  static constexpr bool CHAN = KVT == PKV_KV_INT8_CHANNEL || I4;   // K channel scales folded into q
+  static constexpr int E = BF ? 2 : 1;            // bytes per stored element (INT4: half a byte)
+  static constexpr int CH = BF ? 1 : 2;           // 16-token chunks per step
   static constexpr int TS = 16 * CH;              // tokens per step
-  static constexpr int LPC = I4 ? 1 : D * E / 64; // 16-byte loads per chunk per lane, for K and for V
+  static constexpr int LPC = I4 ? 1 : D * E / 64; // loads per chunk per lane, for K and for V
                                                   // (INT4: one load of D / 8 bytes)
-  static constexpr int KK = D / 32;               // q.K MFMAs per chunk
+  static constexpr int KK = D / 32;               // q.K matrix-core steps per chunk
   static constexpr int NC = D / 16;               // accumulator tiles of 16 dims
   static constexpr int QL = I4 ? 2 : E;           // query dim layout (q_dim0)
   static constexpr int AL = I4 ? 0 : E;           // accumulator dim layout (acc_dim)
+  static constexpr int NQ = CHAN ? 2 : 1;         // query operand sets: the folded query as bf16 hi + lo
+  static constexpr int P4 = D / 8;                // INT4: bytes per piece
+  // bytes of one token's K (V) inside a tile, as an offset from the tile start
+  // for a token at offset t of its block: K pieces are runs of tokens, V
+  // groups of 4 tokens are stored dim by dim (see the pool layout)
+  static constexpr int KTOK = I4 ? P4 : 16;
+  static constexpr int VTOK = I4 ? 4 * P4 : D * E;
+  static constexpr int LPS = CH * 2 * LPC + (TOK ? 2 * CH : 0);   // vector loads of one step
 };
 
+// Registers of one step: K and V loads of each chunk, and the per-token int8
+// scales of the lane's four tokens per chunk.
 template <int D, int KVT>
 struct SplitBuf {
   using G_ = SplitGeo<D, KVT>;
   u32x4 k[G_::CH][G_::LPC];
   u32x4 v[G_::CH][G_::LPC];
-  f32x4 ksc[G_::CH];
-  f32x4 vsc[G_::CH];
+  f32x4 ksc[G_::TOK ? G_::CH : 1];
+  f32x4 vsc[G_::TOK ? G_::CH : 1];
 };
-
-// Wave-uniform description of one issued step.
-struct StepMeta {
-  int t0;       // first token of the step within its row
-  int t_end;    // row's context length (0 for a step past the wave's range)
-  int slot;     // partial slot of the step's segment
-  int flags;    // kNewRow | kFlush, and the row's query heads (<= 16) from bit 8
-};
-constexpr int kNewRow = 1;   // first step of a row in this wave: its q was loaded with the step
-constexpr int kFlush = 2;    // last step of a segment: write the partial
 
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
@@ -353,102 +358,134 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 }
 
 // The query group of one row as the B operand of q.K: lane (j, row) holds
-// head row of the tile.
-template <int KK>
+// head row of the tile; with folded channel scales, set 0 is the bf16 hi part
+// and set 1 the lo part of the folded query (q' = hi + lo to ~16 bits).
+template <int KK, int NQ>
 struct QRegs {
-  bf16x8 q[KK];
-  float qs;       // INT4: the row's head's sum of q over all dims (for the 136 offset)
+  bf16x8 q[NQ][KK];
 };
 
 template <int D, int KVT>
-__device__ __forceinline__ QRegs<SplitGeo<D, KVT>::KK> load_q(const SplitParams& p, int s, int h0, int gt,
-                                                               int lane) {
+__device__ __forceinline__ QRegs<SplitGeo<D, KVT>::KK, SplitGeo<D, KVT>::NQ> load_q(const SplitParams& p, int s,
+                                                                                    int h0, int gt, int lane) {
   using GE = SplitGeo<D, KVT>;
   const int row = lane & 15;
   const int j = lane >> 4;
   // rows past the tile's heads read a valid head; their columns are never stored
   const uint16_t* qh = p.q + ((int64_t)s * p.Hq + h0 + (row < gt ? row : 0)) * p.q_stride;
-  QRegs<GE::KK> r;
+  QRegs<GE::KK, GE::NQ> r;
 #pragma unroll
-  for (int kk = 0; kk < GE::KK; ++kk)
-    r.q[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + q_dim0<GE::QL>(kk, j)));
-  r.qs = 0.f;
-  if constexpr (GE::I4) {
-    float a = 0.f;
+  for (int n = 0; n < GE::NQ; ++n)
 #pragma unroll
     for (int kk = 0; kk < GE::KK; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) a += (float)r.q[kk][e];
-    r.qs = sum_x32(sum_x16(a));      // lanes of one head row hold its 4 dim slots
-  }
+      r.q[n][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + n * D + q_dim0<GE::QL>(kk, j)));
   return r;
 }
 
-// Load the K/V (and int8 scales) of one step.  A chunk at or past t_end -
-// the tail of a row, or any chunk of a step past the wave's range - or wholly
-// before the window's first position reads the tile of block 0, head 0
-// instead: it is masked or never consumed, and the
-// load keeps the number of loads per step fixed, which the compiler's
-// wait-count tracking needs to let later steps' loads stay in flight.
-template <int D, int KVT, int B>
-__device__ __forceinline__ void issue_chunks(SplitBuf<D, KVT>& r, const SplitParams& p, const int (&phys)[4],
-                                             int g, int t0, int t_lo, int t_end, int lane) {
+// INT4: the sum over all dims of the row's head's (folded) query, which the
+// 136 offset of the K operand is taken back with.
+template <int D, int KVT>
+__device__ __forceinline__ float query_sum(const QRegs<SplitGeo<D, KVT>::KK, SplitGeo<D, KVT>::NQ>& q) {
   using GE = SplitGeo<D, KVT>;
-  constexpr int E = GE::E;
+  float a = 0.f;
+#pragma unroll
+  for (int n = 0; n < GE::NQ; ++n)
+#pragma unroll
+    for (int kk = 0; kk < GE::KK; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a += (float)q.q[n][kk][e];
+  return sum_x32(sum_x16(a));      // lanes of one head row hold its 4 dim slots
+}
+
+// Lane-constant byte offsets of a lane's loads inside a tile (or, for the
+// int8 scales, inside a block's scale row).  K: lane (j, row) reads token
+// row of the chunk, piece j (+ 4 u); V and scales: lane j reads tokens
+// 4 j .. 4 j + 3, V dims by row.  With 8-token blocks a chunk covers two
+// blocks: the token (group) index inside its block wraps at 8 (2 groups).
+template <int D, int KVT, int B>
+struct LaneOff {
+  uint32_t k, v, s;
+  __device__ __forceinline__ LaneOff(int lane) {
+    using GE = SplitGeo<D, KVT>;
+    constexpr int TM = (B < 16 ? B : 16) - 1;
+    constexpr int JM = B < 16 ? 1 : 3;
+    const int row = lane & 15;
+    const int j = lane >> 4;
+    if constexpr (GE::I4) {
+      k = (uint32_t)((j * B + (row & TM)) * GE::P4);
+      v = (uint32_t)(((j & JM) * 16 + row) * GE::P4);
+    } else {
+      k = (uint32_t)((j * B + (row & TM)) * 16);
+      v = (uint32_t)(((j & JM) * D + (GE::E == 2 ? 2 * row : 4 * row)) * 4 * GE::E);
+    }
+    s = (uint32_t)(16 * (j & JM));
+  }
+};
+
+// Load the K/V (and int8 scales) of one step of tokens [t0, t0 + TS) of KV
+// head g.  ph holds the step's table entries (one per 16-token chunk when
+// blocks are smaller than a step, two per chunk with 8-token blocks), read
+// for logical blocks clamped to the row's attended range: a chunk outside
+// [t_lo, t_end) re-reads a block of the row and is masked.  The tile base is
+// wave-uniform (scalar registers); the lane offsets are constant, so a step
+// costs no per-lane address arithmetic except with 8-token blocks, where
+// the two halves of a chunk come from two tiles.
+template <int D, int KVT, int B, int NE>
+__device__ __forceinline__ void issue_step(SplitBuf<D, KVT>& r, const SplitParams& p, const int (&ph)[NE], int g,
+                                           int t0, const LaneOff<D, KVT, B>& lo, int lane) {
+  using GE = SplitGeo<D, KVT>;
+  constexpr uint32_t TB = GE::I4 ? (uint32_t)(B * D / 2) : (uint32_t)(B * D * GE::E);
   const int row = lane & 15;
   const int j = lane >> 4;
 #pragma unroll
   for (int h = 0; h < GE::CH; ++h) {
-    const int t = t0 + 16 * h;
-    const bool live = t < t_end && t + 16 > t_lo;  // wave-uniform
-    // with B = 8 the chunk spans two blocks: K lane row reads token t + row,
-    // V (and the int8 scales) lane j tokens t + 4j .. t + 4j + 3
-    const int pa = B < 16 ? phys[2 * h] : phys[h];
-    const int pb = B < 16 ? phys[2 * h + 1] : phys[h];
-    const int pk = row < 8 ? pa : pb;
-    const int pv = j < 2 ? pa : pb;
-    // chunks start at multiples of 16 tokens: with B >= 16 the chunk sits at
-    // offset t % B of one block, with B = 8 it starts both of its blocks
-    constexpr int TM = (B < 16 ? B : 16) - 1;
-    const int toff = (B < 16 || !live) ? 0 : t % B;
-    const int tk = toff + (row & TM);
-    const int tv = toff + ((4 * j) & TM);
-    // tile numbers are below num_blocks * Hkv < 2^31: unsigned 32-bit
-    // products widened once keep the address arithmetic short
-    const uint32_t tilek = live ? (uint32_t)pk * (uint32_t)p.Hkv + (uint32_t)g : 0u;
-    const uint32_t tilev = live ? (uint32_t)pv * (uint32_t)p.Hkv + (uint32_t)g : 0u;
+    const char* kb;
+    const char* vb;
+    const float* kscb = nullptr;
+    const float* vscb = nullptr;
+    if constexpr (B >= 16) {
+      // the chunk lies in one block: entry h (B = 16 with 32-token steps) or
+      // the step's only entry at token offset t0 % B + 16 h
+      constexpr bool one = B >= GE::TS;
+      const uint32_t tok = one ? ((uint32_t)t0 % B) + 16u * h : 0u;
+      const uint32_t tile = (uint32_t)ph[one ? 0 : h] * (uint32_t)p.Hkv + (uint32_t)g;
+      const uint64_t off = (uint64_t)tile * TB;
+      kb = p.k + off + tok * GE::KTOK;
+      vb = p.v + off + tok * GE::VTOK;
+      if constexpr (GE::TOK) {
+        kscb = p.ks + ((uint64_t)tile * B + tok);
+        vscb = p.vs + ((uint64_t)tile * B + tok);
+      }
+    } else {
+      // 8-token blocks: tokens 0-7 of the chunk in entry 2h, 8-15 in 2h + 1
+      const uint64_t oa = (uint64_t)((uint32_t)ph[2 * h] * (uint32_t)p.Hkv + (uint32_t)g);
+      const uint64_t ob = (uint64_t)((uint32_t)ph[2 * h + 1] * (uint32_t)p.Hkv + (uint32_t)g);
+      kb = p.k + (row < 8 ? oa : ob) * TB;
+      vb = p.v + (j < 2 ? oa : ob) * TB;
+      if constexpr (GE::TOK) {
+        kscb = p.ks + (j < 2 ? oa : ob) * B;
+        vscb = p.vs + (j < 2 ? oa : ob) * B;
+      }
+    }
     if constexpr (GE::I4) {
-      // K piece (j, token), V piece (token group, dim row): D / 8 bytes each
-      constexpr int P = D / 8;
-      const char* kt = p.k + (uint64_t)tilek * (uint32_t)(B * D / 2);
-      const char* vt = p.v + (uint64_t)tilev * (uint32_t)(B * D / 2);
-      const char* ka = kt + (j * B + tk) * P;
-      const char* va = vt + ((tv >> 2) * 16 + row) * P;
-      if constexpr (P == 16) {
-        r.k[h][0] = ld16(ka);
-        r.v[h][0] = ld16(va);
+      if constexpr (GE::P4 == 16) {
+        r.k[h][0] = ld16(kb + lo.k);
+        r.v[h][0] = ld16(vb + lo.v);
       } else {
-        const u32x2 k2 = *reinterpret_cast<const u32x2*>(ka);
-        const u32x2 v2 = *reinterpret_cast<const u32x2*>(va);
+        const u32x2 k2 = *reinterpret_cast<const u32x2*>(kb + lo.k);
+        const u32x2 v2 = *reinterpret_cast<const u32x2*>(vb + lo.v);
         r.k[h][0] = u32x4{k2[0], k2[1], 0u, 0u};
         r.v[h][0] = u32x4{v2[0], v2[1], 0u, 0u};
       }
-      continue;
-    }
-    const char* kt = p.k + (uint64_t)tilek * (uint32_t)(B * D * E);
-    const char* vt = p.v + (uint64_t)tilev * (uint32_t)(B * D * E);
+    } else {
 #pragma unroll
-    for (int u = 0; u < GE::LPC; ++u) r.k[h][u] = ld16(kt + ((4 * u + j) * B + tk) * 16);
-    const int grp = tv >> 2;
+      for (int u = 0; u < GE::LPC; ++u) r.k[h][u] = ld16(kb + lo.k + u * 64 * B);
 #pragma unroll
-    for (int u = 0; u < GE::LPC; ++u) {
-      const int d = (E == 2) ? (32 * u + 2 * row) : (64 * u + 4 * row);
-      r.v[h][u] = ld16(vt + (grp * D + d) * 4 * E);
+      for (int u = 0; u < GE::LPC; ++u) r.v[h][u] = ld16(vb + lo.v + u * 256);
     }
-    if constexpr (KVT == PKV_KV_INT8) {
-      const uint64_t so = (uint64_t)tilev * B + tv;
-      r.ksc[h] = *reinterpret_cast<const f32x4*>(p.ks + so);
-      r.vsc[h] = *reinterpret_cast<const f32x4*>(p.vs + so);
+    if constexpr (GE::TOK) {
+      r.ksc[h] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(kscb) + lo.s);
+      r.vsc[h] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(vscb) + lo.s);
     }
   }
 }
@@ -600,14 +637,76 @@ __device__ __forceinline__ void append_token(const SplitParams& p, int s, int g,
 // segment instead of every step.  Any reference gives the same softmax.
 constexpr float kRescaleSlack = 8.0f;
 
-// Online-softmax update of (m_run, l_run, acc) with one step.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed fp16 pair (round to nearest even).
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  f16x2 r;
+  r[0] = (_Float16)a;
+  r[1] = (_Float16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+// Packed fp16 pair plus c (both halves), rounded to nearest even.
+__device__ __forceinline__ uint32_t add_f16x2(uint32_t w, _Float16 c) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, w) + f16x2{c, c});
+}
+
+// V words (4 tokens of one dim, one byte each) -> fp16 pairs of tokens
+// (0, 1) and (2, 3), exactly.  e5m2 is the upper byte of an fp16 with the
+// same exponent bias, so the byte moves into place; an int8 code c is stored
+// as the fp16 1024 + (c + 128) (the byte c ^ 0x80 under the exponent bits of
+// 1024) and 1152 is taken back, exactly, in fp16.
+template <int KVT>
+__device__ __forceinline__ void v_to_f16(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  if constexpr (KVT == PKV_KV_FP8_E5M2) {
+    lo = __builtin_amdgcn_perm(0u, w, 0x010c000cu);
+    hi = __builtin_amdgcn_perm(0u, w, 0x030c020cu);
+  } else {
+    const uint32_t u = w ^ 0x80808080u;
+    lo = add_f16x2(__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u), (_Float16)-1152.0f);
+    hi = add_f16x2(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u), (_Float16)-1152.0f);
+  }
+}
+// INT4 V: pair k of a word (nibbles at bits 4k and 16 + 4k, stored as code
+// + 8) -> the fp16 codes, exactly (1024 + nibble, less 1032).
+__device__ __forceinline__ uint32_t int4_pair_f16(uint32_t w, int k) {
+  return add_f16x2(0x64006400u | ((w >> (4 * k)) & 0x000F000Fu), (_Float16)-1032.0f);
+}
+
+// K operand of q.K step kk of chunk h, as bf16 (exact: 8-bit codes and e5m2
+// widen without rounding; INT4 nibbles become 136 + code).
 template <int D, int KVT>
-__device__ __forceinline__ void compute_step(const SplitBuf<D, KVT>& r, const QRegs<SplitGeo<D, KVT>::KK>& qop,
-                                             const SplitParams& p, int t0, int t_lo, int t_end, int lane,
-                                             float& m_run,
-                                             float& l_run, f32x4* acc) {
+__device__ __forceinline__ bf16x8 k_operand(const SplitBuf<D, KVT>& r, int h, int kk) {
   using GE = SplitGeo<D, KVT>;
-  constexpr int E = GE::E;
+  if constexpr (GE::I4) {
+    const uint32_t wk = r.k[h][0][kk];          // word kk: dims 32 kk + 8 j .. + 7
+    return __builtin_bit_cast(bf16x8, u32x4{int4_pair(wk, 0), int4_pair(wk, 1), int4_pair(wk, 2), int4_pair(wk, 3)});
+  } else if constexpr (GE::E == 2) {
+    return __builtin_bit_cast(bf16x8, r.k[h][kk]);
+  } else {
+    const u32x4 wv = r.k[h][kk >> 1];
+    return (kk & 1) ? widen8<KVT == PKV_KV_FP8_E5M2 ? PKV_KV_FP8_E5M2 : PKV_KV_INT8>(wv[2], wv[3])
+                    : widen8<KVT == PKV_KV_FP8_E5M2 ? PKV_KV_FP8_E5M2 : PKV_KV_INT8>(wv[0], wv[1]);
+  }
+}
+
+// Online-softmax update of (m_run, l_run, acc) with one step of tokens
+// [t0, t0 + TS).  Only an edge step (one reaching past t_end or starting
+// before t_lo) masks: its logits outside [t_lo, t_end) become -inf, and the
+// V elements (or p, when per-token scales multiply it) of those tokens are
+// zeroed so that unwritten slots and blocks before a window (any bit
+// pattern) cannot reach the accumulator through 0 * NaN.
+// P.V: bf16 storage meets p as bf16 hi + lo parts (~16 bits of p); 8-bit and
+// 4-bit storage converts V exactly to fp16 and meets p rounded to fp16
+// (11 bits), one matrix-core step per tile.
+template <int D, int KVT>
+__device__ __forceinline__ void compute_step(const SplitBuf<D, KVT>& r,
+                                             const QRegs<SplitGeo<D, KVT>::KK, SplitGeo<D, KVT>::NQ>& qop,
+                                             float qs, float qk_scale, int t0, int t_lo, int t_end, bool edge,
+                                             int lane, float& m_run, float& l_run,
+                                             f32x4 (&acc)[SplitGeo<D, KVT>::NC]) {
+  using GE = SplitGeo<D, KVT>;
   constexpr int CH = GE::CH;
   const int j = lane >> 4;
   f32x4 z[CH];
@@ -616,37 +715,27 @@ __device__ __forceinline__ void compute_step(const SplitBuf<D, KVT>& r, const QR
     f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < GE::KK; ++kk) {
-      bf16x8 a;
-      if constexpr (GE::I4) {
-        const uint32_t wk = r.k[h][0][kk];          // word kk: dims 32 kk + 8 j .. + 7
-        a = __builtin_bit_cast(bf16x8, u32x4{int4_pair(wk, 0), int4_pair(wk, 1), int4_pair(wk, 2), int4_pair(wk, 3)});
-      } else if constexpr (E == 2) {
-        a = __builtin_bit_cast(bf16x8, r.k[h][kk]);
-      } else {
-        const u32x4 wv = r.k[h][kk >> 1];
-        a = (kk & 1) ? widen8<KVT>(wv[2], wv[3]) : widen8<KVT>(wv[0], wv[1]);
-      }
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop.q[kk], c, 0, 0, 0);
+      const bf16x8 a = k_operand<D, KVT>(r, h, kk);
+#pragma unroll
+      for (int n = 0; n < GE::NQ; ++n) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop.q[n][kk], c, 0, 0, 0);
     }
-    if constexpr (GE::I4) c -= kInt4Bias * qop.qs;  // the K operand held 136 + code
+    if constexpr (GE::I4) c -= kInt4Bias * qs;   // the K operand held 136 + code
+    if constexpr (GE::TOK) c *= r.ksc[h];
     z[h] = c;
+  }
+  if (edge) {
+#pragma unroll
+    for (int h = 0; h < CH; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[h][i] = tok_in(t0 + 16 * h + 4 * j + i, t_lo, t_end) ? z[h][i] : -INFINITY;
   }
   float mloc = -INFINITY;
 #pragma unroll
-  for (int h = 0; h < CH; ++h) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 16 * h + 4 * j + i;
-      float zz = z[h][i] * p.qk_scale;
-      if constexpr (KVT == PKV_KV_INT8) zz *= r.ksc[h][i];
-      zz = (t < t_end && t >= t_lo) ? zz : -INFINITY;
-      z[h][i] = zz;
-      mloc = fmaxf(mloc, zz);
-    }
-  }
-  mloc = max_x32(max_x16(mloc));              // finite: token t0 < t_end is in every step
-  const bool bump = mloc > m_run + kRescaleSlack;   // always true on a segment's first step
-  const float m_ref = bump ? mloc : m_run;
+  for (int h = 0; h < CH; ++h) mloc = fmaxf(fmaxf(mloc, fmaxf(z[h][0], z[h][1])), fmaxf(z[h][2], z[h][3]));
+  // finite: every step holds a token of [t_lo, t_end); qk_scale > 0
+  const float ms = max_x32(max_x16(mloc)) * qk_scale;
+  const bool bump = ms > m_run + kRescaleSlack;   // always true on a segment's first step
+  const float m_ref = bump ? ms : m_run;
   const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - m_ref) : 1.0f;
   // the accumulator is zero until the first step has run, so only a raise of a
   // finite reference needs the rescale (wave-uniform branch)
@@ -655,160 +744,158 @@ __device__ __forceinline__ void compute_step(const SplitBuf<D, KVT>& r, const QR
     for (int c = 0; c < GE::NC; ++c) acc[c] = acc[c] * alpha;
   }
   m_run = m_ref;
+  float pv[CH][4];
   float psum = 0.f;
-  uint32_t ph[CH][2], pl[CH][2];
-#pragma unroll
-  for (int h = 0; h < CH; ++h) {
-    float pv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pv[i] = __builtin_amdgcn_exp2f(z[h][i] - m_ref);
-      psum += pv[i];
-      if constexpr (KVT == PKV_KV_INT8) {
-        const int t = t0 + 16 * h + 4 * j + i;
-        pv[i] = tok_in(t, t_lo, t_end) ? pv[i] * r.vsc[h][i] : 0.f;   // fold the V scale into p
-      }
-    }
-    ph[h][0] = pack_bf16x2(pv[0], pv[1]);
-    ph[h][1] = pack_bf16x2(pv[2], pv[3]);
-    pl[h][0] = pack_bf16x2(pv[0] - bf16_lo(ph[h][0]), pv[1] - bf16_hi(ph[h][0]));
-    pl[h][1] = pack_bf16x2(pv[2] - bf16_lo(ph[h][1]), pv[3] - bf16_hi(ph[h][1]));
-  }
-  if constexpr (GE::I4) {
-    // the sum the 136 offset of V is taken back with: that of the p the
-    // products use (hi + lo parts), which is also the softmax denominator
-    psum = 0.f;
-#pragma unroll
-    for (int h = 0; h < CH; ++h)
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        psum += (bf16_lo(ph[h][e]) + bf16_lo(pl[h][e])) + (bf16_hi(ph[h][e]) + bf16_hi(pl[h][e]));
-  }
-  l_run = l_run * alpha + psum;
-  // V of tokens outside [t_lo, t_end) is zeroed so that unwritten slots and
-  // blocks before a window (any bit pattern) cannot reach the accumulator
-  // through 0 * NaN (wave-uniform branch)
-  if constexpr (GE::I4) {
-    // codes are always finite, and tokens outside [t_lo, t_end) have p = 0
-    const bf16x8 pop = __builtin_bit_cast(bf16x8, u32x4{ph[0][0], ph[0][1], ph[1][0], ph[1][1]});
-    const bf16x8 pop_lo = __builtin_bit_cast(bf16x8, u32x4{pl[0][0], pl[0][1], pl[1][0], pl[1][1]});
-#pragma unroll
-    for (int c = 0; c < GE::NC; ++c) {
-      // word c / 2 of the V piece: pairs (c % 2) and 2 + (c % 2) are tokens
-      // 0, 1 and 2, 3 of the group, dim 16 c + row
-      const uint32_t w0 = r.v[0][0][c >> 1], w1 = r.v[1][0][c >> 1];
-      const bf16x8 aop = __builtin_bit_cast(
-          bf16x8, u32x4{int4_pair(w0, c & 1), int4_pair(w0, 2 + (c & 1)), int4_pair(w1, c & 1), int4_pair(w1, 2 + (c & 1))});
-      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, pop, acc[c], 0, 0, 0);
-      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, pop_lo, acc[c], 0, 0, 0);
-    }
-    return;
-  }
-  u32x4 v[CH][GE::LPC];
 #pragma unroll
   for (int h = 0; h < CH; ++h)
 #pragma unroll
-    for (int u = 0; u < GE::LPC; ++u) v[h][u] = r.v[h][u];
-  if (t0 + GE::TS > t_end || t0 < t_lo) {
+    for (int i = 0; i < 4; ++i) {
+      pv[h][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(z[h][i], qk_scale, -m_ref));
+      psum += pv[h][i];
+    }
+  l_run = l_run * alpha + psum;
+  if constexpr (GE::TOK) {
+    // fold the V scale into p (masked tokens: p = 0 whatever their scale)
 #pragma unroll
     for (int h = 0; h < CH; ++h) {
-      const int tb = t0 + 16 * h + 4 * j;
-      if constexpr (E == 2) {
-        const u32x4 m = u32x4{tok_mask16(tb, t_lo, t_end), tok_mask16(tb + 2, t_lo, t_end),
-                              tok_mask16(tb, t_lo, t_end), tok_mask16(tb + 2, t_lo, t_end)};
 #pragma unroll
-        for (int u = 0; u < GE::LPC; ++u) v[h][u] &= m;
-      } else {
-        const uint32_t m = tok_mask8(tb, t_lo, t_end);
+      for (int i = 0; i < 4; ++i) pv[h][i] *= r.vsc[h][i];
+      if (edge) {
 #pragma unroll
-        for (int u = 0; u < GE::LPC; ++u) v[h][u] &= u32x4{m, m, m, m};
+        for (int i = 0; i < 4; ++i) pv[h][i] = tok_in(t0 + 16 * h + 4 * j + i, t_lo, t_end) ? pv[h][i] : 0.f;
       }
     }
   }
-  if constexpr (CH == 1) {
-    const s16x4 pop = __builtin_bit_cast(s16x4, u32x2{ph[0][0], ph[0][1]});
-    const s16x4 pop_lo = __builtin_bit_cast(s16x4, u32x2{pl[0][0], pl[0][1]});
+  if constexpr (GE::BF) {
+    uint32_t ph[2], pl[2];
+    ph[0] = pack_bf16x2(pv[0][0], pv[0][1]);
+    ph[1] = pack_bf16x2(pv[0][2], pv[0][3]);
+    pl[0] = pack_bf16x2(pv[0][0] - bf16_lo(ph[0]), pv[0][1] - bf16_hi(ph[0]));
+    pl[1] = pack_bf16x2(pv[0][2] - bf16_lo(ph[1]), pv[0][3] - bf16_hi(ph[1]));
+    const s16x4 pop = __builtin_bit_cast(s16x4, u32x2{ph[0], ph[1]});
+    const s16x4 pop_lo = __builtin_bit_cast(s16x4, u32x2{pl[0], pl[1]});
+    u32x4 v[GE::LPC];
+#pragma unroll
+    for (int u = 0; u < GE::LPC; ++u) v[u] = r.v[0][u];
+    if (edge) {
+      const int tb = t0 + 4 * j;
+      const u32x4 m = u32x4{tok_mask16(tb, t_lo, t_end), tok_mask16(tb + 2, t_lo, t_end),
+                            tok_mask16(tb, t_lo, t_end), tok_mask16(tb + 2, t_lo, t_end)};
+#pragma unroll
+      for (int u = 0; u < GE::LPC; ++u) v[u] &= m;
+    }
 #pragma unroll
     for (int c = 0; c < GE::NC; ++c) {
       const int u = c >> 1, e = c & 1;      // load u holds dims (32u + 2row, +1) x 4 tokens
-      const s16x4 aop = __builtin_bit_cast(s16x4, u32x2{v[0][u][2 * e], v[0][u][2 * e + 1]});
+      const s16x4 aop = __builtin_bit_cast(s16x4, u32x2{v[u][2 * e], v[u][2 * e + 1]});
       acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, pop, acc[c], 0, 0, 0);
       acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, pop_lo, acc[c], 0, 0, 0);
     }
   } else {
-    const bf16x8 pop = __builtin_bit_cast(bf16x8, u32x4{ph[0][0], ph[0][1], ph[1][0], ph[1][1]});
-    const bf16x8 pop_lo = __builtin_bit_cast(bf16x8, u32x4{pl[0][0], pl[0][1], pl[1][0], pl[1][1]});
+    const f16x8 pop = __builtin_bit_cast(
+        f16x8, u32x4{pack_f16x2(pv[0][0], pv[0][1]), pack_f16x2(pv[0][2], pv[0][3]), pack_f16x2(pv[1][0], pv[1][1]),
+                     pack_f16x2(pv[1][2], pv[1][3])});
+    // fp8 codes of masked tokens may be inf / NaN patterns: zero them on an
+    // edge step (two copies of the loop, so that other steps carry no mask)
+    auto pv_tiles = [&](auto maskc) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(maskc)::value;
+      uint32_t mk[CH] = {};
+      if constexpr (MASK) {
 #pragma unroll
-    for (int c = 0; c < GE::NC; ++c) {
-      uint32_t a0, a1, a2, a3;
-      const int u = c >> 2, e = c & 3;      // load u holds dims (64u + 4row .. +3) x 4 tokens
-      widen4<KVT>(v[0][u][e], a0, a1);
-      widen4<KVT>(v[1][u][e], a2, a3);
-      const bf16x8 aop = __builtin_bit_cast(bf16x8, u32x4{a0, a1, a2, a3});
-      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, pop, acc[c], 0, 0, 0);
-      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, pop_lo, acc[c], 0, 0, 0);
-    }
+        for (int h = 0; h < CH; ++h) mk[h] = tok_mask8(t0 + 16 * h + 4 * j, t_lo, t_end);
+      }
+#pragma unroll
+      for (int c = 0; c < GE::NC; ++c) {
+        uint32_t a0, a1, a2, a3;
+        if constexpr (GE::I4) {
+          // word c / 2 of the V piece: pairs (c % 2) and 2 + (c % 2) are tokens
+          // 0, 1 and 2, 3 of the group, dim 16 c + row
+          const uint32_t w0 = r.v[0][0][c >> 1], w1 = r.v[1][0][c >> 1];
+          a0 = int4_pair_f16(w0, c & 1);
+          a1 = int4_pair_f16(w0, 2 + (c & 1));
+          a2 = int4_pair_f16(w1, c & 1);
+          a3 = int4_pair_f16(w1, 2 + (c & 1));
+        } else {
+          const int u = c >> 2, e = c & 3;    // load u holds dims (64u + 4row .. +3) x 4 tokens
+          uint32_t w0 = r.v[0][u][e], w1 = r.v[1][u][e];
+          if constexpr (MASK) {
+            w0 &= mk[0];
+            w1 &= mk[1];
+          }
+          v_to_f16<KVT>(w0, a0, a1);
+          v_to_f16<KVT>(w1, a2, a3);
+        }
+        const f16x8 aop = __builtin_bit_cast(f16x8, u32x4{a0, a1, a2, a3});
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, pop, acc[c], 0, 0, 0);
+      }
+    };
+    if (GE::FP8 && edge) pv_tiles(std::true_type{});
+    else pv_tiles(std::false_type{});
   }
 }
 
-// Where the issue side of a wave stands in the flat step list, with the
-// constants of its row (recomputed only when the row changes).
+// Where a walk over the flat step list stands, with the constants of its
+// row (recomputed only when the row changes).
 struct Cursor {
   int s, xi, j;     // sequence, row within the sequence, step within the row
   int n;            // steps of sequence s's rows (from the window's first step)
   int ctx;          // context length of sequence s
   int tb;           // first token of the rows' first step (window start, rounded down)
+  int lo;           // first attended position (window start, or 0)
   int g;            // KV head of the row
   int h0, gt;       // first query head of the row's tile, and its number of heads
-  int x;            // row number s * HQ + xi
-  int phys[4];      // table entries of the step at the cursor (prefetched): one per
-                    // 16-token chunk, two with 8-token blocks
 };
 
-// Row constants of the cursor's row, entered at step j.
+// Row constants of the cursor's row.
 __device__ __forceinline__ void cursor_row(Cursor& c, const SplitParams& p) {
   c.g = p.QT == 1 ? c.xi : c.xi / p.QT;
   const int qt = c.xi - c.g * p.QT;
   c.h0 = c.g * p.G + qt * 16;
   c.gt = min(16, p.G - qt * 16);
-  c.x = c.s * p.HQ + c.xi;
 }
 
-template <int B, int TS>
-__device__ __forceinline__ void cursor_tables(Cursor& c, const SplitParams& p) {
-  const int32_t* row = p.bt + (int64_t)c.s * p.W;
-  constexpr int TB = B < 16 ? B : 16;            // tokens per table entry read
-#pragma unroll
-  for (int h = 0; h < TS / TB; ++h) {
-    int lb = (c.tb + c.j * TS + TB * h) / B;
-    lb = lb < p.W ? lb : p.W - 1;                  // never index past the table row
-    int phys = uniform_load(row + lb);
-    c.phys[h] = phys < 0 ? 0 : (phys >= p.num_blocks ? p.num_blocks - 1 : phys);  // stay inside the pool
+// Move to the first step of the next row that has any (the caller knows
+// there is one: the wave's range reaches it).
+template <int TS, bool kRowConsts = true>
+__device__ __forceinline__ void cursor_next_row(Cursor& c, const SplitParams& p, int max_ctx) {
+  c.j = 0;
+  if (++c.xi == p.HQ) {
+    c.xi = 0;
+    do {
+      ++c.s;
+      c.ctx = clamp_ctx(uniform_load(p.ctx + c.s), max_ctx);
+      c.n = row_steps<TS>(c.ctx, p.win);
+    } while (c.n == 0);
+    c.tb = row_base<TS>(c.ctx, p.win);
+    c.lo = window_lo(c.ctx, p.win);
   }
+  if constexpr (kRowConsts) cursor_row(c, p);
 }
 
 // Partials cross from the waves that write them to the wave that merges them,
 // which may sit on another XCD, whose L2 is not coherent with the writer's.
-// They are therefore stored and loaded as agent-scope relaxed atomics, which
-// go to the coherent level instead of a per-XCD L2; this avoids device-scope
-// fences, which write back or invalidate a whole L2 each time.
-__device__ __forceinline__ void st_agent(float* p, float a, float b) {
-  const unsigned long long v = (unsigned long long)__float_as_uint(a) | ((unsigned long long)__float_as_uint(b) << 32);
-  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ f32x2 ld_agent(const float* p) {
-  const unsigned long long v =
-      __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return f32x2{__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32))};
-}
-
-// The accumulator block of one partial slot (NC * 1 KiB) as a buffer
-// resource, and 16-byte loads / stores of it with the same cache policy
-// (the sc1 scope bit) that an agent-scope atomic access of 8 bytes uses, so
-// they too are coherent across XCDs.  The resource's size bounds every access
-// to the slot.
+// They are therefore stored and loaded with the cache policy of an
+// agent-scope atomic (the sc1 scope bit), which goes to the coherent level
+// instead of a per-XCD L2; this avoids device-scope fences, which write back
+// or invalidate a whole L2 each time.  Every access goes through a buffer
+// resource whose size bounds it to its workspace region.
 constexpr int kCoherentScope = 16;     // raw buffer access aux: sc1
 
+// (m, l) of one (slot, head) in the partial (m, l) region.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ml_rsrc(const SplitParams& p) {
+  return __builtin_amdgcn_make_buffer_rsrc(p.part_ml, (short)0, p.ml_bytes, 0x00020000);
+}
+__device__ __forceinline__ void st_agent2(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(a), __float_as_uint(b)}, r, off, 0, kCoherentScope);
+}
+__device__ __forceinline__ f32x2 ld_agent2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCoherentScope));
+}
+__device__ __forceinline__ uint32_t ml_offset(int slot, int head) { return ((uint32_t)slot * 16u + (uint32_t)head) * 8u; }
+
+// The accumulator block of one partial slot (NC * 1 KiB) as a buffer
+// resource, and 16-byte loads / stores of it.  The resource's size bounds
+// every access to the slot.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(float* acc, int slot, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(acc + (int64_t)slot * (bytes / 4), (short)0, bytes, 0x00020000);
 }
@@ -819,23 +906,31 @@ __device__ __forceinline__ void st_agent4(__amdgpu_buffer_rsrc_t r, int off, f32
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCoherentScope);
 }
 
-// Add `mine` steps to an epoch-tagged row counter; returns the row's total
-// for this epoch after the addition.  Epochs increase from call to call, so
-// raising the counter to (epoch << 32) first turns a counter of an earlier
-// call into a zero count of this one and leaves a counter of this call alone;
-// the add that follows, issued right behind it, takes effect after it (one
-// wave's atomics on one address keep their order).  That costs a single
-// round trip however many waves report at once.  A counter with a larger tag
-// (memory this library never wrote, or epochs that wrapped around) is
-// instead replaced by compare-and-swap; an add that went to such a value is
-// wiped by that replacement and redone by the wave that made it.
-__device__ __forceinline__ int add_steps(uint64_t* ctr, uint32_t epoch, int mine) {
+// Add `mine` steps to an epoch-tagged row counter, in two parts so that the
+// first can be issued well before its result is needed.  One lane of a wave
+// makes the calls: the atomics are per lane, and a wave-wide call would add
+// `mine` once per active lane.  Epochs increase
+// from call to call, so raising the counter to (epoch << 32) first turns a
+// counter of an earlier call into a zero count of this one and leaves a
+// counter of this call alone; the add that follows, issued right behind it,
+// takes effect after it (one wave's atomics on one address keep their
+// order).  That costs a single round trip however many waves report at
+// once.  report_steps issues both and returns the counter's value before the
+// add; report_total gives the row's total for this epoch after the
+// addition.  A counter with a larger tag (memory this library never wrote,
+// or epochs that wrapped around) is instead replaced by compare-and-swap; an
+// add that went to such a value is wiped by that replacement and redone by
+// the wave that made it.
+__device__ __forceinline__ unsigned long long report_steps(uint64_t* ctr, uint32_t epoch, int mine) {
   unsigned long long* c = reinterpret_cast<unsigned long long*>(ctr);
   const unsigned long long tag = (unsigned long long)epoch << 32;
   __hip_atomic_fetch_max(c, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const unsigned long long old =
-      __hip_atomic_fetch_add(c, (unsigned long long)(uint32_t)mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_fetch_add(c, (unsigned long long)(uint32_t)mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int report_total(uint64_t* ctr, uint32_t epoch, int mine, unsigned long long old) {
   if ((uint32_t)(old >> 32) == epoch) return (int)((uint32_t)old + (uint32_t)mine);
+  unsigned long long* c = reinterpret_cast<unsigned long long*>(ctr);
+  const unsigned long long tag = (unsigned long long)epoch << 32;
   unsigned long long expect = old + (uint32_t)mine;
   while (true) {
     const uint32_t base = (uint32_t)(expect >> 32) == epoch ? (uint32_t)expect : 0u;
@@ -912,6 +1007,65 @@ __device__ __forceinline__ void merge_into(float& M, float& L, f32x4 (&A)[NC], f
   M = Mn;
 }
 
+// Normalised output rows of one (sequence, KV head, head tile) row from its
+// merged state: lane (j, row) holds head row of the tile in the accumulator
+// layout AL; L is the softmax denominator of that head.
+template <int D, int AL>
+__device__ __forceinline__ void store_out(const SplitParams& p, int s, int g, int h0, int gt, const f32x4 (&A)[D / 16],
+                                          float L, int lane) {
+  constexpr int NC = D / 16;
+  const int row = lane & 15;
+  const int j = lane >> 4;
+  if (row < gt) {
+    float* orow = p.out + ((int64_t)s * p.Hq + h0 + row) * D;
+    const float inv = p.out_scale / L;
+    const float* vch = p.vs_ch ? p.vs_ch + g * D : nullptr;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int dd = acc_dim<AL>(c, j, i);
+        orow[dd] = vch ? A[c][i] / L * vch[dd] : A[c][i] * inv;
+      }
+  }
+}
+
+// Output rows of a whole-row segment straight from the accumulator (storage
+// without per-channel V scales): 16-byte stores of 4 consecutive dims,
+// through a buffer resource spanning the tile's gt output rows, which drops
+// the stores of lanes whose head lies past them.
+template <int D, int AL>
+__device__ __forceinline__ void store_out_direct(const SplitParams& p, int s, int h0, int gt, const f32x4 (&A)[D / 16],
+                                                 float L, int lane) {
+  static_assert(AL == 1 || AL == 2, "direct output covers the bf16 and 8-bit accumulator layouts");
+  const int row = lane & 15;
+  const int j = lane >> 4;
+  const float inv = p.out_scale / L;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(p.out + ((int64_t)s * p.Hq + h0) * D, (short)0,
+                                                                     gt * D * 4, 0x00020000);
+  const int lo = (row * D + (AL == 2 ? 8 : 16) * j) * 4;
+  if constexpr (AL == 2) {
+    // tiles 2u, 2u + 1 hold dims 32u + 8j + 2i and 32u + 8j + 2i + 1
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u) {
+      const f32x4 a = A[2 * u] * inv, b = A[2 * u + 1] * inv;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{a[0], b[0], a[1], b[1]}), r,
+                                             lo + 128 * u, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{a[2], b[2], a[3], b[3]}), r,
+                                             lo + 128 * u + 16, 0, 0);
+    }
+  } else {
+    // tiles 4u + e hold dims 64u + 16j + 4i + e
+#pragma unroll
+    for (int u = 0; u < D / 64; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4, f32x4{A[4 * u][i], A[4 * u + 1][i], A[4 * u + 2][i], A[4 * u + 3][i]} * inv),
+            r, lo + 256 * u + 16 * i, 0, 0);
+  }
+}
+
 template <int D, int AL>
 __device__ __forceinline__ void merge_row(const SplitParams& p, int x, int s, int xi, int ns, int sx, int N,
                                           int xbv, int lane) {
@@ -929,6 +1083,7 @@ __device__ __forceinline__ void merge_row(const SplitParams& p, int x, int s, in
   const int grp = row / gp;                    // its lane group
   const int src = (j * 16 + hr) * 16;          // byte offset of that head's values in a slot's tile
   const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(p.part_acc, (short)0, p.acc_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t mr = ml_rsrc(p);
   float M = -INFINITY, L = 0.f;
   f32x4 A[NC];
 #pragma unroll
@@ -965,7 +1120,7 @@ __device__ __forceinline__ void merge_row(const SplitParams& p, int x, int s, in
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
           if (nb + k * hs >= cnt) break;         // no lane group has a slot k this round
-          ml[k] = ld_agent(p.part_ml + ((int64_t)slot[k] * 16 + hr) * 2);
+          ml[k] = ld_agent2(mr, ml_offset(slot[k], hr));
           const uint32_t base = (uint32_t)slot[k] * (NC * 1024u) + src;
 #pragma unroll
           for (int c = 0; c < NC; ++c) av[k][c] = ld_agent4(pr, base + c * 1024);
@@ -991,18 +1146,7 @@ __device__ __forceinline__ void merge_row(const SplitParams& p, int x, int s, in
       for (int i = 0; i < 4; ++i) a2[c][i] = __shfl_xor(A[c][i], off, kWave);
     merge_into<NC>(M, L, A, m2, l2, a2);
   }
-  if (row < gt) {
-    float* orow = p.out + ((int64_t)s * p.Hq + h0 + row) * D;
-    const float inv = p.out_scale / L;
-    const float* vch = p.vs_ch ? p.vs_ch + g * D : nullptr;
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int dd = acc_dim<AL>(c, j, i);
-        orow[dd] = vch ? A[c][i] / L * vch[dd] : A[c][i] * inv;
-      }
-  }
+  store_out<D, AL>(p, s, g, h0, gt, A, L, lane);
 }
 
 // Launched with one workgroup (one wave per SIMD) per CU, so the compiler may
@@ -1031,11 +1175,13 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
   constexpr int kSeqRegs = 4;
   int cv[kSeqRegs];          // clamped context length of sequence base + 64k + lane
   auto load_ctx = [&](int base) __attribute__((always_inline)) {
+    // unconditional loads (a lane past the last sequence re-reads it), so
+    // that all of them are in flight before the first is waited for
+    int raw[kSeqRegs];
 #pragma unroll
-    for (int k = 0; k < kSeqRegs; ++k) {
-      const int sq = base + k * kWave + lane;
-      cv[k] = sq < p.S ? clamp_ctx(p.ctx[sq], max_ctx) : 0;
-    }
+    for (int k = 0; k < kSeqRegs; ++k) raw[k] = p.ctx[min(base + k * kWave + lane, p.S - 1)];
+#pragma unroll
+    for (int k = 0; k < kSeqRegs; ++k) cv[k] = base + k * kWave + lane < p.S ? clamp_ctx(raw[k], max_ctx) : 0;
   };
   int total = 0;
   for (int base = 0; base < p.S; base += kSeqRegs * kWave) {
@@ -1099,13 +1245,19 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
   cur.n = __builtin_amdgcn_readfirstlane(cur.n);
   cur.ctx = __builtin_amdgcn_readfirstlane(cur.ctx);
   cur.tb = row_base<TS>(cur.ctx, p.win);
+  cur.lo = window_lo(cur.ctx, p.win);
   cur.xi = __builtin_amdgcn_readfirstlane(cur.xi);
   cur.j = __builtin_amdgcn_readfirstlane(cur.j);
   cum0 = __builtin_amdgcn_readfirstlane(cum0);
   const Cursor first = cur;
 
-  // ---- appending decode: store the new token of every row that ends in this range
-  if (p.new_k) {
+  // ---- appending decode: store the new token of every row that ends in this
+  // range, then wait until the stores have completed, before the load of any
+  // step holding such a token is issued.  When the range's first row ends
+  // past the pipeline's first NBUF - 1 steps (every later row ends later),
+  // those steps' loads are issued first, so the append's own loads, encoding
+  // and stores overlap their memory latency; otherwise the append runs first.
+  auto append_rows = [&]() __attribute__((always_inline)) {
     int as = cur.s, axi = cur.xi, aj = cur.j, an = cur.n, actx = cur.ctx, left = nsteps;
     while (left > 0) {
       const int mine = min(left, an - aj);
@@ -1123,52 +1275,64 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
         } while (an == 0);
       }
     }
-    // the token stores have completed before any load of this wave is issued
     wait_vm_all();
-  }
+  };
+  const bool append_first = p.new_k && cur.n - cur.j - 1 < NBUF - 1;
+  if (append_first) append_rows();
 
   cursor_row(cur, p);
-  cursor_tables<B, TS>(cur, p);
 
+  constexpr int NE = B >= TS ? 1 : TS / B;          // table entries per step
+  const LaneOff<D, KVT, B> lo(lane);
+  // issue side: the cursor of the next step to load, its row's table, and
+  // that step's table entries (fetched one step ahead)
+  Cursor ic = cur;
+  const int32_t* bt_row = p.bt + (int64_t)ic.s * p.W;
+  int ph[NE];
+  auto fetch = [&]() __attribute__((always_inline)) {
+    // logical blocks clamped to those holding attended positions, so a chunk
+    // outside [lo, ctx) never reads a table entry past the context or before
+    // the window (those may name any block)
+    const uint32_t lb0 = (uint32_t)(ic.tb + ic.j * TS) / B;
+    const uint32_t lmin = (uint32_t)ic.lo / B, lmax = (uint32_t)(ic.ctx - 1) / B;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      const uint32_t lb = min(max(lb0 + e, lmin), lmax);
+      const int v = uniform_load(bt_row + lb);
+      ph[e] = v < 0 ? 0 : (v >= p.num_blocks ? p.num_blocks - 1 : v);   // stay inside the pool
+    }
+  };
+  fetch();
+  // compute side: the cursor of the next step to compute
+  Cursor cc = cur;
+
+  using QR = QRegs<GE::KK, GE::NQ>;
   SplitBuf<D, KVT> buf[NBUF];
-  StepMeta meta[NBUF];
-  QRegs<GE::KK> qbuf[NBUF];   // q of a row that starts at the step in the same-index buffer
-  QRegs<GE::KK> qop;          // q of the row being computed
-  int issued = 0;
+  QR qbuf[NBUF];   // q of a row that starts at the step in the same-index buffer
+  QR qop;          // q of the row being computed
+  float qs = 0.f;  // INT4: the sum of qop over the head's dims
+  int issued = 0, consumed = 0;
 
-  // Issue the step at the cursor into buffer r (and, when it starts a row in
-  // this wave, the row's q into qr), then advance the cursor.  Past the end of
-  // the range the K/V loads still happen (see issue_chunks) but nothing is
-  // consumed.  A row's q goes with its first step into the register set of
-  // that step's buffer, so every load is consumed a fixed number of issues
-  // after it was made and the compiler's wait before each compute covers
-  // exactly that step's loads.
-  auto issue = [&](SplitBuf<D, KVT>& r, StepMeta& m, QRegs<GE::KK>& qr) __attribute__((always_inline)) {
-    const bool live = issued < nsteps;
-    const bool new_row = live && (cur.j == 0 || issued == 0);
-    if (new_row) qr = load_q<D, KVT>(p, cur.s, cur.h0, cur.gt, lane);
-    const bool flush = issued + 1 == nsteps || cur.j + 1 == cur.n;
-    m.t0 = cur.tb + cur.j * TS;
-    m.t_end = live ? cur.ctx : 0;
-    m.slot = cur.x + w;
-    m.flags = (new_row ? kNewRow : 0) | (flush ? kFlush : 0) | (cur.gt << 8);
-    issue_chunks<D, KVT, B>(r, p, cur.phys, cur.g, m.t0, window_lo(m.t_end, p.win), m.t_end, lane);
+  // Issue the step at the issue cursor into buffer r (and, when it starts a
+  // row in this wave, the row's q into qr), then advance the cursor and
+  // fetch the next step's table entries.  Past the end of the range the
+  // cursor stays and the loads repeat the last step's (never consumed): every
+  // step issues the same loads, so the compiler's wait before each compute
+  // covers exactly that step's loads and the later ones stay in flight.  A
+  // row's q goes with its first step into the register set of that step's
+  // buffer, so every load is consumed a fixed number of issues after it was
+  // made.
+  auto issue = [&](SplitBuf<D, KVT>& r, QR& qr) __attribute__((always_inline)) {
+    if (issued < nsteps && (ic.j == 0 || issued == 0)) qr = load_q<D, KVT>(p, ic.s, ic.h0, ic.gt, lane);
+    issue_step<D, KVT, B, NE>(r, p, ph, ic.g, ic.tb + ic.j * TS, lo, lane);
     ++issued;
-    if (issued < nsteps) {     // advance to the next step and fetch its table entries
-      if (++cur.j == cur.n) {
-        cur.j = 0;
-        if (++cur.xi == p.HQ) {
-          cur.xi = 0;
-          do {
-            ++cur.s;
-            cur.ctx = clamp_ctx(uniform_load(p.ctx + cur.s), max_ctx);
-            cur.n = row_steps<TS>(cur.ctx, p.win);
-          } while (cur.n == 0);
-          cur.tb = row_base<TS>(cur.ctx, p.win);
-        }
-        cursor_row(cur, p);
+    if (issued < nsteps) {
+      if (++ic.j == ic.n) {
+        const int s0 = ic.s;
+        cursor_next_row<TS>(ic, p, max_ctx);
+        if (ic.s != s0) bt_row = p.bt + (int64_t)ic.s * p.W;
       }
-      cursor_tables<B, TS>(cur, p);
+      fetch();
     }
   };
 
@@ -1178,71 +1342,114 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  auto consume = [&](const SplitBuf<D, KVT>& r, const StepMeta& m, const QRegs<GE::KK>& qr)
-                     __attribute__((always_inline)) {
-    if (m.flags & kNewRow) qop = qr;
-    compute_step<D, KVT>(r, qop, p, m.t0, window_lo(m.t_end, p.win), m.t_end, lane, m_run, l_run, acc);
-    if (m.flags & kFlush) {
+  // Compute the step at the compute cursor from buffer r.  At the end of a
+  // segment (the row's last step, or the range's): a segment that is the
+  // whole row (storage without per-channel V scales) writes the row's output
+  // directly; any other writes its partial.  Only the range's first row can
+  // end inside the range without being whole; when its end leaves NBUF steps
+  // of the range, its partial is reported to the row's counter NBUF steps
+  // later (by then its stores have completed, below), so that the wave is
+  // rarely the one completing that row and the rows it merges when its
+  // range ends are at most its last.
+  constexpr bool kDirect = !GE::CHAN;
+  const int len0 = first.n - first.j;              // steps of the first row in this range (if it ends here)
+  const int whole_from = first.j > 0 ? len0 + 1 : 1;   // consumed count from which a row end closes a whole row
+  const int pend_at = (first.j > 0 && len0 + NBUF <= nsteps) ? len0 + NBUF : -1;
+  unsigned long long pend_old = 0;  // lane 0: the first row's counter before this wave's addition
+  auto consume = [&](const SplitBuf<D, KVT>& r, const QR& qr) __attribute__((always_inline)) {
+    if (cc.j == 0 || consumed == 0) {
+      qop = qr;
+      if constexpr (GE::I4) qs = query_sum<D, KVT>(qop);
+    }
+    const int t0 = cc.tb + cc.j * TS;
+    const bool edge = t0 < cc.lo || t0 + TS > cc.ctx;
+    compute_step<D, KVT>(r, qop, qs, p.qk_scale, t0, cc.lo, cc.ctx, edge, lane, m_run, l_run, acc);
+    ++consumed;
+    if (cc.j + 1 == cc.n || consumed == nsteps) {
       const float l = sum_x32(sum_x16(l_run));
-      if constexpr (GE::I4) {
+      const int g = p.QT == 1 ? cc.xi : cc.xi / p.QT;
+      const int qt = cc.xi - g * p.QT;
+      const int gt = min(16, p.G - qt * 16);
+      if (kDirect && cc.j + 1 == cc.n && consumed >= whole_from) {
+        if constexpr (kDirect) store_out_direct<D, GE::AL>(p, cc.s, g * p.G + qt * 16, gt, acc, l, lane);
+      } else {
+        if (row < gt) {
+          const int slot = cc.s * p.HQ + cc.xi + w;
+          const __amdgpu_buffer_rsrc_t pr = slot_rsrc(p.part_acc, slot, GE::NC * 1024);
 #pragma unroll
-        for (int c = 0; c < GE::NC; ++c) acc[c] -= kInt4Bias * l;   // the V operand held 136 + code
-      }
-      const int gt = m.flags >> 8;
-      if (row < gt) {
-        const __amdgpu_buffer_rsrc_t pr = slot_rsrc(p.part_acc, m.slot, GE::NC * 1024);
-#pragma unroll
-        for (int c = 0; c < GE::NC; ++c) st_agent4(pr, c * 1024 + lane * 16, acc[c]);
-        if (j == 0) st_agent(p.part_ml + ((int64_t)m.slot * 16 + row) * 2, m_run, l);
+          for (int c = 0; c < GE::NC; ++c) st_agent4(pr, c * 1024 + lane * 16, acc[c]);
+          if (j == 0) st_agent2(ml_rsrc(p), ml_offset(slot, row), m_run, l);
+        }
       }
 #pragma unroll
       for (int c = 0; c < GE::NC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
       m_run = -INFINITY;
       l_run = 0.f;
     }
+    if (consumed == pend_at) {
+      // the NBUF steps issued since the partial's stores are all younger than
+      // them, and vector memory operations of a wave complete in issue order:
+      // with at most that many outstanding, the stores have completed
+      vm_wait_at_most<(NBUF * GE::LPS < 63 ? NBUF * GE::LPS : 63)>();
+      __builtin_amdgcn_sched_barrier(0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (lane == 0)
+        pend_old = report_steps(p.row_done + (int64_t)(first.s * p.HQ + first.xi) * kCounterStride, p.epoch, len0);
+    }
+    if (consumed < nsteps && ++cc.j == cc.n) cursor_next_row<TS, false>(cc, p, max_ctx);
   };
 
-  // ---- pipeline: NBUF - 1 steps of loads in flight ahead of the one computed.
-  // Every step issues the same K/V loads (live or not) so the wait before each
-  // compute only covers that step's loads.
+  // ---- pipeline: NBUF - 1 steps of loads in flight ahead of the one computed
   // (the buffer indices must be compile-time constants, or the buffers move
   // to scratch memory: the steps are expanded from an index sequence rather
   // than left to loop unrolling)
   static_for<NBUF - 1>([&](auto bbc) {
     constexpr int bb = decltype(bbc)::value;
-    issue(buf[bb], meta[bb], qbuf[bb]);
+    issue(buf[bb], qbuf[bb]);
   });
+  if (p.new_k && !append_first) append_rows();
   for (int base = 0; base < nsteps; base += NBUF) {
     static_for<NBUF>([&](auto bbc) {
       constexpr int bb = decltype(bbc)::value;
       constexpr int nb = (bb + NBUF - 1) % NBUF;
-      issue(buf[nb], meta[nb], qbuf[nb]);
-      if (base + bb < nsteps) consume(buf[bb], meta[bb], qbuf[bb]);
+      issue(buf[nb], qbuf[nb]);
+      if (base + bb < nsteps) consume(buf[bb], qbuf[bb]);
     });
   }
 
-  // ---- report the rows this range touched; the wave completing a row merges it
+  // ---- report the rows this range wrote partials of; the wave completing a
+  // row merges it.
   // this wave's partial stores have completed (and, being agent-scope, are
   // visible to every XCD) before any counter below is raised
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   wait_vm_all();
   // rows go 64 at a time, one per lane: their counters are raised by
-  // concurrent compare-and-swaps, then the rows this wave completed are merged
+  // concurrent atomics (the first row's by lane 0, possibly inside the loop),
+  // then the rows this wave completed are merged
   int rs = first.s, rxi = first.xi, rn = first.n, rj = first.j, rcum = cum0;
   const int xbv = lane <= 8 ? xcd_begin(N, lane) : 0;     // XCD boundaries of the flat list, for merges
   int left = nsteps;
+  bool first_row = true;
   while (left > 0) {
     int lx = -1, lmine = 0, ln = 0, ls = 0, lxi = 0, lsx = 0;
+    bool lpend = false;
     for (int k = 0; k < kWave && left > 0; ++k) {
       const int mine = min(left, rn - rj);
-      if (lane == k) {
-        lx = rs * p.HQ + rxi;
-        lmine = mine;
-        ln = rn;
-        ls = rs;
-        lxi = rxi;
-        lsx = rcum * p.HQ + rxi * rn;
+      // a whole row written directly has no partial and no counter
+      if (!(kDirect && mine == rn)) {
+        if (lane == k) {
+          lx = rs * p.HQ + rxi;
+          lmine = mine;
+          ln = rn;
+          ls = rs;
+          lxi = rxi;
+          lsx = rcum * p.HQ + rxi * rn;
+          lpend = first_row && pend_at > 0;
+        }
+      } else {
+        --k;     // the lane stays free for the next row
       }
+      first_row = false;
       left -= mine;
       rj = 0;
       if (left > 0 && ++rxi == p.HQ) {
@@ -1255,7 +1462,10 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
       }
     }
     int done_now = 0;
-    if (lx >= 0) done_now = add_steps(p.row_done + (int64_t)lx * kCounterStride, p.epoch, lmine);
+    if (lx >= 0) {
+      uint64_t* ctr = p.row_done + (int64_t)lx * kCounterStride;
+      done_now = report_total(ctr, p.epoch, lmine, lpend ? pend_old : report_steps(ctr, p.epoch, lmine));
+    }
     uint64_t complete = __ballot(lx >= 0 && done_now == ln);   // every partial of the row is in place
     while (complete) {
       const int l = __builtin_ctzll(complete);
@@ -1279,11 +1489,34 @@ hipError_t launch_single(const DecodeParams& p, int D, int kvt, int B, int grid,
 // Steps of K/V registers per wave: one computed, the rest in flight (about
 // 40 KB per wave, 160 KB per CU with one wave per SIMD).
 template <int D, int KVT>
-constexpr int split_nbuf() { return KVT == PKV_KV_INT4 ? 8 : (D == 64 ? 8 : 5); }
+constexpr int split_nbuf() { return D == 64 ? 8 : (KVT == PKV_KV_INT4 ? 6 : 5); }
+
+// f(IC<D>, IC<KVT>, IC<B>) for the split kernel's variants: every storage
+// type has its own (per-channel INT8 folds its K scales into the query as hi
+// + lo parts, which the per-tensor codes kernel does not read).
+template <class F>
+auto with_split_variant(int D, int kvt, int B, F&& f) {
+  auto by_b = [&](auto dc, auto kc) {
+    if (B == 8) return f(dc, kc, IC<8>{});
+    if (B == 16) return f(dc, kc, IC<16>{});
+    return f(dc, kc, IC<32>{});
+  };
+  auto by_kv = [&](auto dc) {
+    switch (kvt) {
+      case PKV_KV_BF16: return by_b(dc, IC<PKV_KV_BF16>{});
+      case PKV_KV_FP8_E5M2: return by_b(dc, IC<PKV_KV_FP8_E5M2>{});
+      case PKV_KV_INT8_TENSOR: return by_b(dc, IC<PKV_KV_INT8_TENSOR>{});
+      case PKV_KV_INT8_CHANNEL: return by_b(dc, IC<PKV_KV_INT8_CHANNEL>{});
+      case PKV_KV_INT4: return by_b(dc, IC<PKV_KV_INT4>{});
+      default: return by_b(dc, IC<PKV_KV_INT8>{});
+    }
+  };
+  return D == 64 ? by_kv(IC<64>{}) : by_kv(IC<128>{});
+}
 constexpr int kMaxBlocksPerCU = 1;       // persistent grid: one workgroup (a wave per SIMD) per CU
 
 const void* split_kernel_fn(int D, int kvt, int B) {
-  return with_variant<true>(D, kvt, B, [](auto dc, auto kc, auto bc) {
+  return with_split_variant(D, kvt, B, [](auto dc, auto kc, auto bc) {
     constexpr int Dv = decltype(dc)::value, Kv = decltype(kc)::value, Bv = decltype(bc)::value;
     return reinterpret_cast<const void*>(&pa_split_kernel<Dv, Kv, Bv, split_nbuf<Dv, Kv>()>);
   });
@@ -1392,7 +1625,7 @@ bool split_sizes(int32_t S, int32_t Hq, int32_t rows_or_0, int32_t D, int32_t W,
 }
 
 void launch_split(const SplitParams& p, int D, int kvt, int B, int grid, hipStream_t stream) {
-  with_variant<true>(D, kvt, B, [&](auto dc, auto kc, auto bc) {
+  with_split_variant(D, kvt, B, [&](auto dc, auto kc, auto bc) {
     constexpr int Dv = decltype(dc)::value, Kv = decltype(kc)::value, Bv = decltype(bc)::value;
     hipLaunchKernelGGL((pa_split_kernel<Dv, Kv, Bv, split_nbuf<Dv, Kv>()>), dim3(grid), dim3(kWave * kNW), 0, stream,
                        p);
@@ -1607,6 +1840,7 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     p.part_ml = reinterpret_cast<float*>(ws + z.cnt_bytes);
     p.part_acc = reinterpret_cast<float*>(ws + z.cnt_bytes + z.ml_bytes);
     p.acc_bytes = (uint32_t)z.acc_bytes;
+    p.ml_bytes = (uint32_t)z.ml_bytes;
     p.W = table_width;
     p.S = num_seqs;
     p.Hq = num_q_heads;
