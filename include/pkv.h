@@ -225,17 +225,25 @@ uint64_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
  *   out[s][h] = softmax(scale * q[s][h] . K_s^T) V_s
  * over the ctx_s cached tokens of KV head h / G, gathered through the block
  * table ([BJD] §2.1 for the formula; [KVP] §三 工作方式 step 4 for the gather;
- * [KVP] §一 for the GQA grouping).  8-bit K/V are widened exactly to bf16 and
- * their scales applied in fp32 before they meet q or p ([KVP] §四: dequantise
- * before compute).  ctx_s == 0 gives a zero row.  Arithmetic: bf16 inputs,
- * fp32 accumulation and softmax.  A stored inf or NaN in V gives a
- * non-finite output element (inf may surface as NaN).
+ * [KVP] §一 for the GQA grouping).  Stored 8-bit and 4-bit codes are
+ * converted exactly and their scales applied in fp32 ([KVP] §四: dequantise
+ * before compute): per-tensor and per-(token, head) K scales multiply the
+ * logits, per-channel K scales are folded into the query (q' = q * s_k held
+ * as two bf16 parts, hi and lo, ~16 significant bits), V scales multiply p
+ * (per token) or the output (per tensor, per channel).  ctx_s == 0 gives a
+ * zero row.  Arithmetic: bf16 q, fp32 accumulation and softmax; p meets V as
+ * two bf16 parts (~16 bits of p) for bf16 storage and in the single-pass
+ * form, while the split form meets 8-bit and 4-bit codes (converted exactly
+ * to fp16) with p rounded to one fp16 (<= 2^-11 relative).  A stored inf or
+ * NaN in V gives a non-finite output element (inf may surface as NaN).
  *   out           device fp32 [S][Hq][D]
  *   q             device bf16 [S][Hq][D]
  *   block_tables  device int32 [S][table_width]
  *   context_lens  device int32 [S], each <= table_width * B
  *   kv_dtype      must equal pool->cfg.kv_dtype
- *   kv_scales     host; fp8 per-tensor scales (NULL = 1.0)
+ *   kv_scales     host; the per-tensor scales of fp8 and INT8-per-tensor
+ *                 storage (NULL = 1.0), positive and finite; not read for
+ *                 other storage types
  *   partition_size 0: single pass, one workgroup per (sequence, KV head), no
  *                 workspace (INT4: one query per sequence through the
  *                 paged_attn_prefill kernel).  Otherwise the split-context form, a positive
@@ -271,8 +279,14 @@ pkv_status paged_attn_decode(float* out, const void* q, const pkv_pool* pool, in
  * cached prompt prefix is reused and only the rest is computed ([BJD] §4.1;
  * [KVP] §五); a whole prompt is the case n_s = ctx_s, a decode step the case
  * n_s = 1.  Every storage type of the pool, with the arithmetic of
- * paged_attn_decode (INT4 and per-channel INT8: the K channel scales are
- * folded into the query first).
+ * paged_attn_decode's single-pass form (INT4 and per-channel INT8: the K
+ * channel scales are folded into the query first), except that INT8 per
+ * (token, head) and per tensor take q.K in fp16: the codes as 1152 + c
+ * (exact) and the query as fp16(q * 2^-8), exact for 2^-6 <= |q| <= 2^23
+ * (smaller elements keep an absolute precision of 2^-17; the shift trades
+ * those for queries up to 2^23 that fp16 could not hold unshifted), and INT8
+ * per tensor and per channel take P.V in fp16, the codes as 1152 + c and p
+ * as two fp16 parts.
  *   out           device fp32 [T][Hq][D], T = num_queries = query_start[S]
  *   q             device bf16 [T][Hq][D]
  *   query_start   device int32 [S + 1], non-decreasing, query_start[0] = 0

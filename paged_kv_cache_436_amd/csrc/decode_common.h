@@ -278,7 +278,7 @@ __device__ __forceinline__ void issue_step(StepRegs<D, KVT>& r, const DecodePara
 // carries ~16 significant bits of q'), over the output row out[s][h], which
 // only that row's final store writes, after every read of q': hi in the first
 // D bf16 slots of the row, lo in the next D (row stride 2 D bf16 elements).
-// Kernels that take one bf16 query operand read hi only.
+// The kernels multiply both parts with the same K operand.
 __global__ __launch_bounds__(256) void fold_q_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ qf,
                                                      const float* __restrict__ ks_ch, int64_t n, int32_t Hq,
                                                      int32_t G, int32_t D) {
@@ -299,9 +299,10 @@ template <int V>
 using IC = std::integral_constant<int, V>;
 
 // f(IC<D>, IC<KVT>, IC<B>) for the kernel variant of head dim D (64, 128),
-// storage kv_dtype and block size B (8, 16, 32).  INT8 with per-tensor or
-// per-channel scales runs the per-tensor codes kernel (the channel scales are
-// folded into q and into the output).
+// storage kv_dtype and block size B (8, 16, 32).  INT8 with per-channel
+// scales has its own variant: plain codes whose K channel scales are folded
+// into the query (read as its bf16 hi and lo parts) and whose V channel
+// scales are applied to the output.
 template <bool kInt4, class F>
 auto with_variant(int D, int kvt, int B, F&& f) {
   auto by_b = [&](auto dc, auto kc) {
@@ -313,8 +314,8 @@ auto with_variant(int D, int kvt, int B, F&& f) {
     switch (kvt) {
       case PKV_KV_BF16: return by_b(dc, IC<PKV_KV_BF16>{});
       case PKV_KV_FP8_E5M2: return by_b(dc, IC<PKV_KV_FP8_E5M2>{});
-      case PKV_KV_INT8_TENSOR:
-      case PKV_KV_INT8_CHANNEL: return by_b(dc, IC<PKV_KV_INT8_TENSOR>{});
+      case PKV_KV_INT8_TENSOR: return by_b(dc, IC<PKV_KV_INT8_TENSOR>{});
+      case PKV_KV_INT8_CHANNEL: return by_b(dc, IC<PKV_KV_INT8_CHANNEL>{});
       case PKV_KV_INT4:
         if constexpr (kInt4) return by_b(dc, IC<PKV_KV_INT4>{});
         [[fallthrough]];

@@ -80,17 +80,22 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
   const int t_lo = window_lo(t_end, p.win);
   const int32_t* bt_row = p.bt + (int64_t)s * p.W;
 
-  // query tile as the B operand of q.K: lane (j, row) holds head row
-  bf16x8 qop[T::KK];
+  // query tile as the B operand of q.K: lane (j, row) holds head row; with
+  // the K channel scales folded in, set 0 is the bf16 hi part of the folded
+  // query and set 1 its lo part (the next D elements of the row)
+  constexpr int NQ = KVT == PKV_KV_INT8_CHANNEL ? 2 : 1;
+  bf16x8 qop[NQ][T::KK];
   {
     const bool valid = row < gt;
     const uint16_t* qh = p.q + ((int64_t)s * p.Hq + h0 + (valid ? row : 0)) * p.q_stride;
 #pragma unroll
-    for (int kk = 0; kk < T::KK; ++kk) {
-      u32x4 raw = *reinterpret_cast<const u32x4*>(qh + q_dim0<E>(kk, j));
-      if (!valid) raw = u32x4{0, 0, 0, 0};
-      qop[kk] = __builtin_bit_cast(bf16x8, raw);
-    }
+    for (int n = 0; n < NQ; ++n)
+#pragma unroll
+      for (int kk = 0; kk < T::KK; ++kk) {
+        u32x4 raw = *reinterpret_cast<const u32x4*>(qh + n * D + q_dim0<E>(kk, j));
+        if (!valid) raw = u32x4{0, 0, 0, 0};
+        qop[n][kk] = __builtin_bit_cast(bf16x8, raw);
+      }
   }
 
   f32x4 acc[T::NC];
@@ -114,7 +119,8 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
           const u32x4 wv = r.k[h][kk >> 1];
           a = (kk & 1) ? widen8<KVT>(wv[2], wv[3]) : widen8<KVT>(wv[0], wv[1]);
         }
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[kk], c, 0, 0, 0);
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[n][kk], c, 0, 0, 0);
       }
       z[h] = c;
     }

@@ -174,11 +174,14 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
   // after the products; the query dims follow the bf16 slot layout and the
   // accumulator dims that of the INT4 V pieces
   constexpr bool I4 = KVT == PKV_KV_INT4;
-  // INT8 codes through fp16 (1152 + code) in q.K, and in P.V too where the
-  // V scale is per tensor or per channel (p <= 2^8 then; per-token V scales
-  // are folded into p, whose range fp16 could not hold, so that V stays bf16)
+  // INT8 codes through fp16 (1152 + code) in q.K where the query is plain
+  // (per-token and per-tensor scales; the per-channel folded query takes the
+  // exact bf16 route with its hi and lo parts, whose magnitudes the fixed
+  // fp16 shift could not hold), and in P.V where the V scale is per tensor or
+  // per channel (p <= 2^8 then; per-token V scales are folded into p, whose
+  // range fp16 could not hold, so that V stays bf16)
   constexpr bool I8K = KVT == PKV_KV_INT8 || KVT == PKV_KV_INT8_TENSOR;
-  constexpr bool I8V = KVT == PKV_KV_INT8_TENSOR;
+  constexpr bool I8V = KVT == PKV_KV_INT8_TENSOR || KVT == PKV_KV_INT8_CHANNEL;
   const float qks = I8K ? p.qk_scale * (1.0f / kInt8QShift) : p.qk_scale;   // the softmax scale of z
   constexpr int QL = I4 ? 2 : E;
   constexpr int AL = I4 ? 0 : E;
@@ -218,8 +221,12 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
   const int32_t* bt_row = p.bt + (int64_t)s * p.W;
 
   // per tile: this lane's column limit (keys [0, lim)) and the query as the
-  // B operand (columns past the chunk read column c0's query, limit 0)
-  bf16x8 qop[NT][T::KK];
+  // B operand (columns past the chunk read column c0's query, limit 0); with
+  // the K channel scales folded in (int8 per channel, INT4), set 0 is the
+  // bf16 hi part of the folded query and set 1 its lo part (the next D
+  // elements of the row), both multiplying the same K operand
+  constexpr int NQ = (KVT == PKV_KV_INT8_CHANNEL || I4) ? 2 : 1;
+  bf16x8 qop[NT][NQ][T::KK];
   float qsum[NT];   // INT4: the column's sum of q over all dims
   int lim[NT];
 #pragma unroll
@@ -230,29 +237,34 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
     lim[nt] = valid ? max(0, first + c / p.G + 1) : 0;
     const uint16_t* qh = p.q + ((int64_t)(q0 + c / p.G) * p.Hq + g * p.G + c % p.G) * p.q_stride;
 #pragma unroll
-    for (int kk = 0; kk < T::KK; ++kk)
-      qop[nt][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + q_dim0<QL>(kk, j)));
+    for (int n = 0; n < NQ; ++n)
+#pragma unroll
+      for (int kk = 0; kk < T::KK; ++kk)
+        qop[nt][n][kk] =
+            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + n * D + q_dim0<QL>(kk, j)));
     qsum[nt] = 0.f;
     if constexpr (I4) {
       float a = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < T::KK; ++kk)
+      for (int n = 0; n < NQ; ++n)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a += (float)qop[nt][kk][e];
+        for (int kk = 0; kk < T::KK; ++kk)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a += (float)qop[nt][n][kk][e];
       qsum[nt] = sum_x32(sum_x16(a));   // lanes of one column hold its 4 dim slots
     } else if constexpr (I8K) {
       // the fp16 operand, and the sum of exactly the values it holds
       float a = 0.f;
 #pragma unroll
       for (int kk = 0; kk < T::KK; ++kk) {
-        const u32x4 wq = __builtin_bit_cast(u32x4, qop[nt][kk]);
+        const u32x4 wq = __builtin_bit_cast(u32x4, qop[nt][0][kk]);
         u32x4 hq;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           hq[e] = pack_f16x2(bf16_lo(wq[e]) * kInt8QShift, bf16_hi(wq[e]) * kInt8QShift);
           a += f16_lo(hq[e]) + f16_hi(hq[e]);
         }
-        qop[nt][kk] = __builtin_bit_cast(bf16x8, hq);
+        qop[nt][0][kk] = __builtin_bit_cast(bf16x8, hq);
       }
       qsum[nt] = sum_x32(sum_x16(a));
     }
@@ -298,11 +310,14 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
         f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < T::KK; ++kk) {
-          if constexpr (I8K)
+          if constexpr (I8K) {
             c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ka[h][kk]),
-                                                       __builtin_bit_cast(f16x8, qop[nt][kk]), c, 0, 0, 0);
-          else
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[h][kk], qop[nt][kk], c, 0, 0, 0);
+                                                       __builtin_bit_cast(f16x8, qop[nt][0][kk]), c, 0, 0, 0);
+          } else {
+#pragma unroll
+            for (int n = 0; n < NQ; ++n)
+              c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[h][kk], qop[nt][n][kk], c, 0, 0, 0);
+          }
         }
         if constexpr (I4) c -= kInt4Bias * qsum[nt];    // the K operand held 136 + code
         if constexpr (I8K) c -= kInt8Bias * qsum[nt];   // the K operand held 1152 + code

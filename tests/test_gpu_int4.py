@@ -18,7 +18,7 @@ from tests.helpers import expanded_slots
 
 pytestmark = pytest.mark.gpu
 
-BAR = (2e-2, 5e-3)
+BAR = (2e-2, 1e-3)     # the split form meets the codes with p as one fp16 (rounding <= 2^-11 relative)
 DT = pkv.PKV_KV_INT4
 
 

@@ -17,7 +17,7 @@ from tests.helpers import expanded_slots
 pytestmark = pytest.mark.gpu
 
 KS, VS = 0.035, 0.03            # per-tensor scales (|x| up to ~4.4 and ~3.8 before saturation)
-BAR = (2e-2, 5e-3)
+BAR = (2e-2, 1e-3)     # the split form meets the codes with p as one fp16 (rounding <= 2^-11 relative)
 
 
 class Case:
