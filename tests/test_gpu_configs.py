@@ -2,11 +2,15 @@
 configuration the benchmark times, against the fp64 oracle.
 
 * 8B-shaped layer step: 64 sequences of 512..4096 tokens, 32 query / 8 KV
-  heads; every output element is checked, and the whole pool bit for bit.
-* 70B-shaped step: 100 sequences of ~4K tokens, 64 / 8 heads, two layers of
-  the 80-layer pool shape; the pool is filled by torch's generator, the step
-  writes each sequence's new token and decodes; a sample of sequences is
-  checked against the oracle, which reads their blocks as torch filled them.
+  heads, planted needle keys in every other sequence; every output element
+  is checked, and the whole pool bit for bit.
+* 70B-shaped step: 100 sequences of ~4K tokens, 64 / 8 heads.  A two-layer
+  pool of the per-layer shape: the pool is filled by torch's generator, the
+  step writes each sequence's new token and decodes; a sample of sequences
+  is checked against the oracle, which reads their blocks as torch filled
+  them.  The full 80-layer pool: the appending decode (the timed form) at
+  layers 0, 39 and 79, every element of all 100 sequences, with needles,
+  and each written layer bit for bit.
 * Shared-prefix copy-on-write: 200 sequences fork one 1500-token prefix and
   generate 64..512 tokens each; every step appends through the block manager,
   copies shared blocks, writes the new token and decodes.  Outputs are
@@ -69,6 +73,13 @@ def test_llama8b_layer_step():
     hist_tab, hist_ctx = bm.block_tables(range(S), W)
     n_hist = int(hist_ctx.sum())
     k_hist, v_hist = workloads.token_kv(w, n_hist)
+    # planted needle keys in the even sequences' histories: a wrong block or
+    # position there moves outputs by O(1); the odd ones keep flat softmaxes
+    q = workloads.queries(w)
+    owner = np.repeat(np.arange(S), hist_ctx)
+    owner[owner % 2 == 1] = -1
+    pos = np.concatenate([np.arange(int(n)) for n in hist_ctx])
+    k_hist = workloads.plant_needles(w, q, k_hist, owner, pos, per_seq=8)
     slots_hist = np.concatenate([expanded_slots(hist_tab[s], int(hist_ctx[s]), B) for s in range(S)])
     cfg = pkv.make_config(1, w.num_blocks, B, Hkv, D)
     pool = pkv.Pool(cfg)
@@ -89,12 +100,14 @@ def test_llama8b_layer_step():
     got_img = read_pool(pool)
     assert images_equal(got_img, img), first_diff(got_img, img)
     del got_img
-    q = workloads.queries(w)
     want = attention.paged_decode(q, img, 0, tab, ctx, w.scale)
+    even, odd = np.arange(0, S, 2), np.arange(1, S, 2)
+    assert np.min(np.max(np.abs(want[even]), axis=(1, 2))) > 0.5    # the needles dominate
     for P in (0, 512, (W * B + 31) // 32 * 32):
         say(f"8B: decode P={P}")
         got = _decode(pool, q, tab, ctx, w.scale, P, Hq)
-        _bars(got, want, 1e-2, 1e-3, f"8B layer P={P}")
+        _bars(got[even], want[even], 1e-2, 1e-3, f"8B layer P={P}, needles")
+        _bars(got[odd], want[odd], 1e-2, 1e-3, f"8B layer P={P}, flat")
 
 
 # ----------------------------------------------------------------------- 70B step
@@ -163,6 +176,105 @@ def test_llama70b_step_sampled():
             assert images_equal(after, subs[s]), f"layer {layer} seq {s}: " + first_diff(after, subs[s])
             want = attention.paged_decode(q[s:s + 1], subs[s], 0, np.arange(nblk)[None, :], ctx[s:s + 1], w.scale)
             _bars(got[s:s + 1], want, 1e-2, 1e-3, f"70B layer {layer} seq {s} ctx {ctx[s]}")
+
+
+def _layer_image(pool, layer):
+    """One layer of a bf16 pool, read from the device into a one-layer image
+    (block numbers unchanged)."""
+    c = pool.cfg
+    img = layout.empty_image(layout.PoolShape(1, c.num_blocks, c.block_size, c.num_kv_heads, c.head_dim))
+    k_off, v_off, _, _ = pool.region_offsets()
+    lb = pool.desc.layer_bytes
+    for off, dst in ((k_off, img.k), (v_off, img.v)):
+        dst[:] = pool.memory[off + layer * lb: off + (layer + 1) * lb].cpu().numpy().view(np.uint16)
+    return img
+
+
+def _needle(q_bits, s, head, D):
+    """K of a planted needle: 4 sqrt(D) q / |q| of query head `head` (bf16 bits)."""
+    qh = (q_bits[s, head].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    nv = qh / max(np.linalg.norm(qh), 1e-6) * 4.0 * math.sqrt(D)
+    return workloads.to_bf16_bits(nv.astype(np.float32))
+
+
+def test_llama70b_append_full_pool_all_sequences():
+    """The timed form, paged_attn_decode_append (the new token's cache write in
+    the decode launch), on the full 80-layer 70B-shaped pool at layers 0, 39
+    and 79 (layer 79's V region lies past 100 GiB), every element of all 100
+    sequences against the oracle.  Every other sequence has planted needle
+    keys in its history, and every fourth one (from s = 1) a needle as its
+    new key, so a wrong block or a missed append moves outputs by O(1).  The
+    layers not written hold NaN bit patterns, so a read of the wrong layer
+    shows too."""
+    import torch
+    say("70B full pool append: setup")
+    w = workloads.llama70b(num_layers=80, extra_steps=1)
+    S, Hq, Hkv, D, B, W, G = (w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                              w.table_width, w.group)
+    cfg = pkv.make_config(80, w.num_blocks, B, Hkv, D)
+    pool = pkv.Pool(cfg)
+    pool.memory.fill_(255)
+    k_off, v_off, _, _ = pool.region_offsets()
+    lb = pool.desc.layer_bytes
+    say(f"70B full pool: {pool.memory.numel() / 2**30:.1f} GiB, layer bytes {lb}")
+    bm = pkv.BlockManager(w.num_blocks, B, w.block_order)
+    for s in range(S):
+        bm.add_seq(s, int(w.context_lens[s]) - 1)
+    slots, pairs = bm.append(range(S))
+    assert pairs.shape[0] == 0
+    tab, ctx = bm.block_tables(range(S), W)
+    P = (W * B + 31) // 32 * 32                     # the benchmark's launch configuration
+    ws = torch.empty(pkv.paged_attn_workspace_bytes(S, Hq, D, W, B, P), dtype=torch.uint8, device="cuda")
+    needles = np.arange(0, S, 2)
+    tail_needles = np.arange(1, S, 4)
+    flat = np.setdiff1d(np.arange(S), np.concatenate([needles, tail_needles]))
+    shape = layout.PoolShape(1, w.num_blocks, B, Hkv, D)
+    for layer in (0, 39, 79):
+        say(f"70B full pool layer {layer}: fill")
+        g = torch.Generator(device="cuda")
+        g.manual_seed(436003 * 1000 + layer)
+        for off in (k_off, v_off):
+            pool.memory[off + layer * lb: off + (layer + 1) * lb].view(torch.bfloat16).normal_(generator=g)
+        r = np.random.default_rng(436079 + layer)
+        q = workloads.normal_bf16(r, (S, Hq, D))
+        k_new = workloads.normal_bf16(r, (S, Hkv, D))
+        v_new = workloads.normal_bf16(r, (S, Hkv, D))
+        img = _layer_image(pool, layer)
+        # needles in the history (K of 8 positions per KV head) and as new keys
+        for s in needles:
+            pos = r.choice(int(ctx[s]) - 1, size=8, replace=False)
+            blk, t = tab[s, pos // B], pos % B
+            for h in range(Hkv):
+                offs = layout.k_offset(shape, 0, blk[:, None], h, t[:, None], np.arange(D)[None, :])
+                img.k[offs] = _needle(q, s, h * G, D)[None, :]
+        for s in tail_needles:
+            for h in range(Hkv):
+                k_new[s, h] = _needle(q, s, h * G, D)
+        pool.memory[k_off + layer * lb: k_off + (layer + 1) * lb].copy_(torch.from_numpy(img.k.view(np.uint8)))
+        want_img = cache_ops.reshape_and_cache(img, 0, k_new, v_new, slots)
+        del img
+        say(f"70B full pool layer {layer}: decode_append P={P}")
+        out = torch.full((S, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+        pkv.paged_attn_decode_append(out, bf16_dev(q), pool, layer, bf16_dev(k_new), bf16_dev(v_new), dev(tab),
+                                     dev(ctx), w.scale, partition_size=P, workspace=ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        after = _layer_image(pool, layer)
+        assert images_equal(after, want_img), f"layer {layer}: " + first_diff(after, want_img)
+        del after
+        say(f"70B full pool layer {layer}: oracle")
+        want = attention.paged_decode(q, want_img, 0, tab, ctx, w.scale)
+        del want_img
+        assert np.min(np.max(np.abs(want[needles]), axis=(1, 2))) > 0.5    # the needles dominate
+        assert np.min(np.max(np.abs(want[tail_needles]), axis=(1, 2))) > 0.5
+        for name, sel in (("flat", flat), ("history needles", needles), ("new-key needles", tail_needles)):
+            _bars(got[sel], want[sel], 1e-2, 1e-3, f"70B full pool layer {layer}, {name} ({sel.size} seqs)")
+    # the layers never written still hold the fill: nothing wrote past its layer
+    for layer in (1, 38, 40, 78):
+        for off in (k_off, v_off):
+            assert bool((pool.memory[off + layer * lb: off + (layer + 1) * lb] == 255).all()), layer
+    del pool, ws
+    torch.cuda.empty_cache()
 
 
 # ----------------------------------------------------------------------- shared-prefix COW
