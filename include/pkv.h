@@ -33,8 +33,10 @@
  *   starting at a multiple of 256 bytes from the base, in this order:
  *     K        [L][NB][H][tile]      tile = B*D elements
  *     V        [L][NB][H][tile]
- *     K scales [L][NB][H][B] float   (int8 storage only)
- *     V scales [L][NB][H][B] float   (int8 storage only)
+ *     K scales [L][NB][H][B] float   (PKV_KV_INT8: per token and head)
+ *              [L][H][D] float       (PKV_KV_INT8_CHANNEL, PKV_KV_INT4)
+ *     V scales as the K scales
+ *   Other storage types have no scale regions.
  *   Inside a K tile, element (token t, dim d) is at
  *       ((d / X) * B + t) * X + d % X
  *   i.e. the tile is D/X runs of B 16-byte pieces: the 16 bytes of dims
@@ -133,14 +135,17 @@ typedef struct {
   uint64_t layer_bytes;   /* NB * H * tile_bytes: one layer of K (or of V)   */
 } pkv_pool;
 
-/* fp8 per-tensor scales: stored = value / scale, value = stored * scale.
- * Ignored for bf16 and int8 storage.  NULL means 1.0 and 1.0. */
+/* Per-tensor scales of PKV_KV_FP8_E5M2 and PKV_KV_INT8_TENSOR storage:
+ * stored = value / scale, value = stored * scale ([KVP] §四: FP8 / INT8 KV
+ * with a scale).  Not read for other storage types.  NULL means 1.0 and
+ * 1.0. */
 typedef struct {
   float k_scale;
   float v_scale;
 } pkv_kv_scales;
 
-/* Thread-local message for the last failed call on this thread ("" if none). */
+/* Thread-local message for the last failed call on this thread ("" if none).
+ * Error reporting is this library's own; the pages say nothing about it. */
 const char* pkv_last_error(void);
 
 /* ------------------------------------------------------------- pool sizing */
@@ -158,7 +163,9 @@ uint64_t kv_pool_bytes(const pkv_pool_config* cfg);
 int64_t kv_pool_num_blocks_for_budget(const pkv_pool_config* cfg, uint64_t budget_bytes);
 
 /* Describe a pool living in dev_mem (device, >= kv_pool_bytes(cfg) bytes,
- * 256-byte aligned).  Host only: records pointers, touches no memory. */
+ * 256-byte aligned): the preallocated pool of fixed-size physical blocks
+ * ([AWA] KV Memory Pool; [KVP] §三 工作方式 steps 1-3).  Host only: records
+ * pointers, touches no memory. */
 pkv_status kv_pool_create(const pkv_pool_config* cfg, void* dev_mem, uint64_t bytes,
                           pkv_pool* out);
 
@@ -216,7 +223,9 @@ pkv_status swap_blocks(const pkv_pool* from, const pkv_pool* to, const int64_t* 
 /* Workspace bytes paged_attn_decode needs for these sizes on the current
  * device (0 when partition_size is 0: the single-pass form needs none).  The
  * split form's grid is sized to the device's compute units, so a workspace
- * sized on one device model may not fit another. */
+ * sized on one device model may not fit another.  The pages are silent on
+ * splitting a context across workgroups; this scratch (partial softmax
+ * states and row counters) is the library's own. */
 uint64_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                     int32_t table_width, int32_t block_size,
                                     int32_t partition_size);
@@ -383,7 +392,15 @@ pkv_status paged_attn_decode_noalloc(const pkv_decode_args* args, hipStream_t st
 /* ------------------------------------------------------------- host checks
  * Validators over HOST copies of device inputs, for callers that want to
  * rule out racing or out-of-range values before a launch.  Return PKV_OK or
- * PKV_ERR_INVALID with a message naming the first bad entry. */
+ * PKV_ERR_INVALID with a message naming the first bad entry.  The pages say
+ * nothing about validation; what is checked follows from the layout above:
+ *   pkv_check_slots   every slot in [0, num_slots) or negative (padding),
+ *                     no slot twice;
+ *   pkv_check_pairs   src and dst in [0, num_blocks), no dst twice, no dst
+ *                     that is also a src;
+ *   pkv_check_tables  each context length in [0, table_width * block_size]
+ *                     and the first ceil(ctx / B) entries of its row in
+ *                     [0, num_blocks). */
 pkv_status pkv_check_slots(const int64_t* slots, int32_t n, int64_t num_slots);
 pkv_status pkv_check_pairs(const int64_t* pairs, int32_t n, int32_t num_blocks);
 pkv_status pkv_check_tables(const int32_t* tables, const int32_t* context_lens, int32_t num_seqs,
@@ -408,26 +425,42 @@ pkv_status pkv_check_tables(const int32_t* tables, const int32_t* context_lens, 
  * Not thread-safe: one manager per thread, or external locking. */
 typedef struct pkv_bm pkv_bm;
 
+/* A manager of num_blocks blocks of block_size tokens, all free, in the
+ * given FIFO order ([AWA] KV Memory Pool: fixed-size blocks preallocated and
+ * handed to sequences on demand).  *out receives it; free with
+ * kv_bm_destroy (host memory only; the pages are silent on teardown). */
 pkv_status kv_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_order,
                         pkv_bm** out);
 void kv_bm_destroy(pkv_bm* bm);
-/* New sequence holding ctx_len tokens (ceil(ctx_len / B) fresh blocks). */
+/* New sequence holding ctx_len tokens (ceil(ctx_len / B) fresh blocks; [KVP]
+ * §三 工作方式 step 2: its block table maps logical block i to physical
+ * block p). */
 pkv_status kv_bm_add_seq(pkv_bm* bm, int32_t seq, int32_t ctx_len);
-/* child shares all of parent's blocks (counts + 1) and its length. */
+/* child shares all of parent's blocks (counts + 1) and its length ([BJD]
+ * §3.1: two requests with the same prefix point their tables at the same
+ * physical blocks; §3.2: the share holds until one of them writes). */
 pkv_status kv_bm_fork(pkv_bm* bm, int32_t parent, int32_t child);
 /* Append one token to each of seqs[0..n) (host arrays).  slots: int64 [n]
- * out; cow_pairs: int64 [n][2] out; *num_pairs: pairs written. */
+ * out; cow_pairs: int64 [n][2] out; *num_pairs: pairs written ([KVP] §三
+ * 工作方式 step 3: a new block only when the last one is full; [BJD] §3.2
+ * copy-on-write of a shared last block). */
 pkv_status kv_bm_append(pkv_bm* bm, const int32_t* seqs, int32_t n, int64_t* slots,
                         int64_t* cow_pairs, int32_t* num_pairs);
+/* Drop a sequence: each of its blocks loses one reference and returns to
+ * the free FIFO at 0 ([KVP] §三 工作方式 step 3: blocks are released when
+ * done and the pool reuses them). */
 pkv_status kv_bm_free_seq(pkv_bm* bm, int32_t seq);
 /* Rows of tables (host int32 [n][width]) for seqs[0..n), padded with 0, and
- * their lengths (context_lens may be NULL). */
+ * their lengths (context_lens may be NULL) - the per-sequence block tables
+ * of [AWA] PagedAttention 的关键数据结构, for upload before a decode. */
 pkv_status kv_bm_block_tables(const pkv_bm* bm, const int32_t* seqs, int32_t n, int32_t* tables,
                               int32_t width, int32_t* context_lens);
 /* used = blocks referenced by some table; total = NB ([KVP] §六 cache usage);
  * failed_allocs = calls refused for lack of blocks ([KVP] §六 preemptions). */
 pkv_status kv_bm_stats(const pkv_bm* bm, int32_t* used, int32_t* total, int64_t* failed_allocs);
-/* Reference count of one block (for tests and leak checks). */
+/* Reference count of one block: the number of tables naming it (the
+ * sharing count [BJD] §3.2's copy-on-write decision reads); for tests and
+ * leak checks; -1 for a block outside [0, NB). */
 int32_t kv_bm_ref_count(const pkv_bm* bm, int32_t block);
 
 /* Prefix caching ([BJD] §4.1: a request whose prompt starts like an earlier
@@ -460,7 +493,9 @@ pkv_status kv_bm_add_seq_tokens(pkv_bm* bm, int32_t seq, const int32_t* tokens, 
  * currently cached. */
 pkv_status kv_bm_prefix_stats(const pkv_bm* bm, int64_t* lookups, int64_t* hits, int32_t* cached_blocks);
 /* The key of a block: SHA-256 of parent (32 bytes; NULL = zeros) followed by
- * tokens[0..n) as little-endian int32 (host arrays; out: 32 bytes). */
+ * tokens[0..n) as little-endian int32 (host arrays; out: 32 bytes) - the
+ * prefix hash of [BJD] §4.1 (the pages name no hash function; SHA-256 is this
+ * library's choice). */
 pkv_status kv_bm_block_key(const uint8_t* parent, const int32_t* tokens, int32_t n, uint8_t* out);
 
 #ifdef __cplusplus
