@@ -246,12 +246,16 @@ __global__ __launch_bounds__(kWave * kNW) void pa_decode_kernel(const DecodePara
 // =====================================================================
 // Split-context persistent kernel (partition_size > 0)
 // =====================================================================
-// A "row" x = (sequence s, KV head g, head tile qt), numbered
-// x = s * HQ + xi with xi = g * QT + qt and HQ = Hkv * QT.  Row x has
-// n_s = ceil(ctx_s / TS) steps of TS tokens.  The flat step list is
-// row 0's steps, then row 1's, ...; row x starts at cum_s * HQ + xi * n_s where
-// cum_s = sum over s' < s of n_s'.  Each wave of the NWV takes one
-// contiguous range of the list.
+// A "row" x = (sequence s, KV head g, head tile qt), numbered head-major:
+// x = xi * S + s with xi = g * QT + qt (HQ = Hkv * QT values).  Row x has
+// n_s = ceil(ctx_s / TS) steps of TS tokens.  The flat step list is row 0's
+// steps, then row 1's, ...: all sequences of xi = 0, then of xi = 1, ...;
+// row x starts at xi * T + cum_s where cum_s = sum over s' < s of n_s' and
+// T = cum_S.  Each wave of the NWV takes one contiguous range of the list.
+// Head-major order gives each XCD (one eighth of the list) the rows of a few
+// KV heads: when sequences share prefix blocks, the prefix tiles of those
+// heads fit the XCD's L2 and are fetched from memory about once, where a
+// sequence-major order would stream every head's prefix through every L2.
 // The grid is one workgroup of four waves per CU.  Workgroups are dispatched
 // to the eight XCDs in turn (workgroup b runs on XCD b % 8), and waves are
 // numbered so that XCD x holds waves [x * WX, (x + 1) * WX), WX = NWV / 8.
@@ -861,20 +865,23 @@ __device__ __forceinline__ void cursor_row(Cursor& c, const SplitParams& p) {
 }
 
 // Move to the first step of the next row that has any (the caller knows
-// there is one: the wave's range reaches it).
+// there is one: the wave's range reaches it): the next sequence with steps,
+// past the last one the first of the next head tile.
 template <int TS, bool kRowConsts = true>
 __device__ __forceinline__ void cursor_next_row(Cursor& c, const SplitParams& p, int max_ctx) {
   c.j = 0;
-  if (++c.xi == p.HQ) {
-    c.xi = 0;
-    do {
-      ++c.s;
-      c.ctx = clamp_ctx(uniform_load(p.ctx + c.s), max_ctx);
-      c.n = row_steps<TS>(c.ctx, p.win);
-    } while (c.n == 0);
-    c.tb = row_base<TS>(c.ctx, p.win);
-    c.lo = window_lo(c.ctx, p.win);
-  }
+  bool next_head = false;
+  do {
+    if (++c.s == p.S) {
+      c.s = 0;
+      next_head = true;
+    }
+    c.ctx = clamp_ctx(uniform_load(p.ctx + c.s), max_ctx);
+    c.n = row_steps<TS>(c.ctx, p.win);
+  } while (c.n == 0);
+  if (next_head) ++c.xi;
+  c.tb = row_base<TS>(c.ctx, p.win);
+  c.lo = window_lo(c.ctx, p.win);
   if constexpr (kRowConsts) cursor_row(c, p);
 }
 
@@ -1209,16 +1216,20 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
       }
     }
   }
-  const int N = __builtin_amdgcn_readfirstlane(total) * p.HQ;
+  const int T = __builtin_amdgcn_readfirstlane(total);   // steps of one head tile's rows
+  const int N = T * p.HQ;
   if (N == 0) return;
   int start, stop;
   wave_range(N, w, p.NWV / 8, start, stop);
   if (start >= stop) return;
   const int nsteps = stop - start;
 
-  // locate the first step: sequence s with cum_s * HQ <= start < cum_{s+1} * HQ
+  // locate the first step: head tile xi = start / T, then the sequence s
+  // with cum_s <= start - xi T < cum_{s+1}
   Cursor cur{};
   int cum0 = 0;
+  const int xi0 = start / T;
+  const int rem0 = start - xi0 * T;
   {
     int acc0 = 0;
     bool found = false;
@@ -1230,7 +1241,7 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
         const int c = cv[k];
         const int n = row_steps<TS>(c, p.win);
         const int incl = wave_incl_scan(n, lane);
-        const bool hit = (acc0 + incl - n) * p.HQ <= start && start < (acc0 + incl) * p.HQ;
+        const bool hit = acc0 + incl - n <= rem0 && rem0 < acc0 + incl;
         const uint64_t m = __ballot(hit);
         if (m) {
           const int l = __builtin_ctzll(m);
@@ -1238,9 +1249,8 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
           cur.n = __shfl(n, l, kWave);
           cur.ctx = __shfl(c, l, kWave);
           cum0 = acc0 + __shfl(incl - n, l, kWave);
-          const int off = start - cum0 * p.HQ;
-          cur.xi = off / cur.n;
-          cur.j = off % cur.n;
+          cur.xi = xi0;
+          cur.j = rem0 - cum0;
           found = true;
         }
         acc0 += __shfl(incl, kWave - 1, kWave);
@@ -1272,10 +1282,12 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
       }
       left -= mine;
       aj = 0;
-      if (left > 0 && ++axi == p.HQ) {
-        axi = 0;
+      if (left > 0) {
         do {
-          ++as;
+          if (++as == p.S) {
+            as = 0;
+            ++axi;
+          }
           actx = clamp_ctx(uniform_load(p.ctx + as), max_ctx);
           an = row_steps<TS>(actx, p.win);
         } while (an == 0);
@@ -1380,7 +1392,7 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
         if constexpr (kDirect) store_out_direct<D, GE::AL>(p, cc.s, g * p.G + qt * 16, gt, acc, l, lane);
       } else {
         if (row < gt) {
-          const int slot = cc.s * p.HQ + cc.xi + w;
+          const int slot = cc.xi * p.S + cc.s + w;
           const __amdgpu_buffer_rsrc_t pr = slot_rsrc(p.part_acc, slot, GE::NC * 1024);
 #pragma unroll
           for (int c = 0; c < GE::NC; ++c) st_agent4(pr, c * 1024 + lane * 16, acc[c]);
@@ -1400,7 +1412,7 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
       __builtin_amdgcn_sched_barrier(0);
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       if (lane == 0)
-        pend_old = report_steps(p.row_done + (int64_t)(first.s * p.HQ + first.xi) * kCounterStride, p.epoch, len0);
+        pend_old = report_steps(p.row_done + (int64_t)(first.xi * p.S + first.s) * kCounterStride, p.epoch, len0);
     }
     if (consumed < nsteps && ++cc.j == cc.n) cursor_next_row<TS, false>(cc, p, max_ctx);
   };
@@ -1444,12 +1456,12 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
       // a whole row written directly has no partial and no counter
       if (!(kDirect && mine == rn)) {
         if (lane == k) {
-          lx = rs * p.HQ + rxi;
+          lx = rxi * p.S + rs;
           lmine = mine;
           ln = rn;
           ls = rs;
           lxi = rxi;
-          lsx = rcum * p.HQ + rxi * rn;
+          lsx = rxi * T + rcum;
           lpend = first_row && pend_at > 0;
         }
       } else {
@@ -1458,11 +1470,14 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
       first_row = false;
       left -= mine;
       rj = 0;
-      if (left > 0 && ++rxi == p.HQ) {
-        rxi = 0;
-        rcum += rn;
+      if (left > 0) {
         do {
-          ++rs;
+          rcum += rn;
+          if (++rs == p.S) {
+            rs = 0;
+            rcum = 0;
+            ++rxi;
+          }
           rn = row_steps<TS>(clamp_ctx(uniform_load(p.ctx + rs), max_ctx), p.win);
         } while (rn == 0);
       }
