@@ -34,7 +34,8 @@ from __future__ import annotations
 import numpy as np
 
 from . import codecs
-from .layout import (KV_BF16, KV_FP8_E5M2, KV_INT4, KV_INT8, KV_INT8_CHANNEL, KV_INT8_TENSOR, PoolImage,
+from .layout import (KV_BF16, KV_FP8_E5M2, KV_INT4, KV_INT8, KV_INT8_CHANNEL, KV_INT8_KCHANNEL_VTENSOR,
+                     KV_INT8_TENSOR, PoolImage,
                      channel_scale_offset, int4_k_nibble, int4_v_nibble, k_offset, read_nibbles,
                      scale_offset, v_offset)
 from .layout import k_tiles_as_tokens as layout_k_tokens
@@ -91,10 +92,13 @@ def _dequant_fixed_scales(p, img, layer, kraw, vraw, k_scale, v_scale):
     if p.kv_dtype == KV_INT4:                # stored nibble = code + 8
         kraw = kraw.astype(np.int64) - 8
         vraw = vraw.astype(np.int64) - 8
-    if p.kv_dtype in (KV_INT8_CHANNEL, KV_INT4):
+    if p.kv_dtype in (KV_INT8_CHANNEL, KV_INT4, KV_INT8_KCHANNEL_VTENSOR):
         co = channel_scale_offset(p, layer, np.arange(p.num_kv_heads)[:, None], np.arange(p.head_dim)[None, :])
         ks = img.k_scale[co].astype(np.float64)[None]      # [1, Hkv, D]
-        vs = img.v_scale[co].astype(np.float64)[None]
+        if p.kv_dtype == KV_INT8_KCHANNEL_VTENSOR:       # V under the call's one scale
+            vs = np.float64(np.float32(v_scale))
+        else:
+            vs = img.v_scale[co].astype(np.float64)[None]
         return kraw.astype(np.float64) * ks, vraw.astype(np.float64) * vs
     raise ValueError(p.kv_dtype)
 
@@ -136,6 +140,10 @@ def gather_kv_by_slot(img: PoolImage, layer: int, block_table_row: np.ndarray,
         co = channel_scale_offset(p, layer, h + 0 * t, d + 0 * t)
         return (kraw.astype(np.float64) * img.k_scale[co].astype(np.float64),
                 vraw.astype(np.float64) * img.v_scale[co].astype(np.float64))
+    if p.kv_dtype == KV_INT8_KCHANNEL_VTENSOR:
+        co = channel_scale_offset(p, layer, h + 0 * t, d + 0 * t)
+        return (kraw.astype(np.float64) * img.k_scale[co].astype(np.float64),
+                vraw.astype(np.float64) * np.float64(np.float32(v_scale)))
     if p.kv_dtype == KV_INT8_TENSOR:
         return (kraw.astype(np.float64) * np.float64(np.float32(k_scale)),
                 vraw.astype(np.float64) * np.float64(np.float32(v_scale)))

@@ -19,7 +19,8 @@ from __future__ import annotations
 import numpy as np
 
 from . import codecs
-from .layout import (KV_BF16, KV_FP8_E5M2, KV_INT4, KV_INT8, KV_INT8_CHANNEL, KV_INT8_TENSOR, PoolImage,
+from .layout import (KV_BF16, KV_FP8_E5M2, KV_INT4, KV_INT8, KV_INT8_CHANNEL, KV_INT8_KCHANNEL_VTENSOR,
+                     KV_INT8_TENSOR, PoolImage,
                      channel_scale_offset, int4_k_nibble, int4_v_nibble, k_offset,
                      scale_offset, tile_base, v_offset, write_nibbles)
 
@@ -83,6 +84,12 @@ def reshape_and_cache(img: PoolImage, layer: int, key_bits: np.ndarray,
         co = channel_scale_offset(p, layer, h3, d3)       # [1, Hkv, D]: the layer's calibrated scales
         out.k[ko] = codecs.int8_encode(codecs.bf16_bits_to_f32(kx), img.k_scale[co])
         out.v[vo] = codecs.int8_encode(codecs.bf16_bits_to_f32(vx), img.v_scale[co])
+    elif p.kv_dtype == KV_INT8_KCHANNEL_VTENSOR:
+        # K and V at different granularities (bjdmk.com.cn article, §5.2: K,
+        # the more sensitive, per channel; V coarser, one scale per tensor)
+        co = channel_scale_offset(p, layer, h3, d3)
+        out.k[ko] = codecs.int8_encode(codecs.bf16_bits_to_f32(kx), img.k_scale[co])
+        out.v[vo] = codecs.int8_encode(codecs.bf16_bits_to_f32(vx), v_scale)
     else:
         raise ValueError(p.kv_dtype)
     return out

@@ -20,6 +20,8 @@ fp8/int8: 1 byte) from the start of the K (or V) region:
           ((layer * NB + block) * Hkv + head) * B + t
     K/V channel scales (INT8 per channel, fp32 elements, set by the caller):
           (layer * Hkv + head) * D + d
+    INT8 with per-channel K and per-tensor V scales keeps the K channel
+    scales only (same index); the call passes the V scale.
     INT8 per tensor and FP8 keep no scales in the pool (the call passes them).
 
 INT4 (per-channel calibrated scales, as INT8 per channel) packs two codes per
@@ -38,8 +40,8 @@ per piece and, inside a 32-bit word, nibble n at bits 4n .. 4n + 3:
 
 with tile nibble 0 at tile_base * 2.  A stored nibble is the code plus 8.
 
-Regions are laid out K, V, K-scales, V-scales, each starting at a multiple of
-256 bytes from the pool base.
+Regions are laid out K, V, K-scales, V-scales (those that exist), each
+starting at a multiple of 256 bytes from the pool base.
 """
 
 from __future__ import annotations
@@ -49,9 +51,13 @@ from dataclasses import dataclass
 import numpy as np
 
 KV_BF16, KV_FP8_E5M2, KV_INT8, KV_INT8_TENSOR, KV_INT8_CHANNEL, KV_INT4 = 0, 1, 2, 3, 4, 5
+# INT8 codes with K per channel (the pool's scales) and V per tensor (the
+# call's scale): K and V quantised at different granularities
+KV_INT8_KCHANNEL_VTENSOR = 6
 # bytes of one entry of the storage array (INT4: one byte holds two codes)
-ELEM_BYTES = {KV_BF16: 2, KV_FP8_E5M2: 1, KV_INT8: 1, KV_INT8_TENSOR: 1, KV_INT8_CHANNEL: 1, KV_INT4: 1}
-INT8_CODES = (KV_INT8, KV_INT8_TENSOR, KV_INT8_CHANNEL)
+ELEM_BYTES = {KV_BF16: 2, KV_FP8_E5M2: 1, KV_INT8: 1, KV_INT8_TENSOR: 1, KV_INT8_CHANNEL: 1, KV_INT4: 1,
+              KV_INT8_KCHANNEL_VTENSOR: 1}
+INT8_CODES = (KV_INT8, KV_INT8_TENSOR, KV_INT8_CHANNEL, KV_INT8_KCHANNEL_VTENSOR)
 REGION_ALIGN = 256
 
 
@@ -96,14 +102,25 @@ class PoolShape:
 
     @property
     def has_channel_scales(self) -> bool:
-        """Per (layer, head, dim) scales, one K and one V region per pool."""
+        """Per (layer, head, dim) scales for K and for V, one region each."""
         return self.kv_dtype in (KV_INT8_CHANNEL, KV_INT4)
 
     @property
+    def has_k_channel_scales(self) -> bool:
+        """Per (layer, head, dim) K scales in the pool (V's may differ)."""
+        return self.has_channel_scales or self.kv_dtype == KV_INT8_KCHANNEL_VTENSOR
+
+    @property
+    def has_v_scales(self) -> bool:
+        """The pool holds a V scale region (beside the K one)."""
+        return self.has_scales or self.has_channel_scales
+
+    @property
     def scale_elems(self) -> int:
+        """Elements of the K scale region (and of the V one, when it exists)."""
         if self.has_scales:
             return self.num_layers * self.num_blocks * self.num_kv_heads * self.block_size
-        if self.has_channel_scales:
+        if self.has_k_channel_scales:
             return self.num_layers * self.num_kv_heads * self.head_dim
         return 0
 
@@ -122,8 +139,11 @@ def region_offsets(p: PoolShape):
     if p.scale_elems:
         s_bytes = p.scale_elems * 4
         ks_off = end
-        vs_off = _align(ks_off + s_bytes)
-        end = _align(vs_off + s_bytes)
+        end = _align(ks_off + s_bytes)
+        vs_off = None
+        if p.has_v_scales:
+            vs_off = end
+            end = _align(vs_off + s_bytes)
         return k_off, v_off, ks_off, vs_off, end
     return k_off, v_off, None, None, end
 
@@ -287,7 +307,7 @@ class PoolImage:
 
 def _storage_dtype(p: PoolShape):
     return {KV_BF16: np.uint16, KV_FP8_E5M2: np.uint8, KV_INT8: np.int8, KV_INT8_TENSOR: np.int8,
-            KV_INT8_CHANNEL: np.int8, KV_INT4: np.uint8}[p.kv_dtype]
+            KV_INT8_CHANNEL: np.int8, KV_INT4: np.uint8, KV_INT8_KCHANNEL_VTENSOR: np.int8}[p.kv_dtype]
 
 
 def empty_image(p: PoolShape, fill: int = 0) -> PoolImage:
@@ -297,7 +317,8 @@ def empty_image(p: PoolShape, fill: int = 0) -> PoolImage:
     ks = vs = None
     if p.scale_elems:
         ks = np.zeros(p.scale_elems, dtype=np.float32)
-        vs = np.zeros(p.scale_elems, dtype=np.float32)
+        if p.has_v_scales:
+            vs = np.zeros(p.scale_elems, dtype=np.float32)
     return PoolImage(p, k, v, ks, vs)
 
 
@@ -314,7 +335,8 @@ def image_from_bytes(p: PoolShape, raw: np.ndarray) -> PoolImage:
     if p.scale_elems:
         sb = p.scale_elems * 4
         ks = raw[ks_off:ks_off + sb].view(np.float32).copy()
-        vs = raw[vs_off:vs_off + sb].view(np.float32).copy()
+        if vs_off is not None:
+            vs = raw[vs_off:vs_off + sb].view(np.float32).copy()
     return PoolImage(p, k, v, ks, vs)
 
 
@@ -329,6 +351,7 @@ def image_to_bytes(img: PoolImage) -> np.ndarray:
     if p.scale_elems:
         ksb = img.k_scale.view(np.uint8)
         raw[ks_off:ks_off + ksb.size] = ksb
-        vsb = img.v_scale.view(np.uint8)
-        raw[vs_off:vs_off + vsb.size] = vsb
+        if vs_off is not None:
+            vsb = img.v_scale.view(np.uint8)
+            raw[vs_off:vs_off + vsb.size] = vsb
     return raw

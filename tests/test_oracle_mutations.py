@@ -3,7 +3,8 @@
 Each case monkeypatches one plausible slip into the oracle and re-runs a pin
 that should then fail: a transposed grouping, a slot off by one, a dropped
 softmax scale, a wrong e5m2 exponent bias, a window one position too wide,
-per-channel scales read with the dims reversed.
+per-channel scales read with the dims reversed, a mixed-granularity V read
+with the K channel scales.
 """
 
 import numpy as np
@@ -120,3 +121,21 @@ def test_causal_limit_off_by_one_is_caught(monkeypatch):
         return out
     monkeypatch.setattr(att, "paged_prefill", bad)
     assert _fails(lambda: tpf.test_whole_prompt_equals_matrix_causal_attention(1))
+
+
+def test_mixed_granularity_v_read_with_a_k_scale_is_caught(monkeypatch):
+    # K per channel, V per tensor: a dequantiser that takes V's scale from the
+    # K channel scales (the per-channel rule applied to both) must fail the
+    # pin tying the mixed type to INT8 per channel with uniform V scales
+    orig = att._dequant_fixed_scales
+
+    def bad(p, img, layer, kraw, vraw, k_scale, v_scale):
+        k, v = orig(p, img, layer, kraw, vraw, k_scale, v_scale)
+        if p.kv_dtype == layout.KV_INT8_KCHANNEL_VTENSOR:
+            co = layout.channel_scale_offset(p, layer, np.arange(p.num_kv_heads)[:, None],
+                                             np.arange(p.head_dim)[None, :])
+            v = vraw.astype(np.float64) * img.k_scale[co].astype(np.float64)[None]
+        return k, v
+    monkeypatch.setattr(att, "_dequant_fixed_scales", bad)
+    assert _fails(ti.test_int8_per_channel_with_equal_v_scales_is_the_mixed_granularity)
+    assert _fails(ti.test_mixed_one_token_context_returns_v_code_times_v_scale)
