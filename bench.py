@@ -37,12 +37,36 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0    # MI355X HBM3E, AMD's published peak
-KV_DTYPES = {"bf16": 0, "fp8": 1, "int8": 2, "int8_tensor": 3, "int8_channel": 4, "int4": 5}
+KV_DTYPES = {"bf16": 0, "fp8": 1, "int8": 2, "int8_tensor": 3, "int8_channel": 4, "int4": 5,
+             "int8_kchannel_vtensor": 6}
 TENSOR_SCALE = 0.035     # per-tensor K and V scale of the 8-bit runs (fp8 and int8_tensor)
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def scale_regions(pool, kvt):
+    """(byte offset, float count) of each scale region the pool holds: per
+    (token, head) for int8, per (layer, KV head, dim) for the calibrated
+    channel scales (K and V, or K only when V has one scale per tensor)."""
+    import paged_kv_cache_436_amd as pkv
+    c = pool.cfg
+    _, _, ks_off, vs_off = pool.region_offsets()
+    if kvt == pkv.PKV_KV_INT8:
+        n = c.num_layers * c.num_blocks * c.num_kv_heads * c.block_size
+    else:
+        n = c.num_layers * c.num_kv_heads * c.head_dim
+    return [(off, n) for off in (ks_off, vs_off) if off is not None]
+
+
+def tensor_scales(kvt):
+    """(K, V) per-tensor scales the 8-bit runs pass with each call."""
+    import paged_kv_cache_436_amd as pkv
+    k = TENSOR_SCALE if kvt in (pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8_TENSOR) else 1.0
+    v = TENSOR_SCALE if kvt in (pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8_TENSOR,
+                                pkv.PKV_KV_INT8_KCHANNEL_VTENSOR) else 1.0
+    return k, v
 
 
 def parse():
@@ -153,10 +177,8 @@ def config_bench(args):
                 region.view(torch.bfloat16).normal_(generator=g)
             else:
                 region.random_(0, 120 if kvt == pkv.PKV_KV_FP8_E5M2 else 256, generator=g)
-        if ks_off is not None:
-            n = (vs_off - ks_off) // 4
-            for off in (ks_off, vs_off):
-                pool.memory[off: off + 4 * n].view(torch.float32).uniform_(0.02, 0.05)
+        for off, n in scale_regions(pool, kvt):
+            pool.memory[off: off + 4 * n].view(torch.float32).uniform_(0.02, 0.05)
         pools.append(pool)
     tables = torch.from_numpy(workloads.static_tables(w)).to(dev)
     ctx = torch.from_numpy(np.asarray(w.context_lens, np.int32) ).to(dev)
@@ -434,12 +456,11 @@ def prefill_bench(args):
             pool.memory[off: off + lb].view(torch.bfloat16).normal_(generator=g)
         else:   # random codes (e5m2: finite patterns below the exponent-31 codes)
             pool.memory[off: off + lb].random_(0, 120 if kvt == pkv.PKV_KV_FP8_E5M2 else 256, generator=g)
-    if ks_off is not None:     # int8 per-token scales, or the calibrated per-channel ones (int8, int4)
-        n = (vs_off - ks_off) // 4
-        lo, hi = (0.3, 0.6) if kvt == pkv.PKV_KV_INT4 else (0.02, 0.05)
-        for off in (ks_off, vs_off):
-            pool.memory[off: off + 4 * n].view(torch.float32).uniform_(lo, hi, generator=g)
-    sc = TENSOR_SCALE if kvt in (pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8_TENSOR) else 1.0
+    # int8 per-token scales, or the calibrated per-channel ones (int8, int4)
+    lo, hi = (0.3, 0.6) if kvt == pkv.PKV_KV_INT4 else (0.02, 0.05)
+    for off, n in scale_regions(pool, kvt):
+        pool.memory[off: off + 4 * n].view(torch.float32).uniform_(lo, hi, generator=g)
+    sck, scv = tensor_scales(kvt)
     tables = torch.from_numpy(w.extra["tables"]).to(dev)
     ctx = torch.from_numpy(ctx_np.astype(np.int32)).to(dev)
     qs = torch.from_numpy(qs_np).to(dev)
@@ -449,7 +470,7 @@ def prefill_bench(args):
     maxq = int(chunk.max())
 
     def call():
-        pkv.paged_attn_prefill(out, q, pool, 0, tables, ctx, qs, w.scale, maxq, k_scale=sc, v_scale=sc, stream=st)
+        pkv.paged_attn_prefill(out, q, pool, 0, tables, ctx, qs, w.scale, maxq, k_scale=sck, v_scale=scv, stream=st)
 
     for _ in range(args.warmup):
         call()
@@ -586,7 +607,7 @@ def main():
     e = 2 if kvt == pkv.PKV_KV_BF16 else 1                          # bytes per stored element (INT4: two per byte)
     token_scales = 2 * 4 if kvt == pkv.PKV_KV_INT8 else 0          # int8: fp32 K and V scale per (token, head)
     tok_bytes = Hkv * (2 * D * e // (2 if kvt == pkv.PKV_KV_INT4 else 1) + token_scales)   # KV bytes per token per layer
-    ks_t = vs_t = TENSOR_SCALE if kvt in (pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8_TENSOR) else 1.0
+    ks_t, vs_t = tensor_scales(kvt)
     if kvt != pkv.PKV_KV_BF16:
         args.no_cpu_baseline = True
     cfg = pkv.make_config(w.num_layers, w.num_blocks, B, Hkv, D, kvt)
@@ -604,10 +625,8 @@ def main():
                 region.view(torch.bfloat16).normal_(generator=g)
             else:   # random codes (int8: +-127 range; e5m2: finite patterns below the exponent-31 codes)
                 region.random_(0, 120 if kvt == pkv.PKV_KV_FP8_E5M2 else 256, generator=g)
-    if ks_off is not None:     # int8 scales: per-token ones, or the calibrated per-channel ones
-        n = pool.memory[ks_off:vs_off].numel() // 4
-        for off in (ks_off, vs_off):
-            pool.memory[off: off + 4 * n].view(torch.float32).uniform_(0.02, 0.05)
+    for off, n in scale_regions(pool, kvt):   # int8 scales: per-token ones, or the calibrated per-channel ones
+        pool.memory[off: off + 4 * n].view(torch.float32).uniform_(0.02, 0.05)
     torch.cuda.synchronize()
     log(f"pool filled in {time.time() - t0:.1f} s")
 

@@ -34,8 +34,9 @@
  *     K        [L][NB][H][tile]      tile = B*D elements
  *     V        [L][NB][H][tile]
  *     K scales [L][NB][H][B] float   (PKV_KV_INT8: per token and head)
- *              [L][H][D] float       (PKV_KV_INT8_CHANNEL, PKV_KV_INT4)
- *     V scales as the K scales
+ *              [L][H][D] float       (PKV_KV_INT8_CHANNEL, PKV_KV_INT4,
+ *                                     PKV_KV_INT8_KCHANNEL_VTENSOR)
+ *     V scales as the K scales (none for PKV_KV_INT8_KCHANNEL_VTENSOR)
  *   Other storage types have no scale regions.
  *   Inside a K tile, element (token t, dim d) is at
  *       ((d / X) * B + t) * X + d % X
@@ -100,11 +101,18 @@ typedef enum {
                               (layer, KV head, dim) for K and for V, kept in
                               the pool's scale regions, which the caller
                               fills ([KVP] §四 per-channel; [BJD] §5.2)     */
-  PKV_KV_INT4 = 5          /* symmetric 4-bit codes clamp(round(x / s), -7,
+  PKV_KV_INT4 = 5,         /* symmetric 4-bit codes clamp(round(x / s), -7,
                               7) under calibrated per-(layer, KV head, dim)
                               scales kept as for PKV_KV_INT8_CHANNEL: a
                               quarter of bf16's bytes ([KVP] §四 INT4 KV,
                               which needs calibration)                      */
+  PKV_KV_INT8_KCHANNEL_VTENSOR = 6 /* int8 codes, K and V at different
+                              granularities ([BJD] §5.2: K, the more
+                              sensitive, per channel; V coarser): K under
+                              calibrated per-(layer, KV head, dim) scales in
+                              the pool's K scale region, V under one
+                              calibrated scale per tensor passed with each
+                              call (pkv_kv_scales.v_scale)                  */
 } pkv_kv_dtype;
 
 typedef struct {
@@ -120,9 +128,9 @@ typedef struct {
  * device addresses inside the caller's buffer.  k_scale / v_scale: for
  * PKV_KV_INT8 the per-(token, head) scales [L][NB][H][B] the cache write
  * fills; for PKV_KV_INT8_CHANNEL and PKV_KV_INT4 the per-channel scales
- * [L][H][D] the caller
- * writes before caching or decoding a layer (element (l, h, d) at
- * (l * H + h) * D + d); NULL otherwise. */
+ * [L][H][D] the caller writes before caching or decoding a layer (element
+ * (l, h, d) at (l * H + h) * D + d); for PKV_KV_INT8_KCHANNEL_VTENSOR
+ * k_scale as for PKV_KV_INT8_CHANNEL and v_scale NULL; NULL otherwise. */
 typedef struct {
   pkv_pool_config cfg;
   void* base;
@@ -135,10 +143,11 @@ typedef struct {
   uint64_t layer_bytes;   /* NB * H * tile_bytes: one layer of K (or of V)   */
 } pkv_pool;
 
-/* Per-tensor scales of PKV_KV_FP8_E5M2 and PKV_KV_INT8_TENSOR storage:
- * stored = value / scale, value = stored * scale ([KVP] §四: FP8 / INT8 KV
- * with a scale).  Not read for other storage types.  NULL means 1.0 and
- * 1.0. */
+/* Per-tensor scales of PKV_KV_FP8_E5M2 and PKV_KV_INT8_TENSOR storage, and
+ * the V scale (v_scale only) of PKV_KV_INT8_KCHANNEL_VTENSOR: stored = value
+ * / scale, value = stored * scale ([KVP] §四: FP8 / INT8 KV with a scale).
+ * Those read must be positive and finite (PKV_ERR_INVALID otherwise); the
+ * others are not read.  NULL means 1.0 and 1.0. */
 typedef struct {
   float k_scale;
   float v_scale;
@@ -185,7 +194,8 @@ pkv_status kv_pool_create(const pkv_pool_config* cfg, void* dev_mem, uint64_t by
  * with scales' k_scale / v_scale (positive and finite for fp8 and INT8_TENSOR,
  * PKV_ERR_INVALID otherwise, as for the decode calls);
  * INT8_CHANNEL with the pool's channel scales of this layer (a scale of 0
- * gives code 0).  Two tokens with the same slot in one call race
+ * gives code 0); INT8_KCHANNEL_VTENSOR K with the pool's K channel scales,
+ * V with scales' v_scale.  Two tokens with the same slot in one call race
  * (pkv_check_slots rejects that). */
 pkv_status reshape_and_cache(const pkv_pool* pool, int32_t layer, const void* key,
                              const void* value, const int64_t* slot_mapping,
@@ -251,8 +261,8 @@ uint64_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
  *   context_lens  device int32 [S], each <= table_width * B
  *   kv_dtype      must equal pool->cfg.kv_dtype
  *   kv_scales     host; the per-tensor scales of fp8 and INT8-per-tensor
- *                 storage (NULL = 1.0), positive and finite; not read for
- *                 other storage types
+ *                 storage and the V scale of INT8_KCHANNEL_VTENSOR (NULL =
+ *                 1.0), positive and finite; the rest is not read
  *   partition_size 0: single pass, one workgroup per (sequence, KV head), no
  *                 workspace (INT4: one query per sequence through the
  *                 paged_attn_prefill kernel).  Otherwise the split-context form, a positive

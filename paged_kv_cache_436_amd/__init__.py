@@ -33,6 +33,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_HIP = 0, -1, -2, -3, -4
 PKV_KV_BF16, PKV_KV_FP8_E5M2, PKV_KV_INT8, PKV_KV_INT8_TENSOR, PKV_KV_INT8_CHANNEL, PKV_KV_INT4 = 0, 1, 2, 3, 4, 5
+PKV_KV_INT8_KCHANNEL_VTENSOR = 6
 ELEM_BYTES = {PKV_KV_BF16: 2, PKV_KV_FP8_E5M2: 1, PKV_KV_INT8: 1}
 
 

@@ -68,8 +68,9 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     int8_t* kd = static_cast<int8_t*>(kdst) + tile;
     int8_t* vd = static_cast<int8_t*>(vdst) + tile;
     for (int d = lane; d < D; d += kWave) {
+      // (per channel with no V channel scales: V per tensor, the call's)
       const float ks = KVT == PKV_KV_INT8_TENSOR ? k_scale : kscale[h * D + d];
-      const float vs = KVT == PKV_KV_INT8_TENSOR ? v_scale : vscale[h * D + d];
+      const float vs = KVT == PKV_KV_INT8_TENSOR ? v_scale : (vscale ? vscale[h * D + d] : v_scale);
       kd[((d >> 4) * B + t) * 16 + (d & 15)] = (int8_t)int8_store(kx[d], ks);
       vd[((t >> 2) * D + d) * 4 + (t & 3)] = (int8_t)int8_store(vx[d], vs);
     }
@@ -232,18 +233,14 @@ extern "C" pkv_status reshape_and_cache(const pkv_pool* pool, int32_t layer, con
   if (num_tokens == 0) { clear_error(); return PKV_OK; }
   if (!key || !value || !slot_mapping) return fail(PKV_ERR_INVALID, "key, value and slot_mapping must be non-NULL");
   float ksc = 1.f, vsc = 1.f;
-  if (scales && (c.kv_dtype == PKV_KV_FP8_E5M2 || c.kv_dtype == PKV_KV_INT8_TENSOR)) {
-    ksc = scales->k_scale;
-    vsc = scales->v_scale;
-    if (!(ksc > 0.f) || !(vsc > 0.f) || !(ksc < INFINITY) || !(vsc < INFINITY))
-      return fail(PKV_ERR_INVALID, "per-tensor scales must be positive and finite");
-  }
+  st = tensor_scales(c.kv_dtype, scales, &ksc, &vsc);
+  if (st != PKV_OK) return st;
   const int64_t waves = (int64_t)num_tokens * c.num_kv_heads;
   const int64_t grid = (waves + 3) / 4;
   if (grid > INT32_MAX) return fail(PKV_ERR_INVALID, "too many tokens in one call");
   char* kl = static_cast<char*>(pool->k) + (uint64_t)layer * pool->layer_bytes;
   char* vl = static_cast<char*>(pool->v) + (uint64_t)layer * pool->layer_bytes;
-  const uint64_t scale_layer = has_channel_scales(c.kv_dtype)
+  const uint64_t scale_layer = has_k_channel_scales(c.kv_dtype)
                                   ? (uint64_t)c.num_kv_heads * c.head_dim
                                   : (uint64_t)c.num_blocks * c.num_kv_heads * c.block_size;
   float* ksl = pool->k_scale ? pool->k_scale + layer * scale_layer : nullptr;
@@ -268,6 +265,7 @@ extern "C" pkv_status reshape_and_cache(const pkv_pool* pool, int32_t layer, con
                          num_slots, kl, vl, ksl, vsl, ksc, vsc);
       break;
     case PKV_KV_INT8_CHANNEL:
+    case PKV_KV_INT8_KCHANNEL_VTENSOR:   // no V channel scales: vsl is NULL, V takes vsc
       hipLaunchKernelGGL(reshape_and_cache_kernel<PKV_KV_INT8_CHANNEL>, dim3((uint32_t)grid), dim3(256), 0,
                          stream, kx, vx, slot_mapping, num_tokens, c.num_kv_heads, c.head_dim, c.block_size,
                          num_slots, kl, vl, ksl, vsl, ksc, vsc);

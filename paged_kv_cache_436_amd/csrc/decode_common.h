@@ -300,9 +300,9 @@ using IC = std::integral_constant<int, V>;
 
 // f(IC<D>, IC<KVT>, IC<B>) for the kernel variant of head dim D (64, 128),
 // storage kv_dtype and block size B (8, 16, 32).  INT8 with per-channel
-// scales has its own variant: plain codes whose K channel scales are folded
-// into the query (read as its bf16 hi and lo parts) and whose V channel
-// scales are applied to the output.
+// K scales has its own variant: plain codes whose K channel scales are folded
+// into the query (read as its bf16 hi and lo parts) and whose V scales (per
+// channel, or one per tensor) are applied to the output.
 template <bool kInt4, class F>
 auto with_variant(int D, int kvt, int B, F&& f) {
   auto by_b = [&](auto dc, auto kc) {
@@ -315,7 +315,8 @@ auto with_variant(int D, int kvt, int B, F&& f) {
       case PKV_KV_BF16: return by_b(dc, IC<PKV_KV_BF16>{});
       case PKV_KV_FP8_E5M2: return by_b(dc, IC<PKV_KV_FP8_E5M2>{});
       case PKV_KV_INT8_TENSOR: return by_b(dc, IC<PKV_KV_INT8_TENSOR>{});
-      case PKV_KV_INT8_CHANNEL: return by_b(dc, IC<PKV_KV_INT8_CHANNEL>{});
+      case PKV_KV_INT8_CHANNEL:
+      case PKV_KV_INT8_KCHANNEL_VTENSOR: return by_b(dc, IC<PKV_KV_INT8_CHANNEL>{});
       case PKV_KV_INT4:
         if constexpr (kInt4) return by_b(dc, IC<PKV_KV_INT4>{});
         [[fallthrough]];

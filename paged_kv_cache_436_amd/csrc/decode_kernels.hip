@@ -1527,7 +1527,8 @@ auto with_split_variant(int D, int kvt, int B, F&& f) {
       case PKV_KV_BF16: return by_b(dc, IC<PKV_KV_BF16>{});
       case PKV_KV_FP8_E5M2: return by_b(dc, IC<PKV_KV_FP8_E5M2>{});
       case PKV_KV_INT8_TENSOR: return by_b(dc, IC<PKV_KV_INT8_TENSOR>{});
-      case PKV_KV_INT8_CHANNEL: return by_b(dc, IC<PKV_KV_INT8_CHANNEL>{});
+      case PKV_KV_INT8_CHANNEL:
+      case PKV_KV_INT8_KCHANNEL_VTENSOR: return by_b(dc, IC<PKV_KV_INT8_CHANNEL>{});
       case PKV_KV_INT4: return by_b(dc, IC<PKV_KV_INT4>{});
       default: return by_b(dc, IC<PKV_KV_INT8>{});
     }
@@ -1719,13 +1720,10 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
   }
   if (((uintptr_t)q) % 16 || ((uintptr_t)out) % 16) return fail(PKV_ERR_INVALID, "q and out must be 16-byte aligned");
   float ksc = 1.f, vsc = 1.f;
-  if (kv_scales && (c.kv_dtype == PKV_KV_FP8_E5M2 || c.kv_dtype == PKV_KV_INT8_TENSOR)) {
-    ksc = kv_scales->k_scale;
-    vsc = kv_scales->v_scale;
-    if (!(ksc > 0.f) || !(vsc > 0.f) || !(ksc < INFINITY) || !(vsc < INFINITY))
-      return fail(PKV_ERR_INVALID, "per-tensor scales must be positive and finite");
-  }
-  const bool channel = has_channel_scales(c.kv_dtype);
+  if (tensor_scales(c.kv_dtype, kv_scales, &ksc, &vsc) != PKV_OK) return PKV_ERR_INVALID;
+  // K channel scales (folded into the query); the pool's V channel scales,
+  // where it has them, multiply the output
+  const bool channel = has_k_channel_scales(c.kv_dtype);
   if (channel && (const void*)out == q)
     return fail(PKV_ERR_INVALID, "out must not alias q for storage with per-channel scales");
   const int32_t G = num_q_heads / c.num_kv_heads;

@@ -1,6 +1,7 @@
 // Internal helpers shared by the library's translation units (not installed).
 #pragma once
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -27,6 +28,7 @@ inline int elem_bits(int32_t kv_dtype) {
     case PKV_KV_INT8_TENSOR: return 8;
     case PKV_KV_INT8_CHANNEL: return 8;
     case PKV_KV_INT4: return 4;
+    case PKV_KV_INT8_KCHANNEL_VTENSOR: return 8;
     default: return 0;
   }
 }
@@ -36,9 +38,40 @@ inline uint64_t tile_bytes_of(const pkv_pool_config& c) {
   return (uint64_t)c.block_size * c.head_dim * elem_bits(c.kv_dtype) / 8;
 }
 
-// Calibrated per-(layer, head, dim) scales kept in the pool.
+// Calibrated per-(layer, head, dim) scales kept in the pool, for K and for V.
 inline bool has_channel_scales(int32_t kv_dtype) {
   return kv_dtype == PKV_KV_INT8_CHANNEL || kv_dtype == PKV_KV_INT4;
+}
+
+// Calibrated per-(layer, head, dim) K scales kept in the pool (the decode
+// kernels fold them into the query); V may have its own granularity.
+inline bool has_k_channel_scales(int32_t kv_dtype) {
+  return has_channel_scales(kv_dtype) || kv_dtype == PKV_KV_INT8_KCHANNEL_VTENSOR;
+}
+
+// The call's per-tensor scales: K and V (fp8, INT8 per tensor), or V only.
+inline bool has_tensor_k_scale(int32_t kv_dtype) {
+  return kv_dtype == PKV_KV_FP8_E5M2 || kv_dtype == PKV_KV_INT8_TENSOR;
+}
+inline bool has_tensor_v_scale(int32_t kv_dtype) {
+  return has_tensor_k_scale(kv_dtype) || kv_dtype == PKV_KV_INT8_KCHANNEL_VTENSOR;
+}
+
+// The call's per-tensor scales of this storage type, checked: *ks / *vs keep
+// 1.0 where the type has no such scale or scales is NULL.
+inline pkv_status tensor_scales(int32_t kv_dtype, const pkv_kv_scales* scales, float* ks, float* vs) {
+  *ks = 1.f;
+  *vs = 1.f;
+  if (!scales) return PKV_OK;
+  if (has_tensor_k_scale(kv_dtype)) {
+    *ks = scales->k_scale;
+    if (!(*ks > 0.f) || !(*ks < INFINITY)) return fail(PKV_ERR_INVALID, "per-tensor scales must be positive and finite");
+  }
+  if (has_tensor_v_scale(kv_dtype)) {
+    *vs = scales->v_scale;
+    if (!(*vs > 0.f) || !(*vs < INFINITY)) return fail(PKV_ERR_INVALID, "per-tensor scales must be positive and finite");
+  }
+  return PKV_OK;
 }
 
 constexpr uint64_t kRegionAlign = 256;

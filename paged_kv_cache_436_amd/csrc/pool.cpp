@@ -49,15 +49,18 @@ bool pool_regions(const pkv_pool_config* cfg, Regions* r) {
   r->total = align_up(r->v + kv);
   r->ks = r->vs = 0;
   r->scale_bytes = 0;
-  if (cfg->kv_dtype == PKV_KV_INT8 || has_channel_scales(cfg->kv_dtype)) {
+  if (cfg->kv_dtype == PKV_KV_INT8 || has_k_channel_scales(cfg->kv_dtype)) {
     const uint64_t sb = cfg->kv_dtype == PKV_KV_INT8
                             ? (uint64_t)cfg->num_layers * cfg->num_blocks * cfg->num_kv_heads * cfg->block_size *
                                   sizeof(float)
                             : (uint64_t)cfg->num_layers * cfg->num_kv_heads * cfg->head_dim * sizeof(float);
     r->scale_bytes = sb;
     r->ks = r->total;
-    r->vs = align_up(r->ks + sb);
-    r->total = align_up(r->vs + sb);
+    r->total = align_up(r->ks + sb);
+    if (cfg->kv_dtype == PKV_KV_INT8 || has_channel_scales(cfg->kv_dtype)) {   // V scales too
+      r->vs = r->total;
+      r->total = align_up(r->vs + sb);
+    }
   }
   return true;
 }
@@ -67,8 +70,9 @@ pkv_status check_pool(const pkv_pool* pool) {
   Regions r;
   if (!pool_regions(&pool->cfg, &r)) return PKV_ERR_INVALID;
   if (!pool->k || !pool->v) return fail(PKV_ERR_INVALID, "pool has no K/V pointers (use kv_pool_create)");
-  if ((pool->cfg.kv_dtype == PKV_KV_INT8 || has_channel_scales(pool->cfg.kv_dtype)) &&
-      (!pool->k_scale || !pool->v_scale))
+  const int32_t t = pool->cfg.kv_dtype;
+  if (((t == PKV_KV_INT8 || has_k_channel_scales(t)) && !pool->k_scale) ||
+      ((t == PKV_KV_INT8 || has_channel_scales(t)) && !pool->v_scale))
     return fail(PKV_ERR_INVALID, "pool has no scale pointers");
   return PKV_OK;
 }
@@ -126,10 +130,8 @@ pkv_status kv_pool_create(const pkv_pool_config* cfg, void* dev_mem, uint64_t by
   char* b = static_cast<char*>(dev_mem);
   out->k = b + r.k;
   out->v = b + r.v;
-  if (r.scale_bytes) {
-    out->k_scale = reinterpret_cast<float*>(b + r.ks);
-    out->v_scale = reinterpret_cast<float*>(b + r.vs);
-  }
+  if (r.scale_bytes) out->k_scale = reinterpret_cast<float*>(b + r.ks);
+  if (r.vs) out->v_scale = reinterpret_cast<float*>(b + r.vs);
   out->tile_bytes = tile_bytes_of(*cfg);
   out->layer_bytes = (uint64_t)cfg->num_blocks * cfg->num_kv_heads * out->tile_bytes;
   clear_error();

@@ -54,10 +54,10 @@ def images_equal(a: olayout.PoolImage, b: olayout.PoolImage) -> bool:
         return False
     if not np.array_equal(a.v.view(np.uint8), b.v.view(np.uint8)):
         return False
-    if a.k_scale is not None:
-        if not np.array_equal(a.k_scale.view(np.uint32), b.k_scale.view(np.uint32)):
+    for x, y in ((a.k_scale, b.k_scale), (a.v_scale, b.v_scale)):
+        if (x is None) != (y is None):
             return False
-        if not np.array_equal(a.v_scale.view(np.uint32), b.v_scale.view(np.uint32)):
+        if x is not None and not np.array_equal(x.view(np.uint32), y.view(np.uint32)):
             return False
     return True
 

@@ -38,7 +38,7 @@ struct Lcg {
 };
 
 void pool_sizing() {
-  for (int dt = 0; dt <= 5; ++dt)
+  for (int dt = 0; dt <= 6; ++dt)
     for (int D : {64, 128})
       for (int B : {8, 16, 32}) {
         pkv_pool_config c{3, 37, B, 2, D, dt};
@@ -59,9 +59,11 @@ void pool_sizing() {
         const uint64_t payload = (uint64_t)c.num_layers * p.layer_bytes;
         CHECK((char*)p.k >= b && (char*)p.k + payload <= (char*)p.v);
         CHECK((char*)p.v + payload <= b + bytes);
-        const bool scales = dt == PKV_KV_INT8 || dt == PKV_KV_INT8_CHANNEL || dt == PKV_KV_INT4;
-        CHECK((p.k_scale != nullptr) == scales && (p.v_scale != nullptr) == scales);
-        if (scales) CHECK((char*)p.k_scale >= (char*)p.v + payload && (char*)p.v_scale < b + bytes);
+        const bool vscales = dt == PKV_KV_INT8 || dt == PKV_KV_INT8_CHANNEL || dt == PKV_KV_INT4;
+        const bool kscales = vscales || dt == PKV_KV_INT8_KCHANNEL_VTENSOR;
+        CHECK((p.k_scale != nullptr) == kscales && (p.v_scale != nullptr) == vscales);
+        if (kscales) CHECK((char*)p.k_scale >= (char*)p.v + payload && (char*)p.k_scale < b + bytes);
+        if (vscales) CHECK((char*)p.v_scale > (char*)p.k_scale && (char*)p.v_scale < b + bytes);
         CHECK(kv_pool_create(&c, mem, bytes - 1, &p) == PKV_ERR_INVALID);
         CHECK(kv_pool_create(&c, b + 16, bytes, &p) == PKV_ERR_INVALID);
         CHECK(kv_pool_create(&c, nullptr, bytes, &p) == PKV_ERR_INVALID);

@@ -1,6 +1,7 @@
-"""INT8 storage with per-tensor and per-channel scales on the GPU, against
-the oracle: the cache write bit for bit (codes; channel scales untouched),
-decode in both forms and the appending form (same bits as the two calls).
+"""INT8 storage with per-tensor and per-channel scales, and with K per
+channel and V per tensor, on the GPU, against the oracle: the cache write
+bit for bit (codes; channel scales untouched), decode in both forms and the
+appending form (same bits as the two calls).
 """
 
 import math
@@ -41,11 +42,12 @@ def _case(rng, dt, ctx, hkv=2, G=4, D=128, B=16, spare=3):
     c.pool = pkv.Pool(c.cfg)
     c.pool.memory.fill_(255)                      # unwritten codes: -1
     _, _, ks, vs = c.pool.region_offsets()
-    if ks is not None:                             # calibrated channel scales, both layers
-        n = 2 * hkv * D
+    n = 2 * hkv * D                                # calibrated channel scales, both layers
+    if ks is not None:
         c.ch_k = rng.uniform(0.02, 0.05, n).astype(np.float32)
-        c.ch_v = rng.uniform(0.02, 0.05, n).astype(np.float32)
         c.pool.memory[ks:ks + 4 * n].view(torch.float32).copy_(torch.from_numpy(c.ch_k))
+    if vs is not None:                             # (none when V has one scale per tensor)
+        c.ch_v = rng.uniform(0.02, 0.05, n).astype(np.float32)
         c.pool.memory[vs:vs + 4 * n].view(torch.float32).copy_(torch.from_numpy(c.ch_v))
     c.hq = hkv * G
     c.q = workloads.to_bf16_bits(rng.standard_normal((len(ctx), c.hq, D), dtype=np.float32))
@@ -77,7 +79,7 @@ def _decode(c, P, window=0, key=None, value=None):
     return out.cpu().numpy(), scale
 
 
-@pytest.mark.parametrize("dt", [pkv.PKV_KV_INT8_TENSOR, pkv.PKV_KV_INT8_CHANNEL])
+@pytest.mark.parametrize("dt", [pkv.PKV_KV_INT8_TENSOR, pkv.PKV_KV_INT8_CHANNEL, pkv.PKV_KV_INT8_KCHANNEL_VTENSOR])
 @pytest.mark.parametrize("D,B", [(128, 16), (64, 32)])
 def test_cache_write_is_bit_exact(dt, D, B):
     rng = np.random.default_rng(12000 + dt + D + B)
@@ -86,7 +88,7 @@ def test_cache_write_is_bit_exact(dt, D, B):
     assert images_equal(got, c.img), first_diff(got, c.img)
 
 
-@pytest.mark.parametrize("dt", [pkv.PKV_KV_INT8_TENSOR, pkv.PKV_KV_INT8_CHANNEL])
+@pytest.mark.parametrize("dt", [pkv.PKV_KV_INT8_TENSOR, pkv.PKV_KV_INT8_CHANNEL, pkv.PKV_KV_INT8_KCHANNEL_VTENSOR])
 @pytest.mark.parametrize("D,B", [(128, 16), (64, 32), (128, 32), (128, 8)])
 @pytest.mark.parametrize("P", [0, 32, 512])
 def test_decode_matches_oracle(dt, D, B, P):
@@ -108,7 +110,7 @@ def test_decode_matches_oracle(dt, D, B, P):
         assert mx <= BAR[0] and rel <= BAR[1]
 
 
-@pytest.mark.parametrize("dt", [pkv.PKV_KV_INT8_TENSOR, pkv.PKV_KV_INT8_CHANNEL])
+@pytest.mark.parametrize("dt", [pkv.PKV_KV_INT8_TENSOR, pkv.PKV_KV_INT8_CHANNEL, pkv.PKV_KV_INT8_KCHANNEL_VTENSOR])
 def test_appending_decode_equals_two_calls(dt):
     import torch
     rng = np.random.default_rng(12200 + dt)

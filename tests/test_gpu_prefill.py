@@ -2,8 +2,8 @@
 prompts, partial chunks after a cached prefix, single tokens, empty chunks,
 chunks longer than the context) over pools written by the GPU cache write,
 for every storage type (bf16, fp8, int8 per token / per tensor / per
-channel, int4), both head dims, block sizes 8 / 16 / 32 and several group
-sizes.
+channel / K per channel with V per tensor, int4), both head dims, block
+sizes 8 / 16 / 32 and several group sizes.
 """
 
 import math
@@ -21,7 +21,8 @@ pytestmark = pytest.mark.gpu
 
 BAR = {pkv.PKV_KV_BF16: (1e-2, 1e-3)}
 BAR8 = (2e-2, 2e-4)    # 8-bit and 4-bit storage: prefill keeps p as two parts and folds q exactly
-SCALES = {pkv.PKV_KV_FP8_E5M2: (0.5, 1.5), pkv.PKV_KV_INT8_TENSOR: (0.035, 0.03)}
+SCALES = {pkv.PKV_KV_FP8_E5M2: (0.5, 1.5), pkv.PKV_KV_INT8_TENSOR: (0.035, 0.03),
+          pkv.PKV_KV_INT8_KCHANNEL_VTENSOR: (0.5, 0.03)}       # its K scale is not read
 
 
 def _run(rng, dt, ctx, chunk, hkv=2, G=4, D=128, B=16, poison=True, needles=0):
@@ -45,14 +46,15 @@ def _run(rng, dt, ctx, chunk, hkv=2, G=4, D=128, B=16, poison=True, needles=0):
     else:
         pool.memory.zero_()
     _, _, ks_off, vs_off = pool.region_offsets()
-    if dt in (pkv.PKV_KV_INT8_CHANNEL, pkv.PKV_KV_INT4):
+    if dt in (pkv.PKV_KV_INT8_CHANNEL, pkv.PKV_KV_INT4, pkv.PKV_KV_INT8_KCHANNEL_VTENSOR):
         # calibrated channel scales: ~absmax / 127 (int8) or / 7 (int4) of N(0, 1) data
-        lo, hi = (0.02, 0.05) if dt == pkv.PKV_KV_INT8_CHANNEL else (0.3, 0.6)
+        lo, hi = (0.3, 0.6) if dt == pkv.PKV_KV_INT4 else (0.02, 0.05)
         n = hkv * D
         pool.memory[ks_off:ks_off + 4 * n].view(torch.float32).copy_(
             torch.from_numpy(rng.uniform(lo, hi, n).astype(np.float32)))
-        pool.memory[vs_off:vs_off + 4 * n].view(torch.float32).copy_(
-            torch.from_numpy(rng.uniform(lo, hi, n).astype(np.float32)))
+        if vs_off is not None:
+            pool.memory[vs_off:vs_off + 4 * n].view(torch.float32).copy_(
+                torch.from_numpy(rng.uniform(lo, hi, n).astype(np.float32)))
     ks, vs = SCALES.get(dt, (1.0, 1.0))
     total = int(ctx.sum())
     k = workloads.to_bf16_bits(rng.standard_normal((max(total, 1), hkv, D), dtype=np.float32))
@@ -99,7 +101,7 @@ def _run(rng, dt, ctx, chunk, hkv=2, G=4, D=128, B=16, poison=True, needles=0):
 
 
 @pytest.mark.parametrize("dt", [pkv.PKV_KV_BF16, pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8, pkv.PKV_KV_INT8_TENSOR,
-                                pkv.PKV_KV_INT8_CHANNEL, pkv.PKV_KV_INT4])
+                                pkv.PKV_KV_INT8_CHANNEL, pkv.PKV_KV_INT4, pkv.PKV_KV_INT8_KCHANNEL_VTENSOR])
 @pytest.mark.parametrize("D,B", [(128, 16), (64, 32), (128, 8), (64, 16)])
 def test_prefill_matches_oracle(dt, D, B):
     say(f"prefill dt={dt} D={D} B={B}")
@@ -145,7 +147,7 @@ def test_prefill_int4_group_sizes():
 
 
 @pytest.mark.parametrize("dt", [pkv.PKV_KV_BF16, pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT8, pkv.PKV_KV_INT8_TENSOR,
-                                pkv.PKV_KV_INT8_CHANNEL, pkv.PKV_KV_INT4])
+                                pkv.PKV_KV_INT8_CHANNEL, pkv.PKV_KV_INT4, pkv.PKV_KV_INT8_KCHANNEL_VTENSOR])
 def test_prefill_peaked_needles(dt):
     """Planted needle keys: reading a wrong block or mis-masking a column
     moves outputs by O(1); the bars are relative to max |out| ~ 1 here."""

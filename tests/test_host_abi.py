@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported_and_bound():
     assert sorted(pkv.SIGNATURES) == names
 
 
-@pytest.mark.parametrize("dt", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("dt", [0, 1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("shape", [(1, 16, 16, 2, 64), (3, 7, 32, 8, 128), (2, 5, 8, 1, 32)])
 def test_pool_bytes_and_regions_match_oracle_layout(dt, shape):
     L, NB, B, H, D = shape
@@ -47,10 +47,8 @@ def test_pool_bytes_and_regions_match_oracle_layout(dt, shape):
     fake_base = 1 << 20                      # host-only call: the pointer is never touched
     assert pkv._lib.kv_pool_create(ctypes.byref(cfg), fake_base, n, ctypes.byref(desc)) == 0
     assert desc.k - fake_base == k and desc.v - fake_base == v
-    if ks is not None:
-        assert desc.k_scale - fake_base == ks and desc.v_scale - fake_base == vs
-    else:
-        assert not desc.k_scale and not desc.v_scale
+    assert (desc.k_scale - fake_base == ks) if ks is not None else not desc.k_scale
+    assert (desc.v_scale - fake_base == vs) if vs is not None else not desc.v_scale
     assert desc.tile_bytes == p.tile_units * olayout.ELEM_BYTES[dt]
     assert desc.layer_bytes == NB * H * desc.tile_bytes
     # too small a buffer, misaligned base
