@@ -1303,10 +1303,12 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
   constexpr int NE = B >= TS ? 1 : TS / B;          // table entries per step
   const LaneOff<D, KVT, B> lo(lane);
   // issue side: the cursor of the next step to load, its row's table, and
-  // that step's table entries (fetched one step ahead)
+  // that step's table entries (fetched one step ahead, as they are read: the
+  // scalar loads' results are first used, to clamp them into the pool, when
+  // that step is issued, so their latency hides behind a step's compute)
   Cursor ic = cur;
   const int32_t* bt_row = p.bt + (int64_t)ic.s * p.W;
-  int ph[NE];
+  int ph_raw[NE];
   auto fetch = [&]() __attribute__((always_inline)) {
     // logical blocks clamped to those holding attended positions, so a chunk
     // outside [lo, ctx) never reads a table entry past the context or before
@@ -1314,11 +1316,7 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
     const uint32_t lb0 = (uint32_t)(ic.tb + ic.j * TS) / B;
     const uint32_t lmin = (uint32_t)ic.lo / B, lmax = (uint32_t)(ic.ctx - 1) / B;
 #pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      const uint32_t lb = min(max(lb0 + e, lmin), lmax);
-      const int v = uniform_load(bt_row + lb);
-      ph[e] = v < 0 ? 0 : (v >= p.num_blocks ? p.num_blocks - 1 : v);   // stay inside the pool
-    }
+    for (int e = 0; e < NE; ++e) ph_raw[e] = uniform_load(bt_row + min(max(lb0 + e, lmin), lmax));
   };
   fetch();
   // compute side: the cursor of the next step to compute
@@ -1342,6 +1340,10 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
   // made.
   auto issue = [&](SplitBuf<D, KVT>& r, QR& qr) __attribute__((always_inline)) {
     if (issued < nsteps && (ic.j == 0 || issued == 0)) qr = load_q<D, KVT>(p, ic.s, ic.h0, ic.gt, lane);
+    int ph[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e)   // stay inside the pool
+      ph[e] = ph_raw[e] < 0 ? 0 : (ph_raw[e] >= p.num_blocks ? p.num_blocks - 1 : ph_raw[e]);
     issue_step<D, KVT, B, NE>(r, p, ph, ic.g, ic.tb + ic.j * TS, lo, lane);
     ++issued;
     if (issued < nsteps) {
