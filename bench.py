@@ -107,6 +107,10 @@ def parse():
                          "one layer per call; TFLOP/s against the bf16 matrix-core peak")
     ap.add_argument("--prefill-workload", default="prefix_cache", choices=["prefix_cache", "full_prompt"],
                     help="with --prefill: prefix_cache (above) or full_prompt (16 whole 4096-token prompts)")
+    ap.add_argument("--compute-probe", action="store_true",
+                    help="instead of the decode step: time the compute of one 16-token bf16 block of one KV head "
+                         "per wave (matrix cores vs vector ALU, no HBM traffic; libpkv_probe.so) against the "
+                         "time the block takes to stream from HBM")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 1 GiB three times (torch copy kernel): the reference for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -562,6 +566,67 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
 
 
+def compute_probe_bench(args):
+    """Per-block compute time of the decode step's arithmetic, with no HBM
+    traffic: q.K^T, softmax update and P.V of one 16-token bf16 block of one
+    KV head (head dim 128) per wave, on the matrix cores (the decode kernel's
+    way) and on the vector ALU, one workgroup of four waves per CU.  The
+    slope between two loop lengths removes launch and prologue time."""
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_436_amd", "libpkv_probe.so"))
+    lib.pkv_probe_compute.restype = ctypes.c_int
+    lib.pkv_probe_compute.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    seed = torch.randn(8192, generator=g, device=dev).to(torch.bfloat16).view(torch.int32)
+    wgs = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    names = {0: "loop and operand changes only", 1: "matrix cores (decode kernel's arithmetic)",
+             2: "vector ALU, 8 query heads per KV head", 3: "vector ALU, 4 query heads per KV head"}
+    n_short, n_long = 2000, 6000
+
+    def run(variant, chunks, reps):
+        rc = lib.pkv_probe_compute(variant, seed.data_ptr(), out.data_ptr(), chunks, wgs, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"pkv_probe_compute({variant}) returned hipError {rc}")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            lib.pkv_probe_compute(variant, seed.data_ptr(), out.data_ptr(), chunks, wgs, stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps           # us per launch
+
+    res = {}
+    for v in (0, 1, 2, 3):
+        log(f"probe variant {v}: {names[v]}")
+        for _ in range(max(args.warmup, 1)):
+            run(v, n_short, 1)
+        t_s = run(v, n_short, args.steps)
+        t_l = run(v, n_long, args.steps)
+        res[v] = (t_l - t_s) * 1e3 / (n_long - n_short)   # ns per block per wave
+        log(f"  {t_s:.1f} us / {n_short} blocks, {t_l:.1f} us / {n_long} blocks: {res[v]:.1f} ns per block")
+    # one 16-token bf16 block of one KV head: K and V, 16 x 128 x 2 bytes each,
+    # streamed by each of the chip's 4 x CUs waves at once
+    waves = 4 * wgs
+    blk = 2 * 16 * 128 * 2
+    mem_peak_ns = blk * waves / 8000e9 * 1e9
+    line = {"metric": "per-block compute ns per wave (16-token bf16 block, head dim 128, no HBM traffic)",
+            "unit": "ns", "waves": waves, "block_bytes": blk,
+            "hbm_ns_per_block_at_peak": round(mem_peak_ns, 1),
+            "variants": {names[v]: round(res[v], 1) for v in res},
+            "compute_ns": {names[v]: round(res[v] - res[0], 1) for v in (1, 2, 3)},
+            "steps": args.steps, "warmup": args.warmup}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -570,6 +635,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.compute_probe:
+        compute_probe_bench(args)
         return
     if args.swap:
         swap_bench(args)

@@ -5,7 +5,8 @@
 HIP sources are compiled by hipcc for --offload-arch=gfx950 with packed-fp32
 instruction selection disabled; host-only C++ (pool description, block
 manager, validators) by g++.  Objects go to paged_kv_cache_436_amd/_build/,
-the library to paged_kv_cache_436_amd/libpkv.so.
+the library to paged_kv_cache_436_amd/libpkv.so, and the compute-only timing
+probe to paged_kv_cache_436_amd/libpkv_probe.so.
 """
 
 from __future__ import annotations
@@ -21,6 +22,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
+# the compute-only timing probe (include/pkv_probe.h), a library of its own
+PROBE_LIB = os.path.join(HERE, "libpkv_probe.so")
+PROBE_SOURCE = "compute_probe.hip"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
@@ -65,6 +69,8 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD, src + ".o")
         objs.append(obj)
         jobs.append([hipcc, *HIPCC_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
+    probe_obj = os.path.join(BUILD, PROBE_SOURCE + ".o")
+    jobs.append([hipcc, *HIPCC_FLAGS, *inc, "-c", os.path.join(CSRC, PROBE_SOURCE), "-o", probe_obj])
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         objs.append(obj)
@@ -76,6 +82,9 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", probe_obj, "-o", tmp])
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

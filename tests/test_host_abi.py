@@ -15,10 +15,11 @@ from oracle import layout as olayout
 from oracle.block_manager import BlockManagerModel
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pkv.h")
+PROBE_HEADER = os.path.join(os.path.dirname(HEADER), "pkv_probe.h")
 
 
-def _declared_functions():
-    text = open(HEADER, encoding="utf-8").read()
+def _declared_functions(header=HEADER):
+    text = open(header, encoding="utf-8").read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
                        text, flags=re.M)
@@ -32,6 +33,14 @@ def test_every_declared_symbol_is_exported_and_bound():
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(pkv.SIGNATURES) == names
+
+
+def test_probe_library_exports_its_header():
+    names = _declared_functions(PROBE_HEADER)
+    assert names == ["pkv_probe_compute"]
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(pkv.LIB_PATH), "libpkv_probe.so"))
+    for n in names:
+        assert hasattr(lib, n), n
 
 
 @pytest.mark.parametrize("dt", [0, 1, 2, 3, 4, 5, 6])
