@@ -46,6 +46,37 @@ same positions qualifies):
 * A cached block freed to count zero keeps its key on the free queue and
   leaves the cache when the queue hands it out again (least recently freed
   first).  A reused free block is taken out of the queue.
+
+Radix-tree prefix cache, the alternative to the hash chain (bjdmk.com.cn
+article, §4.2: cached KV organised as a tree over token sequences, a new
+request takes the longest matching prefix - also one that ends inside a block
+- and the least recently used leaves are evicted first, so shared prefixes
+outlive the branches that use them).  A manager uses one of the two; a call
+of the other kind is refused (ERR_UNSUPPORTED).  With paged storage a tree
+node is one full prompt block: the B token ids it holds, under the node of
+the block before it (the root for block 0).  The rules fixed here:
+
+* Matching walks from the root through children whose B tokens equal the
+  prompt's next block, while the whole block lies before the last prompt
+  token (that token is always computed, as above).  In the first block not
+  matched whole, the child sharing the longest run of leading tokens with the
+  prompt (capped at the last prompt token; the earliest inserted child among
+  equals) gives a partial match of l tokens: the new sequence takes a fresh
+  block and reports the pair (that child, fresh block) for the caller to
+  copy before it computes the rest, so the copy carries the l matched
+  tokens' K/V.  Cached tokens = B * (blocks matched whole) + l.
+* Capacity: the free queue plus every cached block nobody references (all
+  of them can be evicted, leaves first); the blocks matched (and the partial
+  source, held during the call) are not counted.  All or nothing, as above.
+* Fresh blocks come from the free queue (uncached blocks only) while it has
+  any, else by evicting the cached, unreferenced leaf used longest ago (then
+  the deeper, then the lower block id).  Using a block = being matched, or
+  dropping to count zero in free_seq; each free_seq and each radix call is
+  one tick of the clock.
+* The prompt's full fresh blocks are inserted in order as a chain under the
+  last matched block; a block whose tokens a sibling already holds (only the
+  last full block, when the last token cut its match short) and the blocks
+  after it are not inserted.
 """
 
 from __future__ import annotations
@@ -76,9 +107,39 @@ class BlockManagerModel:
         self.block_key: dict[int, bytes] = {}    # block -> its key
         self.lookups = 0
         self.hits = 0
+        # radix tree: 0 no prefix cache used yet, 1 hash chain, 2 radix tree
+        self.mode = 0
+        self.node_parent: dict[int, int] = {}    # cached block -> block before it (ROOT for block 0)
+        self.node_tokens: dict[int, tuple] = {}
+        self.node_depth: dict[int, int] = {}
+        self.children: dict[int, list] = {self.ROOT: []}
+        self.last_use: dict[int, int] = {}
+        self.clock = 0
+        self.radix_lookups = 0
+        self.radix_hits = 0
+
+    ROOT = -1
 
     # ------------------------------------------------------------ helpers
+    def _available(self) -> int:
+        """Blocks a request may obtain: the free queue, and in radix mode the
+        cached blocks nobody references."""
+        extra = sum(1 for b in self.node_parent if self.ref[b] == 0) if self.mode == 2 else 0
+        return len(self.free) + extra
+
+    def _evict(self) -> int:
+        leaves = [b for b in self.node_parent if self.ref[b] == 0 and not self.children[b]]
+        b = min(leaves, key=lambda x: (self.last_use[x], -self.node_depth[x], x))
+        self.children[self.node_parent[b]].remove(b)
+        for d in (self.node_parent, self.node_tokens, self.node_depth, self.children, self.last_use):
+            del d[b]
+        return b
+
     def _take(self) -> int:
+        if self.mode == 2 and not self.free:
+            b = self._evict()
+            self.ref[b] = 1
+            return b
         b = self.free.popleft()
         self.ref[b] = 1
         if b in self.block_key:                  # evicted: its content is about to change
@@ -90,7 +151,7 @@ class BlockManagerModel:
         if seq in self.tables or ctx_len < 0:
             return ERR_INVALID
         need = -(-ctx_len // self.B)
-        if need > len(self.free):
+        if need > self._available():
             self.failed_allocs += 1
             return ERR_OUT_OF_BLOCKS
         self.tables[seq] = [self._take() for _ in range(need)]
@@ -107,6 +168,8 @@ class BlockManagerModel:
         tokens = [int(t) for t in tokens]
         if seq in self.tables:
             return ERR_INVALID, 0
+        if self.mode == 2:
+            return ERR_UNSUPPORTED, 0
         B = self.B
         n = len(tokens)
         full, total = n // B, -(-n // B)
@@ -125,6 +188,7 @@ class BlockManagerModel:
         if total - matched > len(self.free) - matched_free:
             self.failed_allocs += 1
             return ERR_OUT_OF_BLOCKS, 0
+        self.mode = 1
         self.lookups += eligible
         self.hits += matched
         table = []
@@ -149,6 +213,74 @@ class BlockManagerModel:
 
     def prefix_stats(self):
         return self.lookups, self.hits, len(self.cache)
+
+    def add_seq_radix(self, seq: int, tokens):
+        """Returns (status, cached tokens, copy pair (src, dst) or None)."""
+        tokens = [int(t) for t in tokens]
+        if seq in self.tables:
+            return ERR_INVALID, 0, None
+        if self.mode == 1:
+            return ERR_UNSUPPORTED, 0, None
+        B = self.B
+        n = len(tokens)
+        full, total = n // B, -(-n // B)
+        last = n - 1 if n > 0 else 0            # tokens that may be reused
+        node, path = self.ROOT, []
+        while (len(path) + 1) * B <= last:
+            blk = tuple(tokens[len(path) * B:(len(path) + 1) * B])
+            nxt = next((c for c in self.children[node] if self.node_tokens[c] == blk), None)
+            if nxt is None:
+                break
+            path.append(nxt)
+            node = nxt
+        i = len(path)
+        lim = min(B, last - i * B)
+        src, l = -1, 0
+        for c in self.children[node] if lim > 0 else []:
+            t = self.node_tokens[c]
+            k = 0
+            while k < lim and t[k] == tokens[i * B + k]:
+                k += 1
+            if k > l:
+                src, l = c, k
+        pinned = sum(1 for b in path if self.ref[b] == 0) + (1 if src >= 0 and self.ref[src] == 0 else 0)
+        if total - i > self._available() - pinned:
+            self.failed_allocs += 1
+            return ERR_OUT_OF_BLOCKS, 0, None
+        self.mode = 2
+        self.clock += 1
+        for b in path + ([src] if src >= 0 else []):
+            self.ref[b] += 1
+            self.last_use[b] = self.clock
+        table = list(path)
+        parent, insert = node, True
+        for k in range(i, total):
+            b = self._take()
+            table.append(b)
+            if insert and k < full:
+                blk = tuple(tokens[k * B:(k + 1) * B])
+                if any(self.node_tokens[c] == blk for c in self.children[parent]):
+                    insert = False
+                    continue
+                self.node_parent[b] = parent
+                self.node_tokens[b] = blk
+                self.node_depth[b] = k
+                self.children[parent].append(b)
+                self.children[b] = []
+                self.last_use[b] = self.clock
+                parent = b
+        if src >= 0:
+            self.ref[src] -= 1                    # held only while the call took blocks
+        self.tables[seq] = table
+        self.ctx[seq] = n
+        self.radix_lookups += last
+        self.radix_hits += i * B + l
+        return OK, i * B + l, ((src, table[i]) if src >= 0 else None)
+
+    def radix_stats(self):
+        """(lookup tokens, hit tokens, cached blocks, cached blocks nobody references)."""
+        idle = sum(1 for b in self.node_parent if self.ref[b] == 0)
+        return self.radix_lookups, self.radix_hits, len(self.node_parent), idle
 
     def fork(self, parent: int, child: int) -> int:
         if parent not in self.tables or child in self.tables:
@@ -176,7 +308,7 @@ class BlockManagerModel:
                 if self.ref[last] + ref_delta.get(last, 0) > 1:
                     need += 1
                     ref_delta[last] = ref_delta.get(last, 0) - 1
-        if need > len(self.free):
+        if need > self._available():
             self.failed_allocs += 1
             return ERR_OUT_OF_BLOCKS, [], []
         slots, pairs = [], []
@@ -199,10 +331,14 @@ class BlockManagerModel:
     def free_seq(self, seq: int) -> int:
         if seq not in self.tables:
             return ERR_INVALID
+        self.clock += 1
         for b in self.tables.pop(seq):
             self.ref[b] -= 1
             if self.ref[b] == 0:
-                self.free.append(b)
+                if b in self.node_parent:           # stays cached: evictable from now on
+                    self.last_use[b] = self.clock
+                else:
+                    self.free.append(b)
         del self.ctx[seq]
         return OK
 
@@ -213,4 +349,4 @@ class BlockManagerModel:
         return tab + [0] * (width - len(tab))
 
     def stats(self):
-        return self.num_blocks - len(self.free), self.num_blocks, self.failed_allocs
+        return self.num_blocks - self._available(), self.num_blocks, self.failed_allocs

@@ -4,7 +4,8 @@ Each case monkeypatches one plausible slip into the oracle and re-runs a pin
 that should then fail: a transposed grouping, a slot off by one, a dropped
 softmax scale, a wrong e5m2 exponent bias, a window one position too wide,
 per-channel scales read with the dims reversed, a mixed-granularity V read
-with the K channel scales.
+with the K channel scales, a radix-tree partial match without its copy, an
+eviction of the most recently used leaf, an eviction of an inner block.
 """
 
 import numpy as np
@@ -139,3 +140,48 @@ def test_mixed_granularity_v_read_with_a_k_scale_is_caught(monkeypatch):
     monkeypatch.setattr(att, "_dequant_fixed_scales", bad)
     assert _fails(ti.test_int8_per_channel_with_equal_v_scales_is_the_mixed_granularity)
     assert _fails(ti.test_mixed_one_token_context_returns_v_code_times_v_scale)
+
+
+def test_radix_partial_match_without_its_copy_is_caught(monkeypatch):
+    from oracle.block_manager import BlockManagerModel
+    from tests import test_oracle_radix as tr
+    orig = BlockManagerModel.add_seq_radix
+
+    def no_copy(self, seq, tokens):
+        st, cached, pair = orig(self, seq, tokens)
+        return st, cached, None                  # the copy of the partly matched block is lost
+    monkeypatch.setattr(BlockManagerModel, "add_seq_radix", no_copy)
+    assert _fails(lambda: tr.test_pages_example_shares_six_tokens(4))
+
+
+def test_radix_most_recently_used_eviction_is_caught(monkeypatch):
+    from oracle.block_manager import BlockManagerModel
+    from tests import test_oracle_radix as tr
+
+    def evict_mru(self):
+        leaves = [b for b in self.node_parent if self.ref[b] == 0 and not self.children[b]]
+        b = max(leaves, key=lambda x: (self.last_use[x], self.node_depth[x], -x))
+        self.children[self.node_parent[b]].remove(b)
+        for d in (self.node_parent, self.node_tokens, self.node_depth, self.children, self.last_use):
+            del d[b]
+        return b
+    monkeypatch.setattr(BlockManagerModel, "_evict", evict_mru)
+    assert _fails(tr.test_lru_leaves_go_first_and_shared_prefix_survives)
+
+
+def test_radix_eviction_of_an_inner_block_is_caught(monkeypatch):
+    from oracle.block_manager import BlockManagerModel
+    from tests import test_oracle_radix as tr
+
+    def evict_any(self):
+        # the leaf condition forgotten: the shallowest idle block goes, and
+        # its cached children keep pointing at a block that now holds
+        # another sequence's tokens
+        idle = [b for b in self.node_parent if self.ref[b] == 0]
+        b = min(idle, key=lambda x: (self.last_use[x], self.node_depth[x], x))
+        self.children[self.node_parent[b]].remove(b)
+        for d in (self.node_parent, self.node_tokens, self.node_depth, self.last_use):
+            del d[b]
+        return b
+    monkeypatch.setattr(BlockManagerModel, "_evict", evict_any)
+    assert _fails(lambda: [tr.test_random_walk_under_eviction(2, s) for s in range(4)])
