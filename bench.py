@@ -98,6 +98,8 @@ def parse():
     ap.add_argument("--prefix-cache", type=int, default=0,
                     help="host only: N requests sharing a 1500-token system prompt through the block manager's "
                          "prefix cache; report microseconds per request and the prefill tokens it saves")
+    ap.add_argument("--prefix-kind", default="hash", choices=["hash", "radix"],
+                    help="with --prefix-cache: the SHA-256 block chain or the radix tree over token ids")
     ap.add_argument("--swap", type=int, default=0,
                     help="instead of the decode step: swap N blocks of the 70B-shaped pool out to pinned host "
                          "memory and back (swap_blocks), and report GB/s each way")
@@ -343,7 +345,10 @@ def prefix_cache_bench(args):
     """The shared-system-prompt scenario of the bjdmk.com.cn article (§3.2:
     a 1500-token system prompt, 200 concurrent requests): every request is
     that prompt plus 64..512 private tokens; time kv_bm_add_seq_tokens per
-    request (SHA-256 keys over every full block, lookups, allocation)."""
+    request (SHA-256 keys over every full block, lookups, allocation), or
+    kv_bm_add_seq_radix (the walk down the radix tree, which also reuses the
+    system prompt's last 12 tokens through a block copy) with
+    --prefix-kind radix."""
     import paged_kv_cache_436_amd as pkv
 
     n = args.prefix_cache
@@ -353,28 +358,40 @@ def prefix_cache_bench(args):
     prompts = [np.asarray(system + rng.integers(0, 32000, size=int(rng.integers(64, 513))).tolist(), np.int32)
                for _ in range(n)]
     nb = sum(-(-len(p) // B) for p in prompts) + 8
-    times, saved = [], 0
+    radix = args.prefix_kind == "radix"
+    times, saved, copies = [], 0, 0
     for rep in range(args.warmup + args.steps):
         bm = pkv.BlockManager(nb, B)
         t0 = time.perf_counter()
-        cached = [bm.add_seq_tokens(i, p) for i, p in enumerate(prompts)]
+        if radix:
+            res = [bm.add_seq_radix(i, p) for i, p in enumerate(prompts)]
+            cached = [c for c, _ in res]
+        else:
+            cached = [bm.add_seq_tokens(i, p) for i, p in enumerate(prompts)]
         t1 = time.perf_counter()
         if rep >= args.warmup:
             times.append(t1 - t0)
             saved = sum(cached)
-        lookups, hits, keys = bm.prefix_stats()
+            copies = sum(1 for _, pr in res if pr is not None) if radix else 0
+        if radix:
+            lookups, hits, keys, _ = bm.radix_stats()
+        else:
+            lookups, hits, keys = bm.prefix_stats()
         used = bm.stats()[0]
         bm.close()
     per = float(np.median(times)) / n
     total_tokens = sum(len(p) for p in prompts)
-    res = {"metric": "prefix-cache admission: microseconds per request (host)", "value": round(per * 1e6, 2),
+    res = {"metric": f"prefix-cache admission ({args.prefix_kind}): microseconds per request (host)",
+           "value": round(per * 1e6, 2),
            "unit": "us/request", "n_gpus": 0, "steps": args.steps, "warmup": args.warmup,
            "higher_is_better": False, "dtype": "int32", "data": "synthetic",
            "config": {"workload": f"{n} requests = one 1500-token system prompt + 64..512 private tokens, "
                                   "block 16", "prompt_tokens": total_tokens},
            "prefill_tokens_reused": saved, "prefill_fraction_reused": round(saved / total_tokens, 4),
-           "block_lookups": lookups, "block_hits": hits, "blocks_used": used,
-           "blocks_without_sharing": nb - 8}
+           ("token_lookups" if radix else "block_lookups"): lookups, ("token_hits" if radix else "block_hits"): hits,
+           "blocks_used": used, "blocks_without_sharing": nb - 8}
+    if radix:
+        res["partial_block_copies"] = copies
     print(json.dumps(res), flush=True)
 
 

@@ -508,6 +508,50 @@ pkv_status kv_bm_prefix_stats(const pkv_bm* bm, int64_t* lookups, int64_t* hits,
  * library's choice). */
 pkv_status kv_bm_block_key(const uint8_t* parent, const int32_t* tokens, int32_t n, uint8_t* out);
 
+/* Radix-tree prefix cache, the alternative to the hash chain above ([BJD]
+ * §4.2: the cached KV forms a tree over token sequences; a request reuses
+ * its longest matching prefix, also a partial one, and computes and inserts
+ * the rest; under memory pressure the least recently used leaves go first,
+ * so shared prefixes outlive the branches using them).  A manager uses one
+ * of the two caches: the first successful call picks it, and a call of the
+ * other kind then returns PKV_ERR_UNSUPPORTED.  With paged storage a node is
+ * a full prompt block: its B token ids, under the node of the block before
+ * it (block 0 under the root).  Rules fixed by this library:
+ *  - matching walks from the root through the child whose B tokens equal
+ *    the prompt's next block, while that block lies wholly before the
+ *    prompt's last token (which is always computed, as above); in the first
+ *    block not matched whole, the child sharing the longest run of leading
+ *    tokens (capped at the last token; the earliest inserted among equals)
+ *    gives l > 0 further tokens: the sequence gets a fresh block there and
+ *    copy_pair = (that child, the fresh block), which the caller copies
+ *    (copy_blocks) before computing tokens from *cached_tokens on, so the
+ *    copy carries the l matched tokens' K/V; else copy_pair = (-1, -1);
+ *    *cached_tokens = B * (whole blocks matched) + l < n;
+ *  - fresh blocks come from the free FIFO (blocks outside the tree) while it
+ *    has any, else by evicting the tree leaf nobody references that was used
+ *    longest ago (then the deeper, then the lower block id); a block is used
+ *    when matched (whole or as the copy source) and when a kv_bm_free_seq
+ *    drops its count to 0 - a tree block at count 0 stays in the tree, its
+ *    K/V intact, until evicted; every kv_bm_free_seq and every successful
+ *    kv_bm_add_seq_radix is one tick of that clock;
+ *  - the prompt's fresh full blocks are inserted in order as a chain under
+ *    the last block matched whole; a block whose tokens a sibling already
+ *    holds (only when the last token cut a whole match short) and the blocks
+ *    after it are not inserted; partial last blocks and appended tokens are
+ *    never cached;
+ *  - all or nothing: PKV_ERR_OUT_OF_BLOCKS with no change when the free FIFO
+ *    and the evictable tree blocks (those nobody references, less the ones
+ *    this request matches) cannot cover the fresh blocks;
+ *  - kv_bm_stats counts tree blocks nobody references as free.
+ * tokens: host int32 [n]; copy_pair: host int64 [2], required. */
+pkv_status kv_bm_add_seq_radix(pkv_bm* bm, int32_t seq, const int32_t* tokens, int32_t n,
+                               int32_t* cached_tokens, int64_t* copy_pair);
+/* Tokens eligible for reuse and tokens reused by kv_bm_add_seq_radix so far
+ * ([KVP] §六 hit rate, per token), the blocks in the tree, and those of them
+ * nobody references (evictable). */
+pkv_status kv_bm_radix_stats(const pkv_bm* bm, int64_t* lookup_tokens, int64_t* hit_tokens, int32_t* cached_blocks,
+                             int32_t* idle_blocks);
+
 #ifdef __cplusplus
 }
 #endif

@@ -114,6 +114,8 @@ SIGNATURES = {
     "kv_bm_add_seq_tokens": (_I32, [_P, _I32, _I32P, _I32, _I32P]),
     "kv_bm_prefix_stats": (_I32, [_P, _I64P, _I64P, _I32P]),
     "kv_bm_block_key": (_I32, [_P, _I32P, _I32, _P]),
+    "kv_bm_add_seq_radix": (_I32, [_P, _I32, _I32P, _I32, _I32P, _I64P]),
+    "kv_bm_radix_stats": (_I32, [_P, _I64P, _I64P, _I32P, _I32P]),
 }
 for _name, (_res, _args) in SIGNATURES.items():
     _fn = getattr(_lib, _name)
@@ -403,6 +405,24 @@ class BlockManager:
         cached = ctypes.c_int32(0)
         _check(_lib.kv_bm_add_seq_tokens(self._h, seq, _np_ptr(t, ctypes.c_int32), t.size, ctypes.byref(cached)))
         return cached.value
+
+    def add_seq_radix(self, seq: int, tokens):
+        """New sequence holding the prompt ``tokens``, reusing its longest
+        prefix found in the radix tree; returns (cached tokens, copy pair
+        (src, dst) to copy before computing the rest, or None)."""
+        t = np.ascontiguousarray(tokens, dtype=np.int32)
+        cached = ctypes.c_int32(0)
+        pair = np.full(2, -1, dtype=np.int64)
+        _check(_lib.kv_bm_add_seq_radix(self._h, seq, _np_ptr(t, ctypes.c_int32), t.size, ctypes.byref(cached),
+                                        _np_ptr(pair, ctypes.c_int64)))
+        return cached.value, (None if pair[0] < 0 else (int(pair[0]), int(pair[1])))
+
+    def radix_stats(self):
+        """(lookup tokens, hit tokens, blocks in the tree, of them unreferenced)."""
+        lk, hit, nodes, idle = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.kv_bm_radix_stats(self._h, ctypes.byref(lk), ctypes.byref(hit), ctypes.byref(nodes),
+                                      ctypes.byref(idle)))
+        return lk.value, hit.value, nodes.value, idle.value
 
     def prefix_stats(self):
         """(full-block lookups, hits, cached keys)."""

@@ -10,10 +10,17 @@
 // key hashes its tokens and the key of the block before it, and a request
 // whose prompt starts with a cached run of blocks reuses them (same article,
 // §4.1 prefix caching; §4.3: only an exact, position-aligned prefix is
-// reused).  The tie-break rules that make tables, slots and copy pairs unique
-// are stated with the declarations in pkv.h.
+// reused).  Alternatively the cached prompt blocks form a radix tree over
+// their token ids (same article, §4.2): a request takes the longest matching
+// prefix, also one ending inside a block (that block is copied), and the
+// least recently used leaves are evicted first.  The tie-break rules that
+// make tables, slots and copy pairs unique are stated with the declarations
+// in pkv.h.
+#include <algorithm>
 #include <deque>
 #include <new>
+#include <set>
+#include <tuple>
 #include <unordered_map>
 #include <utility>
 #include <vector>
@@ -54,12 +61,78 @@ struct pkv_bm {
   std::vector<uint8_t> keyed;
   int64_t lookups = 0, hits = 0;
 
+  // which prefix cache is in use: none yet, the hash chain, or the radix tree
+  enum Mode { kNone, kHash, kRadix } mode = kNone;
+  // radix tree: a node is a cached full prompt block.  parent: the node of
+  // the block before it (kRoot for block 0), kNoNode for blocks outside the
+  // tree; children in insertion order; the B token ids of node b at
+  // tokens[b * B ..).  In radix mode num_free also counts the cached blocks
+  // nobody references (idle), which eviction hands out leaves first, least
+  // recently used first.
+  static constexpr int32_t kRoot = -1, kNoNode = -2;
+  std::vector<int32_t> parent;
+  std::vector<std::vector<int32_t>> children;
+  std::vector<int32_t> root_children;
+  std::vector<int32_t> tokens;
+  std::vector<int64_t> last_use;
+  std::vector<int32_t> depth;
+  std::set<std::tuple<int64_t, int32_t, int32_t>> evictable;   // (last use, -depth, block) of idle leaves
+  int64_t idle = 0;
+  int64_t clock = 0;
+  int64_t radix_lookups = 0, radix_hits = 0;
+
+  bool in_tree(int32_t b) const { return !parent.empty() && parent[(size_t)b] != kNoNode; }
+  std::vector<int32_t>& kids(int32_t b) { return b == kRoot ? root_children : children[(size_t)b]; }
+  std::tuple<int64_t, int32_t, int32_t> ev_key(int32_t b) const {
+    return {last_use[(size_t)b], -depth[(size_t)b], b};
+  }
+  void radix_arrays() {
+    if (parent.empty()) {
+      parent.assign((size_t)num_blocks, kNoNode);
+      children.resize((size_t)num_blocks);
+      tokens.resize((size_t)num_blocks * (size_t)block_size);
+      last_use.assign((size_t)num_blocks, 0);
+      depth.assign((size_t)num_blocks, 0);
+    }
+  }
+  // a tree node that nobody references becomes idle (and evictable once it
+  // is a leaf)
+  void make_idle(int32_t b) {
+    last_use[(size_t)b] = clock;
+    ++idle;
+    ++num_free;
+    if (children[(size_t)b].empty()) evictable.insert(ev_key(b));
+  }
+  // an idle node gains a reference
+  void wake(int32_t b) {
+    if (children[(size_t)b].empty()) evictable.erase(ev_key(b));
+    --idle;
+    --num_free;
+  }
+  // remove the least recently used idle leaf from the tree; its parent may
+  // become an idle leaf in turn
+  int32_t evict() {
+    const int32_t b = std::get<2>(*evictable.begin());
+    evictable.erase(evictable.begin());
+    const int32_t pa = parent[(size_t)b];
+    std::vector<int32_t>& sib = kids(pa);
+    sib.erase(std::find(sib.begin(), sib.end(), b));
+    if (pa != kRoot && sib.empty() && ref[(size_t)pa] == 0) evictable.insert(ev_key(pa));
+    parent[(size_t)b] = kNoNode;
+    --idle;
+    --num_free;
+    return b;
+  }
+
   void push_free(int32_t b) {
     free_list.emplace_back(b, ++gen[(size_t)b]);
     ++num_free;
   }
   void release(int32_t b) {
-    if (--ref[(size_t)b] == 0) push_free(b);
+    if (--ref[(size_t)b] == 0) {
+      if (in_tree(b)) make_idle(b);
+      else push_free(b);
+    }
   }
   void unkey(int32_t b) {
     if (keyed[(size_t)b]) {
@@ -67,9 +140,15 @@ struct pkv_bm {
       keyed[(size_t)b] = 0;
     }
   }
-  // The front live free block, now referenced once; it leaves the cache
-  // (its content is about to be overwritten).
+  // The front live free block (radix mode: an evicted idle leaf once the
+  // free list holds none), now referenced once; it leaves the cache (its
+  // content is about to be overwritten).
   int32_t take() {
+    if (mode == kRadix && num_free == idle) {
+      const int32_t b = evict();
+      ref[(size_t)b] = 1;
+      return b;
+    }
     while (true) {
       const auto e = free_list.front();
       free_list.pop_front();
@@ -240,6 +319,7 @@ pkv_status kv_bm_free_seq(pkv_bm* bm, int32_t seq) {
     set_error("sequence %d does not exist", seq);
     return PKV_ERR_INVALID;
   }
+  ++bm->clock;
   for (int32_t b : it->second.table) bm->release(b);
   bm->seqs.erase(it);
   clear_error();
@@ -315,6 +395,8 @@ pkv_status kv_bm_add_seq_tokens(pkv_bm* bm, int32_t seq, const int32_t* tokens, 
     set_error("sequence %d already exists", seq);
     return PKV_ERR_INVALID;
   }
+  if (bm->mode == pkv_bm::kRadix)
+    return fail(PKV_ERR_UNSUPPORTED, "this block manager's prefix cache is the radix tree (kv_bm_add_seq_radix)");
   const int32_t B = bm->block_size;
   const int64_t full = n / B;
   const int64_t total = ((int64_t)n + B - 1) / B;
@@ -340,6 +422,7 @@ pkv_status kv_bm_add_seq_tokens(pkv_bm* bm, int32_t seq, const int32_t* tokens, 
               (long long)(bm->num_free - matched_free));
     return PKV_ERR_OUT_OF_BLOCKS;
   }
+  bm->mode = pkv_bm::kHash;
   bm->lookups += eligible;
   bm->hits += matched;
   pkv_bm::Seq s;
@@ -373,6 +456,118 @@ pkv_status kv_bm_prefix_stats(const pkv_bm* bm, int64_t* lookups, int64_t* hits,
   if (lookups) *lookups = bm->lookups;
   if (hits) *hits = bm->hits;
   if (cached_blocks) *cached_blocks = (int32_t)bm->cache.size();
+  return PKV_OK;
+}
+
+pkv_status kv_bm_add_seq_radix(pkv_bm* bm, int32_t seq, const int32_t* tokens, int32_t n,
+                               int32_t* cached_tokens, int64_t* copy_pair) {
+  if (!bm) return fail(PKV_ERR_INVALID, "bm is NULL");
+  if (n < 0 || (n > 0 && !tokens) || !copy_pair) return fail(PKV_ERR_INVALID, "bad token arguments");
+  if (bm->seqs.count(seq)) {
+    set_error("sequence %d already exists", seq);
+    return PKV_ERR_INVALID;
+  }
+  if (bm->mode == pkv_bm::kHash)
+    return fail(PKV_ERR_UNSUPPORTED, "this block manager's prefix cache is the hash chain (kv_bm_add_seq_tokens)");
+  bm->radix_arrays();
+  const int32_t B = bm->block_size;
+  const int64_t full = n / B;
+  const int64_t total = ((int64_t)n + B - 1) / B;
+  const int64_t last = n > 0 ? n - 1 : 0;   // tokens that may be reused (the last one is always computed)
+  auto same = [&](int32_t b, int64_t blk) {
+    return std::equal(tokens + blk * B, tokens + (blk + 1) * B, bm->tokens.begin() + (int64_t)b * B);
+  };
+  // whole blocks along the tree
+  int32_t node = pkv_bm::kRoot;
+  std::vector<int32_t> path;
+  while ((int64_t)(path.size() + 1) * B <= last) {
+    const int64_t blk = (int64_t)path.size();
+    int32_t nxt = -1;
+    for (int32_t c : bm->kids(node))
+      if (same(c, blk)) {
+        nxt = c;
+        break;
+      }
+    if (nxt < 0) break;
+    path.push_back(nxt);
+    node = nxt;
+  }
+  const int64_t i = (int64_t)path.size();
+  // the child sharing the most leading tokens of the next block
+  const int64_t lim = std::min<int64_t>(B, last - i * B);
+  int32_t src = -1;
+  int64_t l = 0;
+  if (lim > 0) {
+    for (int32_t c : bm->kids(node)) {
+      const int32_t* t = bm->tokens.data() + (int64_t)c * B;
+      int64_t k = 0;
+      while (k < lim && t[k] == tokens[i * B + k]) ++k;
+      if (k > l) {
+        src = c;
+        l = k;
+      }
+    }
+  }
+  int64_t pinned = src >= 0 && bm->ref[(size_t)src] == 0 ? 1 : 0;
+  for (int32_t b : path) pinned += bm->ref[(size_t)b] == 0 ? 1 : 0;
+  if (total - i > bm->num_free - pinned) {
+    bm->failed_allocs++;
+    set_error("sequence %d needs %lld fresh blocks, %lld obtainable", seq, (long long)(total - i),
+              (long long)(bm->num_free - pinned));
+    return PKV_ERR_OUT_OF_BLOCKS;
+  }
+  bm->mode = pkv_bm::kRadix;
+  ++bm->clock;
+  std::vector<int32_t> used = path;
+  if (src >= 0) used.push_back(src);
+  for (int32_t b : used) {
+    if (bm->ref[(size_t)b] == 0) bm->wake(b);
+    bm->ref[(size_t)b]++;
+    bm->last_use[(size_t)b] = bm->clock;
+  }
+  pkv_bm::Seq s;
+  s.table = path;
+  s.table.reserve((size_t)total);
+  int32_t par = node;
+  bool insert = true;
+  for (int64_t k = i; k < total; ++k) {
+    const int32_t b = bm->take();
+    s.table.push_back(b);
+    if (!insert || k >= full) continue;
+    bool dup = false;
+    for (int32_t c : bm->kids(par)) dup = dup || same(c, k);
+    if (dup) {   // a sibling holds these tokens: the chain stops here
+      insert = false;
+      continue;
+    }
+    bm->parent[(size_t)b] = par;
+    bm->kids(par).push_back(b);
+    std::copy(tokens + k * B, tokens + (k + 1) * B, bm->tokens.begin() + (int64_t)b * B);
+    bm->depth[(size_t)b] = (int32_t)k;
+    bm->last_use[(size_t)b] = bm->clock;
+    par = b;
+  }
+  if (src >= 0 && --bm->ref[(size_t)src] == 0) bm->make_idle(src);   // held only while blocks were taken
+  copy_pair[0] = src >= 0 ? src : -1;
+  copy_pair[1] = src >= 0 ? s.table[(size_t)i] : -1;
+  s.len = n;
+  bm->seqs.emplace(seq, std::move(s));
+  bm->radix_lookups += last;
+  bm->radix_hits += i * B + l;
+  if (cached_tokens) *cached_tokens = (int32_t)(i * B + l);
+  clear_error();
+  return PKV_OK;
+}
+
+pkv_status kv_bm_radix_stats(const pkv_bm* bm, int64_t* lookup_tokens, int64_t* hit_tokens, int32_t* cached_blocks,
+                             int32_t* idle_blocks) {
+  if (!bm) return fail(PKV_ERR_INVALID, "bm is NULL");
+  int32_t nodes = 0;
+  for (size_t b = 0; b < bm->parent.size(); ++b) nodes += bm->parent[b] != pkv_bm::kNoNode ? 1 : 0;
+  if (lookup_tokens) *lookup_tokens = bm->radix_lookups;
+  if (hit_tokens) *hit_tokens = bm->radix_hits;
+  if (cached_blocks) *cached_blocks = nodes;
+  if (idle_blocks) *idle_blocks = (int32_t)bm->idle;
   return PKV_OK;
 }
 

@@ -4,13 +4,15 @@
 // every operation what pkv.h promises: reference counts equal the number of
 // tables naming a block, tables hold ceil(len / B) blocks, an append's slot
 // is table[pos / B] * B + pos % B, a copy-on-write pair copies a block that
-// was shared into one that was free, a refused call changes nothing.
+// was shared into one that was free, a refused call changes nothing; and the
+// radix-tree prefix cache with a simulated pool memory (below).
 // tests/test_host_sanitize.py builds it with AddressSanitizer and
 // UndefinedBehaviorSanitizer together with pool.cpp and block_manager.cpp.
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <iterator>
 #include <map>
 #include <set>
 #include <vector>
@@ -283,6 +285,115 @@ void create_errors_and_keys() {
   kv_bm_destroy(nullptr);
 }
 
+// The radix-tree prefix cache on a small pool (eviction runs often), with a
+// simulated pool memory: each slot holds the token id whose K/V it stores.
+// A request writes its tokens from the cached count on after copying its
+// pair, an append writes one token after its copy-on-write pairs, and every
+// live sequence must read back its own tokens after every call.
+void radix_walk(uint64_t seed) {
+  const int NB = 40, width = 64;
+  Lcg r{seed * 7 + 1};
+  const int sizes[] = {1, 2, 3, 4, 8, 16};
+  const int B = sizes[seed % 6];
+  pkv_bm* bm = nullptr;
+  CHECK(kv_bm_create(NB, B, nullptr, &bm) == PKV_OK);
+  std::vector<std::vector<int32_t>> mem((size_t)NB, std::vector<int32_t>((size_t)B, -1));
+  std::map<int32_t, std::vector<int32_t>> hist;
+  std::set<int32_t> live;
+  std::vector<std::vector<int32_t>> stems(4);
+  for (auto& st : stems) {
+    st.resize((size_t)r.below(5 * B + 2));
+    for (auto& t : st) t = r.below(3);
+  }
+  int32_t next_id = 0;
+  int64_t n_partial = 0, n_hit_tokens = 0;
+  auto slot_of = [&](const View& v, int32_t s, int32_t pos) -> int32_t& {
+    return mem[(size_t)v.tab.at(s)[(size_t)(pos / B)]][(size_t)(pos % B)];
+  };
+  for (int it = 0; it < 3000; ++it) {
+    const int op = r.below(10);
+    if (op < 4) {
+      const auto& st = stems[(size_t)r.below(4)];
+      std::vector<int32_t> toks(st.begin(), st.begin() + r.below((int)st.size() + 1));
+      for (int k = r.below(2 * B + 2); k > 0; --k) toks.push_back(r.below(3));
+      int32_t cached = -1;
+      int64_t pair[2] = {-7, -7};
+      const pkv_status s = kv_bm_add_seq_radix(bm, next_id, toks.data(), (int32_t)toks.size(), &cached, pair);
+      CHECK(s == PKV_OK || s == PKV_ERR_OUT_OF_BLOCKS);
+      if (s == PKV_OK) {
+        live.insert(next_id);
+        const View v = snapshot(bm, live, width);
+        CHECK(cached >= 0 && (toks.empty() ? cached == 0 : cached < (int32_t)toks.size()));
+        CHECK((pair[0] >= 0) == (cached % B != 0));
+        if (pair[0] >= 0) {
+          CHECK(pair[0] < NB && pair[1] == v.tab.at(next_id)[(size_t)(cached / B)]);
+          mem[(size_t)pair[1]] = mem[(size_t)pair[0]];
+          ++n_partial;
+        }
+        for (int32_t p = 0; p < (int32_t)toks.size(); ++p) {
+          int32_t& m = slot_of(v, next_id, p);
+          if (p < cached) CHECK(m == toks[(size_t)p]);
+          else m = toks[(size_t)p];
+        }
+        hist[next_id] = toks;
+        n_hit_tokens += cached;
+      }
+      ++next_id;
+    } else if (op < 6 && !live.empty()) {
+      std::vector<int32_t> seqs;
+      for (int32_t s : live)
+        if (r.below(2)) seqs.push_back(s);
+      if (seqs.empty()) continue;
+      std::vector<int64_t> slots(seqs.size()), pairs(2 * seqs.size());
+      int32_t np = -1;
+      const pkv_status st =
+          kv_bm_append(bm, seqs.data(), (int32_t)seqs.size(), slots.data(), pairs.data(), &np);
+      CHECK(st == PKV_OK || st == PKV_ERR_OUT_OF_BLOCKS);
+      if (st != PKV_OK) continue;
+      for (int32_t k = 0; k < np; ++k) mem[(size_t)pairs[(size_t)(2 * k + 1)]] = mem[(size_t)pairs[(size_t)(2 * k)]];
+      for (size_t k = 0; k < seqs.size(); ++k) {
+        const int32_t t = r.below(3);
+        mem[(size_t)(slots[k] / B)][(size_t)(slots[k] % B)] = t;
+        hist[seqs[k]].push_back(t);
+      }
+    } else if (op < 7 && !live.empty()) {
+      auto p = live.begin();
+      std::advance(p, r.below((int)live.size()));
+      CHECK(kv_bm_fork(bm, *p, next_id) == PKV_OK);
+      hist[next_id] = hist[*p];
+      live.insert(next_id++);
+    } else if (!live.empty()) {
+      auto p = live.begin();
+      std::advance(p, r.below((int)live.size()));
+      CHECK(kv_bm_free_seq(bm, *p) == PKV_OK);
+      hist.erase(*p);
+      live.erase(p);
+    }
+    const View v = snapshot(bm, live, width);
+    invariants(bm, v, NB, B, width);
+    for (const auto& [s, toks] : hist)
+      for (int32_t p = 0; p < (int32_t)toks.size(); ++p) CHECK(slot_of(v, s, p) == toks[(size_t)p]);
+    int64_t lookups = -1, hits = -1;
+    int32_t nodes = -1, idle = -1;
+    CHECK(kv_bm_radix_stats(bm, &lookups, &hits, &nodes, &idle) == PKV_OK);
+    CHECK(hits == n_hit_tokens && hits <= lookups && idle >= 0 && idle <= nodes && nodes <= NB);
+  }
+  // one prefix cache per manager; bad arguments
+  int32_t cached = 0;
+  int64_t pair[2];
+  const int32_t t3[] = {0, 1, 2};
+  CHECK(kv_bm_add_seq_tokens(bm, next_id, t3, 3, &cached) == PKV_ERR_UNSUPPORTED);
+  CHECK(kv_bm_add_seq_radix(bm, next_id, t3, 3, &cached, nullptr) == PKV_ERR_INVALID);
+  CHECK(kv_bm_add_seq_radix(bm, next_id, nullptr, 3, &cached, pair) == PKV_ERR_INVALID);
+  CHECK(kv_bm_add_seq_radix(nullptr, next_id, t3, 3, &cached, pair) == PKV_ERR_INVALID);
+  CHECK(kv_bm_radix_stats(nullptr, nullptr, nullptr, nullptr, nullptr) == PKV_ERR_INVALID);
+  CHECK(n_partial > 0 || B == 1);   // with one-token blocks every match is whole
+  std::printf("radix walk %llu: B %d, %lld partial matches, %lld cached tokens\n", (unsigned long long)seed, B,
+              (long long)n_partial, (long long)n_hit_tokens);
+  for (int32_t s : live) CHECK(kv_bm_free_seq(bm, s) == PKV_OK);
+  kv_bm_destroy(bm);
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -291,6 +402,7 @@ int main(int argc, char** argv) {
   validators();
   create_errors_and_keys();
   for (uint64_t k = 0; k < 4; ++k) block_manager_walk(seed + k);
+  for (uint64_t k = 0; k < 6; ++k) radix_walk(seed + k);
   std::printf("host api check passed\n");
   return 0;
 }

@@ -1,6 +1,7 @@
 """Prefix caching end to end on the GPU: a second request whose prompt starts
 with the first one's reuses its cached blocks, writes KV only past the
-reused prefix, and decodes to the oracle's output over the full prompt."""
+reused prefix, and decodes to the oracle's output over the full prompt; the radix-tree
+form also reuses a prefix that ends inside a block, through a block copy."""
 
 import numpy as np
 import pytest
@@ -134,6 +135,79 @@ def test_whole_prompt_hit_leaves_last_block_to_prefill_then_decodes():
     got_img = read_pool(pool)
     assert images_equal(got_img, img), first_diff(got_img, img)
     want = attention.paged_decode(q, img, 0, tables, ctx, scale)
+    mx, rel = errors(out.cpu().numpy(), want)
+    say(f"  decode: max_abs={mx:.3e} rel={rel:.3e}")
+    assert mx <= 1e-2 and rel <= 1e-3
+
+
+def test_radix_partial_block_hit_copies_then_prefills_the_rest():
+    """Radix-tree reuse that ends inside a block (bjdmk.com.cn article,
+    §4.2): the second prompt shares 263 tokens with the first (16 whole
+    blocks + 7 tokens of the 17th); it reuses the 16 blocks, copies the
+    first prompt's 17th block into its own fresh block (copy_blocks with the
+    pair the manager returned), writes K/V from position 263 on, and its
+    prefill of the remaining tokens and a decode step match the oracle, and
+    attention over its own full K/V."""
+    import torch
+    rng = np.random.default_rng(13700)
+    B, H, G, D, NB, W = 16, 2, 4, 128, 64, 24
+    hq = H * G
+    cfg = pkv.make_config(1, NB, B, H, D, pkv.PKV_KV_BF16)
+    pool = pkv.Pool(cfg)
+    pool.memory.fill_(255)
+    bm = pkv.BlockManager(NB, B, rng.permutation(NB))
+    shared = rng.integers(0, 1000, size=263).tolist()
+    prompts = [shared + [1001] + rng.integers(0, 1000, size=40).tolist(),
+               shared + [1002] + rng.integers(0, 1000, size=20).tolist()]
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
+    img = read_pool(pool)
+    kv = {}
+    for s, pr in enumerate(prompts):
+        cached, pair = bm.add_seq_radix(s, pr)
+        say(f"request {s}: {len(pr)} tokens, {cached} reused, copy {pair}")
+        n = len(pr)
+        tab, ctx = bm.block_tables([s], W)
+        if s:
+            assert cached == 263 and pair == (int(kv[0][2][16]), int(tab[0][16]))
+            assert (tab[0][:16] == kv[0][2][:16]).all()
+            pk = dev(np.asarray([pair], dtype=np.int64))
+            pkv.copy_blocks(pool, pk)
+            img = cache_ops.copy_blocks(img, np.asarray([pair], dtype=np.int64))
+        else:
+            assert (cached, pair) == (0, None)
+        k = workloads.to_bf16_bits(rng.standard_normal((n, H, D), dtype=np.float32))
+        v = workloads.to_bf16_bits(rng.standard_normal((n, H, D), dtype=np.float32))
+        if s:
+            k[:263], v[:263] = kv[0][0][:263], kv[0][1][:263]     # the shared tokens' K/V are request 0's
+        kv[s] = (k, v, tab[0].copy())
+        pos = np.arange(cached, n)
+        slots = tab[0][pos // B].astype(np.int64) * B + pos % B
+        pkv.reshape_and_cache(pool, 0, bf16_dev(k[cached:]), bf16_dev(v[cached:]), dev(slots))
+        img = cache_ops.reshape_and_cache(img, 0, k[cached:], v[cached:], slots)
+        got_img = read_pool(pool)
+        assert images_equal(got_img, img), first_diff(got_img, img)
+        m = n - cached
+        q = workloads.to_bf16_bits(rng.standard_normal((m, hq, D), dtype=np.float32))
+        qs = np.array([0, m], np.int32)
+        out = torch.full((m, hq, D), float("nan"), dtype=torch.float32, device="cuda")
+        pkv.paged_attn_prefill(out, bf16_dev(q), pool, 0, dev(tab), dev(ctx), dev(qs), scale, m)
+        torch.cuda.synchronize()
+        want = attention.paged_prefill(q, img, 0, tab, ctx, qs, scale)
+        mx, rel = errors(out.cpu().numpy(), want)
+        say(f"  prefill of {m} tokens: max_abs={mx:.3e} rel={rel:.3e}")
+        assert mx <= 1e-2 and rel <= 1e-3
+    # decode of both over the pool equals attention over each one's own K/V
+    tables, ctx = bm.block_tables([0, 1], W)
+    q = workloads.to_bf16_bits(rng.standard_normal((2, hq, D), dtype=np.float32))
+    out = torch.empty((2, hq, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(pkv.paged_attn_workspace_bytes(2, hq, D, W, B, 64), dtype=torch.uint8, device="cuda")
+    pkv.paged_attn_decode(out, bf16_dev(q), pool, 0, dev(tables), dev(ctx), scale, partition_size=64, workspace=ws)
+    torch.cuda.synchronize()
+    want = attention.paged_decode(q, img, 0, tables, ctx, scale)
+    for s in range(2):
+        ref = attention.attend(codecs.bf16_bits_to_f64(q[s]), codecs.bf16_bits_to_f64(kv[s][0]),
+                               codecs.bf16_bits_to_f64(kv[s][1]), scale)
+        assert np.max(np.abs(ref - want[s])) < 1e-12
     mx, rel = errors(out.cpu().numpy(), want)
     say(f"  decode: max_abs={mx:.3e} rel={rel:.3e}")
     assert mx <= 1e-2 and rel <= 1e-3
