@@ -323,7 +323,7 @@ struct SplitGeo {
   static constexpr bool TOK = KVT == PKV_KV_INT8;                  // per-(token, head) scales
   static constexpr bool CHAN = KVT == PKV_KV_INT8_CHANNEL || I4;   // K channel scales folded into q
   static constexpr int E = BF ? 2 : 1;            // bytes per stored element (INT4: half a byte)
-  static constexpr int CH = BF ? 1 : 2;           // 16-token chunks per step
+  static constexpr int CH = BF ? 1 : (I4 ? 4 : 2);   // 16-token chunks per step (8 KiB of K + V, 4 KiB for INT4)
   static constexpr int TS = 16 * CH;              // tokens per step
   static constexpr int LPC = I4 ? 1 : D * E / 64; // loads per chunk per lane, for K and for V
                                                   // (INT4: one load of D / 8 bytes)
@@ -454,11 +454,12 @@ __device__ __forceinline__ void issue_step(SplitBuf<D, KVT>& r, const SplitParam
     const float* kscb = nullptr;
     const float* vscb = nullptr;
     if constexpr (B >= 16) {
-      // the chunk lies in one block: entry h (B = 16 with 32-token steps) or
-      // the step's only entry at token offset t0 % B + 16 h
+      // the chunk lies in one block: the step's only entry at token offset
+      // t0 % B + 16 h, or (steps longer than a block, which start at a block
+      // boundary) entry 16 h / B at offset 16 h % B
       constexpr bool one = B >= GE::TS;
-      const uint32_t tok = one ? ((uint32_t)t0 % B) + 16u * h : 0u;
-      const uint32_t tile = (uint32_t)ph[one ? 0 : h] * (uint32_t)p.Hkv + (uint32_t)g;
+      const uint32_t tok = one ? ((uint32_t)t0 % B) + 16u * h : (16u * h) % B;
+      const uint32_t tile = (uint32_t)ph[one ? 0 : (16 * h) / B] * (uint32_t)p.Hkv + (uint32_t)g;
       const uint64_t off = (uint64_t)tile * TB;
       kb = p.k + off + tok * GE::KTOK;
       vb = p.v + off + tok * GE::VTOK;
@@ -678,11 +679,18 @@ __device__ __forceinline__ void v_to_f16(uint32_t w, uint32_t& lo, uint32_t& hi)
     hi = add_f16x2(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u), (_Float16)-1152.0f);
   }
 }
-// INT4 V: pair k of a word (nibbles at bits 4k and 16 + 4k, stored as code
-// + 8) -> the fp16 codes, exactly (1024 + nibble, less 1032).
-__device__ __forceinline__ uint32_t int4_pair_f16(uint32_t w, int k) {
-  return add_f16x2(0x64006400u | ((w >> (4 * k)) & 0x000F000Fu), (_Float16)-1032.0f);
+// INT4 V: pair k of a word (nibbles at bits 4k and 16 + 4k, u = code + 8)
+// as fp16 subnormals, exactly: pairs 0 and 2 (the latter from the word
+// shifted by 8) are u * 2^-24, pairs 1 and 3, masked in place, u * 2^-20.
+// One AND per pair and one shift per word; a tile's operand holds pairs of
+// one scale, and when a segment ends its accumulator is scaled back and
+// 8 * (sum of the p that entered the products) taken off (kInt4VScale).
+__device__ __forceinline__ uint32_t int4_pair_sub(uint32_t w, int k) {
+  const uint32_t x = k & 2 ? w >> 8 : w;
+  return x & (k & 1 ? 0x00F000F0u : 0x000F000Fu);
 }
+// The factor that turns an INT4 accumulator tile c back into sum p * u.
+__device__ __forceinline__ constexpr float kInt4VScale(int c) { return c & 1 ? 0x1p20f : 0x1p24f; }
 
 // K operand of q.K step kk of chunk h, as bf16 (exact: 8-bit codes and e5m2
 // widen without rounding; INT4 nibbles become 136 + code).
@@ -715,7 +723,7 @@ __device__ __forceinline__ void compute_step(const SplitBuf<D, KVT>& r,
                                              const QRegs<SplitGeo<D, KVT>::KK, SplitGeo<D, KVT>::NQ>& qop,
                                              float qs, float qk_scale, int t0, int t_lo, int t_end, bool edge,
                                              int lane, float& m_run, float& l_run,
-                                             f32x4 (&acc)[SplitGeo<D, KVT>::NC]) {
+                                             f32x4 (&acc)[SplitGeo<D, KVT>::NC], f32x4& psum16) {
   using GE = SplitGeo<D, KVT>;
   constexpr int CH = GE::CH;
   const int j = lane >> 4;
@@ -752,6 +760,7 @@ __device__ __forceinline__ void compute_step(const SplitBuf<D, KVT>& r,
   if (__builtin_amdgcn_ballot_w64(bump && m_run > -INFINITY)) {
 #pragma unroll
     for (int c = 0; c < GE::NC; ++c) acc[c] = acc[c] * alpha;
+    if constexpr (GE::I4) psum16 = psum16 * alpha;
   }
   m_run = m_ref;
   float pv[CH][4];
@@ -802,11 +811,17 @@ __device__ __forceinline__ void compute_step(const SplitBuf<D, KVT>& r,
       acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aop, pop_lo, acc[c], 0, 0, 0);
     }
   } else {
-    const f16x8 pop = __builtin_bit_cast(
-        f16x8, u32x4{pack_f16x2(pv[0][0], pv[0][1]), pack_f16x2(pv[0][2], pv[0][3]), pack_f16x2(pv[1][0], pv[1][1]),
-                     pack_f16x2(pv[1][2], pv[1][3])});
+    // one 16x16x32 product per tile and pair of chunks
+    f16x8 pop[CH / 2];
+#pragma unroll
+    for (int hp = 0; hp < CH / 2; ++hp)
+      pop[hp] = __builtin_bit_cast(f16x8, u32x4{pack_f16x2(pv[2 * hp][0], pv[2 * hp][1]),
+                                                pack_f16x2(pv[2 * hp][2], pv[2 * hp][3]),
+                                                pack_f16x2(pv[2 * hp + 1][0], pv[2 * hp + 1][1]),
+                                                pack_f16x2(pv[2 * hp + 1][2], pv[2 * hp + 1][3])});
     // fp8 codes of masked tokens may be inf / NaN patterns: zero them on an
-    // edge step (two copies of the loop, so that other steps carry no mask)
+    // edge step (two copies of the loop, so that other steps carry no mask);
+    // other codes decode to finite values, which p = 0 cancels
     auto pv_tiles = [&](auto maskc) __attribute__((always_inline)) {
       constexpr bool MASK = decltype(maskc)::value;
       uint32_t mk[CH] = {};
@@ -815,28 +830,39 @@ __device__ __forceinline__ void compute_step(const SplitBuf<D, KVT>& r,
         for (int h = 0; h < CH; ++h) mk[h] = tok_mask8(t0 + 16 * h + 4 * j, t_lo, t_end);
       }
 #pragma unroll
-      for (int c = 0; c < GE::NC; ++c) {
-        uint32_t a0, a1, a2, a3;
-        if constexpr (GE::I4) {
-          // word c / 2 of the V piece: pairs (c % 2) and 2 + (c % 2) are tokens
-          // 0, 1 and 2, 3 of the group, dim 16 c + row
-          const uint32_t w0 = r.v[0][0][c >> 1], w1 = r.v[1][0][c >> 1];
-          a0 = int4_pair_f16(w0, c & 1);
-          a1 = int4_pair_f16(w0, 2 + (c & 1));
-          a2 = int4_pair_f16(w1, c & 1);
-          a3 = int4_pair_f16(w1, 2 + (c & 1));
-        } else {
-          const int u = c >> 2, e = c & 3;    // load u holds dims (64u + 4row .. +3) x 4 tokens
-          uint32_t w0 = r.v[0][u][e], w1 = r.v[1][u][e];
-          if constexpr (MASK) {
-            w0 &= mk[0];
-            w1 &= mk[1];
+      for (int hp = 0; hp < CH / 2; ++hp)
+#pragma unroll
+        for (int c = 0; c < GE::NC; ++c) {
+          uint32_t a0, a1, a2, a3;
+          if constexpr (GE::I4) {
+            // word c / 2 of the V piece: pairs (c % 2) and 2 + (c % 2) are
+            // tokens 0, 1 and 2, 3 of the group, dim 16 c + row
+            const uint32_t w0 = r.v[2 * hp][0][c >> 1], w1 = r.v[2 * hp + 1][0][c >> 1];
+            a0 = int4_pair_sub(w0, c & 1);
+            a1 = int4_pair_sub(w0, 2 + (c & 1));
+            a2 = int4_pair_sub(w1, c & 1);
+            a3 = int4_pair_sub(w1, 2 + (c & 1));
+          } else {
+            const int u = c >> 2, e = c & 3;    // load u holds dims (64u + 4row .. +3) x 4 tokens
+            uint32_t w0 = r.v[2 * hp][u][e], w1 = r.v[2 * hp + 1][u][e];
+            if constexpr (MASK) {
+              w0 &= mk[2 * hp];
+              w1 &= mk[2 * hp + 1];
+            }
+            v_to_f16<KVT>(w0, a0, a1);
+            v_to_f16<KVT>(w1, a2, a3);
           }
-          v_to_f16<KVT>(w0, a0, a1);
-          v_to_f16<KVT>(w1, a2, a3);
+          const f16x8 aop = __builtin_bit_cast(f16x8, u32x4{a0, a1, a2, a3});
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, pop[hp], acc[c], 0, 0, 0);
         }
-        const f16x8 aop = __builtin_bit_cast(f16x8, u32x4{a0, a1, a2, a3});
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, pop, acc[c], 0, 0, 0);
+      if constexpr (GE::I4) {
+        // the sum of the fp16 p that entered the products, per head (every
+        // row of the product: a matrix of ones times P)
+        const _Float16 one = (_Float16)1.0f;
+#pragma unroll
+        for (int hp = 0; hp < CH / 2; ++hp)
+          psum16 = __builtin_amdgcn_mfma_f32_16x16x32_f16(f16x8{one, one, one, one, one, one, one, one}, pop[hp],
+                                                          psum16, 0, 0, 0);
       }
     };
     if (GE::FP8 && edge) pv_tiles(std::true_type{});
@@ -1359,6 +1385,7 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
   f32x4 acc[GE::NC];
 #pragma unroll
   for (int c = 0; c < GE::NC; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 psum16 = f32x4{0.f, 0.f, 0.f, 0.f};   // INT4: sum of the fp16 p per head (all four entries)
   float m_run = -INFINITY;
   float l_run = 0.f;
 
@@ -1383,10 +1410,15 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
     }
     const int t0 = cc.tb + cc.j * TS;
     const bool edge = t0 < cc.lo || t0 + TS > cc.ctx;
-    compute_step<D, KVT>(r, qop, qs, p.qk_scale, t0, cc.lo, cc.ctx, edge, lane, m_run, l_run, acc);
+    compute_step<D, KVT>(r, qop, qs, p.qk_scale, t0, cc.lo, cc.ctx, edge, lane, m_run, l_run, acc, psum16);
     ++consumed;
     if (cc.j + 1 == cc.n || consumed == nsteps) {
       const float l = sum_x32(sum_x16(l_run));
+      if constexpr (GE::I4) {
+#pragma unroll
+        for (int c = 0; c < GE::NC; ++c) acc[c] = acc[c] * kInt4VScale(c) - 8.0f * psum16[0];
+        psum16 = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
       const int g = p.QT == 1 ? cc.xi : cc.xi / p.QT;
       const int qt = cc.xi - g * p.QT;
       const int gt = min(16, p.G - qt * 16);
@@ -1512,7 +1544,7 @@ hipError_t launch_single(const DecodeParams& p, int D, int kvt, int B, int grid,
 // Steps of K/V registers per wave: one computed, the rest in flight (about
 // 40 KB per wave, 160 KB per CU with one wave per SIMD).
 template <int D, int KVT>
-constexpr int split_nbuf() { return D == 64 ? 8 : (KVT == PKV_KV_INT4 ? 6 : 5); }
+constexpr int split_nbuf() { return D == 64 ? 8 : (KVT == PKV_KV_INT4 ? 4 : 5); }
 
 // f(IC<D>, IC<KVT>, IC<B>) for the split kernel's variants: every storage
 // type has its own (per-channel INT8 folds its K scales into the query as hi
@@ -1746,7 +1778,7 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
       set_error("partition_size %d must be 0 or a positive multiple of 32", partition_size);
       return PKV_ERR_INVALID;
     }
-    const int TS = c.kv_dtype == PKV_KV_BF16 ? 16 : 32;
+    const int TS = c.kv_dtype == PKV_KV_BF16 ? 16 : (c.kv_dtype == PKV_KV_INT4 ? 64 : 32);
     const int64_t steps_ub = rows * ceil_div((int64_t)table_width * c.block_size, TS);
     if (steps_ub > INT32_MAX / 2) return fail(PKV_ERR_INVALID, "problem too large for one call");
     if (!split_sizes(num_seqs, num_q_heads, use_scratch ? (int32_t)rows : 0, c.head_dim, table_width,
