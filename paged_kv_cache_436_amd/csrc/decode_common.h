@@ -172,16 +172,16 @@ __device__ __forceinline__ int acc_dim(int c, int j, int i) {
 // kernels subtract the constant 136 after the products: 136 * sum(q) from
 // each logit, 136 * sum(p) from each accumulator.
 constexpr float kInt4Bias = 136.0f;
-// (x & mask) | orv in one v_and_or_b32, the mask in a VGPR and orv in an
-// SGPR: a three-operand instruction cannot take two literal constants, so
-// the compiler would otherwise emit an AND and an OR.
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t orv) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask), "s"(orv));
-  return r;
-}
+// The mask and the OR constant pass through an empty asm statement that
+// makes them register values the compiler cannot fold back into literals
+// (it is pure, so it is computed once and shared): (w & mask) | or then
+// compiles to one v_and_or_b32 instead of an AND and an OR with literal
+// operands, and the compiler still sees every instruction it schedules.
 __device__ __forceinline__ uint32_t int4_pair(uint32_t w, int k) {
-  return and_or(k ? w >> (4 * k) : w, 0x000F000Fu, 0x43004300u);
+  uint32_t mask = 0x000F000Fu, orv = 0x43004300u;
+  asm("" : "+v"(mask));
+  asm("" : "+s"(orv));
+  return ((k ? w >> (4 * k) : w) & mask) | orv;
 }
 
 // =====================================================================

@@ -17,19 +17,29 @@ namespace {
 // sequence's chunk is token c / G of the chunk and head g G + c % G.  Token k
 // of a chunk of n sits at position ctx - n + k and sees positions 0 .. ctx -
 // n + k, so each column masks the keys at or past its own limit.
-// Every wave owns kPrefillNT tiles of 16 columns and streams all of their
+// Every wave owns prefill_nt() tiles of 16 columns and streams all of their
 // keys itself: each K/V step it loads is widened once and feeds the products
 // of all its tiles, and the wave writes its columns' outputs from registers
 // (no cross-wave merge).  The four waves of a workgroup take consecutive
 // column spans of one (sequence, KV head), so they read the same keys at
-// about the same time and share them through L2.  kPrefillBuf steps of K/V
-// are in registers: one computed, the others in flight.  The streaming
-// softmax keeps a reference max per column that is raised only when a logit
-// exceeds it by kPrefillSlack (log2 units), so the accumulators are rescaled
-// a few times per column instead of at every step.
-constexpr int kPrefillNT = 1;          // 16-column tiles per wave
-constexpr int kPrefillBuf = 2;         // K/V steps held per wave
+// about the same time and share them through L2.  A wave holds one step of
+// K/V: its load latency, and the serial q.K -> softmax -> P.V chain of a
+// step, are covered by the other tiles' work and by a second wave on the
+// SIMD (the kernel is built for two waves per SIMD: at most 256 registers),
+// which measured faster than keeping a step in flight at fewer tiles.  The
+// streaming softmax keeps a reference max per column that is raised only
+// when a logit exceeds it by kPrefillSlack (log2 units), so the accumulators
+// are rescaled a few times per column instead of at every step.
+constexpr int kPrefillBuf = 1;         // K/V steps held per wave
 constexpr float kPrefillSlack = 8.0f;  // p < 2^8 between rescales
+constexpr int kPrefillWavesPerSimd = 2;
+
+// 16-column tiles per wave: three where they fit the register budget of two
+// waves per SIMD without spilling, else two.
+template <int D, int KVT, int B>
+constexpr int prefill_nt() {
+  return D == 64 || (KVT == PKV_KV_BF16 && B < 32) || KVT == PKV_KV_FP8_E5M2 ? 3 : 2;
+}
 
 // INT4 step loads: per 16-token chunk one K piece (lane slot j, token row)
 // and one V piece (token group of lane slot j, dim row) of D / 8 bytes each,
@@ -158,14 +168,15 @@ struct PrefillParams {
   const int32_t* qstart;      // [S + 1]: sequence s's queries are rows qstart[s] .. qstart[s+1] - 1;
                               // null: one query per sequence, row s (a decode step)
   int32_t tiles;              // workgroup column spans per (sequence, KV head):
-                              // ceil(max_query_len * G / (16 kPrefillNT kNW))
+                              // ceil(max_query_len * G / (16 prefill_nt() kNW))
   int32_t T;                  // rows of q and out
   int32_t maxq;               // queries per sequence served (later ones are left unwritten)
 };
 
 template <int D, int KVT, int B>
-__global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillParams pp) {
-  constexpr int NT = kPrefillNT;
+__global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(kPrefillWavesPerSimd, kPrefillWavesPerSimd)))
+void pa_prefill_kernel(const PrefillParams pp) {
+  constexpr int NT = prefill_nt<D, KVT, B>();
   constexpr int NB = kPrefillBuf;
   const DecodeParams& p = pp.d;
   using T = Tile<D, KVT>;
@@ -567,6 +578,13 @@ __global__ __launch_bounds__(kWave * kNW) void pa_prefill_kernel(const PrefillPa
   }
 }
 
+// prefill_nt() of the variant the call runs
+int prefill_tiles_per_wave(int D, int kvt, int B) {
+  return with_variant<true>(D, kvt, B, [](auto dc, auto kc, auto bc) {
+    return prefill_nt<decltype(dc)::value, decltype(kc)::value, decltype(bc)::value>();
+  });
+}
+
 hipError_t launch_prefill(const PrefillParams& p, int D, int kvt, int B, int grid, hipStream_t stream) {
   return with_variant<true>(D, kvt, B, [&](auto dc, auto kc, auto bc) {
     hipLaunchKernelGGL((pa_prefill_kernel<decltype(dc)::value, decltype(kc)::value, decltype(bc)::value>),
@@ -582,7 +600,7 @@ hipError_t launch_prefill(const PrefillParams& p, int D, int kvt, int B, int gri
 hipError_t launch_prefill_as_decode(const PrefillDecodeArgs& a, hipStream_t stream) {
   const pkv_pool_config& c = a.pool->cfg;
   const int32_t G = a.num_q_heads / c.num_kv_heads;
-  const int64_t span = 16 * kPrefillNT * kNW;
+  const int64_t span = 16 * prefill_tiles_per_wave(c.head_dim, c.kv_dtype, c.block_size) * kNW;
   const int64_t tiles = (G + span - 1) / span;
   const int64_t items = (int64_t)a.num_seqs * c.num_kv_heads * tiles;
   if (items > INT32_MAX / 2) return hipErrorInvalidValue;
@@ -665,7 +683,7 @@ extern "C" pkv_status paged_attn_prefill(float* out, const void* q, const pkv_po
   if (channel && (const void*)out == q)
     return fail(PKV_ERR_INVALID, "out must not alias q for storage with per-channel scales");
   const int32_t G = num_q_heads / c.num_kv_heads;
-  const int64_t span = 16 * kPrefillNT * kNW;   // columns per workgroup
+  const int64_t span = 16 * prefill_tiles_per_wave(c.head_dim, c.kv_dtype, c.block_size) * kNW;   // columns per workgroup
   const int64_t tiles = ((int64_t)max_query_len * G + span - 1) / span;
   const int64_t items = (int64_t)num_seqs * c.num_kv_heads * tiles;
   if (items > INT32_MAX / 2) return fail(PKV_ERR_INVALID, "too many query tiles in one call");
