@@ -252,8 +252,10 @@ uint64_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
  * (per token) or the output (per tensor, per channel).  ctx_s == 0 gives a
  * zero row.  Arithmetic: bf16 q, fp32 accumulation and softmax; p meets V as
  * two bf16 parts (~16 bits of p) for bf16 storage and in the single-pass
- * form, while the split form meets 8-bit and 4-bit codes (converted exactly
- * to fp16) with p rounded to one fp16 (<= 2^-11 relative).  A stored inf or
+ * form, while the split form meets 8-bit codes (converted exactly to fp16)
+ * and 4-bit codes (the exact fp16 values u * 2^-24 or u * 2^-20 of u = code +
+ * 8, the scale and 8 * sum(p) taken back exactly after the products) with p
+ * rounded to one fp16 (<= 2^-11 relative).  A stored inf or
  * NaN in V gives a non-finite output element (inf may surface as NaN).
  *   out           device fp32 [S][Hq][D]
  *   q             device bf16 [S][Hq][D]
