@@ -248,7 +248,9 @@ uint64_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
  * converted exactly and their scales applied in fp32 ([KVP] §四: dequantise
  * before compute): per-tensor and per-(token, head) K scales multiply the
  * logits, per-channel K scales are folded into the query (q' = q * s_k held
- * as two bf16 parts, hi and lo, ~16 significant bits), V scales multiply p
+ * as two bf16 parts, hi and lo, ~16 significant bits; the split form folds
+ * each query as it loads it, the single-pass forms in a first pass that
+ * stages q' in out's rows, so out must not alias q), V scales multiply p
  * (per token) or the output (per tensor, per channel).  ctx_s == 0 gives a
  * zero row.  Arithmetic: bf16 q, fp32 accumulation and softmax; p meets V as
  * two bf16 parts (~16 bits of p) for bf16 storage and in the single-pass

@@ -310,9 +310,8 @@ struct SplitParams {
   uint32_t epoch;             // this call's tag for row_done
   float qk_scale;
   float out_scale;
-  const float* ks_ch;         // int8 per channel: this layer's K / V scales [Hkv][D], else null
-  const float* vs_ch;
-  int32_t q_stride;           // elements between q rows: D, or 2 D for the folded q of int8 per channel
+  const float* ks_ch;         // int8 per channel, INT4: this layer's K / V scales [Hkv][D], else null
+  const float* vs_ch;         // (the K scales are folded into the query as it is loaded)
 };
 
 template <int D, int KVT>
@@ -382,13 +381,33 @@ __device__ __forceinline__ QRegs<SplitGeo<D, KVT>::KK, SplitGeo<D, KVT>::NQ> loa
   const int row = lane & 15;
   const int j = lane >> 4;
   // rows past the tile's heads read a valid head; their columns are never stored
-  const uint16_t* qh = p.q + ((int64_t)s * p.Hq + h0 + (row < gt ? row : 0)) * p.q_stride;
+  const int h = h0 + (row < gt ? row : 0);
+  const uint16_t* qh = p.q + ((int64_t)s * p.Hq + h) * D;
   QRegs<GE::KK, GE::NQ> r;
+  if constexpr (GE::CHAN) {
+    // the K channel scales folded into the query as it is loaded:
+    // q' = fp32(q) * s_k[g][d], hi = bf16(q'), lo = bf16(q' - hi), both
+    // rounded to nearest even (the query fold kernel's arithmetic)
+    const float* ksc = p.ks_ch + (h / p.G) * D;
 #pragma unroll
-  for (int n = 0; n < GE::NQ; ++n)
+    for (int kk = 0; kk < GE::KK; ++kk) {
+      const int d0 = q_dim0<GE::QL>(kk, j);
+      const bf16x8 raw = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + d0));
+      const f32x4 sa = *reinterpret_cast<const f32x4*>(ksc + d0);
+      const f32x4 sb = *reinterpret_cast<const f32x4*>(ksc + d0 + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = (float)raw[e] * (e < 4 ? sa[e] : sb[e - 4]);
+        const __bf16 hi = (__bf16)x;
+        r.q[0][kk][e] = hi;
+        r.q[1][kk][e] = (__bf16)(x - (float)hi);
+      }
+    }
+  } else {
 #pragma unroll
     for (int kk = 0; kk < GE::KK; ++kk)
-      r.q[n][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + n * D + q_dim0<GE::QL>(kk, j)));
+      r.q[0][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + q_dim0<GE::QL>(kk, j)));
+  }
   return r;
 }
 
@@ -1808,11 +1827,12 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     split_grid_wg = split_grid(steps_ub, cus, bpc);
     if (split_grid_wg * kNW + z.rows > z.slots_cap) return fail(PKV_ERR_INVALID, "internal: workspace sizing");
   }
-  // the query the kernels read: q itself, or (per-channel int8) q with the K
-  // channel scales folded in, written into the output rows first
+  // the query the kernels read: q itself, or (K channel scales, single-pass
+  // forms) q with the scales folded in, written into the output rows first;
+  // the split form folds them as it loads each query
   const uint16_t* qk = static_cast<const uint16_t*>(q);
   int32_t q_stride = c.head_dim;
-  if (channel) {
+  if (channel && partition_size == 0) {
     const int64_t n = (int64_t)num_seqs * num_q_heads * c.head_dim;
     const int64_t blocks = (n + 255) / 256;
     if (blocks > INT32_MAX) return fail(PKV_ERR_INVALID, "too many queries in one call");
@@ -1874,7 +1894,6 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     const int64_t grid = split_grid_wg;
     SplitParams p{};
     p.q = qk;
-    p.q_stride = q_stride;
     p.ks_ch = channel ? ksl : nullptr;
     p.vs_ch = channel ? vsl : nullptr;
     p.out = out;
