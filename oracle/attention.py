@@ -198,6 +198,47 @@ def paged_decode(q_bits: np.ndarray, img: PoolImage, layer: int,
     return out
 
 
+def shared_prefix_bounds(ctx: int, prefix_len: int):
+    """How a sequence of ``ctx`` positions splits against a shared prefix of
+    ``prefix_len`` positions: (positions read through the shared table, the
+    first position read through the sequence's own table)."""
+    return min(ctx, prefix_len), prefix_len
+
+
+def paged_decode_shared_prefix(q_bits: np.ndarray, img: PoolImage, layer: int,
+                               block_tables: np.ndarray, context_lens: np.ndarray,
+                               prefix_table: np.ndarray, prefix_len: int, scale: float,
+                               k_scale: float = 1.0, v_scale: float = 1.0, seqs=None) -> np.ndarray:
+    """Paged decode of sequences that share a cached prompt prefix.
+
+    Requests that start with the same prompt have block tables naming the
+    same physical blocks for it (bjdmk.com.cn article, §3.1; §3.2: a
+    1500-token system prompt held once for 200 concurrent requests).
+    Reading of a decode over such a batch: the shared blocks are named once, by
+    ``prefix_table`` (physical blocks of positions [0, prefix_len),
+    prefix_len a multiple of the block size); sequence s reads positions
+    [0, min(ctx_s, prefix_len)) through it and positions [prefix_len, ctx_s)
+    through its own table row, whose entries below prefix_len / B are not
+    read.  The attention is ``attend`` over those positions in order - the
+    same decode as ``paged_decode`` with the shared blocks written into
+    every sequence's table.
+
+    Returns [S, Hq, D] float64 (rows of sequences not in ``seqs`` are zero).
+    """
+    q_bits = np.asarray(q_bits, dtype=np.uint16)
+    S, hq, dim = q_bits.shape
+    out = np.zeros((S, hq, dim), dtype=np.float64)
+    idx = range(S) if seqs is None else seqs
+    for s in idx:
+        ctx = int(context_lens[s])
+        n_shared, own_from = shared_prefix_bounds(ctx, int(prefix_len))
+        Kp, Vp = gather_kv(img, layer, prefix_table, n_shared, k_scale, v_scale)
+        Ko, Vo = gather_kv(img, layer, block_tables[s], ctx, k_scale, v_scale, own_from)
+        out[s] = attend(codecs.bf16_bits_to_f64(q_bits[s]), np.concatenate([Kp, Ko]),
+                        np.concatenate([Vp, Vo]), scale)
+    return out
+
+
 def paged_prefill(q_bits: np.ndarray, img: PoolImage, layer: int, block_tables: np.ndarray,
                   context_lens: np.ndarray, query_start: np.ndarray, scale: float,
                   k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:

@@ -5,7 +5,9 @@ that should then fail: a transposed grouping, a slot off by one, a dropped
 softmax scale, a wrong e5m2 exponent bias, a window one position too wide,
 per-channel scales read with the dims reversed, a mixed-granularity V read
 with the K channel scales, a radix-tree partial match without its copy, an
-eviction of the most recently used leaf, an eviction of an inner block.
+eviction of the most recently used leaf, an eviction of an inner block, a
+shared prefix read through the sequences' own tables, a shared prefix read
+past a short context, a shared/own boundary one position off.
 """
 
 import numpy as np
@@ -18,6 +20,7 @@ from tests import test_oracle_codecs as tc
 from tests import test_oracle_paging as tp
 from tests import test_oracle_int8_scales as ti
 from tests import test_oracle_window as tw
+from tests import test_oracle_shared_prefix as tsp
 from oracle import layout
 
 
@@ -185,3 +188,18 @@ def test_radix_eviction_of_an_inner_block_is_caught(monkeypatch):
         return b
     monkeypatch.setattr(BlockManagerModel, "_evict", evict_any)
     assert _fails(lambda: [tr.test_random_walk_under_eviction(2, s) for s in range(4)])
+
+
+def test_shared_prefix_read_through_own_tables_is_caught(monkeypatch):
+    monkeypatch.setattr(att, "shared_prefix_bounds", lambda ctx, P: (0, 0))
+    assert _fails(lambda: tsp.test_shared_prefix_matches_sdpa_on_the_token_lists(0))
+
+
+def test_shared_prefix_past_a_short_context_is_caught(monkeypatch):
+    monkeypatch.setattr(att, "shared_prefix_bounds", lambda ctx, P: (P, P))
+    assert _fails(lambda: tsp.test_shared_prefix_equals_decode_of_materialised_copies(layout.KV_BF16))
+
+
+def test_shared_prefix_boundary_off_by_one_is_caught(monkeypatch):
+    monkeypatch.setattr(att, "shared_prefix_bounds", lambda ctx, P: (max(min(ctx, P) - 1, 0), max(P - 1, 0)))
+    assert _fails(lambda: tsp.test_shared_prefix_matches_sdpa_on_the_token_lists(1))
