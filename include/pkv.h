@@ -403,6 +403,52 @@ pkv_status paged_attn_decode_ex(const pkv_decode_args* args, hipStream_t stream)
  * race: order them on one stream or with events. */
 pkv_status paged_attn_decode_noalloc(const pkv_decode_args* args, hipStream_t stream);
 
+/* Decode of a batch whose sequences share a cached prompt prefix.  Requests
+ * that start with one prompt have tables naming the same physical blocks for
+ * it ([BJD] §3.1), and a prompt shared by many requests is held once ([BJD]
+ * §3.2: a 1500-token system prompt for 200 concurrent requests).  The result
+ * is paged_attn_decode_ex's for tables whose first prefix_len / B entries
+ * are prefix_table; the pages describe the sharing of the blocks, not how
+ * attention over them is computed.  Here the shared blocks are read once
+ * per KV head for the whole batch instead of once per sequence:
+ *   1. the split-context form attends each sequence's own positions
+ *      [prefix_len, ctx_s) and keeps every output row's softmax state;
+ *   2. a second launch attends, per KV head, the prefix positions
+ *      [0, min(ctx_s, prefix_len)) of all (sequence, query head) pairs
+ *      together - their queries are the columns of the matrix-core products,
+ *      as paged_attn_prefill's tokens are - in key chunks, and the last chunk
+ *      of a column span to finish merges the chunks' partial states with
+ *      the first pass's rows (exact softmax merge, fp32).
+ *   args          as for paged_attn_decode_ex (plain or appending form, every
+ *                 storage type); partition_size must be positive and
+ *                 sliding_window 0, else PKV_ERR_UNSUPPORTED; the workspace
+ *                 (256-byte aligned, scratch) must hold
+ *                 paged_attn_shared_prefix_workspace_bytes bytes.
+ *   prefix_table  device int32 [prefix_len / B]: the physical blocks of
+ *                 positions [0, prefix_len), read for every sequence in place
+ *                 of the first prefix_len / B entries of its own table row
+ *                 (those are not read and may hold anything).
+ *   prefix_len    >= 0 and a multiple of B (else PKV_ERR_INVALID); 0 is
+ *                 paged_attn_decode_ex.
+ * A sequence with ctx_s <= prefix_len attends its first ctx_s positions,
+ * all in the prefix; in the appending form nothing is written for it (its
+ * new token would land in a shared block, which a caller copies first).
+ * Arithmetic: the split form's for each sequence's own positions,
+ * paged_attn_prefill's (single-pass decode arithmetic) for the prefix.
+ * Launches: the split kernel, the query fold for storage with K channel
+ * scales, the prefix pass; asynchronous on `stream`. */
+pkv_status paged_attn_decode_shared_prefix(const pkv_decode_args* args, const int32_t* prefix_table,
+                                           int32_t prefix_len, hipStream_t stream);
+
+/* Workspace bytes paged_attn_decode_shared_prefix needs on the current
+ * device (the split form's workspace, each row's softmax state, the folded
+ * query for storage with K channel scales, and the prefix pass's partial
+ * states - one per key chunk and (sequence, query head) - and counters);
+ * 0 for sizes that are invalid or too large for one call. */
+uint64_t paged_attn_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                  int32_t head_dim, int32_t table_width, int32_t block_size,
+                                                  int32_t kv_dtype, int32_t prefix_len);
+
 /* ------------------------------------------------------------- host checks
  * Validators over HOST copies of device inputs, for callers that want to
  * rule out racing or out-of-range values before a launch.  Return PKV_OK or

@@ -97,6 +97,8 @@ SIGNATURES = {
                                         _I32, _F, _I32, ctypes.POINTER(KVScales), _I32, _P, _U64, _P]),
     "paged_attn_decode_ex": (_I32, [ctypes.POINTER(DecodeArgs), _P]),
     "paged_attn_decode_noalloc": (_I32, [ctypes.POINTER(DecodeArgs), _P]),
+    "paged_attn_decode_shared_prefix": (_I32, [ctypes.POINTER(DecodeArgs), _P, _I32, _P]),
+    "paged_attn_shared_prefix_workspace_bytes": (_U64, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "paged_attn_prefill": (_I32, [_P, _P, ctypes.POINTER(PoolDesc), _I32, _P, _I32, _P, _P, _I32, _I32, _I32,
                                   _I32, _F, _I32, ctypes.POINTER(KVScales), _P]),
     "pkv_check_slots": (_I32, [_I64P, _I32, _I64]),
@@ -275,6 +277,36 @@ def paged_attn_decode_ex(out, q, pool: Pool, layer: int, block_tables, context_l
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.paged_attn_decode_ex(ctypes.byref(a), _stream(stream)))
+
+
+def paged_attn_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, table_width,
+                                             block_size, kv_dtype, prefix_len) -> int:
+    return int(_lib.paged_attn_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                             table_width, block_size, kv_dtype, prefix_len))
+
+
+def paged_attn_decode_shared_prefix(out, q, pool: Pool, layer: int, block_tables, context_lens, scale: float,
+                                    prefix_table, prefix_len: int, kv_dtype: int | None = None,
+                                    k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 512,
+                                    workspace=None, key=None, value=None, stream=None):
+    """Decode of sequences sharing a prompt prefix (see pkv.h): positions
+    below prefix_len are read through prefix_table (int32 device tensor of
+    prefix_len / B blocks) for every sequence, once per KV head."""
+    S, hq, _ = q.shape
+    sc = KVScales(k_scale, v_scale)
+    a = DecodeArgs()
+    a.out, a.q, a.pool, a.layer = _ptr(out), _ptr(q), ctypes.pointer(pool.desc), layer
+    a.key, a.value = _ptr(key), _ptr(value)
+    a.block_tables, a.table_width = _ptr(block_tables), block_tables.shape[1]
+    a.context_lens, a.num_seqs, a.num_q_heads = _ptr(context_lens), S, hq
+    a.scale = float(scale)
+    a.kv_dtype = pool.cfg.kv_dtype if kv_dtype is None else kv_dtype
+    a.kv_scales = ctypes.pointer(sc)
+    a.partition_size, a.sliding_window = partition_size, 0
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.paged_attn_decode_shared_prefix(ctypes.byref(a), _ptr(prefix_table), int(prefix_len),
+                                                _stream(stream)))
 
 
 def paged_attn_decode_noalloc(out, q, pool: Pool, layer: int, block_tables, context_lens, scale: float,

@@ -302,6 +302,67 @@ __global__ __launch_bounds__(256) void fold_q_kernel(const uint16_t* __restrict_
   qf[row * 2 * D + D + d] = (uint16_t)lo;
 }
 
+// Partials cross from the waves that write them to the wave that merges them,
+// which may sit on another XCD, whose L2 is not coherent with the writer's.
+// They are therefore stored and loaded with the cache policy of an
+// agent-scope atomic (the sc1 scope bit), which goes to the coherent level
+// instead of a per-XCD L2; this avoids device-scope fences, which write back
+// or invalidate a whole L2 each time.  Every access goes through a buffer
+// resource whose size bounds it to its workspace region.
+constexpr int kCoherentScope = 16;     // raw buffer access aux: sc1
+
+__device__ __forceinline__ void st_agent2(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(a), __float_as_uint(b)}, r, off, 0, kCoherentScope);
+}
+__device__ __forceinline__ f32x2 ld_agent2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCoherentScope));
+}
+
+// 16-byte loads / stores of partials with the coherent-level cache policy.
+__device__ __forceinline__ f32x4 ld_agent4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherentScope));
+}
+__device__ __forceinline__ void st_agent4(__amdgpu_buffer_rsrc_t r, int off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCoherentScope);
+}
+
+// Add `mine` steps to an epoch-tagged row counter, in two parts so that the
+// first can be issued well before its result is needed.  One lane of a wave
+// makes the calls: the atomics are per lane, and a wave-wide call would add
+// `mine` once per active lane.  Epochs increase
+// from call to call, so raising the counter to (epoch << 32) first turns a
+// counter of an earlier call into a zero count of this one and leaves a
+// counter of this call alone; the add that follows, issued right behind it,
+// takes effect after it (one wave's atomics on one address keep their
+// order).  That costs a single round trip however many waves report at
+// once.  report_steps issues both and returns the counter's value before the
+// add; report_total gives the row's total for this epoch after the
+// addition.  A counter with a larger tag (memory this library never wrote,
+// or epochs that wrapped around) is instead replaced by compare-and-swap; an
+// add that went to such a value is wiped by that replacement and redone by
+// the wave that made it.
+__device__ __forceinline__ unsigned long long report_steps(uint64_t* ctr, uint32_t epoch, int mine) {
+  unsigned long long* c = reinterpret_cast<unsigned long long*>(ctr);
+  const unsigned long long tag = (unsigned long long)epoch << 32;
+  __hip_atomic_fetch_max(c, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_fetch_add(c, (unsigned long long)(uint32_t)mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int report_total(uint64_t* ctr, uint32_t epoch, int mine, unsigned long long old) {
+  if ((uint32_t)(old >> 32) == epoch) return (int)((uint32_t)old + (uint32_t)mine);
+  unsigned long long* c = reinterpret_cast<unsigned long long*>(ctr);
+  const unsigned long long tag = (unsigned long long)epoch << 32;
+  unsigned long long expect = old + (uint32_t)mine;
+  while (true) {
+    const uint32_t base = (uint32_t)(expect >> 32) == epoch ? (uint32_t)expect : 0u;
+    const unsigned long long want = tag | (base + (uint32_t)mine);
+    unsigned long long prev = expect;
+    if (__hip_atomic_compare_exchange_strong(c, &prev, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return (int)(base + (uint32_t)mine);
+    expect = prev;
+  }
+}
+
 // ---------------------------------------------------------------- launches
 template <int V>
 using IC = std::integral_constant<int, V>;

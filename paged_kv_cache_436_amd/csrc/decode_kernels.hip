@@ -312,7 +312,24 @@ struct SplitParams {
   float out_scale;
   const float* ks_ch;         // int8 per channel, INT4: this layer's K / V scales [Hkv][D], else null
   const float* vs_ch;         // (the K scales are folded into the query as it is loaded)
+  int32_t prefix_len;         // shared-prefix decode: positions below it are left to the prefix pass, else 0
+  float* ml_out;              // shared-prefix decode: [S][Hq] (m, l) of every output row, else null
 };
+
+// First attended position of a row: the sliding window's start, or, in a
+// shared-prefix decode, the end of the shared prefix (the prefix pass
+// attends the positions before it), and the row's first step and step count
+// from there (no step when nothing is left to attend).
+__device__ __forceinline__ int split_lo(int ctx, const SplitParams& p) {
+  return p.prefix_len > 0 ? min(ctx, p.prefix_len) : window_lo(ctx, p.win);
+}
+template <int TS>
+__device__ __forceinline__ int split_base(int ctx, const SplitParams& p) { return split_lo(ctx, p) / TS * TS; }
+template <int TS>
+__device__ __forceinline__ int split_steps(int ctx, const SplitParams& p) {
+  const int lo = split_lo(ctx, p);
+  return lo >= ctx ? 0 : (ctx - lo / TS * TS + TS - 1) / TS;
+}
 
 template <int D, int KVT>
 struct SplitGeo {
@@ -922,83 +939,24 @@ __device__ __forceinline__ void cursor_next_row(Cursor& c, const SplitParams& p,
       next_head = true;
     }
     c.ctx = clamp_ctx(uniform_load(p.ctx + c.s), max_ctx);
-    c.n = row_steps<TS>(c.ctx, p.win);
+    c.n = split_steps<TS>(c.ctx, p);
   } while (c.n == 0);
   if (next_head) ++c.xi;
-  c.tb = row_base<TS>(c.ctx, p.win);
-  c.lo = window_lo(c.ctx, p.win);
+  c.tb = split_base<TS>(c.ctx, p);
+  c.lo = split_lo(c.ctx, p);
   if constexpr (kRowConsts) cursor_row(c, p);
 }
-
-// Partials cross from the waves that write them to the wave that merges them,
-// which may sit on another XCD, whose L2 is not coherent with the writer's.
-// They are therefore stored and loaded with the cache policy of an
-// agent-scope atomic (the sc1 scope bit), which goes to the coherent level
-// instead of a per-XCD L2; this avoids device-scope fences, which write back
-// or invalidate a whole L2 each time.  Every access goes through a buffer
-// resource whose size bounds it to its workspace region.
-constexpr int kCoherentScope = 16;     // raw buffer access aux: sc1
 
 // (m, l) of one (slot, head) in the partial (m, l) region.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t ml_rsrc(const SplitParams& p) {
   return __builtin_amdgcn_make_buffer_rsrc(p.part_ml, (short)0, p.ml_bytes, 0x00020000);
 }
-__device__ __forceinline__ void st_agent2(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b) {
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(a), __float_as_uint(b)}, r, off, 0, kCoherentScope);
-}
-__device__ __forceinline__ f32x2 ld_agent2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCoherentScope));
-}
 __device__ __forceinline__ uint32_t ml_offset(int slot, int head) { return ((uint32_t)slot * 16u + (uint32_t)head) * 8u; }
 
 // The accumulator block of one partial slot (NC * 1 KiB) as a buffer
-// resource, and 16-byte loads / stores of it.  The resource's size bounds
-// every access to the slot.
+// resource; every access through it stays inside the slot.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(float* acc, int slot, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(acc + (int64_t)slot * (bytes / 4), (short)0, bytes, 0x00020000);
-}
-__device__ __forceinline__ f32x4 ld_agent4(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherentScope));
-}
-__device__ __forceinline__ void st_agent4(__amdgpu_buffer_rsrc_t r, int off, f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCoherentScope);
-}
-
-// Add `mine` steps to an epoch-tagged row counter, in two parts so that the
-// first can be issued well before its result is needed.  One lane of a wave
-// makes the calls: the atomics are per lane, and a wave-wide call would add
-// `mine` once per active lane.  Epochs increase
-// from call to call, so raising the counter to (epoch << 32) first turns a
-// counter of an earlier call into a zero count of this one and leaves a
-// counter of this call alone; the add that follows, issued right behind it,
-// takes effect after it (one wave's atomics on one address keep their
-// order).  That costs a single round trip however many waves report at
-// once.  report_steps issues both and returns the counter's value before the
-// add; report_total gives the row's total for this epoch after the
-// addition.  A counter with a larger tag (memory this library never wrote,
-// or epochs that wrapped around) is instead replaced by compare-and-swap; an
-// add that went to such a value is wiped by that replacement and redone by
-// the wave that made it.
-__device__ __forceinline__ unsigned long long report_steps(uint64_t* ctr, uint32_t epoch, int mine) {
-  unsigned long long* c = reinterpret_cast<unsigned long long*>(ctr);
-  const unsigned long long tag = (unsigned long long)epoch << 32;
-  __hip_atomic_fetch_max(c, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return __hip_atomic_fetch_add(c, (unsigned long long)(uint32_t)mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int report_total(uint64_t* ctr, uint32_t epoch, int mine, unsigned long long old) {
-  if ((uint32_t)(old >> 32) == epoch) return (int)((uint32_t)old + (uint32_t)mine);
-  unsigned long long* c = reinterpret_cast<unsigned long long*>(ctr);
-  const unsigned long long tag = (unsigned long long)epoch << 32;
-  unsigned long long expect = old + (uint32_t)mine;
-  while (true) {
-    const uint32_t base = (uint32_t)(expect >> 32) == epoch ? (uint32_t)expect : 0u;
-    const unsigned long long want = tag | (base + (uint32_t)mine);
-    unsigned long long prev = expect;
-    if (__hip_atomic_compare_exchange_strong(c, &prev, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT))
-      return (int)(base + (uint32_t)mine);
-    expect = prev;
-  }
 }
 
 constexpr int kXcdWeight[8] = {256, 224, 256, 224, 256, 224, 256, 224};
@@ -1068,13 +1026,21 @@ __device__ __forceinline__ void merge_into(float& M, float& L, f32x4 (&A)[NC], f
 // Normalised output rows of one (sequence, KV head, head tile) row from its
 // merged state: lane (j, row) holds head row of the tile in the accumulator
 // layout AL; L is the softmax denominator of that head.
+// A shared-prefix decode also keeps each output row's softmax state (m, l)
+// (reference max of the scaled logits in log2 units, and the sum relative to
+// it), which the prefix pass merges its own with.
+__device__ __forceinline__ void store_ml(const SplitParams& p, int s, int h, float m, float l) {
+  *reinterpret_cast<f32x2*>(p.ml_out + ((int64_t)s * p.Hq + h) * 2) = f32x2{m, l};
+}
+
 template <int D, int AL>
 __device__ __forceinline__ void store_out(const SplitParams& p, int s, int g, int h0, int gt, const f32x4 (&A)[D / 16],
-                                          float L, int lane) {
+                                          float M, float L, int lane) {
   constexpr int NC = D / 16;
   const int row = lane & 15;
   const int j = lane >> 4;
   if (row < gt) {
+    if (p.ml_out && j == 0) store_ml(p, s, h0 + row, M, L);
     float* orow = p.out + ((int64_t)s * p.Hq + h0 + row) * D;
     const float inv = p.out_scale / L;
     const float* vch = p.vs_ch ? p.vs_ch + g * D : nullptr;
@@ -1094,10 +1060,11 @@ __device__ __forceinline__ void store_out(const SplitParams& p, int s, int g, in
 // the stores of lanes whose head lies past them.
 template <int D, int AL>
 __device__ __forceinline__ void store_out_direct(const SplitParams& p, int s, int h0, int gt, const f32x4 (&A)[D / 16],
-                                                 float L, int lane) {
+                                                 float M, float L, int lane) {
   static_assert(AL == 1 || AL == 2, "direct output covers the bf16 and 8-bit accumulator layouts");
   const int row = lane & 15;
   const int j = lane >> 4;
+  if (p.ml_out && j == 0 && row < gt) store_ml(p, s, h0 + row, M, L);
   const float inv = p.out_scale / L;
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(p.out + ((int64_t)s * p.Hq + h0) * D, (short)0,
                                                                      gt * D * 4, 0x00020000);
@@ -1204,7 +1171,7 @@ __device__ __forceinline__ void merge_row(const SplitParams& p, int x, int s, in
       for (int i = 0; i < 4; ++i) a2[c][i] = __shfl_xor(A[c][i], off, kWave);
     merge_into<NC>(M, L, A, m2, l2, a2);
   }
-  store_out<D, AL>(p, s, g, h0, gt, A, L, lane);
+  store_out<D, AL>(p, s, g, h0, gt, A, M, L, lane);
 }
 
 // Launched with one workgroup (one wave per SIMD) per CU, so the compiler may
@@ -1246,7 +1213,7 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
     load_ctx(base);
 #pragma unroll
     for (int k = 0; k < kSeqRegs; ++k) {
-      const int n = row_steps<TS>(cv[k], p.win);
+      const int n = split_steps<TS>(cv[k], p);
       total += wave_sum(n);
       if (w == 0) {
         const int b0 = base + k * kWave;
@@ -1257,6 +1224,8 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
           float* o = p.out + (int64_t)se * p.Hq * D;
           for (int i = lane * 4; i < p.Hq * D; i += kWave * 4)
             *reinterpret_cast<f32x4*>(o + i) = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (p.ml_out)   // nothing attended: the prefix pass takes its own state alone
+            for (int h = lane; h < p.Hq; h += kWave) store_ml(p, se, h, -INFINITY, 0.f);
         }
       }
     }
@@ -1284,7 +1253,7 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
       for (int k = 0; k < kSeqRegs; ++k) {
         if (found) break;
         const int c = cv[k];
-        const int n = row_steps<TS>(c, p.win);
+        const int n = split_steps<TS>(c, p);
         const int incl = wave_incl_scan(n, lane);
         const bool hit = acc0 + incl - n <= rem0 && rem0 < acc0 + incl;
         const uint64_t m = __ballot(hit);
@@ -1305,8 +1274,8 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
   cur.s = __builtin_amdgcn_readfirstlane(cur.s);
   cur.n = __builtin_amdgcn_readfirstlane(cur.n);
   cur.ctx = __builtin_amdgcn_readfirstlane(cur.ctx);
-  cur.tb = row_base<TS>(cur.ctx, p.win);
-  cur.lo = window_lo(cur.ctx, p.win);
+  cur.tb = split_base<TS>(cur.ctx, p);
+  cur.lo = split_lo(cur.ctx, p);
   cur.xi = __builtin_amdgcn_readfirstlane(cur.xi);
   cur.j = __builtin_amdgcn_readfirstlane(cur.j);
   cum0 = __builtin_amdgcn_readfirstlane(cum0);
@@ -1334,7 +1303,7 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
             ++axi;
           }
           actx = clamp_ctx(uniform_load(p.ctx + as), max_ctx);
-          an = row_steps<TS>(actx, p.win);
+          an = split_steps<TS>(actx, p);
         } while (an == 0);
       }
     }
@@ -1442,7 +1411,7 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
       const int qt = cc.xi - g * p.QT;
       const int gt = min(16, p.G - qt * 16);
       if (kDirect && cc.j + 1 == cc.n && consumed >= whole_from) {
-        if constexpr (kDirect) store_out_direct<D, GE::AL>(p, cc.s, g * p.G + qt * 16, gt, acc, l, lane);
+        if constexpr (kDirect) store_out_direct<D, GE::AL>(p, cc.s, g * p.G + qt * 16, gt, acc, m_run, l, lane);
       } else {
         if (row < gt) {
           const int slot = cc.xi * p.S + cc.s + w;
@@ -1531,7 +1500,7 @@ __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 
             rcum = 0;
             ++rxi;
           }
-          rn = row_steps<TS>(clamp_ctx(uniform_load(p.ctx + rs), max_ctx), p.win);
+          rn = split_steps<TS>(clamp_ctx(uniform_load(p.ctx + rs), max_ctx), p);
         } while (rn == 0);
       }
     }
@@ -1726,6 +1695,17 @@ extern "C" uint64_t paged_attn_workspace_bytes(int32_t num_seqs, int32_t num_q_h
 
 namespace {
 
+// The shared-prefix form's arguments and workspace regions past the split
+// form's own (which comes first, as for paged_attn_decode).
+struct SharedPrefixCall {
+  const int32_t* prefix_table;
+  int32_t prefix_len;
+  float* ml;               // [S][Hq] (m, l) of the rows the split pass writes
+  uint16_t* qfold;         // [S][Hq][2 D] the query with K channel scales folded in (those storage types)
+  char* pass_ws;           // the prefix pass's partials and counters
+  PrefixPassGeometry geo;
+};
+
 // A decode call.  With use_scratch the split form's workspace is this
 // device's copy of the static scratch array (sized exactly for the call and
 // refused beyond kScratchBytes) and the workspace arguments are ignored.
@@ -1734,7 +1714,7 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
                        const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
                        int32_t kv_dtype, const pkv_kv_scales* kv_scales, int32_t partition_size,
                        int32_t sliding_window, void* workspace, uint64_t workspace_bytes, hipStream_t stream,
-                       bool use_scratch = false) {
+                       bool use_scratch = false, const SharedPrefixCall* sp = nullptr) {
   const bool append = key != nullptr || value != nullptr;
   pkv_status st = check_pool(pool);
   if (st != PKV_OK) return st;
@@ -1926,8 +1906,44 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
     p.epoch = next_epoch();
     p.qk_scale = scale * kLog2e * ksc;
     p.out_scale = vsc;
+    p.prefix_len = sp ? sp->prefix_len : 0;
+    p.ml_out = sp ? sp->ml : nullptr;
     launch_split(p, c.head_dim, c.kv_dtype, c.block_size, (int)grid, stream);
     e = hipGetLastError();
+    if (e == hipSuccess && sp) {
+      // the shared prefix, attended once per KV head for all sequences and
+      // merged into the rows the split pass wrote
+      PrefixPassArgs a{};
+      a.d.q = qk;
+      a.d.q_stride = q_stride;
+      if (channel) {   // the prefill kernel's products read the folded query
+        const int64_t n = (int64_t)num_seqs * num_q_heads * c.head_dim;
+        hipLaunchKernelGGL(fold_q_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, stream, qk, sp->qfold,
+                           ksl, n, num_q_heads, G, c.head_dim);
+        a.d.q = sp->qfold;
+        a.d.q_stride = 2 * c.head_dim;
+      }
+      a.d.out = out;
+      a.d.pool = pool;
+      a.d.layer = layer;
+      a.d.block_tables = sp->prefix_table;
+      a.d.table_width = sp->prefix_len / c.block_size;
+      a.d.context_lens = context_lens;
+      a.d.num_seqs = num_seqs;
+      a.d.num_q_heads = num_q_heads;
+      a.d.sliding_window = 0;
+      a.d.qk_scale = p.qk_scale;
+      a.d.out_scale = vsc;
+      a.d.ks = ksl;
+      a.d.vs = vsl;
+      a.d.vs_ch = channel ? vsl : nullptr;
+      a.prefix_len = sp->prefix_len;
+      a.merge_ml = sp->ml;
+      a.workspace = sp->pass_ws;
+      a.epoch = next_epoch();
+      a.geo = sp->geo;
+      e = launch_prefix_pass(a, stream);
+    }
   }
   if (e != hipSuccess) {
     set_error("paged_attn_decode launch failed: %s", hipGetErrorString(e));
@@ -1977,4 +1993,97 @@ extern "C" pkv_status paged_attn_decode_noalloc(const pkv_decode_args* a, hipStr
   return decode_impl(a->out, a->q, a->pool, a->layer, a->key, a->value, a->block_tables, a->table_width,
                      a->context_lens, a->num_seqs, a->num_q_heads, a->scale, a->kv_dtype, a->kv_scales,
                      a->partition_size, a->sliding_window, nullptr, 0, stream, true);
+}
+
+namespace {
+
+// Workspace layout of a shared-prefix decode: the split form's regions, the
+// rows' (m, l), the folded query (storage with K channel scales), then the
+// prefix pass's partials and counters.
+struct SharedPrefixSizes {
+  uint64_t split, ml, qfold, pass, total;
+  PrefixPassGeometry geo;
+};
+bool shared_prefix_sizes(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t W, int32_t B, int32_t kvt,
+                         int32_t prefix_len, SharedPrefixSizes* z) {
+  SplitSizes sz;
+  if (!split_sizes(S, Hq, 0, D, W, B, 1, &sz)) return false;
+  int cus = 0;
+  if (device_cus(&cus) != 0) return false;
+  if (!prefix_pass_geometry(S, Hq, Hkv, D, kvt, B, prefix_len, cus, &z->geo)) return false;
+  z->split = (uint64_t)(sz.cnt_bytes + sz.ml_bytes + sz.acc_bytes);
+  z->ml = align_up((uint64_t)S * Hq * 2 * sizeof(float));
+  z->qfold = has_k_channel_scales(kvt) ? align_up((uint64_t)S * Hq * 2 * D * sizeof(uint16_t)) : 0;
+  z->pass = z->geo.part_o_bytes + z->geo.part_ml_bytes + z->geo.ctr_bytes;
+  z->total = z->split + z->ml + z->qfold + z->pass;
+  return true;
+}
+
+}  // namespace
+
+extern "C" uint64_t paged_attn_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                                             int32_t num_kv_heads, int32_t head_dim,
+                                                             int32_t table_width, int32_t block_size,
+                                                             int32_t kv_dtype, int32_t prefix_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || head_dim <= 0 ||
+      table_width <= 0 || block_size <= 0 || prefix_len < 0)
+    return 0;
+  if (prefix_len == 0) return paged_attn_workspace_bytes(num_seqs, num_q_heads, head_dim, table_width, block_size, 32);
+  SharedPrefixSizes z;
+  if (!shared_prefix_sizes(num_seqs, num_q_heads, num_kv_heads, head_dim, table_width, block_size, kv_dtype,
+                           prefix_len, &z))
+    return 0;
+  return z.total;
+}
+
+extern "C" pkv_status paged_attn_decode_shared_prefix(const pkv_decode_args* a, const int32_t* prefix_table,
+                                                      int32_t prefix_len, hipStream_t stream) {
+  if (!a) return fail(PKV_ERR_INVALID, "NULL argument block");
+  if ((a->key == nullptr) != (a->value == nullptr)) return fail(PKV_ERR_INVALID, "key and value must both be given");
+  if (prefix_len < 0) return fail(PKV_ERR_INVALID, "prefix_len is negative");
+  if (prefix_len == 0)
+    return decode_impl(a->out, a->q, a->pool, a->layer, a->key, a->value, a->block_tables, a->table_width,
+                       a->context_lens, a->num_seqs, a->num_q_heads, a->scale, a->kv_dtype, a->kv_scales,
+                       a->partition_size, a->sliding_window, a->workspace, a->workspace_bytes, stream);
+  pkv_status st = check_pool(a->pool);
+  if (st != PKV_OK) return st;
+  const pkv_pool_config& c = a->pool->cfg;
+  if (prefix_len % c.block_size != 0) {
+    set_error("prefix_len %d is not a multiple of the block size %d", prefix_len, c.block_size);
+    return PKV_ERR_INVALID;
+  }
+  if (prefix_len > INT32_MAX / 2) return fail(PKV_ERR_INVALID, "prefix_len too large");
+  if (!prefix_table) return fail(PKV_ERR_INVALID, "NULL prefix_table");
+  if (a->partition_size == 0)
+    return fail(PKV_ERR_UNSUPPORTED, "the shared-prefix decode runs in the split-context form (partition_size > 0)");
+  if (a->sliding_window != 0) return fail(PKV_ERR_UNSUPPORTED, "the shared-prefix decode takes no sliding window");
+  if (a->num_seqs <= 0) return decode_impl(a->out, a->q, a->pool, a->layer, a->key, a->value, a->block_tables,
+                                           a->table_width, a->context_lens, a->num_seqs, a->num_q_heads, a->scale,
+                                           a->kv_dtype, a->kv_scales, a->partition_size, 0, a->workspace,
+                                           a->workspace_bytes, stream);
+  if (a->num_q_heads <= 0 || a->num_q_heads % c.num_kv_heads != 0 || a->table_width <= 0)
+    return decode_impl(a->out, a->q, a->pool, a->layer, a->key, a->value, a->block_tables, a->table_width,
+                       a->context_lens, a->num_seqs, a->num_q_heads, a->scale, a->kv_dtype, a->kv_scales,
+                       a->partition_size, 0, a->workspace, a->workspace_bytes, stream);   // reports the error
+  SharedPrefixSizes z;
+  if (!shared_prefix_sizes(a->num_seqs, a->num_q_heads, c.num_kv_heads, c.head_dim, a->table_width, c.block_size,
+                           c.kv_dtype, prefix_len, &z))
+    return fail(PKV_ERR_INVALID, "shared-prefix decode too large for one call");
+  if (!a->workspace || a->workspace_bytes < z.total) {
+    set_error("workspace of %llu bytes needed, got %llu", (unsigned long long)z.total,
+              (unsigned long long)a->workspace_bytes);
+    return PKV_ERR_INVALID;
+  }
+  if (((uintptr_t)a->workspace) % 256) return fail(PKV_ERR_INVALID, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(a->workspace);
+  SharedPrefixCall sp{};
+  sp.prefix_table = prefix_table;
+  sp.prefix_len = prefix_len;
+  sp.ml = reinterpret_cast<float*>(ws + z.split);
+  sp.qfold = z.qfold ? reinterpret_cast<uint16_t*>(ws + z.split + z.ml) : nullptr;
+  sp.pass_ws = ws + z.split + z.ml + z.qfold;
+  sp.geo = z.geo;
+  return decode_impl(a->out, a->q, a->pool, a->layer, a->key, a->value, a->block_tables, a->table_width,
+                     a->context_lens, a->num_seqs, a->num_q_heads, a->scale, a->kv_dtype, a->kv_scales,
+                     a->partition_size, 0, a->workspace, z.split, stream, false, &sp);
 }

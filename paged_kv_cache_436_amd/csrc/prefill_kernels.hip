@@ -4,6 +4,8 @@
 // prefix is reused and only the rest is computed; "KV Cache 原理与
 // PagedAttention", §五).  The K/V of every position, the new tokens included,
 // are in the pool before the call (reshape_and_cache).
+#include <algorithm>
+
 #include "decode_common.h"
 
 namespace pkv {
@@ -171,13 +173,113 @@ struct PrefillParams {
                               // ceil(max_query_len * G / (16 prefill_nt() kNW))
   int32_t T;                  // rows of q and out
   int32_t maxq;               // queries per sequence served (later ones are left unwritten)
+  // The shared-prefix pass of a decode (pa_prefix_kernel only): the columns
+  // of KV head g are the (sequence, head) pairs of all T sequences; column
+  // (s, h) attends positions [0, min(ctx_s, prefix_len)) of the shared
+  // prefix, whose blocks are row 0 of d.bt (width d.W).  The prefix is cut
+  // into `chunks` key ranges of chunk_len positions (a multiple of kStep),
+  // one per workgroup; each writes its columns' partial results (normalised
+  // output and (m, l)), and the last of a column span's chunks merges them
+  // with the result of the other positions already in out (their (m, l) in
+  // merge_ml) into out.
+  const float* merge_ml;      // [T][Hq] (m, l) of out's rows
+  float* part_o;              // [chunks][T][Hq][D] partial outputs
+  float* part_ml;             // [chunks][T][Hq] partial (m, l)
+  uint32_t part_o_bytes, part_ml_bytes;
+  uint64_t* ctr;              // [Hkv][tiles][kNW] x kPrefixCounterStride, epoch-tagged arrival counts
+  uint32_t epoch;
+  int32_t prefix_len, chunk_len, chunks;
+  int32_t cpw;                // columns per wave: a multiple of 16, at most 16 prefill_nt()
 };
 
-template <int D, int KVT, int B>
-__global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(kPrefillWavesPerSimd, kPrefillWavesPerSimd)))
-void pa_prefill_kernel(const PrefillParams pp) {
-  constexpr int NT = prefill_nt<D, KVT, B>();
-  constexpr int NB = kPrefillBuf;
+constexpr int kPrefixCounterStride = 16;   // uint64 words per arrival counter (one per 128-byte line)
+constexpr int kPrefixBuf = 3;              // K/V steps held per wave in the shared-prefix pass
+
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+constexpr int kMaxPrefixChunks = 16;
+
+// The end of a shared-prefix pass wave: count this wave's arrival on the
+// counter of its (KV head, column span, wave) and, if it is the last of the
+// `chunks` key ranges to arrive, merge every chunk's partial of its columns
+// with the result of the other positions in out: with the (m, l) of each
+// part (reference max of the scaled logits in log2 units and the sum
+// relative to it, l = 0 for a part that attended nothing), weight w = l
+// 2^(m - M) over M the largest m of a non-empty part, out = sum w o / sum w
+// (zero when every part is empty).  Lane (j, row) merges column row of each
+// tile, dims j D / 4 .. (j + 1) D / 4 - 1.
+template <int D>
+__device__ __forceinline__ void prefix_merge(const PrefillParams& pp, int g, int ct, int w, int c0, int cols,
+                                             __amdgpu_buffer_rsrc_t por, __amdgpu_buffer_rsrc_t pmr, int lane) {
+  const DecodeParams& p = pp.d;
+  // the partial stores have completed (agent scope: visible to every XCD)
+  // before the arrival is counted
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  wait_vm_all();
+  int arrived = 0;
+  if (lane == 0) {
+    uint64_t* c = pp.ctr + ((int64_t)(g * pp.tiles + ct) * kNW + w) * kPrefixCounterStride;
+    arrived = report_total(c, pp.epoch, 1, report_steps(c, pp.epoch, 1));
+  }
+  if (__shfl(arrived, 0, kWave) != pp.chunks) return;
+  // the loads below follow the counter update that found every chunk in
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  constexpr int DL = D / 4;            // dims per lane
+  const int row = lane & 15;
+  const int j = lane >> 4;
+  const int TH = pp.T * p.Hq;
+  for (int cl = row; cl < cols; cl += 16) {
+    const int cq = c0 + cl;
+    const int64_t oi = (int64_t)(cq / p.G) * p.Hq + g * p.G + cq % p.G;
+    float* orow = p.out + oi * D + j * DL;
+    const f32x2 mls = *reinterpret_cast<const f32x2*>(pp.merge_ml + oi * 2);
+    f32x2 mlk[kMaxPrefixChunks];
+    float M = mls[1] > 0.f ? mls[0] : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kMaxPrefixChunks; ++k) {
+      if (k < pp.chunks) {
+        mlk[k] = ld_agent2(pmr, ((uint32_t)k * (uint32_t)TH + (uint32_t)oi) * 8u);
+        if (mlk[k][1] > 0.f) M = fmaxf(M, mlk[k][0]);
+      }
+    }
+    float W = 0.f;
+    f32x4 a[DL / 4];
+    {
+      const float ws = mls[1] > 0.f ? mls[1] * __builtin_amdgcn_exp2f(mls[0] - M) : 0.f;
+      W += ws;
+#pragma unroll
+      for (int u = 0; u < DL / 4; ++u) a[u] = ws * *reinterpret_cast<const f32x4*>(orow + 4 * u);
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxPrefixChunks; ++k) {
+      if (k < pp.chunks) {
+        const float wk = mlk[k][1] > 0.f ? mlk[k][1] * __builtin_amdgcn_exp2f(mlk[k][0] - M) : 0.f;
+        W += wk;
+        const uint32_t base = (((uint32_t)k * (uint32_t)TH + (uint32_t)oi) * (uint32_t)D + (uint32_t)(j * DL)) * 4u;
+#pragma unroll
+        for (int u = 0; u < DL / 4; ++u) a[u] += wk * ld_agent4(por, (int)(base + 16u * (uint32_t)u));
+      }
+    }
+    const float inv = W > 0.f ? 1.f / W : 0.f;
+#pragma unroll
+    for (int u = 0; u < DL / 4; ++u) *reinterpret_cast<f32x4*>(orow + 4 * u) = a[u] * inv;
+  }
+}
+
+// The body of both kernels: SH selects the shared-prefix pass (columns
+// across sequences, one key chunk per workgroup, partials merged by the last
+// chunk) over the prefill (columns of one sequence's chunk, causal).
+template <int D, int KVT, int B, int NT, int NB, bool SH>
+__device__ __forceinline__ void prefill_body(const PrefillParams& pp) {
   const DecodeParams& p = pp.d;
   using T = Tile<D, KVT>;
   constexpr int E = T::E;
@@ -202,32 +304,55 @@ void pa_prefill_kernel(const PrefillParams pp) {
   const int per_xcd = (nwg + 7) / 8;
   const int item = xcd * per_xcd + (int)blockIdx.x / 8;
   if (item >= p.num_items) return;
+  // prefill: item = (sequence s, KV head g, column span ct); shared-prefix
+  // pass: (KV head g, key chunk kc, column span ct), the spans of one chunk
+  // adjacent so that they read its keys from one L2
   const int ct = item % pp.tiles;
-  const int g = (item / pp.tiles) % p.Hkv;
-  const int s = item / (pp.tiles * p.Hkv);
+  const int g = SH ? item / (pp.tiles * pp.chunks) : (item / pp.tiles) % p.Hkv;
+  const int s = SH ? 0 : item / (pp.tiles * p.Hkv);
+  const int kc = SH ? (item / pp.tiles) % pp.chunks : 0;
   const int lane = threadIdx.x % kWave;
   const int w = threadIdx.x / kWave;
   const int row = lane & 15;
   const int j = lane >> 4;
   // query rows, kept inside [0, T) whatever query_start holds
-  const int q0 = pp.qstart ? min(max(pp.qstart[s], 0), pp.T) : s;
-  const int n = pp.qstart ? min(max(pp.qstart[s + 1], q0), pp.T) - q0 : 1;
-  const int ncol = min(n, pp.maxq) * p.G;         // positions still follow the whole chunk
-  const int c0 = (ct * kNW + w) * 16 * NT;       // this wave's first column
+  const int q0 = SH ? 0 : (pp.qstart ? min(max(pp.qstart[s], 0), pp.T) : s);
+  const int n = SH ? pp.T : (pp.qstart ? min(max(pp.qstart[s + 1], q0), pp.T) - q0 : 1);
+  const int ncol = (SH ? n : min(n, pp.maxq)) * p.G;   // positions still follow the whole chunk
+  const int cpw = SH ? pp.cpw : 16 * NT;         // columns per wave
+  const int c0 = (ct * kNW + w) * cpw;           // this wave's first column
   if (c0 >= ncol) return;                        // no barrier follows: waves are independent
-  const int cols = min(16 * NT, ncol - c0);
+  const int cols = min(cpw, ncol - c0);
 
-  const int ctx = clamp_ctx(p.ctx[s], p.W * B);
+  const int ctx = SH ? pp.prefix_len : clamp_ctx(p.ctx[s], p.W * B);
   const int first = ctx - n;                     // position of the chunk's token 0
-  const int t_end = max(0, first + (c0 + cols - 1) / p.G + 1);   // the wave's largest limit
+  // shared-prefix pass: this workgroup's keys [k0, k1) of the prefix
+  const int k0 = SH ? kc * pp.chunk_len : 0;
+  const int k1 = SH ? min(k0 + pp.chunk_len, pp.prefix_len) : 0;
+  // a column's keys end at its limit; t_end is the wave's largest limit and
+  // every valid column sees the keys below lim_lo (its smallest): steps
+  // wholly below it need no mask.  Prefill: causal limits, column c0's the
+  // smallest; shared-prefix pass: min(ctx_s, k1) of the column's sequence
+  int t_end, lim_lo;
+  if constexpr (SH) {
+    int hi = 0, lo = k1;
+    for (int c = lane; c < cols; c += kWave) {
+      const int l = min(max(p.ctx[(c0 + c) / p.G], 0), k1);
+      hi = max(hi, l);
+      lo = min(lo, l);
+    }
+    t_end = wave_max_i(hi);
+    lim_lo = wave_min_i(lo);
+  } else {
+    t_end = max(0, first + (c0 + cols - 1) / p.G + 1);
+    lim_lo = max(0, first + c0 / p.G + 1);
+  }
   const int nsteps = (t_end + kStep - 1) / kStep;
-  // every valid column sees the keys below this one (column c0's limit, the
-  // smallest): steps wholly below it need no causal mask
-  const int lim_lo = max(0, first + c0 / p.G + 1);
   // one query per sequence (a decode step) may attend to a sliding window:
   // positions [t_lo, ctx); the steps start at the one holding t_lo and the
-  // keys before it are masked (their blocks may hold anything)
-  const int t_lo = pp.qstart ? 0 : window_lo(ctx, p.win);
+  // keys before it are masked (their blocks may hold anything).  The
+  // shared-prefix pass starts at its chunk (a multiple of kStep).
+  const int t_lo = SH ? k0 : (pp.qstart ? 0 : window_lo(ctx, p.win));
   const int s0 = t_lo / kStep;
   const int32_t* bt_row = p.bt + (int64_t)s * p.W;
 
@@ -245,7 +370,7 @@ void pa_prefill_kernel(const PrefillParams pp) {
     const int cl = 16 * nt + row;
     const bool valid = cl < cols;
     const int c = c0 + (valid ? cl : 0);
-    lim[nt] = valid ? max(0, first + c / p.G + 1) : 0;
+    lim[nt] = !valid ? 0 : (SH ? min(max(p.ctx[c / p.G], 0), k1) : max(0, first + c / p.G + 1));
     const uint16_t* qh = p.q + ((int64_t)(q0 + c / p.G) * p.Hq + g * p.G + c % p.G) * p.q_stride;
 #pragma unroll
     for (int n = 0; n < NQ; ++n)
@@ -533,14 +658,28 @@ void pa_prefill_kernel(const PrefillParams pp) {
     });
   }
 
-  // outputs: column `row` of tile nt; this lane holds dims acc_dim(cc, j, .)
+  // outputs: column `row` of tile nt; this lane holds dims acc_dim(cc, j, .).
+  // The shared-prefix pass writes them, and the column's (m, l), as this
+  // chunk's partial, with the coherent-level policy (the merging wave may be
+  // on another XCD).
+  const int TH = pp.T * p.Hq;
+  const __amdgpu_buffer_rsrc_t por = __builtin_amdgcn_make_buffer_rsrc(pp.part_o, (short)0, pp.part_o_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t pmr = __builtin_amdgcn_make_buffer_rsrc(pp.part_ml, (short)0, pp.part_ml_bytes, 0x00020000);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int cl = 16 * nt + row;
     const float L = sum_x32(sum_x16(l_run[nt]));
     if (cl >= cols) continue;
     const int cq = c0 + cl;
-    float* orow = p.out + ((int64_t)(q0 + cq / p.G) * p.Hq + g * p.G + cq % p.G) * D;
+    const int64_t orow_i = (int64_t)(q0 + cq / p.G) * p.Hq + g * p.G + cq % p.G;   // output row (sequence, head)
+    float* orow = p.out + orow_i * D;
+    const uint32_t prow = SH ? ((uint32_t)kc * (uint32_t)TH + (uint32_t)orow_i) * (uint32_t)(D * 4) : 0u;
+    auto put = [&](int d, f32x4 v) __attribute__((always_inline)) {   // dims d .. d + 3
+      if constexpr (SH)
+        st_agent4(por, (int)(prow + 4u * (uint32_t)d), v);
+      else
+        *reinterpret_cast<f32x4*>(orow + d) = v;
+    };
     const float inv = L > 0.f ? 1.f / L : 0.f;   // no key at all (position < 0): zero row
     float o[T::NC][4];
 #pragma unroll
@@ -556,15 +695,13 @@ void pa_prefill_kernel(const PrefillParams pp) {
     if constexpr (I4) {
       // tile cc holds dims 16 cc + 4j + {0 .. 3}
 #pragma unroll
-      for (int cc = 0; cc < T::NC; ++cc)
-        *reinterpret_cast<f32x4*>(orow + 16 * cc + 4 * j) = f32x4{o[cc][0], o[cc][1], o[cc][2], o[cc][3]};
+      for (int cc = 0; cc < T::NC; ++cc) put(16 * cc + 4 * j, f32x4{o[cc][0], o[cc][1], o[cc][2], o[cc][3]});
     } else if constexpr (E == 2) {
       // tiles 2u, 2u + 1 hold dims 32u + 8j + 2 i2 + {0, 1}: 8 consecutive floats
 #pragma unroll
       for (int u = 0; u < T::NC / 2; ++u) {
-        float* dst = orow + 32 * u + 8 * j;
-        *reinterpret_cast<f32x4*>(dst) = f32x4{o[2 * u][0], o[2 * u + 1][0], o[2 * u][1], o[2 * u + 1][1]};
-        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[2 * u][2], o[2 * u + 1][2], o[2 * u][3], o[2 * u + 1][3]};
+        put(32 * u + 8 * j, f32x4{o[2 * u][0], o[2 * u + 1][0], o[2 * u][1], o[2 * u + 1][1]});
+        put(32 * u + 8 * j + 4, f32x4{o[2 * u][2], o[2 * u + 1][2], o[2 * u][3], o[2 * u + 1][3]});
       }
     } else {
       // tiles 4u .. 4u + 3 hold dims 64u + 16j + 4 i2 + {0 .. 3}
@@ -572,10 +709,28 @@ void pa_prefill_kernel(const PrefillParams pp) {
       for (int u = 0; u < T::NC / 4; ++u)
 #pragma unroll
         for (int i2 = 0; i2 < 4; ++i2)
-          *reinterpret_cast<f32x4*>(orow + 64 * u + 16 * j + 4 * i2) =
-              f32x4{o[4 * u][i2], o[4 * u + 1][i2], o[4 * u + 2][i2], o[4 * u + 3][i2]};
+          put(64 * u + 16 * j + 4 * i2, f32x4{o[4 * u][i2], o[4 * u + 1][i2], o[4 * u + 2][i2], o[4 * u + 3][i2]});
+    }
+    if constexpr (SH) {
+      if (j == 0) st_agent2(pmr, ((uint32_t)kc * (uint32_t)TH + (uint32_t)orow_i) * 8u, m_run[nt], L);
     }
   }
+  if constexpr (SH) prefix_merge<D>(pp, g, ct, w, c0, cols, por, pmr, lane);
+}
+
+template <int D, int KVT, int B>
+__global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(kPrefillWavesPerSimd, kPrefillWavesPerSimd)))
+void pa_prefill_kernel(const PrefillParams pp) {
+  prefill_body<D, KVT, B, prefill_nt<D, KVT, B>(), kPrefillBuf, false>(pp);
+}
+
+// The shared-prefix pass of a decode: one wave per SIMD holding kPrefixBuf
+// steps of K/V (a wave streams one key chunk, a few steps, so their loads
+// are kept in flight rather than covered by a second wave on the SIMD).
+template <int D, int KVT, int B>
+__global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void pa_prefix_kernel(const PrefillParams pp) {
+  prefill_body<D, KVT, B, prefill_nt<D, KVT, B>(), kPrefixBuf, true>(pp);
 }
 
 // prefill_nt() of the variant the call runs
@@ -588,6 +743,14 @@ int prefill_tiles_per_wave(int D, int kvt, int B) {
 hipError_t launch_prefill(const PrefillParams& p, int D, int kvt, int B, int grid, hipStream_t stream) {
   return with_variant<true>(D, kvt, B, [&](auto dc, auto kc, auto bc) {
     hipLaunchKernelGGL((pa_prefill_kernel<decltype(dc)::value, decltype(kc)::value, decltype(bc)::value>),
+                       dim3(grid), dim3(kWave * kNW), 0, stream, p);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_prefix(const PrefillParams& p, int D, int kvt, int B, int grid, hipStream_t stream) {
+  return with_variant<true>(D, kvt, B, [&](auto dc, auto kc, auto bc) {
+    hipLaunchKernelGGL((pa_prefix_kernel<decltype(dc)::value, decltype(kc)::value, decltype(bc)::value>),
                        dim3(grid), dim3(kWave * kNW), 0, stream, p);
     return hipGetLastError();
   });
@@ -632,6 +795,81 @@ hipError_t launch_prefill_as_decode(const PrefillDecodeArgs& a, hipStream_t stre
   pp.T = a.num_seqs;
   pp.maxq = 1;
   return launch_prefill(pp, c.head_dim, c.kv_dtype, c.block_size, (int)((items + 7) / 8 * 8), stream);
+}
+
+// Geometry of the shared-prefix pass: column spans of at most kNW waves of
+// 16 prefill_nt() columns, balanced so that the waves of a head carry about
+// the same number of columns, and enough key chunks that the workgroups
+// cover the compute units about once.
+bool prefix_pass_geometry(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t kv_dtype, int32_t block_size, int32_t prefix_len, int cus,
+                          PrefixPassGeometry* g) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || prefix_len <= 0 || cus <= 0) return false;
+  const int64_t G = num_q_heads / num_kv_heads;
+  const int64_t ncol = (int64_t)num_seqs * G;
+  const int64_t span = 16 * (int64_t)prefill_tiles_per_wave(head_dim, kv_dtype, block_size) * kNW;
+  const int64_t tiles = (ncol + span - 1) / span;
+  const int64_t per_wave = (ncol + kNW * tiles - 1) / (kNW * tiles);
+  const int64_t steps = ((int64_t)prefix_len + kStep - 1) / kStep;
+  const int64_t want = ((int64_t)cus + num_kv_heads * tiles - 1) / (num_kv_heads * tiles);
+  int64_t chunks = std::max<int64_t>(1, std::min<int64_t>({want, (int64_t)kMaxPrefixChunks, steps}));
+  const int64_t chunk_len = (steps + chunks - 1) / chunks * kStep;
+  chunks = ((int64_t)prefix_len + chunk_len - 1) / chunk_len;
+  const int64_t items = (int64_t)num_kv_heads * tiles * chunks;
+  if (items > INT32_MAX / 2 || tiles > INT32_MAX) return false;
+  g->tiles = (int32_t)tiles;
+  g->cpw = (int32_t)((per_wave + 15) / 16 * 16);
+  g->chunks = (int32_t)chunks;
+  g->chunk_len = (int32_t)chunk_len;
+  const uint64_t rows = (uint64_t)num_seqs * (uint64_t)num_q_heads;
+  g->part_o_bytes = align_up((uint64_t)chunks * rows * (uint64_t)head_dim * sizeof(float));
+  g->part_ml_bytes = align_up((uint64_t)chunks * rows * 2 * sizeof(float));
+  g->ctr_bytes = align_up((uint64_t)num_kv_heads * tiles * kNW * kPrefixCounterStride * sizeof(uint64_t));
+  return g->part_o_bytes < (1ull << 32) && g->part_ml_bytes < (1ull << 32);
+}
+
+hipError_t launch_prefix_pass(const PrefixPassArgs& a, hipStream_t stream) {
+  const pkv_pool_config& c = a.d.pool->cfg;
+  const int64_t items = (int64_t)c.num_kv_heads * a.geo.tiles * a.geo.chunks;
+  PrefillParams pp{};
+  DecodeParams& p = pp.d;
+  p.q = a.d.q;
+  p.q_stride = a.d.q_stride;
+  p.vs_ch = a.d.vs_ch;
+  p.out = a.d.out;
+  p.k = static_cast<char*>(a.d.pool->k) + (uint64_t)a.d.layer * a.d.pool->layer_bytes;
+  p.v = static_cast<char*>(a.d.pool->v) + (uint64_t)a.d.layer * a.d.pool->layer_bytes;
+  p.ks = a.d.ks;
+  p.vs = a.d.vs;
+  p.bt = a.d.block_tables;
+  p.ctx = a.d.context_lens;
+  p.W = a.d.table_width;
+  p.S = a.d.num_seqs;
+  p.Hq = a.d.num_q_heads;
+  p.Hkv = c.num_kv_heads;
+  p.G = a.d.num_q_heads / c.num_kv_heads;
+  p.QT = 1;
+  p.num_blocks = c.num_blocks;
+  p.num_items = (int32_t)items;
+  p.win = 0;
+  p.qk_scale = a.d.qk_scale;
+  p.out_scale = a.d.out_scale;
+  pp.qstart = nullptr;
+  pp.tiles = a.geo.tiles;
+  pp.T = a.d.num_seqs;
+  pp.maxq = 1;
+  pp.merge_ml = a.merge_ml;
+  pp.part_o = reinterpret_cast<float*>(a.workspace);
+  pp.part_ml = reinterpret_cast<float*>(a.workspace + a.geo.part_o_bytes);
+  pp.part_o_bytes = (uint32_t)a.geo.part_o_bytes;
+  pp.part_ml_bytes = (uint32_t)a.geo.part_ml_bytes;
+  pp.ctr = reinterpret_cast<uint64_t*>(a.workspace + a.geo.part_o_bytes + a.geo.part_ml_bytes);
+  pp.epoch = a.epoch;
+  pp.prefix_len = a.prefix_len;
+  pp.chunk_len = a.geo.chunk_len;
+  pp.chunks = a.geo.chunks;
+  pp.cpw = a.geo.cpw;
+  return launch_prefix(pp, c.head_dim, c.kv_dtype, c.block_size, (int)((items + 7) / 8 * 8), stream);
 }
 
 }  // namespace pkv

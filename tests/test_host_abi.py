@@ -276,3 +276,30 @@ def test_cache_write_refuses_non_finite_per_tensor_scales():
             sc = pkv.KVScales(ks, vs)
             st = pkv._lib.reshape_and_cache(ctypes.byref(d), 0, P, P, P, 3, ctypes.byref(sc), None)
             assert st == pkv.PKV_ERR_INVALID and "finite" in pkv.last_error(), (dt, ks, vs)
+
+
+def test_shared_prefix_decode_checks_arguments_on_the_host():
+    """The shared-prefix decode's own rules (prefix_len a multiple of B and
+    not negative, a prefix table, the split-context form, no sliding window)
+    come back as status codes before any launch."""
+    P = 1 << 24
+    bf16 = pkv.PKV_KV_BF16
+    sc = pkv.KVScales(1.0, 1.0)
+    d = _fake_pool(bf16)
+    B = d.cfg.block_size
+
+    def call(prefix_len=2 * B, table=P, part=512, window=0):
+        args = pkv.DecodeArgs(out=P, q=P + 4096, pool=ctypes.pointer(d), layer=0, key=None, value=None,
+                              block_tables=P, table_width=4, context_lens=P, num_seqs=2, num_q_heads=4, scale=0.1,
+                              kv_dtype=bf16, kv_scales=ctypes.pointer(sc), partition_size=part,
+                              sliding_window=window, workspace=None, workspace_bytes=0)
+        return pkv._lib.paged_attn_decode_shared_prefix(ctypes.byref(args), table, prefix_len, None)
+
+    assert call(prefix_len=-B) == pkv.PKV_ERR_INVALID and "negative" in pkv.last_error()
+    assert call(prefix_len=B + 1) == pkv.PKV_ERR_INVALID and "multiple" in pkv.last_error()
+    assert call(table=None) == pkv.PKV_ERR_INVALID and "prefix_table" in pkv.last_error()
+    assert call(part=0) == pkv.PKV_ERR_UNSUPPORTED and "split" in pkv.last_error()
+    assert call(window=8) == pkv.PKV_ERR_UNSUPPORTED and "window" in pkv.last_error()
+    assert pkv._lib.paged_attn_decode_shared_prefix(None, P, B, None) == pkv.PKV_ERR_INVALID
+    assert pkv.paged_attn_shared_prefix_workspace_bytes(2, 4, 2, 64, 4, B, bf16, -B) == 0
+    assert pkv.paged_attn_shared_prefix_workspace_bytes(2, 3, 2, 64, 4, B, bf16, B) == 0
