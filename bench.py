@@ -89,6 +89,9 @@ def parse():
                          "(paged_attn_decode_ex; bytes counted over those positions)")
     ap.add_argument("--kv-dtype", default="bf16", choices=sorted(KV_DTYPES),
                     help="KV storage of the pool (8-bit pools hold random codes; the oracle sample runs for bf16 only)")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="with --config cow_prefix: decode through paged_attn_decode_shared_prefix, which reads the "
+                         "93 shared prefix blocks once per KV head instead of once per sequence")
     ap.add_argument("--config", default="", choices=["", "llama8b", "long32k_fp8", "long32k_int8", "cow_prefix"],
                     help="instead of the 70B step: one decode layer of another workload (8B-shaped: 64 seqs, "
                          "ctx 512..4096; 32K quantised: 8 seqs x 32768, block 32, partition 512), rotating over "
@@ -274,7 +277,26 @@ def cow_bench(args):
     vn = torch.randn((S, H, D), generator=g, device=dev).to(torch.bfloat16)
     out = torch.empty((S, H, D), dtype=torch.float32, device=dev)
     P = (W * B + 31) // 32 * 32
-    ws = torch.empty(pkv.paged_attn_workspace_bytes(S, H, D, W, B, P), dtype=torch.uint8, device=dev)
+    prefix_blocks = prefix // B                  # full prefix blocks stay shared for the whole run
+    shared = bool(args.shared_prefix)
+    if shared:
+        # the shared blocks named once: the decode reads them once per KV head
+        d_prefix = torch.from_numpy(np.ascontiguousarray(tab0[0][:prefix_blocks], np.int32)).to(dev)
+        ws = torch.empty(pkv.paged_attn_shared_prefix_workspace_bytes(S, H, H, D, W, B, pkv.PKV_KV_BF16,
+                                                                      prefix_blocks * B),
+                         dtype=torch.uint8, device=dev)
+    else:
+        ws = torch.empty(pkv.paged_attn_workspace_bytes(S, H, D, W, B, P), dtype=torch.uint8, device=dev)
+
+    def decode(o, q, tab, ctx, key=None, value=None, st=None, shared_form=shared):
+        if shared_form:
+            pkv.paged_attn_decode_shared_prefix(o, q, pool, 0, tab, ctx, w.scale, d_prefix, prefix_blocks * B,
+                                                partition_size=P, workspace=ws, key=key, value=value, stream=st)
+        elif key is not None:
+            pkv.paged_attn_decode_append(o, q, pool, 0, key, value, tab, ctx, w.scale, partition_size=P,
+                                         workspace=ws, stream=st)
+        else:
+            pkv.paged_attn_decode(o, q, pool, 0, tab, ctx, w.scale, partition_size=P, workspace=ws, stream=st)
     st = torch.cuda.current_stream()
     # two sets of pinned staging and device tables: the host prepares step
     # i + 1 while the GPU runs step i
@@ -287,11 +309,10 @@ def cow_bench(args):
     t0s, c0s = bm.block_tables(np.arange(S, dtype=np.int32), W)
     td, cd = torch.from_numpy(t0s).to(dev), torch.from_numpy(c0s).to(dev)
     for _ in range(args.warmup):
-        pkv.paged_attn_decode(out, q_all, pool, 0, td, cd, w.scale, partition_size=P, workspace=ws, stream=st)
+        decode(out, q_all, td, cd, st=st)
     torch.cuda.synchronize()
     logical = unique = seq_steps = pairs_total = 0
     ev = []
-    prefix_blocks = prefix // B                  # full prefix blocks stay shared for the whole run
     t_start = time.perf_counter()
     for step in range(steps):
         k = step & 1
@@ -308,8 +329,7 @@ def cow_bench(args):
             pairs_total += pairs.shape[0]
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(st)
-        pkv.paged_attn_decode_append(out[:n], q_all[:n], pool, 0, kn[:n], vn[:n], tab_d[k][:n], ctx_d[k][:n],
-                                     w.scale, partition_size=P, workspace=ws, stream=st)
+        decode(out[:n], q_all[:n], tab_d[k][:n], ctx_d[k][:n], kn[:n], vn[:n], st=st)
         e1.record(st)
         ev.append((e0, e1))
         done[k] = e1
@@ -321,13 +341,27 @@ def cow_bench(args):
     wall = time.perf_counter() - t_start
     gpu = sum(a.elapsed_time(b) for a, b in ev) * 1e-3
     blk_bytes = H * 2 * D * 2 * B
+    # the final shared state through both forms: the shared-prefix decode
+    # against the plain one (the GPU parity tests compare both with the oracle)
+    tf, cf = bm.block_tables(np.arange(S, dtype=np.int32), W)
+    tfd, cfd = torch.from_numpy(tf).to(dev), torch.from_numpy(cf).to(dev)
+    o_a = torch.empty_like(out)
+    o_b = torch.empty_like(out)
+    decode(o_a, q_all, tfd, cfd, st=st)
+    ws_plain = torch.empty(pkv.paged_attn_workspace_bytes(S, H, D, W, B, P), dtype=torch.uint8, device=dev)
+    pkv.paged_attn_decode(o_b, q_all, pool, 0, tfd, cfd, w.scale, partition_size=P, workspace=ws_plain, stream=st)
+    torch.cuda.synchronize()
+    form_diff = float((o_a - o_b).abs().max())
     res = {"metric": "paged decode KV-read GB/s (% of MI355X HBM peak) + decode seq-steps/s",
            "value": round(seq_steps / wall, 1), "unit": "seq-steps/s", "n_gpus": 1, "steps": steps,
            "warmup": args.warmup, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "shared-prefix copy-on-write run: 200 seqs forked from a 1500-token prefix, "
                                   "40q/40kv heads, head_dim 128, bf16 KV, block 16, 64..512 generated tokens each, "
                                   "appending decode per step",
+                      "decode_call": ("paged_attn_decode_shared_prefix (the 93 shared blocks read once per KV head)"
+                                      if shared else "paged_attn_decode_append"),
                       "seq_steps": seq_steps, "cow_pairs": pairs_total},
+           "final_state_max_abs_diff_vs_plain_decode": form_diff,
            "wall_s": round(wall, 4), "decode_gpu_s": round(gpu, 4),
            "logical_kv_gbs_decode": round(logical / gpu / 1e9, 1),
            "unique_kv_gbs_decode": round(unique / gpu / 1e9, 1),

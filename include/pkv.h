@@ -416,9 +416,9 @@ pkv_status paged_attn_decode_noalloc(const pkv_decode_args* args, hipStream_t st
  *   2. a second launch attends, per KV head, the prefix positions
  *      [0, min(ctx_s, prefix_len)) of all (sequence, query head) pairs
  *      together - their queries are the columns of the matrix-core products,
- *      as paged_attn_prefill's tokens are - in key chunks, and the last chunk
- *      of a column span to finish merges the chunks' partial states with
- *      the first pass's rows (exact softmax merge, fp32).
+ *      as paged_attn_prefill's tokens are; a workgroup's four waves share
+ *      its columns and split the prefix's keys - and merges the partial
+ *      states with the first pass's rows (exact softmax merge, fp32).
  *   args          as for paged_attn_decode_ex (plain or appending form, every
  *                 storage type); partition_size must be positive and
  *                 sliding_window 0, else PKV_ERR_UNSUPPORTED; the workspace
@@ -441,10 +441,10 @@ pkv_status paged_attn_decode_shared_prefix(const pkv_decode_args* args, const in
                                            int32_t prefix_len, hipStream_t stream);
 
 /* Workspace bytes paged_attn_decode_shared_prefix needs on the current
- * device (the split form's workspace, each row's softmax state, the folded
- * query for storage with K channel scales, and the prefix pass's partial
- * states - one per key chunk and (sequence, query head) - and counters);
- * 0 for sizes that are invalid or too large for one call. */
+ * device for any batch of at most num_seqs sequences (the split form's
+ * workspace, each row's softmax state, and the folded query for storage
+ * with K channel scales); 0 for sizes that are invalid or too large for one
+ * call. */
 uint64_t paged_attn_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                                   int32_t head_dim, int32_t table_width, int32_t block_size,
                                                   int32_t kv_dtype, int32_t prefix_len);

@@ -1702,7 +1702,6 @@ struct SharedPrefixCall {
   int32_t prefix_len;
   float* ml;               // [S][Hq] (m, l) of the rows the split pass writes
   uint16_t* qfold;         // [S][Hq][2 D] the query with K channel scales folded in (those storage types)
-  char* pass_ws;           // the prefix pass's partials and counters
   PrefixPassGeometry geo;
 };
 
@@ -1939,8 +1938,6 @@ pkv_status decode_impl(float* out, const void* q, const pkv_pool* pool, int32_t 
       a.d.vs_ch = channel ? vsl : nullptr;
       a.prefix_len = sp->prefix_len;
       a.merge_ml = sp->ml;
-      a.workspace = sp->pass_ws;
-      a.epoch = next_epoch();
       a.geo = sp->geo;
       e = launch_prefix_pass(a, stream);
     }
@@ -1998,24 +1995,20 @@ extern "C" pkv_status paged_attn_decode_noalloc(const pkv_decode_args* a, hipStr
 namespace {
 
 // Workspace layout of a shared-prefix decode: the split form's regions, the
-// rows' (m, l), the folded query (storage with K channel scales), then the
-// prefix pass's partials and counters.
+// rows' (m, l), then the folded query (storage with K channel scales).
 struct SharedPrefixSizes {
-  uint64_t split, ml, qfold, pass, total;
+  uint64_t split, ml, qfold, total;
   PrefixPassGeometry geo;
 };
 bool shared_prefix_sizes(int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t W, int32_t B, int32_t kvt,
                          int32_t prefix_len, SharedPrefixSizes* z) {
   SplitSizes sz;
   if (!split_sizes(S, Hq, 0, D, W, B, 1, &sz)) return false;
-  int cus = 0;
-  if (device_cus(&cus) != 0) return false;
-  if (!prefix_pass_geometry(S, Hq, Hkv, D, kvt, B, prefix_len, cus, &z->geo)) return false;
+  if (!prefix_pass_geometry(S, Hq, Hkv, D, kvt, B, prefix_len, &z->geo)) return false;
   z->split = (uint64_t)(sz.cnt_bytes + sz.ml_bytes + sz.acc_bytes);
   z->ml = align_up((uint64_t)S * Hq * 2 * sizeof(float));
   z->qfold = has_k_channel_scales(kvt) ? align_up((uint64_t)S * Hq * 2 * D * sizeof(uint16_t)) : 0;
-  z->pass = z->geo.part_o_bytes + z->geo.part_ml_bytes + z->geo.ctr_bytes;
-  z->total = z->split + z->ml + z->qfold + z->pass;
+  z->total = z->split + z->ml + z->qfold;
   return true;
 }
 
@@ -2033,7 +2026,7 @@ extern "C" uint64_t paged_attn_shared_prefix_workspace_bytes(int32_t num_seqs, i
   if (!shared_prefix_sizes(num_seqs, num_q_heads, num_kv_heads, head_dim, table_width, block_size, kv_dtype,
                            prefix_len, &z))
     return 0;
-  return z.total;
+  return z.total;   // every region grows with num_seqs: it also serves smaller batches
 }
 
 extern "C" pkv_status paged_attn_decode_shared_prefix(const pkv_decode_args* a, const int32_t* prefix_table,
@@ -2081,7 +2074,6 @@ extern "C" pkv_status paged_attn_decode_shared_prefix(const pkv_decode_args* a, 
   sp.prefix_len = prefix_len;
   sp.ml = reinterpret_cast<float*>(ws + z.split);
   sp.qfold = z.qfold ? reinterpret_cast<uint16_t*>(ws + z.split + z.ml) : nullptr;
-  sp.pass_ws = ws + z.split + z.ml + z.qfold;
   sp.geo = z.geo;
   return decode_impl(a->out, a->q, a->pool, a->layer, a->key, a->value, a->block_tables, a->table_width,
                      a->context_lens, a->num_seqs, a->num_q_heads, a->scale, a->kv_dtype, a->kv_scales,

@@ -112,25 +112,19 @@ hipError_t launch_prefill_as_decode(const PrefillDecodeArgs& a, hipStream_t stre
 // The shared-prefix pass of a decode (prefill_kernels.hip): for every KV
 // head, the (sequence, head) pairs of all sequences attend the shared prefix
 // (positions [0, min(ctx_s, prefix_len)), read through d.block_tables = the
-// prefix table of d.table_width entries), cut into key chunks; the last
-// chunk to finish merges the chunks with the result already in d.out, whose
-// (m, l) per row are in merge_ml.  d.sliding_window must be 0.
+// prefix table of d.table_width entries), and their results are merged with
+// the result already in d.out, whose (m, l) per row are in merge_ml.
+// d.sliding_window must be 0.
 struct PrefixPassGeometry {
-  int32_t tiles;       // column spans per KV head
-  int32_t cpw;         // columns per wave (multiple of 16)
-  int32_t chunks;      // key chunks
-  int32_t chunk_len;   // positions per chunk (multiple of 32)
-  uint64_t part_o_bytes, part_ml_bytes, ctr_bytes;   // workspace regions, 256-byte multiples
+  int32_t tiles;       // column groups per KV head (one workgroup each)
+  int32_t chunk_len;   // prefix positions per wave (multiple of 32)
 };
 bool prefix_pass_geometry(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                          int32_t kv_dtype, int32_t block_size, int32_t prefix_len, int cus,
-                          PrefixPassGeometry* g);
+                          int32_t kv_dtype, int32_t block_size, int32_t prefix_len, PrefixPassGeometry* g);
 struct PrefixPassArgs {
   PrefillDecodeArgs d;
   int32_t prefix_len;
   const float* merge_ml;   // [S][Hq] (m, l) of d.out's rows
-  char* workspace;         // part_o, part_ml, counters of the geometry, in that order
-  uint32_t epoch;
   PrefixPassGeometry geo;
 };
 hipError_t launch_prefix_pass(const PrefixPassArgs& a, hipStream_t stream);

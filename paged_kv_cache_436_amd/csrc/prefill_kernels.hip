@@ -176,23 +176,15 @@ struct PrefillParams {
   // The shared-prefix pass of a decode (pa_prefix_kernel only): the columns
   // of KV head g are the (sequence, head) pairs of all T sequences; column
   // (s, h) attends positions [0, min(ctx_s, prefix_len)) of the shared
-  // prefix, whose blocks are row 0 of d.bt (width d.W).  The prefix is cut
-  // into `chunks` key ranges of chunk_len positions (a multiple of kStep),
-  // one per workgroup; each writes its columns' partial results (normalised
-  // output and (m, l)), and the last of a column span's chunks merges them
-  // with the result of the other positions already in out (their (m, l) in
-  // merge_ml) into out.
+  // prefix, whose blocks are row 0 of d.bt (width d.W).  The four waves of a
+  // workgroup take the same 16 prefill_nt() columns and split the prefix
+  // into key ranges of chunk_len positions (a multiple of kStep); their
+  // partial results meet in LDS, where they are merged with the result of
+  // the other positions already in out (its (m, l) in merge_ml) into out.
   const float* merge_ml;      // [T][Hq] (m, l) of out's rows
-  float* part_o;              // [chunks][T][Hq][D] partial outputs
-  float* part_ml;             // [chunks][T][Hq] partial (m, l)
-  uint32_t part_o_bytes, part_ml_bytes;
-  uint64_t* ctr;              // [Hkv][tiles][kNW] x kPrefixCounterStride, epoch-tagged arrival counts
-  uint32_t epoch;
-  int32_t prefix_len, chunk_len, chunks;
-  int32_t cpw;                // columns per wave: a multiple of 16, at most 16 prefill_nt()
+  int32_t prefix_len, chunk_len;
 };
 
-constexpr int kPrefixCounterStride = 16;   // uint64 words per arrival counter (one per 128-byte line)
 constexpr int kPrefixBuf = 3;              // K/V steps held per wave in the shared-prefix pass
 
 __device__ __forceinline__ int wave_max_i(int v) {
@@ -206,78 +198,9 @@ __device__ __forceinline__ int wave_min_i(int v) {
   return v;
 }
 
-constexpr int kMaxPrefixChunks = 16;
-
-// The end of a shared-prefix pass wave: count this wave's arrival on the
-// counter of its (KV head, column span, wave) and, if it is the last of the
-// `chunks` key ranges to arrive, merge every chunk's partial of its columns
-// with the result of the other positions in out: with the (m, l) of each
-// part (reference max of the scaled logits in log2 units and the sum
-// relative to it, l = 0 for a part that attended nothing), weight w = l
-// 2^(m - M) over M the largest m of a non-empty part, out = sum w o / sum w
-// (zero when every part is empty).  Lane (j, row) merges column row of each
-// tile, dims j D / 4 .. (j + 1) D / 4 - 1.
-template <int D>
-__device__ __forceinline__ void prefix_merge(const PrefillParams& pp, int g, int ct, int w, int c0, int cols,
-                                             __amdgpu_buffer_rsrc_t por, __amdgpu_buffer_rsrc_t pmr, int lane) {
-  const DecodeParams& p = pp.d;
-  // the partial stores have completed (agent scope: visible to every XCD)
-  // before the arrival is counted
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  wait_vm_all();
-  int arrived = 0;
-  if (lane == 0) {
-    uint64_t* c = pp.ctr + ((int64_t)(g * pp.tiles + ct) * kNW + w) * kPrefixCounterStride;
-    arrived = report_total(c, pp.epoch, 1, report_steps(c, pp.epoch, 1));
-  }
-  if (__shfl(arrived, 0, kWave) != pp.chunks) return;
-  // the loads below follow the counter update that found every chunk in
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  constexpr int DL = D / 4;            // dims per lane
-  const int row = lane & 15;
-  const int j = lane >> 4;
-  const int TH = pp.T * p.Hq;
-  for (int cl = row; cl < cols; cl += 16) {
-    const int cq = c0 + cl;
-    const int64_t oi = (int64_t)(cq / p.G) * p.Hq + g * p.G + cq % p.G;
-    float* orow = p.out + oi * D + j * DL;
-    const f32x2 mls = *reinterpret_cast<const f32x2*>(pp.merge_ml + oi * 2);
-    f32x2 mlk[kMaxPrefixChunks];
-    float M = mls[1] > 0.f ? mls[0] : -INFINITY;
-#pragma unroll
-    for (int k = 0; k < kMaxPrefixChunks; ++k) {
-      if (k < pp.chunks) {
-        mlk[k] = ld_agent2(pmr, ((uint32_t)k * (uint32_t)TH + (uint32_t)oi) * 8u);
-        if (mlk[k][1] > 0.f) M = fmaxf(M, mlk[k][0]);
-      }
-    }
-    float W = 0.f;
-    f32x4 a[DL / 4];
-    {
-      const float ws = mls[1] > 0.f ? mls[1] * __builtin_amdgcn_exp2f(mls[0] - M) : 0.f;
-      W += ws;
-#pragma unroll
-      for (int u = 0; u < DL / 4; ++u) a[u] = ws * *reinterpret_cast<const f32x4*>(orow + 4 * u);
-    }
-#pragma unroll
-    for (int k = 0; k < kMaxPrefixChunks; ++k) {
-      if (k < pp.chunks) {
-        const float wk = mlk[k][1] > 0.f ? mlk[k][1] * __builtin_amdgcn_exp2f(mlk[k][0] - M) : 0.f;
-        W += wk;
-        const uint32_t base = (((uint32_t)k * (uint32_t)TH + (uint32_t)oi) * (uint32_t)D + (uint32_t)(j * DL)) * 4u;
-#pragma unroll
-        for (int u = 0; u < DL / 4; ++u) a[u] += wk * ld_agent4(por, (int)(base + 16u * (uint32_t)u));
-      }
-    }
-    const float inv = W > 0.f ? 1.f / W : 0.f;
-#pragma unroll
-    for (int u = 0; u < DL / 4; ++u) *reinterpret_cast<f32x4*>(orow + 4 * u) = a[u] * inv;
-  }
-}
-
 // The body of both kernels: SH selects the shared-prefix pass (columns
-// across sequences, one key chunk per workgroup, partials merged by the last
-// chunk) over the prefill (columns of one sequence's chunk, causal).
+// across sequences, the prefix's keys split over a workgroup's waves and
+// merged in LDS) over the prefill (columns of one sequence's chunk, causal).
 template <int D, int KVT, int B, int NT, int NB, bool SH>
 __device__ __forceinline__ void prefill_body(const PrefillParams& pp) {
   const DecodeParams& p = pp.d;
@@ -305,12 +228,11 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& pp) {
   const int item = xcd * per_xcd + (int)blockIdx.x / 8;
   if (item >= p.num_items) return;
   // prefill: item = (sequence s, KV head g, column span ct); shared-prefix
-  // pass: (KV head g, key chunk kc, column span ct), the spans of one chunk
-  // adjacent so that they read its keys from one L2
+  // pass: (KV head g, column group ct), the groups of a head adjacent so
+  // that they read its keys through one L2
   const int ct = item % pp.tiles;
-  const int g = SH ? item / (pp.tiles * pp.chunks) : (item / pp.tiles) % p.Hkv;
+  const int g = SH ? item / pp.tiles : (item / pp.tiles) % p.Hkv;
   const int s = SH ? 0 : item / (pp.tiles * p.Hkv);
-  const int kc = SH ? (item / pp.tiles) % pp.chunks : 0;
   const int lane = threadIdx.x % kWave;
   const int w = threadIdx.x / kWave;
   const int row = lane & 15;
@@ -319,15 +241,17 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& pp) {
   const int q0 = SH ? 0 : (pp.qstart ? min(max(pp.qstart[s], 0), pp.T) : s);
   const int n = SH ? pp.T : (pp.qstart ? min(max(pp.qstart[s + 1], q0), pp.T) - q0 : 1);
   const int ncol = (SH ? n : min(n, pp.maxq)) * p.G;   // positions still follow the whole chunk
-  const int cpw = SH ? pp.cpw : 16 * NT;         // columns per wave
-  const int c0 = (ct * kNW + w) * cpw;           // this wave's first column
-  if (c0 >= ncol) return;                        // no barrier follows: waves are independent
+  constexpr int cpw = 16 * NT;                   // columns per wave
+  // this wave's first column (the shared-prefix pass: the workgroup's, the
+  // same for its four waves, so that they leave together or not at all)
+  const int c0 = SH ? ct * cpw : (ct * kNW + w) * cpw;
+  if (c0 >= ncol) return;                        // prefill: no barrier follows, waves are independent
   const int cols = min(cpw, ncol - c0);
 
   const int ctx = SH ? pp.prefix_len : clamp_ctx(p.ctx[s], p.W * B);
   const int first = ctx - n;                     // position of the chunk's token 0
-  // shared-prefix pass: this workgroup's keys [k0, k1) of the prefix
-  const int k0 = SH ? kc * pp.chunk_len : 0;
+  // shared-prefix pass: this wave's keys [k0, k1) of the prefix
+  const int k0 = SH ? w * pp.chunk_len : 0;
   const int k1 = SH ? min(k0 + pp.chunk_len, pp.prefix_len) : 0;
   // a column's keys end at its limit; t_end is the wave's largest limit and
   // every valid column sees the keys below lim_lo (its smallest): steps
@@ -660,25 +584,20 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& pp) {
 
   // outputs: column `row` of tile nt; this lane holds dims acc_dim(cc, j, .).
   // The shared-prefix pass writes them, and the column's (m, l), as this
-  // chunk's partial, with the coherent-level policy (the merging wave may be
-  // on another XCD).
-  const int TH = pp.T * p.Hq;
-  const __amdgpu_buffer_rsrc_t por = __builtin_amdgcn_make_buffer_rsrc(pp.part_o, (short)0, pp.part_o_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t pmr = __builtin_amdgcn_make_buffer_rsrc(pp.part_ml, (short)0, pp.part_ml_bytes, 0x00020000);
+  // wave's partial into LDS.
+  constexpr int kPartFloats = SH ? kNW * NT * 16 * D : 1;
+  __shared__ __attribute__((aligned(16))) float lds_o[kPartFloats];
+  __shared__ f32x2 lds_ml[SH ? kNW * NT * 16 : 1];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int cl = 16 * nt + row;
     const float L = sum_x32(sum_x16(l_run[nt]));
     if (cl >= cols) continue;
     const int cq = c0 + cl;
-    const int64_t orow_i = (int64_t)(q0 + cq / p.G) * p.Hq + g * p.G + cq % p.G;   // output row (sequence, head)
-    float* orow = p.out + orow_i * D;
-    const uint32_t prow = SH ? ((uint32_t)kc * (uint32_t)TH + (uint32_t)orow_i) * (uint32_t)(D * 4) : 0u;
+    float* orow = p.out + ((int64_t)(q0 + cq / p.G) * p.Hq + g * p.G + cq % p.G) * D;
+    float* prow = lds_o + ((w * NT + nt) * 16 + row) * D;
     auto put = [&](int d, f32x4 v) __attribute__((always_inline)) {   // dims d .. d + 3
-      if constexpr (SH)
-        st_agent4(por, (int)(prow + 4u * (uint32_t)d), v);
-      else
-        *reinterpret_cast<f32x4*>(orow + d) = v;
+      *reinterpret_cast<f32x4*>((SH ? prow : orow) + d) = v;
     };
     const float inv = L > 0.f ? 1.f / L : 0.f;   // no key at all (position < 0): zero row
     float o[T::NC][4];
@@ -712,10 +631,51 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& pp) {
           put(64 * u + 16 * j + 4 * i2, f32x4{o[4 * u][i2], o[4 * u + 1][i2], o[4 * u + 2][i2], o[4 * u + 3][i2]});
     }
     if constexpr (SH) {
-      if (j == 0) st_agent2(pmr, ((uint32_t)kc * (uint32_t)TH + (uint32_t)orow_i) * 8u, m_run[nt], L);
+      if (j == 0) lds_ml[(w * NT + nt) * 16 + row] = f32x2{m_run[nt], L};
     }
   }
-  if constexpr (SH) prefix_merge<D>(pp, g, ct, w, c0, cols, por, pmr, lane);
+  if constexpr (SH) {
+    // Wave nt (< NT) merges tile nt's columns: the four waves' partials and
+    // the result of the other positions in out.  With (m, l) per part
+    // (reference max of the scaled logits in log2 units, sum relative to
+    // it; l = 0 for a part that attended nothing), weight w = l 2^(m - M)
+    // over M the largest m of a non-empty part; out = sum w o / sum w, zero
+    // when every part is empty.  Lane (j, row): column row, dims j D / 4 ..
+    __syncthreads();
+    if (w >= NT) return;
+    constexpr int DL = D / 4;
+    const int cl = 16 * w + row;
+    if (cl >= cols) return;
+    const int cq = c0 + cl;
+    const int64_t oi = (int64_t)(cq / p.G) * p.Hq + g * p.G + cq % p.G;
+    float* orow = p.out + oi * D + j * DL;
+    const f32x2 mls = *reinterpret_cast<const f32x2*>(pp.merge_ml + oi * 2);
+    f32x4 a[DL / 4];
+#pragma unroll
+    for (int u = 0; u < DL / 4; ++u) a[u] = *reinterpret_cast<const f32x4*>(orow + 4 * u);
+    f32x2 ml[kNW];
+    float M = mls[1] > 0.f ? mls[0] : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kNW; ++k) {
+      ml[k] = lds_ml[(k * NT + w) * 16 + row];
+      if (ml[k][1] > 0.f) M = fmaxf(M, ml[k][0]);
+    }
+    const float ws = mls[1] > 0.f ? mls[1] * __builtin_amdgcn_exp2f(mls[0] - M) : 0.f;
+    float W = ws;
+#pragma unroll
+    for (int u = 0; u < DL / 4; ++u) a[u] = a[u] * ws;
+#pragma unroll
+    for (int k = 0; k < kNW; ++k) {
+      const float wk = ml[k][1] > 0.f ? ml[k][1] * __builtin_amdgcn_exp2f(ml[k][0] - M) : 0.f;
+      W += wk;
+      const float* src = lds_o + ((k * NT + w) * 16 + row) * D + j * DL;
+#pragma unroll
+      for (int u = 0; u < DL / 4; ++u) a[u] += wk * *reinterpret_cast<const f32x4*>(src + 4 * u);
+    }
+    const float inv = W > 0.f ? 1.f / W : 0.f;
+#pragma unroll
+    for (int u = 0; u < DL / 4; ++u) *reinterpret_cast<f32x4*>(orow + 4 * u) = a[u] * inv;
+  }
 }
 
 template <int D, int KVT, int B>
@@ -797,40 +757,26 @@ hipError_t launch_prefill_as_decode(const PrefillDecodeArgs& a, hipStream_t stre
   return launch_prefill(pp, c.head_dim, c.kv_dtype, c.block_size, (int)((items + 7) / 8 * 8), stream);
 }
 
-// Geometry of the shared-prefix pass: column spans of at most kNW waves of
-// 16 prefill_nt() columns, balanced so that the waves of a head carry about
-// the same number of columns, and enough key chunks that the workgroups
-// cover the compute units about once.
+// Geometry of the shared-prefix pass: workgroups of 16 prefill_nt()
+// columns of one KV head, whose four waves split the prefix's steps evenly.
 bool prefix_pass_geometry(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                          int32_t kv_dtype, int32_t block_size, int32_t prefix_len, int cus,
-                          PrefixPassGeometry* g) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || prefix_len <= 0 || cus <= 0) return false;
+                          int32_t kv_dtype, int32_t block_size, int32_t prefix_len, PrefixPassGeometry* g) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || prefix_len <= 0) return false;
   const int64_t G = num_q_heads / num_kv_heads;
   const int64_t ncol = (int64_t)num_seqs * G;
-  const int64_t span = 16 * (int64_t)prefill_tiles_per_wave(head_dim, kv_dtype, block_size) * kNW;
-  const int64_t tiles = (ncol + span - 1) / span;
-  const int64_t per_wave = (ncol + kNW * tiles - 1) / (kNW * tiles);
+  const int64_t cols = 16 * (int64_t)prefill_tiles_per_wave(head_dim, kv_dtype, block_size);
+  const int64_t tiles = (ncol + cols - 1) / cols;
   const int64_t steps = ((int64_t)prefix_len + kStep - 1) / kStep;
-  const int64_t want = ((int64_t)cus + num_kv_heads * tiles - 1) / (num_kv_heads * tiles);
-  int64_t chunks = std::max<int64_t>(1, std::min<int64_t>({want, (int64_t)kMaxPrefixChunks, steps}));
-  const int64_t chunk_len = (steps + chunks - 1) / chunks * kStep;
-  chunks = ((int64_t)prefix_len + chunk_len - 1) / chunk_len;
-  const int64_t items = (int64_t)num_kv_heads * tiles * chunks;
-  if (items > INT32_MAX / 2 || tiles > INT32_MAX) return false;
+  const int64_t items = (int64_t)num_kv_heads * tiles;
+  if (items > INT32_MAX / 2) return false;
   g->tiles = (int32_t)tiles;
-  g->cpw = (int32_t)((per_wave + 15) / 16 * 16);
-  g->chunks = (int32_t)chunks;
-  g->chunk_len = (int32_t)chunk_len;
-  const uint64_t rows = (uint64_t)num_seqs * (uint64_t)num_q_heads;
-  g->part_o_bytes = align_up((uint64_t)chunks * rows * (uint64_t)head_dim * sizeof(float));
-  g->part_ml_bytes = align_up((uint64_t)chunks * rows * 2 * sizeof(float));
-  g->ctr_bytes = align_up((uint64_t)num_kv_heads * tiles * kNW * kPrefixCounterStride * sizeof(uint64_t));
-  return g->part_o_bytes < (1ull << 32) && g->part_ml_bytes < (1ull << 32);
+  g->chunk_len = (int32_t)((steps + kNW - 1) / kNW * kStep);
+  return true;
 }
 
 hipError_t launch_prefix_pass(const PrefixPassArgs& a, hipStream_t stream) {
   const pkv_pool_config& c = a.d.pool->cfg;
-  const int64_t items = (int64_t)c.num_kv_heads * a.geo.tiles * a.geo.chunks;
+  const int64_t items = (int64_t)c.num_kv_heads * a.geo.tiles;
   PrefillParams pp{};
   DecodeParams& p = pp.d;
   p.q = a.d.q;
@@ -859,16 +805,8 @@ hipError_t launch_prefix_pass(const PrefixPassArgs& a, hipStream_t stream) {
   pp.T = a.d.num_seqs;
   pp.maxq = 1;
   pp.merge_ml = a.merge_ml;
-  pp.part_o = reinterpret_cast<float*>(a.workspace);
-  pp.part_ml = reinterpret_cast<float*>(a.workspace + a.geo.part_o_bytes);
-  pp.part_o_bytes = (uint32_t)a.geo.part_o_bytes;
-  pp.part_ml_bytes = (uint32_t)a.geo.part_ml_bytes;
-  pp.ctr = reinterpret_cast<uint64_t*>(a.workspace + a.geo.part_o_bytes + a.geo.part_ml_bytes);
-  pp.epoch = a.epoch;
   pp.prefix_len = a.prefix_len;
   pp.chunk_len = a.geo.chunk_len;
-  pp.chunks = a.geo.chunks;
-  pp.cpw = a.geo.cpw;
   return launch_prefix(pp, c.head_dim, c.kv_dtype, c.block_size, (int)((items + 7) / 8 * 8), stream);
 }
 

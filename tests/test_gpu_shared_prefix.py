@@ -6,8 +6,9 @@ block of 0xFF bytes (NaN bf16 / NaN e5m2 / -1 codes with NaN scales) that
 is never written: a read of the own row below the prefix would reach the
 output.  Contexts cover the empty sequence, contexts that end inside the
 prefix or exactly at its end, and ones running past it; sizes cover several
-key chunks and column spans of the prefix pass, every storage type, block
-sizes 8 / 16 / 32, head dims 64 / 128 and GQA groups of 1, 3 and 4 heads.
+column groups per KV head in the prefix pass and prefixes split over its
+waves, every storage type, block sizes 8 / 16 / 32, head dims 64 / 128 and
+GQA groups of 1, 3 and 4 heads.
 """
 
 import math
@@ -141,10 +142,10 @@ def test_shared_prefix_matches_oracle(dt, D, B, hkv, G):
 
 
 @pytest.mark.parametrize("dt", [pkv.PKV_KV_BF16, pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT4])
-def test_many_sequences_span_several_chunks_and_column_spans(dt):
-    """200 sequences of one KV head group size 1 (the shared-prompt batch's
-    shape, fewer heads): the prefix pass cuts the columns into more than one
-    span and the prefix into several key chunks."""
+def test_many_sequences_span_several_column_groups(dt):
+    """200 sequences with one query head per KV head (the shared-prompt
+    batch's shape, fewer heads): the prefix pass takes several column groups
+    per KV head, each splitting the 1488-position prefix over its waves."""
     rng = np.random.default_rng(14500 + dt)
     B = 16
     ctx = [1488 + int(x) for x in rng.integers(1, 96, size=200)]
@@ -226,3 +227,25 @@ def test_shared_prefix_repeats_bit_for_bit():
     a, _ = _run(c, ws=ws)
     b, _ = _run(c, ws=ws)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_workspace_sized_for_a_batch_serves_every_smaller_batch():
+    """The workspace for 200 sequences also serves a call over the first n
+    of them."""
+    import torch
+    rng = np.random.default_rng(14900)
+    ctx = [1488 + int(x) for x in rng.integers(1, 64, size=200)]
+    c = _case(rng, pkv.PKV_KV_BF16, 93, ctx, 4, 1, 128, 16)
+    nbytes = pkv.paged_attn_shared_prefix_workspace_bytes(200, 4, 4, 128, c.width, 16, pkv.PKV_KV_BF16, c.P)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(128)))
+    want = _want(c, scale)
+    for n in (200, 191, 150, 97, 48, 1):
+        assert pkv.paged_attn_shared_prefix_workspace_bytes(n, 4, 4, 128, c.width, 16, pkv.PKV_KV_BF16, c.P) <= nbytes
+        out = torch.full((n, 4, 128), float("nan"), dtype=torch.float32, device="cuda")
+        pkv.paged_attn_decode_shared_prefix(out, c.d_q[:n], c.pool, 1, c.d_tables[:n], c.d_ctx[:n], scale,
+                                            c.d_prefix, c.P, workspace=ws)
+        torch.cuda.synchronize()
+        mx, rel = errors(out.cpu().numpy(), want[:n])
+        say(f"shared prefix n={n}: max_abs={mx:.3e} rel={rel:.3e}")
+        assert mx <= 1e-2 and rel <= 1e-3, n
