@@ -25,6 +25,7 @@ the same workload.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -210,11 +211,14 @@ def config_bench(args):
     torch.cuda.synchronize()
     K = 3 * args.steps
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gc.collect()
+    gc.disable()                      # no garbage-collector pass between the timed launches
     e0.record(st)
     for i in range(K):
         call(i)
     e1.record(st)
     torch.cuda.synchronize()
+    gc.enable()
     per = e0.elapsed_time(e1) * 1e-3 / K
     tok = int(np.asarray(w.context_lens, np.int64).sum())
     nbytes = tok * Hkv * (2 * D * e + (8 if kvt == pkv.PKV_KV_INT8 else 0))
@@ -300,30 +304,51 @@ def cow_bench(args):
     st = torch.cuda.current_stream()
     # two sets of pinned staging and device tables: the host prepares step
     # i + 1 while the GPU runs step i
-    tab_h = [torch.empty((S, W), dtype=torch.int32, pin_memory=True) for _ in range(2)]
-    ctx_h = [torch.empty(S, dtype=torch.int32, pin_memory=True) for _ in range(2)]
-    tab_d = [torch.empty((S, W), dtype=torch.int32, device=dev) for _ in range(2)]
-    ctx_d = [torch.empty(S, dtype=torch.int32, device=dev) for _ in range(2)]
+    # (tables and lengths share one staging buffer: one host-to-device copy per step)
+    stage_h = [torch.empty(S * W + S, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+    stage_d = [torch.empty(S * W + S, dtype=torch.int32, device=dev) for _ in range(2)]
+    tab_h = [b[:S * W].view(S, W) for b in stage_h]
+    ctx_h = [b[S * W:] for b in stage_h]
+    tab_d = [b[:S * W].view(S, W) for b in stage_d]
+    ctx_d = [b[S * W:] for b in stage_d]
     done = [None, None]
     # warm-up: decodes of the shared state (no append, nothing changes)
     t0s, c0s = bm.block_tables(np.arange(S, dtype=np.int32), W)
     td, cd = torch.from_numpy(t0s).to(dev), torch.from_numpy(c0s).to(dev)
     for _ in range(args.warmup):
         decode(out, q_all, td, cd, st=st)
+    # the block copy the first step makes runs once untimed too (between two
+    # blocks that hold nothing yet), so that no first-launch cost of its
+    # kernel lands inside the timed run
+    spare = np.setdiff1d(np.arange(w.num_blocks), t0s[:, :prefix_blocks + 1])[:2]
+    pkv.copy_blocks(pool, torch.from_numpy(spare.reshape(1, 2).astype(np.int64)).to(dev), stream=st)
+    for k in range(2):                # and so do the staging uploads and the timing events
+        stage_d[k].copy_(stage_h[k], non_blocking=True)
+    ew = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ew[0].record(st)
+    ew[1].record(st)
     torch.cuda.synchronize()
     logical = unique = seq_steps = pairs_total = 0
     ev = []
+    waited = 0.0                      # host time spent waiting for the GPU (staging reuse)
+    marks = []                        # host clock at each step's start
+    # no garbage-collector pass inside the timed run (a full pass over the
+    # process's objects stalled one step for ~37 ms)
+    gc.collect()
+    gc.disable()
     t_start = time.perf_counter()
     for step in range(steps):
+        marks.append(time.perf_counter())
         k = step & 1
         active = np.nonzero(gen > step)[0].astype(np.int32)
         n = active.size
         slots, pairs = bm.append(active)
         if done[k] is not None:
-            done[k].synchronize()     # the copies out of this staging set (two steps ago) are done
+            tw = time.perf_counter()
+            done[k].synchronize()     # the copy out of this staging set (two steps ago) is done
+            waited += time.perf_counter() - tw
         tab_np, ctx_np = bm.block_tables(active, W, out=tab_h[k].numpy()[:n], ctx_out=ctx_h[k].numpy()[:n])
-        tab_d[k][:n].copy_(tab_h[k][:n], non_blocking=True)
-        ctx_d[k][:n].copy_(ctx_h[k][:n], non_blocking=True)
+        stage_d[k].copy_(stage_h[k], non_blocking=True)
         if pairs.shape[0]:
             pkv.copy_blocks(pool, torch.from_numpy(pairs).to(dev, non_blocking=False), stream=st)
             pairs_total += pairs.shape[0]
@@ -339,6 +364,7 @@ def cow_bench(args):
         seq_steps += n
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    gc.enable()
     gpu = sum(a.elapsed_time(b) for a, b in ev) * 1e-3
     blk_bytes = H * 2 * D * 2 * B
     # the final shared state through both forms: the shared-prefix decode
@@ -363,6 +389,9 @@ def cow_bench(args):
                       "seq_steps": seq_steps, "cow_pairs": pairs_total},
            "final_state_max_abs_diff_vs_plain_decode": form_diff,
            "wall_s": round(wall, 4), "decode_gpu_s": round(gpu, 4),
+           "host_wait_s": round(waited, 4),
+           "longest_steps_ms": [[int(i), round(float(d) * 1e3, 3)] for d, i in
+                                sorted(zip(np.diff(marks + [t_start + wall]), range(steps)), reverse=True)[:4]],
            "logical_kv_gbs_decode": round(logical / gpu / 1e9, 1),
            "unique_kv_gbs_decode": round(unique / gpu / 1e9, 1),
            "unique_pct_of_hbm_peak": round(100 * unique / gpu / 1e9 / HBM_PEAK_GBS, 2),
@@ -832,11 +861,14 @@ def main():
     torch.cuda.synchronize()
     log("warmup done")
     kv_bytes.clear()
+    gc.collect()
+    gc.disable()                      # no garbage-collector pass inside the timed steps
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i, True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    gc.enable()
     elapsed = t1 - t0
     ms_per_step = elapsed * 1e3 / args.steps
     kv_per_step = sum(kv_bytes) / args.steps
