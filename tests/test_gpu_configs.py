@@ -339,6 +339,22 @@ def test_shared_prefix_copy_on_write_run():
     got = _decode(pool, q, tab, ctx, w.scale, P, H)
     want = attention.paged_decode(q, img, 0, tab, ctx, w.scale)
     _bars(got, want, 1e-2, 1e-3, "COW final, all sequences")
+    # the same state through the shared-prefix decode: the 93 full prefix
+    # blocks named once, read once per KV head
+    import torch
+    pb = prefix // B
+    assert all(np.array_equal(tab[s_, :pb], tab0[0][:pb]) for s_ in range(S))
+    ws = torch.empty(pkv.paged_attn_shared_prefix_workspace_bytes(S, H, H, D, W, B, pkv.PKV_KV_BF16, pb * B),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.full((S, H, D), float("nan"), dtype=torch.float32, device="cuda")
+    say("COW final decode through the shared-prefix form")
+    pkv.paged_attn_decode_shared_prefix(out, bf16_dev(q), pool, 0, dev(tab), dev(ctx), w.scale,
+                                        dev(np.ascontiguousarray(tab0[0][:pb], np.int32)), pb * B,
+                                        partition_size=P, workspace=ws)
+    torch.cuda.synchronize()
+    want_sp = attention.paged_decode_shared_prefix(q, img, 0, tab, ctx, tab0[0][:pb], pb * B, w.scale)
+    assert np.array_equal(want_sp, want)          # tables that name the shared blocks: the same decode
+    _bars(out.cpu().numpy(), want, 1e-2, 1e-3, "COW final, shared-prefix form")
     used, total, failed = bm.stats()
     say(f"COW blocks used {used} of {total}, failed allocations {failed}")
     got_img = read_pool(pool)
