@@ -1,7 +1,9 @@
 """Pins of the oracle's paged prefill (a chunk of new tokens per sequence,
 causal over the cache): the whole-prompt case against a matrix-form causal
-softmax attention written independently here, the chunk's last token against
-the decode oracle, chunking invariance (one chunk or two give the same rows),
+softmax attention written independently here, chunks at the end of each
+context against torch's scaled_dot_product_attention with an explicit
+boolean causal mask (a library routine), the chunk's last token against the
+decode oracle, chunking invariance (one chunk or two give the same rows),
 and zero rows for queries with no position.
 """
 
@@ -88,3 +90,42 @@ def test_queries_without_a_position_are_zero():
     q = workloads.to_bf16_bits(rng.standard_normal((6, 2, 32), dtype=np.float32))
     got = attention.paged_prefill(q, img, 0, bt, np.array([4]), np.array([0, 6]), 0.2)
     assert not got[:2].any() and np.all(np.abs(got[2:]).sum(axis=(1, 2)) > 0)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_chunks_match_torch_sdpa_with_a_causal_mask(seed):
+    """Chunks of new tokens at the end of each context (some longer than
+    the context, whose extra queries get zero rows) against torch's
+    scaled_dot_product_attention in float64 with an explicit boolean mask
+    over the whole context (a library routine given the mask)."""
+    import torch
+    rng = np.random.default_rng(14100 + seed)
+    G = int(rng.choice([1, 2, 4]))
+    H, D, B = 2, 16, int(rng.choice([4, 8]))
+    ctx = [int(x) for x in rng.integers(1, 40, size=4)]
+    n = [int(rng.integers(0, c + 3)) for c in ctx]            # up to 2 past the context
+    img, bt, k, v = _pool(rng, ctx, B=B, H=H, D=D)
+    qs = np.concatenate([[0], np.cumsum(n)])
+    q = workloads.to_bf16_bits(rng.standard_normal((int(qs[-1]), H * G, D), dtype=np.float32))
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
+    got = attention.paged_prefill(q, img, 0, bt, np.asarray(ctx), qs, scale)
+    off = np.concatenate([[0], np.cumsum(ctx)])
+    for s in range(len(ctx)):
+        if n[s] == 0:
+            continue
+        c = ctx[s]
+        kk = torch.from_numpy(codecs.bf16_bits_to_f64(k[off[s]:off[s] + c])).permute(1, 0, 2)
+        vv = torch.from_numpy(codecs.bf16_bits_to_f64(v[off[s]:off[s] + c])).permute(1, 0, 2)
+        kk = kk.repeat_interleave(G, dim=0).contiguous()
+        vv = vv.repeat_interleave(G, dim=0).contiguous()
+        qq = torch.from_numpy(codecs.bf16_bits_to_f64(q[qs[s]:qs[s + 1]])).permute(1, 0, 2).contiguous()
+        pos = c - n[s] + torch.arange(n[s])                  # each query's position
+        mask = torch.arange(c)[None, :] <= pos[:, None]      # [n, c]: keys at or before the position
+        valid = pos >= 0
+        want = torch.zeros_like(qq)
+        if valid.any():
+            o = torch.nn.functional.scaled_dot_product_attention(qq[:, valid], kk, vv, attn_mask=mask[valid],
+                                                                 scale=float(np.float32(scale)))
+            want[:, valid] = o
+        want = want.permute(1, 0, 2).numpy()
+        assert np.max(np.abs(got[qs[s]:qs[s + 1]] - want)) < 1e-12, s
