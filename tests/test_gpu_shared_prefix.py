@@ -141,6 +141,23 @@ def test_shared_prefix_matches_oracle(dt, D, B, hkv, G):
     assert not got[c.ctx == 0].any()
 
 
+@pytest.mark.parametrize("hkv,G", [(2, 8), (1, 20)])
+@pytest.mark.parametrize("dt", [pkv.PKV_KV_BF16, pkv.PKV_KV_INT8])
+def test_wide_query_groups(dt, hkv, G):
+    """Query groups of 8 (the 70B shape) and 20 (more than one 16-head tile
+    per KV head in the split pass; columns of one sequence spread over two
+    tiles in the prefix pass)."""
+    rng = np.random.default_rng(14400 + 3 * dt + G)
+    c = _case(rng, dt, 10, _ctx_mix(160, rng, 12), hkv, G, 128, 16)
+    say(f"shared prefix wide groups dt={dt} hkv={hkv} G={G}")
+    got, scale = _run(c)
+    want = _want(c, scale)
+    assert np.all(np.isfinite(got))
+    mx, rel = errors(got, want)
+    say(f"  max_abs={mx:.3e} rel={rel:.3e}")
+    assert mx <= _bar(dt)[0] and rel <= _bar(dt)[1]
+
+
 @pytest.mark.parametrize("dt", [pkv.PKV_KV_BF16, pkv.PKV_KV_FP8_E5M2, pkv.PKV_KV_INT4])
 def test_many_sequences_span_several_column_groups(dt):
     """200 sequences with one query head per KV head (the shared-prompt
