@@ -296,11 +296,11 @@ def cow_bench(args):
         if shared_form:
             pkv.paged_attn_decode_shared_prefix(o, q, pool, 0, tab, ctx, w.scale, d_prefix, prefix_blocks * B,
                                                 partition_size=P, workspace=ws, key=key, value=value, stream=st)
-        elif key is not None:
-            pkv.paged_attn_decode_append(o, q, pool, 0, key, value, tab, ctx, w.scale, partition_size=P,
-                                         workspace=ws, stream=st)
         else:
-            pkv.paged_attn_decode(o, q, pool, 0, tab, ctx, w.scale, partition_size=P, workspace=ws, stream=st)
+            # the tables share the prefix's blocks: K/V loaded with the default
+            # cache policy, so that a block's other readers find it in L2
+            pkv.paged_attn_decode_ex(o, q, pool, 0, tab, ctx, w.scale, partition_size=P, workspace=ws, key=key,
+                                     value=value, keep_kv_cached=True, stream=st)
     st = torch.cuda.current_stream()
     # two sets of pinned staging and device tables: the host prepares step
     # i + 1 while the GPU runs step i
@@ -385,7 +385,7 @@ def cow_bench(args):
                                   "40q/40kv heads, head_dim 128, bf16 KV, block 16, 64..512 generated tokens each, "
                                   "appending decode per step",
                       "decode_call": ("paged_attn_decode_shared_prefix (the 93 shared blocks read once per KV head)"
-                                      if shared else "paged_attn_decode_append"),
+                                      if shared else "paged_attn_decode_ex, appending, PKV_DECODE_KEEP_KV_CACHED"),
                       "seq_steps": seq_steps, "cow_pairs": pairs_total},
            "final_state_max_abs_diff_vs_plain_decode": form_diff,
            "wall_s": round(wall, 4), "decode_gpu_s": round(gpu, 4),

@@ -378,7 +378,20 @@ typedef struct {
   int32_t sliding_window;
   void* workspace;             /* device */
   uint64_t workspace_bytes;
+  uint32_t flags;              /* 0, or PKV_DECODE_KEEP_KV_CACHED (other bits: PKV_ERR_INVALID) */
 } pkv_decode_args;
+
+/* pkv_decode_args.flags.  The split form loads K/V tiles with the
+ * non-temporal hint by default: when each sequence's blocks are its own,
+ * every tile is read once per call, and streaming it keeps the reused lines
+ * (queries, tables, partials) in the L2 and the MALL.  When tables share
+ * blocks - sequences forked from one prompt, a cached prefix reused by many
+ * requests ([BJD] §3.1, §3.2) - and the call is not
+ * paged_attn_decode_shared_prefix, PKV_DECODE_KEEP_KV_CACHED loads them with
+ * the default policy, so that the other readers of a shared block find it
+ * in the caches.  Results are identical either way; paged_attn_decode and
+ * paged_attn_decode_append stream. */
+#define PKV_DECODE_KEEP_KV_CACHED 1u
 
 /* Decode with every option: same behaviour, ownership and errors as
  * paged_attn_decode (key == NULL) or paged_attn_decode_append (key set);

@@ -34,6 +34,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 PKV_OK, PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_HIP = 0, -1, -2, -3, -4
 PKV_KV_BF16, PKV_KV_FP8_E5M2, PKV_KV_INT8, PKV_KV_INT8_TENSOR, PKV_KV_INT8_CHANNEL, PKV_KV_INT4 = 0, 1, 2, 3, 4, 5
 PKV_KV_INT8_KCHANNEL_VTENSOR = 6
+PKV_DECODE_KEEP_KV_CACHED = 1
 ELEM_BYTES = {PKV_KV_BF16: 2, PKV_KV_FP8_E5M2: 1, PKV_KV_INT8: 1}
 
 
@@ -72,7 +73,7 @@ class DecodeArgs(ctypes.Structure):
                 ("num_q_heads", ctypes.c_int32), ("scale", ctypes.c_float), ("kv_dtype", ctypes.c_int32),
                 ("kv_scales", ctypes.POINTER(KVScales)), ("partition_size", ctypes.c_int32),
                 ("sliding_window", ctypes.c_int32), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_uint64)]
+                ("workspace_bytes", ctypes.c_uint64), ("flags", ctypes.c_uint32)]
 
 
 _P = ctypes.c_void_p
@@ -259,10 +260,11 @@ def paged_attn_decode_append(out, q, pool: Pool, layer: int, key, value, block_t
 def paged_attn_decode_ex(out, q, pool: Pool, layer: int, block_tables, context_lens, scale: float,
                         kv_dtype: int | None = None, k_scale: float = 1.0, v_scale: float = 1.0,
                         partition_size: int = 0, workspace=None, key=None, value=None, sliding_window: int = 0,
-                        stream=None):
+                        keep_kv_cached: bool = False, stream=None):
     """Decode with every option (see pkv.h): the appending form when key and
     value are given, attention restricted to the last ``sliding_window``
-    positions when it is > 0."""
+    positions when it is > 0, K/V loaded with the default cache policy
+    instead of streamed when ``keep_kv_cached`` (tables that share blocks)."""
     S, hq, _ = q.shape
     sc = KVScales(k_scale, v_scale)
     a = DecodeArgs()
@@ -276,6 +278,7 @@ def paged_attn_decode_ex(out, q, pool: Pool, layer: int, block_tables, context_l
     a.partition_size, a.sliding_window = partition_size, sliding_window
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a.flags = PKV_DECODE_KEEP_KV_CACHED if keep_kv_cached else 0
     _check(_lib.paged_attn_decode_ex(ctypes.byref(a), _stream(stream)))
 
 
@@ -288,7 +291,8 @@ def paged_attn_shared_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads
 def paged_attn_decode_shared_prefix(out, q, pool: Pool, layer: int, block_tables, context_lens, scale: float,
                                     prefix_table, prefix_len: int, kv_dtype: int | None = None,
                                     k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 512,
-                                    workspace=None, key=None, value=None, stream=None):
+                                    workspace=None, key=None, value=None, keep_kv_cached: bool = False,
+                                    stream=None):
     """Decode of sequences sharing a prompt prefix (see pkv.h): positions
     below prefix_len are read through prefix_table (int32 device tensor of
     prefix_len / B blocks) for every sequence, once per KV head."""
@@ -305,6 +309,7 @@ def paged_attn_decode_shared_prefix(out, q, pool: Pool, layer: int, block_tables
     a.partition_size, a.sliding_window = partition_size, 0
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a.flags = PKV_DECODE_KEEP_KV_CACHED if keep_kv_cached else 0
     _check(_lib.paged_attn_decode_shared_prefix(ctypes.byref(a), _ptr(prefix_table), int(prefix_len),
                                                 _stream(stream)))
 
@@ -312,7 +317,7 @@ def paged_attn_decode_shared_prefix(out, q, pool: Pool, layer: int, block_tables
 def paged_attn_decode_noalloc(out, q, pool: Pool, layer: int, block_tables, context_lens, scale: float,
                               kv_dtype: int | None = None, k_scale: float = 1.0, v_scale: float = 1.0,
                               partition_size: int = 0, key=None, value=None, sliding_window: int = 0,
-                              stream=None):
+                              keep_kv_cached: bool = False, stream=None):
     """paged_attn_decode_ex without a workspace argument: the split form's
     scratch is the library's static device array (see pkv.h)."""
     S, hq, _ = q.shape
@@ -327,6 +332,7 @@ def paged_attn_decode_noalloc(out, q, pool: Pool, layer: int, block_tables, cont
     a.kv_scales = ctypes.pointer(sc)
     a.partition_size, a.sliding_window = partition_size, sliding_window
     a.workspace, a.workspace_bytes = None, 0
+    a.flags = PKV_DECODE_KEEP_KV_CACHED if keep_kv_cached else 0
     _check(_lib.paged_attn_decode_noalloc(ctypes.byref(a), _stream(stream)))
 
 

@@ -264,6 +264,9 @@ def test_attention_entry_points_check_arguments_on_the_host():
     args.sliding_window, args.q = 40, P
     assert pkv._lib.paged_attn_decode_ex(ctypes.byref(args), None) == pkv.PKV_ERR_INVALID
     assert "alias" in pkv.last_error()
+    args.q, args.flags = P + 4096, 2           # a flag bit this library does not define
+    assert pkv._lib.paged_attn_decode_ex(ctypes.byref(args), None) == pkv.PKV_ERR_INVALID
+    assert "flags" in pkv.last_error()
 
 
 def test_cache_write_refuses_non_finite_per_tensor_scales():
