@@ -113,6 +113,9 @@ def parse():
                          "one layer per call; TFLOP/s against the bf16 matrix-core peak")
     ap.add_argument("--prefill-workload", default="prefix_cache", choices=["prefix_cache", "full_prompt"],
                     help="with --prefill: prefix_cache (above) or full_prompt (16 whole 4096-token prompts)")
+    ap.add_argument("--p-one-part", action="store_true",
+                    help="with --prefill: PKV_PREFILL_P_ONE_PART (softmax weights meet V rounded once, one "
+                         "matrix-core product per P.V tile instead of two)")
     ap.add_argument("--compute-probe", action="store_true",
                     help="instead of the decode step: time the compute of one 16-token bf16 block of one KV head "
                          "per wave (matrix cores vs vector ALU, no HBM traffic; libpkv_probe.so) against the "
@@ -554,7 +557,8 @@ def prefill_bench(args):
     maxq = int(chunk.max())
 
     def call():
-        pkv.paged_attn_prefill(out, q, pool, 0, tables, ctx, qs, w.scale, maxq, k_scale=sck, v_scale=scv, stream=st)
+        pkv.paged_attn_prefill(out, q, pool, 0, tables, ctx, qs, w.scale, maxq, k_scale=sck, v_scale=scv,
+                               p_one_part=args.p_one_part, stream=st)
 
     for _ in range(args.warmup):
         call()
@@ -620,13 +624,14 @@ def prefill_bench(args):
                                    "bf16 KV, block 16, one layer") if args.prefill_workload == "prefix_cache" else
                                   ("paged prefill of 16 whole 4096-token prompts, 64q/8kv heads, head_dim 128, bf16 "
                                    "KV, block 16, one layer"),
-                      "new_tokens": T, "max_query_len": maxq, "flops_per_call": flops},
+                      "new_tokens": T, "max_query_len": maxq, "flops_per_call": flops,
+                      "p_operand": "one rounded part" if args.p_one_part else "hi + lo parts"},
            "roofline": {"bound": "mfma", "kernel": "pa_prefill_kernel", "achieved": round(tfs, 2),
                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tfs / MFMA_BF16_PEAK_TFLOPS, 4),
                         "traffic": (measured_traffic(PREFILL_PROFILE, PREFILL_SRCS)
                                     if args.prefill_workload == "prefix_cache" and kvt == pkv.PKV_KV_BF16
-                                    else None),
+                                    and not args.p_one_part else None),
                         "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated)"},
            "cpu_baseline": cpu, "parity_sample": parity}
     print(json.dumps(res), flush=True)

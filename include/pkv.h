@@ -328,6 +328,28 @@ pkv_status paged_attn_prefill(float* out, const void* q, const pkv_pool* pool, i
                               int32_t max_query_len, int32_t num_q_heads, float scale, int32_t kv_dtype,
                               const pkv_kv_scales* kv_scales, hipStream_t stream);
 
+/* paged_attn_prefill with options (flags; 0 is paged_attn_prefill itself).
+ * The pages fix no precision for the products of the softmax weights with
+ * V ([KVP] §四 and [BJD] §5 speak only of the KV storage types), so the
+ * prefill offers a faster reading beside its default:
+ * PKV_PREFILL_P_ONE_PART: each weight p meets V rounded once - to bf16, or
+ * to fp16 where V enters the products as fp16 (INT8 per tensor, per
+ * channel) - instead of as hi + lo parts, which halves the matrix-core
+ * products of P.V (a third of all the products of a step).  The softmax
+ * denominator is then the sum of the rounded weights (INT8 per token-head,
+ * whose weights carry the V scale: of the unrounded ones), so with u =
+ * 2^-8 (bf16) or 2^-11 (fp16) an output element moves by at most about
+ * u * (max - min) of the V values its query attends (INT8 per token-head:
+ * u * max |V|) beyond the default's error.  Unknown flag bits:
+ * PKV_ERR_INVALID.  Arguments, layouts and the other errors as for
+ * paged_attn_prefill. */
+#define PKV_PREFILL_P_ONE_PART 1u
+pkv_status paged_attn_prefill_ex(float* out, const void* q, const pkv_pool* pool, int32_t layer,
+                                 const int32_t* block_tables, int32_t table_width, const int32_t* context_lens,
+                                 const int32_t* query_start, int32_t num_seqs, int32_t num_queries,
+                                 int32_t max_query_len, int32_t num_q_heads, float scale, int32_t kv_dtype,
+                                 const pkv_kv_scales* kv_scales, uint32_t flags, hipStream_t stream);
+
 /* One decode step with its cache write in the same launch: for each sequence s
  * with ctx_s > 0, the new token's K and V (key, value: device bf16
  * [S][H][D], 16-byte aligned) are stored at position ctx_s - 1 - the slot the

@@ -35,6 +35,7 @@ PKV_OK, PKV_ERR_INVALID, PKV_ERR_UNSUPPORTED, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_HIP
 PKV_KV_BF16, PKV_KV_FP8_E5M2, PKV_KV_INT8, PKV_KV_INT8_TENSOR, PKV_KV_INT8_CHANNEL, PKV_KV_INT4 = 0, 1, 2, 3, 4, 5
 PKV_KV_INT8_KCHANNEL_VTENSOR = 6
 PKV_DECODE_KEEP_KV_CACHED = 1
+PKV_PREFILL_P_ONE_PART = 1
 ELEM_BYTES = {PKV_KV_BF16: 2, PKV_KV_FP8_E5M2: 1, PKV_KV_INT8: 1}
 
 
@@ -78,6 +79,7 @@ class DecodeArgs(ctypes.Structure):
 
 _P = ctypes.c_void_p
 _I32, _I64, _U64, _F = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
+_U32 = ctypes.c_uint32
 _I32P = ctypes.POINTER(ctypes.c_int32)
 _I64P = ctypes.POINTER(ctypes.c_int64)
 
@@ -102,6 +104,8 @@ SIGNATURES = {
     "paged_attn_shared_prefix_workspace_bytes": (_U64, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "paged_attn_prefill": (_I32, [_P, _P, ctypes.POINTER(PoolDesc), _I32, _P, _I32, _P, _P, _I32, _I32, _I32,
                                   _I32, _F, _I32, ctypes.POINTER(KVScales), _P]),
+    "paged_attn_prefill_ex": (_I32, [_P, _P, ctypes.POINTER(PoolDesc), _I32, _P, _I32, _P, _P, _I32, _I32, _I32,
+                                     _I32, _F, _I32, ctypes.POINTER(KVScales), _U32, _P]),
     "pkv_check_slots": (_I32, [_I64P, _I32, _I64]),
     "pkv_check_pairs": (_I32, [_I64P, _I32, _I32]),
     "pkv_check_tables": (_I32, [_I32P, _I32P, _I32, _I32, _I32, _I32]),
@@ -338,17 +342,22 @@ def paged_attn_decode_noalloc(out, q, pool: Pool, layer: int, block_tables, cont
 
 def paged_attn_prefill(out, q, pool: Pool, layer: int, block_tables, context_lens, query_start, scale: float,
                        max_query_len: int, kv_dtype: int | None = None, k_scale: float = 1.0,
-                       v_scale: float = 1.0, stream=None):
+                       v_scale: float = 1.0, p_one_part: bool = False, stream=None):
     """Causal attention of a chunk of new tokens per sequence over its cached
     context (see pkv.h): q, out are [T][Hq][D] (bf16, fp32); query_start is
-    int32 [S + 1] on the device; max_query_len bounds every chunk."""
+    int32 [S + 1] on the device; max_query_len bounds every chunk.
+    p_one_part: paged_attn_prefill_ex with PKV_PREFILL_P_ONE_PART."""
     T, hq, _ = q.shape
     S = context_lens.shape[0]
     sc = KVScales(k_scale, v_scale)
     kvd = pool.cfg.kv_dtype if kv_dtype is None else kv_dtype
-    _check(_lib.paged_attn_prefill(_ptr(out), _ptr(q), ctypes.byref(pool.desc), layer, _ptr(block_tables),
-                                   block_tables.shape[1], _ptr(context_lens), _ptr(query_start), S, T,
-                                   int(max_query_len), hq, float(scale), kvd, ctypes.byref(sc), _stream(stream)))
+    args = (_ptr(out), _ptr(q), ctypes.byref(pool.desc), layer, _ptr(block_tables), block_tables.shape[1],
+            _ptr(context_lens), _ptr(query_start), S, T, int(max_query_len), hq, float(scale), kvd,
+            ctypes.byref(sc))
+    if p_one_part:
+        _check(_lib.paged_attn_prefill_ex(*args, PKV_PREFILL_P_ONE_PART, _stream(stream)))
+    else:
+        _check(_lib.paged_attn_prefill(*args, _stream(stream)))
 
 
 # ------------------------------------------------------------------- checks

@@ -201,7 +201,11 @@ __device__ __forceinline__ int wave_min_i(int v) {
 // The body of both kernels: SH selects the shared-prefix pass (columns
 // across sequences, the prefix's keys split over a workgroup's waves and
 // merged in LDS) over the prefill (columns of one sequence's chunk, causal).
-template <int D, int KVT, int B, int NT, int NB, bool SH>
+// P1: p meets V as one rounded part (bf16, or fp16 where V enters as fp16)
+// instead of hi + lo parts, one matrix-core product per tile instead of two;
+// the softmax denominator is then the sum of the rounded p (per-token INT8,
+// whose p carries the V scale: the sum of the unrounded p).
+template <int D, int KVT, int B, int NT, int NB, bool SH, bool P1>
 __device__ __forceinline__ void prefill_body(const PrefillParams& pp) {
   const DecodeParams& p = pp.d;
   using T = Tile<D, KVT>;
@@ -481,38 +485,47 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& pp) {
         if constexpr (I8V) {   // fp16 parts for the fp16 V operand
           ph[h][0] = pack_f16x2(pv[0], pv[1]);
           ph[h][1] = pack_f16x2(pv[2], pv[3]);
-          pl[h][0] = pack_f16x2(pv[0] - f16_lo(ph[h][0]), pv[1] - f16_hi(ph[h][0]));
-          pl[h][1] = pack_f16x2(pv[2] - f16_lo(ph[h][1]), pv[3] - f16_hi(ph[h][1]));
+          if constexpr (!P1) {
+            pl[h][0] = pack_f16x2(pv[0] - f16_lo(ph[h][0]), pv[1] - f16_hi(ph[h][0]));
+            pl[h][1] = pack_f16x2(pv[2] - f16_lo(ph[h][1]), pv[3] - f16_hi(ph[h][1]));
+          }
         } else {
           ph[h][0] = pack_bf16x2(pv[0], pv[1]);
           ph[h][1] = pack_bf16x2(pv[2], pv[3]);
-          pl[h][0] = pack_bf16x2(pv[0] - bf16_lo(ph[h][0]), pv[1] - bf16_hi(ph[h][0]));
-          pl[h][1] = pack_bf16x2(pv[2] - bf16_lo(ph[h][1]), pv[3] - bf16_hi(ph[h][1]));
+          if constexpr (!P1) {
+            pl[h][0] = pack_bf16x2(pv[0] - bf16_lo(ph[h][0]), pv[1] - bf16_hi(ph[h][0]));
+            pl[h][1] = pack_bf16x2(pv[2] - bf16_lo(ph[h][1]), pv[3] - bf16_hi(ph[h][1]));
+          }
         }
       }
       if constexpr (I8V) {
         // the sum the 1152 offset of V is taken back with: that of the p the
-        // products use (hi + lo parts), which is also the softmax denominator
+        // products use, which is also the softmax denominator
         psum = 0.f;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int e = 0; e < 2; ++e)
-            psum += (f16_lo(ph[h][e]) + f16_lo(pl[h][e])) + (f16_hi(ph[h][e]) + f16_hi(pl[h][e]));
+          for (int e = 0; e < 2; ++e) {
+            psum += f16_lo(ph[h][e]) + f16_hi(ph[h][e]);
+            if constexpr (!P1) psum += f16_lo(pl[h][e]) + f16_hi(pl[h][e]);
+          }
       }
-      if constexpr (I4) {
-        // the sum the 136 offset of V is taken back with: that of the p the
-        // products use (hi + lo parts), which is also the softmax denominator
+      if constexpr (I4 || (P1 && !I8V && KVT != PKV_KV_INT8)) {
+        // INT4: the sum the 136 offset of V is taken back with; with one
+        // part, the sum of the rounded p: that of the p the products use,
+        // which is also the softmax denominator
         psum = 0.f;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int e = 0; e < 2; ++e)
-            psum += (bf16_lo(ph[h][e]) + bf16_lo(pl[h][e])) + (bf16_hi(ph[h][e]) + bf16_hi(pl[h][e]));
+          for (int e = 0; e < 2; ++e) {
+            psum += bf16_lo(ph[h][e]) + bf16_hi(ph[h][e]);
+            if constexpr (!P1) psum += bf16_lo(pl[h][e]) + bf16_hi(pl[h][e]);
+          }
       }
       l_run[nt] = l_run[nt] * alpha[nt] + psum;
       pop[nt] = __builtin_bit_cast(bf16x8, u32x4{ph[0][0], ph[0][1], ph[1][0], ph[1][1]});
-      pop_lo[nt] = __builtin_bit_cast(bf16x8, u32x4{pl[0][0], pl[0][1], pl[1][0], pl[1][1]});
+      if constexpr (!P1) pop_lo[nt] = __builtin_bit_cast(bf16x8, u32x4{pl[0][0], pl[0][1], pl[1][0], pl[1][1]});
     }
 #pragma unroll
     for (int cc = 0; cc < T::NC; ++cc) {
@@ -548,11 +561,12 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& pp) {
         if constexpr (I8V) {
           acc[nt][cc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, va),
                                                                __builtin_bit_cast(f16x8, pop[nt]), acc[nt][cc], 0, 0, 0);
-          acc[nt][cc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, va),
-                                                               __builtin_bit_cast(f16x8, pop_lo[nt]), acc[nt][cc], 0, 0, 0);
+          if constexpr (!P1)
+            acc[nt][cc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, va),
+                                                                 __builtin_bit_cast(f16x8, pop_lo[nt]), acc[nt][cc], 0, 0, 0);
         } else {
           acc[nt][cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop[nt], acc[nt][cc], 0, 0, 0);
-          acc[nt][cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_lo[nt], acc[nt][cc], 0, 0, 0);
+          if constexpr (!P1) acc[nt][cc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_lo[nt], acc[nt][cc], 0, 0, 0);
         }
       }
     }
@@ -678,10 +692,10 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& pp) {
   }
 }
 
-template <int D, int KVT, int B>
+template <int D, int KVT, int B, bool P1>
 __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(kPrefillWavesPerSimd, kPrefillWavesPerSimd)))
 void pa_prefill_kernel(const PrefillParams pp) {
-  prefill_body<D, KVT, B, prefill_nt<D, KVT, B>(), kPrefillBuf, false>(pp);
+  prefill_body<D, KVT, B, prefill_nt<D, KVT, B>(), kPrefillBuf, false, P1>(pp);
 }
 
 // The shared-prefix pass of a decode: one wave per SIMD holding kPrefixBuf
@@ -690,7 +704,7 @@ void pa_prefill_kernel(const PrefillParams pp) {
 template <int D, int KVT, int B>
 __global__ __launch_bounds__(kWave * kNW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void pa_prefix_kernel(const PrefillParams pp) {
-  prefill_body<D, KVT, B, prefill_nt<D, KVT, B>(), kPrefixBuf, true>(pp);
+  prefill_body<D, KVT, B, prefill_nt<D, KVT, B>(), kPrefixBuf, true, false>(pp);
 }
 
 // prefill_nt() of the variant the call runs
@@ -700,10 +714,14 @@ int prefill_tiles_per_wave(int D, int kvt, int B) {
   });
 }
 
-hipError_t launch_prefill(const PrefillParams& p, int D, int kvt, int B, int grid, hipStream_t stream) {
+hipError_t launch_prefill(const PrefillParams& p, int D, int kvt, int B, int grid, bool one_part,
+                          hipStream_t stream) {
   return with_variant<true>(D, kvt, B, [&](auto dc, auto kc, auto bc) {
-    hipLaunchKernelGGL((pa_prefill_kernel<decltype(dc)::value, decltype(kc)::value, decltype(bc)::value>),
-                       dim3(grid), dim3(kWave * kNW), 0, stream, p);
+    constexpr int D_ = decltype(dc)::value, K_ = decltype(kc)::value, B_ = decltype(bc)::value;
+    if (one_part)
+      hipLaunchKernelGGL((pa_prefill_kernel<D_, K_, B_, true>), dim3(grid), dim3(kWave * kNW), 0, stream, p);
+    else
+      hipLaunchKernelGGL((pa_prefill_kernel<D_, K_, B_, false>), dim3(grid), dim3(kWave * kNW), 0, stream, p);
     return hipGetLastError();
   });
 }
@@ -754,7 +772,7 @@ hipError_t launch_prefill_as_decode(const PrefillDecodeArgs& a, hipStream_t stre
   pp.tiles = (int32_t)tiles;
   pp.T = a.num_seqs;
   pp.maxq = 1;
-  return launch_prefill(pp, c.head_dim, c.kv_dtype, c.block_size, (int)((items + 7) / 8 * 8), stream);
+  return launch_prefill(pp, c.head_dim, c.kv_dtype, c.block_size, (int)((items + 7) / 8 * 8), false, stream);
 }
 
 // Geometry of the shared-prefix pass: workgroups of 16 prefill_nt()
@@ -814,12 +832,16 @@ hipError_t launch_prefix_pass(const PrefixPassArgs& a, hipStream_t stream) {
 
 using namespace pkv;
 
-extern "C" pkv_status paged_attn_prefill(float* out, const void* q, const pkv_pool* pool, int32_t layer,
-                                         const int32_t* block_tables, int32_t table_width,
-                                         const int32_t* context_lens, const int32_t* query_start,
-                                         int32_t num_seqs, int32_t num_queries, int32_t max_query_len,
-                                         int32_t num_q_heads, float scale, int32_t kv_dtype,
-                                         const pkv_kv_scales* kv_scales, hipStream_t stream) {
+extern "C" pkv_status paged_attn_prefill_ex(float* out, const void* q, const pkv_pool* pool, int32_t layer,
+                                            const int32_t* block_tables, int32_t table_width,
+                                            const int32_t* context_lens, const int32_t* query_start,
+                                            int32_t num_seqs, int32_t num_queries, int32_t max_query_len,
+                                            int32_t num_q_heads, float scale, int32_t kv_dtype,
+                                            const pkv_kv_scales* kv_scales, uint32_t flags, hipStream_t stream) {
+  if (flags & ~PKV_PREFILL_P_ONE_PART) {
+    set_error("unknown prefill flags 0x%x", flags);
+    return PKV_ERR_INVALID;
+  }
   pkv_status st = check_pool(pool);
   if (st != PKV_OK) return st;
   const pkv_pool_config& c = pool->cfg;
@@ -905,11 +927,22 @@ extern "C" pkv_status paged_attn_prefill(float* out, const void* q, const pkv_po
   pp.tiles = (int32_t)tiles;
   pp.T = num_queries;
   pp.maxq = max_query_len;
-  const hipError_t e = launch_prefill(pp, c.head_dim, c.kv_dtype, c.block_size, (int)((items + 7) / 8 * 8), stream);
+  const hipError_t e = launch_prefill(pp, c.head_dim, c.kv_dtype, c.block_size, (int)((items + 7) / 8 * 8),
+                                      (flags & PKV_PREFILL_P_ONE_PART) != 0, stream);
   if (e != hipSuccess) {
     set_error("paged_attn_prefill launch failed: %s", hipGetErrorString(e));
     return PKV_ERR_HIP;
   }
   clear_error();
   return PKV_OK;
+}
+
+extern "C" pkv_status paged_attn_prefill(float* out, const void* q, const pkv_pool* pool, int32_t layer,
+                                         const int32_t* block_tables, int32_t table_width,
+                                         const int32_t* context_lens, const int32_t* query_start,
+                                         int32_t num_seqs, int32_t num_queries, int32_t max_query_len,
+                                         int32_t num_q_heads, float scale, int32_t kv_dtype,
+                                         const pkv_kv_scales* kv_scales, hipStream_t stream) {
+  return paged_attn_prefill_ex(out, q, pool, layer, block_tables, table_width, context_lens, query_start, num_seqs,
+                               num_queries, max_query_len, num_q_heads, scale, kv_dtype, kv_scales, 0u, stream);
 }

@@ -25,7 +25,7 @@ SCALES = {pkv.PKV_KV_FP8_E5M2: (0.5, 1.5), pkv.PKV_KV_INT8_TENSOR: (0.035, 0.03)
           pkv.PKV_KV_INT8_KCHANNEL_VTENSOR: (0.5, 0.03)}       # its K scale is not read
 
 
-def _run(rng, dt, ctx, chunk, hkv=2, G=4, D=128, B=16, poison=True, needles=0):
+def _run(rng, dt, ctx, chunk, hkv=2, G=4, D=128, B=16, poison=True, needles=0, p_one_part=False, info=None):
     import torch
     ctx = np.asarray(ctx, np.int32)
     S = len(ctx)
@@ -93,10 +93,12 @@ def _run(rng, dt, ctx, chunk, hkv=2, G=4, D=128, B=16, poison=True, needles=0):
     out = torch.full((max(T, 1), hq, D), float("nan"), dtype=torch.float32, device="cuda")
     pkv.paged_attn_prefill(out, bf16_dev(q) if T else torch.empty((0, hq, D), dtype=torch.bfloat16, device="cuda"),
                            pool, 0, dev(tables), dev(ctx), dev(qs), scale, int(chunk.max()) if S else 0,
-                           k_scale=ks, v_scale=vs)
+                           k_scale=ks, v_scale=vs, p_one_part=p_one_part)
     torch.cuda.synchronize()
     got = out.cpu().numpy()[:T]
     want = attention.paged_prefill(q, img, 0, tables, ctx, qs, scale, ks, vs)
+    if info is not None:
+        info.update(img=img, tables=tables, ctx=ctx, qs=qs, ks=ks, vs=vs, G=G)
     return got, want
 
 

@@ -246,6 +246,13 @@ def test_attention_entry_points_check_arguments_on_the_host():
     assert prefill(nseq=0) == pkv.PKV_OK         # nothing to do: no launch
     assert prefill(d=_fake_pool(bf16, D=96)) == pkv.PKV_ERR_UNSUPPORTED
 
+    def prefill_ex(flags, layer=0):
+        return pkv._lib.paged_attn_prefill_ex(P, P, ctypes.byref(desc), layer, P, 4, P, P, 2, 5, 3, 4, 0.1, bf16,
+                                              ctypes.byref(sc), flags, None)
+
+    assert prefill_ex(2) == pkv.PKV_ERR_INVALID and "flags" in pkv.last_error()
+    assert prefill_ex(pkv.PKV_PREFILL_P_ONE_PART, layer=2) == pkv.PKV_ERR_INVALID and "layer" in pkv.last_error()
+
     def decode(d=desc, kvd=bf16, part=0, hq=4):
         return pkv._lib.paged_attn_decode(P, P, ctypes.byref(d), 0, P, 4, P, 2, hq, 0.1, kvd, ctypes.byref(sc),
                                           part, None, 0, None)
