@@ -163,14 +163,17 @@ def test_prefill_peaked_needles(dt):
     assert mx <= bar[0] and rel <= bar[1]
 
 
-def test_prefill_prefix_cache_workload_full_size_sampled():
+@pytest.mark.parametrize("p_one_part", [False, True])
+def test_prefill_prefix_cache_workload_full_size_sampled(p_one_part):
     """The benchmark's prefill workload at full size (200 prompts sharing the
     93 cached blocks of a 1500-token system prompt, 60,750 new tokens, 64 q /
     8 kv heads, the benchmark's launch), checked on sampled sequences: the
-    shortest and longest chunks and two random ones."""
+    shortest and longest chunks and two random ones.  With one-part weights
+    the bar adds the rounding bound of test_gpu_prefill_one_part.py:
+    2u / (1 - u) * (max v - min v) / 2 per KV head and dim, u = 2^-8."""
     import torch
     from oracle import layout
-    say("prefill prefix-cache workload, full size")
+    say(f"prefill prefix-cache workload, full size, one part {p_one_part}")
     w = workloads.prefix_prefill()
     S, Hq, Hkv, D, B = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
     ctx = np.asarray(w.context_lens, np.int32)
@@ -188,7 +191,8 @@ def test_prefill_prefix_cache_workload_full_size_sampled():
         pool.memory[off: off + lb].view(torch.bfloat16).normal_(generator=g)
     q = torch.randn((T, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
     out = torch.full((T, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
-    pkv.paged_attn_prefill(out, q, pool, 0, dev(tabs), dev(ctx), dev(qs), w.scale, int(chunk.max()))
+    pkv.paged_attn_prefill(out, q, pool, 0, dev(tabs), dev(ctx), dev(qs), w.scale, int(chunk.max()),
+                           p_one_part=p_one_part)
     torch.cuda.synchronize()
     rng = np.random.default_rng(436109)
     pick = sorted({int(np.argmin(chunk)), int(np.argmax(chunk)), *rng.choice(S, size=2, replace=False).tolist()})
@@ -206,7 +210,15 @@ def test_prefill_prefix_cache_workload_full_size_sampled():
         got = out[qs[s]:qs[s + 1]].cpu().numpy()
         mx, rel = errors(got, want)
         say(f"  seq {s}: ctx {ctx[s]} chunk {chunk[s]} max_abs={mx:.3e} rel={rel:.3e}")
-        assert mx <= BAR[pkv.PKV_KV_BF16][0] and rel <= BAR[pkv.PKV_KV_BF16][1]
+        if p_one_part:
+            _, V = attention.gather_kv(img, 0, np.arange(nblk, dtype=np.int32), int(ctx[s]))
+            u = 2.0**-8
+            bound = np.repeat(u / (1 - u) * (V.max(axis=0) - V.min(axis=0)), Hq // Hkv, axis=0)[None]
+            slack = BAR[pkv.PKV_KV_BF16][1] * np.max(np.abs(want))
+            assert np.max(np.abs(got - want) - bound) <= slack
+            assert mx <= BAR[pkv.PKV_KV_BF16][0]
+        else:
+            assert mx <= BAR[pkv.PKV_KV_BF16][0] and rel <= BAR[pkv.PKV_KV_BF16][1]
     assert torch.isfinite(out).all()
 
 
