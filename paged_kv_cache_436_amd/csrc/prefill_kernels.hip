@@ -304,8 +304,13 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& pp) {
     for (int n = 0; n < NQ; ++n)
 #pragma unroll
       for (int kk = 0; kk < T::KK; ++kk)
-        qop[nt][n][kk] =
-            __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qh + n * D + q_dim0<QL>(kk, j)));
+        // a prefill reads each query once and writes each output row once:
+        // both move with the non-temporal hint, so that they leave the L2s
+        // to the K/V tiles, which the chunk's column tiles read again (the
+        // shared-prefix pass re-reads its rows to merge, and keeps them cached)
+        qop[nt][n][kk] = __builtin_bit_cast(
+            bf16x8, SH ? *reinterpret_cast<const u32x4*>(qh + n * D + q_dim0<QL>(kk, j))
+                       : __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qh + n * D + q_dim0<QL>(kk, j))));
     qsum[nt] = 0.f;
     if constexpr (I4) {
       float a = 0.f;
@@ -611,7 +616,10 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& pp) {
     float* orow = p.out + ((int64_t)(q0 + cq / p.G) * p.Hq + g * p.G + cq % p.G) * D;
     float* prow = lds_o + ((w * NT + nt) * 16 + row) * D;
     auto put = [&](int d, f32x4 v) __attribute__((always_inline)) {   // dims d .. d + 3
-      *reinterpret_cast<f32x4*>((SH ? prow : orow) + d) = v;
+      if constexpr (SH)
+        *reinterpret_cast<f32x4*>(prow + d) = v;
+      else
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(orow + d));
     };
     const float inv = L > 0.f ? 1.f / L : 0.f;   // no key at all (position < 0): zero row
     float o[T::NC][4];
